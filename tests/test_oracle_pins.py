@@ -1,0 +1,323 @@
+"""Pins of the CPU oracle against things other than itself (CPU only).
+
+* an independent pure-Python brute force on tiny dyadic inputs, where every
+  routing score is exact in float32 and float64 so ties are frequent and the
+  tie rules must agree exactly;
+* a hand-derived golden case (tests/golden/hand_routing.json);
+* reductions to textbook attention: a full routing budget is dense causal
+  attention, R = 0 is block-banded causal attention (the pages' local-only
+  control), both checked against torch's scaled_dot_product_attention in
+  float64;
+* invariants: causality of routing and attention, forced target under the same
+  budget, linearity in V, overflow equal to the closed form of a planted
+  address histogram, zero overflow of the balanced generator;
+* the pages' level of agreement between sparse gathering and a dense
+  selected-mask computation.
+"""
+
+import dataclasses
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tests._brute import brute_rope, brute_routed_attention
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _dyadic_inputs(w, seed, bias=False):
+    """Values on a coarse dyadic grid: every routing sum is exact in float32."""
+    rng = np.random.default_rng(seed)
+    S, D, G, C = w.seq, w.head_dim, w.subspaces, w.codes
+    q = rng.integers(-2, 3, size=(S, D)) / 2.0
+    k = rng.integers(-2, 3, size=(S, D)) / 2.0
+    v = rng.standard_normal((S, D))
+    cb = rng.integers(-2, 3, size=(G, C, D)) / 4.0
+    b = rng.integers(-2, 3, size=(G, C)) / 8.0 if bias else None
+    return q, k, v, cb, b
+
+
+SMALL = [
+    dict(seq=64, head_dim=4, block=4, subspaces=2, codes=3, capacity=2, probes=2, max_cand=0, remote=2, local=2),
+    dict(seq=48, head_dim=4, block=4, subspaces=1, codes=4, capacity=1, probes=3, max_cand=2, remote=1, local=1),
+    dict(seq=64, head_dim=2, block=8, subspaces=3, codes=2, capacity=3, probes=5, max_cand=0, remote=3, local=1),
+    dict(seq=96, head_dim=4, block=4, subspaces=2, codes=2, capacity=4, probes=4, max_cand=6, remote=4, local=3),
+    dict(seq=32, head_dim=4, block=2, subspaces=2, codes=2, capacity=2, probes=1, max_cand=0, remote=0, local=2),
+]
+
+
+def _w(**kw):
+    base = synth.workload("tiny")
+    return dataclasses.replace(base, **kw)
+
+
+@pytest.mark.parametrize("case", range(len(SMALL)))
+@pytest.mark.parametrize("seed", [0, 1, 2])
+@pytest.mark.parametrize("rdtype", [np.float32, np.float64])
+def test_oracle_equals_brute_force_on_dyadic_inputs(case, seed, rdtype):
+    w = _w(**SMALL[case])
+    q, k, v, cb, b = _dyadic_inputs(w, seed, bias=(seed == 1))
+    r = oracle.route_head(q, k, cb, b, w, rdtype=rdtype)
+    out = oracle.attention_dense(q, k, v, r["sel"], w.block, w.local)
+    bf = brute_routed_attention(q.tolist(), k.tolist(), v.tolist(), cb.tolist(),
+                                None if b is None else b.tolist(), w)
+    assert r["addr"].tolist() == bf["addr"]
+    assert r["overflow"] == bf["overflow"]
+    for t in range(w.seq):
+        assert [i for i in r["sel"][t] if i >= 0] == bf["sel"][t], t
+    np.testing.assert_allclose(out, np.array(bf["out"]), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("seed", [0, 3])
+def test_forced_target_matches_brute_force(seed):
+    w = _w(**SMALL[0])
+    q, k, v, cb, b = _dyadic_inputs(w, seed)
+    rng = np.random.default_rng(100 + seed)
+    force = rng.integers(-1, w.seq // w.block, size=w.seq)
+    r = oracle.route_head(q, k, cb, b, w, force=force, rdtype=np.float32)
+    bf = brute_routed_attention(q.tolist(), k.tolist(), v.tolist(), cb.tolist(), None, w, force=force.tolist())
+    for t in range(w.seq):
+        assert [i for i in r["sel"][t] if i >= 0] == bf["sel"][t], t
+    out = oracle.attention_dense(q, k, v, r["sel"], w.block, w.local)
+    np.testing.assert_allclose(out, np.array(bf["out"]), rtol=0, atol=1e-12)
+
+
+def test_hand_derived_golden_case():
+    g = json.load(open(os.path.join(GOLDEN, "hand_routing.json")))
+    c = g["config"]
+    w = _w(seq=len(g["k"]), head_dim=2, block=c["block"], subspaces=c["subspaces"], codes=c["codes"],
+           capacity=c["capacity"], probes=c["probes"], max_cand=c["max_cand"], remote=c["remote"],
+           local=c["local"])
+    q, k, v = (np.array(g[n], dtype=np.float64) for n in ("q", "k", "v"))
+    cb = np.array(g["codebook"], dtype=np.float64)
+    r = oracle.route_head(q, k, cb, None, w)
+    assert r["addr"].tolist() == g["addr"]
+    assert r["overflow"] == g["overflow"]
+    assert [[i for i in row if i >= 0] for row in r["sel"]] == g["sel"]
+    out = oracle.attention_dense(q, k, v, r["sel"], w.block, w.local)
+    for t, vis in g["visible_dots"].items():
+        t = int(t)
+        wts = np.array([math.exp(d / math.sqrt(2.0)) for _, d in vis])
+        expect = (wts[:, None] * v[[s for s, _ in vis]]).sum(0) / wts.sum()
+        np.testing.assert_allclose(out[t], expect, rtol=0, atol=1e-14)
+
+
+def _sdpa(q, k, v, mask=None, causal=False):
+    t = [torch.from_numpy(np.asarray(a, dtype=np.float64))[None, None] for a in (q, k, v)]
+    m = None if mask is None else torch.from_numpy(mask)[None, None]
+    return torch.nn.functional.scaled_dot_product_attention(*t, attn_mask=m, is_causal=causal)[0, 0].numpy()
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_full_budget_is_dense_causal_attention(seed):
+    """P = A, capacity >= nb, M = P*capacity and R >= nb select every eligible block."""
+    nb, blk = 8, 8
+    w = _w(seq=nb * blk, head_dim=16, block=blk, subspaces=2, codes=3, capacity=nb, probes=9,
+           max_cand=0, remote=nb, local=2)
+    rng = np.random.default_rng(seed)
+    q, k, v = (rng.standard_normal((w.seq, w.head_dim)) for _ in range(3))
+    cb = rng.standard_normal((2, 3, 16)) / 4
+    r = oracle.route_head(q, k, cb, None, w)
+    out = oracle.attention_dense(q, k, v, r["sel"], w.block, w.local)
+    np.testing.assert_allclose(out, _sdpa(q, k, v, causal=True), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("local", [1, 2, 3])
+def test_local_only_is_block_banded_causal_attention(local):
+    nb, blk, D = 10, 4, 8
+    w = _w(seq=nb * blk, head_dim=D, block=blk, remote=0, local=local)
+    rng = np.random.default_rng(local)
+    q, k, v = (rng.standard_normal((w.seq, D)) for _ in range(3))
+    cb = rng.standard_normal((2, 4, D))
+    r = oracle.route_head(q, k, cb, None, w)
+    assert (r["sel"].size == 0) or np.all(r["sel"] < 0)
+    t = np.arange(w.seq)
+    band = (t[None, :] <= t[:, None]) & (t[None, :] // blk >= t[:, None] // blk - local + 1)
+    out = oracle.attention_dense(q, k, v, r["sel"], blk, local)
+    np.testing.assert_allclose(out, _sdpa(q, k, v, mask=band), rtol=0, atol=1e-12)
+    # a window wider than the sequence is plain causal attention
+    r2 = oracle.route_head(q, k, cb, None, dataclasses.replace(w, local=nb))
+    out2 = oracle.attention_dense(q, k, v, r2["sel"], blk, nb)
+    np.testing.assert_allclose(out2, _sdpa(q, k, v, causal=True), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("t0", [70, 127, 200])
+def test_routing_and_attention_are_causal(t0):
+    """Changing tokens after t0 leaves every selection and output up to t0 bit-identical."""
+    w = synth.workload("recall", batch=1, heads=1, seq=256, block=16)
+    inp = synth.make_core_inputs(w, 5)
+    q, k, v = (inp[n][0, 0].copy() for n in ("q", "k", "v"))
+    cb = inp["codebook"][0]
+    r1 = oracle.route_head(q, k, cb, None, w)
+    o1 = oracle.attention_dense(q, k, v, r1["sel"], w.block, w.local)
+    rng = np.random.default_rng(9)
+    for a in (q, k, v):
+        a[t0 + 1:] = rng.standard_normal(a[t0 + 1:].shape).astype(np.float32) * 3
+    r2 = oracle.route_head(q, k, cb, None, w)
+    o2 = oracle.attention_dense(q, k, v, r2["sel"], w.block, w.local)
+    assert np.array_equal(r1["sel"][:t0 + 1], r2["sel"][:t0 + 1])
+    assert np.array_equal(o1[:t0 + 1], o2[:t0 + 1])
+    assert not np.array_equal(o1[t0 + 1:], o2[t0 + 1:])
+
+
+def test_forced_target_keeps_budget_and_recovers_recall():
+    """Forcing the planted block puts it in every last-block selection, never exceeding R."""
+    w = synth.workload("recall", batch=4, heads=2)
+    inp = synth.make_core_inputs(w, 1)
+    last = np.arange((w.nblocks - 1) * w.block, w.seq)
+    for b in range(w.batch):
+        for h in range(w.heads):
+            args = (inp["q"][b, h], inp["k"][b, h], inp["codebook"][h], None, w)
+            free = oracle.route_head(*args, tokens=last)
+            forced = oracle.route_head(*args, force=inp["force"][b, h], tokens=last)
+            p = int(inp["planted"][b])
+            assert forced["force_ignored"] == 0
+            for row in range(len(last)):
+                s = [i for i in forced["sel"][row] if i >= 0]
+                assert p in s and len(s) <= w.remote and len(set(s)) == len(s)
+                s0 = [i for i in free["sel"][row] if i >= 0]
+                if p in s0:
+                    assert s == s0
+                elif len(s0) == w.remote:
+                    assert s[:-1] == s0[:-1]
+            out = oracle.attention_dense(inp["q"][b, h], inp["k"][b, h], inp["v"][b, h], forced["sel"],
+                                         w.block, w.local, tokens=last)
+            pk = oracle.attention_packed(inp["q"][b, h], inp["k"][b, h], inp["v"][b, h], forced["sel"],
+                                         w.block, w.local, tokens=last)
+            np.testing.assert_allclose(out, pk, rtol=0, atol=1e-12)
+
+
+def test_attention_is_linear_in_v():
+    w = synth.workload("recall", batch=1, heads=1, seq=512)
+    inp = synth.make_core_inputs(w, 2)
+    q, k = inp["q"][0, 0], inp["k"][0, 0]
+    r = oracle.route_head(q, k, inp["codebook"][0], None, w)
+    rng = np.random.default_rng(3)
+    v1, v2 = rng.standard_normal((2, w.seq, w.head_dim))
+    a, b = 0.75, -2.5
+    lhs = oracle.attention_dense(q, k, a * v1 + b * v2, r["sel"], w.block, w.local)
+    rhs = a * oracle.attention_dense(q, k, v1, r["sel"], w.block, w.local) + \
+        b * oracle.attention_dense(q, k, v2, r["sel"], w.block, w.local)
+    np.testing.assert_allclose(lhs, rhs, rtol=0, atol=1e-12)
+
+
+def _planted_keys(target, w, rng, gain):
+    """Keys whose block summaries sit on codebook rows chosen by ``target`` (digits most significant first)."""
+    G, C, D, blk = w.subspaces, w.codes, w.head_dim, w.block
+    cb = rng.standard_normal((G, C, D)) / math.sqrt(D)
+    unit = cb / np.linalg.norm(cb, axis=-1, keepdims=True)
+    k = rng.standard_normal((w.seq, D)) * 0.2
+    for i, a in enumerate(target):
+        push = sum(unit[g, (a // C ** (G - 1 - g)) % C] for g in range(G))
+        k[i * blk:(i + 1) * blk] += gain * push
+    return k, cb
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_overflow_equals_closed_form_of_planted_histogram(seed):
+    w = _w(seq=64 * 16, head_dim=32, block=16, subspaces=2, codes=4, capacity=3, local=2)
+    rng = np.random.default_rng(seed)
+    nb, A = w.nblocks, w.addresses
+    # a skewed assignment: address a drawn with probability ~ 1/(a+1)
+    p = 1.0 / np.arange(1, A + 1)
+    target = rng.choice(A, size=nb, p=p / p.sum())
+    k, cb = _planted_keys(target, w, rng, gain=6.0)
+    q = rng.standard_normal((w.seq, w.head_dim))
+    r = oracle.route_head(q, k, cb, None, w, tokens=[0])
+    assert r["addr"].tolist() == target.tolist()
+    hist = np.bincount(target[: nb - w.local], minlength=A)
+    assert r["overflow"] == int(np.maximum(hist - w.capacity, 0).sum())
+    assert r["overflow"] > 0
+
+
+@pytest.mark.parametrize("seq", [4096, 8192])
+def test_balanced_generator_has_zero_overflow(seq):
+    """The pages report zero posting overflow in their balanced scaling runs."""
+    w = synth.workload("sweep", seq=seq)
+    inp = synth.make_core_inputs(w, 0)
+    for h in range(w.heads):
+        ks = oracle.block_summaries(inp["k"][0, h], w.block)
+        _, addr, margin = oracle.block_addresses(ks, inp["codebook"][h], None)
+        assert np.array_equal(addr, inp["target_addr"][h])
+        assert margin.min() > 1e-2
+        assert oracle.posting_overflow(oracle.posting_lists(addr, w.addresses, w.local), w.capacity) == 0
+
+
+def test_tie_rules():
+    """Equal summaries tie in the rerank (smaller block wins); equal codebook rows tie in the argmax."""
+    w = _w(seq=8 * 4, head_dim=4, block=4, subspaces=1, codes=3, capacity=8, probes=1, max_cand=0,
+           remote=1, local=1)
+    rng = np.random.default_rng(0)
+    k = rng.standard_normal((w.seq, 4))
+    cb = np.zeros((1, 3, 4))
+    cb[0, 0] = cb[0, 1] = [1.0, 0.0, 0.0, 0.0]   # codes 0 and 1 identical
+    cb[0, 2] = [-5.0, 0.0, 0.0, 0.0]
+    k[:, 0] = np.abs(k[:, 0]) + 0.1              # keep code 2 out of the way
+    k[4:8] = k[0:4]                              # blocks 0 and 1 identical -> identical summaries
+    k[0:8, 0] += 10.0                            # and they lead the rerank
+    q = np.tile([1.0, 0.0, 0.0, 0.0], (w.seq, 1))
+    r = oracle.route_head(q, k, cb, None, w)
+    assert set(r["codes"][:, 0].tolist()) == {0}
+    t = w.seq - 1
+    assert r["sel"][t][0] == 0  # block 0 and 1 tie; the smaller index wins
+
+
+@pytest.mark.parametrize("dtype", [np.float64, np.float32])
+def test_sparse_gather_matches_dense_selected_mask(dtype):
+    """The pages report the sparse selected-set attention within 1.43e-6 of a dense selected-mask
+    oracle; the oracle's two attention codes agree to rounding (float64) and within the fp32
+    parity tolerance of 1e-5 when the gather runs in float32."""
+    w = synth.workload("recall", batch=1, heads=1, seq=1024)
+    inp = synth.make_core_inputs(w, 0)
+    q, k, v = (inp[n][0, 0] for n in ("q", "k", "v"))
+    r = oracle.route_head(q, k, inp["codebook"][0], None, w)
+    dense = oracle.attention_dense(q, k, v, r["sel"], w.block, w.local)
+    packed = oracle.attention_packed(q, k, v, r["sel"], w.block, w.local, dtype=dtype)
+    tol = 1e-12 if dtype == np.float64 else 1e-5
+    assert np.abs(dense - packed).max() <= tol
+
+
+def test_rope_is_complex_rotation_and_relative():
+    rng = np.random.default_rng(0)
+    S, D = 12, 8
+    x = rng.standard_normal((S, D))
+    got = oracle.rope(x, 10000.0)
+    np.testing.assert_allclose(got, np.array(brute_rope(x.tolist(), 10000.0)), rtol=0, atol=1e-13)
+    np.testing.assert_allclose(got[0], x[0], rtol=0, atol=0)
+    # <rope(q)_m, rope(k)_n> depends only on m - n
+    qv, kv = rng.standard_normal((2, D))
+    qq = oracle.rope(np.tile(qv, (S, 1)), 10000.0)
+    kk = oracle.rope(np.tile(kv, (S, 1)), 10000.0)
+    assert abs(qq[7] @ kk[4] - qq[5] @ kk[2]) < 1e-12
+    assert abs(qq[3] @ kk[3] - qv @ kv) < 1e-12
+
+
+def test_mixer_matches_brute_force():
+    """delta = concat_h(attention) Wo with Q = RoPE(x Wq), K = RoPE(x Wk), V = x Wv (no biases)."""
+    w = synth.workload("tiny", seq=64, width=16, heads=2, head_dim=8, block=8, codes=2, capacity=2,
+                       probes=2, remote=1, local=1)
+    inp = synth.make_mixer_inputs(w, 0)
+    delta, routes = oracle.mixer_forward(inp["x"], inp["wq"], inp["wk"], inp["wv"], inp["wo"],
+                                         inp["codebook"], None, w, rdtype=np.float64)
+    x = inp["x"][0].astype(np.float64)
+    H, D = w.heads, w.head_dim
+    o = np.zeros((w.seq, H * D))
+    for h in range(H):
+        cols = slice(h * D, (h + 1) * D)
+        proj = [[[sum(x[s, c] * inp[m][c, h * D + d] for c in range(w.width)) for d in range(D)]
+                 for s in range(w.seq)] for m in ("wq", "wk", "wv")]
+        qh, kh = brute_rope(proj[0], w.rope_base), brute_rope(proj[1], w.rope_base)
+        r = routes[0][h]
+        for name, m in (("probe_margin", 1e-9), ("sel_margin", 1e-9)):
+            assert np.all(r[name] > m)
+        assert r["addr_margin"].min() > 1e-9
+        bf = brute_routed_attention(qh, kh, proj[2], inp["codebook"][h].tolist(), None, w)
+        assert [[i for i in row if i >= 0] for row in r["sel"]] == bf["sel"]
+        o[:, cols] = np.array(bf["out"])
+    np.testing.assert_allclose(delta[0], o @ inp["wo"].astype(np.float64), rtol=0, atol=1e-11)
