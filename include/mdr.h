@@ -1,0 +1,204 @@
+/*
+ * mdr.h -- C ABI of the MI355X (gfx950) library for the forward pass of
+ * Monodratic routed sparse causal attention.
+ *
+ * The method (aitechinspire.com write-up of Monodratic, "Snapshot: key facts
+ * from the report" and "What's the core idea?"; remio.ai, "Monodratic claims
+ * learned routing can make sparse causal attention more selective", section
+ * "Monodratic turns sparse attention into a retrieval decision"):
+ *   after RoPE, source blocks get learned product addresses and are filed in
+ *   bounded causal posting lists; each query probes product addresses, reranks
+ *   the returned candidates, keeps a fixed number R of remote blocks, adds
+ *   guaranteed local blocks and runs exact causal softmax over the tokens of
+ *   those blocks.  The operator is stateless: [batch, sequence, width] in, an
+ *   attention delta out; normalisation, residuals, feed-forward layers and
+ *   scheduling belong to the host model.
+ *
+ * Conventions shared by every entry point
+ *   - Pointers are device pointers unless stated otherwise.  The caller owns
+ *     every buffer; the library allocates nothing and keeps no state between
+ *     calls.  Buffers must be 16-byte aligned and contiguous row-major.
+ *   - `stream` is a hipStream_t (NULL = the legacy default stream).  All work is
+ *     queued on it asynchronously; nothing synchronises the host.
+ *   - Arguments are validated on the host before anything is queued.  A bad
+ *     argument returns MDR_ERR_INVALID_ARG, an unsupported size or dtype
+ *     MDR_ERR_UNSUPPORTED, a short workspace MDR_ERR_WORKSPACE; in all three
+ *     cases nothing is launched.  A failed launch returns MDR_ERR_HIP.  Faults
+ *     inside a kernel surface at the caller's next synchronisation.
+ *   - Q, K, V, x, out, delta and the projection weights share one dtype
+ *     (cfg->dtype: MDR_F32 or MDR_BF16).  Router arithmetic (summaries, logits,
+ *     scores) and softmax accumulation are fp32; codebook and bias are fp32.
+ *   - Results are bitwise reproducible run to run.  Calls that share a
+ *     workspace or output buffers must not overlap in time.
+ *
+ * Routing semantics (each is a reading of the pages where they leave a step
+ * open):
+ *   summary of block i      = mean of its post-RoPE key rows
+ *   code_g(i)               = argmax_c <codebook[h,g,c,:], summary> + bias[h,g,c]
+ *                             (ties to the smaller code)
+ *   address(i)              = sum_g code_g * C^(G-1-g)        (A = C^G addresses)
+ *   eligibility             = block i is visible to query block j iff i <= j - L
+ *   posting view (a, j)     = the newest `capacity` eligible blocks filed under
+ *                             address a, newest first; overflow of (b,h) =
+ *                             sum_a max(0, n_a - capacity) over blocks i < nb - L
+ *   probes of token t       = the P addresses with the largest
+ *                             sum_g (<codebook[h,g,c_g,:], q_t> + bias[h,g,c_g]),
+ *                             ties to the smaller address
+ *   candidates              = views of the probed addresses concatenated in probe
+ *                             rank order, cut at M (max_cand; 0 means P*capacity)
+ *   selection               = top-R candidates by <q_t, summary_i> (unscaled),
+ *                             ties to the smaller block, padded with -1
+ *   attention of token t    = softmax(q_t k_s * scale) over s in the selected
+ *                             blocks and in the L most recent blocks with s <= t
+ */
+#ifndef MDR_H
+#define MDR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MDR_ABI_VERSION 1
+
+typedef enum {
+  MDR_OK = 0,
+  MDR_ERR_INVALID_ARG = 1,
+  MDR_ERR_UNSUPPORTED = 2,
+  MDR_ERR_WORKSPACE = 3,
+  MDR_ERR_HIP = 4
+} mdr_status;
+
+typedef enum { MDR_F32 = 0, MDR_BF16 = 1 } mdr_dtype;
+
+/* Sizes of one call.  nb = seq / block blocks per sequence.
+ * Supported on gfx950: head_dim in {32, 64, 128}; block in {32, 64, 128};
+ * seq % block == 0; 1 <= subspaces <= 4; codes >= 2; subspaces*codes <= 64;
+ * codes^subspaces <= 4096; 1 <= probes <= min(16, codes^subspaces);
+ * remote <= 16; local >= 1; nb <= 8192. */
+typedef struct {
+  int32_t batch;       /* B */
+  int32_t seq;         /* S, tokens per sequence */
+  int32_t heads;       /* H */
+  int32_t head_dim;    /* D */
+  int32_t width;       /* W, mixer only (0 for the core entry points) */
+  int32_t block;       /* tokens per block */
+  int32_t subspaces;   /* G, code components per product address */
+  int32_t codes;       /* C, codes per component */
+  int32_t capacity;    /* posting view capacity per address */
+  int32_t probes;      /* P, addresses probed per query token */
+  int32_t max_cand;    /* M, candidate cut (0 => probes * capacity) */
+  int32_t remote;      /* R, remote blocks kept per query token */
+  int32_t local;       /* L, local blocks including the current one */
+  int32_t dtype;       /* mdr_dtype */
+  float rope_base;     /* mixer only: RoPE base (pairs (i, i + D/2), theta_i = base^(-2i/D)) */
+  float softmax_scale; /* 0 => 1/sqrt(head_dim) */
+} mdr_config;
+
+/* Optional device outputs of the routing stages.  Any NULL member is kept in
+ * the workspace instead.  Layouts:
+ *   ksum [B,H,nb,D] fp32   addr [B,H,nb]        post_off [B,H,A+1]
+ *   post_idx [B,H,nb] (CSR entries: the blocks of address a in ascending order
+ *   at post_idx[post_off[a] .. post_off[a+1]); entries past post_off[A] are -1)
+ *   overflow [B,H]          sel [B,H,S,R] (-1 padded)   n_cand [B,H,S] */
+typedef struct {
+  float* ksum;
+  int32_t* addr;
+  int32_t* post_off;
+  int32_t* post_idx;
+  int32_t* overflow;
+  int32_t* sel;
+  int32_t* n_cand;
+} mdr_routing;
+
+/* MDR_ABI_VERSION of the built library. */
+int mdr_abi_version(void);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char* mdr_status_string(int status);
+
+/* Host-only validation of a configuration.  Returns MDR_OK, MDR_ERR_INVALID_ARG
+ * or MDR_ERR_UNSUPPORTED; touches no device. */
+mdr_status mdr_check_config(const mdr_config* cfg);
+
+/* Host-only: bytes of device workspace every entry point below needs for `cfg`
+ * (mdr_mixer_forward included when cfg->width > 0).  *bytes is set on MDR_OK. */
+mdr_status mdr_workspace_size(const mdr_config* cfg, size_t* bytes);
+
+/* The routed attention core on post-RoPE inputs (the whole path: addressing,
+ * posting lists, probe + rerank, selected-set attention).
+ *   q, k, v    [B,H,S,D] in cfg->dtype
+ *   codebook   [H,G,C,D] fp32; code_bias [H,G,C] fp32 or NULL (zero)
+ *   force      [B,H,S] int32 or NULL: a block to force into token t's selection
+ *              under the same budget R (the pages' forced-target diagnostic,
+ *              aitechinspire.com "Snapshot"; remio.ai "Why learned product-hash
+ *              routing matters now").  It is used only when 0 <= f <= j - L; it
+ *              fills a free slot or replaces the lowest-ranked one.  -1 = none.
+ *   out        [B,H,S,D] in cfg->dtype, overwritten
+ *   routing    optional outputs (may be NULL)
+ *   workspace  >= mdr_workspace_size bytes, 256-byte aligned */
+mdr_status mdr_routed_attention(const mdr_config* cfg, const void* q, const void* k, const void* v,
+                                const float* codebook, const float* code_bias, const int32_t* force,
+                                void* out, const mdr_routing* routing, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
+/* The stateless mixer, [B,S,W] -> attention delta [B,S,W] (aitechinspire.com,
+ * "Snapshot: key facts from the report"): Q = RoPE(x Wq), K = RoPE(x Wk),
+ * V = x Wv (no biases), the routed attention core per head, then
+ * delta = concat_h(O) Wo.  The host adds delta to its residual stream.
+ *   x [B,S,W]; wq, wk, wv [W, H*D]; wo [H*D, W] (all cfg->dtype, row-major)
+ *   codebook, code_bias, routing, workspace as above; delta [B,S,W] overwritten. */
+mdr_status mdr_mixer_forward(const mdr_config* cfg, const void* x, const void* wq, const void* wk,
+                             const void* wv, const void* wo, const float* codebook,
+                             const float* code_bias, void* delta, const mdr_routing* routing,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---- staged entry points: one stage each, its upstream passed in, so any
+ * stage can be fed another implementation's upstream output. ---- */
+
+/* Block summaries and product addresses (remio.ai "Monodratic turns sparse
+ * attention into a retrieval decision": a product address combines the
+ * decisions of several learned code components).
+ *   k [B,H,S,D]; codebook [H,G,C,D]; code_bias [H,G,C] or NULL;
+ *   ksum [B,H,nb,D] fp32 out; addr [B,H,nb] out. */
+mdr_status mdr_stage_address(const mdr_config* cfg, const void* k, const float* codebook,
+                             const float* code_bias, float* ksum, int32_t* addr, void* stream);
+
+/* Bounded causal posting lists as CSR plus overflow counts (aitechinspire.com
+ * "Snapshot": source blocks assigned to bounded causal posting lists; remio.ai
+ * same section: a strict capacity bounds each list, overflow drops blocks).
+ *   addr [B,H,nb] in (values must lie in [0, A)); post_off [B,H,A+1],
+ *   post_idx [B,H,nb], overflow [B,H] out. */
+mdr_status mdr_stage_post(const mdr_config* cfg, const int32_t* addr, int32_t* post_off,
+                          int32_t* post_idx, int32_t* overflow, void* stream);
+
+/* Query probe, candidate gathering and rerank to R remote blocks
+ * (aitechinspire.com "Snapshot": each query probes product addresses,
+ * reranks returned candidates and selects a fixed number of remote blocks).
+ *   q [B,H,S,D]; codebook, code_bias as above; ksum [B,H,nb,D] fp32;
+ *   post_off [B,H,A+1], post_idx [B,H,nb] (CSR as produced by
+ *   mdr_stage_post); force [B,H,S] or NULL; sel [B,H,S,R] out;
+ *   n_cand [B,H,S] out or NULL. */
+mdr_status mdr_stage_probe_rerank(const mdr_config* cfg, const void* q, const float* codebook,
+                                  const float* code_bias, const float* ksum, const int32_t* post_off,
+                                  const int32_t* post_idx, const int32_t* force, int32_t* sel,
+                                  int32_t* n_cand, void* stream);
+
+/* Exact causal softmax over the selected remote blocks plus the L local blocks
+ * (aitechinspire.com "Snapshot" and "What's the core idea?": no approximation
+ * after selection).
+ *   q, k, v [B,H,S,D]; sel [B,H,S,R] in: entry r of token t (block j) is used
+ *   when 0 <= sel <= j - L and it does not repeat an earlier entry of the same
+ *   token; other entries are ignored.  out [B,H,S,D] overwritten.
+ *   workspace >= mdr_workspace_size bytes. */
+mdr_status mdr_stage_attend(const mdr_config* cfg, const void* q, const void* k, const void* v,
+                            const int32_t* sel, void* out, void* workspace, size_t workspace_bytes,
+                            void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MDR_H */

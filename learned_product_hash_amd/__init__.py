@@ -1,0 +1,191 @@
+"""Python binding of libmdr.so, the gfx950 HIP library for the forward pass of
+Monodratic routed sparse causal attention.
+
+Argument marshalling only: every step of the path runs in the library's HIP
+kernels.  torch supplies device memory and streams; it is imported before the
+library so the library binds to the HIP runtime torch has already loaded.
+
+The functions carry the names of the C entry points declared in
+``include/mdr.h`` and raise :class:`MdrError` on any status other than MDR_OK.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # noqa: F401  (loads the HIP runtime the library must share)
+
+__all__ = [
+    "LIB_PATH", "MdrError", "MdrConfig", "MdrRouting", "MDR_F32", "MDR_BF16", "config", "lib",
+    "mdr_abi_version", "mdr_status_string", "mdr_check_config", "mdr_workspace_size",
+    "mdr_routed_attention", "mdr_mixer_forward", "mdr_stage_address", "mdr_stage_post",
+    "mdr_stage_probe_rerank", "mdr_stage_attend", "workspace", "routing_buffers",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmdr.so")
+
+MDR_OK, MDR_ERR_INVALID_ARG, MDR_ERR_UNSUPPORTED, MDR_ERR_WORKSPACE, MDR_ERR_HIP = range(5)
+MDR_F32, MDR_BF16 = 0, 1
+
+
+class MdrError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {mdr_status_string(status)} ({status})")
+
+
+class MdrConfig(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "batch", "seq", "heads", "head_dim", "width", "block", "subspaces", "codes", "capacity",
+        "probes", "max_cand", "remote", "local", "dtype")] + [
+        ("rope_base", ctypes.c_float), ("softmax_scale", ctypes.c_float)]
+
+
+class MdrRouting(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "ksum", "addr", "post_off", "post_idx", "overflow", "sel", "n_cand")]
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m learned_product_hash_amd.build`")
+    return ctypes.CDLL(LIB_PATH)
+
+
+lib = _load()
+
+_vp, _i32, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+_cfgp = ctypes.POINTER(MdrConfig)
+_rtp = ctypes.POINTER(MdrRouting)
+_SIGS = {
+    "mdr_abi_version": ([], _i32),
+    "mdr_status_string": ([_i32], ctypes.c_char_p),
+    "mdr_check_config": ([_cfgp], _i32),
+    "mdr_workspace_size": ([_cfgp, ctypes.POINTER(_sz)], _i32),
+    "mdr_routed_attention": ([_cfgp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _rtp, _vp, _sz, _vp], _i32),
+    "mdr_mixer_forward": ([_cfgp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _rtp, _vp, _sz, _vp], _i32),
+    "mdr_stage_address": ([_cfgp, _vp, _vp, _vp, _vp, _vp, _vp], _i32),
+    "mdr_stage_post": ([_cfgp, _vp, _vp, _vp, _vp, _vp], _i32),
+    "mdr_stage_probe_rerank": ([_cfgp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp], _i32),
+    "mdr_stage_attend": ([_cfgp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], _i32),
+}
+for _name, (_args, _res) in _SIGS.items():
+    _fn = getattr(lib, _name)
+    _fn.argtypes = _args
+    _fn.restype = _res
+
+
+def config(**fields) -> MdrConfig:
+    """An MdrConfig with unspecified fields zero (dtype accepts "f32"/"bf16")."""
+    f = dict(fields)
+    if isinstance(f.get("dtype"), str):
+        f["dtype"] = {"f32": MDR_F32, "bf16": MDR_BF16}[f["dtype"]]
+    return MdrConfig(**f)
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libmdr must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+
+
+def _check(status: int, where: str):
+    if status != MDR_OK:
+        raise MdrError(status, where)
+
+
+def _routing(r):
+    if r is None:
+        return None
+    if isinstance(r, MdrRouting):
+        return ctypes.byref(r)
+    rt = MdrRouting(**{k: _ptr(v) for k, v in r.items() if v is not None})
+    return ctypes.byref(rt)
+
+
+def mdr_abi_version() -> int:
+    return lib.mdr_abi_version()
+
+
+def mdr_status_string(status: int) -> str:
+    return lib.mdr_status_string(status).decode()
+
+
+def mdr_check_config(cfg: MdrConfig) -> int:
+    """Returns the status code (does not raise)."""
+    return lib.mdr_check_config(ctypes.byref(cfg))
+
+
+def mdr_workspace_size(cfg: MdrConfig) -> int:
+    n = _sz(0)
+    _check(lib.mdr_workspace_size(ctypes.byref(cfg), ctypes.byref(n)), "mdr_workspace_size")
+    return n.value
+
+
+def workspace(cfg: MdrConfig, device="cuda") -> torch.Tensor:
+    """A device buffer of mdr_workspace_size(cfg) bytes."""
+    return torch.empty(max(1, mdr_workspace_size(cfg)), dtype=torch.uint8, device=device)
+
+
+def routing_buffers(cfg: MdrConfig, device="cuda") -> dict:
+    """Device tensors for every routing output of ``cfg``."""
+    B, H, S, D = cfg.batch, cfg.heads, cfg.seq, cfg.head_dim
+    nb = S // cfg.block
+    A = cfg.codes ** cfg.subspaces
+    i32 = dict(dtype=torch.int32, device=device)
+    return dict(ksum=torch.empty(B, H, nb, D, dtype=torch.float32, device=device),
+                addr=torch.empty(B, H, nb, **i32), post_off=torch.empty(B, H, A + 1, **i32),
+                post_idx=torch.empty(B, H, nb, **i32), overflow=torch.empty(B, H, **i32),
+                sel=torch.empty(B, H, S, cfg.remote, **i32), n_cand=torch.empty(B, H, S, **i32))
+
+
+def _ws(ws):
+    return (None, 0) if ws is None else (_ptr(ws), ws.numel() * ws.element_size())
+
+
+def mdr_routed_attention(cfg, q, k, v, codebook, code_bias, force, out, routing=None, ws=None, stream=None):
+    wp, wn = _ws(ws)
+    _check(lib.mdr_routed_attention(ctypes.byref(cfg), _ptr(q), _ptr(k), _ptr(v), _ptr(codebook),
+                                    _ptr(code_bias), _ptr(force), _ptr(out), _routing(routing), wp, wn,
+                                    _stream(stream)), "mdr_routed_attention")
+
+
+def mdr_mixer_forward(cfg, x, wq, wk, wv, wo, codebook, code_bias, delta, routing=None, ws=None, stream=None):
+    wp, wn = _ws(ws)
+    _check(lib.mdr_mixer_forward(ctypes.byref(cfg), _ptr(x), _ptr(wq), _ptr(wk), _ptr(wv), _ptr(wo),
+                                 _ptr(codebook), _ptr(code_bias), _ptr(delta), _routing(routing), wp, wn,
+                                 _stream(stream)), "mdr_mixer_forward")
+
+
+def mdr_stage_address(cfg, k, codebook, code_bias, ksum, addr, stream=None):
+    _check(lib.mdr_stage_address(ctypes.byref(cfg), _ptr(k), _ptr(codebook), _ptr(code_bias), _ptr(ksum),
+                                 _ptr(addr), _stream(stream)), "mdr_stage_address")
+
+
+def mdr_stage_post(cfg, addr, post_off, post_idx, overflow, stream=None):
+    _check(lib.mdr_stage_post(ctypes.byref(cfg), _ptr(addr), _ptr(post_off), _ptr(post_idx), _ptr(overflow),
+                              _stream(stream)), "mdr_stage_post")
+
+
+def mdr_stage_probe_rerank(cfg, q, codebook, code_bias, ksum, post_off, post_idx, force, sel, n_cand=None,
+                           stream=None):
+    _check(lib.mdr_stage_probe_rerank(ctypes.byref(cfg), _ptr(q), _ptr(codebook), _ptr(code_bias), _ptr(ksum),
+                                      _ptr(post_off), _ptr(post_idx), _ptr(force), _ptr(sel), _ptr(n_cand),
+                                      _stream(stream)), "mdr_stage_probe_rerank")
+
+
+def mdr_stage_attend(cfg, q, k, v, sel, out, ws, stream=None):
+    wp, wn = _ws(ws)
+    _check(lib.mdr_stage_attend(ctypes.byref(cfg), _ptr(q), _ptr(k), _ptr(v), _ptr(sel), _ptr(out), wp, wn,
+                                _stream(stream)), "mdr_stage_attend")

@@ -1,0 +1,277 @@
+// C ABI of the routed-attention library: host-side validation, workspace planning and the
+// launch sequences.  No entry point allocates memory or keeps state between calls.
+#include <math.h>
+#include <string.h>
+
+#include "mdr_internal.h"
+
+using namespace mdr;
+
+namespace {
+
+mdr_status shape_from_config(const mdr_config* cfg, bool mixer, Shape* out) {
+  if (!cfg) return MDR_ERR_INVALID_ARG;
+  const mdr_config& c = *cfg;
+  if (c.batch < 1 || c.seq < 1 || c.heads < 1 || c.head_dim < 1 || c.block < 1 || c.subspaces < 1 ||
+      c.codes < 1 || c.capacity < 1 || c.probes < 1 || c.max_cand < 0 || c.remote < 0 || c.local < 1)
+    return MDR_ERR_INVALID_ARG;
+  if (c.seq % c.block != 0) return MDR_ERR_INVALID_ARG;
+  if (c.dtype != MDR_F32 && c.dtype != MDR_BF16) return MDR_ERR_INVALID_ARG;
+  if (!(c.softmax_scale >= 0.f) || isinf(c.softmax_scale)) return MDR_ERR_INVALID_ARG;
+  if (mixer && (c.width < 1 || !(c.rope_base > 0.f) || isinf(c.rope_base))) return MDR_ERR_INVALID_ARG;
+  if (c.head_dim != 32 && c.head_dim != 64 && c.head_dim != 128) return MDR_ERR_UNSUPPORTED;
+  if (c.block != 32 && c.block != 64 && c.block != 128) return MDR_ERR_UNSUPPORTED;
+  if (c.subspaces > kMaxSubspaces || c.subspaces * c.codes > kMaxCodesTotal) return MDR_ERR_UNSUPPORTED;
+  long long A = 1;
+  for (int g = 0; g < c.subspaces; ++g) {
+    A *= c.codes;
+    if (A > kMaxAddresses) return MDR_ERR_UNSUPPORTED;
+  }
+  if (c.probes > A) return MDR_ERR_INVALID_ARG;
+  if (c.probes > kMaxProbes || c.remote > kMaxRemote) return MDR_ERR_UNSUPPORTED;
+  const int nb = c.seq / c.block;
+  if (nb > kMaxBlocks) return MDR_ERR_UNSUPPORTED;
+  if ((long long)c.batch * c.heads > 65535) return MDR_ERR_UNSUPPORTED;
+  if (mixer && (long long)c.heads * c.head_dim > (1LL << 30)) return MDR_ERR_UNSUPPORTED;
+  Shape s;
+  memset(&s, 0, sizeof(s));
+  s.B = c.batch;
+  s.H = c.heads;
+  s.S = c.seq;
+  s.D = c.head_dim;
+  s.W = c.width;
+  s.blk = c.block;
+  s.nb = nb;
+  s.G = c.subspaces;
+  s.C = c.codes;
+  s.A = (int)A;
+  s.cap = c.capacity;
+  s.P = c.probes;
+  long long M = c.max_cand > 0 ? (long long)c.max_cand : (long long)c.probes * c.capacity;
+  s.M = (int)(M > (1LL << 30) ? (1LL << 30) : M);
+  s.R = c.remote;
+  s.L = c.local;
+  s.dtype = c.dtype;
+  s.scale = c.softmax_scale > 0.f ? c.softmax_scale : 1.0f / sqrtf((float)c.head_dim);
+  s.rope_base = c.rope_base;
+  const long long ne = nb > c.local ? nb - c.local : 0;
+  s.bins_per_bh = (long long)c.block * ne * (ne + 1) / 2;
+  // remote work items per (b,h): sum_i ceil(pairs_i / 64), bounded two ways
+  long long by_cap = 0;
+  for (long long i = 0; i < ne; ++i) by_cap += ((ne - i) * c.block + kPairsPerChunk - 1) / kPairsPerChunk;
+  long long by_pairs = ((long long)c.seq * c.remote + kPairsPerChunk - 1) / kPairsPerChunk + ne;
+  long long ch = by_cap < by_pairs ? by_cap : by_pairs;
+  if (ch > 0x7fffffffLL) return MDR_ERR_UNSUPPORTED;
+  s.chunks_per_bh = (int)ch;
+  *out = s;
+  return MDR_OK;
+}
+
+size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Workspace regions; with base == nullptr only the size is computed.
+size_t layout(const Shape& s, char* base, Buffers* b) {
+  const size_t BH = (size_t)s.B * s.H, e = s.dtype == MDR_BF16 ? 2 : 4;
+  size_t off = 0;
+  auto take = [&](size_t bytes) -> char* {
+    char* p = base ? base + off : nullptr;
+    off += align_up(bytes ? bytes : 4);
+    return p;
+  };
+  Buffers t;
+  t.ksum = (float*)take(BH * s.nb * s.D * 4);
+  t.addr = (int32_t*)take(BH * s.nb * 4);
+  t.off = (int32_t*)take(BH * (s.A + 1) * 4);
+  t.idx = (int32_t*)take(BH * s.nb * 4);
+  t.overflow = (int32_t*)take(BH * 4);
+  t.sel = (int32_t*)take(BH * s.S * s.R * 4);
+  t.ncand = (int32_t*)take(BH * s.S * 4);
+  t.cnt = (int32_t*)take(BH * s.nb * 4);
+  t.chunk_off = (int32_t*)take(BH * (s.nb + 1) * 4);
+  t.bins = (int32_t*)take(BH * (size_t)s.bins_per_bh * 4);
+  t.part_o = take(BH * s.S * s.R * s.D * e);
+  t.part_ml = (float*)take(BH * s.S * s.R * 8);
+  if (s.W > 0) {
+    const size_t qkv = BH * s.S * s.D * e;
+    t.mq = take(qkv);
+    t.mk = take(qkv);
+    t.mv = take(qkv);
+    t.mo = take(qkv);
+  } else {
+    t.mq = t.mk = t.mv = t.mo = nullptr;
+  }
+  if (b) *b = t;
+  return off;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+mdr_status hip_status(hipError_t e) { return e == hipSuccess ? MDR_OK : MDR_ERR_HIP; }
+
+#define MDR_TRY(call)                          \
+  do {                                         \
+    hipError_t e_ = (call);                    \
+    if (e_ != hipSuccess) return MDR_ERR_HIP;  \
+  } while (0)
+
+mdr_status check_workspace(const Shape& s, void* ws, size_t ws_bytes, Buffers* b) {
+  const size_t need = layout(s, nullptr, nullptr);
+  if (!ws || ((uintptr_t)ws & 255) != 0) return MDR_ERR_INVALID_ARG;
+  if (ws_bytes < need) return MDR_ERR_WORKSPACE;
+  layout(s, (char*)ws, b);
+  return MDR_OK;
+}
+
+void apply_routing(const mdr_routing* r, Buffers* b) {
+  if (!r) return;
+  if (r->ksum) b->ksum = r->ksum;
+  if (r->addr) b->addr = r->addr;
+  if (r->post_off) b->off = r->post_off;
+  if (r->post_idx) b->idx = r->post_idx;
+  if (r->overflow) b->overflow = r->overflow;
+  if (r->sel) b->sel = r->sel;
+  if (r->n_cand) b->ncand = r->n_cand;
+}
+
+bool routing_aligned(const mdr_routing* r) {
+  return !r || aligned16(r->ksum);
+}
+
+// The four stages of the core on post-RoPE q, k, v already in device memory.
+mdr_status run_core(const Shape& s, const void* q, const void* k, const void* v, const float* cb, const float* bias,
+                    const int32_t* force, void* out, const Buffers& b, hipStream_t st) {
+  const bool remote = s.R > 0 && s.nb > s.L;
+  MDR_TRY(launch_address(s, k, cb, bias, b.ksum, b.addr, remote ? b.cnt : nullptr, st));
+  MDR_TRY(launch_post(s, b.addr, b.off, b.idx, b.overflow, st));
+  MDR_TRY(launch_probe_rerank(s, q, cb, bias, b.ksum, b.off, b.idx, force, b.sel, b.ncand,
+                              remote ? b.cnt : nullptr, remote ? b.bins : nullptr, st));
+  MDR_TRY(launch_attend(s, q, k, v, b.sel, out, b, st));
+  return MDR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mdr_abi_version(void) { return MDR_ABI_VERSION; }
+
+const char* mdr_status_string(int status) {
+  switch (status) {
+    case MDR_OK: return "MDR_OK";
+    case MDR_ERR_INVALID_ARG: return "MDR_ERR_INVALID_ARG";
+    case MDR_ERR_UNSUPPORTED: return "MDR_ERR_UNSUPPORTED";
+    case MDR_ERR_WORKSPACE: return "MDR_ERR_WORKSPACE";
+    case MDR_ERR_HIP: return "MDR_ERR_HIP";
+    default: return "MDR_UNKNOWN_STATUS";
+  }
+}
+
+mdr_status mdr_check_config(const mdr_config* cfg) {
+  Shape s;
+  return shape_from_config(cfg, cfg && cfg->width > 0, &s);
+}
+
+mdr_status mdr_workspace_size(const mdr_config* cfg, size_t* bytes) {
+  if (!bytes) return MDR_ERR_INVALID_ARG;
+  Shape s;
+  const mdr_status st = shape_from_config(cfg, cfg && cfg->width > 0, &s);
+  if (st != MDR_OK) return st;
+  *bytes = layout(s, nullptr, nullptr);
+  return MDR_OK;
+}
+
+mdr_status mdr_routed_attention(const mdr_config* cfg, const void* q, const void* k, const void* v,
+                                const float* codebook, const float* code_bias, const int32_t* force, void* out,
+                                const mdr_routing* routing, void* workspace, size_t workspace_bytes, void* stream) {
+  Shape s;
+  mdr_status st = shape_from_config(cfg, false, &s);
+  if (st != MDR_OK) return st;
+  s.W = 0;
+  if (!q || !k || !v || !codebook || !out) return MDR_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(codebook) ||
+      !routing_aligned(routing))
+    return MDR_ERR_INVALID_ARG;
+  Buffers b;
+  st = check_workspace(s, workspace, workspace_bytes, &b);
+  if (st != MDR_OK) return st;
+  apply_routing(routing, &b);
+  return run_core(s, q, k, v, codebook, code_bias, force, out, b, (hipStream_t)stream);
+}
+
+mdr_status mdr_mixer_forward(const mdr_config* cfg, const void* x, const void* wq, const void* wk, const void* wv,
+                             const void* wo, const float* codebook, const float* code_bias, void* delta,
+                             const mdr_routing* routing, void* workspace, size_t workspace_bytes, void* stream) {
+  Shape s;
+  mdr_status st = shape_from_config(cfg, true, &s);
+  if (st != MDR_OK) return st;
+  if (!x || !wq || !wk || !wv || !wo || !codebook || !delta) return MDR_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(wq) || !aligned16(wk) || !aligned16(wv) || !aligned16(wo) || !aligned16(delta) ||
+      !aligned16(codebook) || !routing_aligned(routing))
+    return MDR_ERR_INVALID_ARG;
+  Buffers b;
+  st = check_workspace(s, workspace, workspace_bytes, &b);
+  if (st != MDR_OK) return st;
+  apply_routing(routing, &b);
+  hipStream_t hs = (hipStream_t)stream;
+  MDR_TRY(launch_project_heads(s, x, wq, b.mq, true, hs));
+  MDR_TRY(launch_project_heads(s, x, wk, b.mk, true, hs));
+  MDR_TRY(launch_project_heads(s, x, wv, b.mv, false, hs));
+  st = run_core(s, b.mq, b.mk, b.mv, codebook, code_bias, nullptr, b.mo, b, hs);
+  if (st != MDR_OK) return st;
+  MDR_TRY(launch_project_out(s, b.mo, wo, delta, hs));
+  return MDR_OK;
+}
+
+mdr_status mdr_stage_address(const mdr_config* cfg, const void* k, const float* codebook, const float* code_bias,
+                             float* ksum, int32_t* addr, void* stream) {
+  Shape s;
+  mdr_status st = shape_from_config(cfg, false, &s);
+  if (st != MDR_OK) return st;
+  if (!k || !codebook || !ksum || !addr) return MDR_ERR_INVALID_ARG;
+  if (!aligned16(k) || !aligned16(ksum)) return MDR_ERR_INVALID_ARG;
+  return hip_status(launch_address(s, k, codebook, code_bias, ksum, addr, nullptr, (hipStream_t)stream));
+}
+
+mdr_status mdr_stage_post(const mdr_config* cfg, const int32_t* addr, int32_t* post_off, int32_t* post_idx,
+                          int32_t* overflow, void* stream) {
+  Shape s;
+  mdr_status st = shape_from_config(cfg, false, &s);
+  if (st != MDR_OK) return st;
+  if (!addr || !post_off || !post_idx || !overflow) return MDR_ERR_INVALID_ARG;
+  return hip_status(launch_post(s, addr, post_off, post_idx, overflow, (hipStream_t)stream));
+}
+
+mdr_status mdr_stage_probe_rerank(const mdr_config* cfg, const void* q, const float* codebook,
+                                  const float* code_bias, const float* ksum, const int32_t* post_off,
+                                  const int32_t* post_idx, const int32_t* force, int32_t* sel, int32_t* n_cand,
+                                  void* stream) {
+  Shape s;
+  mdr_status st = shape_from_config(cfg, false, &s);
+  if (st != MDR_OK) return st;
+  if (!q || !codebook || !ksum || !post_off || !post_idx || (!sel && s.R > 0)) return MDR_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(ksum)) return MDR_ERR_INVALID_ARG;
+  return hip_status(launch_probe_rerank(s, q, codebook, code_bias, ksum, post_off, post_idx, force, sel, n_cand,
+                                        nullptr, nullptr, (hipStream_t)stream));
+}
+
+mdr_status mdr_stage_attend(const mdr_config* cfg, const void* q, const void* k, const void* v, const int32_t* sel,
+                            void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  Shape s;
+  mdr_status st = shape_from_config(cfg, false, &s);
+  if (st != MDR_OK) return st;
+  s.W = 0;
+  if (!q || !k || !v || !out || (!sel && s.R > 0)) return MDR_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return MDR_ERR_INVALID_ARG;
+  Buffers b;
+  st = check_workspace(s, workspace, workspace_bytes, &b);
+  if (st != MDR_OK) return st;
+  hipStream_t hs = (hipStream_t)stream;
+  if (s.R > 0 && s.nb > s.L) {
+    MDR_TRY(launch_fill(b.cnt, (long long)s.B * s.H * s.nb, 0, hs));
+    MDR_TRY(launch_pair_bin(s, sel, b.cnt, b.bins, hs));
+  }
+  MDR_TRY(launch_attend(s, q, k, v, sel, out, b, hs));
+  return MDR_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,470 @@
+// Selected-set attention of Monodratic routed sparse causal attention on gfx950.
+//
+// The method runs exact causal softmax over the tokens of the selected remote blocks and the
+// guaranteed local blocks, with no approximation after selection (aitechinspire.com write-up,
+// "Snapshot: key facts from the report" and "What's the core idea?"; remio.ai, "Monodratic
+// claims learned routing can make sparse causal attention more selective", section "Monodratic
+// turns sparse attention into a retrieval decision").  Selecting whole blocks keeps data
+// movement regular (same article, section "Why learned product-hash routing matters now").
+//
+// Routing is per query token, so the remote blocks of neighbouring tokens differ.  Reading
+// each token's remote blocks separately would move every block many times, so the remote part
+// is regrouped by block:
+//   k_pair_bin     (token, slot) pairs appended to the bin of their selected block
+//   k_pair_plan    per (b,h): exclusive scan of ceil(pairs / 64) over the blocks
+//   k_attn_remote  one work-group per 64 pairs of one block: the block's K/V is staged in LDS
+//                  once, the pairs' queries are gathered, S^T = K Q^T and O^T = V^T P^T run on
+//                  MFMA, and each pair's softmax partial (max, sum, normalised output) is stored
+//   k_attn_local   one work-group per query block: the L local blocks through LDS on MFMA with
+//                  the causal mask on the diagonal block and an online softmax, then the
+//                  remote partials of each token are merged in slot order and O is written.
+//
+// MFMA lane layouts (gfx950, 64 lanes): for v_mfma_f32_16x16x32_bf16 lane l supplies
+// A[l%16][8(l/16)+e] and B[8(l/16)+e][l%16], e = 0..7, and receives C[4(l/16)+k][l%16],
+// k = 0..3; for v_mfma_f32_16x16x4_f32 lane l supplies A[l%16][l/16] and B[l/16][l%16].
+// Scores are computed transposed (keys as rows, queries as columns) so each lane keeps one
+// query (l%16) through the softmax and the PV product.
+#include "mdr_internal.h"
+
+#include <math.h>
+
+#include <type_traits>
+
+namespace mdr {
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+template <typename T, int D, int BLK>
+struct Tile {
+  static constexpr bool bf = std::is_same<T, bf16>::value;
+  static constexpr int KST = bf ? D + 8 : D + 4;     // K rows in LDS (elements)
+  static constexpr int VST = bf ? BLK + 8 : D + 4;   // bf16: V^T rows [D][VST]; f32: V rows [BLK][VST]
+  static constexpr int K_ELEMS = BLK * KST;
+  static constexpr int V_ELEMS = bf ? D * VST : BLK * VST;
+  static constexpr int NQF = bf ? D / 32 : D / 4;    // query operand registers
+  static constexpr int NT = BLK / 16;                // 16-key sub-tiles
+  static constexpr int ND = D / 16;                  // 16-wide d tiles
+  static constexpr int VEC = 16 / sizeof(T);
+  static constexpr size_t LDS_BYTES = (size_t)(K_ELEMS + V_ELEMS) * sizeof(T);
+};
+
+template <typename T, int D>
+struct QFrag;
+template <int D>
+struct QFrag<bf16, D> {
+  bf16x8 v[D / 32];
+};
+template <int D>
+struct QFrag<float, D> {
+  float v[D / 4];
+};
+
+// Query operand of S^T = K Q^T for the query row qp (lane's query is l%16).
+template <typename T, int D>
+__device__ inline void load_q(QFrag<T, D>& qf, const T* qp, int lane) {
+  const int s = lane >> 4;
+  if constexpr (std::is_same<T, bf16>::value) {
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk) qf.v[kk] = *(const bf16x8*)(qp + 32 * kk + 8 * s);
+  } else {
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) {
+      const float4 v = *(const float4*)(qp + s * (D / 4) + 4 * c);
+      qf.v[4 * c + 0] = v.x;
+      qf.v[4 * c + 1] = v.y;
+      qf.v[4 * c + 2] = v.z;
+      qf.v[4 * c + 3] = v.w;
+    }
+  }
+}
+
+// Stage one block of K (row-major) and V (transposed for bf16) into LDS.
+template <typename T, int D, int BLK, int NTHR>
+__device__ inline void load_kv(const T* __restrict__ Kg, const T* __restrict__ Vg, T* Ks, T* Vx, int tid) {
+  using TL = Tile<T, D, BLK>;
+  constexpr int NCH = D / TL::VEC;
+  constexpr int TOTAL = BLK * NCH;
+#pragma unroll
+  for (int c = tid; c < TOTAL; c += NTHR) {
+    const int row = c / NCH, ch = c % NCH;
+    const uint4 kv = *(const uint4*)(Kg + (size_t)row * D + ch * TL::VEC);
+    *(uint4*)(Ks + row * TL::KST + ch * TL::VEC) = kv;
+    const uint4 vv = *(const uint4*)(Vg + (size_t)row * D + ch * TL::VEC);
+    if constexpr (TL::bf) {
+      const bf16* ve = (const bf16*)&vv;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) Vx[(ch * 8 + e) * TL::VST + row] = ve[e];
+    } else {
+      *(uint4*)(Vx + row * TL::VST + ch * TL::VEC) = vv;
+    }
+  }
+}
+
+// S^T tile n (keys 16n..16n+15 as rows, the wave's 16 queries as columns).
+template <typename T, int D, int BLK>
+__device__ inline f32x4 score_tile(const QFrag<T, D>& qf, const T* Ks, int n, int lane) {
+  using TL = Tile<T, D, BLK>;
+  const int s = lane >> 4, r = lane & 15;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (TL::bf) {
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk) {
+      const bf16x8 a = *(const bf16x8*)(Ks + (16 * n + r) * TL::KST + 32 * kk + 8 * s);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf.v[kk], acc, 0, 0, 0);
+    }
+  } else {
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) {
+      const float4 a = *(const float4*)(Ks + (16 * n + r) * TL::KST + s * (D / 4) + 4 * c);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.x, qf.v[4 * c + 0], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.y, qf.v[4 * c + 1], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.z, qf.v[4 * c + 2], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.w, qf.v[4 * c + 3], acc, 0, 0, 0);
+    }
+  }
+  return acc;
+}
+
+// O^T += V^T P^T over one block; p[n][k] = P^T[16n + 4(l/16) + k][l%16].
+template <typename T, int D, int BLK>
+__device__ inline void pv_block(f32x4 (&o)[D / 16], const f32x4 (&p)[BLK / 16], const T* Vx, int lane) {
+  using TL = Tile<T, D, BLK>;
+  const int s = lane >> 4, r = lane & 15;
+  if constexpr (TL::bf) {
+#pragma unroll
+    for (int pp = 0; pp < BLK / 32; ++pp) {
+      bf16x8 b;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        b[k] = (bf16)p[2 * pp][k];
+        b[4 + k] = (bf16)p[2 * pp + 1][k];
+      }
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) {
+        const bf16* vr = Vx + (16 * dt + r) * TL::VST + 32 * pp + 4 * s;
+        const bf16x4 lo = *(const bf16x4*)vr;
+        const bf16x4 hi = *(const bf16x4*)(vr + 16);
+        const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, o[dt], 0, 0, 0);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int n = 0; n < BLK / 16; ++n) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) {
+          const float a = Vx[(16 * n + 4 * s + k) * TL::VST + 16 * dt + r];
+          o[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, p[n][k], o[dt], 0, 0, 0);
+        }
+      }
+    }
+  }
+}
+
+__device__ inline float wave_max16(float x) {
+  x = fmaxf(x, __shfl_xor(x, 16));
+  return fmaxf(x, __shfl_xor(x, 32));
+}
+__device__ inline float wave_sum16(float x) {
+  x += __shfl_xor(x, 16);
+  return x + __shfl_xor(x, 32);
+}
+
+template <typename T>
+__device__ inline void store4(T* dst, const f32x4& v, float mul) {
+  if constexpr (std::is_same<T, bf16>::value) {
+    const bf16x4 b = {(bf16)(v[0] * mul), (bf16)(v[1] * mul), (bf16)(v[2] * mul), (bf16)(v[3] * mul)};
+    *(bf16x4*)dst = b;
+  } else {
+    *(float4*)dst = make_float4(v[0] * mul, v[1] * mul, v[2] * mul, v[3] * mul);
+  }
+}
+
+template <typename T>
+__device__ inline f32x4 load4(const T* src) {
+  if constexpr (std::is_same<T, bf16>::value) {
+    const bf16x4 b = *(const bf16x4*)src;
+    return f32x4{(float)b[0], (float)b[1], (float)b[2], (float)b[3]};
+  } else {
+    const float4 v = *(const float4*)src;
+    return f32x4{v.x, v.y, v.z, v.w};
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_fill(int32_t* p, long long n, int32_t value) {
+  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long long)gridDim.x * 256) p[i] = value;
+}
+
+__global__ __launch_bounds__(256) void k_pair_bin(const int32_t* __restrict__ sel, int32_t* __restrict__ cnt,
+                                                  int32_t* __restrict__ bins, Shape s) {
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  const int bh = blockIdx.y;
+  if (t >= s.S) return;
+  const int j = t / s.blk;
+  const int32_t* row = sel + ((size_t)bh * s.S + t) * s.R;
+  for (int r = 0; r < s.R; ++r) {
+    if (!sel_entry_valid(row, r, j, s.L)) continue;
+    const int i = row[r];
+    const int pos = atomicAdd(&cnt[(size_t)bh * s.nb + i], 1);
+    if (pos < (s.nb - s.L - i) * s.blk)
+      bins[(size_t)bh * s.bins_per_bh + bin_offset(i, s.nb, s.L, s.blk) + pos] = t * s.R + r;
+  }
+}
+
+__global__ __launch_bounds__(256) void k_pair_plan(const int32_t* __restrict__ cnt, int32_t* __restrict__ chunk_off,
+                                                   Shape s) {
+  __shared__ int part[256];
+  const int tid = threadIdx.x, bh = blockIdx.x;
+  const int nb = s.nb;
+  const int seg = (nb + 255) / 256;
+  const int i0 = min(nb, tid * seg), i1 = min(nb, i0 + seg);
+  const int32_t* c = cnt + (size_t)bh * nb;
+  int sum = 0;
+  for (int i = i0; i < i1; ++i) sum += (c[i] + kPairsPerChunk - 1) / kPairsPerChunk;
+  part[tid] = sum;
+  __syncthreads();
+  if (tid == 0) {
+    int run = 0;
+    for (int w = 0; w < 256; ++w) {
+      const int v = part[w];
+      part[w] = run;
+      run += v;
+    }
+    chunk_off[(size_t)bh * (nb + 1) + nb] = run;
+  }
+  __syncthreads();
+  int run = part[tid];
+  for (int i = i0; i < i1; ++i) {
+    chunk_off[(size_t)bh * (nb + 1) + i] = run;
+    run += (c[i] + kPairsPerChunk - 1) / kPairsPerChunk;
+  }
+}
+
+// One work-group = up to 64 (token, slot) pairs that selected the same block.
+template <typename T, int D, int BLK>
+__global__ __launch_bounds__(256) void k_attn_remote(const T* __restrict__ Q, const T* __restrict__ K,
+                                                     const T* __restrict__ V, const int32_t* __restrict__ cnt,
+                                                     const int32_t* __restrict__ chunk_off,
+                                                     const int32_t* __restrict__ bins, T* __restrict__ part_o,
+                                                     float* __restrict__ part_ml, Shape s) {
+  using TL = Tile<T, D, BLK>;
+  extern __shared__ __align__(16) char lds_raw[];
+  T* Ks = (T*)lds_raw;
+  T* Vx = Ks + TL::K_ELEMS;
+  const int x = blockIdx.x, bh = blockIdx.y;
+  const int32_t* co = chunk_off + (size_t)bh * (s.nb + 1);
+  if (x >= co[s.nb]) return;  // uniform for the work-group, before any barrier
+  int lo = 0, hi = s.nb - 1;  // the block whose chunk range holds x
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (co[mid] <= x)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  const int i = lo;
+  const int p0 = (x - co[i]) * kPairsPerChunk;
+  const int npairs = min(kPairsPerChunk, cnt[(size_t)bh * s.nb + i] - p0);
+  const int32_t* bp = bins + (size_t)bh * s.bins_per_bh + bin_offset(i, s.nb, s.L, s.blk) + p0;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const size_t rowbase = (size_t)bh * s.S;
+  load_kv<T, D, BLK, 256>(K + (rowbase + (size_t)i * BLK) * D, V + (rowbase + (size_t)i * BLK) * D, Ks, Vx, tid);
+  const int slot = wave * 16 + (lane & 15);
+  const bool valid = slot < npairs;
+  const int pv = valid ? bp[slot] : 0;
+  const int t = pv / s.R, r = pv % s.R;
+  QFrag<T, D> qf;
+  load_q<T, D>(qf, Q + (rowbase + t) * D, lane);
+  __syncthreads();
+  const float c = s.scale * kLog2e;
+  f32x4 p[TL::NT];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int n = 0; n < TL::NT; ++n) {
+    p[n] = score_tile<T, D, BLK>(qf, Ks, n, lane);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      p[n][k] *= c;
+      mx = fmaxf(mx, p[n][k]);
+    }
+  }
+  mx = wave_max16(mx);
+  float sum = 0.f;
+#pragma unroll
+  for (int n = 0; n < TL::NT; ++n)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      p[n][k] = exp2f(p[n][k] - mx);
+      sum += p[n][k];
+    }
+  sum = wave_sum16(sum);
+  f32x4 o[TL::ND];
+#pragma unroll
+  for (int dt = 0; dt < TL::ND; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  pv_block<T, D, BLK>(o, p, Vx, lane);
+  if (valid) {
+    const size_t pr = (rowbase + t) * s.R + r;
+    const float inv = 1.f / sum;
+#pragma unroll
+    for (int dt = 0; dt < TL::ND; ++dt) store4<T>(part_o + pr * D + 16 * dt + 4 * (lane >> 4), o[dt], inv);
+    if ((lane >> 4) == 0) *(float2*)(part_ml + 2 * pr) = make_float2(mx, sum);
+  }
+}
+
+// One work-group per query block: local blocks + merge of the remote partials.
+template <typename T, int D, int BLK>
+__global__ __launch_bounds__(BLK * 4) void k_attn_local(const T* __restrict__ Q, const T* __restrict__ K,
+                                                        const T* __restrict__ V, const int32_t* __restrict__ sel,
+                                                        const T* __restrict__ part_o,
+                                                        const float* __restrict__ part_ml, T* __restrict__ out,
+                                                        Shape s) {
+  using TL = Tile<T, D, BLK>;
+  constexpr int NTHR = BLK * 4;
+  extern __shared__ __align__(16) char lds_raw[];
+  T* Ks = (T*)lds_raw;
+  T* Vx = Ks + TL::K_ELEMS;
+  const int j = blockIdx.x, bh = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int qi = wave * 16 + (lane & 15);
+  const int t = j * BLK + qi;
+  const size_t rowbase = (size_t)bh * s.S;
+  QFrag<T, D> qf;
+  load_q<T, D>(qf, Q + (rowbase + t) * D, lane);
+  const float c = s.scale * kLog2e;
+  float m = -INFINITY, l = 0.f;
+  f32x4 o[TL::ND];
+#pragma unroll
+  for (int dt = 0; dt < TL::ND; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int j0 = max(0, j - s.L + 1);
+  for (int jj = j0; jj <= j; ++jj) {
+    if (jj != j0) __syncthreads();
+    load_kv<T, D, BLK, NTHR>(K + (rowbase + (size_t)jj * BLK) * D, V + (rowbase + (size_t)jj * BLK) * D, Ks, Vx,
+                             tid);
+    __syncthreads();
+    f32x4 p[TL::NT];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int n = 0; n < TL::NT; ++n) {
+      p[n] = score_tile<T, D, BLK>(qf, Ks, n, lane);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        float v = p[n][k] * c;
+        if (jj == j && 16 * n + 4 * (lane >> 4) + k > qi) v = -INFINITY;
+        p[n][k] = v;
+        mx = fmaxf(mx, v);
+      }
+    }
+    mx = wave_max16(mx);
+    const float mnew = fmaxf(m, mx);
+    const float alpha = exp2f(m - mnew);
+    float sum = 0.f;
+#pragma unroll
+    for (int n = 0; n < TL::NT; ++n)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        p[n][k] = exp2f(p[n][k] - mnew);
+        sum += p[n][k];
+      }
+    sum = wave_sum16(sum);
+    l = l * alpha + sum;
+    m = mnew;
+#pragma unroll
+    for (int dt = 0; dt < TL::ND; ++dt) o[dt] *= alpha;
+    pv_block<T, D, BLK>(o, p, Vx, lane);
+  }
+  // merge remote partials in slot order
+  const int32_t* row = sel + (rowbase + t) * s.R;
+  for (int r = 0; r < s.R; ++r) {
+    if (!sel_entry_valid(row, r, j, s.L)) continue;
+    const size_t pr = (rowbase + t) * s.R + r;
+    const float2 ml = *(const float2*)(part_ml + 2 * pr);
+    const float mnew = fmaxf(m, ml.x);
+    const float a = exp2f(m - mnew);
+    const float b = exp2f(ml.x - mnew) * ml.y;
+#pragma unroll
+    for (int dt = 0; dt < TL::ND; ++dt) {
+      const f32x4 po = load4<T>(part_o + pr * D + 16 * dt + 4 * (lane >> 4));
+      o[dt] = o[dt] * a + po * b;
+    }
+    l = l * a + b;
+    m = mnew;
+  }
+  const float inv = 1.f / l;
+#pragma unroll
+  for (int dt = 0; dt < TL::ND; ++dt) store4<T>(out + (rowbase + t) * D + 16 * dt + 4 * (lane >> 4), o[dt], inv);
+}
+
+template <typename T, int D, int BLK>
+hipError_t attend_impl(const Shape& s, const void* q, const void* k, const void* v, const int32_t* sel, void* out,
+                       const Buffers& b, hipStream_t st) {
+  using TL = Tile<T, D, BLK>;
+  const size_t lds = TL::LDS_BYTES;
+  const bool remote = s.R > 0 && s.nb > s.L;
+  if (remote) {
+    hipLaunchKernelGGL(k_pair_plan, dim3(s.B * s.H), dim3(256), 0, st, b.cnt, b.chunk_off, s);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (lds > 65536) hipFuncSetAttribute((const void*)k_attn_remote<T, D, BLK>,
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    hipLaunchKernelGGL((k_attn_remote<T, D, BLK>), dim3(s.chunks_per_bh, s.B * s.H), dim3(256), lds, st,
+                       (const T*)q, (const T*)k, (const T*)v, b.cnt, b.chunk_off, b.bins, (T*)b.part_o, b.part_ml,
+                       s);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (lds > 65536) hipFuncSetAttribute((const void*)k_attn_local<T, D, BLK>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  hipLaunchKernelGGL((k_attn_local<T, D, BLK>), dim3(s.nb, s.B * s.H), dim3(BLK * 4), lds, st, (const T*)q,
+                     (const T*)k, (const T*)v, sel, (const T*)b.part_o, b.part_ml, (T*)out, s);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t attend_blk(const Shape& s, const void* q, const void* k, const void* v, const int32_t* sel, void* out,
+                      const Buffers& b, hipStream_t st) {
+  switch (s.blk) {
+    case 32: return attend_impl<T, D, 32>(s, q, k, v, sel, out, b, st);
+    case 64: return attend_impl<T, D, 64>(s, q, k, v, sel, out, b, st);
+    case 128: return attend_impl<T, D, 128>(s, q, k, v, sel, out, b, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <typename T>
+hipError_t attend_d(const Shape& s, const void* q, const void* k, const void* v, const int32_t* sel, void* out,
+                    const Buffers& b, hipStream_t st) {
+  switch (s.D) {
+    case 32: return attend_blk<T, 32>(s, q, k, v, sel, out, b, st);
+    case 64: return attend_blk<T, 64>(s, q, k, v, sel, out, b, st);
+    case 128: return attend_blk<T, 128>(s, q, k, v, sel, out, b, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_fill(int32_t* p, long long n, int32_t value, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  long long blocks = (n + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(k_fill, dim3((unsigned)blocks), dim3(256), 0, st, p, n, value);
+  return hipGetLastError();
+}
+
+hipError_t launch_pair_bin(const Shape& s, const int32_t* sel, int32_t* cnt, int32_t* bins, hipStream_t st) {
+  hipLaunchKernelGGL(k_pair_bin, dim3((s.S + 255) / 256, s.B * s.H), dim3(256), 0, st, sel, cnt, bins, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_attend(const Shape& s, const void* q, const void* k, const void* v, const int32_t* sel, void* out,
+                         const Buffers& b, hipStream_t st) {
+  if (s.dtype == MDR_BF16) return attend_d<bf16>(s, q, k, v, sel, out, b, st);
+  return attend_d<float>(s, q, k, v, sel, out, b, st);
+}
+
+}  // namespace mdr

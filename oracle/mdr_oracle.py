@@ -166,26 +166,35 @@ def address_scores(mu: np.ndarray, n_codes: int) -> np.ndarray:
 
 
 def top_probes(sigma: np.ndarray, probes: int):
-    """Top-P addresses by score, ties to the smaller address; and the P-th minus (P+1)-th score."""
+    """Top-P addresses by score, ties to the smaller address.
+
+    Also returns the decision margin: the smallest gap between consecutive scores
+    among the best min(P + 1, A) (rank order matters downstream, not only the
+    boundary between the P-th and the (P+1)-th address)."""
     order = np.argsort(-sigma, axis=-1, kind="stable")
     top = order[..., :probes]
     A = sigma.shape[-1]
-    if probes < A:
-        s = np.take_along_axis(sigma, order[..., probes - 1:probes + 1], axis=-1).astype(np.float64)
-        margin = s[..., 0] - s[..., 1]
+    n = min(probes + 1, A)
+    if n >= 2:
+        s = np.take_along_axis(sigma, order[..., :n], axis=-1).astype(np.float64)
+        margin = (s[..., :-1] - s[..., 1:]).min(axis=-1)
     else:
         margin = np.full(sigma.shape[:-1], INF)
     return top, margin
 
 
 def rerank(q_t: np.ndarray, ksum: np.ndarray, cands: list, remote: int, rdtype=np.float32):
-    """Top-R candidates by <q_t, summary>, ties to the smaller block; (selected, margin)."""
+    """Top-R candidates by <q_t, summary>, ties to the smaller block; (selected, margin).
+
+    The margin is the smallest gap between consecutive scores among the best
+    min(R + 1, n) candidates (the selection is stored in rank order)."""
     if not cands or remote == 0:
         return [], INF
     rho = np.asarray(ksum[cands], dtype=rdtype) @ np.asarray(q_t, dtype=rdtype)
     order = sorted(range(len(cands)), key=lambda n: (-float(rho[n]), cands[n]))
     sel = [cands[n] for n in order[:remote]]
-    margin = float(rho[order[remote - 1]]) - float(rho[order[remote]]) if len(cands) > remote else INF
+    top = [float(rho[n]) for n in order[:remote + 1]]
+    margin = min((a - b for a, b in zip(top[:-1], top[1:])), default=INF)
     return sel, margin
 
 

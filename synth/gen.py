@@ -105,11 +105,17 @@ def workload(name: str, **over) -> Workload:
 
 def bf16_round(x: np.ndarray) -> np.ndarray:
     """Round float32 values to the nearest bf16 value (ties to even); returns float32."""
-    x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    lsb = (u >> 16) & 1
-    u = ((u + 0x7FFF + lsb) & 0xFFFF0000).astype(np.uint32)
-    return u.view(np.float32).reshape(x.shape)
+    x = np.array(x, dtype=np.float32, copy=True, order="C")
+    u = x.view(np.uint32)
+    flat = u.reshape(-1)
+    step = 1 << 24
+    for s in range(0, flat.size, step):  # chunked to bound temporaries; finite inputs cannot overflow
+        c = flat[s:s + step]
+        lsb = (c >> 16) & 1
+        c += np.uint32(0x7FFF)
+        c += lsb
+        c &= np.uint32(0xFFFF0000)
+    return x
 
 
 def _normal(rng, shape, std=1.0):

@@ -1,0 +1,121 @@
+"""The C-ABI library on the host (no GPU needed): it loads, exports every function
+include/mdr.h declares, and rejects bad arguments before anything is launched."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mdr.h")
+LIB = os.path.join(ROOT, "learned_product_hash_amd", "libmdr.so")
+
+
+def _ensure_built():
+    if not os.path.exists(LIB):
+        from learned_product_hash_amd.build import build
+
+        build()
+
+
+@pytest.fixture(scope="module")
+def mdr():
+    _ensure_built()
+    import learned_product_hash_amd as m
+
+    return m
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mdr_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("mdr_routed_attention", "mdr_mixer_forward", "mdr_stage_address", "mdr_stage_post",
+              "mdr_stage_probe_rerank", "mdr_stage_attend", "mdr_workspace_size", "mdr_check_config"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(mdr):
+    lib = ctypes.CDLL(LIB)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert mdr.mdr_abi_version() == 1
+
+
+def _good(**over):
+    f = dict(batch=1, seq=4096, heads=8, head_dim=64, block=64, subspaces=2, codes=16, capacity=2, probes=4,
+             remote=2, local=2, dtype="bf16")
+    f.update(over)
+    return f
+
+
+def test_valid_configs_pass(mdr):
+    assert mdr.mdr_check_config(mdr.config(**_good())) == 0
+    for w in ("tiny", "recall", "sweep", "long", "skew"):
+        import synth
+
+        wl = synth.workload(w)
+        c = mdr.config(batch=wl.batch, seq=wl.seq, heads=wl.heads, head_dim=wl.head_dim, width=wl.width,
+                       block=wl.block, subspaces=wl.subspaces, codes=wl.codes, capacity=wl.capacity,
+                       probes=wl.probes, max_cand=wl.max_cand, remote=wl.remote, local=wl.local,
+                       dtype=wl.dtype, rope_base=wl.rope_base)
+        assert mdr.mdr_check_config(c) == 0, w
+        assert mdr.mdr_workspace_size(c) > 0
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(seq=4000), 1),            # seq % block != 0
+    (dict(batch=0), 1),
+    (dict(local=0), 1),
+    (dict(capacity=0), 1),
+    (dict(probes=0), 1),
+    (dict(remote=-1), 1),
+    (dict(dtype=7), 1),
+    (dict(probes=300, codes=16), 1),  # more probes than addresses (A = 256)
+    (dict(head_dim=48), 2),
+    (dict(block=16), 2),
+    (dict(remote=17), 2),
+    (dict(probes=17), 2),
+    (dict(subspaces=5, codes=2), 2),
+    (dict(codes=128), 2),           # 2 x 128 codes exceed the 64 logits per query
+    (dict(subspaces=4, codes=16), 2),  # 65536 addresses
+    (dict(seq=64 * 9000), 2),       # more than 8192 blocks
+])
+def test_invalid_configs_are_rejected_on_the_host(mdr, over, status):
+    cfg = mdr.config(**_good(**over))
+    assert mdr.mdr_check_config(cfg) == status
+    with pytest.raises(mdr.MdrError) as e:
+        mdr.mdr_workspace_size(cfg)
+    assert e.value.status == status
+
+
+def test_entry_points_validate_before_launching(mdr):
+    """Null pointers, misalignment and short workspaces return a status; no device is touched."""
+    lib = mdr.lib
+    cfg = mdr.config(**_good())
+    need = mdr.mdr_workspace_size(cfg)
+    p = 1 << 20  # a fake, 256-byte aligned address: never dereferenced on these paths
+    c = ctypes.byref(cfg)
+    assert lib.mdr_routed_attention(c, None, p, p, p, None, None, p, None, p, need, None) == 1
+    assert lib.mdr_routed_attention(c, p + 2, p, p, p, None, None, p, None, p, need, None) == 1
+    assert lib.mdr_routed_attention(c, p, p, p, p, None, None, p, None, p, need - 1, None) == 3
+    assert lib.mdr_routed_attention(c, p, p, p, p, None, None, p, None, p + 16, need, None) == 1
+    assert lib.mdr_stage_attend(c, p, p, p, p, p, p, need - 1, None) == 3
+    assert lib.mdr_stage_attend(c, p, p, p, None, p, p, need, None) == 1
+    assert lib.mdr_stage_post(c, None, p, p, p, None) == 1
+    assert lib.mdr_stage_address(c, p, p, None, p + 4, p, None) == 1
+    assert lib.mdr_stage_probe_rerank(c, p, p, None, p, p, p, None, None, None, None) == 1
+    mix = mdr.config(**_good(width=0))
+    assert lib.mdr_mixer_forward(ctypes.byref(mix), p, p, p, p, p, p, None, p, None, p, 1 << 40, None) == 1
+    assert mdr.mdr_status_string(3) == "MDR_ERR_WORKSPACE"
+
+
+def test_workspace_grows_with_the_mixer_buffers(mdr):
+    core = mdr.mdr_workspace_size(mdr.config(**_good()))
+    mixer = mdr.mdr_workspace_size(mdr.config(**_good(width=512, rope_base=10000.0)))
+    assert mixer > core

@@ -1,0 +1,298 @@
+"""Parity of the HIP path with the CPU oracle on the GPU (through the C ABI).
+
+Routing indices must match exactly wherever the oracle's decision margin
+exceeds 1e-4 (near-ties are counted); attention must match within 1e-5
+absolute in fp32 and 2e-2 in bf16.  Each stage is also run on the oracle's
+own upstream output, so a near-tie upstream cannot cascade into a failure.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tests._gpu import (NEAR, TOL, attention_rows, cfg_of, compare_addresses, compare_selection, dev, host,
+                        io_dtype, run_core, small)
+
+pytestmark = pytest.mark.gpu
+
+NAMES = ["tiny", "recall", "sweep", "long", "skew"]
+
+
+@pytest.mark.parametrize("name", NAMES)
+def test_stage_address(gpu_lib, name):
+    mdr = gpu_lib
+    w = small(name)
+    inp = synth.make_core_inputs(w, 0)
+    cfg = cfg_of(mdr, w)
+    k = dev(inp["k"], io_dtype(w))
+    ksum = torch.empty(w.batch, w.heads, w.nblocks, w.head_dim, dtype=torch.float32, device="cuda")
+    addr = torch.empty(w.batch, w.heads, w.nblocks, dtype=torch.int32, device="cuda")
+    bias = None if inp["bias"] is None else dev(inp["bias"], torch.float32)
+    mdr.mdr_stage_address(cfg, k, dev(inp["codebook"], torch.float32), bias, ksum, addr)
+    torch.cuda.synchronize()
+    ksum, addr = host(ksum), host(addr)
+    near = 0
+    for b in range(w.batch):
+        for h in range(w.heads):
+            ks = oracle.block_summaries(inp["k"][b, h], w.block)
+            np.testing.assert_allclose(ksum[b, h], ks, rtol=1e-5, atol=1e-6)
+            near += compare_addresses(w, inp, addr[b, h], b, h)
+    print(f"{name}: address near-ties {near}")
+
+
+@pytest.mark.parametrize("nb,G,C,L,cap,skew", [(16, 2, 4, 2, 8, 0.0), (512, 2, 16, 2, 4, 0.0),
+                                               (64, 3, 8, 2, 8, 2.0), (1024, 2, 32, 2, 16, 1.5),
+                                               (3, 2, 4, 2, 1, 0.0), (2, 1, 4, 2, 1, 0.0), (100, 1, 7, 1, 3, 1.0),
+                                               (8192, 3, 16, 3, 2, 0.5)])
+def test_stage_post(gpu_lib, nb, G, C, L, cap, skew):
+    """CSR and overflow from arbitrary address arrays must equal the oracle's exactly."""
+    mdr = gpu_lib
+    A = C ** G
+    rng = np.random.default_rng(nb + A)
+    BH = 3
+    p = 1.0 / np.arange(1, A + 1) ** skew
+    addr = rng.choice(A, size=(1, BH, nb), p=p / p.sum()).astype(np.int32)
+    cfg = mdr.config(batch=1, seq=nb * 32, heads=BH, head_dim=32, block=32, subspaces=G, codes=C, capacity=cap,
+                     probes=1, remote=1, local=L, dtype="f32")
+    assert mdr.mdr_check_config(cfg) == 0
+    off = torch.empty(1, BH, A + 1, dtype=torch.int32, device="cuda")
+    idx = torch.empty(1, BH, nb, dtype=torch.int32, device="cuda")
+    ovf = torch.empty(1, BH, dtype=torch.int32, device="cuda")
+    mdr.mdr_stage_post(cfg, dev(addr), off, idx, ovf)
+    torch.cuda.synchronize()
+    off, idx, ovf = host(off), host(idx), host(ovf)
+    for h in range(BH):
+        lists = oracle.posting_lists(addr[0, h], A, L)
+        o_off, o_idx = oracle.posting_csr(lists)
+        assert np.array_equal(off[0, h], o_off)
+        assert np.array_equal(idx[0, h, :len(o_idx)], o_idx)
+        assert np.all(idx[0, h, len(o_idx):] == -1)
+        assert ovf[0, h] == oracle.posting_overflow(lists, cap)
+
+
+@pytest.mark.parametrize("name", NAMES)
+def test_stage_probe_rerank_on_oracle_index(gpu_lib, name):
+    mdr = gpu_lib
+    w = small(name)
+    inp = synth.make_core_inputs(w, 1)
+    force = inp.get("force")
+    cfg = cfg_of(mdr, w)
+    B, H, S, nb = w.batch, w.heads, w.seq, w.nblocks
+    routes = [[oracle.route_head(inp["q"][b, h], inp["k"][b, h], inp["codebook"][h],
+                                 None if inp["bias"] is None else inp["bias"][h], w,
+                                 None if force is None else force[b, h]) for h in range(H)] for b in range(B)]
+    ksum = np.stack([np.stack([r["ksum"] for r in rb]) for rb in routes]).astype(np.float32)
+    off = np.stack([np.stack([r["off"] for r in rb]) for rb in routes]).astype(np.int32)
+    idx = np.full((B, H, nb), -1, dtype=np.int32)
+    for b in range(B):
+        for h in range(H):
+            idx[b, h, :len(routes[b][h]["idx"])] = routes[b][h]["idx"]
+    sel = torch.empty(B, H, S, w.remote, dtype=torch.int32, device="cuda")
+    ncand = torch.empty(B, H, S, dtype=torch.int32, device="cuda")
+    bias = None if inp["bias"] is None else dev(inp["bias"], torch.float32)
+    mdr.mdr_stage_probe_rerank(cfg, dev(inp["q"], io_dtype(w)), dev(inp["codebook"], torch.float32), bias,
+                               dev(ksum), dev(off), dev(idx), None if force is None else dev(force), sel, ncand)
+    torch.cuda.synchronize()
+    sel, ncand = host(sel), host(ncand)
+    near = 0
+    for b in range(B):
+        for h in range(H):
+            r = routes[b][h]
+            near += compare_selection(r, sel[b, h])
+            sure = r["probe_margin"] > NEAR
+            assert np.array_equal(ncand[b, h][sure], r["n_cand"][sure])
+    print(f"{name}: probe/rerank near-tie tokens {near} of {B * H * S}")
+
+
+@pytest.mark.parametrize("name", NAMES)
+def test_stage_attend_on_oracle_selection(gpu_lib, name):
+    mdr = gpu_lib
+    w = small(name)
+    inp = synth.make_core_inputs(w, 2)
+    B, H = w.batch, w.heads
+    sel = np.stack([np.stack([oracle.route_head(inp["q"][b, h], inp["k"][b, h], inp["codebook"][h],
+                                                None if inp["bias"] is None else inp["bias"][h], w)["sel"]
+                              for h in range(H)]) for b in range(B)]).astype(np.int32)
+    cfg = cfg_of(mdr, w)
+    dt = io_dtype(w)
+    q, k, v = (dev(inp[n], dt) for n in ("q", "k", "v"))
+    out = torch.empty_like(q)
+    mdr.mdr_stage_attend(cfg, q, k, v, dev(sel), out, mdr.workspace(cfg))
+    torch.cuda.synchronize()
+    out = host(out)
+    err = 0.0
+    for b in range(B):
+        for h in range(H):
+            ref = attention_rows(w, inp, sel[b, h], b, h, None, dense=w.seq <= 4096)
+            err = max(err, float(np.abs(out[b, h] - ref).max()))
+    print(f"{name}: max abs err {err:.3g}")
+    assert err <= TOL[w.dtype]
+
+
+@pytest.mark.parametrize("name", NAMES)
+def test_routed_attention_end_to_end(gpu_lib, name):
+    mdr = gpu_lib
+    w = small(name)
+    inp = synth.make_core_inputs(w, 0)
+    res = run_core(mdr, w, inp, force=inp.get("force"))
+    near_a = near_s = 0
+    err = 0.0
+    for b in range(w.batch):
+        for h in range(w.heads):
+            na = compare_addresses(w, inp, res["addr"][b, h], b, h)
+            near_a += na
+            f = None if inp.get("force") is None else inp["force"][b, h]
+            r = oracle.route_head(inp["q"][b, h], inp["k"][b, h], inp["codebook"][h],
+                                  None if inp["bias"] is None else inp["bias"][h], w, f)
+            if na == 0:
+                assert res["overflow"][b, h] == r["overflow"]
+                assert np.array_equal(res["post_off"][b, h], r["off"])
+                near_s += compare_selection(r, res["sel"][b, h])
+            ref = attention_rows(w, inp, res["sel"][b, h], b, h, None, dense=w.seq <= 4096)
+            err = max(err, float(np.abs(res["out"][b, h] - ref).max()))
+    print(f"{name}: address near-ties {near_a}, selection near-ties {near_s}, max abs err {err:.3g}")
+    assert err <= TOL[w.dtype]
+
+
+def test_recall_forced_target_full_batch(gpu_lib):
+    """All 16 sequences of the recall workload; forcing the planted block puts it into every selection of
+    the last query block under the same budget R."""
+    mdr = gpu_lib
+    w = synth.workload("recall")
+    inp = synth.make_core_inputs(w, 0)
+    free = run_core(mdr, w, inp)
+    forced = run_core(mdr, w, inp, force=inp["force"])
+    last = slice((w.nblocks - 1) * w.block, w.seq)
+    hits_free = hits_forced = 0
+    for b in range(w.batch):
+        p = inp["planted"][b]
+        for h in range(w.heads):
+            hits_free += int(np.sum(np.any(free["sel"][b, h, last] == p, axis=1)))
+            s = forced["sel"][b, h, last]
+            hits_forced += int(np.sum(np.any(s == p, axis=1)))
+            assert np.all((s >= 0).sum(axis=1) <= w.remote)
+            ref = attention_rows(w, inp, forced["sel"][b, h], b, h, None, dense=True)
+            assert np.abs(forced["out"][b, h] - ref).max() <= TOL[w.dtype]
+    total = w.batch * w.heads * w.block
+    print(f"planted-block recall: untrained router {hits_free}/{total}, forced {hits_forced}/{total}")
+    assert hits_forced == total
+
+
+def test_deterministic(gpu_lib):
+    mdr = gpu_lib
+    w = small("skew")
+    inp = synth.make_core_inputs(w, 3)
+    a = run_core(mdr, w, inp)
+    b = run_core(mdr, w, inp)
+    for n in ("out", "sel", "addr", "post_idx", "overflow", "ksum"):
+        assert np.array_equal(a[n], b[n]), n
+
+
+@pytest.mark.parametrize("name,t0", [("recall", 1000), ("sweep", 2047), ("skew", 3000)])
+def test_causal_on_gpu(gpu_lib, name, t0):
+    """Perturbing tokens after t0 leaves every selection and output up to t0 bit-identical."""
+    mdr = gpu_lib
+    w = small(name)
+    inp = synth.make_core_inputs(w, 4)
+    a = run_core(mdr, w, inp)
+    rng = np.random.default_rng(5)
+    for n in ("q", "k", "v"):
+        x = inp[n].copy()
+        x[:, :, t0 + 1:] = synth.bf16_round(rng.standard_normal(x[:, :, t0 + 1:].shape).astype(np.float32) * 2)
+        inp[n] = x
+    b = run_core(mdr, w, inp)
+    assert np.array_equal(a["sel"][:, :, :t0 + 1], b["sel"][:, :, :t0 + 1])
+    assert np.array_equal(a["out"][:, :, :t0 + 1], b["out"][:, :, :t0 + 1])
+    assert not np.array_equal(a["out"][:, :, t0 + 1:], b["out"][:, :, t0 + 1:])
+
+
+@pytest.mark.parametrize("over", [
+    dict(remote=0),                      # local-only control
+    dict(seq=64, local=2),               # nb == L: nothing is ever eligible
+    dict(seq=128, local=1),
+    dict(local=1, capacity=1, probes=1),
+    dict(local=3, remote=5, probes=3),
+    dict(seq=1024 + 64),                 # blocks not a multiple of the 64-token waves
+])
+def test_edge_cases(gpu_lib, over):
+    mdr = gpu_lib
+    w = small("recall", batch=2, **over)
+    inp = synth.make_core_inputs(dataclass_replace_plant(w), 6)
+    res = run_core(mdr, w, inp)
+    for b in range(w.batch):
+        for h in range(w.heads):
+            r = oracle.route_head(inp["q"][b, h], inp["k"][b, h], inp["codebook"][h], None, w)
+            compare_addresses(w, inp, res["addr"][b, h], b, h)
+            compare_selection(r, res["sel"][b, h])
+            ref = attention_rows(w, inp, res["sel"][b, h], b, h, None, dense=True)
+            assert np.abs(res["out"][b, h] - ref).max() <= TOL[w.dtype]
+
+
+def dataclass_replace_plant(w):
+    import dataclasses
+
+    return dataclasses.replace(w, plant="none")
+
+
+def test_mixer_forward(gpu_lib):
+    """[batch, seq, width] -> attention delta on the tiny workload (fp32, 1e-5)."""
+    mdr = gpu_lib
+    w = synth.workload("tiny")
+    inp = synth.make_mixer_inputs(w, 0)
+    cfg = cfg_of(mdr, w)
+    t = {n: dev(inp[n], torch.float32) for n in ("x", "wq", "wk", "wv", "wo", "codebook")}
+    delta = torch.empty_like(t["x"])
+    rt = mdr.routing_buffers(cfg)
+    mdr.mdr_mixer_forward(cfg, t["x"], t["wq"], t["wk"], t["wv"], t["wo"], t["codebook"], None, delta, rt,
+                          mdr.workspace(cfg))
+    torch.cuda.synchronize()
+    sel = host(rt["sel"])
+    ref, routes = oracle.mixer_forward(inp["x"], inp["wq"], inp["wk"], inp["wv"], inp["wo"], inp["codebook"], None,
+                                       w, sel_override=sel)
+    for h in range(w.heads):
+        compare_selection(routes[0][h], sel[0, h])
+    err = float(np.abs(host(delta) - ref).max())
+    print(f"mixer max abs err {err:.3g}")
+    assert err <= TOL["f32"]
+
+
+FULL = {
+    "sweep": dict(),
+    "long": dict(),
+    "skew": dict(),
+}
+
+
+@pytest.mark.parametrize("name", list(FULL))
+def test_full_size_sampled(gpu_lib, name):
+    """The largest workloads at full size in the benchmark's launch configuration, checked on sampled
+    tokens (routing with the near-tie rule, overflow of every head, attention rows with the GPU's
+    selection)."""
+    mdr = gpu_lib
+    w = synth.workload(name, **FULL[name])
+    inp = synth.make_core_inputs(w, 0)
+    res = run_core(mdr, w, inp)
+    rng = np.random.default_rng(7)
+    heads = [(b, h) for b in range(w.batch) for h in range(w.heads)]
+    for b, h in heads:
+        ks = oracle.block_summaries(inp["k"][b, h], w.block)
+        bias = None if inp["bias"] is None else inp["bias"][h]
+        _, addr, margin = oracle.block_addresses(ks, inp["codebook"][h], bias)
+        if margin.min() > NEAR:
+            assert np.array_equal(res["addr"][b, h], addr)
+            lists = oracle.posting_lists(addr, w.addresses, w.local)
+            assert res["overflow"][b, h] == oracle.posting_overflow(lists, w.capacity)
+    picks = [heads[i] for i in rng.choice(len(heads), size=min(4, len(heads)), replace=False)]
+    err = 0.0
+    for b, h in picks:
+        toks = np.unique(np.concatenate([rng.choice(w.seq, 96, replace=False), [0, w.block - 1, w.seq - 1]]))
+        r = oracle.route_head(inp["q"][b, h], inp["k"][b, h], inp["codebook"][h],
+                              None if inp["bias"] is None else inp["bias"][h], w, tokens=toks)
+        compare_selection(r, res["sel"][b, h], rows=toks)
+        ref = attention_rows(w, inp, res["sel"][b, h][toks], b, h, toks)
+        err = max(err, float(np.abs(res["out"][b, h][toks] - ref).max()))
+    print(f"{name} full size: overflow total {int(res['overflow'].sum())}, "
+          f"R_eff {float((res['sel'] >= 0).sum(-1).mean()):.3f}, sampled max abs err {err:.3g}")
+    assert err <= TOL[w.dtype]
