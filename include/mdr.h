@@ -77,7 +77,8 @@ typedef enum { MDR_F32 = 0, MDR_BF16 = 1 } mdr_dtype;
  * Supported on gfx950: head_dim in {32, 64, 128}; block in {32, 64, 128};
  * seq % block == 0; 1 <= subspaces <= 4; codes >= 2; subspaces*codes <= 64;
  * codes^subspaces <= 4096; 1 <= probes <= min(16, codes^subspaces);
- * remote <= 16; local >= 1; nb <= 8192. */
+ * remote <= 16; local >= 1; nb <= 8192; the probe stage's per-token scratch
+ * (about 128 * 4 * (G*ceil16(C) + G*min(P,C) + 2P + 2R) bytes) must fit in LDS. */
 typedef struct {
   int32_t batch;       /* B */
   int32_t seq;         /* S, tokens per sequence */
@@ -143,6 +144,21 @@ mdr_status mdr_routed_attention(const mdr_config* cfg, const void* q, const void
                                 const float* codebook, const float* code_bias, const int32_t* force,
                                 void* out, const mdr_routing* routing, void* workspace,
                                 size_t workspace_bytes, void* stream);
+
+/* Kernels of the core path, in launch order (the profiling form below records
+ * an event before each and one after the last). */
+#define MDR_CORE_KERNELS 5 /* address, post, probe_rerank, attn_remote, attn_local */
+
+/* Profiling form of mdr_routed_attention, for timing each kernel on `stream`:
+ * events[k] (a hipEvent_t created by the caller) is recorded just before the
+ * k-th kernel of the core path and events[MDR_CORE_KERNELS] after the last one.
+ * A kernel a configuration does not need (attn_remote when R = 0 or nb <= L)
+ * gets two adjacent events.  Everything else is as in
+ * mdr_routed_attention; a NULL `events` array is rejected. */
+mdr_status mdr_routed_attention_profiled(const mdr_config* cfg, const void* q, const void* k, const void* v,
+                                         const float* codebook, const float* code_bias, const int32_t* force,
+                                         void* out, const mdr_routing* routing, void* workspace,
+                                         size_t workspace_bytes, void* const* events, void* stream);
 
 /* The stateless mixer, [B,S,W] -> attention delta [B,S,W] (aitechinspire.com,
  * "Snapshot: key facts from the report"): Q = RoPE(x Wq), K = RoPE(x Wk),

@@ -19,7 +19,7 @@ import torch  # noqa: F401  (loads the HIP runtime the library must share)
 __all__ = [
     "LIB_PATH", "MdrError", "MdrConfig", "MdrRouting", "MDR_F32", "MDR_BF16", "config", "lib",
     "mdr_abi_version", "mdr_status_string", "mdr_check_config", "mdr_workspace_size",
-    "mdr_routed_attention", "mdr_mixer_forward", "mdr_stage_address", "mdr_stage_post",
+    "mdr_routed_attention", "mdr_routed_attention_profiled", "mdr_mixer_forward", "mdr_stage_address", "mdr_stage_post",
     "mdr_stage_probe_rerank", "mdr_stage_attend", "workspace", "routing_buffers",
 ]
 
@@ -49,7 +49,7 @@ class MdrRouting(ctypes.Structure):
 
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run `python -m learned_product_hash_amd.build`")
+        raise ImportError(f"{LIB_PATH} is not built; run `python learned_product_hash_amd/build.py`")
     return ctypes.CDLL(LIB_PATH)
 
 
@@ -64,6 +64,8 @@ _SIGS = {
     "mdr_check_config": ([_cfgp], _i32),
     "mdr_workspace_size": ([_cfgp, ctypes.POINTER(_sz)], _i32),
     "mdr_routed_attention": ([_cfgp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _rtp, _vp, _sz, _vp], _i32),
+    "mdr_routed_attention_profiled": ([_cfgp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _rtp, _vp, _sz,
+                                       ctypes.POINTER(_vp), _vp], _i32),
     "mdr_mixer_forward": ([_cfgp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _rtp, _vp, _sz, _vp], _i32),
     "mdr_stage_address": ([_cfgp, _vp, _vp, _vp, _vp, _vp, _vp], _i32),
     "mdr_stage_post": ([_cfgp, _vp, _vp, _vp, _vp, _vp], _i32),
@@ -159,6 +161,20 @@ def mdr_routed_attention(cfg, q, k, v, codebook, code_bias, force, out, routing=
     _check(lib.mdr_routed_attention(ctypes.byref(cfg), _ptr(q), _ptr(k), _ptr(v), _ptr(codebook),
                                     _ptr(code_bias), _ptr(force), _ptr(out), _routing(routing), wp, wn,
                                     _stream(stream)), "mdr_routed_attention")
+
+
+MDR_CORE_KERNELS = 5
+CORE_KERNELS = ("address", "post", "probe_rerank", "attn_remote", "attn_local")
+
+
+def mdr_routed_attention_profiled(cfg, q, k, v, codebook, code_bias, force, out, events, routing=None, ws=None,
+                                  stream=None):
+    """``events``: MDR_CORE_KERNELS + 1 raw hipEvent_t handles (ints) created by the caller."""
+    wp, wn = _ws(ws)
+    arr = (_vp * (MDR_CORE_KERNELS + 1))(*events)
+    _check(lib.mdr_routed_attention_profiled(ctypes.byref(cfg), _ptr(q), _ptr(k), _ptr(v), _ptr(codebook),
+                                             _ptr(code_bias), _ptr(force), _ptr(out), _routing(routing), wp, wn,
+                                             arr, _stream(stream)), "mdr_routed_attention_profiled")
 
 
 def mdr_mixer_forward(cfg, x, wq, wk, wv, wo, codebook, code_bias, delta, routing=None, ws=None, stream=None):

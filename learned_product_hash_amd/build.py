@@ -1,6 +1,9 @@
 """Build the gfx950 HIP library ``libmdr.so`` in-tree with hipcc.
 
-    python -m learned_product_hash_amd.build
+    python learned_product_hash_amd/build.py
+
+(Run it as a file, or load it by path as __graft_entry__ does: importing the package
+itself loads the library, which may be missing or stale before a build.)
 
 Each ``csrc/*.hip`` file is compiled to an object under ``_build/`` (in
 parallel), then linked into ``learned_product_hash_amd/libmdr.so``.  Always

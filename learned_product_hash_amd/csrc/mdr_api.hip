@@ -1,6 +1,7 @@
 // C ABI of the routed-attention library: host-side validation, workspace planning and the
 // launch sequences.  No entry point allocates memory or keeps state between calls.
 #include <math.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include "mdr_internal.h"
@@ -55,14 +56,16 @@ mdr_status shape_from_config(const mdr_config* cfg, bool mixer, Shape* out) {
   s.scale = c.softmax_scale > 0.f ? c.softmax_scale : 1.0f / sqrtf((float)c.head_dim);
   s.rope_base = c.rope_base;
   const long long ne = nb > c.local ? nb - c.local : 0;
-  s.bins_per_bh = (long long)c.block * ne * (ne + 1) / 2;
-  // remote work items per (b,h): sum_i ceil(pairs_i / 64), bounded two ways
-  long long by_cap = 0;
-  for (long long i = 0; i < ne; ++i) by_cap += ((ne - i) * c.block + kPairsPerChunk - 1) / kPairsPerChunk;
-  long long by_pairs = ((long long)c.seq * c.remote + kPairsPerChunk - 1) / kPairsPerChunk + ne;
-  long long ch = by_cap < by_pairs ? by_cap : by_pairs;
-  if (ch > 0x7fffffffLL) return MDR_ERR_UNSUPPORTED;
-  s.chunks_per_bh = (int)ch;
+  s.ne = (int)ne;
+  s.cells_per_bh = ne * (ne + 1) / 2;
+  // split heavy blocks over several remote work-groups: about two chunks of 64 pairs each
+  const long long avg_chunks = ne > 0 ? ((long long)c.seq * c.remote / ne + kPairsPerChunk - 1) / kPairsPerChunk : 0;
+  long long split = avg_chunks / 2;
+  s.split = (int)(split < 1 ? 1 : split > 8 ? 8 : split);
+  s.csr_lds = ((long long)s.A + 1 + ne) * 4 <= 16384;
+  s.fixed_probe = probe_fixed_shape(s);
+  if (probe_lds_bytes(s) > 160 * 1024) return MDR_ERR_UNSUPPORTED;
+  if (s.R > 0 && ne > 0 && remote_lds_bytes(s) > 160 * 1024) return MDR_ERR_UNSUPPORTED;
   *out = s;
   return MDR_OK;
 }
@@ -86,9 +89,8 @@ size_t layout(const Shape& s, char* base, Buffers* b) {
   t.overflow = (int32_t*)take(BH * 4);
   t.sel = (int32_t*)take(BH * s.S * s.R * 4);
   t.ncand = (int32_t*)take(BH * s.S * 4);
-  t.cnt = (int32_t*)take(BH * s.nb * 4);
-  t.chunk_off = (int32_t*)take(BH * (s.nb + 1) * 4);
-  t.bins = (int32_t*)take(BH * (size_t)s.bins_per_bh * 4);
+  t.cellcnt = (int32_t*)take(BH * (size_t)s.cells_per_bh * 4);
+  t.bins = (int32_t*)take(BH * (size_t)s.cells_per_bh * s.blk * 4);
   t.part_o = take(BH * s.S * s.R * s.D * e);
   t.part_ml = (float*)take(BH * s.S * s.R * 8);
   if (s.W > 0) {
@@ -138,14 +140,19 @@ bool routing_aligned(const mdr_routing* r) {
 }
 
 // The four stages of the core on post-RoPE q, k, v already in device memory.
+// ev (optional, MDR_CORE_KERNELS + 1 entries): recorded before each kernel and after the last.
 mdr_status run_core(const Shape& s, const void* q, const void* k, const void* v, const float* cb, const float* bias,
-                    const int32_t* force, void* out, const Buffers& b, hipStream_t st) {
-  const bool remote = s.R > 0 && s.nb > s.L;
-  MDR_TRY(launch_address(s, k, cb, bias, b.ksum, b.addr, remote ? b.cnt : nullptr, st));
+                    const int32_t* force, void* out, const Buffers& b, hipStream_t st, hipEvent_t* ev = nullptr) {
+  const bool remote = s.R > 0 && s.ne > 0;
+  if (ev) MDR_TRY(hipEventRecord(ev[0], st));
+  MDR_TRY(launch_address(s, k, cb, bias, b.ksum, b.addr, remote ? b.cellcnt : nullptr, st));
+  if (ev) MDR_TRY(hipEventRecord(ev[1], st));
   MDR_TRY(launch_post(s, b.addr, b.off, b.idx, b.overflow, st));
+  if (ev) MDR_TRY(hipEventRecord(ev[2], st));
   MDR_TRY(launch_probe_rerank(s, q, cb, bias, b.ksum, b.off, b.idx, force, b.sel, b.ncand,
-                              remote ? b.cnt : nullptr, remote ? b.bins : nullptr, st));
-  MDR_TRY(launch_attend(s, q, k, v, b.sel, out, b, st));
+                              remote ? b.cellcnt : nullptr, remote ? b.bins : nullptr, st));
+  MDR_TRY(launch_attend(s, q, k, v, b.sel, out, b, st, ev ? ev + 3 : nullptr));
+  if (ev) MDR_TRY(hipEventRecord(ev[MDR_CORE_KERNELS], st));
   return MDR_OK;
 }
 
@@ -196,6 +203,27 @@ mdr_status mdr_routed_attention(const mdr_config* cfg, const void* q, const void
   if (st != MDR_OK) return st;
   apply_routing(routing, &b);
   return run_core(s, q, k, v, codebook, code_bias, force, out, b, (hipStream_t)stream);
+}
+
+mdr_status mdr_routed_attention_profiled(const mdr_config* cfg, const void* q, const void* k, const void* v,
+                                         const float* codebook, const float* code_bias, const int32_t* force,
+                                         void* out, const mdr_routing* routing, void* workspace,
+                                         size_t workspace_bytes, void* const* events, void* stream) {
+  Shape s;
+  mdr_status st = shape_from_config(cfg, false, &s);
+  if (st != MDR_OK) return st;
+  s.W = 0;
+  if (!q || !k || !v || !codebook || !out || !events) return MDR_ERR_INVALID_ARG;
+  for (int i = 0; i <= MDR_CORE_KERNELS; ++i)
+    if (!events[i]) return MDR_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(codebook) ||
+      !routing_aligned(routing))
+    return MDR_ERR_INVALID_ARG;
+  Buffers b;
+  st = check_workspace(s, workspace, workspace_bytes, &b);
+  if (st != MDR_OK) return st;
+  apply_routing(routing, &b);
+  return run_core(s, q, k, v, codebook, code_bias, force, out, b, (hipStream_t)stream, (hipEvent_t*)events);
 }
 
 mdr_status mdr_mixer_forward(const mdr_config* cfg, const void* x, const void* wq, const void* wk, const void* wv,
@@ -266,9 +294,9 @@ mdr_status mdr_stage_attend(const mdr_config* cfg, const void* q, const void* k,
   st = check_workspace(s, workspace, workspace_bytes, &b);
   if (st != MDR_OK) return st;
   hipStream_t hs = (hipStream_t)stream;
-  if (s.R > 0 && s.nb > s.L) {
-    MDR_TRY(launch_fill(b.cnt, (long long)s.B * s.H * s.nb, 0, hs));
-    MDR_TRY(launch_pair_bin(s, sel, b.cnt, b.bins, hs));
+  if (s.R > 0 && s.ne > 0) {
+    MDR_TRY(launch_fill(b.cellcnt, (long long)s.B * s.H * s.cells_per_bh, 0, hs));
+    MDR_TRY(launch_pair_bin(s, sel, b.cellcnt, b.bins, hs));
   }
   MDR_TRY(launch_attend(s, q, k, v, sel, out, b, hs));
   return MDR_OK;

@@ -10,11 +10,13 @@
 // Routing is per query token, so the remote blocks of neighbouring tokens differ.  Reading
 // each token's remote blocks separately would move every block many times, so the remote part
 // is regrouped by block:
-//   k_pair_bin     (token, slot) pairs appended to the bin of their selected block
-//   k_pair_plan    per (b,h): exclusive scan of ceil(pairs / 64) over the blocks
-//   k_attn_remote  one work-group per 64 pairs of one block: the block's K/V is staged in LDS
-//                  once, the pairs' queries are gathered, S^T = K Q^T and O^T = V^T P^T run on
-//                  MFMA, and each pair's softmax partial (max, sum, normalised output) is stored
+//   pairs          each selected (token, slot) pair is appended to the cell (remote block i, query
+//                  block j) -- by the probe kernel, or by k_pair_bin when a selection is passed in;
+//                  only the work-group owning query block j writes a cell, so no counter is hot
+//   k_attn_remote  one work-group per selected block (split when blocks are heavy): the block's
+//                  K/V is staged in LDS once, its pairs are walked 64 at a time, the pairs'
+//                  queries are gathered, S^T = K Q^T and O^T = V^T P^T run on MFMA, and each
+//                  pair's softmax partial (max, sum, normalised output) is stored
 //   k_attn_local   one work-group per query block: the L local blocks through LDS on MFMA with
 //                  the causal mask on the diagonal block and an online softmax, then the
 //                  remote partials of each token are merged in slot order and O is written.
@@ -200,119 +202,104 @@ __global__ __launch_bounds__(256) void k_fill(int32_t* p, long long n, int32_t v
   for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long long)gridDim.x * 256) p[i] = value;
 }
 
-__global__ __launch_bounds__(256) void k_pair_bin(const int32_t* __restrict__ sel, int32_t* __restrict__ cnt,
+__global__ __launch_bounds__(256) void k_pair_bin(const int32_t* __restrict__ sel, int32_t* __restrict__ cellcnt,
                                                   int32_t* __restrict__ bins, Shape s) {
   const int t = blockIdx.x * 256 + threadIdx.x;
   const int bh = blockIdx.y;
   if (t >= s.S) return;
   const int j = t / s.blk;
   const int32_t* row = sel + ((size_t)bh * s.S + t) * s.R;
-  for (int r = 0; r < s.R; ++r) {
-    if (!sel_entry_valid(row, r, j, s.L)) continue;
-    const int i = row[r];
-    const int pos = atomicAdd(&cnt[(size_t)bh * s.nb + i], 1);
-    if (pos < (s.nb - s.L - i) * s.blk)
-      bins[(size_t)bh * s.bins_per_bh + bin_offset(i, s.nb, s.L, s.blk) + pos] = t * s.R + r;
-  }
+  for (int r = 0; r < s.R; ++r)
+    if (sel_entry_valid(row, r, j, s.L)) record_pair(cellcnt, bins, s, bh, row[r], j, t, r);
 }
 
-__global__ __launch_bounds__(256) void k_pair_plan(const int32_t* __restrict__ cnt, int32_t* __restrict__ chunk_off,
-                                                   Shape s) {
-  __shared__ int part[256];
-  const int tid = threadIdx.x, bh = blockIdx.x;
-  const int nb = s.nb;
-  const int seg = (nb + 255) / 256;
-  const int i0 = min(nb, tid * seg), i1 = min(nb, i0 + seg);
-  const int32_t* c = cnt + (size_t)bh * nb;
-  int sum = 0;
-  for (int i = i0; i < i1; ++i) sum += (c[i] + kPairsPerChunk - 1) / kPairsPerChunk;
-  part[tid] = sum;
-  __syncthreads();
-  if (tid == 0) {
-    int run = 0;
-    for (int w = 0; w < 256; ++w) {
-      const int v = part[w];
-      part[w] = run;
-      run += v;
-    }
-    chunk_off[(size_t)bh * (nb + 1) + nb] = run;
-  }
-  __syncthreads();
-  int run = part[tid];
-  for (int i = i0; i < i1; ++i) {
-    chunk_off[(size_t)bh * (nb + 1) + i] = run;
-    run += (c[i] + kPairsPerChunk - 1) / kPairsPerChunk;
-  }
-}
-
-// One work-group = up to 64 (token, slot) pairs that selected the same block.
+// One work-group per (remote block i, split): the pairs of block i are the concatenation of its
+// cells (i, j), j = i + L .. nb - 1.  The work-group scans the cell counts into LDS, stages the
+// block's K/V in LDS once, and processes its chunks of 64 pairs (chunk c goes to split c % splits):
+// each wave gathers 16 pairs' queries, S^T = K Q^T and O^T = V^T P^T on MFMA, and every pair's
+// softmax partial is stored at [token][slot].
 template <typename T, int D, int BLK>
 __global__ __launch_bounds__(256) void k_attn_remote(const T* __restrict__ Q, const T* __restrict__ K,
-                                                     const T* __restrict__ V, const int32_t* __restrict__ cnt,
-                                                     const int32_t* __restrict__ chunk_off,
+                                                     const T* __restrict__ V, const int32_t* __restrict__ cellcnt,
                                                      const int32_t* __restrict__ bins, T* __restrict__ part_o,
                                                      float* __restrict__ part_ml, Shape s) {
   using TL = Tile<T, D, BLK>;
   extern __shared__ __align__(16) char lds_raw[];
   T* Ks = (T*)lds_raw;
   T* Vx = Ks + TL::K_ELEMS;
-  const int x = blockIdx.x, bh = blockIdx.y;
-  const int32_t* co = chunk_off + (size_t)bh * (s.nb + 1);
-  if (x >= co[s.nb]) return;  // uniform for the work-group, before any barrier
-  int lo = 0, hi = s.nb - 1;  // the block whose chunk range holds x
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (co[mid] <= x)
-      lo = mid;
-    else
-      hi = mid - 1;
-  }
-  const int i = lo;
-  const int p0 = (x - co[i]) * kPairsPerChunk;
-  const int npairs = min(kPairsPerChunk, cnt[(size_t)bh * s.nb + i] - p0);
-  const int32_t* bp = bins + (size_t)bh * s.bins_per_bh + bin_offset(i, s.nb, s.L, s.blk) + p0;
+  int* pre = (int*)(Vx + TL::V_ELEMS);  // [ncell + 1] exclusive prefix of the cell counts
+  __shared__ int scan_tmp[4];
+  const int i = blockIdx.x, bh = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int ncell = s.ne - i;
+  const long long row0 = (long long)bh * s.cells_per_bh + cell_row(i, s.ne);
+  int run = 0;
+  for (int c0 = 0; c0 < ncell; c0 += 256) {
+    const int c = c0 + tid;
+    const int v = c < ncell ? min(cellcnt[row0 + c], BLK) : 0;
+    int tot;
+    const int ex = block_exclusive_scan<256>(v, scan_tmp, &tot);
+    if (c < ncell) pre[c] = run + ex;
+    run += tot;
+  }
+  if (tid == 0) pre[ncell] = run;
+  const int total = run;
+  const int nch = (total + kPairsPerChunk - 1) / kPairsPerChunk;
+  if ((int)blockIdx.z >= nch) return;  // uniform for the work-group
   const size_t rowbase = (size_t)bh * s.S;
   load_kv<T, D, BLK, 256>(K + (rowbase + (size_t)i * BLK) * D, V + (rowbase + (size_t)i * BLK) * D, Ks, Vx, tid);
-  const int slot = wave * 16 + (lane & 15);
-  const bool valid = slot < npairs;
-  const int pv = valid ? bp[slot] : 0;
-  const int t = pv / s.R, r = pv % s.R;
-  QFrag<T, D> qf;
-  load_q<T, D>(qf, Q + (rowbase + t) * D, lane);
   __syncthreads();
   const float c = s.scale * kLog2e;
-  f32x4 p[TL::NT];
-  float mx = -INFINITY;
-#pragma unroll
-  for (int n = 0; n < TL::NT; ++n) {
-    p[n] = score_tile<T, D, BLK>(qf, Ks, n, lane);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      p[n][k] *= c;
-      mx = fmaxf(mx, p[n][k]);
+  for (int ch = blockIdx.z; ch < nch; ch += gridDim.z) {
+    const int pidx = ch * kPairsPerChunk + wave * 16 + (lane & 15);
+    const bool valid = pidx < total;
+    int pv = 0;
+    if (valid) {
+      int lo = 0, hi = ncell - 1;  // the cell whose range holds pidx
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (pre[mid] <= pidx)
+          lo = mid;
+        else
+          hi = mid - 1;
+      }
+      pv = bins[(row0 + lo) * BLK + (pidx - pre[lo])];
     }
-  }
-  mx = wave_max16(mx);
-  float sum = 0.f;
+    const int t = pv / s.R, r = pv % s.R;
+    QFrag<T, D> qf;
+    load_q<T, D>(qf, Q + (rowbase + t) * D, lane);
+    f32x4 p[TL::NT];
+    float mx = -INFINITY;
 #pragma unroll
-  for (int n = 0; n < TL::NT; ++n)
+    for (int n = 0; n < TL::NT; ++n) {
+      p[n] = score_tile<T, D, BLK>(qf, Ks, n, lane);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      p[n][k] = exp2f(p[n][k] - mx);
-      sum += p[n][k];
+      for (int k = 0; k < 4; ++k) {
+        p[n][k] *= c;
+        mx = fmaxf(mx, p[n][k]);
+      }
     }
-  sum = wave_sum16(sum);
-  f32x4 o[TL::ND];
+    mx = wave_max16(mx);
+    float sum = 0.f;
 #pragma unroll
-  for (int dt = 0; dt < TL::ND; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  pv_block<T, D, BLK>(o, p, Vx, lane);
-  if (valid) {
-    const size_t pr = (rowbase + t) * s.R + r;
-    const float inv = 1.f / sum;
+    for (int n = 0; n < TL::NT; ++n)
 #pragma unroll
-    for (int dt = 0; dt < TL::ND; ++dt) store4<T>(part_o + pr * D + 16 * dt + 4 * (lane >> 4), o[dt], inv);
-    if ((lane >> 4) == 0) *(float2*)(part_ml + 2 * pr) = make_float2(mx, sum);
+      for (int k = 0; k < 4; ++k) {
+        p[n][k] = exp2f(p[n][k] - mx);
+        sum += p[n][k];
+      }
+    sum = wave_sum16(sum);
+    f32x4 o[TL::ND];
+#pragma unroll
+    for (int dt = 0; dt < TL::ND; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    pv_block<T, D, BLK>(o, p, Vx, lane);
+    if (valid) {
+      const size_t pr = (rowbase + t) * s.R + r;
+      const float inv = 1.f / sum;
+#pragma unroll
+      for (int dt = 0; dt < TL::ND; ++dt) store4<T>(part_o + pr * D + 16 * dt + 4 * (lane >> 4), o[dt], inv);
+      if ((lane >> 4) == 0) *(float2*)(part_ml + 2 * pr) = make_float2(mx, sum);
+    }
   }
 }
 
@@ -401,47 +388,66 @@ __global__ __launch_bounds__(BLK * 4) void k_attn_local(const T* __restrict__ Q,
 
 template <typename T, int D, int BLK>
 hipError_t attend_impl(const Shape& s, const void* q, const void* k, const void* v, const int32_t* sel, void* out,
-                       const Buffers& b, hipStream_t st) {
+                       const Buffers& b, hipStream_t st, hipEvent_t* ev) {
   using TL = Tile<T, D, BLK>;
   const size_t lds = TL::LDS_BYTES;
-  const bool remote = s.R > 0 && s.nb > s.L;
+  const bool remote = s.R > 0 && s.ne > 0;
+  hipError_t e;
+  if (ev && (e = hipEventRecord(ev[0], st)) != hipSuccess) return e;
   if (remote) {
-    hipLaunchKernelGGL(k_pair_plan, dim3(s.B * s.H), dim3(256), 0, st, b.cnt, b.chunk_off, s);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    if (lds > 65536) hipFuncSetAttribute((const void*)k_attn_remote<T, D, BLK>,
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    hipLaunchKernelGGL((k_attn_remote<T, D, BLK>), dim3(s.chunks_per_bh, s.B * s.H), dim3(256), lds, st,
-                       (const T*)q, (const T*)k, (const T*)v, b.cnt, b.chunk_off, b.bins, (T*)b.part_o, b.part_ml,
-                       s);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    const size_t rl = remote_lds_bytes(s);
+    if (rl > 65536 && (e = hipFuncSetAttribute((const void*)k_attn_remote<T, D, BLK>,
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)rl)) != hipSuccess)
+      return e;
+    hipLaunchKernelGGL((k_attn_remote<T, D, BLK>), dim3(s.ne, s.B * s.H, s.split), dim3(256), rl, st, (const T*)q,
+                       (const T*)k, (const T*)v, b.cellcnt, b.bins, (T*)b.part_o, b.part_ml, s);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  if (lds > 65536) hipFuncSetAttribute((const void*)k_attn_local<T, D, BLK>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (ev && (e = hipEventRecord(ev[1], st)) != hipSuccess) return e;
+  if (lds > 65536 && (e = hipFuncSetAttribute((const void*)k_attn_local<T, D, BLK>,
+                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)) != hipSuccess)
+    return e;
   hipLaunchKernelGGL((k_attn_local<T, D, BLK>), dim3(s.nb, s.B * s.H), dim3(BLK * 4), lds, st, (const T*)q,
                      (const T*)k, (const T*)v, sel, (const T*)b.part_o, b.part_ml, (T*)out, s);
   return hipGetLastError();
 }
 
 template <typename T, int D>
-hipError_t attend_blk(const Shape& s, const void* q, const void* k, const void* v, const int32_t* sel, void* out,
-                      const Buffers& b, hipStream_t st) {
+size_t remote_lds_d(const Shape& s) {
   switch (s.blk) {
-    case 32: return attend_impl<T, D, 32>(s, q, k, v, sel, out, b, st);
-    case 64: return attend_impl<T, D, 64>(s, q, k, v, sel, out, b, st);
-    case 128: return attend_impl<T, D, 128>(s, q, k, v, sel, out, b, st);
+    case 32: return Tile<T, D, 32>::LDS_BYTES;
+    case 64: return Tile<T, D, 64>::LDS_BYTES;
+    default: return Tile<T, D, 128>::LDS_BYTES;
+  }
+}
+
+template <typename T>
+size_t remote_lds_t(const Shape& s) {
+  switch (s.D) {
+    case 32: return remote_lds_d<T, 32>(s);
+    case 64: return remote_lds_d<T, 64>(s);
+    default: return remote_lds_d<T, 128>(s);
+  }
+}
+
+template <typename T, int D>
+hipError_t attend_blk(const Shape& s, const void* q, const void* k, const void* v, const int32_t* sel, void* out,
+                      const Buffers& b, hipStream_t st, hipEvent_t* ev) {
+  switch (s.blk) {
+    case 32: return attend_impl<T, D, 32>(s, q, k, v, sel, out, b, st, ev);
+    case 64: return attend_impl<T, D, 64>(s, q, k, v, sel, out, b, st, ev);
+    case 128: return attend_impl<T, D, 128>(s, q, k, v, sel, out, b, st, ev);
     default: return hipErrorInvalidValue;
   }
 }
 
 template <typename T>
 hipError_t attend_d(const Shape& s, const void* q, const void* k, const void* v, const int32_t* sel, void* out,
-                    const Buffers& b, hipStream_t st) {
+                    const Buffers& b, hipStream_t st, hipEvent_t* ev) {
   switch (s.D) {
-    case 32: return attend_blk<T, 32>(s, q, k, v, sel, out, b, st);
-    case 64: return attend_blk<T, 64>(s, q, k, v, sel, out, b, st);
-    case 128: return attend_blk<T, 128>(s, q, k, v, sel, out, b, st);
+    case 32: return attend_blk<T, 32>(s, q, k, v, sel, out, b, st, ev);
+    case 64: return attend_blk<T, 64>(s, q, k, v, sel, out, b, st, ev);
+    case 128: return attend_blk<T, 128>(s, q, k, v, sel, out, b, st, ev);
     default: return hipErrorInvalidValue;
   }
 }
@@ -456,15 +462,20 @@ hipError_t launch_fill(int32_t* p, long long n, int32_t value, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_pair_bin(const Shape& s, const int32_t* sel, int32_t* cnt, int32_t* bins, hipStream_t st) {
-  hipLaunchKernelGGL(k_pair_bin, dim3((s.S + 255) / 256, s.B * s.H), dim3(256), 0, st, sel, cnt, bins, s);
+hipError_t launch_pair_bin(const Shape& s, const int32_t* sel, int32_t* cellcnt, int32_t* bins, hipStream_t st) {
+  hipLaunchKernelGGL(k_pair_bin, dim3((s.S + 255) / 256, s.B * s.H), dim3(256), 0, st, sel, cellcnt, bins, s);
   return hipGetLastError();
 }
 
+size_t remote_lds_bytes(const Shape& s) {
+  const size_t kv = s.dtype == MDR_BF16 ? remote_lds_t<bf16>(s) : remote_lds_t<float>(s);
+  return kv + (size_t)(s.ne + 1) * 4;
+}
+
 hipError_t launch_attend(const Shape& s, const void* q, const void* k, const void* v, const int32_t* sel, void* out,
-                         const Buffers& b, hipStream_t st) {
-  if (s.dtype == MDR_BF16) return attend_d<bf16>(s, q, k, v, sel, out, b, st);
-  return attend_d<float>(s, q, k, v, sel, out, b, st);
+                         const Buffers& b, hipStream_t st, hipEvent_t* ev) {
+  if (s.dtype == MDR_BF16) return attend_d<bf16>(s, q, k, v, sel, out, b, st, ev);
+  return attend_d<float>(s, q, k, v, sel, out, b, st, ev);
 }
 
 }  // namespace mdr

@@ -28,9 +28,14 @@ struct Shape {
   int B, H, S, D, W, blk, nb, G, C, A, cap, P, M, R, L, dtype;
   float scale;      // softmax scale (1/sqrt(D) unless given)
   float rope_base;  // mixer only
-  long long bins_per_bh;   // capacity of the per-(b,h) pair bins
-  int chunks_per_bh;       // upper bound of remote work items per (b,h)
+  int ne;           // blocks that some query block can see: nb - L (or 0)
+  long long cells_per_bh;  // (remote block i, query block j) cells with j >= i + L: ne (ne + 1) / 2
+  int split;        // remote work-groups per block
+  int csr_lds;      // probe stage stages the posting-list CSR in LDS
+  int fixed_probe;  // probe stage uses its compile-time specialisation for these sizes
 };
+
+constexpr int kProbeThreads = 128;  // query tokens per probe work-group (one per lane)
 
 // Device buffers of one call (workspace regions or caller-provided outputs).
 struct Buffers {
@@ -41,9 +46,8 @@ struct Buffers {
   int32_t* overflow;
   int32_t* sel;
   int32_t* ncand;
-  int32_t* cnt;        // [B,H,nb] selections per block
-  int32_t* chunk_off;  // [B,H,nb+1] exclusive scan of per-block remote chunks
-  int32_t* bins;       // [B,H,bins_per_bh] (t*R + r) grouped by selected block
+  int32_t* cellcnt;    // [B,H,cells] pairs per (remote block i, query block j) cell
+  int32_t* bins;       // [B,H,cells,blk] (t*R + r) of the pairs of each cell
   void* part_o;        // [B,H,S,R,D] remote partial outputs (normalised), io dtype
   float* part_ml;      // [B,H,S,R,2] remote partial (max in log2 units, sum)
   void* mq;            // mixer: Q, K, V, O in [B,H,S,D]
@@ -52,11 +56,11 @@ struct Buffers {
   void* mo;
 };
 
-// First bin slot of block i: blocks before i can be chosen by (nb - L - i') * blk tokens each.
-__host__ __device__ inline long long bin_offset(int i, int nb, int L, int blk) {
-  long long n = nb - L;
-  long long ii = i;
-  return (long long)blk * (ii * n - ii * (ii - 1) / 2);
+// The cells of remote block i are (i, j) for j = i + L .. nb - 1, stored contiguously; a cell
+// holds the pairs of query block j that selected block i (at most blk of them).
+__host__ __device__ inline long long cell_row(int i, int ne) {
+  const long long ii = i;
+  return ii * ne - ii * (ii - 1) / 2;
 }
 
 // Selection entry r of a token in query block j is used iff it is an eligible block
@@ -69,20 +73,60 @@ __device__ inline bool sel_entry_valid(const int32_t* row, int r, int j, int L) 
   return true;
 }
 
+// Append pair (t, r) of query block j to the cell (i, j).  Only the work-group that owns query
+// block j touches the cell, so its counter sees at most blk atomic adds.
+__device__ inline void record_pair(int32_t* cellcnt, int32_t* bins, const Shape& s, int bh, int i, int j, int t,
+                                   int r) {
+  const long long cell = (long long)bh * s.cells_per_bh + cell_row(i, s.ne) + (j - i - s.L);
+  const int pos = atomicAdd(&cellcnt[cell], 1);
+  if (pos < s.blk) bins[cell * s.blk + pos] = t * s.R + r;
+}
+
+// Exclusive scan of one int per thread over a work-group of NT threads (NT a multiple of 64).
+// tmp holds NT/64 ints.  Returns the exclusive prefix; *total receives the sum.
+template <int NT>
+__device__ inline int block_exclusive_scan(int v, int* tmp, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) tmp[wave] = x;
+  __syncthreads();
+  int before = 0, sum = 0;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) {
+    const int tw = tmp[w];
+    before += (w < wave) ? tw : 0;
+    sum += tw;
+  }
+  __syncthreads();
+  *total = sum;
+  return before + x - v;
+}
+
 // Launchers (return hipGetLastError()).
+// cell_zero (optional): the address kernel of block i clears the cell counters of row i.
 hipError_t launch_address(const Shape& s, const void* k, const float* codebook, const float* bias,
-                          float* ksum, int32_t* addr, int32_t* cnt_zero, hipStream_t st);
+                          float* ksum, int32_t* addr, int32_t* cell_zero, hipStream_t st);
 hipError_t launch_post(const Shape& s, const int32_t* addr, int32_t* off, int32_t* idx,
                        int32_t* overflow, hipStream_t st);
 hipError_t launch_probe_rerank(const Shape& s, const void* q, const float* codebook, const float* bias,
                                const float* ksum, const int32_t* off, const int32_t* idx,
-                               const int32_t* force, int32_t* sel, int32_t* ncand, int32_t* cnt,
+                               const int32_t* force, int32_t* sel, int32_t* ncand, int32_t* cellcnt,
                                int32_t* bins, hipStream_t st);
+size_t probe_lds_bytes(const Shape& s);
+bool probe_fixed_shape(const Shape& s);
 hipError_t launch_fill(int32_t* p, long long n, int32_t value, hipStream_t st);
-hipError_t launch_pair_bin(const Shape& s, const int32_t* sel, int32_t* cnt, int32_t* bins,
+hipError_t launch_pair_bin(const Shape& s, const int32_t* sel, int32_t* cellcnt, int32_t* bins,
                            hipStream_t st);
+size_t remote_lds_bytes(const Shape& s);
+// ev (optional, 2 entries): recorded before attn_remote and attn_local.
 hipError_t launch_attend(const Shape& s, const void* q, const void* k, const void* v,
-                         const int32_t* sel, void* out, const Buffers& b, hipStream_t st);
+                         const int32_t* sel, void* out, const Buffers& b, hipStream_t st,
+                         hipEvent_t* ev = nullptr);
 hipError_t launch_project_heads(const Shape& s, const void* x, const void* w, void* out, bool rope,
                                 hipStream_t st);
 hipError_t launch_project_out(const Shape& s, const void* o, const void* wo, void* delta,

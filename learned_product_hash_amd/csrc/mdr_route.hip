@@ -15,6 +15,8 @@
 
 #include <float.h>
 
+#include <type_traits>
+
 namespace mdr {
 
 namespace {
@@ -44,7 +46,7 @@ __device__ inline float to_f(bf16 x) { return (float)x; }
 template <typename T, int D>
 __global__ __launch_bounds__(256) void k_address(const T* __restrict__ K, const float* __restrict__ cb,
                                                  const float* __restrict__ bias, float* __restrict__ ksum,
-                                                 int32_t* __restrict__ addr, int32_t* __restrict__ cnt_zero,
+                                                 int32_t* __restrict__ addr, int32_t* __restrict__ cell_zero,
                                                  Shape s) {
   constexpr int VEC = Vec16<T>::n;
   constexpr int NCH = D / VEC;
@@ -102,7 +104,10 @@ __global__ __launch_bounds__(256) void k_address(const T* __restrict__ K, const 
       a = a * s.C + best;
     }
     addr[(size_t)bh * s.nb + i] = a;
-    if (cnt_zero) cnt_zero[(size_t)bh * s.nb + i] = 0;
+  }
+  if (cell_zero && i < s.ne) {
+    int32_t* row = cell_zero + (size_t)bh * s.cells_per_bh + cell_row(i, s.ne);
+    for (int c = tid; c < s.ne - i; c += 256) row[c] = 0;
   }
 }
 
@@ -117,8 +122,7 @@ __global__ __launch_bounds__(256) void k_post(const int32_t* __restrict__ addr, 
                                               int32_t* __restrict__ idx, int32_t* __restrict__ overflow,
                                               Shape s) {
   __shared__ int hist[kMaxAddresses];
-  __shared__ int part[256];
-  __shared__ int ovf[256];
+  __shared__ int part[4];
   __shared__ int total;
   const int tid = threadIdx.x;
   const int bh = blockIdx.x;
@@ -140,30 +144,19 @@ __global__ __launch_bounds__(256) void k_post(const int32_t* __restrict__ addr, 
     sum += hist[a];
     over += max(0, hist[a] - s.cap);
   }
-  part[tid] = sum;
-  ovf[tid] = over;
-  __syncthreads();
+  int tot_over = 0, tot = 0;
+  block_exclusive_scan<256>(over, part, &tot_over);
+  int run = block_exclusive_scan<256>(sum, part, &tot);
   if (tid == 0) {
-    int run = 0, tot = 0;
-    for (int w = 0; w < 256; ++w) {
-      const int v = part[w];
-      part[w] = run;
-      run += v;
-      tot += ovf[w];
-    }
-    overflow[bh] = tot;
-    off[(size_t)bh * (A + 1) + A] = run;
-    total = run;
+    overflow[bh] = tot_over;
+    off[(size_t)bh * (A + 1) + A] = tot;
+    total = tot;
   }
-  __syncthreads();
-  {
-    int run = part[tid];
-    for (int a = a0; a < a1; ++a) {
-      const int v = hist[a];
-      off[(size_t)bh * (A + 1) + a] = run;
-      hist[a] = run;  // becomes the scatter cursor of address a
-      run += v;
-    }
+  for (int a = a0; a < a1; ++a) {
+    const int v = hist[a];
+    off[(size_t)bh * (A + 1) + a] = run;
+    hist[a] = run;  // becomes the scatter cursor of address a
+    run += v;
   }
   __syncthreads();
   int32_t* out = idx + (size_t)bh * s.nb;
@@ -199,150 +192,209 @@ __global__ __launch_bounds__(256) void k_post(const int32_t* __restrict__ addr, 
 }
 
 // ---------------------------------------------------------------------------------------------
-// Probe + rerank, one lane per query token, one wave per work-group (per-lane scratch lives in
-// LDS, laid out [slot][lane] so lanes never conflict).
-//   mu[g,c]   = <codebook[h,g,c], q_t> + bias[h,g,c]
-//   probes    = top-P addresses by sigma(a) = sum_g mu[g, c_g(a)] (summed in subspace order),
-//               ties to the smaller address.  Only the top-min(P,C) codes of each subspace can
-//               take part in a top-P address (any other code is beaten by P addresses that swap
-//               it for a better code of the same subspace), so those combinations are scored.
+// Probe + rerank.  A work-group of kProbeThreads lanes handles as many consecutive query tokens of
+// one (b,h), one token per lane for the ranking steps (per-lane scratch lives in LDS, laid out
+// [slot][lane] so lanes never conflict):
+//   mu[g,c]   = <codebook[h,g,c], q_t> + bias[h,g,c], for all tokens of the work-group at once on
+//               MFMA (fp32 16x16x4; tokens as rows, codes as columns, subspaces padded to 16 codes)
+//   probes    = top-P addresses by sigma(a) = sum_g mu[g, c_g(a)] (summed in subspace order), ties to
+//               the smaller address.  With the codes of each subspace ranked by (mu desc, code asc),
+//               an address whose subspace ranks are (k_0, .., k_{G-1}) is beaten by every address
+//               with ranks k'_g <= k_g, i.e. by prod_g (k_g + 1) - 1 others, so only rank vectors
+//               with prod_g (k_g + 1) <= P are scored.
 //   candidates= for each probe in rank order, the newest `capacity` CSR entries <= j - L,
 //               newest first, until M candidates
 //   selection = top-R candidates by <q_t, summary_i>, ties to the smaller block
-// Optionally the selected (token, slot) pairs are appended to per-block bins for the
-// block-grouped attention (cnt must be zero on entry).
+// Optionally each selected (token, slot) pair is appended to the cell (block, query block).
 template <typename T, int D>
-__global__ __launch_bounds__(64) void k_probe_rerank(const T* __restrict__ Q, const float* __restrict__ cb,
-                                                     const float* __restrict__ bias,
-                                                     const float* __restrict__ ksum,
-                                                     const int32_t* __restrict__ off,
-                                                     const int32_t* __restrict__ idx,
-                                                     const int32_t* __restrict__ force,
-                                                     int32_t* __restrict__ sel, int32_t* __restrict__ ncand,
-                                                     int32_t* __restrict__ cnt, int32_t* __restrict__ bins,
-                                                     Shape s) {
-  extern __shared__ float smem[];
-  const int lane = threadIdx.x;
-  const int GC = s.G * s.C;
-  const int P = s.P, R = s.R, C = s.C, G = s.G;
-  float* mu = smem;                           // [GC][64]
-  int* tc = (int*)(mu + GC * kWave);           // [G][P][64] top codes per subspace
-  float* tpv = (float*)(tc + G * P * kWave);   // [P][64] top-P scores
-  int* tpa = (int*)(tpv + P * kWave);          // [P][64] top-P addresses
-  float* trv = (float*)(tpa + P * kWave);      // [R][64] top-R scores
-  int* tri = (int*)(trv + R * kWave);          // [R][64] top-R blocks
+__global__ __launch_bounds__(kProbeThreads) void k_probe_rerank(
+    const T* __restrict__ Q, const float* __restrict__ cb, const float* __restrict__ bias,
+    const float* __restrict__ ksum, const int32_t* __restrict__ off, const int32_t* __restrict__ idx,
+    const int32_t* __restrict__ force, int32_t* __restrict__ sel, int32_t* __restrict__ ncand,
+    int32_t* __restrict__ cellcnt, int32_t* __restrict__ bins, Shape s) {
+  constexpr int NT = kProbeThreads;
+  extern __shared__ __align__(16) float smem[];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int bh = blockIdx.y, h = bh % s.H;
-  const int t = blockIdx.x * kWave + lane;
+  const int tbase = blockIdx.x * NT;
+  const int t = tbase + tid;
+  const int C = s.C, G = s.G, P = s.P, R = s.R, A = s.A;
+  const int CP = (C + 15) & ~15;
+  const int MST = G * CP + 4;
+  const int Pg = min(P, C);
+  float* mu = smem;                                  // [NT][MST]
+  int* tcode = (int*)(mu + NT * MST);                // [G*Pg][NT]
+  float* tpv = (float*)(tcode + G * Pg * NT);        // [P][NT]
+  int* tpa = (int*)(tpv + P * NT);                   // [P][NT]
+  float* trv = (float*)(tpa + P * NT);               // [R][NT]
+  int* tri = (int*)(trv + R * NT);                   // [R][NT]
+  int* csr = tri + R * NT;                           // off [A+1], idx [ne] when staged
+  const int32_t* offp = off + (size_t)bh * (A + 1);
+  const int32_t* idxp = idx + (size_t)bh * s.nb;
+  if (s.csr_lds) {
+    for (int k = tid; k <= A; k += NT) csr[k] = offp[k];
+    for (int k = tid; k < s.ne; k += NT) csr[A + 1 + k] = idxp[k];
+    offp = csr;
+    idxp = csr + A + 1;
+  }
+
+  // ---- mu on MFMA.  Lane l supplies Q[token 16tt + l%16][d] and W[code 16ct + l%16][d] for
+  // d = (l/16)(D/4) + kk (a fixed permutation of the contraction index) and receives
+  // mu[token 16tt + 4(l/16) + k][code 16ct + l%16].
+  {
+    const int r16 = lane & 15, s4 = lane >> 4;
+    float qa[4][D / 4];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      if (wave * 64 + tt * 16 >= NT) break;
+      int tq = tbase + wave * 64 + tt * 16 + r16;
+      tq = tq < s.S ? tq : s.S - 1;
+      const T* qp = Q + ((size_t)bh * s.S + tq) * D + s4 * (D / 4);
+      constexpr int VEC = Vec16<T>::n;
+#pragma unroll
+      for (int c = 0; c < D / 4 / VEC; ++c) {
+        typename Vec16<T>::type v = *(const typename Vec16<T>::type*)(qp + c * VEC);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) qa[tt][c * VEC + e] = to_f(v[e]);
+      }
+    }
+    const float* cbh = cb + (size_t)h * G * C * D;
+    for (int g = 0; g < G; ++g) {
+      for (int ct = 0; ct < CP / 16; ++ct) {
+        const int code = ct * 16 + r16;
+        float wb[D / 4];
+        if (code < C) {
+          const float4* wp = (const float4*)(cbh + ((size_t)g * C + code) * D + s4 * (D / 4));
+#pragma unroll
+          for (int c = 0; c < D / 16; ++c) {
+            const float4 v = wp[c];
+            wb[4 * c] = v.x;
+            wb[4 * c + 1] = v.y;
+            wb[4 * c + 2] = v.z;
+            wb[4 * c + 3] = v.w;
+          }
+        } else {
+#pragma unroll
+          for (int c = 0; c < D / 4; ++c) wb[c] = 0.f;
+        }
+        const float bv = (bias && code < C) ? bias[(h * G + g) * C + code] : 0.f;
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+          if (wave * 64 + tt * 16 >= NT) break;
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kk = 0; kk < D / 4; ++kk)
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[tt][kk], wb[kk], acc, 0, 0, 0);
+#pragma unroll
+          for (int k = 0; k < 4; ++k)
+            mu[(wave * 64 + tt * 16 + 4 * s4 + k) * MST + g * CP + code] = acc[k] + bv;
+        }
+      }
+    }
+  }
+  __syncthreads();
   if (t >= s.S) return;  // no barriers below
   const int j = t / s.blk;
   const int cutoff = j - s.L;
+  const float* mrow = mu + tid * MST;
 
-  float qv[D];
-  {
-    const T* qp = Q + ((size_t)bh * s.S + t) * D;
-    constexpr int VEC = Vec16<T>::n;
-#pragma unroll
-    for (int c = 0; c < D / VEC; ++c) {
-      typename Vec16<T>::type v = *(const typename Vec16<T>::type*)(qp + c * VEC);
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) qv[c * VEC + e] = to_f(v[e]);
-    }
-  }
-  const float* cbh = cb + (size_t)h * GC * D;
-  for (int gc = 0; gc < GC; ++gc) {
-    const float* w = cbh + (size_t)gc * D;
-    float acc = 0.f;
-#pragma unroll
-    for (int d = 0; d < D; ++d) acc = fmaf(w[d], qv[d], acc);
-    if (bias) acc += bias[h * GC + gc];
-    mu[gc * kWave + lane] = acc;
-  }
-  // top-min(P, C) codes of every subspace, by (mu desc, code asc)
-  const int Pg = min(P, C);
+  // ---- top-min(P, C) codes of every subspace, by (mu desc, code asc)
   for (int g = 0; g < G; ++g) {
     float pv = FLT_MAX;
     int pc = -1;
-    bool first = true;
     for (int p = 0; p < Pg; ++p) {
       int bc = -1;
       float bv = -FLT_MAX;
       for (int c = 0; c < C; ++c) {
-        const float v = mu[(g * C + c) * kWave + lane];
-        const bool after = first || (v < pv) || (v == pv && c > pc);
+        const float v = mrow[g * CP + c];
+        const bool after = (v < pv) || (v == pv && c > pc);
         if (after && (bc < 0 || v > bv)) {
           bc = c;
           bv = v;
         }
       }
-      tc[(g * P + p) * kWave + lane] = bc;
+      tcode[(g * Pg + p) * NT + tid] = bc;
       pv = bv;
       pc = bc;
-      first = false;
     }
   }
-  // score the Pg^G code combinations, keep the top-P addresses
+  // ---- score the rank vectors with prod (k_g + 1) <= P, keep the top-P addresses
   int ncomb = 1;
   for (int g = 0; g < G; ++g) ncomb *= Pg;
   int np = 0;
   for (int kc = 0; kc < ncomb; ++kc) {
-    int code[kMaxSubspaces];
-    int rem = kc;
+    int rk[kMaxSubspaces];
+    int rem = kc, prod = 1;
 #pragma unroll
     for (int g = kMaxSubspaces - 1; g >= 0; --g) {
       if (g < G) {
-        code[g] = tc[(g * P + rem % Pg) * kWave + lane];
+        rk[g] = rem % Pg;
         rem /= Pg;
+        prod *= rk[g] + 1;
       }
     }
-    float sig = mu[code[0] * kWave + lane];
-    int a = code[0];
+    if (prod > P) continue;
+    int c0 = tcode[rk[0] * NT + tid];
+    float sig = mrow[c0];
+    int a = c0;
 #pragma unroll
     for (int g = 1; g < kMaxSubspaces; ++g) {
       if (g < G) {
-        sig += mu[(g * C + code[g]) * kWave + lane];
-        a = a * C + code[g];
+        const int cg = tcode[(g * Pg + rk[g]) * NT + tid];
+        sig += mrow[g * CP + cg];
+        a = a * C + cg;
       }
     }
     int pos;
     if (np == P) {
-      const float wv = tpv[(P - 1) * kWave + lane];
-      const int wa = tpa[(P - 1) * kWave + lane];
+      const float wv = tpv[(P - 1) * NT + tid];
+      const int wa = tpa[(P - 1) * NT + tid];
       if (!(sig > wv || (sig == wv && a < wa))) continue;
       pos = P - 1;
     } else {
       pos = np++;
     }
     while (pos > 0) {
-      const float pvv = tpv[(pos - 1) * kWave + lane];
-      const int pa = tpa[(pos - 1) * kWave + lane];
+      const float pvv = tpv[(pos - 1) * NT + tid];
+      const int pa = tpa[(pos - 1) * NT + tid];
       if (!(sig > pvv || (sig == pvv && a < pa))) break;
-      tpv[pos * kWave + lane] = pvv;
-      tpa[pos * kWave + lane] = pa;
+      tpv[pos * NT + tid] = pvv;
+      tpa[pos * NT + tid] = pa;
       --pos;
     }
-    tpv[pos * kWave + lane] = sig;
-    tpa[pos * kWave + lane] = a;
+    tpv[pos * NT + tid] = sig;
+    tpa[pos * NT + tid] = a;
   }
-  // candidates in probe rank order, rerank by <q_t, summary>
+
+  // ---- candidates in probe rank order, rerank by <q_t, summary>
   int nc = 0, nr = 0;
   if (cutoff >= 0 && R > 0) {
-    const int32_t* offh = off + (size_t)bh * (s.A + 1);
-    const int32_t* idxh = idx + (size_t)bh * s.nb;
+    float qv[D];
+    {
+      const T* qp = Q + ((size_t)bh * s.S + t) * D;
+      constexpr int VEC = Vec16<T>::n;
+#pragma unroll
+      for (int c = 0; c < D / VEC; ++c) {
+        typename Vec16<T>::type v = *(const typename Vec16<T>::type*)(qp + c * VEC);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) qv[c * VEC + e] = to_f(v[e]);
+      }
+    }
     const float* ksh = ksum + (size_t)bh * s.nb * D;
     for (int p = 0; p < np && nc < s.M; ++p) {
-      const int a = tpa[p * kWave + lane];
-      const int lo = offh[a], hi = offh[a + 1];
+      const int a = tpa[p * NT + tid];
+      const int lo = offp[a], hi = offp[a + 1];
       int l0 = lo, l1 = hi;  // first entry > cutoff
       while (l0 < l1) {
         const int mid = (l0 + l1) >> 1;
-        if (idxh[mid] <= cutoff)
+        if (idxp[mid] <= cutoff)
           l0 = mid + 1;
         else
           l1 = mid;
       }
-      const int take = min(s.cap, l0 - lo);
-      for (int e = 0; e < take && nc < s.M; ++e) {
-        const int i = idxh[l0 - 1 - e];
+      const int take = min(min(s.cap, l0 - lo), s.M - nc);
+      for (int e = 0; e < take; ++e) {
+        const int i = idxp[l0 - 1 - e];
         ++nc;
         const float4* kr = (const float4*)(ksh + (size_t)i * D);
         float rho = 0.f;
@@ -356,23 +408,23 @@ __global__ __launch_bounds__(64) void k_probe_rerank(const T* __restrict__ Q, co
         }
         int pos;
         if (nr == R) {
-          const float wv = trv[(R - 1) * kWave + lane];
-          const int wi = tri[(R - 1) * kWave + lane];
+          const float wv = trv[(R - 1) * NT + tid];
+          const int wi = tri[(R - 1) * NT + tid];
           if (!(rho > wv || (rho == wv && i < wi))) continue;
           pos = R - 1;
         } else {
           pos = nr++;
         }
         while (pos > 0) {
-          const float pvv = trv[(pos - 1) * kWave + lane];
-          const int pi = tri[(pos - 1) * kWave + lane];
+          const float pvv = trv[(pos - 1) * NT + tid];
+          const int pi = tri[(pos - 1) * NT + tid];
           if (!(rho > pvv || (rho == pvv && i < pi))) break;
-          trv[pos * kWave + lane] = pvv;
-          tri[pos * kWave + lane] = pi;
+          trv[pos * NT + tid] = pvv;
+          tri[pos * NT + tid] = pi;
           --pos;
         }
-        trv[pos * kWave + lane] = rho;
-        tri[pos * kWave + lane] = i;
+        trv[pos * NT + tid] = rho;
+        tri[pos * NT + tid] = i;
       }
     }
   }
@@ -380,25 +432,270 @@ __global__ __launch_bounds__(64) void k_probe_rerank(const T* __restrict__ Q, co
     const int f = force[(size_t)bh * s.S + t];
     if (f >= 0 && f <= cutoff) {
       bool present = false;
-      for (int r = 0; r < nr; ++r) present |= (tri[r * kWave + lane] == f);
+      for (int r = 0; r < nr; ++r) present |= (tri[r * NT + tid] == f);
       if (!present) {
         if (nr < R)
-          tri[(nr++) * kWave + lane] = f;
+          tri[(nr++) * NT + tid] = f;
         else
-          tri[(R - 1) * kWave + lane] = f;
+          tri[(R - 1) * NT + tid] = f;
       }
     }
   }
   int32_t* srow = sel + ((size_t)bh * s.S + t) * R;
-  for (int r = 0; r < R; ++r) srow[r] = r < nr ? tri[r * kWave + lane] : -1;
+  for (int r = 0; r < R; ++r) srow[r] = r < nr ? tri[r * NT + tid] : -1;
+  if (ncand) ncand[(size_t)bh * s.S + t] = nc;
+  if (bins)
+    for (int r = 0; r < nr; ++r) record_pair(cellcnt, bins, s, bh, tri[r * NT + tid], j, t, r);
+}
+
+// ---------------------------------------------------------------------------------------------
+// The same probe + rerank with the routing sizes fixed at compile time (G subspaces of C codes,
+// P probes, R remote blocks): every per-token list lives in registers, rank vectors are
+// enumerated at compile time, and the top-P / top-R lists are kept sorted by an unrolled
+// insertion network.  Semantics are identical to k_probe_rerank.
+template <int K>
+__device__ inline void insert_sorted(float (&v)[K], int (&id)[K], float x, int a) {
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    const bool better = x > v[k] || (x == v[k] && a < id[k]);
+    const float tv = v[k];
+    const int ta = id[k];
+    v[k] = better ? x : tv;
+    id[k] = better ? a : ta;
+    x = better ? tv : x;
+    a = better ? ta : a;
+  }
+}
+
+template <int G, int PG>
+struct RankSpace {
+  static constexpr int count() {
+    int n = 1;
+    for (int g = 0; g < G; ++g) n *= PG;
+    return n;
+  }
+};
+
+template <typename T, int D, int G, int C, int P, int R>
+__global__ __launch_bounds__(kProbeThreads) void k_probe_fixed(
+    const T* __restrict__ Q, const float* __restrict__ cb, const float* __restrict__ bias,
+    const float* __restrict__ ksum, const int32_t* __restrict__ off, const int32_t* __restrict__ idx,
+    const int32_t* __restrict__ force, int32_t* __restrict__ sel, int32_t* __restrict__ ncand,
+    int32_t* __restrict__ cellcnt, int32_t* __restrict__ bins, Shape s) {
+  constexpr int NT = kProbeThreads;
+  constexpr int CP = (C + 15) & ~15;
+  constexpr int MST = G * CP + 1;  // odd stride: each lane's row starts in its own bank
+  constexpr int PG = P < C ? P : C;
+  extern __shared__ __align__(16) float smem[];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int bh = blockIdx.y, h = bh % s.H;
+  const int tbase = blockIdx.x * NT;
+  const int t = tbase + tid;
+  const int A = s.A;
+  float* mu = smem;                   // [NT][MST]
+  int* csr = (int*)(mu + NT * MST);   // off [A+1], idx [ne] when staged
+  const int32_t* offp = off + (size_t)bh * (A + 1);
+  const int32_t* idxp = idx + (size_t)bh * s.nb;
+  if (s.csr_lds) {
+    for (int k = tid; k <= A; k += NT) csr[k] = offp[k];
+    for (int k = tid; k < s.ne; k += NT) csr[A + 1 + k] = idxp[k];
+    offp = csr;
+    idxp = csr + A + 1;
+  }
+  // ---- mu on MFMA (same lane layout as k_probe_rerank)
+  {
+    const int r16 = lane & 15, s4 = lane >> 4;
+    const float* cbh = cb + (size_t)h * G * C * D;
+    float wb[G][CP / 16][D / 4];
+    float bv[G][CP / 16];
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int ct = 0; ct < CP / 16; ++ct) {
+        const int code = ct * 16 + r16;
+        if (code < C) {
+          const float4* wp = (const float4*)(cbh + ((size_t)g * C + code) * D + s4 * (D / 4));
+#pragma unroll
+          for (int c = 0; c < D / 16; ++c) {
+            const float4 v = wp[c];
+            wb[g][ct][4 * c] = v.x;
+            wb[g][ct][4 * c + 1] = v.y;
+            wb[g][ct][4 * c + 2] = v.z;
+            wb[g][ct][4 * c + 3] = v.w;
+          }
+        } else {
+#pragma unroll
+          for (int c = 0; c < D / 4; ++c) wb[g][ct][c] = 0.f;
+        }
+        bv[g][ct] = (bias && code < C) ? bias[(h * G + g) * C + code] : 0.f;
+      }
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      if (wave * 64 + tt * 16 >= NT) break;
+      int tq = tbase + wave * 64 + tt * 16 + r16;
+      tq = tq < s.S ? tq : s.S - 1;
+      float qa[D / 4];
+      const T* qp = Q + ((size_t)bh * s.S + tq) * D + s4 * (D / 4);
+      constexpr int VEC = Vec16<T>::n;
+#pragma unroll
+      for (int c = 0; c < D / 4 / VEC; ++c) {
+        typename Vec16<T>::type v = *(const typename Vec16<T>::type*)(qp + c * VEC);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) qa[c * VEC + e] = to_f(v[e]);
+      }
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int ct = 0; ct < CP / 16; ++ct) {
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kk = 0; kk < D / 4; ++kk)
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[kk], wb[g][ct][kk], acc, 0, 0, 0);
+#pragma unroll
+          for (int k = 0; k < 4; ++k)
+            mu[(wave * 64 + tt * 16 + 4 * s4 + k) * MST + g * CP + ct * 16 + r16] = acc[k] + bv[g][ct];
+        }
+    }
+  }
+  __syncthreads();
+  if (t >= s.S) return;  // no barriers below
+  const int j = t / s.blk;
+  const int cutoff = j - s.L;
+  const float* mrow = mu + tid * MST;
+
+  // ---- top-PG codes of every subspace by (mu desc, code asc)
+  int tcode[G][PG];
+  float tval[G][PG];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    float m[C];
+#pragma unroll
+    for (int c = 0; c < C; ++c) m[c] = mrow[g * CP + c];
+    float pv = FLT_MAX;
+    int pc = -1;
+#pragma unroll
+    for (int p = 0; p < PG; ++p) {
+      int bc = -1;
+      float bvv = -FLT_MAX;
+#pragma unroll
+      for (int c = 0; c < C; ++c) {
+        const bool after = (m[c] < pv) || (m[c] == pv && c > pc);
+        const bool take = after && (bc < 0 || m[c] > bvv);
+        bc = take ? c : bc;
+        bvv = take ? m[c] : bvv;
+      }
+      tcode[g][p] = bc;
+      tval[g][p] = bvv;
+      pv = bvv;
+      pc = bc;
+    }
+  }
+  // ---- rank vectors with prod (k_g + 1) <= P, top-P addresses
+  float tpv[P];
+  int tpa[P];
+#pragma unroll
+  for (int p = 0; p < P; ++p) {
+    tpv[p] = -INFINITY;
+    tpa[p] = 0x7fffffff;
+  }
+  constexpr int NCOMB = RankSpace<G, PG>::count();
+#pragma unroll
+  for (int kc = 0; kc < NCOMB; ++kc) {
+    int rem = kc, prod = 1;
+    int rk[G];
+#pragma unroll
+    for (int g = G - 1; g >= 0; --g) {
+      rk[g] = rem % PG;
+      rem /= PG;
+      prod *= rk[g] + 1;
+    }
+    if (prod <= P) {
+      float sig = tval[0][rk[0]];
+      int a = tcode[0][rk[0]];
+#pragma unroll
+      for (int g = 1; g < G; ++g) {
+        sig += tval[g][rk[g]];
+        a = a * C + tcode[g][rk[g]];
+      }
+      insert_sorted<P>(tpv, tpa, sig, a);
+    }
+  }
+  // ---- candidates in probe rank order, rerank by <q_t, summary>
+  float trv[R > 0 ? R : 1];
+  int tri[R > 0 ? R : 1];
+#pragma unroll
+  for (int r = 0; r < (R > 0 ? R : 1); ++r) {
+    trv[r] = -INFINITY;
+    tri[r] = 0x7fffffff;
+  }
+  int nc = 0;
+  if (cutoff >= 0 && R > 0) {
+    float qv[D];
+    {
+      const T* qp = Q + ((size_t)bh * s.S + t) * D;
+      constexpr int VEC = Vec16<T>::n;
+#pragma unroll
+      for (int c = 0; c < D / VEC; ++c) {
+        typename Vec16<T>::type v = *(const typename Vec16<T>::type*)(qp + c * VEC);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) qv[c * VEC + e] = to_f(v[e]);
+      }
+    }
+    const float* ksh = ksum + (size_t)bh * s.nb * D;
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      const int a = tpa[p];
+      const int lo = offp[a], hi = offp[a + 1];
+      int l0 = lo, l1 = hi;  // first entry > cutoff
+      while (l0 < l1) {
+        const int mid = (l0 + l1) >> 1;
+        if (idxp[mid] <= cutoff)
+          l0 = mid + 1;
+        else
+          l1 = mid;
+      }
+      const int take = min(min(s.cap, l0 - lo), s.M - nc);
+      for (int e = 0; e < take; ++e) {
+        const int i = idxp[l0 - 1 - e];
+        const float4* kr = (const float4*)(ksh + (size_t)i * D);
+        float rho = 0.f;
+#pragma unroll
+        for (int c = 0; c < D / 4; ++c) {
+          const float4 kv = kr[c];
+          rho = fmaf(kv.x, qv[4 * c + 0], rho);
+          rho = fmaf(kv.y, qv[4 * c + 1], rho);
+          rho = fmaf(kv.z, qv[4 * c + 2], rho);
+          rho = fmaf(kv.w, qv[4 * c + 3], rho);
+        }
+        insert_sorted<(R > 0 ? R : 1)>(trv, tri, rho, i);
+      }
+      nc += take > 0 ? take : 0;
+    }
+  }
+  int nr = nc < R ? nc : R;
+  if (force && R > 0) {
+    const int f = force[(size_t)bh * s.S + t];
+    if (f >= 0 && f <= cutoff) {
+      bool present = false;
+#pragma unroll
+      for (int r = 0; r < (R > 0 ? R : 1); ++r) present |= (r < nr && tri[r] == f);
+      if (!present) {
+        const int slot = nr < R ? nr : R - 1;
+#pragma unroll
+        for (int r = 0; r < (R > 0 ? R : 1); ++r)
+          if (r == slot) tri[r] = f;
+        nr = nr < R ? nr + 1 : R;
+      }
+    }
+  }
+  int32_t* srow = sel + ((size_t)bh * s.S + t) * R;
+#pragma unroll
+  for (int r = 0; r < R; ++r) srow[r] = r < nr ? tri[r] : -1;
   if (ncand) ncand[(size_t)bh * s.S + t] = nc;
   if (bins) {
-    for (int r = 0; r < nr; ++r) {
-      const int i = tri[r * kWave + lane];
-      const int pos = atomicAdd(&cnt[(size_t)bh * s.nb + i], 1);
-      if (pos < (s.nb - s.L - i) * s.blk)
-        bins[(size_t)bh * s.bins_per_bh + bin_offset(i, s.nb, s.L, s.blk) + pos] = t * R + r;
-    }
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      if (r < nr) record_pair(cellcnt, bins, s, bh, tri[r], j, t, r);
   }
 }
 
@@ -422,27 +719,66 @@ hipError_t address_dispatch(const Shape& s, const void* k, const float* cb, cons
   return hipGetLastError();
 }
 
+template <typename T, int D, int G, int C, int P, int R>
+hipError_t probe_fixed_launch(const Shape& s, const void* q, const float* cb, const float* bias, const float* ksum,
+                              const int32_t* off, const int32_t* idx, const int32_t* force, int32_t* sel,
+                              int32_t* ncand, int32_t* cellcnt, int32_t* bins, hipStream_t st) {
+  dim3 grid((s.S + kProbeThreads - 1) / kProbeThreads, s.B * s.H);
+  const size_t lds = probe_lds_bytes(s);
+  if (lds > 65536) {
+    hipError_t e = hipFuncSetAttribute((const void*)k_probe_fixed<T, D, G, C, P, R>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((k_probe_fixed<T, D, G, C, P, R>), grid, dim3(kProbeThreads), lds, st, (const T*)q, cb, bias,
+                     ksum, off, idx, force, sel, ncand, cellcnt, bins, s);
+  return hipGetLastError();
+}
+
+// Shapes with a compile-time specialisation (the five workload families); others use k_probe_rerank.
+#define MDR_PROBE_FIXED_SHAPES(X) \
+  X(bf16, 64, 2, 16, 4, 2)        \
+  X(bf16, 128, 2, 32, 4, 4)       \
+  X(bf16, 128, 3, 8, 6, 8)        \
+  X(float, 64, 2, 8, 16, 2)       \
+  X(float, 32, 2, 4, 2, 2)
+
 template <typename T>
 hipError_t probe_dispatch(const Shape& s, const void* q, const float* cb, const float* bias, const float* ksum,
                           const int32_t* off, const int32_t* idx, const int32_t* force, int32_t* sel,
-                          int32_t* ncand, int32_t* cnt, int32_t* bins, hipStream_t st) {
-  dim3 grid((s.S + kWave - 1) / kWave, s.B * s.H);
-  const size_t lds = (size_t)(s.G * s.C + s.G * s.P + 2 * s.P + 2 * s.R) * kWave * 4;
+                          int32_t* ncand, int32_t* cellcnt, int32_t* bins, hipStream_t st) {
+#define MDR_FIXED(TT, DD, GG, CC, PP, RR)                                                                        \
+  if (std::is_same<T, TT>::value && s.D == DD && s.G == GG && s.C == CC && s.P == PP && s.R == RR && s.fixed_probe) \
+    return probe_fixed_launch<TT, DD, GG, CC, PP, RR>(s, q, cb, bias, ksum, off, idx, force, sel, ncand, cellcnt, \
+                                                      bins, st);
+  MDR_PROBE_FIXED_SHAPES(MDR_FIXED)
+#undef MDR_FIXED
+  dim3 grid((s.S + kProbeThreads - 1) / kProbeThreads, s.B * s.H);
+  const size_t lds = probe_lds_bytes(s);
+  const void* fn = nullptr;
+  switch (s.D) {
+    case 32: fn = (const void*)k_probe_rerank<T, 32>; break;
+    case 64: fn = (const void*)k_probe_rerank<T, 64>; break;
+    case 128: fn = (const void*)k_probe_rerank<T, 128>; break;
+    default: return hipErrorInvalidValue;
+  }
+  if (lds > 65536) {
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
   switch (s.D) {
     case 32:
-      hipLaunchKernelGGL((k_probe_rerank<T, 32>), grid, dim3(kWave), lds, st, (const T*)q, cb, bias, ksum, off,
-                         idx, force, sel, ncand, cnt, bins, s);
+      hipLaunchKernelGGL((k_probe_rerank<T, 32>), grid, dim3(kProbeThreads), lds, st, (const T*)q, cb, bias, ksum,
+                         off, idx, force, sel, ncand, cellcnt, bins, s);
       break;
     case 64:
-      hipLaunchKernelGGL((k_probe_rerank<T, 64>), grid, dim3(kWave), lds, st, (const T*)q, cb, bias, ksum, off,
-                         idx, force, sel, ncand, cnt, bins, s);
-      break;
-    case 128:
-      hipLaunchKernelGGL((k_probe_rerank<T, 128>), grid, dim3(kWave), lds, st, (const T*)q, cb, bias, ksum, off,
-                         idx, force, sel, ncand, cnt, bins, s);
+      hipLaunchKernelGGL((k_probe_rerank<T, 64>), grid, dim3(kProbeThreads), lds, st, (const T*)q, cb, bias, ksum,
+                         off, idx, force, sel, ncand, cellcnt, bins, s);
       break;
     default:
-      return hipErrorInvalidValue;
+      hipLaunchKernelGGL((k_probe_rerank<T, 128>), grid, dim3(kProbeThreads), lds, st, (const T*)q, cb, bias,
+                         ksum, off, idx, force, sel, ncand, cellcnt, bins, s);
+      break;
   }
   return hipGetLastError();
 }
@@ -450,9 +786,28 @@ hipError_t probe_dispatch(const Shape& s, const void* q, const float* cb, const 
 }  // namespace
 
 hipError_t launch_address(const Shape& s, const void* k, const float* codebook, const float* bias, float* ksum,
-                          int32_t* addr, int32_t* cnt_zero, hipStream_t st) {
-  if (s.dtype == MDR_BF16) return address_dispatch<bf16>(s, k, codebook, bias, ksum, addr, cnt_zero, st);
-  return address_dispatch<float>(s, k, codebook, bias, ksum, addr, cnt_zero, st);
+                          int32_t* addr, int32_t* cell_zero, hipStream_t st) {
+  if (s.dtype == MDR_BF16) return address_dispatch<bf16>(s, k, codebook, bias, ksum, addr, cell_zero, st);
+  return address_dispatch<float>(s, k, codebook, bias, ksum, addr, cell_zero, st);
+}
+
+bool probe_fixed_shape(const Shape& s) {
+  const bool bf = s.dtype == MDR_BF16;
+#define MDR_MATCH(TT, DD, GG, CC, PP, RR)                                                                  \
+  if ((std::is_same<TT, bf16>::value == bf) && s.D == DD && s.G == GG && s.C == CC && s.P == PP && s.R == RR) \
+    return true;
+  MDR_PROBE_FIXED_SHAPES(MDR_MATCH)
+#undef MDR_MATCH
+  return false;
+}
+
+size_t probe_lds_bytes(const Shape& s) {
+  const int CP = (s.C + 15) & ~15;
+  if (s.fixed_probe) return ((size_t)kProbeThreads * (s.G * CP + 1) + (s.csr_lds ? (size_t)(s.A + 1 + s.ne) : 0)) * 4;
+  const int Pg = s.P < s.C ? s.P : s.C;
+  const size_t words = (size_t)kProbeThreads * (s.G * CP + 4) + (size_t)kProbeThreads * (s.G * Pg + 2 * s.P + 2 * s.R) +
+                       (s.csr_lds ? (size_t)(s.A + 1 + s.ne) : 0);
+  return words * 4;
 }
 
 hipError_t launch_post(const Shape& s, const int32_t* addr, int32_t* off, int32_t* idx, int32_t* overflow,
@@ -463,10 +818,10 @@ hipError_t launch_post(const Shape& s, const int32_t* addr, int32_t* off, int32_
 
 hipError_t launch_probe_rerank(const Shape& s, const void* q, const float* codebook, const float* bias,
                                const float* ksum, const int32_t* off, const int32_t* idx, const int32_t* force,
-                               int32_t* sel, int32_t* ncand, int32_t* cnt, int32_t* bins, hipStream_t st) {
+                               int32_t* sel, int32_t* ncand, int32_t* cellcnt, int32_t* bins, hipStream_t st) {
   if (s.dtype == MDR_BF16)
-    return probe_dispatch<bf16>(s, q, codebook, bias, ksum, off, idx, force, sel, ncand, cnt, bins, st);
-  return probe_dispatch<float>(s, q, codebook, bias, ksum, off, idx, force, sel, ncand, cnt, bins, st);
+    return probe_dispatch<bf16>(s, q, codebook, bias, ksum, off, idx, force, sel, ncand, cellcnt, bins, st);
+  return probe_dispatch<float>(s, q, codebook, bias, ksum, off, idx, force, sel, ncand, cellcnt, bins, st);
 }
 
 }  // namespace mdr

@@ -14,9 +14,9 @@ LIB = os.path.join(ROOT, "learned_product_hash_amd", "libmdr.so")
 
 def _ensure_built():
     if not os.path.exists(LIB):
-        from learned_product_hash_amd.build import build
+        import __graft_entry__
 
-        build()
+        __graft_entry__.build()
 
 
 @pytest.fixture(scope="module")

@@ -296,3 +296,25 @@ def test_full_size_sampled(gpu_lib, name):
     print(f"{name} full size: overflow total {int(res['overflow'].sum())}, "
           f"R_eff {float((res['sel'] >= 0).sum(-1).mean()):.3f}, sampled max abs err {err:.3g}")
     assert err <= TOL[w.dtype]
+
+
+@pytest.mark.parametrize("name,over", [("sweep", dict(probes=3)), ("long", dict(remote=3)),
+                                       ("skew", dict(probes=5, remote=7)), ("recall", dict(codes=6, probes=11)),
+                                       ("tiny", dict(subspaces=1, codes=8, probes=3))])
+def test_generic_probe_kernel(gpu_lib, name, over):
+    """Routing sizes outside the compile-time specialisations run the generic probe kernel."""
+    mdr = gpu_lib
+    w = small(name, **over)
+    inp = synth.make_core_inputs(dataclass_replace_plant(w) if w.plant == "recall" else w, 8)
+    res = run_core(mdr, w, inp)
+    near = 0
+    for b in range(w.batch):
+        for h in range(w.heads):
+            if compare_addresses(w, inp, res["addr"][b, h], b, h):
+                continue
+            r = oracle.route_head(inp["q"][b, h], inp["k"][b, h], inp["codebook"][h],
+                                  None if inp["bias"] is None else inp["bias"][h], w)
+            near += compare_selection(r, res["sel"][b, h])
+            ref = attention_rows(w, inp, res["sel"][b, h], b, h, None, dense=w.seq <= 4096)
+            assert np.abs(res["out"][b, h] - ref).max() <= TOL[w.dtype]
+    print(f"{name} {over}: selection near-ties {near}")
