@@ -66,6 +66,8 @@ def parse(argv=None):
                     help="run one elementwise copy of 512 MiB first (counter calibration)")
     ap.add_argument("--cpu-heads", type=int, default=4)
     ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
+    ap.add_argument("--summarize-rocprof", nargs=2, metavar=("KERNEL_STATS_CSV", "COMMAND"),
+                    help="write profiles/routed_attention_kernels_<workload>.md from a rocprofv3 --stats CSV")
     return ap.parse_args(argv)
 
 
@@ -365,11 +367,34 @@ def ingest_pmc(fetch_csv, write_csv, w):
 
 # ----------------------------------------------------------------------------- main
 
+def summarize_rocprof(stats_csv, command, w):
+    """Short markdown table of the library's kernels from a rocprofv3 kernel_stats.csv."""
+    rows = list(csv.DictReader(open(stats_csv)))
+    lines = [f"# rocprofv3 kernel statistics: routed attention, {describe(w)}", "",
+             "Command (run from the repository root on one MI355X):", "", f"    {command}", "",
+             "| kernel | calls | avg us | min us | max us | share of GPU time |", "|---|---|---|---|---|---|"]
+    for k, sym in KERNEL_SYMBOL.items():
+        for r in rows:
+            if sym in r["Name"]:
+                lines.append(f"| {k} (`{sym}`) | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                             f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                             f"{float(r['Percentage']):.1f}% |")
+    other = sum(float(r["Percentage"]) for r in rows if not any(sym in r["Name"] for sym in KERNEL_SYMBOL.values()))
+    lines += ["", f"Other kernels (input generation, torch copies, routing statistics): {other:.1f}% of GPU time.", ""]
+    out = os.path.join(ROOT, "profiles", f"routed_attention_kernels_{w.name}_{w.seq // 1024}k.md")
+    os.makedirs(os.path.dirname(out), exist_ok=True)
+    open(out, "w").write("\n".join(lines))
+    print(open(out).read())
+
+
 def main(argv=None):
     a = parse(argv)
     w = make_workload(a.workload, a.seq)
     if a.ingest_pmc:
         ingest_pmc(*a.ingest_pmc, w)
+        return 0
+    if a.summarize_rocprof:
+        summarize_rocprof(*a.summarize_rocprof, w)
         return 0
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print(json.dumps({"error": "this build runs on one GPU only: the path shards over (batch, head) with no "
