@@ -48,8 +48,10 @@ mdr_status shape_from_config(const mdr_config* cfg, bool mixer, Shape* out) {
   s.A = (int)A;
   s.cap = c.capacity;
   s.P = c.probes;
-  long long M = c.max_cand > 0 ? (long long)c.max_cand : (long long)c.probes * c.capacity;
-  s.M = (int)(M > (1LL << 30) ? (1LL << 30) : M);
+  // at most probes * capacity candidates can exist, so a larger cut changes nothing
+  const long long pc = (long long)c.probes * c.capacity;
+  long long M = c.max_cand > 0 && c.max_cand < pc ? (long long)c.max_cand : pc;
+  s.M = (int)(M > (1LL << 20) ? (1LL << 20) : M);
   s.R = c.remote;
   s.L = c.local;
   s.dtype = c.dtype;
@@ -58,9 +60,9 @@ mdr_status shape_from_config(const mdr_config* cfg, bool mixer, Shape* out) {
   const long long ne = nb > c.local ? nb - c.local : 0;
   s.ne = (int)ne;
   s.cells_per_bh = ne * (ne + 1) / 2;
-  // split heavy blocks over several remote work-groups: about two chunks of 64 pairs each
-  const long long avg_chunks = ne > 0 ? ((long long)c.seq * c.remote / ne + kPairsPerChunk - 1) / kPairsPerChunk : 0;
-  long long split = avg_chunks / 2;
+  // split heavy blocks over several remote work-groups when blocks average several iterations
+  const long long avg_pairs = ne > 0 ? (long long)c.seq * c.remote / ne : 0;
+  long long split = avg_pairs / 512;
   s.split = (int)(split < 1 ? 1 : split > 8 ? 8 : split);
   s.csr_lds = ((long long)s.A + 1 + ne) * 4 <= 16384;
   s.fixed_probe = probe_fixed_shape(s);

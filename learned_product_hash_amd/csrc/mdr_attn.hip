@@ -42,9 +42,9 @@ template <typename T, int D, int BLK>
 struct Tile {
   static constexpr bool bf = std::is_same<T, bf16>::value;
   static constexpr int KST = bf ? D + 8 : D + 4;     // K rows in LDS (elements)
-  static constexpr int VST = bf ? BLK + 8 : D + 4;   // bf16: V^T rows [D][VST]; f32: V rows [BLK][VST]
+  static constexpr int VST = KST;                    // V rows in LDS (elements), row-major like K
   static constexpr int K_ELEMS = BLK * KST;
-  static constexpr int V_ELEMS = bf ? D * VST : BLK * VST;
+  static constexpr int V_ELEMS = BLK * VST;
   static constexpr int NQF = bf ? D / 32 : D / 4;    // query operand registers
   static constexpr int NT = BLK / 16;                // 16-key sub-tiles
   static constexpr int ND = D / 16;                  // 16-wide d tiles
@@ -82,7 +82,7 @@ __device__ inline void load_q(QFrag<T, D>& qf, const T* qp, int lane) {
   }
 }
 
-// Stage one block of K (row-major) and V (transposed for bf16) into LDS.
+// Stage one block of K and V into LDS, row-major, with 16-byte copies.
 template <typename T, int D, int BLK, int NTHR>
 __device__ inline void load_kv(const T* __restrict__ Kg, const T* __restrict__ Vg, T* Ks, T* Vx, int tid) {
   using TL = Tile<T, D, BLK>;
@@ -94,13 +94,7 @@ __device__ inline void load_kv(const T* __restrict__ Kg, const T* __restrict__ V
     const uint4 kv = *(const uint4*)(Kg + (size_t)row * D + ch * TL::VEC);
     *(uint4*)(Ks + row * TL::KST + ch * TL::VEC) = kv;
     const uint4 vv = *(const uint4*)(Vg + (size_t)row * D + ch * TL::VEC);
-    if constexpr (TL::bf) {
-      const bf16* ve = (const bf16*)&vv;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) Vx[(ch * 8 + e) * TL::VST + row] = ve[e];
-    } else {
-      *(uint4*)(Vx + row * TL::VST + ch * TL::VEC) = vv;
-    }
+    *(uint4*)(Vx + row * TL::VST + ch * TL::VEC) = vv;
   }
 }
 
@@ -129,7 +123,9 @@ __device__ inline f32x4 score_tile(const QFrag<T, D>& qf, const T* Ks, int n, in
   return acc;
 }
 
-// O^T += V^T P^T over one block; p[n][k] = P^T[16n + 4(l/16) + k][l%16].
+// O^T += V^T P^T over one block; p[n][k] = P^T[16n + 4(l/16) + k][l%16].  For bf16 the MFMA's
+// k-slot 8(l/16) + e stands for key 32pp + 4(l/16) + e (e < 4) or 32pp + 16 + 4(l/16) + e - 4 (e >= 4),
+// the same permutation on both operands, so P needs no shuffle.
 template <typename T, int D, int BLK>
 __device__ inline void pv_block(f32x4 (&o)[D / 16], const f32x4 (&p)[BLK / 16], const T* Vx, int lane) {
   using TL = Tile<T, D, BLK>;
@@ -145,10 +141,15 @@ __device__ inline void pv_block(f32x4 (&o)[D / 16], const f32x4 (&p)[BLK / 16], 
       }
 #pragma unroll
       for (int dt = 0; dt < D / 16; ++dt) {
-        const bf16* vr = Vx + (16 * dt + r) * TL::VST + 32 * pp + 4 * s;
-        const bf16x4 lo = *(const bf16x4*)vr;
-        const bf16x4 hi = *(const bf16x4*)(vr + 16);
-        const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        // V^T[d][key] for the 8 keys of this lane's k-slots: 32pp + 4s + {0..3} and + 16 + {0..3};
+        // with a 144-byte row stride the four lane groups (s) hit disjoint bank windows
+        const bf16* vc = Vx + (32 * pp + 4 * s) * TL::VST + 16 * dt + r;
+        bf16x8 a;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          a[e] = vc[e * TL::VST];
+          a[4 + e] = vc[(16 + e) * TL::VST];
+        }
         o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, o[dt], 0, 0, 0);
       }
     }
@@ -215,64 +216,83 @@ __global__ __launch_bounds__(256) void k_pair_bin(const int32_t* __restrict__ se
 
 // One work-group per (remote block i, split): the pairs of block i are the concatenation of its
 // cells (i, j), j = i + L .. nb - 1.  The work-group scans the cell counts into LDS, stages the
-// block's K/V in LDS once, and processes its chunks of 64 pairs (chunk c goes to split c % splits):
-// each wave gathers 16 pairs' queries, S^T = K Q^T and O^T = V^T P^T on MFMA, and every pair's
-// softmax partial is stored at [token][slot].
+// block's K/V in LDS once, and walks its pairs kRemoteWaves * 16 at a time (iteration c goes to
+// split c % splits): each wave gathers 16 pairs' queries, S^T = K Q^T and O^T = V^T P^T run on
+// MFMA, and every pair's softmax partial is stored at [token][slot].  The next iteration's pair
+// ids and query rows are loaded before the current one is computed.
+constexpr int kRemoteWaves = 8;
+
 template <typename T, int D, int BLK>
-__global__ __launch_bounds__(256) void k_attn_remote(const T* __restrict__ Q, const T* __restrict__ K,
-                                                     const T* __restrict__ V, const int32_t* __restrict__ cellcnt,
-                                                     const int32_t* __restrict__ bins, T* __restrict__ part_o,
-                                                     float* __restrict__ part_ml, Shape s) {
+__global__ __launch_bounds__(kRemoteWaves * 64) void k_attn_remote(const T* __restrict__ Q, const T* __restrict__ K,
+                                                                   const T* __restrict__ V,
+                                                                   const int32_t* __restrict__ cellcnt,
+                                                                   const int32_t* __restrict__ bins,
+                                                                   T* __restrict__ part_o, float* __restrict__ part_ml,
+                                                                   Shape s) {
   using TL = Tile<T, D, BLK>;
+  constexpr int NTHR = kRemoteWaves * 64;
+  constexpr int PER_IT = kRemoteWaves * 16;
   extern __shared__ __align__(16) char lds_raw[];
   T* Ks = (T*)lds_raw;
   T* Vx = Ks + TL::K_ELEMS;
   int* pre = (int*)(Vx + TL::V_ELEMS);  // [ncell + 1] exclusive prefix of the cell counts
-  __shared__ int scan_tmp[4];
+  __shared__ int scan_tmp[kRemoteWaves];
   const int i = blockIdx.x, bh = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int ncell = s.ne - i;
   const long long row0 = (long long)bh * s.cells_per_bh + cell_row(i, s.ne);
   int run = 0;
-  for (int c0 = 0; c0 < ncell; c0 += 256) {
+  for (int c0 = 0; c0 < ncell; c0 += NTHR) {
     const int c = c0 + tid;
     const int v = c < ncell ? min(cellcnt[row0 + c], BLK) : 0;
     int tot;
-    const int ex = block_exclusive_scan<256>(v, scan_tmp, &tot);
+    const int ex = block_exclusive_scan<NTHR>(v, scan_tmp, &tot);
     if (c < ncell) pre[c] = run + ex;
     run += tot;
   }
   if (tid == 0) pre[ncell] = run;
   const int total = run;
-  const int nch = (total + kPairsPerChunk - 1) / kPairsPerChunk;
-  if ((int)blockIdx.z >= nch) return;  // uniform for the work-group
+  const int nit = (total + PER_IT - 1) / PER_IT;
+  if ((int)blockIdx.z >= nit) return;  // uniform for the work-group
   const size_t rowbase = (size_t)bh * s.S;
-  load_kv<T, D, BLK, 256>(K + (rowbase + (size_t)i * BLK) * D, V + (rowbase + (size_t)i * BLK) * D, Ks, Vx, tid);
+  load_kv<T, D, BLK, NTHR>(K + (rowbase + (size_t)i * BLK) * D, V + (rowbase + (size_t)i * BLK) * D, Ks, Vx, tid);
   __syncthreads();
   const float c = s.scale * kLog2e;
-  for (int ch = blockIdx.z; ch < nch; ch += gridDim.z) {
-    const int pidx = ch * kPairsPerChunk + wave * 16 + (lane & 15);
-    const bool valid = pidx < total;
-    int pv = 0;
-    if (valid) {
-      int lo = 0, hi = ncell - 1;  // the cell whose range holds pidx
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (pre[mid] <= pidx)
-          lo = mid;
-        else
-          hi = mid - 1;
-      }
-      pv = bins[(row0 + lo) * BLK + (pidx - pre[lo])];
+  // pair id of this lane's slot in iteration it (-1 when past the end)
+  auto pair_at = [&](int it) -> int {
+    const int pidx = it * PER_IT + wave * 16 + (lane & 15);
+    if (pidx >= total) return -1;
+    int lo = 0, hi = ncell - 1;  // the cell whose range holds pidx
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (pre[mid] <= pidx)
+        lo = mid;
+      else
+        hi = mid - 1;
     }
-    const int t = pv / s.R, r = pv % s.R;
-    QFrag<T, D> qf;
-    load_q<T, D>(qf, Q + (rowbase + t) * D, lane);
+    return bins[(row0 + lo) * BLK + (pidx - pre[lo])];
+  };
+  int it = blockIdx.z;
+  if (it * PER_IT + wave * 16 >= total) return;  // this wave has no pairs at all (no barriers below)
+  int pv = pair_at(it);
+  QFrag<T, D> qf;
+  load_q<T, D>(qf, Q + (rowbase + (pv < 0 ? 0 : pv / s.R)) * D, lane);
+  for (; it < nit; it += gridDim.z) {
+    const int cur = pv;
+    const QFrag<T, D> qc = qf;
+    const int nx = it + (int)gridDim.z;
+    if (nx < nit && nx * PER_IT + wave * 16 < total) {
+      pv = pair_at(nx);
+      load_q<T, D>(qf, Q + (rowbase + (pv < 0 ? 0 : pv / s.R)) * D, lane);
+    } else {
+      pv = -1;
+    }
+    if (it * PER_IT + wave * 16 >= total) break;
     f32x4 p[TL::NT];
     float mx = -INFINITY;
 #pragma unroll
     for (int n = 0; n < TL::NT; ++n) {
-      p[n] = score_tile<T, D, BLK>(qf, Ks, n, lane);
+      p[n] = score_tile<T, D, BLK>(qc, Ks, n, lane);
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         p[n][k] *= c;
@@ -293,7 +313,8 @@ __global__ __launch_bounds__(256) void k_attn_remote(const T* __restrict__ Q, co
 #pragma unroll
     for (int dt = 0; dt < TL::ND; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     pv_block<T, D, BLK>(o, p, Vx, lane);
-    if (valid) {
+    if (cur >= 0) {
+      const int t = cur / s.R, r = cur % s.R;
       const size_t pr = (rowbase + t) * s.R + r;
       const float inv = 1.f / sum;
 #pragma unroll
@@ -399,7 +420,8 @@ hipError_t attend_impl(const Shape& s, const void* q, const void* k, const void*
     if (rl > 65536 && (e = hipFuncSetAttribute((const void*)k_attn_remote<T, D, BLK>,
                                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)rl)) != hipSuccess)
       return e;
-    hipLaunchKernelGGL((k_attn_remote<T, D, BLK>), dim3(s.ne, s.B * s.H, s.split), dim3(256), rl, st, (const T*)q,
+    hipLaunchKernelGGL((k_attn_remote<T, D, BLK>), dim3(s.ne, s.B * s.H, s.split), dim3(kRemoteWaves * 64), rl, st,
+                       (const T*)q,
                        (const T*)k, (const T*)v, b.cellcnt, b.bins, (T*)b.part_o, b.part_ml, s);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }

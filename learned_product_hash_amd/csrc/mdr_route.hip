@@ -457,13 +457,40 @@ template <int K>
 __device__ inline void insert_sorted(float (&v)[K], int (&id)[K], float x, int a) {
 #pragma unroll
   for (int k = 0; k < K; ++k) {
-    const bool better = x > v[k] || (x == v[k] && a < id[k]);
+    const bool better = (x > v[k]) | ((x == v[k]) & (a < id[k]));
     const float tv = v[k];
     const int ta = id[k];
     v[k] = better ? x : tv;
     id[k] = better ? a : ta;
     x = better ? tv : x;
     a = better ? ta : a;
+  }
+}
+
+// (value, index) ranked by value descending then index ascending, as one unsigned 64-bit key: the
+// high word is the float's bits made order-preserving, the low word the complemented index.  A
+// larger key is a better entry, so every comparison is a single 64-bit compare.
+__device__ inline uint64_t rank_key(float v, int idx) {
+  uint32_t u = __float_as_uint(v);
+  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((uint64_t)u << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)idx);
+}
+__device__ inline float key_value(uint64_t k) {
+  uint32_t u = (uint32_t)(k >> 32);
+  u = (u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u;
+  return __uint_as_float(u);
+}
+__device__ inline int key_index(uint64_t k) { return (int)(0xFFFFFFFFu - (uint32_t)k); }
+
+// Keep top[0..K) sorted (best first) while inserting x; empty slots hold 0, below every real key.
+template <int K>
+__device__ inline void insert_key(uint64_t (&top)[K], uint64_t x) {
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    const bool better = x > top[k];
+    const uint64_t t = top[k];
+    top[k] = better ? x : t;
+    x = better ? t : x;
   }
 }
 
@@ -493,72 +520,152 @@ __global__ __launch_bounds__(kProbeThreads) void k_probe_fixed(
   const int t = tbase + tid;
   const int A = s.A;
   float* mu = smem;                   // [NT][MST]
-  int* csr = (int*)(mu + NT * MST);   // off [A+1], idx [ne] when staged
-  const int32_t* offp = off + (size_t)bh * (A + 1);
-  const int32_t* idxp = idx + (size_t)bh * s.nb;
-  if (s.csr_lds) {
-    for (int k = tid; k <= A; k += NT) csr[k] = offp[k];
-    for (int k = tid; k < s.ne; k += NT) csr[A + 1 + k] = idxp[k];
-    offp = csr;
-    idxp = csr + A + 1;
+  int* csr = (int*)(smem + max(NT * MST, NT * s.M * 2));  // off [A+1], idx [ne] when staged
+  // the posting-list CSR of this (b,h) in LDS (this kernel is only used when it fits); up to 8
+  // independent loads per lane in flight before the LDS stores
+  {
+    const int32_t* og = off + (size_t)bh * (A + 1);
+    const int32_t* ig = idx + (size_t)bh * s.nb;
+    const int n = A + 1 + s.ne;
+    for (int k0 = 0; k0 < n; k0 += 8 * NT) {
+      int v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int k = k0 + u * NT + tid;
+        v[u] = k < n ? (k <= A ? og[k] : ig[k - A - 1]) : 0;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int k = k0 + u * NT + tid;
+        if (k < n) csr[k] = v[u];
+      }
+    }
   }
-  // ---- mu on MFMA (same lane layout as k_probe_rerank)
+  const int* offp = csr;
+  const int* idxp = csr + A + 1;
+  // ---- mu on MFMA.  fp32 inputs: v_mfma_f32_16x16x4_f32 with the lane layout of k_probe_rerank.
+  // bf16 inputs: every fp32 codebook value is split exactly into three bf16 parts
+  // (w = hi + mid + lo, 8 significand bits each), and mu accumulates q*hi + q*mid + q*lo on
+  // v_mfma_f32_16x16x32_bf16; q is exact in bf16, so every product is exact and only the fp32
+  // accumulation rounds, as in an fp32 dot product.  Lane l supplies Q[token 16tt + l%16][d] and
+  // W[code 16ct + l%16][d] for d = 32kk + 8(l/16) + e and receives mu[token 16tt + 4(l/16) + k][code].
   {
     const int r16 = lane & 15, s4 = lane >> 4;
     const float* cbh = cb + (size_t)h * G * C * D;
-    float wb[G][CP / 16][D / 4];
-    float bv[G][CP / 16];
-#pragma unroll
-    for (int g = 0; g < G; ++g)
-#pragma unroll
-      for (int ct = 0; ct < CP / 16; ++ct) {
-        const int code = ct * 16 + r16;
-        if (code < C) {
-          const float4* wp = (const float4*)(cbh + ((size_t)g * C + code) * D + s4 * (D / 4));
-#pragma unroll
-          for (int c = 0; c < D / 16; ++c) {
-            const float4 v = wp[c];
-            wb[g][ct][4 * c] = v.x;
-            wb[g][ct][4 * c + 1] = v.y;
-            wb[g][ct][4 * c + 2] = v.z;
-            wb[g][ct][4 * c + 3] = v.w;
-          }
-        } else {
-#pragma unroll
-          for (int c = 0; c < D / 4; ++c) wb[g][ct][c] = 0.f;
-        }
-        bv[g][ct] = (bias && code < C) ? bias[(h * G + g) * C + code] : 0.f;
-      }
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-      if (wave * 64 + tt * 16 >= NT) break;
-      int tq = tbase + wave * 64 + tt * 16 + r16;
-      tq = tq < s.S ? tq : s.S - 1;
-      float qa[D / 4];
-      const T* qp = Q + ((size_t)bh * s.S + tq) * D + s4 * (D / 4);
-      constexpr int VEC = Vec16<T>::n;
-#pragma unroll
-      for (int c = 0; c < D / 4 / VEC; ++c) {
-        typename Vec16<T>::type v = *(const typename Vec16<T>::type*)(qp + c * VEC);
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) qa[c * VEC + e] = to_f(v[e]);
-      }
+    if constexpr (std::is_same<T, bf16>::value) {
+      bf16x8 wh[G][CP / 16][D / 32], wm[G][CP / 16][D / 32], wl[G][CP / 16][D / 32];
+      float bv[G][CP / 16];
 #pragma unroll
       for (int g = 0; g < G; ++g)
 #pragma unroll
         for (int ct = 0; ct < CP / 16; ++ct) {
-          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+          const int code = ct * 16 + r16;
 #pragma unroll
-          for (int kk = 0; kk < D / 4; ++kk)
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[kk], wb[g][ct][kk], acc, 0, 0, 0);
+          for (int kk = 0; kk < D / 32; ++kk) {
+            float wv[8];
+            if (code < C) {
+              const float4* wp = (const float4*)(cbh + ((size_t)g * C + code) * D + 32 * kk + 8 * s4);
+              const float4 a = wp[0], b = wp[1];
+              wv[0] = a.x; wv[1] = a.y; wv[2] = a.z; wv[3] = a.w;
+              wv[4] = b.x; wv[5] = b.y; wv[6] = b.z; wv[7] = b.w;
+            } else {
 #pragma unroll
-          for (int k = 0; k < 4; ++k)
-            mu[(wave * 64 + tt * 16 + 4 * s4 + k) * MST + g * CP + ct * 16 + r16] = acc[k] + bv[g][ct];
+              for (int e = 0; e < 8; ++e) wv[e] = 0.f;
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const bf16 hi = (bf16)wv[e];
+              const float r1 = wv[e] - (float)hi;
+              const bf16 mi = (bf16)r1;
+              const bf16 lo = (bf16)(r1 - (float)mi);
+              wh[g][ct][kk][e] = hi;
+              wm[g][ct][kk][e] = mi;
+              wl[g][ct][kk][e] = lo;
+            }
+          }
+          bv[g][ct] = (bias && code < C) ? bias[(h * G + g) * C + code] : 0.f;
         }
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        if (wave * 64 + tt * 16 >= NT) break;
+        int tq = tbase + wave * 64 + tt * 16 + r16;
+        tq = tq < s.S ? tq : s.S - 1;
+        bf16x8 qa[D / 32];
+        const T* qp = Q + ((size_t)bh * s.S + tq) * D + 8 * s4;
+#pragma unroll
+        for (int kk = 0; kk < D / 32; ++kk) qa[kk] = *(const bf16x8*)(qp + 32 * kk);
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+          for (int ct = 0; ct < CP / 16; ++ct) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < D / 32; ++kk) {
+              acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[kk], wh[g][ct][kk], acc, 0, 0, 0);
+              acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[kk], wm[g][ct][kk], acc, 0, 0, 0);
+              acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[kk], wl[g][ct][kk], acc, 0, 0, 0);
+            }
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+              mu[(wave * 64 + tt * 16 + 4 * s4 + k) * MST + g * CP + ct * 16 + r16] = acc[k] + bv[g][ct];
+          }
+      }
+    } else {
+      float wb[G][CP / 16][D / 4];
+      float bv[G][CP / 16];
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int ct = 0; ct < CP / 16; ++ct) {
+          const int code = ct * 16 + r16;
+          if (code < C) {
+            const float4* wp = (const float4*)(cbh + ((size_t)g * C + code) * D + s4 * (D / 4));
+#pragma unroll
+            for (int c = 0; c < D / 16; ++c) {
+              const float4 v = wp[c];
+              wb[g][ct][4 * c] = v.x;
+              wb[g][ct][4 * c + 1] = v.y;
+              wb[g][ct][4 * c + 2] = v.z;
+              wb[g][ct][4 * c + 3] = v.w;
+            }
+          } else {
+#pragma unroll
+            for (int c = 0; c < D / 4; ++c) wb[g][ct][c] = 0.f;
+          }
+          bv[g][ct] = (bias && code < C) ? bias[(h * G + g) * C + code] : 0.f;
+        }
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        if (wave * 64 + tt * 16 >= NT) break;
+        int tq = tbase + wave * 64 + tt * 16 + r16;
+        tq = tq < s.S ? tq : s.S - 1;
+        float qa[D / 4];
+        const T* qp = Q + ((size_t)bh * s.S + tq) * D + s4 * (D / 4);
+#pragma unroll
+        for (int c = 0; c < D / 16; ++c) {
+          const float4 v = *(const float4*)(qp + 4 * c);
+          qa[4 * c] = v.x;
+          qa[4 * c + 1] = v.y;
+          qa[4 * c + 2] = v.z;
+          qa[4 * c + 3] = v.w;
+        }
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+          for (int ct = 0; ct < CP / 16; ++ct) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < D / 4; ++kk)
+              acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[kk], wb[g][ct][kk], acc, 0, 0, 0);
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+              mu[(wave * 64 + tt * 16 + 4 * s4 + k) * MST + g * CP + ct * 16 + r16] = acc[k] + bv[g][ct];
+          }
+      }
     }
   }
   __syncthreads();
-  if (t >= s.S) return;  // no barriers below
+  const bool active = t < s.S;
   const int j = t / s.blk;
   const int cutoff = j - s.L;
   const float* mrow = mu + tid * MST;
@@ -568,36 +675,21 @@ __global__ __launch_bounds__(kProbeThreads) void k_probe_fixed(
   float tval[G][PG];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    float m[C];
+    uint64_t top[PG];
 #pragma unroll
-    for (int c = 0; c < C; ++c) m[c] = mrow[g * CP + c];
-    float pv = FLT_MAX;
-    int pc = -1;
+    for (int p = 0; p < PG; ++p) top[p] = 0;
+#pragma unroll
+    for (int c = 0; c < C; ++c) insert_key<PG>(top, rank_key(mrow[g * CP + c], c));
 #pragma unroll
     for (int p = 0; p < PG; ++p) {
-      int bc = -1;
-      float bvv = -FLT_MAX;
-#pragma unroll
-      for (int c = 0; c < C; ++c) {
-        const bool after = (m[c] < pv) || (m[c] == pv && c > pc);
-        const bool take = after && (bc < 0 || m[c] > bvv);
-        bc = take ? c : bc;
-        bvv = take ? m[c] : bvv;
-      }
-      tcode[g][p] = bc;
-      tval[g][p] = bvv;
-      pv = bvv;
-      pc = bc;
+      tcode[g][p] = key_index(top[p]);
+      tval[g][p] = key_value(top[p]);
     }
   }
-  // ---- rank vectors with prod (k_g + 1) <= P, top-P addresses
-  float tpv[P];
-  int tpa[P];
+  // ---- rank vectors with prod (k_g + 1) <= P, top-P addresses by (sigma desc, address asc)
+  uint64_t tpk[P];
 #pragma unroll
-  for (int p = 0; p < P; ++p) {
-    tpv[p] = -INFINITY;
-    tpa[p] = 0x7fffffff;
-  }
+  for (int p = 0; p < P; ++p) tpk[p] = 0;
   constexpr int NCOMB = RankSpace<G, PG>::count();
 #pragma unroll
   for (int kc = 0; kc < NCOMB; ++kc) {
@@ -617,33 +709,21 @@ __global__ __launch_bounds__(kProbeThreads) void k_probe_fixed(
         sig += tval[g][rk[g]];
         a = a * C + tcode[g][rk[g]];
       }
-      insert_sorted<P>(tpv, tpa, sig, a);
+      insert_key<P>(tpk, rank_key(sig, a));
     }
   }
-  // ---- candidates in probe rank order, rerank by <q_t, summary>
-  float trv[R > 0 ? R : 1];
-  int tri[R > 0 ? R : 1];
+  int tpa[P];
 #pragma unroll
-  for (int r = 0; r < (R > 0 ? R : 1); ++r) {
-    trv[r] = -INFINITY;
-    tri[r] = 0x7fffffff;
-  }
+  for (int p = 0; p < P; ++p) tpa[p] = key_index(tpk[p]);
+  // ---- candidate ranges: probe p contributes the `take[p]` newest entries <= cutoff of its list,
+  // ending at CSR position lim[p] (exclusive), until M candidates
+  int lim[P], take[P];
   int nc = 0;
-  if (cutoff >= 0 && R > 0) {
-    float qv[D];
-    {
-      const T* qp = Q + ((size_t)bh * s.S + t) * D;
-      constexpr int VEC = Vec16<T>::n;
 #pragma unroll
-      for (int c = 0; c < D / VEC; ++c) {
-        typename Vec16<T>::type v = *(const typename Vec16<T>::type*)(qp + c * VEC);
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) qv[c * VEC + e] = to_f(v[e]);
-      }
-    }
-    const float* ksh = ksum + (size_t)bh * s.nb * D;
-#pragma unroll
-    for (int p = 0; p < P; ++p) {
+  for (int p = 0; p < P; ++p) {
+    take[p] = 0;
+    lim[p] = 0;
+    if (active && cutoff >= 0 && R > 0) {
       const int a = tpa[p];
       const int lo = offp[a], hi = offp[a + 1];
       int l0 = lo, l1 = hi;  // first entry > cutoff
@@ -654,24 +734,94 @@ __global__ __launch_bounds__(kProbeThreads) void k_probe_fixed(
         else
           l1 = mid;
       }
-      const int take = min(min(s.cap, l0 - lo), s.M - nc);
-      for (int e = 0; e < take; ++e) {
-        const int i = idxp[l0 - 1 - e];
-        const float4* kr = (const float4*)(ksh + (size_t)i * D);
-        float rho = 0.f;
-#pragma unroll
-        for (int c = 0; c < D / 4; ++c) {
-          const float4 kv = kr[c];
-          rho = fmaf(kv.x, qv[4 * c + 0], rho);
-          rho = fmaf(kv.y, qv[4 * c + 1], rho);
-          rho = fmaf(kv.z, qv[4 * c + 2], rho);
-          rho = fmaf(kv.w, qv[4 * c + 3], rho);
-        }
-        insert_sorted<(R > 0 ? R : 1)>(trv, tri, rho, i);
-      }
-      nc += take > 0 ? take : 0;
+      const int tk = min(min(s.cap, l0 - lo), s.M - nc);
+      take[p] = tk > 0 ? tk : 0;
+      lim[p] = l0;
+      nc += take[p];
     }
   }
+  // ---- the work-group's candidates as one list (token-major) in LDS, in the place of mu
+  __shared__ int scan_tmp[kProbeThreads / 64];
+  int total;
+  const int base = block_exclusive_scan<NT>(nc, scan_tmp, &total);
+  int* clist = (int*)smem;                // [total] (local token << 16) | block
+  float* rho = smem + NT * s.M;           // [total]
+  __shared__ int tok_base[NT], tok_n[NT];
+  {
+    int k = base;
+#pragma unroll
+    for (int p = 0; p < P; ++p)
+      for (int e = 0; e < take[p]; ++e) clist[k++] = (tid << 16) | idxp[lim[p] - 1 - e];
+  }
+  __syncthreads();
+  // ---- rerank scores: a quad of lanes per token (tokens quad, quad + NT/4, ...), each lane a
+  // contiguous quarter of D; the quad keeps the token's quarter of q in registers and has up to
+  // four candidates' summary slices in flight; the quarters are added in a fixed order
+  tok_base[tid] = base;
+  tok_n[tid] = nc;
+  __syncthreads();
+  {
+    constexpr int NQ = NT / 4;
+    const int quad = tid >> 2, ql = tid & 3;
+    const float* ksh = ksum + (size_t)bh * s.nb * D;
+    for (int lt = quad; lt < NT; lt += NQ) {
+      const int b0 = tok_base[lt], n0 = tok_n[lt];
+      if (n0 == 0) continue;
+      float qf[D / 4];
+      {
+        const T* qp = Q + ((size_t)bh * s.S + tbase + lt) * D + ql * (D / 4);
+#pragma unroll
+        for (int c = 0; c < D / 16; ++c) {
+          if constexpr (std::is_same<T, bf16>::value) {
+            const bf16x4 qb = *(const bf16x4*)(qp + 4 * c);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) qf[4 * c + e] = (float)qb[e];
+          } else {
+            const float4 q4 = *(const float4*)(qp + 4 * c);
+            qf[4 * c] = q4.x;
+            qf[4 * c + 1] = q4.y;
+            qf[4 * c + 2] = q4.z;
+            qf[4 * c + 3] = q4.w;
+          }
+        }
+      }
+      for (int k0 = 0; k0 < n0; k0 += 4) {
+        float4 kv[4][D / 16];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int k = b0 + (k0 + u < n0 ? k0 + u : k0);
+          const float4* kr = (const float4*)(ksh + (size_t)(clist[k] & 0xffff) * D + ql * (D / 4));
+#pragma unroll
+          for (int c = 0; c < D / 16; ++c) kv[u][c] = kr[c];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          float a = 0.f;
+#pragma unroll
+          for (int c = 0; c < D / 16; ++c) {
+            a = fmaf(kv[u][c].x, qf[4 * c], a);
+            a = fmaf(kv[u][c].y, qf[4 * c + 1], a);
+            a = fmaf(kv[u][c].z, qf[4 * c + 2], a);
+            a = fmaf(kv[u][c].w, qf[4 * c + 3], a);
+          }
+          a += __shfl_xor(a, 1);
+          a += __shfl_xor(a, 2);
+          if (ql == 0 && k0 + u < n0) rho[b0 + k0 + u] = a;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  if (!active) return;  // no barriers below
+  // ---- top-R of the token's candidates by (score desc, block asc)
+  constexpr int RK = R > 0 ? R : 1;
+  uint64_t trk[RK];
+#pragma unroll
+  for (int r = 0; r < RK; ++r) trk[r] = 0;
+  for (int k = base; k < base + nc; ++k) insert_key<RK>(trk, rank_key(rho[k], clist[k] & 0xffff));
+  int tri[RK];
+#pragma unroll
+  for (int r = 0; r < RK; ++r) tri[r] = key_index(trk[r]);
   int nr = nc < R ? nc : R;
   if (force && R > 0) {
     const int f = force[(size_t)bh * s.S + t];
@@ -792,6 +942,7 @@ hipError_t launch_address(const Shape& s, const void* k, const float* codebook, 
 }
 
 bool probe_fixed_shape(const Shape& s) {
+  if (!s.csr_lds) return false;
   const bool bf = s.dtype == MDR_BF16;
 #define MDR_MATCH(TT, DD, GG, CC, PP, RR)                                                                  \
   if ((std::is_same<TT, bf16>::value == bf) && s.D == DD && s.G == GG && s.C == CC && s.P == PP && s.R == RR) \
@@ -803,7 +954,11 @@ bool probe_fixed_shape(const Shape& s) {
 
 size_t probe_lds_bytes(const Shape& s) {
   const int CP = (s.C + 15) & ~15;
-  if (s.fixed_probe) return ((size_t)kProbeThreads * (s.G * CP + 1) + (s.csr_lds ? (size_t)(s.A + 1 + s.ne) : 0)) * 4;
+  if (s.fixed_probe) {
+    // mu rows during the logits, then the work-group's candidate list (block ids and scores)
+    const size_t mu_w = (size_t)kProbeThreads * (s.G * CP + 1), pairs_w = (size_t)kProbeThreads * s.M * 2;
+    return ((mu_w > pairs_w ? mu_w : pairs_w) + (s.csr_lds ? (size_t)(s.A + 1 + s.ne) : 0)) * 4;
+  }
   const int Pg = s.P < s.C ? s.P : s.C;
   const size_t words = (size_t)kProbeThreads * (s.G * CP + 4) + (size_t)kProbeThreads * (s.G * Pg + 2 * s.P + 2 * s.R) +
                        (s.csr_lds ? (size_t)(s.A + 1 + s.ne) : 0);
