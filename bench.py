@@ -41,7 +41,7 @@ HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
 KERNEL_SYMBOL = {  # substrings of the kernels' symbol names in rocprofv3 output
     "address": "k_address",
     "post": "k_post",
-    "probe_rerank": "k_probe_rerank",
+    "probe_rerank": "k_probe",
     "attn_remote": "k_attn_remote",
     "attn_local": "k_attn_local",
 }
@@ -50,6 +50,13 @@ KERNEL_SOURCE = {
     "attn_remote": "mdr_attn.hip", "attn_local": "mdr_attn.hip",
 }
 CALIB_BYTES = 512 << 20
+HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000  # hipEventDisableSystemFence (hip_runtime_api.h)
+PMC_COMMANDS = [  # run from the repository root on one MI355X, TMPDIR=/tmp
+    "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmcf -o f -- "
+    "python3 bench.py --steps 3 --warmup 1 --calib-copy --no-cpu --no-sweep",
+    "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmcw -o w -- "
+    "python3 bench.py --steps 3 --warmup 1 --calib-copy --no-cpu --no-sweep",
+]
 
 
 def parse(argv=None):
@@ -64,7 +71,7 @@ def parse(argv=None):
     ap.add_argument("--no-sweep", action="store_true", help="skip the 4K-32K exponent sweep")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run one elementwise copy of 512 MiB first (counter calibration)")
-    ap.add_argument("--cpu-heads", type=int, default=4)
+    ap.add_argument("--cpu-heads", type=int, default=8)
     ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     ap.add_argument("--summarize-rocprof", nargs=2, metavar=("KERNEL_STATS_CSV", "COMMAND"),
                     help="write profiles/routed_attention_kernels_<workload>.md from a rocprofv3 --stats CSV")
@@ -88,7 +95,7 @@ class HipEvents:
             raise RuntimeError("libamdhip64 is not mapped; initialise torch.cuda first")
         self.ct = ctypes
         self.hip = ctypes.CDLL(path)
-        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
         self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
 
@@ -96,8 +103,10 @@ class HipEvents:
         out = []
         for _ in range(n):
             h = self.ct.c_void_p()
-            if self.hip.hipEventCreate(self.ct.byref(h)) != 0:
-                raise RuntimeError("hipEventCreate failed")
+            # without the system-scope fence an event adds ~1 us instead of ~5 us between kernels, so the
+            # per-kernel intervals agree with rocprofv3's kernel durations
+            if self.hip.hipEventCreateWithFlags(self.ct.byref(h), HIP_EVENT_DISABLE_SYSTEM_FENCE) != 0:
+                raise RuntimeError("hipEventCreateWithFlags failed")
             out.append(h.value)
         return out
 
@@ -203,8 +212,11 @@ def stage_bytes(w):
 
 
 def source_digest(kernel):
-    path = os.path.join(ROOT, "learned_product_hash_amd", "csrc", KERNEL_SOURCE[kernel])
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+    """Digest of the kernel's source file and the shared device header it includes."""
+    h = hashlib.sha256()
+    for f in (KERNEL_SOURCE[kernel], "mdr_internal.h"):
+        h.update(open(os.path.join(ROOT, "learned_product_hash_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
 
 
 def traffic_path(w):
@@ -348,7 +360,7 @@ def ingest_pmc(fetch_csv, write_csv, w):
         raise SystemExit("no calibration copy dispatch found (run bench.py with --calib-copy)")
     kib = CALIB_BYTES / 1024.0
     sf, sw = kib / calib_f[0], kib / calib_w[0]
-    res = {"workload": describe(w), "calibration": {"copy_bytes": CALIB_BYTES, "fetch_kib": calib_f[0],
+    res = {"workload": describe(w), "commands": PMC_COMMANDS, "calibration": {"copy_bytes": CALIB_BYTES, "fetch_kib": calib_f[0],
                                                    "write_kib": calib_w[0], "fetch_scale": sf, "write_scale": sw},
            "kernels": {}}
     for k, sym in KERNEL_SYMBOL.items():
