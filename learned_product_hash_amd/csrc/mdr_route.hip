@@ -453,20 +453,6 @@ __global__ __launch_bounds__(kProbeThreads) void k_probe_rerank(
 // P probes, R remote blocks): every per-token list lives in registers, rank vectors are
 // enumerated at compile time, and the top-P / top-R lists are kept sorted by an unrolled
 // insertion network.  Semantics are identical to k_probe_rerank.
-template <int K>
-__device__ inline void insert_sorted(float (&v)[K], int (&id)[K], float x, int a) {
-#pragma unroll
-  for (int k = 0; k < K; ++k) {
-    const bool better = (x > v[k]) | ((x == v[k]) & (a < id[k]));
-    const float tv = v[k];
-    const int ta = id[k];
-    v[k] = better ? x : tv;
-    id[k] = better ? a : ta;
-    x = better ? tv : x;
-    a = better ? ta : a;
-  }
-}
-
 // (value, index) ranked by value descending then index ascending, as one unsigned 64-bit key: the
 // high word is the float's bits made order-preserving, the low word the complemented index.  A
 // larger key is a better entry, so every comparison is a single 64-bit compare.
@@ -503,167 +489,152 @@ struct RankSpace {
   }
 };
 
+// Lane layout of the MFMA operands below: lane l = 16 s4 + r16 holds D/4 dims of one row (a token
+// of Q or a code of the codebook).  bf16: dims 32kk + 8 s4 + e (the k-slots of v_mfma_f32_16x16x32_bf16);
+// fp32: dims s4 (D/4) + x (one k-step of v_mfma_f32_16x16x4f32 per x).
+template <bool BF, int D>
+__device__ inline int operand_dim(int s4, int x) {
+  return BF ? 32 * (x >> 3) + 8 * s4 + (x & 7) : s4 * (D / 4) + x;
+}
+
+// Small bf16 shapes keep four waves per SIMD, so that eight 128-token work-groups share a CU.
+constexpr int probe_min_waves(int bytes, int D, int C) { return bytes == 2 && D <= 64 && C <= 16 ? 4 : 1; }
+
 template <typename T, int D, int G, int C, int P, int R>
-__global__ __launch_bounds__(kProbeThreads) void k_probe_fixed(
+__global__ __launch_bounds__(kProbeThreads) __attribute__((amdgpu_waves_per_eu(probe_min_waves((int)sizeof(T), D, C)))) void k_probe_fixed(
     const T* __restrict__ Q, const float* __restrict__ cb, const float* __restrict__ bias,
     const float* __restrict__ ksum, const int32_t* __restrict__ off, const int32_t* __restrict__ idx,
     const int32_t* __restrict__ force, int32_t* __restrict__ sel, int32_t* __restrict__ ncand,
     int32_t* __restrict__ cellcnt, int32_t* __restrict__ bins, Shape s) {
   constexpr int NT = kProbeThreads;
+  static_assert(NT % 64 == 0, "whole waves of 64 tokens");
+  constexpr bool BF = std::is_same<T, bf16>::value;
   constexpr int CP = (C + 15) & ~15;
   constexpr int MST = G * CP + 1;  // odd stride: each lane's row starts in its own bank
   constexpr int PG = P < C ? P : C;
+  constexpr int DQ = D / 4;        // operand dims per lane
   extern __shared__ __align__(16) float smem[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r16 = lane & 15, s4 = lane >> 4;
   const int bh = blockIdx.y, h = bh % s.H;
   const int tbase = blockIdx.x * NT;
   const int t = tbase + tid;
   const int A = s.A;
-  float* mu = smem;                   // [NT][MST]
-  int* csr = (int*)(smem + max(NT * MST, NT * s.M * 2));  // off [A+1], idx [ne] when staged
-  // the posting-list CSR of this (b,h) in LDS (this kernel is only used when it fits); up to 8
-  // independent loads per lane in flight before the LDS stores
-  {
-    const int32_t* og = off + (size_t)bh * (A + 1);
-    const int32_t* ig = idx + (size_t)bh * s.nb;
-    const int n = A + 1 + s.ne;
-    for (int k0 = 0; k0 < n; k0 += 8 * NT) {
-      int v[8];
+  float* mu = smem;                                       // [NT][MST]
+  int* csr = (int*)(smem + max(NT * MST, NT * s.M * 2));  // off [A+1], idx [ne]
+  // ---- every independent global read first: the CSR of this (b,h) (first 8 per lane), the codebook
+  // rows and biases of this lane's codes, the query rows of this lane's four 16-token tiles
+  const int32_t* og = off + (size_t)bh * (A + 1);
+  const int32_t* ig = idx + (size_t)bh * s.nb;
+  const int ncsr = A + 1 + s.ne;
+  int cv[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int k = k0 + u * NT + tid;
-        v[u] = k < n ? (k <= A ? og[k] : ig[k - A - 1]) : 0;
-      }
+  for (int u = 0; u < 8; ++u) {
+    const int k = u * NT + tid;
+    cv[u] = k < ncsr ? (k <= A ? og[k] : ig[k - A - 1]) : 0;
+  }
+  const float* cbh = cb + (size_t)h * G * C * D;
+  float wv[G][CP / 16][DQ];
+  float bv[G][CP / 16];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int k = k0 + u * NT + tid;
-        if (k < n) csr[k] = v[u];
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int ct = 0; ct < CP / 16; ++ct) {
+      const int code = ct * 16 + r16;
+      const float* wr = cbh + ((size_t)g * C + (code < C ? code : 0)) * D;
+#pragma unroll
+      for (int x = 0; x < DQ; x += 4) {
+        const float4 v = *(const float4*)(wr + operand_dim<BF, D>(s4, x));
+        wv[g][ct][x] = code < C ? v.x : 0.f;
+        wv[g][ct][x + 1] = code < C ? v.y : 0.f;
+        wv[g][ct][x + 2] = code < C ? v.z : 0.f;
+        wv[g][ct][x + 3] = code < C ? v.w : 0.f;
       }
+      bv[g][ct] = (bias && code < C) ? bias[(h * G + g) * C + code] : 0.f;
+    }
+  constexpr int QV = DQ * (int)sizeof(T) / 16;  // 16-byte pieces of a lane's query slice
+  uint4 qraw[4][QV];
+#pragma unroll
+  for (int tt = 0; tt < 4; ++tt) {
+    int tq = tbase + wave * 64 + tt * 16 + r16;
+    tq = tq < s.S ? tq : s.S - 1;
+    const T* qp = Q + ((size_t)bh * s.S + tq) * D;
+#pragma unroll
+    for (int c = 0; c < QV; ++c) qraw[tt][c] = *(const uint4*)(qp + operand_dim<BF, D>(s4, c * (16 / (int)sizeof(T))));
+  }
+  int fv = -1;
+  if (force && R > 0 && t < s.S) fv = force[(size_t)bh * s.S + t];
+  // ---- the posting-list CSR into LDS (this kernel is only used when it fits)
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int k = u * NT + tid;
+    if (k < ncsr) csr[k] = cv[u];
+  }
+  for (int k0 = 8 * NT; k0 < ncsr; k0 += 8 * NT) {
+    int v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int k = k0 + u * NT + tid;
+      v[u] = k < ncsr ? (k <= A ? og[k] : ig[k - A - 1]) : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int k = k0 + u * NT + tid;
+      if (k < ncsr) csr[k] = v[u];
     }
   }
   const int* offp = csr;
   const int* idxp = csr + A + 1;
-  // ---- mu on MFMA.  fp32 inputs: v_mfma_f32_16x16x4_f32 with the lane layout of k_probe_rerank.
-  // bf16 inputs: every fp32 codebook value is split exactly into three bf16 parts
-  // (w = hi + mid + lo, 8 significand bits each), and mu accumulates q*hi + q*mid + q*lo on
+  // ---- mu on MFMA: lane l receives mu[token 16tt + 4(l/16) + k][code 16ct + l%16].  fp32 inputs use
+  // v_mfma_f32_16x16x4_f32.  For bf16 inputs every fp32 codebook value is split exactly into three
+  // bf16 parts (w = hi + mid + lo, 8 significand bits each) and mu accumulates q*hi + q*mid + q*lo on
   // v_mfma_f32_16x16x32_bf16; q is exact in bf16, so every product is exact and only the fp32
-  // accumulation rounds, as in an fp32 dot product.  Lane l supplies Q[token 16tt + l%16][d] and
-  // W[code 16ct + l%16][d] for d = 32kk + 8(l/16) + e and receives mu[token 16tt + 4(l/16) + k][code].
-  {
-    const int r16 = lane & 15, s4 = lane >> 4;
-    const float* cbh = cb + (size_t)h * G * C * D;
-    if constexpr (std::is_same<T, bf16>::value) {
-      bf16x8 wh[G][CP / 16][D / 32], wm[G][CP / 16][D / 32], wl[G][CP / 16][D / 32];
-      float bv[G][CP / 16];
+  // accumulation rounds, as in an fp32 dot product.
 #pragma unroll
-      for (int g = 0; g < G; ++g)
+  for (int g = 0; g < G; ++g)
 #pragma unroll
-        for (int ct = 0; ct < CP / 16; ++ct) {
-          const int code = ct * 16 + r16;
+    for (int ct = 0; ct < CP / 16; ++ct) {
+      if constexpr (BF) {
+        bf16x8 wh[D / 32], wm[D / 32], wl[D / 32];
+#pragma unroll
+        for (int kk = 0; kk < D / 32; ++kk)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float w = wv[g][ct][8 * kk + e];
+            const bf16 hi = (bf16)w;
+            const float r1 = w - (float)hi;
+            const bf16 mi = (bf16)r1;
+            wh[kk][e] = hi;
+            wm[kk][e] = mi;
+            wl[kk][e] = (bf16)(r1 - (float)mi);
+          }
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int kk = 0; kk < D / 32; ++kk) {
-            float wv[8];
-            if (code < C) {
-              const float4* wp = (const float4*)(cbh + ((size_t)g * C + code) * D + 32 * kk + 8 * s4);
-              const float4 a = wp[0], b = wp[1];
-              wv[0] = a.x; wv[1] = a.y; wv[2] = a.z; wv[3] = a.w;
-              wv[4] = b.x; wv[5] = b.y; wv[6] = b.z; wv[7] = b.w;
-            } else {
-#pragma unroll
-              for (int e = 0; e < 8; ++e) wv[e] = 0.f;
-            }
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const bf16 hi = (bf16)wv[e];
-              const float r1 = wv[e] - (float)hi;
-              const bf16 mi = (bf16)r1;
-              const bf16 lo = (bf16)(r1 - (float)mi);
-              wh[g][ct][kk][e] = hi;
-              wm[g][ct][kk][e] = mi;
-              wl[g][ct][kk][e] = lo;
-            }
+            const bf16x8 qa = *(const bf16x8*)&qraw[tt][kk];
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, wh[kk], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, wm[kk], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, wl[kk], acc, 0, 0, 0);
           }
-          bv[g][ct] = (bias && code < C) ? bias[(h * G + g) * C + code] : 0.f;
+#pragma unroll
+          for (int k = 0; k < 4; ++k)
+            mu[(wave * 64 + tt * 16 + 4 * s4 + k) * MST + g * CP + ct * 16 + r16] = acc[k] + bv[g][ct];
         }
+      } else {
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt) {
-        if (wave * 64 + tt * 16 >= NT) break;
-        int tq = tbase + wave * 64 + tt * 16 + r16;
-        tq = tq < s.S ? tq : s.S - 1;
-        bf16x8 qa[D / 32];
-        const T* qp = Q + ((size_t)bh * s.S + tq) * D + 8 * s4;
+        for (int tt = 0; tt < 4; ++tt) {
+          const float* qa = (const float*)&qraw[tt][0];
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kk = 0; kk < D / 32; ++kk) qa[kk] = *(const bf16x8*)(qp + 32 * kk);
+          for (int x = 0; x < DQ; ++x) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[x], wv[g][ct][x], acc, 0, 0, 0);
 #pragma unroll
-        for (int g = 0; g < G; ++g)
-#pragma unroll
-          for (int ct = 0; ct < CP / 16; ++ct) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kk = 0; kk < D / 32; ++kk) {
-              acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[kk], wh[g][ct][kk], acc, 0, 0, 0);
-              acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[kk], wm[g][ct][kk], acc, 0, 0, 0);
-              acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[kk], wl[g][ct][kk], acc, 0, 0, 0);
-            }
-#pragma unroll
-            for (int k = 0; k < 4; ++k)
-              mu[(wave * 64 + tt * 16 + 4 * s4 + k) * MST + g * CP + ct * 16 + r16] = acc[k] + bv[g][ct];
-          }
-      }
-    } else {
-      float wb[G][CP / 16][D / 4];
-      float bv[G][CP / 16];
-#pragma unroll
-      for (int g = 0; g < G; ++g)
-#pragma unroll
-        for (int ct = 0; ct < CP / 16; ++ct) {
-          const int code = ct * 16 + r16;
-          if (code < C) {
-            const float4* wp = (const float4*)(cbh + ((size_t)g * C + code) * D + s4 * (D / 4));
-#pragma unroll
-            for (int c = 0; c < D / 16; ++c) {
-              const float4 v = wp[c];
-              wb[g][ct][4 * c] = v.x;
-              wb[g][ct][4 * c + 1] = v.y;
-              wb[g][ct][4 * c + 2] = v.z;
-              wb[g][ct][4 * c + 3] = v.w;
-            }
-          } else {
-#pragma unroll
-            for (int c = 0; c < D / 4; ++c) wb[g][ct][c] = 0.f;
-          }
-          bv[g][ct] = (bias && code < C) ? bias[(h * G + g) * C + code] : 0.f;
+          for (int k = 0; k < 4; ++k)
+            mu[(wave * 64 + tt * 16 + 4 * s4 + k) * MST + g * CP + ct * 16 + r16] = acc[k] + bv[g][ct];
         }
-#pragma unroll
-      for (int tt = 0; tt < 4; ++tt) {
-        if (wave * 64 + tt * 16 >= NT) break;
-        int tq = tbase + wave * 64 + tt * 16 + r16;
-        tq = tq < s.S ? tq : s.S - 1;
-        float qa[D / 4];
-        const T* qp = Q + ((size_t)bh * s.S + tq) * D + s4 * (D / 4);
-#pragma unroll
-        for (int c = 0; c < D / 16; ++c) {
-          const float4 v = *(const float4*)(qp + 4 * c);
-          qa[4 * c] = v.x;
-          qa[4 * c + 1] = v.y;
-          qa[4 * c + 2] = v.z;
-          qa[4 * c + 3] = v.w;
-        }
-#pragma unroll
-        for (int g = 0; g < G; ++g)
-#pragma unroll
-          for (int ct = 0; ct < CP / 16; ++ct) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kk = 0; kk < D / 4; ++kk)
-              acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[kk], wb[g][ct][kk], acc, 0, 0, 0);
-#pragma unroll
-            for (int k = 0; k < 4; ++k)
-              mu[(wave * 64 + tt * 16 + 4 * s4 + k) * MST + g * CP + ct * 16 + r16] = acc[k] + bv[g][ct];
-          }
       }
     }
-  }
   __syncthreads();
   const bool active = t < s.S;
   const int j = t / s.blk;
@@ -746,7 +717,6 @@ __global__ __launch_bounds__(kProbeThreads) void k_probe_fixed(
   const int base = block_exclusive_scan<NT>(nc, scan_tmp, &total);
   int* clist = (int*)smem;                // [total] (local token << 16) | block
   float* rho = smem + NT * s.M;           // [total]
-  __shared__ int tok_base[NT], tok_n[NT];
   {
     int k = base;
 #pragma unroll
@@ -754,59 +724,68 @@ __global__ __launch_bounds__(kProbeThreads) void k_probe_fixed(
       for (int e = 0; e < take[p]; ++e) clist[k++] = (tid << 16) | idxp[lim[p] - 1 - e];
   }
   __syncthreads();
-  // ---- rerank scores: a quad of lanes per token (tokens quad, quad + NT/4, ...), each lane a
-  // contiguous quarter of D; the quad keeps the token's quarter of q in registers and has up to
-  // four candidates' summary slices in flight; the quarters are added in a fixed order
-  tok_base[tid] = base;
-  tok_n[tid] = nc;
-  __syncthreads();
+  // ---- rerank scores: LPT adjacent lanes share a token (token wave*64 + (64/LPT)m + lane/LPT,
+  // m = 0..LPT-1); lane o = lane%LPT takes dims 4*LPT*c + 4o + e, so the group reads 16*LPT contiguous
+  // bytes of a summary per load.  Several candidates are in flight at a time; the partial dots are
+  // added in a fixed order (xor 1, 2, ...).  The query slices are read again (from L2) rather than
+  // kept live through the selection above, the next token's while the current one is scored.
   {
-    constexpr int NQ = NT / 4;
-    const int quad = tid >> 2, ql = tid & 3;
+    constexpr int LPT = 4;
+    constexpr int NC4 = D / (4 * LPT);   // float4 per candidate per lane
+    constexpr int UB = 16 / NC4;         // candidates in flight
     const float* ksh = ksum + (size_t)bh * s.nb * D;
-    for (int lt = quad; lt < NT; lt += NQ) {
-      const int b0 = tok_base[lt], n0 = tok_n[lt];
-      if (n0 == 0) continue;
-      float qf[D / 4];
-      {
-        const T* qp = Q + ((size_t)bh * s.S + tbase + lt) * D + ql * (D / 4);
+    const int grp = lane / LPT, lo = lane % LPT;
+    using QP = typename std::conditional<BF, uint2, uint4>::type;  // 4 query values
+    auto q_slice = [&](int m, QP (&raw)[NC4]) {
+      int tq = tbase + wave * 64 + (64 / LPT) * m + grp;
+      tq = tq < s.S ? tq : s.S - 1;
+      const T* qp = Q + ((size_t)bh * s.S + tq) * D + 4 * lo;
 #pragma unroll
-        for (int c = 0; c < D / 16; ++c) {
-          if constexpr (std::is_same<T, bf16>::value) {
-            const bf16x4 qb = *(const bf16x4*)(qp + 4 * c);
+      for (int c = 0; c < NC4; ++c) raw[c] = *(const QP*)(qp + 4 * LPT * c);
+    };
+    QP qnext[NC4];
+    q_slice(0, qnext);
+    for (int m = 0; m < LPT; ++m) {
+      const int src = (64 / LPT) * m + grp;
+      const int b0 = __shfl(base, src), n0 = __shfl(nc, src);
+      float qf[4 * NC4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) qf[4 * c + e] = (float)qb[e];
-          } else {
-            const float4 q4 = *(const float4*)(qp + 4 * c);
-            qf[4 * c] = q4.x;
-            qf[4 * c + 1] = q4.y;
-            qf[4 * c + 2] = q4.z;
-            qf[4 * c + 3] = q4.w;
-          }
+      for (int c = 0; c < NC4; ++c) {
+        if constexpr (BF) {
+          const bf16x4 qb = *(const bf16x4*)&qnext[c];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) qf[4 * c + e] = (float)qb[e];
+        } else {
+          const float4 q4 = *(const float4*)&qnext[c];
+          qf[4 * c] = q4.x;
+          qf[4 * c + 1] = q4.y;
+          qf[4 * c + 2] = q4.z;
+          qf[4 * c + 3] = q4.w;
         }
       }
-      for (int k0 = 0; k0 < n0; k0 += 4) {
-        float4 kv[4][D / 16];
+      if (m + 1 < LPT) q_slice(m + 1, qnext);
+      for (int k0 = 0; k0 < n0; k0 += UB) {
+        float4 kv[UB][NC4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int k = b0 + (k0 + u < n0 ? k0 + u : k0);
-          const float4* kr = (const float4*)(ksh + (size_t)(clist[k] & 0xffff) * D + ql * (D / 4));
+        for (int u = 0; u < UB; ++u) {
+          const int i = clist[b0 + (k0 + u < n0 ? k0 + u : k0)] & 0xffff;
+          const float* kr = ksh + (size_t)i * D + 4 * lo;
 #pragma unroll
-          for (int c = 0; c < D / 16; ++c) kv[u][c] = kr[c];
+          for (int c = 0; c < NC4; ++c) kv[u][c] = *(const float4*)(kr + 4 * LPT * c);
         }
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < UB; ++u) {
           float a = 0.f;
 #pragma unroll
-          for (int c = 0; c < D / 16; ++c) {
+          for (int c = 0; c < NC4; ++c) {
             a = fmaf(kv[u][c].x, qf[4 * c], a);
             a = fmaf(kv[u][c].y, qf[4 * c + 1], a);
             a = fmaf(kv[u][c].z, qf[4 * c + 2], a);
             a = fmaf(kv[u][c].w, qf[4 * c + 3], a);
           }
-          a += __shfl_xor(a, 1);
-          a += __shfl_xor(a, 2);
-          if (ql == 0 && k0 + u < n0) rho[b0 + k0 + u] = a;
+#pragma unroll
+          for (int x = 1; x < LPT; x <<= 1) a += __shfl_xor(a, x);
+          if (lo == 0 && k0 + u < n0) rho[b0 + k0 + u] = a;
         }
       }
     }
@@ -824,7 +803,7 @@ __global__ __launch_bounds__(kProbeThreads) void k_probe_fixed(
   for (int r = 0; r < RK; ++r) tri[r] = key_index(trk[r]);
   int nr = nc < R ? nc : R;
   if (force && R > 0) {
-    const int f = force[(size_t)bh * s.S + t];
+    const int f = fv;
     if (f >= 0 && f <= cutoff) {
       bool present = false;
 #pragma unroll
