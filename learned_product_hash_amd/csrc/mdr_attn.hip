@@ -82,22 +82,6 @@ __device__ inline void load_q(QFrag<T, D>& qf, const T* qp, int lane) {
   }
 }
 
-// Stage one block of K and V into LDS, row-major, with 16-byte copies.
-template <typename T, int D, int BLK, int NTHR>
-__device__ inline void load_kv(const T* __restrict__ Kg, const T* __restrict__ Vg, T* Ks, T* Vx, int tid) {
-  using TL = Tile<T, D, BLK>;
-  constexpr int NCH = D / TL::VEC;
-  constexpr int TOTAL = BLK * NCH;
-#pragma unroll
-  for (int c = tid; c < TOTAL; c += NTHR) {
-    const int row = c / NCH, ch = c % NCH;
-    const uint4 kv = *(const uint4*)(Kg + (size_t)row * D + ch * TL::VEC);
-    *(uint4*)(Ks + row * TL::KST + ch * TL::VEC) = kv;
-    const uint4 vv = *(const uint4*)(Vg + (size_t)row * D + ch * TL::VEC);
-    *(uint4*)(Vx + row * TL::VST + ch * TL::VEC) = vv;
-  }
-}
-
 // S^T tile n (keys 16n..16n+15 as rows, the wave's 16 queries as columns).
 template <typename T, int D, int BLK>
 __device__ inline f32x4 score_tile(const QFrag<T, D>& qf, const T* Ks, int n, int lane) {
@@ -187,16 +171,57 @@ __device__ inline void store4(T* dst, const f32x4& v, float mul) {
   }
 }
 
+// Raw 16- and 8-byte register vectors (native vector types, so they stay in registers).
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+// Four consecutive values of T as raw bits (a partial's or an output's column quad).
 template <typename T>
-__device__ inline f32x4 load4(const T* src) {
+using Raw4 = typename std::conditional<std::is_same<T, bf16>::value, u32x2, u32x4>::type;
+
+template <typename T>
+__device__ inline f32x4 unpack4(const Raw4<T>& r) {
   if constexpr (std::is_same<T, bf16>::value) {
-    const bf16x4 b = *(const bf16x4*)src;
+    const bf16x4 b = *(const bf16x4*)&r;
     return f32x4{(float)b[0], (float)b[1], (float)b[2], (float)b[3]};
   } else {
-    const float4 v = *(const float4*)src;
+    const float4 v = *(const float4*)&r;
     return f32x4{v.x, v.y, v.z, v.w};
   }
 }
+
+// One block of K and V held in registers between its global read and its LDS store, so that the
+// read can be issued long before the LDS is free.
+template <typename T, int D, int BLK, int NTHR>
+struct KVRegs {
+  using TL = Tile<T, D, BLK>;
+  static constexpr int NCH = D / TL::VEC;
+  static constexpr int TOTAL = BLK * NCH;
+  static constexpr int NL = (TOTAL + NTHR - 1) / NTHR;
+  u32x4 k[NL], v[NL];
+  __device__ __forceinline__ void load(const T* __restrict__ Kg, const T* __restrict__ Vg, int tid) {
+#pragma unroll
+    for (int u = 0; u < NL; ++u) {
+      const int c = u * NTHR + tid;
+      if (TOTAL % NTHR == 0 || c < TOTAL) {
+        const int row = c / NCH, ch = c % NCH;
+        k[u] = *(const u32x4*)(Kg + (size_t)row * D + ch * TL::VEC);
+        v[u] = *(const u32x4*)(Vg + (size_t)row * D + ch * TL::VEC);
+      }
+    }
+  }
+  __device__ __forceinline__ void store(T* Ks, T* Vx, int tid) const {
+#pragma unroll
+    for (int u = 0; u < NL; ++u) {
+      const int c = u * NTHR + tid;
+      if (TOTAL % NTHR == 0 || c < TOTAL) {
+        const int row = c / NCH, ch = c % NCH;
+        *(u32x4*)(Ks + row * TL::KST + ch * TL::VEC) = k[u];
+        *(u32x4*)(Vx + row * TL::VST + ch * TL::VEC) = v[u];
+      }
+    }
+  }
+};
 
 // ---------------------------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_fill(int32_t* p, long long n, int32_t value) {
@@ -241,6 +266,10 @@ __global__ __launch_bounds__(kRemoteWaves * 64) void k_attn_remote(const T* __re
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int ncell = s.ne - i;
   const long long row0 = (long long)bh * s.cells_per_bh + cell_row(i, s.ne);
+  const size_t rowbase = (size_t)bh * s.S;
+  // the block's K/V is requested before the cell counts are scanned
+  KVRegs<T, D, BLK, NTHR> kv;
+  kv.load(K + (rowbase + (size_t)i * BLK) * D, V + (rowbase + (size_t)i * BLK) * D, tid);
   int run = 0;
   for (int c0 = 0; c0 < ncell; c0 += NTHR) {
     const int c = c0 + tid;
@@ -254,12 +283,11 @@ __global__ __launch_bounds__(kRemoteWaves * 64) void k_attn_remote(const T* __re
   const int total = run;
   const int nit = (total + PER_IT - 1) / PER_IT;
   if ((int)blockIdx.z >= nit) return;  // uniform for the work-group
-  const size_t rowbase = (size_t)bh * s.S;
-  load_kv<T, D, BLK, NTHR>(K + (rowbase + (size_t)i * BLK) * D, V + (rowbase + (size_t)i * BLK) * D, Ks, Vx, tid);
+  kv.store(Ks, Vx, tid);
   __syncthreads();
   const float c = s.scale * kLog2e;
   // pair id of this lane's slot in iteration it (-1 when past the end)
-  auto pair_at = [&](int it) -> int {
+  auto pair_at = [&](int it) __attribute__((always_inline)) -> int {
     const int pidx = it * PER_IT + wave * 16 + (lane & 15);
     if (pidx >= total) return -1;
     int lo = 0, hi = ncell - 1;  // the cell whose range holds pidx
@@ -324,13 +352,20 @@ __global__ __launch_bounds__(kRemoteWaves * 64) void k_attn_remote(const T* __re
   }
 }
 
-// One work-group per query block: local blocks + merge of the remote partials.
+// One work-group per query block: local blocks + merge of the remote partials.  Every read that
+// does not depend on another is issued at the start: the query rows, the first local block of K/V
+// (held in registers until the LDS takes it; each later block is read while the previous one is
+// scored), the selection row and the first kLocalSlots remote partials (their addresses do not
+// depend on the selection; unused ones are ignored).
+constexpr int kLocalSlots = 2;
+
+// bf16 tiles with D <= 64 are held to four waves per SIMD (four 256-thread work-groups per CU).
+constexpr int local_min_waves(int bytes, int D) { return bytes == 2 && D <= 64 ? 4 : 1; }
+
 template <typename T, int D, int BLK>
-__global__ __launch_bounds__(BLK * 4) void k_attn_local(const T* __restrict__ Q, const T* __restrict__ K,
-                                                        const T* __restrict__ V, const int32_t* __restrict__ sel,
-                                                        const T* __restrict__ part_o,
-                                                        const float* __restrict__ part_ml, T* __restrict__ out,
-                                                        Shape s) {
+__global__ __launch_bounds__(BLK * 4) __attribute__((amdgpu_waves_per_eu(local_min_waves((int)sizeof(T), D)))) void k_attn_local(
+    const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, const int32_t* __restrict__ sel,
+    const T* __restrict__ part_o, const float* __restrict__ part_ml, T* __restrict__ out, Shape s) {
   using TL = Tile<T, D, BLK>;
   constexpr int NTHR = BLK * 4;
   extern __shared__ __align__(16) char lds_raw[];
@@ -340,20 +375,40 @@ __global__ __launch_bounds__(BLK * 4) void k_attn_local(const T* __restrict__ Q,
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int qi = wave * 16 + (lane & 15);
   const int t = j * BLK + qi;
+  const int c4 = 4 * (lane >> 4);
   const size_t rowbase = (size_t)bh * s.S;
+  const int j0 = max(0, j - s.L + 1);
+  KVRegs<T, D, BLK, NTHR> kv;
+  kv.load(K + (rowbase + (size_t)j0 * BLK) * D, V + (rowbase + (size_t)j0 * BLK) * D, tid);
   QFrag<T, D> qf;
   load_q<T, D>(qf, Q + (rowbase + t) * D, lane);
+  const int32_t* row = sel + (rowbase + t) * s.R;
+  int sr[kLocalSlots];
+  float2 pml[kLocalSlots];
+  Raw4<T> praw[kLocalSlots][TL::ND];
+#pragma unroll
+  for (int r = 0; r < kLocalSlots; ++r) {
+    if (r < s.R) {
+      const size_t pr = (rowbase + t) * s.R + r;
+      sr[r] = row[r];
+      pml[r] = *(const float2*)(part_ml + 2 * pr);
+#pragma unroll
+      for (int dt = 0; dt < TL::ND; ++dt) praw[r][dt] = *(const Raw4<T>*)(part_o + pr * D + 16 * dt + c4);
+    }
+  }
   const float c = s.scale * kLog2e;
   float m = -INFINITY, l = 0.f;
   f32x4 o[TL::ND];
 #pragma unroll
   for (int dt = 0; dt < TL::ND; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int j0 = max(0, j - s.L + 1);
   for (int jj = j0; jj <= j; ++jj) {
-    if (jj != j0) __syncthreads();
-    load_kv<T, D, BLK, NTHR>(K + (rowbase + (size_t)jj * BLK) * D, V + (rowbase + (size_t)jj * BLK) * D, Ks, Vx,
-                             tid);
+    if (jj != j0) __syncthreads();  // the previous block is no longer read
+    kv.store(Ks, Vx, tid);
     __syncthreads();
+    if (jj < j) {  // the next block's read overlaps this block's softmax
+      const size_t nx = (rowbase + (size_t)(jj + 1) * BLK) * D;
+      kv.load(K + nx, V + nx, tid);
+    }
     f32x4 p[TL::NT];
     float mx = -INFINITY;
 #pragma unroll
@@ -362,7 +417,7 @@ __global__ __launch_bounds__(BLK * 4) void k_attn_local(const T* __restrict__ Q,
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         float v = p[n][k] * c;
-        if (jj == j && 16 * n + 4 * (lane >> 4) + k > qi) v = -INFINITY;
+        if (jj == j && 16 * n + c4 + k > qi) v = -INFINITY;
         p[n][k] = v;
         mx = fmaxf(mx, v);
       }
@@ -385,26 +440,37 @@ __global__ __launch_bounds__(BLK * 4) void k_attn_local(const T* __restrict__ Q,
     for (int dt = 0; dt < TL::ND; ++dt) o[dt] *= alpha;
     pv_block<T, D, BLK>(o, p, Vx, lane);
   }
-  // merge remote partials in slot order
-  const int32_t* row = sel + (rowbase + t) * s.R;
-  for (int r = 0; r < s.R; ++r) {
-    if (!sel_entry_valid(row, r, j, s.L)) continue;
-    const size_t pr = (rowbase + t) * s.R + r;
-    const float2 ml = *(const float2*)(part_ml + 2 * pr);
+  // merge the remote partials in slot order: entry r counts when 0 <= sel <= j - L and it does not
+  // repeat an earlier entry of the row
+  auto merge = [&](float2 ml, const Raw4<T> (&po)[TL::ND]) __attribute__((always_inline)) {
     const float mnew = fmaxf(m, ml.x);
     const float a = exp2f(m - mnew);
     const float b = exp2f(ml.x - mnew) * ml.y;
 #pragma unroll
-    for (int dt = 0; dt < TL::ND; ++dt) {
-      const f32x4 po = load4<T>(part_o + pr * D + 16 * dt + 4 * (lane >> 4));
-      o[dt] = o[dt] * a + po * b;
-    }
+    for (int dt = 0; dt < TL::ND; ++dt) o[dt] = o[dt] * a + unpack4<T>(po[dt]) * b;
     l = l * a + b;
     m = mnew;
+  };
+#pragma unroll
+  for (int r = 0; r < kLocalSlots; ++r) {
+    if (r < s.R) {
+      bool ok = sr[r] >= 0 && sr[r] <= j - s.L;
+#pragma unroll
+      for (int p = 0; p < r; ++p) ok = ok && sr[p] != sr[r];
+      if (ok) merge(pml[r], praw[r]);
+    }
+  }
+  for (int r = kLocalSlots; r < s.R; ++r) {
+    if (!sel_entry_valid(row, r, j, s.L)) continue;
+    const size_t pr = (rowbase + t) * s.R + r;
+    Raw4<T> po[TL::ND];
+#pragma unroll
+    for (int dt = 0; dt < TL::ND; ++dt) po[dt] = *(const Raw4<T>*)(part_o + pr * D + 16 * dt + c4);
+    merge(*(const float2*)(part_ml + 2 * pr), po);
   }
   const float inv = 1.f / l;
 #pragma unroll
-  for (int dt = 0; dt < TL::ND; ++dt) store4<T>(out + (rowbase + t) * D + 16 * dt + 4 * (lane >> 4), o[dt], inv);
+  for (int dt = 0; dt < TL::ND; ++dt) store4<T>(out + (rowbase + t) * D + 16 * dt + c4, o[dt], inv);
 }
 
 template <typename T, int D, int BLK>
