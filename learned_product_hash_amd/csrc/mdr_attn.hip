@@ -152,6 +152,10 @@ __device__ inline void pv_block(f32x4 (&o)[D / 16], const f32x4 (&p)[BLK / 16], 
   }
 }
 
+// 2^x with the hardware instruction alone (no rescaling of denormal results: those flush to zero,
+// which is below anything a softmax weight here can resolve).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 __device__ inline float wave_max16(float x) {
   x = fmaxf(x, __shfl_xor(x, 16));
   return fmaxf(x, __shfl_xor(x, 32));
@@ -316,24 +320,22 @@ __global__ __launch_bounds__(kRemoteWaves * 64) void k_attn_remote(const T* __re
       pv = -1;
     }
     if (it * PER_IT + wave * 16 >= total) break;
+    // softmax in base 2 with the scale folded in: p = 2^(c s - c max s), c = scale * log2(e) > 0
     f32x4 p[TL::NT];
     float mx = -INFINITY;
 #pragma unroll
     for (int n = 0; n < TL::NT; ++n) {
       p[n] = score_tile<T, D, BLK>(qc, Ks, n, lane);
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        p[n][k] *= c;
-        mx = fmaxf(mx, p[n][k]);
-      }
+      for (int k = 0; k < 4; ++k) mx = fmaxf(mx, p[n][k]);
     }
-    mx = wave_max16(mx);
+    mx = c * wave_max16(mx);
     float sum = 0.f;
 #pragma unroll
     for (int n = 0; n < TL::NT; ++n)
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        p[n][k] = exp2f(p[n][k] - mx);
+        p[n][k] = fast_exp2(fmaf(p[n][k], c, -mx));
         sum += p[n][k];
       }
     sum = wave_sum16(sum);
@@ -371,7 +373,8 @@ __global__ __launch_bounds__(BLK * 4) __attribute__((amdgpu_waves_per_eu(local_m
   extern __shared__ __align__(16) char lds_raw[];
   T* Ks = (T*)lds_raw;
   T* Vx = Ks + TL::K_ELEMS;
-  const int j = blockIdx.x, bh = blockIdx.y;
+  const int wg = xcd_chunked(blockIdx.x, gridDim.x);  // query blocks of one head in order per XCD
+  const int j = wg % s.nb, bh = wg / s.nb;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int qi = wave * 16 + (lane & 15);
   const int t = j * BLK + qi;
@@ -401,7 +404,10 @@ __global__ __launch_bounds__(BLK * 4) __attribute__((amdgpu_waves_per_eu(local_m
   f32x4 o[TL::ND];
 #pragma unroll
   for (int dt = 0; dt < TL::ND; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int jj = j0; jj <= j; ++jj) {
+  // one local block: stage it, score it, fold it into the running (m, l, o); only the diagonal
+  // block (jj == j) needs the causal mask
+  auto block_step = [&](auto diag_tag, int jj) __attribute__((always_inline)) {
+    constexpr bool DIAG = decltype(diag_tag)::value;
     if (jj != j0) __syncthreads();  // the previous block is no longer read
     kv.store(Ks, Vx, tid);
     __syncthreads();
@@ -416,21 +422,19 @@ __global__ __launch_bounds__(BLK * 4) __attribute__((amdgpu_waves_per_eu(local_m
       p[n] = score_tile<T, D, BLK>(qf, Ks, n, lane);
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        float v = p[n][k] * c;
-        if (jj == j && 16 * n + c4 + k > qi) v = -INFINITY;
-        p[n][k] = v;
-        mx = fmaxf(mx, v);
+        if (DIAG && 16 * n + c4 + k > qi) p[n][k] = -INFINITY;
+        mx = fmaxf(mx, p[n][k]);
       }
     }
-    mx = wave_max16(mx);
-    const float mnew = fmaxf(m, mx);
-    const float alpha = exp2f(m - mnew);
+    // base-2 softmax with the scale folded in (c = scale * log2(e) > 0); m is kept in scaled units
+    const float mnew = fmaxf(m, c * wave_max16(mx));
+    const float alpha = fast_exp2(m - mnew);
     float sum = 0.f;
 #pragma unroll
     for (int n = 0; n < TL::NT; ++n)
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        p[n][k] = exp2f(p[n][k] - mnew);
+        p[n][k] = fast_exp2(fmaf(p[n][k], c, -mnew));
         sum += p[n][k];
       }
     sum = wave_sum16(sum);
@@ -439,13 +443,15 @@ __global__ __launch_bounds__(BLK * 4) __attribute__((amdgpu_waves_per_eu(local_m
 #pragma unroll
     for (int dt = 0; dt < TL::ND; ++dt) o[dt] *= alpha;
     pv_block<T, D, BLK>(o, p, Vx, lane);
-  }
+  };
+  for (int jj = j0; jj < j; ++jj) block_step(std::false_type{}, jj);
+  block_step(std::true_type{}, j);
   // merge the remote partials in slot order: entry r counts when 0 <= sel <= j - L and it does not
   // repeat an earlier entry of the row
   auto merge = [&](float2 ml, const Raw4<T> (&po)[TL::ND]) __attribute__((always_inline)) {
     const float mnew = fmaxf(m, ml.x);
-    const float a = exp2f(m - mnew);
-    const float b = exp2f(ml.x - mnew) * ml.y;
+    const float a = fast_exp2(m - mnew);
+    const float b = fast_exp2(ml.x - mnew) * ml.y;
 #pragma unroll
     for (int dt = 0; dt < TL::ND; ++dt) o[dt] = o[dt] * a + unpack4<T>(po[dt]) * b;
     l = l * a + b;
@@ -495,7 +501,7 @@ hipError_t attend_impl(const Shape& s, const void* q, const void* k, const void*
   if (lds > 65536 && (e = hipFuncSetAttribute((const void*)k_attn_local<T, D, BLK>,
                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)) != hipSuccess)
     return e;
-  hipLaunchKernelGGL((k_attn_local<T, D, BLK>), dim3(s.nb, s.B * s.H), dim3(BLK * 4), lds, st, (const T*)q,
+  hipLaunchKernelGGL((k_attn_local<T, D, BLK>), dim3(s.nb * s.B * s.H), dim3(BLK * 4), lds, st, (const T*)q,
                      (const T*)k, (const T*)v, sel, (const T*)b.part_o, b.part_ml, (T*)out, s);
   return hipGetLastError();
 }

@@ -82,6 +82,18 @@ __device__ inline void record_pair(int32_t* cellcnt, int32_t* bins, const Shape&
   if (pos < s.blk) bins[cell * s.blk + pos] = t * s.R + r;
 }
 
+// Work-groups are handed to the 8 XCDs of the chip in turn (linear id mod 8), and each XCD has its
+// own L2.  xcd_chunked(id, n) renumbers the n work-groups of a 1-D grid so that each XCD receives a
+// contiguous run of logical indices, in order: neighbours that share data (adjacent query blocks
+// reading the same K/V block) then run on the same XCD at about the same time.  A bijection on
+// [0, n) for any n.
+constexpr int kXcds = 8;
+__device__ inline int xcd_chunked(int id, int n) {
+  const int x = id % kXcds, k = id / kXcds;
+  const int q = n / kXcds, r = n % kXcds;
+  return x * q + min(x, r) + k;
+}
+
 // Exclusive scan of one int per thread over a work-group of NT threads (NT a multiple of 64).
 // tmp holds NT/64 ints.  Returns the exclusive prefix; *total receives the sum.
 template <int NT>

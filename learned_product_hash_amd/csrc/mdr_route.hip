@@ -43,6 +43,9 @@ __device__ inline float to_f(bf16 x) { return (float)x; }
 // 16-byte column chunk; the row groups are then added in a fixed order, so the result is
 // deterministic.  Codes are argmaxes of <codebook[h,g,c], summary> + bias[h,g,c] (first
 // maximum wins), the address is the mixed-radix number with subspace 0 most significant.
+// The codebook rows are requested together with the key rows: four adjacent lanes share one code
+// (each a quarter of D, added in a fixed order), and one wave finds each subspace's argmax with
+// a butterfly over (logit, code).
 template <typename T, int D>
 __global__ __launch_bounds__(256) void k_address(const T* __restrict__ K, const float* __restrict__ cb,
                                                  const float* __restrict__ bias, float* __restrict__ ksum,
@@ -51,25 +54,48 @@ __global__ __launch_bounds__(256) void k_address(const T* __restrict__ K, const 
   constexpr int VEC = Vec16<T>::n;
   constexpr int NCH = D / VEC;
   constexpr int RG = 256 / NCH;
+  constexpr int LPC = 256 / kMaxCodesTotal;  // lanes per code
+  constexpr int DPL = D / LPC;               // codebook dims per lane
+  static_assert(DPL % 4 == 0, "whole float4 per lane");
   __shared__ float red[RG][D + 1];
   __shared__ float kbar[D];
   __shared__ float logit[kMaxCodesTotal];
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
   const int i = blockIdx.x;
   const int bh = blockIdx.y;
   const int h = bh % s.H;
+  const int GC = s.G * s.C;
+  // codebook slice of this lane: code cc, dims [part * DPL, (part + 1) * DPL)
+  const int cc = tid / LPC, part = tid % LPC;
+  float w[DPL];
+  {
+    const float* wr = cb + ((size_t)h * GC + (cc < GC ? cc : 0)) * D + part * DPL;
+#pragma unroll
+    for (int d = 0; d < DPL; d += 4) {
+      const float4 v = *(const float4*)(wr + d);
+      w[d] = v.x;
+      w[d + 1] = v.y;
+      w[d + 2] = v.z;
+      w[d + 3] = v.w;
+    }
+  }
+  const float bv = (bias && cc < GC) ? bias[h * GC + cc] : 0.f;
   const T* base = K + ((size_t)bh * s.S + (size_t)i * s.blk) * D;
   const int ch = tid % NCH, rg = tid / NCH;
-  float part[VEC];
+  float acc4[VEC];
 #pragma unroll
-  for (int e = 0; e < VEC; ++e) part[e] = 0.f;
+  for (int e = 0; e < VEC; ++e) acc4[e] = 0.f;
   for (int r = rg; r < s.blk; r += RG) {
     typename Vec16<T>::type v = *(const typename Vec16<T>::type*)(base + (size_t)r * D + ch * VEC);
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) part[e] += to_f(v[e]);
+    for (int e = 0; e < VEC; ++e) acc4[e] += to_f(v[e]);
   }
 #pragma unroll
-  for (int e = 0; e < VEC; ++e) red[rg][ch * VEC + e] = part[e];
+  for (int e = 0; e < VEC; ++e) red[rg][ch * VEC + e] = acc4[e];
+  if (cell_zero && i < s.ne) {
+    int32_t* row = cell_zero + (size_t)bh * s.cells_per_bh + cell_row(i, s.ne);
+    for (int c = tid; c < s.ne - i; c += 256) row[c] = 0;
+  }
   __syncthreads();
   if (tid < D) {
     float acc = 0.f;
@@ -79,35 +105,34 @@ __global__ __launch_bounds__(256) void k_address(const T* __restrict__ K, const 
     ksum[((size_t)bh * s.nb + i) * D + tid] = m;
   }
   __syncthreads();
-  const int GC = s.G * s.C;
-  if (tid < GC) {
-    const float* w = cb + ((size_t)h * GC + tid) * D;
+  {
     float acc = 0.f;
-#pragma unroll 8
-    for (int d = 0; d < D; ++d) acc = fmaf(w[d], kbar[d], acc);
-    if (bias) acc += bias[h * GC + tid];
-    logit[tid] = acc;
+#pragma unroll
+    for (int d = 0; d < DPL; ++d) acc = fmaf(w[d], kbar[part * DPL + d], acc);
+#pragma unroll
+    for (int x = 1; x < LPC; x <<= 1) acc += __shfl_xor(acc, x);
+    if (part == 0 && cc < GC) logit[cc] = acc + bv;
   }
   __syncthreads();
-  if (tid == 0) {
+  if (tid < 64) {
     int a = 0;
     for (int g = 0; g < s.G; ++g) {
-      int best = 0;
-      float bv = logit[g * s.C];
-      for (int c = 1; c < s.C; ++c) {
-        const float v = logit[g * s.C + c];
-        if (v > bv) {
-          bv = v;
-          best = c;
+      // lanes 0..C-1 hold the subspace's logits; the butterfly keeps the larger logit, the
+      // smaller code on ties
+      float v = lane < s.C ? logit[g * s.C + lane] : -INFINITY;
+      int c = lane < s.C ? lane : 0x7fffffff;
+#pragma unroll
+      for (int x = 32; x >= 1; x >>= 1) {
+        const float ov = __shfl_xor(v, x);
+        const int oc = __shfl_xor(c, x);
+        if (ov > v || (ov == v && oc < c)) {
+          v = ov;
+          c = oc;
         }
       }
-      a = a * s.C + best;
+      a = a * s.C + c;
     }
-    addr[(size_t)bh * s.nb + i] = a;
-  }
-  if (cell_zero && i < s.ne) {
-    int32_t* row = cell_zero + (size_t)bh * s.cells_per_bh + cell_row(i, s.ne);
-    for (int c = tid; c < s.ne - i; c += 256) row[c] = 0;
+    if (tid == 0) addr[(size_t)bh * s.nb + i] = a;
   }
 }
 
