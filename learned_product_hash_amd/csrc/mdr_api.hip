@@ -149,10 +149,14 @@ mdr_status run_core(const Shape& s, const void* q, const void* k, const void* v,
   if (ev) MDR_TRY(hipEventRecord(ev[0], st));
   MDR_TRY(launch_address(s, k, cb, bias, b.ksum, b.addr, remote ? b.cellcnt : nullptr, st));
   if (ev) MDR_TRY(hipEventRecord(ev[1], st));
-  MDR_TRY(launch_post(s, b.addr, b.off, b.idx, b.overflow, st));
+  // the posting lists are built inside the probe kernel where a specialised probe exists (the post
+  // interval of a profiled call is then empty)
+  const bool fused = probe_fuses_post(s);
+  if (!fused) MDR_TRY(launch_post(s, b.addr, b.off, b.idx, b.overflow, st));
   if (ev) MDR_TRY(hipEventRecord(ev[2], st));
+  const FusedPost fp{b.addr, b.off, b.idx, b.overflow};
   MDR_TRY(launch_probe_rerank(s, q, cb, bias, b.ksum, b.off, b.idx, force, b.sel, b.ncand,
-                              remote ? b.cellcnt : nullptr, remote ? b.bins : nullptr, st));
+                              remote ? b.cellcnt : nullptr, remote ? b.bins : nullptr, st, fused ? &fp : nullptr));
   MDR_TRY(launch_attend(s, q, k, v, b.sel, out, b, st, ev ? ev + 3 : nullptr));
   if (ev) MDR_TRY(hipEventRecord(ev[MDR_CORE_KERNELS], st));
   return MDR_OK;

@@ -125,10 +125,20 @@ hipError_t launch_address(const Shape& s, const void* k, const float* codebook, 
                           float* ksum, int32_t* addr, int32_t* cell_zero, hipStream_t st);
 hipError_t launch_post(const Shape& s, const int32_t* addr, int32_t* off, int32_t* idx,
                        int32_t* overflow, hipStream_t st);
+// Posting lists built inside the probe kernel (from the block addresses) instead of read: every
+// work-group builds its (b,h)'s CSR in LDS and work-group 0 of each (b,h) also writes it out.
+struct FusedPost {
+  const int32_t* addr;
+  int32_t* off;
+  int32_t* idx;
+  int32_t* overflow;
+};
 hipError_t launch_probe_rerank(const Shape& s, const void* q, const float* codebook, const float* bias,
                                const float* ksum, const int32_t* off, const int32_t* idx,
                                const int32_t* force, int32_t* sel, int32_t* ncand, int32_t* cellcnt,
-                               int32_t* bins, hipStream_t st);
+                               int32_t* bins, hipStream_t st, const FusedPost* fuse = nullptr);
+// True when launch_probe_rerank accepts `fuse` for this shape (the compile-time specialised probe).
+bool probe_fuses_post(const Shape& s);
 size_t probe_lds_bytes(const Shape& s);
 bool probe_fixed_shape(const Shape& s);
 hipError_t launch_fill(int32_t* p, long long n, int32_t value, hipStream_t st);

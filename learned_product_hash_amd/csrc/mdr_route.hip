@@ -147,6 +147,7 @@ __global__ __launch_bounds__(256) void k_post(const int32_t* __restrict__ addr, 
                                               int32_t* __restrict__ idx, int32_t* __restrict__ overflow,
                                               Shape s) {
   __shared__ int hist[kMaxAddresses];
+  __shared__ int ads[kMaxBlocks];  // this (b,h)'s addresses, read from global memory once
   __shared__ int part[4];
   __shared__ int total;
   const int tid = threadIdx.x;
@@ -155,9 +156,10 @@ __global__ __launch_bounds__(256) void k_post(const int32_t* __restrict__ addr, 
   const int n_elig = s.nb > s.L ? s.nb - s.L : 0;
   const int32_t* ad = addr + (size_t)bh * s.nb;
   for (int a = tid; a < A; a += 256) hist[a] = 0;
+  for (int i = tid; i < n_elig; i += 256) ads[i] = ad[i];
   __syncthreads();
   for (int i = tid; i < n_elig; i += 256) {
-    const int a = ad[i];
+    const int a = ads[i];
     if (a >= 0 && a < A) atomicAdd(&hist[a], 1);  // out-of-range addresses are not filed
   }
   __syncthreads();
@@ -192,7 +194,7 @@ __global__ __launch_bounds__(256) void k_post(const int32_t* __restrict__ addr, 
     const unsigned long long lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     for (int c0 = 0; c0 < n_elig; c0 += kWave) {
       const int i = c0 + lane;
-      int a = i < n_elig ? ad[i] : -1;
+      int a = i < n_elig ? ads[i] : -1;
       const bool valid = a >= 0 && a < A;
       if (!valid) a = 0;
       unsigned long long same = __ballot(valid);
@@ -514,6 +516,82 @@ struct RankSpace {
   }
 };
 
+// Posting lists of one (b,h) built in LDS from its block addresses ads[0..ne) (the filed blocks),
+// with the semantics of k_post: counts per address, exclusive offsets, then a stable scatter by
+// wave 0 (per 64-block chunk a lane's slot is the number of earlier lanes with the same address,
+// found with one ballot per address bit, plus that address's running cursor), so each list holds
+// its blocks in ascending order.  cur [A] is scratch.  Ends with a barrier.  When `publish`, the
+// work-group also writes the CSR (with -1 beyond the filed entries) and the overflow count.
+template <int NT>
+__device__ void build_posting_csr(const int* ads, int* cur, int* offl, int* idxl, const Shape& s, int bh,
+                                  bool publish, const FusedPost& fp) {
+  const int tid = threadIdx.x;
+  const int A = s.A, ne = s.ne;
+  for (int a = tid; a <= A; a += NT) offl[a] = 0;
+  __syncthreads();
+  for (int i = tid; i < ne; i += NT) {
+    const int a = ads[i];
+    if (a >= 0 && a < A) atomicAdd(&offl[a], 1);
+  }
+  __syncthreads();
+  // thread tid owns the contiguous address segment [a0, a1)
+  __shared__ int part[NT / 64];
+  const int seg = (A + NT - 1) / NT;
+  const int a0 = min(A, tid * seg), a1 = min(A, a0 + seg);
+  int sum = 0, over = 0;
+  for (int a = a0; a < a1; ++a) {
+    const int n = offl[a];
+    sum += n;
+    over += max(0, n - s.cap);
+  }
+  int tot = 0, tot_over = 0;
+  int run = block_exclusive_scan<NT>(sum, part, &tot);
+  if (publish) block_exclusive_scan<NT>(over, part, &tot_over);
+  for (int a = a0; a < a1; ++a) {
+    const int n = offl[a];
+    offl[a] = run;
+    cur[a] = run;
+    run += n;
+  }
+  if (tid == 0) offl[A] = tot;
+  __syncthreads();
+  if (tid < 64) {
+    const int lane = tid;
+    int nbits = 0;
+    while ((1 << nbits) < A) ++nbits;
+    const unsigned long long lt = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+    for (int c0 = 0; c0 < ne; c0 += 64) {
+      const int i = c0 + lane;
+      int a = i < ne ? ads[i] : -1;
+      const bool valid = a >= 0 && a < A;
+      if (!valid) a = 0;
+      unsigned long long same = __ballot(valid);
+      for (int b = 0; b < nbits; ++b) {
+        const bool bit = (a >> b) & 1;
+        const unsigned long long m1 = __ballot(bit);
+        same &= bit ? m1 : ~m1;
+      }
+      if (valid) {
+        const int rank = __popcll(same & lt);
+        const int count = __popcll(same);
+        const int c = cur[a];
+        idxl[c + rank] = i;
+        __builtin_amdgcn_wave_barrier();
+        if (rank == count - 1) cur[a] = c + count;
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
+  }
+  __syncthreads();
+  if (publish) {
+    int32_t* og = fp.off + (size_t)bh * (A + 1);
+    int32_t* ig = fp.idx + (size_t)bh * s.nb;
+    for (int a = tid; a <= A; a += NT) og[a] = offl[a];
+    for (int i = tid; i < s.nb; i += NT) ig[i] = i < tot ? idxl[i] : -1;
+    if (tid == 0) fp.overflow[bh] = tot_over;
+  }
+}
+
 // Lane layout of the MFMA operands below: lane l = 16 s4 + r16 holds D/4 dims of one row (a token
 // of Q or a code of the codebook).  bf16: dims 32kk + 8 s4 + e (the k-slots of v_mfma_f32_16x16x32_bf16);
 // fp32: dims s4 (D/4) + x (one k-step of v_mfma_f32_16x16x4f32 per x).
@@ -525,12 +603,12 @@ __device__ inline int operand_dim(int s4, int x) {
 // Small bf16 shapes keep four waves per SIMD, so that eight 128-token work-groups share a CU.
 constexpr int probe_min_waves(int bytes, int D, int C) { return bytes == 2 && D <= 64 && C <= 16 ? 4 : 1; }
 
-template <typename T, int D, int G, int C, int P, int R>
+template <typename T, int D, int G, int C, int P, int R, bool FUSED>
 __global__ __launch_bounds__(kProbeThreads) __attribute__((amdgpu_waves_per_eu(probe_min_waves((int)sizeof(T), D, C)))) void k_probe_fixed(
     const T* __restrict__ Q, const float* __restrict__ cb, const float* __restrict__ bias,
     const float* __restrict__ ksum, const int32_t* __restrict__ off, const int32_t* __restrict__ idx,
     const int32_t* __restrict__ force, int32_t* __restrict__ sel, int32_t* __restrict__ ncand,
-    int32_t* __restrict__ cellcnt, int32_t* __restrict__ bins, Shape s) {
+    int32_t* __restrict__ cellcnt, int32_t* __restrict__ bins, FusedPost fp, Shape s) {
   constexpr int NT = kProbeThreads;
   static_assert(NT % 64 == 0, "whole waves of 64 tokens");
   constexpr bool BF = std::is_same<T, bf16>::value;
@@ -551,12 +629,17 @@ __global__ __launch_bounds__(kProbeThreads) __attribute__((amdgpu_waves_per_eu(p
   // rows and biases of this lane's codes, the query rows of this lane's four 16-token tiles
   const int32_t* og = off + (size_t)bh * (A + 1);
   const int32_t* ig = idx + (size_t)bh * s.nb;
+  const int32_t* ag = FUSED ? fp.addr + (size_t)bh * s.nb : nullptr;
   const int ncsr = A + 1 + s.ne;
+  const int nread = FUSED ? s.ne : ncsr;  // addresses of the filed blocks, or the CSR itself
   int cv[8];
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
     const int k = u * NT + tid;
-    cv[u] = k < ncsr ? (k <= A ? og[k] : ig[k - A - 1]) : 0;
+    if (FUSED)
+      cv[u] = k < nread ? ag[k] : 0;
+    else
+      cv[u] = k < nread ? (k <= A ? og[k] : ig[k - A - 1]) : 0;
   }
   const float* cbh = cb + (size_t)h * G * C * D;
   float wv[G][CP / 16][DQ];
@@ -589,25 +672,31 @@ __global__ __launch_bounds__(kProbeThreads) __attribute__((amdgpu_waves_per_eu(p
   }
   int fv = -1;
   if (force && R > 0 && t < s.S) fv = force[(size_t)bh * s.S + t];
-  // ---- the posting-list CSR into LDS (this kernel is only used when it fits)
+  // ---- the posting-list CSR into LDS (this kernel is only used when it fits): read as is, or
+  // built here from the addresses (FUSED), in the mu region, before the logits need it
+  int* stage = FUSED ? (int*)mu : csr;  // addresses [ne] and list cursors [A] | the CSR
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
     const int k = u * NT + tid;
-    if (k < ncsr) csr[k] = cv[u];
+    if (k < nread) stage[k] = cv[u];
   }
-  for (int k0 = 8 * NT; k0 < ncsr; k0 += 8 * NT) {
+  for (int k0 = 8 * NT; k0 < nread; k0 += 8 * NT) {
     int v[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int k = k0 + u * NT + tid;
-      v[u] = k < ncsr ? (k <= A ? og[k] : ig[k - A - 1]) : 0;
+      if (FUSED)
+        v[u] = k < nread ? ag[k] : 0;
+      else
+        v[u] = k < nread ? (k <= A ? og[k] : ig[k - A - 1]) : 0;
     }
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int k = k0 + u * NT + tid;
-      if (k < ncsr) csr[k] = v[u];
+      if (k < nread) stage[k] = v[u];
     }
   }
+  if constexpr (FUSED) build_posting_csr<NT>(stage, stage + s.ne, csr, csr + A + 1, s, bh, blockIdx.x == 0, fp);
   const int* offp = csr;
   const int* idxp = csr + A + 1;
   // ---- mu on MFMA: lane l receives mu[token 16tt + 4(l/16) + k][code 16ct + l%16].  fp32 inputs use
@@ -873,20 +962,34 @@ hipError_t address_dispatch(const Shape& s, const void* k, const float* cb, cons
   return hipGetLastError();
 }
 
-template <typename T, int D, int G, int C, int P, int R>
-hipError_t probe_fixed_launch(const Shape& s, const void* q, const float* cb, const float* bias, const float* ksum,
-                              const int32_t* off, const int32_t* idx, const int32_t* force, int32_t* sel,
-                              int32_t* ncand, int32_t* cellcnt, int32_t* bins, hipStream_t st) {
+template <typename T, int D, int G, int C, int P, int R, bool FUSED>
+hipError_t probe_fixed_launch_t(const Shape& s, const void* q, const float* cb, const float* bias, const float* ksum,
+                                const int32_t* off, const int32_t* idx, const int32_t* force, int32_t* sel,
+                                int32_t* ncand, int32_t* cellcnt, int32_t* bins, const FusedPost& fp,
+                                hipStream_t st) {
   dim3 grid((s.S + kProbeThreads - 1) / kProbeThreads, s.B * s.H);
   const size_t lds = probe_lds_bytes(s);
   if (lds > 65536) {
-    hipError_t e = hipFuncSetAttribute((const void*)k_probe_fixed<T, D, G, C, P, R>,
+    hipError_t e = hipFuncSetAttribute((const void*)k_probe_fixed<T, D, G, C, P, R, FUSED>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((k_probe_fixed<T, D, G, C, P, R>), grid, dim3(kProbeThreads), lds, st, (const T*)q, cb, bias,
-                     ksum, off, idx, force, sel, ncand, cellcnt, bins, s);
+  hipLaunchKernelGGL((k_probe_fixed<T, D, G, C, P, R, FUSED>), grid, dim3(kProbeThreads), lds, st, (const T*)q, cb,
+                     bias, ksum, off, idx, force, sel, ncand, cellcnt, bins, fp, s);
   return hipGetLastError();
+}
+
+template <typename T, int D, int G, int C, int P, int R>
+hipError_t probe_fixed_launch(const Shape& s, const void* q, const float* cb, const float* bias, const float* ksum,
+                              const int32_t* off, const int32_t* idx, const int32_t* force, int32_t* sel,
+                              int32_t* ncand, int32_t* cellcnt, int32_t* bins, const FusedPost* fuse,
+                              hipStream_t st) {
+  if (fuse)
+    return probe_fixed_launch_t<T, D, G, C, P, R, true>(s, q, cb, bias, ksum, off, idx, force, sel, ncand, cellcnt,
+                                                         bins, *fuse, st);
+  const FusedPost none{nullptr, nullptr, nullptr, nullptr};
+  return probe_fixed_launch_t<T, D, G, C, P, R, false>(s, q, cb, bias, ksum, off, idx, force, sel, ncand, cellcnt,
+                                                        bins, none, st);
 }
 
 // Shapes with a compile-time specialisation (the five workload families); others use k_probe_rerank.
@@ -900,13 +1003,15 @@ hipError_t probe_fixed_launch(const Shape& s, const void* q, const float* cb, co
 template <typename T>
 hipError_t probe_dispatch(const Shape& s, const void* q, const float* cb, const float* bias, const float* ksum,
                           const int32_t* off, const int32_t* idx, const int32_t* force, int32_t* sel,
-                          int32_t* ncand, int32_t* cellcnt, int32_t* bins, hipStream_t st) {
+                          int32_t* ncand, int32_t* cellcnt, int32_t* bins, const FusedPost* fuse,
+                          hipStream_t st) {
 #define MDR_FIXED(TT, DD, GG, CC, PP, RR)                                                                        \
   if (std::is_same<T, TT>::value && s.D == DD && s.G == GG && s.C == CC && s.P == PP && s.R == RR && s.fixed_probe) \
     return probe_fixed_launch<TT, DD, GG, CC, PP, RR>(s, q, cb, bias, ksum, off, idx, force, sel, ncand, cellcnt, \
-                                                      bins, st);
+                                                      bins, fuse, st);
   MDR_PROBE_FIXED_SHAPES(MDR_FIXED)
 #undef MDR_FIXED
+  if (fuse) return hipErrorInvalidValue;  // only the specialised probe builds the lists itself
   dim3 grid((s.S + kProbeThreads - 1) / kProbeThreads, s.B * s.H);
   const size_t lds = probe_lds_bytes(s);
   const void* fn = nullptr;
@@ -977,10 +1082,17 @@ hipError_t launch_post(const Shape& s, const int32_t* addr, int32_t* off, int32_
 
 hipError_t launch_probe_rerank(const Shape& s, const void* q, const float* codebook, const float* bias,
                                const float* ksum, const int32_t* off, const int32_t* idx, const int32_t* force,
-                               int32_t* sel, int32_t* ncand, int32_t* cellcnt, int32_t* bins, hipStream_t st) {
+                               int32_t* sel, int32_t* ncand, int32_t* cellcnt, int32_t* bins, hipStream_t st,
+                               const FusedPost* fuse) {
   if (s.dtype == MDR_BF16)
-    return probe_dispatch<bf16>(s, q, codebook, bias, ksum, off, idx, force, sel, ncand, cellcnt, bins, st);
-  return probe_dispatch<float>(s, q, codebook, bias, ksum, off, idx, force, sel, ncand, cellcnt, bins, st);
+    return probe_dispatch<bf16>(s, q, codebook, bias, ksum, off, idx, force, sel, ncand, cellcnt, bins, fuse, st);
+  return probe_dispatch<float>(s, q, codebook, bias, ksum, off, idx, force, sel, ncand, cellcnt, bins, fuse, st);
+}
+
+bool probe_fuses_post(const Shape& s) {
+  // the fixed probe stages the addresses and list cursors in its mu region
+  const int CP = (s.C + 15) & ~15;
+  return s.fixed_probe && (long long)s.ne + s.A <= (long long)kProbeThreads * (s.G * CP + 1);
 }
 
 }  // namespace mdr

@@ -149,6 +149,9 @@ def test_routed_attention_end_to_end(gpu_lib, name):
             if na == 0:
                 assert res["overflow"][b, h] == r["overflow"]
                 assert np.array_equal(res["post_off"][b, h], r["off"])
+                n_filed = len(r["idx"])
+                assert np.array_equal(res["post_idx"][b, h][:n_filed], r["idx"])
+                assert np.all(res["post_idx"][b, h][n_filed:] == -1)
                 near_s += compare_selection(r, res["sel"][b, h])
             ref = attention_rows(w, inp, res["sel"][b, h], b, h, None, dense=w.seq <= 4096)
             err = max(err, float(np.abs(res["out"][b, h] - ref).max()))
