@@ -98,6 +98,7 @@ class HipEvents:
         self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
         self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
 
     def create(self, n):
         out = []
@@ -109,6 +110,10 @@ class HipEvents:
                 raise RuntimeError("hipEventCreateWithFlags failed")
             out.append(h.value)
         return out
+
+    def record(self, ev, stream):
+        if self.hip.hipEventRecord(ev, stream) != 0:
+            raise RuntimeError("hipEventRecord failed")
 
     def elapsed_ms(self, a, b):
         ms = self.ct.c_float()
@@ -234,6 +239,21 @@ def load_traffic(w, kernel):
     return k["bytes_per_launch"]
 
 
+def attention_stage(w, t_att):
+    """The selected-set attention (remote + local kernels) against the HBM peak, two ways:
+    (i) compulsory bytes (Q, K, V, O once + sel) / time; (ii) measured HBM bytes (FETCH_SIZE +
+    WRITE_SIZE of both kernels, when counters for these sources exist) / time."""
+    alg = stage_bytes(w)
+    out = {"ms": round(t_att, 5), "alg_bytes": alg,
+           "frac_of_hbm_peak": round(alg / (t_att * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+    tr = [load_traffic(w, k) for k in ("attn_remote", "attn_local")]
+    if all(t is not None for t in tr):
+        gbps = sum(tr) / (t_att * 1e-3) / 1e9
+        out.update(measured_bytes=round(sum(tr)), measured_gbps=round(gbps, 1),
+                   measured_frac_of_hbm_peak=round(gbps / HBM_PEAK_GBPS, 4))
+    return out
+
+
 # ----------------------------------------------------------------------------- timing
 
 def timed_region(run, hip, steps, warmup):
@@ -251,12 +271,25 @@ def timed_region(run, hip, steps, warmup):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     per = [0.0] * nk
+    totals = []
     for s in range(steps):
         ev = events[s * (nk + 1):(s + 1) * (nk + 1)]
         for i in range(nk):
             per[i] += hip.elapsed_ms(ev[i], ev[i + 1])
+        totals.append(hip.elapsed_ms(ev[0], ev[nk]))
     hip.destroy(events)
-    return wall, [p / steps for p in per]
+    run.step_quantiles = [round(float(x), 4) for x in __import__("numpy").percentile(totals, [10, 50, 90])]
+    # an interval between two events also holds the second event's own cost on the stream; measure
+    # it with back-to-back pairs on the same stream and take it off every kernel interval
+    pairs = hip.create(2 * steps)
+    stream = torch.cuda.current_stream().cuda_stream
+    for s in range(steps):
+        hip.record(pairs[2 * s], stream)
+        hip.record(pairs[2 * s + 1], stream)
+    torch.cuda.synchronize()
+    overhead = sum(hip.elapsed_ms(pairs[2 * s], pairs[2 * s + 1]) for s in range(steps)) / steps
+    hip.destroy(pairs)
+    return wall, [max(0.0, p / steps - overhead) for p in per], overhead
 
 
 def plain_region(run, steps):
@@ -279,16 +312,18 @@ def attended_pairs(w, pairs):
     return pairs * w.block + w.batch * w.heads * int((t - lo + 1).sum())
 
 
-def exponent_sweep(mdr, hip, seqs, seed):
+def exponent_sweep(mdr, seqs, seed):
     """OLS slope of ln(time) against ln(S), and against ln(attended pairs), over the sweep lengths."""
     import numpy as np
 
     rows = []
     for s in seqs:
         run = Run(mdr, make_workload("sweep", s), seed)
-        _, per = timed_region(run, hip, 20, 3)
+        for _ in range(3):
+            run.step()
+        ms = plain_region(run, 20) / 20 * 1e3  # wall time per call of the plain entry point
         st = run.routing_stats()
-        rows.append(dict(seq=s, ms=sum(per), R_eff=st["R_eff"], overflow=st["overflow"],
+        rows.append(dict(seq=s, ms=ms, R_eff=st["R_eff"], overflow=st["overflow"],
                          attended=attended_pairs(run.w, st["pairs"])))
         del run
     lt = np.log([r["ms"] for r in rows])
@@ -427,7 +462,7 @@ def main(argv=None):
         torch.cuda.synchronize()
         del src, dst
     run = Run(mdr, w, a.seed)
-    wall, per = timed_region(run, hip, a.steps, a.warmup)
+    wall, per, ev_overhead = timed_region(run, hip, a.steps, a.warmup)
     plain = plain_region(run, a.steps)
     st = run.routing_stats()
     names = list(mdr.CORE_KERNELS)
@@ -460,13 +495,14 @@ def main(argv=None):
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": None if traffic is None else round(traffic)},
         "kernels": kernels,
-        "attention_stage": {"ms": round(t_att, 5), "alg_bytes": stage_bytes(w),
-                            "frac_of_hbm_peak": round(stage_bytes(w) / (t_att * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)},
+        "attention_stage": attention_stage(w, t_att),
         "plain_entry_point_ms_per_step": round(plain / a.steps * 1e3, 4),
+        "event_overhead_ms": round(ev_overhead, 5),
+        "profiled_step_ms_p10_p50_p90": run.step_quantiles,
         "routing": st,
     }
     if not a.no_sweep and a.workload == "sweep":
-        res["exponent"] = exponent_sweep(mdr, hip, (4096, 8192, 16384, 32768), a.seed)
+        res["exponent"] = exponent_sweep(mdr, (4096, 8192, 16384, 32768), a.seed)
     if not a.no_cpu:
         res["cpu_baseline"] = cpu_baseline(run, a.cpu_heads)
     print(json.dumps(res))
