@@ -905,39 +905,72 @@ __global__ __launch_bounds__(kProbeThreads) __attribute__((amdgpu_waves_per_eu(p
     }
   }
   __syncthreads();
-  if (!active) return;  // no barriers below
   // ---- top-R of the token's candidates by (score desc, block asc)
   constexpr int RK = R > 0 ? R : 1;
-  uint64_t trk[RK];
-#pragma unroll
-  for (int r = 0; r < RK; ++r) trk[r] = 0;
-  for (int k = base; k < base + nc; ++k) insert_key<RK>(trk, rank_key(rho[k], clist[k] & 0xffff));
   int tri[RK];
+  int nr = 0;
+  if (active) {
+    uint64_t trk[RK];
 #pragma unroll
-  for (int r = 0; r < RK; ++r) tri[r] = key_index(trk[r]);
-  int nr = nc < R ? nc : R;
-  if (force && R > 0) {
-    const int f = fv;
-    if (f >= 0 && f <= cutoff) {
-      bool present = false;
+    for (int r = 0; r < RK; ++r) trk[r] = 0;
+    for (int k = base; k < base + nc; ++k) insert_key<RK>(trk, rank_key(rho[k], clist[k] & 0xffff));
 #pragma unroll
-      for (int r = 0; r < (R > 0 ? R : 1); ++r) present |= (r < nr && tri[r] == f);
-      if (!present) {
-        const int slot = nr < R ? nr : R - 1;
+    for (int r = 0; r < RK; ++r) tri[r] = key_index(trk[r]);
+    nr = nc < R ? nc : R;
+    if (force && R > 0) {
+      const int f = fv;
+      if (f >= 0 && f <= cutoff) {
+        bool present = false;
 #pragma unroll
-        for (int r = 0; r < (R > 0 ? R : 1); ++r)
-          if (r == slot) tri[r] = f;
-        nr = nr < R ? nr + 1 : R;
+        for (int r = 0; r < RK; ++r) present |= (r < nr && tri[r] == f);
+        if (!present) {
+          const int slot = nr < R ? nr : R - 1;
+#pragma unroll
+          for (int r = 0; r < RK; ++r)
+            if (r == slot) tri[r] = f;
+          nr = nr < R ? nr + 1 : R;
+        }
       }
     }
+    int32_t* srow = sel + ((size_t)bh * s.S + t) * R;
+#pragma unroll
+    for (int r = 0; r < R; ++r) srow[r] = r < nr ? tri[r] : -1;
+    if (ncand) ncand[(size_t)bh * s.S + t] = nc;
   }
-  int32_t* srow = sel + ((size_t)bh * s.S + t) * R;
+  if (!bins) return;  // uniform
+  // ---- file each selected pair in its (remote block i, query block j) cell.  The work-group owns
+  // the cells of its query blocks, so when they fit (in the place of mu) it counts them in LDS, stores
+  // each pair at the slot that count gives, and then writes the non-zero counts (the address kernel
+  // has cleared all of them); otherwise it appends with global atomics.
+  const int nqb = NT / s.blk;  // whole query blocks per work-group
+  if (nqb * s.ne <= NT * MST) {
+    int* cnt = (int*)mu;  // [nqb][ne]
+    __syncthreads();      // every rho / clist read is done
+    for (int c = tid; c < nqb * s.ne; c += NT) cnt[c] = 0;
+    __syncthreads();
+    const int jb = tbase / s.blk;
+    if (active) {
 #pragma unroll
-  for (int r = 0; r < R; ++r) srow[r] = r < nr ? tri[r] : -1;
-  if (ncand) ncand[(size_t)bh * s.S + t] = nc;
-  if (bins) {
+      for (int r = 0; r < RK; ++r) {
+        if (r < nr) {
+          const int i = tri[r];
+          const int pos = atomicAdd(&cnt[(j - jb) * s.ne + i], 1);
+          const long long cell = (long long)bh * s.cells_per_bh + cell_row(i, s.ne) + (j - i - s.L);
+          if (pos < s.blk) bins[cell * s.blk + pos] = t * s.R + r;
+        }
+      }
+    }
+    __syncthreads();
+    for (int c = tid; c < nqb * s.ne; c += NT) {
+      const int n = cnt[c];
+      if (n > 0) {
+        const int jj = jb + c / s.ne, i = c % s.ne;
+        cellcnt[(long long)bh * s.cells_per_bh + cell_row(i, s.ne) + (jj - i - s.L)] = n;
+      }
+    }
+  } else if (active) {
 #pragma unroll
-    for (int r = 0; r < R; ++r)
+    for (int r = 0; r < RK; ++r)
       if (r < nr) record_pair(cellcnt, bins, s, bh, tri[r], j, t, r);
   }
 }
