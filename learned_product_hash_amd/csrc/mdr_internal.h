@@ -94,6 +94,15 @@ __device__ inline int xcd_chunked(int id, int n) {
   return x * q + min(x, r) + k;
 }
 
+// Work-group barrier that orders LDS accesses only: global loads still in flight stay in flight
+// across it (the fences are restricted to the local address space).  Used where a barrier
+// protects LDS data only.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Exclusive scan of one int per thread over a work-group of NT threads (NT a multiple of 64).
 // tmp holds NT/64 ints.  Returns the exclusive prefix; *total receives the sum.
 template <int NT>
@@ -106,7 +115,7 @@ __device__ inline int block_exclusive_scan(int v, int* tmp, int* total) {
     if (lane >= o) x += y;
   }
   if (lane == 63) tmp[wave] = x;
-  __syncthreads();
+  lds_barrier();
   int before = 0, sum = 0;
 #pragma unroll
   for (int w = 0; w < NT / 64; ++w) {
@@ -114,7 +123,7 @@ __device__ inline int block_exclusive_scan(int v, int* tmp, int* total) {
     before += (w < wave) ? tw : 0;
     sum += tw;
   }
-  __syncthreads();
+  lds_barrier();
   *total = sum;
   return before + x - v;
 }

@@ -528,12 +528,12 @@ __device__ void build_posting_csr(const int* ads, int* cur, int* offl, int* idxl
   const int tid = threadIdx.x;
   const int A = s.A, ne = s.ne;
   for (int a = tid; a <= A; a += NT) offl[a] = 0;
-  __syncthreads();
+  lds_barrier();
   for (int i = tid; i < ne; i += NT) {
     const int a = ads[i];
     if (a >= 0 && a < A) atomicAdd(&offl[a], 1);
   }
-  __syncthreads();
+  lds_barrier();
   // thread tid owns the contiguous address segment [a0, a1)
   __shared__ int part[NT / 64];
   const int seg = (A + NT - 1) / NT;
@@ -554,7 +554,7 @@ __device__ void build_posting_csr(const int* ads, int* cur, int* offl, int* idxl
     run += n;
   }
   if (tid == 0) offl[A] = tot;
-  __syncthreads();
+  lds_barrier();
   if (tid < 64) {
     const int lane = tid;
     int nbits = 0;
@@ -582,7 +582,7 @@ __device__ void build_posting_csr(const int* ads, int* cur, int* offl, int* idxl
       __builtin_amdgcn_wave_barrier();
     }
   }
-  __syncthreads();
+  lds_barrier();
   if (publish) {
     int32_t* og = fp.off + (size_t)bh * (A + 1);
     int32_t* ig = fp.idx + (size_t)bh * s.nb;
@@ -625,8 +625,7 @@ __global__ __launch_bounds__(kProbeThreads) __attribute__((amdgpu_waves_per_eu(p
   const int A = s.A;
   float* mu = smem;                                       // [NT][MST]
   int* csr = (int*)(smem + max(NT * MST, NT * s.M * 2));  // off [A+1], idx [ne]
-  // ---- every independent global read first: the CSR of this (b,h) (first 8 per lane), the codebook
-  // rows and biases of this lane's codes, the query rows of this lane's four 16-token tiles
+  // ---- the addresses (or the CSR) of this (b,h), first 8 per lane
   const int32_t* og = off + (size_t)bh * (A + 1);
   const int32_t* ig = idx + (size_t)bh * s.nb;
   const int32_t* ag = FUSED ? fp.addr + (size_t)bh * s.nb : nullptr;
@@ -641,6 +640,32 @@ __global__ __launch_bounds__(kProbeThreads) __attribute__((amdgpu_waves_per_eu(p
     else
       cv[u] = k < nread ? (k <= A ? og[k] : ig[k - A - 1]) : 0;
   }
+  // ---- the posting-list CSR into LDS (this kernel is only used when it fits): read as is, or
+  // built here from the addresses (FUSED), in the mu region, before the logits need it
+  int* stage = FUSED ? (int*)mu : csr;  // addresses [ne] and list cursors [A] | the CSR
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int k = u * NT + tid;
+    if (k < nread) stage[k] = cv[u];
+  }
+  for (int k0 = 8 * NT; k0 < nread; k0 += 8 * NT) {
+    int v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int k = k0 + u * NT + tid;
+      if (FUSED)
+        v[u] = k < nread ? ag[k] : 0;
+      else
+        v[u] = k < nread ? (k <= A ? og[k] : ig[k - A - 1]) : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int k = k0 + u * NT + tid;
+      if (k < nread) stage[k] = v[u];
+    }
+  }
+  // the codebook rows and biases of this lane's codes and the query rows of its four 16-token tiles
+  // are requested next, so that they arrive while the lists are built
   const float* cbh = cb + (size_t)h * G * C * D;
   float wv[G][CP / 16][DQ];
   float bv[G][CP / 16];
@@ -672,30 +697,6 @@ __global__ __launch_bounds__(kProbeThreads) __attribute__((amdgpu_waves_per_eu(p
   }
   int fv = -1;
   if (force && R > 0 && t < s.S) fv = force[(size_t)bh * s.S + t];
-  // ---- the posting-list CSR into LDS (this kernel is only used when it fits): read as is, or
-  // built here from the addresses (FUSED), in the mu region, before the logits need it
-  int* stage = FUSED ? (int*)mu : csr;  // addresses [ne] and list cursors [A] | the CSR
-#pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    const int k = u * NT + tid;
-    if (k < nread) stage[k] = cv[u];
-  }
-  for (int k0 = 8 * NT; k0 < nread; k0 += 8 * NT) {
-    int v[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int k = k0 + u * NT + tid;
-      if (FUSED)
-        v[u] = k < nread ? ag[k] : 0;
-      else
-        v[u] = k < nread ? (k <= A ? og[k] : ig[k - A - 1]) : 0;
-    }
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int k = k0 + u * NT + tid;
-      if (k < nread) stage[k] = v[u];
-    }
-  }
   if constexpr (FUSED) build_posting_csr<NT>(stage, stage + s.ne, csr, csr + A + 1, s, bh, blockIdx.x == 0, fp);
   const int* offp = csr;
   const int* idxp = csr + A + 1;
@@ -749,7 +750,7 @@ __global__ __launch_bounds__(kProbeThreads) __attribute__((amdgpu_waves_per_eu(p
         }
       }
     }
-  __syncthreads();
+  lds_barrier();
   const bool active = t < s.S;
   const int j = t / s.blk;
   const int cutoff = j - s.L;
@@ -837,7 +838,7 @@ __global__ __launch_bounds__(kProbeThreads) __attribute__((amdgpu_waves_per_eu(p
     for (int p = 0; p < P; ++p)
       for (int e = 0; e < take[p]; ++e) clist[k++] = (tid << 16) | idxp[lim[p] - 1 - e];
   }
-  __syncthreads();
+  lds_barrier();
   // ---- rerank scores: LPT adjacent lanes share a token (token wave*64 + (64/LPT)m + lane/LPT,
   // m = 0..LPT-1); lane o = lane%LPT takes dims 4*LPT*c + 4o + e, so the group reads 16*LPT contiguous
   // bytes of a summary per load.  Several candidates are in flight at a time; the partial dots are
@@ -904,7 +905,7 @@ __global__ __launch_bounds__(kProbeThreads) __attribute__((amdgpu_waves_per_eu(p
       }
     }
   }
-  __syncthreads();
+  lds_barrier();
   // ---- top-R of the token's candidates by (score desc, block asc)
   constexpr int RK = R > 0 ? R : 1;
   int tri[RK];
@@ -945,9 +946,9 @@ __global__ __launch_bounds__(kProbeThreads) __attribute__((amdgpu_waves_per_eu(p
   const int nqb = NT / s.blk;  // whole query blocks per work-group
   if (nqb * s.ne <= NT * MST) {
     int* cnt = (int*)mu;  // [nqb][ne]
-    __syncthreads();      // every rho / clist read is done
+    lds_barrier();      // every rho / clist read is done
     for (int c = tid; c < nqb * s.ne; c += NT) cnt[c] = 0;
-    __syncthreads();
+    lds_barrier();
     const int jb = tbase / s.blk;
     if (active) {
 #pragma unroll
@@ -960,7 +961,7 @@ __global__ __launch_bounds__(kProbeThreads) __attribute__((amdgpu_waves_per_eu(p
         }
       }
     }
-    __syncthreads();
+    lds_barrier();
     for (int c = tid; c < nqb * s.ne; c += NT) {
       const int n = cnt[c];
       if (n > 0) {
