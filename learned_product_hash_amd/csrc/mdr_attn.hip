@@ -357,14 +357,14 @@ __global__ __launch_bounds__(kRemoteWaves * 64) void k_attn_remote(const T* __re
 // One work-group per query block: local blocks + merge of the remote partials.  Every read that
 // does not depend on another is issued at the start: the query rows, the first local block of K/V
 // (held in registers until the LDS takes it; each later block is read while the previous one is
-// scored), the selection row and the first kLocalSlots remote partials (their addresses do not
-// depend on the selection; unused ones are ignored).
-constexpr int kLocalSlots = 2;
+// scored), the selection row and the first RS = min(R, 2) remote partials (their addresses do not
+// depend on the selection; unused ones are ignored).  RS is a template argument so that these
+// reads form one straight-line block the compiler need not wait on early.
 
 // bf16 tiles with D <= 64 are held to four waves per SIMD (four 256-thread work-groups per CU).
 constexpr int local_min_waves(int bytes, int D) { return bytes == 2 && D <= 64 ? 4 : 1; }
 
-template <typename T, int D, int BLK>
+template <typename T, int D, int BLK, int RS>
 __global__ __launch_bounds__(BLK * 4) __attribute__((amdgpu_waves_per_eu(local_min_waves((int)sizeof(T), D)))) void k_attn_local(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, const int32_t* __restrict__ sel,
     const T* __restrict__ part_o, const float* __restrict__ part_ml, T* __restrict__ out, Shape s) {
@@ -385,19 +385,21 @@ __global__ __launch_bounds__(BLK * 4) __attribute__((amdgpu_waves_per_eu(local_m
   kv.load(K + (rowbase + (size_t)j0 * BLK) * D, V + (rowbase + (size_t)j0 * BLK) * D, tid);
   QFrag<T, D> qf;
   load_q<T, D>(qf, Q + (rowbase + t) * D, lane);
+  // reads complete in issue order: keep the K/V and query reads ahead of the partials, which are
+  // needed last
+  __builtin_amdgcn_sched_barrier(0);
   const int32_t* row = sel + (rowbase + t) * s.R;
-  int sr[kLocalSlots];
-  float2 pml[kLocalSlots];
-  Raw4<T> praw[kLocalSlots][TL::ND];
+  constexpr int RA = RS > 0 ? RS : 1;
+  int sr[RA];
+  float2 pml[RA];
+  Raw4<T> praw[RA][TL::ND];
 #pragma unroll
-  for (int r = 0; r < kLocalSlots; ++r) {
-    if (r < s.R) {
-      const size_t pr = (rowbase + t) * s.R + r;
-      sr[r] = row[r];
-      pml[r] = *(const float2*)(part_ml + 2 * pr);
+  for (int r = 0; r < RS; ++r) {
+    const size_t pr = (rowbase + t) * s.R + r;
+    sr[r] = row[r];
+    pml[r] = *(const float2*)(part_ml + 2 * pr);
 #pragma unroll
-      for (int dt = 0; dt < TL::ND; ++dt) praw[r][dt] = *(const Raw4<T>*)(part_o + pr * D + 16 * dt + c4);
-    }
+    for (int dt = 0; dt < TL::ND; ++dt) praw[r][dt] = *(const Raw4<T>*)(part_o + pr * D + 16 * dt + c4);
   }
   const float c = s.scale * kLog2e;
   float m = -INFINITY, l = 0.f;
@@ -444,8 +446,15 @@ __global__ __launch_bounds__(BLK * 4) __attribute__((amdgpu_waves_per_eu(local_m
     for (int dt = 0; dt < TL::ND; ++dt) o[dt] *= alpha;
     pv_block<T, D, BLK>(o, p, Vx, lane);
   };
-  for (int jj = j0; jj < j; ++jj) block_step(std::false_type{}, jj);
-  block_step(std::true_type{}, j);
+  if (s.L == 2 && j >= 1) {
+    // the common window, written out without a loop so that the compiler tracks every read in
+    // flight precisely (a loop header merges that state and forces early waits)
+    block_step(std::false_type{}, j - 1);
+    block_step(std::true_type{}, j);
+  } else {
+    for (int jj = j0; jj < j; ++jj) block_step(std::false_type{}, jj);
+    block_step(std::true_type{}, j);
+  }
   // merge the remote partials in slot order: entry r counts when 0 <= sel <= j - L and it does not
   // repeat an earlier entry of the row
   auto merge = [&](float2 ml, const Raw4<T> (&po)[TL::ND]) __attribute__((always_inline)) {
@@ -458,15 +467,13 @@ __global__ __launch_bounds__(BLK * 4) __attribute__((amdgpu_waves_per_eu(local_m
     m = mnew;
   };
 #pragma unroll
-  for (int r = 0; r < kLocalSlots; ++r) {
-    if (r < s.R) {
-      bool ok = sr[r] >= 0 && sr[r] <= j - s.L;
+  for (int r = 0; r < RS; ++r) {
+    bool ok = sr[r] >= 0 && sr[r] <= j - s.L;
 #pragma unroll
-      for (int p = 0; p < r; ++p) ok = ok && sr[p] != sr[r];
-      if (ok) merge(pml[r], praw[r]);
-    }
+    for (int p = 0; p < r; ++p) ok = ok && sr[p] != sr[r];
+    if (ok) merge(pml[r], praw[r]);
   }
-  for (int r = kLocalSlots; r < s.R; ++r) {
+  for (int r = RS; r < s.R; ++r) {
     if (!sel_entry_valid(row, r, j, s.L)) continue;
     const size_t pr = (rowbase + t) * s.R + r;
     Raw4<T> po[TL::ND];
@@ -477,6 +484,19 @@ __global__ __launch_bounds__(BLK * 4) __attribute__((amdgpu_waves_per_eu(local_m
   const float inv = 1.f / l;
 #pragma unroll
   for (int dt = 0; dt < TL::ND; ++dt) store4<T>(out + (rowbase + t) * D + 16 * dt + c4, o[dt], inv);
+}
+
+template <typename T, int D, int BLK, int RS>
+hipError_t launch_local(const Shape& s, const void* q, const void* k, const void* v, const int32_t* sel, void* out,
+                        const Buffers& b, hipStream_t st) {
+  const size_t lds = Tile<T, D, BLK>::LDS_BYTES;
+  hipError_t e;
+  if (lds > 65536 && (e = hipFuncSetAttribute((const void*)k_attn_local<T, D, BLK, RS>,
+                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)) != hipSuccess)
+    return e;
+  hipLaunchKernelGGL((k_attn_local<T, D, BLK, RS>), dim3(s.nb * s.B * s.H), dim3(BLK * 4), lds, st, (const T*)q,
+                     (const T*)k, (const T*)v, sel, (const T*)b.part_o, b.part_ml, (T*)out, s);
+  return hipGetLastError();
 }
 
 template <typename T, int D, int BLK>
@@ -498,12 +518,9 @@ hipError_t attend_impl(const Shape& s, const void* q, const void* k, const void*
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (ev && (e = hipEventRecord(ev[1], st)) != hipSuccess) return e;
-  if (lds > 65536 && (e = hipFuncSetAttribute((const void*)k_attn_local<T, D, BLK>,
-                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)) != hipSuccess)
-    return e;
-  hipLaunchKernelGGL((k_attn_local<T, D, BLK>), dim3(s.nb * s.B * s.H), dim3(BLK * 4), lds, st, (const T*)q,
-                     (const T*)k, (const T*)v, sel, (const T*)b.part_o, b.part_ml, (T*)out, s);
-  return hipGetLastError();
+  return s.R >= 2   ? launch_local<T, D, BLK, 2>(s, q, k, v, sel, out, b, st)
+         : s.R == 1 ? launch_local<T, D, BLK, 1>(s, q, k, v, sel, out, b, st)
+                    : launch_local<T, D, BLK, 0>(s, q, k, v, sel, out, b, st);
 }
 
 template <typename T, int D>
