@@ -306,26 +306,21 @@ __global__ __launch_bounds__(kRemoteWaves * 64) void k_attn_remote(const T* __re
   };
   int it = blockIdx.z;
   if (it * PER_IT + wave * 16 >= total) return;  // this wave has no pairs at all (no barriers below)
-  int pv = pair_at(it);
+  // software pipeline over this wave's iterations: the next pair id is requested before the current
+  // tile is scored and its query row right after, so neither read waits on the other's round trip
+  int cur = pair_at(it);
   QFrag<T, D> qf;
-  load_q<T, D>(qf, Q + (rowbase + (pv < 0 ? 0 : pv / s.R)) * D, lane);
+  load_q<T, D>(qf, Q + (rowbase + (cur < 0 ? 0 : cur / s.R)) * D, lane);
   for (; it < nit; it += gridDim.z) {
-    const int cur = pv;
-    const QFrag<T, D> qc = qf;
     const int nx = it + (int)gridDim.z;
-    if (nx < nit && nx * PER_IT + wave * 16 < total) {
-      pv = pair_at(nx);
-      load_q<T, D>(qf, Q + (rowbase + (pv < 0 ? 0 : pv / s.R)) * D, lane);
-    } else {
-      pv = -1;
-    }
-    if (it * PER_IT + wave * 16 >= total) break;
+    const bool more = nx < nit && nx * PER_IT + wave * 16 < total;  // uniform per wave
+    const int nxt = more ? pair_at(nx) : -1;
     // softmax in base 2 with the scale folded in: p = 2^(c s - c max s), c = scale * log2(e) > 0
     f32x4 p[TL::NT];
     float mx = -INFINITY;
 #pragma unroll
     for (int n = 0; n < TL::NT; ++n) {
-      p[n] = score_tile<T, D, BLK>(qc, Ks, n, lane);
+      p[n] = score_tile<T, D, BLK>(qf, Ks, n, lane);
 #pragma unroll
       for (int k = 0; k < 4; ++k) mx = fmaxf(mx, p[n][k]);
     }
@@ -343,6 +338,7 @@ __global__ __launch_bounds__(kRemoteWaves * 64) void k_attn_remote(const T* __re
 #pragma unroll
     for (int dt = 0; dt < TL::ND; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     pv_block<T, D, BLK>(o, p, Vx, lane);
+    if (more) load_q<T, D>(qf, Q + (rowbase + (nxt < 0 ? 0 : nxt / s.R)) * D, lane);
     if (cur >= 0) {
       const int t = cur / s.R, r = cur % s.R;
       const size_t pr = (rowbase + t) * s.R + r;
@@ -351,6 +347,8 @@ __global__ __launch_bounds__(kRemoteWaves * 64) void k_attn_remote(const T* __re
       for (int dt = 0; dt < TL::ND; ++dt) store4<T>(part_o + pr * D + 16 * dt + 4 * (lane >> 4), o[dt], inv);
       if ((lane >> 4) == 0) *(float2*)(part_ml + 2 * pr) = make_float2(mx, sum);
     }
+    if (!more) break;
+    cur = nxt;
   }
 }
 
