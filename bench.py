@@ -73,6 +73,7 @@ def parse(argv=None):
                     help="run one elementwise copy of 512 MiB first (counter calibration)")
     ap.add_argument("--cpu-heads", type=int, default=8)
     ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
+    ap.add_argument("--bench-log", default=None, help="with --summarize-rocprof: bench.py's stdout of the same run")
     ap.add_argument("--summarize-rocprof", nargs=2, metavar=("KERNEL_STATS_CSV", "COMMAND"),
                     help="write profiles/routed_attention_kernels_<workload>.md from a rocprofv3 --stats CSV")
     return ap.parse_args(argv)
@@ -414,18 +415,26 @@ def ingest_pmc(fetch_csv, write_csv, w):
 
 # ----------------------------------------------------------------------------- main
 
-def summarize_rocprof(stats_csv, command, w):
-    """Short markdown table of the library's kernels from a rocprofv3 kernel_stats.csv."""
+def summarize_rocprof(stats_csv, command, w, bench_log=None):
+    """Short markdown table of the library's kernels from a rocprofv3 kernel_stats.csv, with the
+    HIP-event averages bench.py printed in the same run (bench_log: its stdout) beside them."""
     rows = list(csv.DictReader(open(stats_csv)))
+    events = {}
+    if bench_log:
+        for line in open(bench_log):
+            if line.startswith("{"):
+                events = {k: v["ms"] * 1e3 for k, v in json.loads(line)["kernels"].items()}
     lines = [f"# rocprofv3 kernel statistics: routed attention, {describe(w)}", "",
              "Command (run from the repository root on one MI355X):", "", f"    {command}", "",
-             "| kernel | calls | avg us | min us | max us | share of GPU time |", "|---|---|---|---|---|---|"]
+             "| kernel | calls | avg us | min us | max us | share of GPU time | bench.py HIP-event avg us |",
+             "|---|---|---|---|---|---|---|"]
     for k, sym in KERNEL_SYMBOL.items():
         for r in rows:
             if sym in r["Name"]:
+                ev = f"{events[k]:.2f}" if k in events else "-"
                 lines.append(f"| {k} (`{sym}`) | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                              f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
-                             f"{float(r['Percentage']):.1f}% |")
+                             f"{float(r['Percentage']):.1f}% | {ev} |")
     other = sum(float(r["Percentage"]) for r in rows if not any(sym in r["Name"] for sym in KERNEL_SYMBOL.values()))
     lines += ["", f"Other kernels (input generation, torch copies, routing statistics): {other:.1f}% of GPU time.", ""]
     out = os.path.join(ROOT, "profiles", f"routed_attention_kernels_{w.name}_{w.seq // 1024}k.md")
@@ -441,7 +450,7 @@ def main(argv=None):
         ingest_pmc(*a.ingest_pmc, w)
         return 0
     if a.summarize_rocprof:
-        summarize_rocprof(*a.summarize_rocprof, w)
+        summarize_rocprof(*a.summarize_rocprof, w, a.bench_log)
         return 0
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print(json.dumps({"error": "this build runs on one GPU only: the path shards over (batch, head) with no "
