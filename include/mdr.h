@@ -213,6 +213,66 @@ mdr_status mdr_stage_attend(const mdr_config* cfg, const void* q, const void* k,
                             const int32_t* sel, void* out, void* workspace, size_t workspace_bytes,
                             void* stream);
 
+/* ---- streaming decode ----
+ * Incremental routing for decoding (remio.ai, "What sparse attention
+ * researchers should watch next", names it the open systems question).  Each
+ * (b,h)'s posting lists are ring buffers of `capacity` entries per address:
+ * block i is filed when it becomes eligible (for query block i + L), evicting
+ * the address's oldest entry when full (remio.ai, "Monodratic turns sparse
+ * attention into a retrieval decision": strict capacity, overflow drops
+ * blocks).  A ring holds exactly the newest `capacity` eligible blocks of its
+ * address, the view the prefill path reads, so a decoded token gets the
+ * routing and output the prefill path gives the same token.
+ *
+ * cfg describes the cache: seq = its capacity in tokens; every other field as
+ * for mdr_routed_attention (width ignored).  Additionally (remote + local) *
+ * block <= 4096 and the candidate cut M <= 1024, else MDR_ERR_UNSUPPORTED.
+ *
+ * The state is one caller-owned device buffer of mdr_decode_state_size bytes
+ * (256-byte aligned); its regions are described by mdr_decode_view.  Calls
+ * that share a state must be ordered on one stream. */
+
+/* Bytes of decode state for cfg; 0 when cfg is invalid or unsupported. */
+size_t mdr_decode_state_size(const mdr_config* cfg);
+
+/* Device pointers into a decode state (host arithmetic only, nothing launched):
+ *   ring [B,H,A,capacity] filed block ids, the n-th block filed under address
+ *     a sitting in slot n % capacity (-1 while empty);
+ *   ring_n [B,H,A] blocks filed per address; overflow [B,H] blocks evicted;
+ *   summarized [B,H] and filed [B,H] block counts (blocks 0 .. count - 1);
+ *   addr [B,H,nb] and ksum [B,H,nb,D] fp32 of the summarised blocks. */
+typedef struct {
+  int32_t* ring;
+  int32_t* ring_n;
+  int32_t* overflow;
+  int32_t* summarized;
+  int32_t* filed;
+  int32_t* addr;
+  float* ksum;
+} mdr_decode_view;
+mdr_status mdr_decode_state_view(const mdr_config* cfg, void* state, mdr_decode_view* view);
+
+/* Resets the state for a cache holding n_tokens tokens (0 <= n_tokens < seq):
+ * summarises the complete blocks among them and files the blocks a token at
+ * position n_tokens may see (i <= n_tokens / block - L).
+ *   k_cache [B,H,seq,D] (rows 0 .. n_tokens - 1 read); codebook [H,G,C,D] fp32;
+ *   code_bias [H,G,C] or NULL. */
+mdr_status mdr_decode_prime(const mdr_config* cfg, const void* k_cache, const float* codebook,
+                            const float* code_bias, int32_t n_tokens, void* state, size_t state_bytes,
+                            void* stream);
+
+/* Routes and attends the n_new tokens at positions pos .. pos + n_new - 1, which
+ * must lie in one block and continue where the prime or the previous step
+ * ended.  Their K/V rows must already be in the cache.  Files any block that
+ * became eligible first.
+ *   q_new [B,H,n_new,D] (post-RoPE); k_cache, v_cache [B,H,seq,D];
+ *   force [B,H,n_new] or NULL (as in mdr_routed_attention); out [B,H,n_new,D]
+ *   overwritten; sel [B,H,n_new,R] out (-1 padded) or NULL. */
+mdr_status mdr_decode_step(const mdr_config* cfg, const void* q_new, const void* k_cache, const void* v_cache,
+                           const float* codebook, const float* code_bias, const int32_t* force, int32_t pos,
+                           int32_t n_new, void* out, int32_t* sel, void* state, size_t state_bytes,
+                           void* stream);
+
 #ifdef __cplusplus
 }
 #endif

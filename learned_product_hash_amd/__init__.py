@@ -47,6 +47,11 @@ class MdrRouting(ctypes.Structure):
         "ksum", "addr", "post_off", "post_idx", "overflow", "sel", "n_cand")]
 
 
+class MdrDecodeView(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "ring", "ring_n", "overflow", "summarized", "filed", "addr", "ksum")]
+
+
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built; run `python learned_product_hash_amd/build.py`")
@@ -71,6 +76,11 @@ _SIGS = {
     "mdr_stage_post": ([_cfgp, _vp, _vp, _vp, _vp, _vp], _i32),
     "mdr_stage_probe_rerank": ([_cfgp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp], _i32),
     "mdr_stage_attend": ([_cfgp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], _i32),
+    "mdr_decode_state_size": ([_cfgp], _sz),
+    "mdr_decode_state_view": ([_cfgp, _vp, ctypes.POINTER(MdrDecodeView)], _i32),
+    "mdr_decode_prime": ([_cfgp, _vp, _vp, _vp, ctypes.c_int32, _vp, _sz, _vp], _i32),
+    "mdr_decode_step": ([_cfgp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int32, ctypes.c_int32, _vp, _vp, _vp, _sz,
+                         _vp], _i32),
 }
 for _name, (_args, _res) in _SIGS.items():
     _fn = getattr(lib, _name)
@@ -205,3 +215,52 @@ def mdr_stage_attend(cfg, q, k, v, sel, out, ws, stream=None):
     wp, wn = _ws(ws)
     _check(lib.mdr_stage_attend(ctypes.byref(cfg), _ptr(q), _ptr(k), _ptr(v), _ptr(sel), _ptr(out), wp, wn,
                                 _stream(stream)), "mdr_stage_attend")
+
+
+# ---- streaming decode
+
+def mdr_decode_state_size(cfg) -> int:
+    n = lib.mdr_decode_state_size(ctypes.byref(cfg))
+    if n == 0:
+        raise MdrError(MDR_ERR_UNSUPPORTED if mdr_check_config(cfg) == MDR_OK else mdr_check_config(cfg),
+                       "mdr_decode_state_size")
+    return n
+
+
+def decode_state(cfg, device="cuda") -> torch.Tensor:
+    """A device buffer of mdr_decode_state_size(cfg) bytes."""
+    return torch.empty(mdr_decode_state_size(cfg), dtype=torch.uint8, device=device)
+
+
+def mdr_decode_state_view(cfg, state) -> dict:
+    """Tensors viewing the regions of a decode state (no copy)."""
+    v = MdrDecodeView()
+    _check(lib.mdr_decode_state_view(ctypes.byref(cfg), _ptr(state), ctypes.byref(v)), "mdr_decode_state_view")
+    B, H, D, cap = cfg.batch, cfg.heads, cfg.head_dim, cfg.capacity
+    nb = cfg.seq // cfg.block
+    A = cfg.codes ** cfg.subspaces
+    base = state.data_ptr()
+
+    def region(ptr, shape, dtype):
+        n = 1
+        for x in shape:
+            n *= x
+        off = ptr - base
+        return state[off:off + n * 4].view(dtype).view(*shape)
+
+    return dict(ring=region(v.ring, (B, H, A, cap), torch.int32), ring_n=region(v.ring_n, (B, H, A), torch.int32),
+                overflow=region(v.overflow, (B, H), torch.int32), summarized=region(v.summarized, (B, H), torch.int32),
+                filed=region(v.filed, (B, H), torch.int32), addr=region(v.addr, (B, H, nb), torch.int32),
+                ksum=region(v.ksum, (B, H, nb, D), torch.float32))
+
+
+def mdr_decode_prime(cfg, k_cache, codebook, code_bias, n_tokens, state, stream=None):
+    _check(lib.mdr_decode_prime(ctypes.byref(cfg), _ptr(k_cache), _ptr(codebook), _ptr(code_bias), int(n_tokens),
+                                _ptr(state), state.numel(), _stream(stream)), "mdr_decode_prime")
+
+
+def mdr_decode_step(cfg, q_new, k_cache, v_cache, codebook, code_bias, force, pos, out, sel, state, stream=None):
+    n_new = q_new.shape[2]
+    _check(lib.mdr_decode_step(ctypes.byref(cfg), _ptr(q_new), _ptr(k_cache), _ptr(v_cache), _ptr(codebook),
+                               _ptr(code_bias), _ptr(force), int(pos), int(n_new), _ptr(out), _ptr(sel), _ptr(state),
+                               state.numel(), _stream(stream)), "mdr_decode_step")

@@ -1,0 +1,126 @@
+// Block key summary and product address of one block, shared by the prefill address kernel and
+// the decode filing kernel so that both produce bit-identical summaries and addresses.
+//
+// Summary: the mean of the block's post-RoPE key rows, in fp32 (a fixed order of additions: each
+// thread sums a fixed set of rows of one 16-byte column chunk, the row groups are then added in
+// order).  Address: per subspace g, code_g = argmax_c <codebook[h,g,c], summary> + bias[h,g,c]
+// (first maximum wins), combined as a mixed-radix number with subspace 0 most significant
+// (remio.ai, "Monodratic turns sparse attention into a retrieval decision": a product address
+// combines the decisions of several learned code components).
+#pragma once
+
+#include "mdr_internal.h"
+
+namespace mdr {
+
+template <typename T>
+struct Vec16;  // 16-byte vector of T
+template <>
+struct Vec16<float> {
+  typedef float4 type;
+  static constexpr int n = 4;
+};
+template <>
+struct Vec16<bf16> {
+  typedef bf16x8 type;
+  static constexpr int n = 8;
+};
+
+__device__ inline float to_f(float x) { return x; }
+__device__ inline float to_f(bf16 x) { return (float)x; }
+
+template <typename T, int D>
+struct AddressLds {
+  static constexpr int NCH = D / Vec16<T>::n;  // 16-byte chunks per row
+  static constexpr int RG = 256 / NCH;         // row groups
+  float red[RG][D + 1];
+  float kbar[D];
+  float logit[kMaxCodesTotal];
+};
+
+// All 256 threads of the work-group call it (it contains barriers).  The codebook rows are
+// requested together with the key rows: four adjacent lanes share one code (each a quarter of D,
+// added in a fixed order), and one wave takes each subspace's argmax with a butterfly over
+// (logit, code).  Writes ksum[bh, i, :] and addr[bh, i].
+template <typename T, int D>
+__device__ __forceinline__ void block_address(const T* __restrict__ K, const float* __restrict__ cb,
+                                              const float* __restrict__ bias, float* __restrict__ ksum,
+                                              int32_t* __restrict__ addr, int i, int bh, AddressLds<T, D>& sm,
+                                              const Shape& s) {
+  constexpr int VEC = Vec16<T>::n;
+  constexpr int NCH = AddressLds<T, D>::NCH;
+  constexpr int RG = AddressLds<T, D>::RG;
+  constexpr int LPC = 256 / kMaxCodesTotal;  // lanes per code
+  constexpr int DPL = D / LPC;               // codebook dims per lane
+  static_assert(DPL % 4 == 0, "whole float4 per lane");
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int h = bh % s.H;
+  const int GC = s.G * s.C;
+  // codebook slice of this lane: code cc, dims [part * DPL, (part + 1) * DPL)
+  const int cc = tid / LPC, part = tid % LPC;
+  float w[DPL];
+  {
+    const float* wr = cb + ((size_t)h * GC + (cc < GC ? cc : 0)) * D + part * DPL;
+#pragma unroll
+    for (int d = 0; d < DPL; d += 4) {
+      const float4 v = *(const float4*)(wr + d);
+      w[d] = v.x;
+      w[d + 1] = v.y;
+      w[d + 2] = v.z;
+      w[d + 3] = v.w;
+    }
+  }
+  const float bv = (bias && cc < GC) ? bias[h * GC + cc] : 0.f;
+  const T* base = K + ((size_t)bh * s.S + (size_t)i * s.blk) * D;
+  const int ch = tid % NCH, rg = tid / NCH;
+  float acc4[VEC];
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) acc4[e] = 0.f;
+  for (int r = rg; r < s.blk; r += RG) {
+    typename Vec16<T>::type v = *(const typename Vec16<T>::type*)(base + (size_t)r * D + ch * VEC);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) acc4[e] += to_f(v[e]);
+  }
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) sm.red[rg][ch * VEC + e] = acc4[e];
+  __syncthreads();
+  if (tid < D) {
+    float acc = 0.f;
+    for (int g = 0; g < RG; ++g) acc += sm.red[g][tid];
+    const float m = acc / (float)s.blk;
+    sm.kbar[tid] = m;
+    ksum[((size_t)bh * s.nb + i) * D + tid] = m;
+  }
+  __syncthreads();
+  {
+    float acc = 0.f;
+#pragma unroll
+    for (int d = 0; d < DPL; ++d) acc = fmaf(w[d], sm.kbar[part * DPL + d], acc);
+#pragma unroll
+    for (int x = 1; x < LPC; x <<= 1) acc += __shfl_xor(acc, x);
+    if (part == 0 && cc < GC) sm.logit[cc] = acc + bv;
+  }
+  __syncthreads();
+  if (tid < 64) {
+    int a = 0;
+    for (int g = 0; g < s.G; ++g) {
+      // lanes 0..C-1 hold the subspace's logits; the butterfly keeps the larger logit, the
+      // smaller code on ties
+      float v = lane < s.C ? sm.logit[g * s.C + lane] : -INFINITY;
+      int c = lane < s.C ? lane : 0x7fffffff;
+#pragma unroll
+      for (int x = 32; x >= 1; x >>= 1) {
+        const float ov = __shfl_xor(v, x);
+        const int oc = __shfl_xor(c, x);
+        if (ov > v || (ov == v && oc < c)) {
+          v = ov;
+          c = oc;
+        }
+      }
+      a = a * s.C + c;
+    }
+    if (tid == 0) addr[(size_t)bh * s.nb + i] = a;
+  }
+}
+
+}  // namespace mdr

@@ -126,6 +126,50 @@ mdr_status check_workspace(const Shape& s, void* ws, size_t ws_bytes, Buffers* b
   return MDR_OK;
 }
 
+// Decode: the core config plus the per-token limits of the decode kernel.
+mdr_status decode_shape(const mdr_config* cfg, Shape* out) {
+  Shape s;
+  mdr_status st = shape_from_config(cfg, false, &s);
+  if (st != MDR_OK) return st;
+  s.W = 0;
+  if ((long long)(s.R + s.L) * s.blk > kDecMaxKeys || s.M > kDecMaxCand) return MDR_ERR_UNSUPPORTED;
+  *out = s;
+  return MDR_OK;
+}
+
+// Blocks a token at position pos may see remotely: i <= pos / block - L.
+int decode_eligible(const Shape& s, int pos) {
+  const int e = pos / s.blk - s.L + 1;
+  return e > 0 ? e : 0;
+}
+
+size_t decode_layout(const Shape& s, char* base, DecState* d) {
+  const size_t BH = (size_t)s.B * s.H;
+  size_t off = 0;
+  auto take = [&](size_t bytes) -> char* {
+    char* p = base ? base + off : nullptr;
+    off += align_up(bytes ? bytes : 4);
+    return p;
+  };
+  DecState t;
+  t.ring = (int32_t*)take(BH * s.A * s.cap * 4);
+  t.ring_n = (int32_t*)take(BH * s.A * 4);
+  t.overflow = (int32_t*)take(BH * 4);
+  t.summarized = (int32_t*)take(BH * 4);
+  t.filed = (int32_t*)take(BH * 4);
+  t.addr = (int32_t*)take(BH * s.nb * 4);
+  t.ksum = (float*)take(BH * s.nb * s.D * 4);
+  if (d) *d = t;
+  return off;
+}
+
+mdr_status check_decode_state(const Shape& s, void* state, size_t bytes, DecState* d) {
+  if (!state || ((uintptr_t)state & 255) != 0) return MDR_ERR_INVALID_ARG;
+  if (bytes < decode_layout(s, nullptr, nullptr)) return MDR_ERR_WORKSPACE;
+  decode_layout(s, (char*)state, d);
+  return MDR_OK;
+}
+
 void apply_routing(const mdr_routing* r, Buffers* b) {
   if (!r) return;
   if (r->ksum) b->ksum = r->ksum;
@@ -305,6 +349,76 @@ mdr_status mdr_stage_attend(const mdr_config* cfg, const void* q, const void* k,
     MDR_TRY(launch_pair_bin(s, sel, b.cellcnt, b.bins, hs));
   }
   MDR_TRY(launch_attend(s, q, k, v, sel, out, b, hs));
+  return MDR_OK;
+}
+
+// ---- streaming decode
+
+size_t mdr_decode_state_size(const mdr_config* cfg) {
+  Shape s;
+  if (decode_shape(cfg, &s) != MDR_OK) return 0;
+  return decode_layout(s, nullptr, nullptr);
+}
+
+mdr_status mdr_decode_state_view(const mdr_config* cfg, void* state, mdr_decode_view* view) {
+  Shape s;
+  mdr_status st = decode_shape(cfg, &s);
+  if (st != MDR_OK) return st;
+  if (!state || !view || ((uintptr_t)state & 255) != 0) return MDR_ERR_INVALID_ARG;
+  DecState d;
+  decode_layout(s, (char*)state, &d);
+  view->ring = d.ring;
+  view->ring_n = d.ring_n;
+  view->overflow = d.overflow;
+  view->summarized = d.summarized;
+  view->filed = d.filed;
+  view->addr = d.addr;
+  view->ksum = d.ksum;
+  return MDR_OK;
+}
+
+mdr_status mdr_decode_prime(const mdr_config* cfg, const void* k_cache, const float* codebook,
+                            const float* code_bias, int32_t n_tokens, void* state, size_t state_bytes, void* stream) {
+  Shape s;
+  mdr_status st = decode_shape(cfg, &s);
+  if (st != MDR_OK) return st;
+  if (!k_cache || !codebook || !aligned16(k_cache) || !aligned16(codebook)) return MDR_ERR_INVALID_ARG;
+  if (n_tokens < 0 || n_tokens >= s.S) return MDR_ERR_INVALID_ARG;
+  DecState d;
+  st = check_decode_state(s, state, state_bytes, &d);
+  if (st != MDR_OK) return st;
+  hipStream_t hs = (hipStream_t)stream;
+  const long long BH = (long long)s.B * s.H;
+  const int complete = n_tokens / s.blk;
+  const int target = decode_eligible(s, n_tokens);
+  MDR_TRY(launch_fill(d.ring, BH * s.A * s.cap, -1, hs));
+  MDR_TRY(launch_fill(d.ring_n, BH * s.A, 0, hs));
+  MDR_TRY(launch_fill(d.overflow, BH, 0, hs));
+  MDR_TRY(launch_fill(d.filed, BH, 0, hs));
+  MDR_TRY(launch_fill(d.summarized, BH, complete, hs));
+  if (complete > 0) MDR_TRY(launch_address(s, k_cache, codebook, code_bias, d.ksum, d.addr, nullptr, hs, 0, complete));
+  MDR_TRY(launch_decode_file(s, k_cache, codebook, code_bias, d, target, hs));
+  return MDR_OK;
+}
+
+mdr_status mdr_decode_step(const mdr_config* cfg, const void* q_new, const void* k_cache, const void* v_cache,
+                           const float* codebook, const float* code_bias, const int32_t* force, int32_t pos,
+                           int32_t n_new, void* out, int32_t* sel, void* state, size_t state_bytes, void* stream) {
+  Shape s;
+  mdr_status st = decode_shape(cfg, &s);
+  if (st != MDR_OK) return st;
+  if (!q_new || !k_cache || !v_cache || !codebook || !out) return MDR_ERR_INVALID_ARG;
+  if (!aligned16(q_new) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) || !aligned16(codebook))
+    return MDR_ERR_INVALID_ARG;
+  if (pos < 0 || n_new < 1 || (long long)pos + n_new > s.S) return MDR_ERR_INVALID_ARG;
+  if (pos / s.blk != (pos + n_new - 1) / s.blk) return MDR_ERR_INVALID_ARG;  // one query block per call
+  if (n_new > 65535) return MDR_ERR_UNSUPPORTED;
+  DecState d;
+  st = check_decode_state(s, state, state_bytes, &d);
+  if (st != MDR_OK) return st;
+  hipStream_t hs = (hipStream_t)stream;
+  MDR_TRY(launch_decode_file(s, k_cache, codebook, code_bias, d, decode_eligible(s, pos), hs));
+  MDR_TRY(launch_decode_attend(s, q_new, k_cache, v_cache, codebook, code_bias, d, force, pos, n_new, out, sel, hs));
   return MDR_OK;
 }
 

@@ -56,6 +56,19 @@ struct Buffers {
   void* mo;
 };
 
+// Streaming-decode state (one region of a caller-owned buffer each).
+struct DecState {
+  int32_t* ring;        // [B,H,A,cap] filed block ids; block n of an address sits in slot n % cap
+  int32_t* ring_n;      // [B,H,A] blocks filed per address so far
+  int32_t* overflow;    // [B,H] blocks evicted so far
+  int32_t* summarized;  // [B,H] blocks whose summary and address are in ksum / addr
+  int32_t* filed;       // [B,H] blocks filed so far (blocks 0 .. filed - 1)
+  int32_t* addr;        // [B,H,nb]
+  float* ksum;          // [B,H,nb,D]
+};
+constexpr int kDecMaxKeys = 4096;  // (R + L) * block keys per decoded token
+constexpr int kDecMaxCand = 1024;  // candidates per decoded token
+
 // The cells of remote block i are (i, j) for j = i + L .. nb - 1, stored contiguously; a cell
 // holds the pairs of query block j that selected block i (at most blk of them).
 __host__ __device__ inline long long cell_row(int i, int ne) {
@@ -130,8 +143,9 @@ __device__ inline int block_exclusive_scan(int v, int* tmp, int* total) {
 
 // Launchers (return hipGetLastError()).
 // cell_zero (optional): the address kernel of block i clears the cell counters of row i.
+// Blocks [i0, i0 + n) (n < 0: to the end).
 hipError_t launch_address(const Shape& s, const void* k, const float* codebook, const float* bias,
-                          float* ksum, int32_t* addr, int32_t* cell_zero, hipStream_t st);
+                          float* ksum, int32_t* addr, int32_t* cell_zero, hipStream_t st, int i0 = 0, int n = -1);
 hipError_t launch_post(const Shape& s, const int32_t* addr, int32_t* off, int32_t* idx,
                        int32_t* overflow, hipStream_t st);
 // Posting lists built inside the probe kernel (from the block addresses) instead of read: every
@@ -149,6 +163,14 @@ hipError_t launch_probe_rerank(const Shape& s, const void* q, const float* codeb
 // True when launch_probe_rerank accepts `fuse` for this shape (the compile-time specialised probe).
 bool probe_fuses_post(const Shape& s);
 size_t probe_lds_bytes(const Shape& s);
+// Decode: file blocks [filed, target) of every (b,h) (summarising those not summarised yet), then
+// route and attend tokens pos .. pos + n_new - 1 (one query block).
+hipError_t launch_decode_file(const Shape& s, const void* k_cache, const float* codebook, const float* bias,
+                              const DecState& d, int target, hipStream_t st);
+hipError_t launch_decode_attend(const Shape& s, const void* q_new, const void* k_cache, const void* v_cache,
+                                const float* codebook, const float* bias, const DecState& d,
+                                const int32_t* force, int pos, int n_new, void* out, int32_t* sel,
+                                hipStream_t st);
 bool probe_fixed_shape(const Shape& s);
 hipError_t launch_fill(int32_t* p, long long n, int32_t value, hipStream_t st);
 hipError_t launch_pair_bin(const Shape& s, const int32_t* sel, int32_t* cellcnt, int32_t* bins,

@@ -12,6 +12,7 @@
 // collects candidates, reranks them and keeps a fixed number of remote blocks.  A block may
 // never be visible to a query placed before it.
 #include "mdr_internal.h"
+#include "mdr_address.h"
 
 #include <float.h>
 
@@ -21,119 +22,23 @@ namespace mdr {
 
 namespace {
 
-template <typename T>
-struct Vec16;  // 16-byte vector of T
-template <>
-struct Vec16<float> {
-  typedef float4 type;
-  static constexpr int n = 4;
-};
-template <>
-struct Vec16<bf16> {
-  typedef bf16x8 type;
-  static constexpr int n = 8;
-};
-
-__device__ inline float to_f(float x) { return x; }
-__device__ inline float to_f(bf16 x) { return (float)x; }
-
 // ---------------------------------------------------------------------------------------------
-// Block key summary (mean of the block's key rows, fp32) and product address.
-// One work-group of 256 threads per (b,h, block).  Each thread sums a fixed set of rows of one
-// 16-byte column chunk; the row groups are then added in a fixed order, so the result is
-// deterministic.  Codes are argmaxes of <codebook[h,g,c], summary> + bias[h,g,c] (first
-// maximum wins), the address is the mixed-radix number with subspace 0 most significant.
-// The codebook rows are requested together with the key rows: four adjacent lanes share one code
-// (each a quarter of D, added in a fixed order), and one wave finds each subspace's argmax with
-// a butterfly over (logit, code).
+// Block key summaries and product addresses: one work-group of 256 threads per (b,h, block); the
+// arithmetic is block_address() (mdr_address.h), shared with the decode path.  The work-group of
+// block i also clears the cell counters of row i when asked.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void k_address(const T* __restrict__ K, const float* __restrict__ cb,
                                                  const float* __restrict__ bias, float* __restrict__ ksum,
                                                  int32_t* __restrict__ addr, int32_t* __restrict__ cell_zero,
-                                                 Shape s) {
-  constexpr int VEC = Vec16<T>::n;
-  constexpr int NCH = D / VEC;
-  constexpr int RG = 256 / NCH;
-  constexpr int LPC = 256 / kMaxCodesTotal;  // lanes per code
-  constexpr int DPL = D / LPC;               // codebook dims per lane
-  static_assert(DPL % 4 == 0, "whole float4 per lane");
-  __shared__ float red[RG][D + 1];
-  __shared__ float kbar[D];
-  __shared__ float logit[kMaxCodesTotal];
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int i = blockIdx.x;
+                                                 int i0, Shape s) {
+  __shared__ AddressLds<T, D> sm;
+  const int i = i0 + blockIdx.x;
   const int bh = blockIdx.y;
-  const int h = bh % s.H;
-  const int GC = s.G * s.C;
-  // codebook slice of this lane: code cc, dims [part * DPL, (part + 1) * DPL)
-  const int cc = tid / LPC, part = tid % LPC;
-  float w[DPL];
-  {
-    const float* wr = cb + ((size_t)h * GC + (cc < GC ? cc : 0)) * D + part * DPL;
-#pragma unroll
-    for (int d = 0; d < DPL; d += 4) {
-      const float4 v = *(const float4*)(wr + d);
-      w[d] = v.x;
-      w[d + 1] = v.y;
-      w[d + 2] = v.z;
-      w[d + 3] = v.w;
-    }
-  }
-  const float bv = (bias && cc < GC) ? bias[h * GC + cc] : 0.f;
-  const T* base = K + ((size_t)bh * s.S + (size_t)i * s.blk) * D;
-  const int ch = tid % NCH, rg = tid / NCH;
-  float acc4[VEC];
-#pragma unroll
-  for (int e = 0; e < VEC; ++e) acc4[e] = 0.f;
-  for (int r = rg; r < s.blk; r += RG) {
-    typename Vec16<T>::type v = *(const typename Vec16<T>::type*)(base + (size_t)r * D + ch * VEC);
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) acc4[e] += to_f(v[e]);
-  }
-#pragma unroll
-  for (int e = 0; e < VEC; ++e) red[rg][ch * VEC + e] = acc4[e];
   if (cell_zero && i < s.ne) {
     int32_t* row = cell_zero + (size_t)bh * s.cells_per_bh + cell_row(i, s.ne);
-    for (int c = tid; c < s.ne - i; c += 256) row[c] = 0;
+    for (int c = threadIdx.x; c < s.ne - i; c += 256) row[c] = 0;
   }
-  __syncthreads();
-  if (tid < D) {
-    float acc = 0.f;
-    for (int g = 0; g < RG; ++g) acc += red[g][tid];
-    const float m = acc / (float)s.blk;
-    kbar[tid] = m;
-    ksum[((size_t)bh * s.nb + i) * D + tid] = m;
-  }
-  __syncthreads();
-  {
-    float acc = 0.f;
-#pragma unroll
-    for (int d = 0; d < DPL; ++d) acc = fmaf(w[d], kbar[part * DPL + d], acc);
-#pragma unroll
-    for (int x = 1; x < LPC; x <<= 1) acc += __shfl_xor(acc, x);
-    if (part == 0 && cc < GC) logit[cc] = acc + bv;
-  }
-  __syncthreads();
-  if (tid < 64) {
-    int a = 0;
-    for (int g = 0; g < s.G; ++g) {
-      // lanes 0..C-1 hold the subspace's logits; the butterfly keeps the larger logit, the
-      // smaller code on ties
-      float v = lane < s.C ? logit[g * s.C + lane] : -INFINITY;
-      int c = lane < s.C ? lane : 0x7fffffff;
-#pragma unroll
-      for (int x = 32; x >= 1; x >>= 1) {
-        const float ov = __shfl_xor(v, x);
-        const int oc = __shfl_xor(c, x);
-        if (ov > v || (ov == v && oc < c)) {
-          v = ov;
-          c = oc;
-        }
-      }
-      a = a * s.C + c;
-    }
-    if (tid == 0) addr[(size_t)bh * s.nb + i] = a;
-  }
+  block_address<T, D>(K, cb, bias, ksum, addr, i, bh, sm, s);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -978,17 +883,18 @@ __global__ __launch_bounds__(kProbeThreads) __attribute__((amdgpu_waves_per_eu(p
 
 template <typename T>
 hipError_t address_dispatch(const Shape& s, const void* k, const float* cb, const float* bias, float* ksum,
-                            int32_t* addr, int32_t* cnt, hipStream_t st) {
-  dim3 grid(s.nb, s.B * s.H);
+                            int32_t* addr, int32_t* cnt, int i0, int n, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  dim3 grid(n, s.B * s.H);
   switch (s.D) {
     case 32:
-      hipLaunchKernelGGL((k_address<T, 32>), grid, dim3(256), 0, st, (const T*)k, cb, bias, ksum, addr, cnt, s);
+      hipLaunchKernelGGL((k_address<T, 32>), grid, dim3(256), 0, st, (const T*)k, cb, bias, ksum, addr, cnt, i0, s);
       break;
     case 64:
-      hipLaunchKernelGGL((k_address<T, 64>), grid, dim3(256), 0, st, (const T*)k, cb, bias, ksum, addr, cnt, s);
+      hipLaunchKernelGGL((k_address<T, 64>), grid, dim3(256), 0, st, (const T*)k, cb, bias, ksum, addr, cnt, i0, s);
       break;
     case 128:
-      hipLaunchKernelGGL((k_address<T, 128>), grid, dim3(256), 0, st, (const T*)k, cb, bias, ksum, addr, cnt, s);
+      hipLaunchKernelGGL((k_address<T, 128>), grid, dim3(256), 0, st, (const T*)k, cb, bias, ksum, addr, cnt, i0, s);
       break;
     default:
       return hipErrorInvalidValue;
@@ -1079,9 +985,10 @@ hipError_t probe_dispatch(const Shape& s, const void* q, const float* cb, const 
 }  // namespace
 
 hipError_t launch_address(const Shape& s, const void* k, const float* codebook, const float* bias, float* ksum,
-                          int32_t* addr, int32_t* cell_zero, hipStream_t st) {
-  if (s.dtype == MDR_BF16) return address_dispatch<bf16>(s, k, codebook, bias, ksum, addr, cell_zero, st);
-  return address_dispatch<float>(s, k, codebook, bias, ksum, addr, cell_zero, st);
+                          int32_t* addr, int32_t* cell_zero, hipStream_t st, int i0, int n) {
+  if (n < 0) n = s.nb - i0;
+  if (s.dtype == MDR_BF16) return address_dispatch<bf16>(s, k, codebook, bias, ksum, addr, cell_zero, i0, n, st);
+  return address_dispatch<float>(s, k, codebook, bias, ksum, addr, cell_zero, i0, n, st);
 }
 
 bool probe_fixed_shape(const Shape& s) {

@@ -119,3 +119,39 @@ def test_workspace_grows_with_the_mixer_buffers(mdr):
     core = mdr.mdr_workspace_size(mdr.config(**_good()))
     mixer = mdr.mdr_workspace_size(mdr.config(**_good(width=512, rope_base=10000.0)))
     assert mixer > core
+
+
+def test_decode_state_size_and_view(mdr):
+    cfg = mdr.config(**_good())
+    n = mdr.mdr_decode_state_size(cfg)
+    A = 16 * 16
+    nb = 4096 // 64
+    assert n >= 8 * (A * 2 + A + nb) * 4 + 8 * nb * 64 * 4
+    # (remote + local) * block above 4096 keys, or an invalid config: no state
+    assert mdr.lib.mdr_decode_state_size(ctypes.byref(mdr.config(**_good(remote=16, local=60)))) == 0
+    assert mdr.lib.mdr_decode_state_size(ctypes.byref(mdr.config(**_good(seq=4000)))) == 0
+    v = mdr.MdrDecodeView()
+    base = 1 << 20
+    assert mdr.lib.mdr_decode_state_view(ctypes.byref(cfg), base, ctypes.byref(v)) == 0
+    ptrs = [v.ring, v.ring_n, v.overflow, v.summarized, v.filed, v.addr, v.ksum]
+    assert ptrs == sorted(ptrs) and ptrs[0] == base and ptrs[-1] + nb * 64 * 4 * 8 <= base + n
+    assert all(p % 256 == 0 for p in ptrs)
+    assert mdr.lib.mdr_decode_state_view(ctypes.byref(cfg), base + 4, ctypes.byref(v)) == 1
+
+
+def test_decode_entry_points_validate_before_launching(mdr):
+    lib = mdr.lib
+    cfg = mdr.config(**_good())
+    c = ctypes.byref(cfg)
+    n = mdr.mdr_decode_state_size(cfg)
+    p = 1 << 20
+    assert lib.mdr_decode_prime(c, p, p, None, 100, p, n - 1, None) == 3      # short state
+    assert lib.mdr_decode_prime(c, p, p, None, -1, p, n, None) == 1           # n_tokens < 0
+    assert lib.mdr_decode_prime(c, p, p, None, 4096, p, n, None) == 1         # nothing left to decode
+    assert lib.mdr_decode_prime(c, None, p, None, 100, p, n, None) == 1
+    # tokens 63 and 64 lie in two blocks
+    assert lib.mdr_decode_step(c, p, p, p, p, None, None, 63, 2, p, None, p, n, None) == 1
+    assert lib.mdr_decode_step(c, p, p, p, p, None, None, 4095, 2, p, None, p, n, None) == 1  # past seq
+    assert lib.mdr_decode_step(c, p, p, p, p, None, None, 10, 0, p, None, p, n, None) == 1
+    assert lib.mdr_decode_step(c, p, p, p, p, None, None, 10, 1, p + 2, None, p, n, None) == 1  # misaligned out
+    assert lib.mdr_decode_step(c, p, p, p, p, None, None, 10, 1, p, None, p + 16, n, None) == 1  # state alignment
