@@ -69,6 +69,7 @@ def parse(argv=None):
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-sweep", action="store_true", help="skip the 4K-32K exponent sweep")
+    ap.add_argument("--no-decode", action="store_true", help="skip the streaming-decode timing")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run one elementwise copy of 512 MiB first (counter calibration)")
     ap.add_argument("--cpu-heads", type=int, default=8)
@@ -338,6 +339,55 @@ def exponent_sweep(mdr, seqs, seed):
                      "(fixed, balanced setup; CPU hardware not stated)")
 
 
+def decode_bench(run, batch, steps=48, warmup=4):
+    """Streaming decode on the same workload: the cache holds the workload's K/V (replicated over
+    `batch` sequences), the state is primed on all but the last block, and single-token steps
+    continue from there.  Returns time per step and its compulsory bytes (per decoded token and
+    head: q, o, the K/V rows of the selected remote blocks and of the local window, the summaries
+    of its candidates)."""
+    import torch
+
+    mdr, w = run.mdr, run.w
+    B, H, S, D, blk = batch, w.heads, w.seq, w.head_dim, w.block
+    e = 2 if w.dtype == "bf16" else 4
+    rep = lambda t: t.expand(B, *t.shape[1:]).contiguous() if B != t.shape[0] else t
+    q, k, v = rep(run.q), rep(run.k), rep(run.v)
+    cfg = mdr.config(batch=B, seq=S, heads=H, head_dim=D, block=blk, subspaces=w.subspaces, codes=w.codes,
+                     capacity=w.capacity, probes=w.probes, max_cand=w.max_cand, remote=w.remote, local=w.local,
+                     dtype=w.dtype)
+    state = mdr.decode_state(cfg)
+    n0 = S - blk
+    mdr.mdr_decode_prime(cfg, k, run.cb, run.bias, n0, state)
+    out = torch.empty(B, H, 1, D, dtype=q.dtype, device="cuda")
+    sel = torch.empty(B, H, 1, w.remote, dtype=torch.int32, device="cuda")
+    qs = [q[:, :, t:t + 1].contiguous() for t in range(n0, n0 + warmup + steps)]
+    sels = []
+    for i in range(warmup):
+        mdr.mdr_decode_step(cfg, qs[i], k, v, run.cb, run.bias, None, n0 + i, out, sel, state)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(warmup, warmup + steps):
+        mdr.mdr_decode_step(cfg, qs[i], k, v, run.cb, run.bias, None, n0 + i, out, sel, state)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    # compulsory bytes of the timed steps, from their selections (re-run untimed to read them)
+    mdr.mdr_decode_prime(cfg, k, run.cb, run.bias, n0, state)
+    nbytes = 0
+    for i in range(warmup + steps):
+        t = n0 + i
+        mdr.mdr_decode_step(cfg, qs[i], k, v, run.cb, run.bias, None, t, out, sel, state)
+        if i >= warmup:
+            nsel = int((sel >= 0).sum().item())
+            local = t - max(0, (t // blk - w.local + 1) * blk) + 1
+            nbytes += 2 * D * e * B * H + nsel * blk * 2 * D * e + B * H * local * 2 * D * e
+    nbytes /= steps
+    return {"workload": f"sweep context {n0}-{n0 + warmup + steps} tokens, B{B} H{H}, one new token per call",
+            "batch": B, "ms_per_step": round(ms, 5), "tokens_per_s": round(B / (ms * 1e-3), 1),
+            "alg_bytes_per_step": int(nbytes), "alg_gbps": round(nbytes / (ms * 1e-3) / 1e9, 1)}
+
+
 def cpu_baseline(run, heads):
     """The oracle as it stands (routing + gathered fp64 attention), one thread, on a bounded sample."""
     import numpy as np
@@ -510,6 +560,8 @@ def main(argv=None):
         "profiled_step_ms_p10_p50_p90": run.step_quantiles,
         "routing": st,
     }
+    if not a.no_decode and a.workload == "sweep":
+        res["decode"] = [decode_bench(run, b) for b in (1, 16)]
     if not a.no_sweep and a.workload == "sweep":
         res["exponent"] = exponent_sweep(mdr, (4096, 8192, 16384, 32768), a.seed)
     if not a.no_cpu:

@@ -236,14 +236,14 @@ mdr_status mdr_stage_attend(const mdr_config* cfg, const void* q, const void* k,
 size_t mdr_decode_state_size(const mdr_config* cfg);
 
 /* Device pointers into a decode state (host arithmetic only, nothing launched):
- *   ring [B,H,A,capacity] filed block ids, the n-th block filed under address
- *     a sitting in slot n % capacity (-1 while empty);
- *   ring_n [B,H,A] blocks filed per address; overflow [B,H] blocks evicted;
+ *   ring [B,H,A,capacity+1]: per address, the number n of blocks filed so far,
+ *     then `capacity` slots of block ids, the k-th block filed (k = 0, 1, ...)
+ *     sitting in slot k % capacity (-1 while empty);
+ *   overflow [B,H] blocks evicted;
  *   summarized [B,H] and filed [B,H] block counts (blocks 0 .. count - 1);
  *   addr [B,H,nb] and ksum [B,H,nb,D] fp32 of the summarised blocks. */
 typedef struct {
   int32_t* ring;
-  int32_t* ring_n;
   int32_t* overflow;
   int32_t* summarized;
   int32_t* filed;

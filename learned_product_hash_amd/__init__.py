@@ -49,7 +49,7 @@ class MdrRouting(ctypes.Structure):
 
 class MdrDecodeView(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
-        "ring", "ring_n", "overflow", "summarized", "filed", "addr", "ksum")]
+        "ring", "overflow", "summarized", "filed", "addr", "ksum")]
 
 
 def _load() -> ctypes.CDLL:
@@ -248,7 +248,8 @@ def mdr_decode_state_view(cfg, state) -> dict:
         off = ptr - base
         return state[off:off + n * 4].view(dtype).view(*shape)
 
-    return dict(ring=region(v.ring, (B, H, A, cap), torch.int32), ring_n=region(v.ring_n, (B, H, A), torch.int32),
+    ring = region(v.ring, (B, H, A, cap + 1), torch.int32)
+    return dict(ring=ring[..., 1:], ring_n=ring[..., 0],
                 overflow=region(v.overflow, (B, H), torch.int32), summarized=region(v.summarized, (B, H), torch.int32),
                 filed=region(v.filed, (B, H), torch.int32), addr=region(v.addr, (B, H, nb), torch.int32),
                 ksum=region(v.ksum, (B, H, nb, D), torch.float32))

@@ -152,8 +152,7 @@ size_t decode_layout(const Shape& s, char* base, DecState* d) {
     return p;
   };
   DecState t;
-  t.ring = (int32_t*)take(BH * s.A * s.cap * 4);
-  t.ring_n = (int32_t*)take(BH * s.A * 4);
+  t.ring = (int32_t*)take(BH * s.A * (s.cap + 1) * 4);
   t.overflow = (int32_t*)take(BH * 4);
   t.summarized = (int32_t*)take(BH * 4);
   t.filed = (int32_t*)take(BH * 4);
@@ -368,7 +367,6 @@ mdr_status mdr_decode_state_view(const mdr_config* cfg, void* state, mdr_decode_
   DecState d;
   decode_layout(s, (char*)state, &d);
   view->ring = d.ring;
-  view->ring_n = d.ring_n;
   view->overflow = d.overflow;
   view->summarized = d.summarized;
   view->filed = d.filed;
@@ -391,8 +389,7 @@ mdr_status mdr_decode_prime(const mdr_config* cfg, const void* k_cache, const fl
   const long long BH = (long long)s.B * s.H;
   const int complete = n_tokens / s.blk;
   const int target = decode_eligible(s, n_tokens);
-  MDR_TRY(launch_fill(d.ring, BH * s.A * s.cap, -1, hs));
-  MDR_TRY(launch_fill(d.ring_n, BH * s.A, 0, hs));
+  MDR_TRY(launch_ring_reset(d.ring, BH * s.A, s.cap, hs));
   MDR_TRY(launch_fill(d.overflow, BH, 0, hs));
   MDR_TRY(launch_fill(d.filed, BH, 0, hs));
   MDR_TRY(launch_fill(d.summarized, BH, complete, hs));
@@ -417,7 +414,10 @@ mdr_status mdr_decode_step(const mdr_config* cfg, const void* q_new, const void*
   st = check_decode_state(s, state, state_bytes, &d);
   if (st != MDR_OK) return st;
   hipStream_t hs = (hipStream_t)stream;
-  MDR_TRY(launch_decode_file(s, k_cache, codebook, code_bias, d, decode_eligible(s, pos), hs));
+  // steps continue where the previous call ended, so a block can become eligible only when pos opens
+  // a new query block; the filing kernel (which files [filed, eligible) itself) runs only then
+  if (pos == 0 || decode_eligible(s, pos) != decode_eligible(s, pos - 1))
+    MDR_TRY(launch_decode_file(s, k_cache, codebook, code_bias, d, decode_eligible(s, pos), hs));
   MDR_TRY(launch_decode_attend(s, q_new, k_cache, v_cache, codebook, code_bias, d, force, pos, n_new, out, sel, hs));
   return MDR_OK;
 }

@@ -44,10 +44,10 @@ __global__ __launch_bounds__(256) void k_dec_file(const T* __restrict__ K, const
     __syncthreads();
     if (tid == 0) {
       const int a = d.addr[(size_t)bh * s.nb + i];
-      int32_t* n_a = d.ring_n + (size_t)bh * s.A + a;
-      const int n = *n_a;
-      d.ring[((size_t)bh * s.A + a) * s.cap + n % s.cap] = i;
-      *n_a = n + 1;
+      int32_t* rec = d.ring + ((size_t)bh * s.A + a) * (s.cap + 1);
+      const int n = rec[0];
+      rec[1 + n % s.cap] = i;
+      rec[0] = n + 1;
       if (n >= s.cap) d.overflow[bh] += 1;
     }
   }
@@ -55,6 +55,13 @@ __global__ __launch_bounds__(256) void k_dec_file(const T* __restrict__ K, const
     d.summarized[bh] = max(summ, target);
     d.filed[bh] = max(filed, target);
   }
+}
+
+// Every ring record to (0 filed, empty slots).
+__global__ __launch_bounds__(256) void k_ring_reset(int32_t* ring, long long records, int cap) {
+  const long long n = records * (cap + 1);
+  for (long long x = (long long)blockIdx.x * 256 + threadIdx.x; x < n; x += (long long)gridDim.x * 256)
+    ring[x] = x % (cap + 1) == 0 ? 0 : -1;
 }
 
 // (value, index) as one 64-bit key ordered by value descending, then index ascending.
@@ -86,56 +93,104 @@ __global__ __launch_bounds__(256) void k_dec_attend(const T* __restrict__ Qn, co
                                                     Shape s) {
   constexpr int LPC = 256 / kMaxCodesTotal;  // lanes per code logit
   constexpr int DPL = D / LPC;
+  constexpr int KG = 16;      // key groups in the weighted sum of V
+  constexpr int DL = D / 16;  // dims per lane there (16 lanes cover a row)
+  constexpr int VK = 16;      // keys per lane whose V rows are requested before the softmax
+  constexpr int RECMAX = kMaxProbes * 17;
   __shared__ float qs[D];
   __shared__ float mu[kMaxCodesTotal];
   __shared__ int probes[kMaxProbes];
   __shared__ int pstart[kMaxProbes + 1];
+  __shared__ int rec[RECMAX];  // the probed addresses' ring records (when capacity <= 16)
   __shared__ int cand[kDecMaxCand];
   __shared__ float rho[kDecMaxCand];
   __shared__ int selb[kMaxRemote];
   __shared__ int nsel_s;
   __shared__ float sc[kDecMaxKeys];
-  __shared__ float part[4][D];
+  __shared__ float part[KG][D];
   __shared__ float wred[4];
   // thread 0's selection lists (LDS rather than scratch)
   __shared__ int tcode[kMaxSubspaces][kMaxProbes];
   __shared__ float tval[kMaxSubspaces][kMaxProbes];
-  __shared__ uint64_t top[kMaxProbes];
   __shared__ uint64_t best[kMaxProbes];
+  __shared__ uint64_t vkey[256];
   const int ti = blockIdx.x, bh = blockIdx.y, h = bh % s.H;
   const int t = pos + ti, j = t / s.blk;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int GC = s.G * s.C;
   const size_t qrow = (size_t)bh * n_new + ti;
+  // the query row and this lane's codebook slice (code cc, dims [pl·DPL, (pl+1)·DPL)) together
+  const int cc = tid / LPC, pl = tid % LPC;
+  float w[DPL];
+  {
+    const float* wr = cb + ((size_t)h * GC + (cc < GC ? cc : 0)) * D + pl * DPL;
+#pragma unroll
+    for (int x = 0; x < DPL; ++x) w[x] = wr[x];
+  }
+  const float bv = (bias && cc < GC) ? bias[h * GC + cc] : 0.f;
   if (tid < D) qs[tid] = (float)Qn[qrow * D + tid];
   __syncthreads();
   // ---- probe logits mu[g, c] = <codebook[h, g, c], q> + bias: four adjacent lanes per code
   {
-    const int cc = tid / LPC, pl = tid % LPC;
     float acc = 0.f;
-    if (cc < GC) {
-      const float* wr = cb + ((size_t)h * GC + cc) * D + pl * DPL;
 #pragma unroll
-      for (int x = 0; x < DPL; ++x) acc = fmaf(wr[x], qs[pl * DPL + x], acc);
-    }
+    for (int x = 0; x < DPL; ++x) acc = fmaf(w[x], qs[pl * DPL + x], acc);
 #pragma unroll
     for (int x = 1; x < LPC; x <<= 1) acc += __shfl_xor(acc, x);
-    if (pl == 0 && cc < GC) mu[cc] = acc + (bias ? bias[h * GC + cc] : 0.f);
+    if (pl == 0 && cc < GC) mu[cc] = acc + bv;
   }
   __syncthreads();
   // ---- top-P addresses by (sum_g mu[g, c_g] desc, address asc).  Only the top-min(P, C) codes of
   // a subspace can take part, and only rank vectors with prod (k_g + 1) <= P (each is beaten by
-  // prod (k_g + 1) - 1 others); they are visited depth first.
-  if (tid == 0) {
-    const int PG = s.P < s.C ? s.P : s.C;
-    for (int g = 0; g < s.G; ++g) {
-      int n = 0;
-      for (int c = 0; c < s.C; ++c) n = dec_insert(top, n, PG, dec_key(mu[g * s.C + c], c));
-      for (int r = 0; r < PG; ++r) {
-        tcode[g][r] = dec_key_index(top[r]);
-        tval[g][r] = mu[g * s.C + tcode[g][r]];
+  // prod (k_g + 1) - 1 others).  Wave g ranks subspace g's codes (a code's rank = the number of
+  // codes with a larger key); one thread per rank vector scores it; a vector's rank among the
+  // scored ones places it.  Keys are distinct, so every rank is.
+  const int PG = s.P < s.C ? s.P : s.C;
+  if (tid < s.P) probes[tid] = -1;  // filled below (there are always at least P candidates)
+  if (wave < s.G) {
+    const int g = wave;
+    const uint64_t key = lane < s.C ? dec_key(mu[g * s.C + lane], lane) : 0;
+    int rank = 0;
+    for (int o = 0; o < s.C; ++o) {
+      const uint64_t ok = ((uint64_t)(uint32_t)__shfl((int)(key >> 32), o) << 32) | (uint32_t)__shfl((int)key, o);
+      rank += ok > key;
+    }
+    if (lane < s.C && rank < PG) {
+      tcode[g][rank] = lane;
+      tval[g][rank] = mu[g * s.C + lane];
+    }
+  }
+  __syncthreads();
+  int nvec = 1;
+  for (int g = 0; g < s.G; ++g) nvec *= PG;
+  if (nvec <= 256) {
+    uint64_t key = 0;
+    if (tid < nvec) {
+      int rem = tid, prod = 1;
+      int rk[kMaxSubspaces];
+      for (int g = s.G - 1; g >= 0; --g) {
+        rk[g] = rem % PG;
+        rem /= PG;
+        prod *= rk[g] + 1;
+      }
+      if (prod <= s.P) {
+        float sig = 0.f;
+        int a = 0;
+        for (int g = 0; g < s.G; ++g) {
+          sig += tval[g][rk[g]];
+          a = a * s.C + tcode[g][rk[g]];
+        }
+        key = dec_key(sig, a);
       }
     }
+    vkey[tid] = key;
+    __syncthreads();
+    if (key != 0) {
+      int rank = 0;
+      for (int o = 0; o < nvec; ++o) rank += vkey[o] > key;
+      if (rank < s.P) probes[rank] = dec_key_index(key);
+    }
+  } else if (tid == 0) {  // large rank spaces: depth-first over the vectors with prod <= P
     int nb = 0;
     int rk[kMaxSubspaces], prod[kMaxSubspaces + 1];
     int g = 0;
@@ -161,13 +216,22 @@ __global__ __launch_bounds__(256) void k_dec_attend(const T* __restrict__ Qn, co
       }
       nb = dec_insert(best, nb, s.P, dec_key(sig, a));
     }
-    // views in probe rank order, newest first, cut at M
+    for (int p = 0; p < s.P; ++p) probes[p] = dec_key_index(best[p]);
+  }
+  __syncthreads();
+  // ---- the probed rings (count, then slots) in one read each; views in probe rank order, newest
+  // first, cut at M
+  const int RL = s.cap + 1;
+  const bool rec_lds = s.P * RL <= RECMAX;  // uniform
+  auto ring_of = [&](int p) -> const int32_t* { return d.ring + ((size_t)bh * s.A + max(probes[p], 0)) * RL; };
+  if (rec_lds)
+    for (int x = tid; x < s.P * RL; x += 256) rec[x] = probes[x / RL] < 0 ? 0 : ring_of(x / RL)[x % RL];
+  __syncthreads();
+  if (tid == 0) {
     int run = 0;
     for (int p = 0; p < s.P; ++p) {
-      const int a = dec_key_index(best[p]);
-      probes[p] = a;
       pstart[p] = run;
-      const int n = d.ring_n[(size_t)bh * s.A + a];
+      const int n = probes[p] < 0 ? 0 : rec_lds ? rec[p * RL] : ring_of(p)[0];
       run = min(s.M, run + min(n, s.cap));
     }
     pstart[s.P] = run;
@@ -178,9 +242,9 @@ __global__ __launch_bounds__(256) void k_dec_attend(const T* __restrict__ Qn, co
     const int p = x / s.cap, e = x % s.cap;
     const int k = pstart[p] + e;
     if (k < pstart[p + 1]) {
-      const int a = probes[p];
-      const int n = d.ring_n[(size_t)bh * s.A + a];
-      cand[k] = d.ring[((size_t)bh * s.A + a) * s.cap + (n - 1 - e) % s.cap];
+      const int32_t* r = rec_lds ? rec + p * RL : ring_of(p);
+      const int n = r[0];
+      cand[k] = r[1 + (n - 1 - e) % s.cap];
     }
   }
   __syncthreads();
@@ -206,11 +270,17 @@ __global__ __launch_bounds__(256) void k_dec_attend(const T* __restrict__ Qn, co
     }
   }
   __syncthreads();
-  // ---- top-R by (score desc, block asc), then the forced target under the same budget
+  // ---- top-R by (score desc, block asc): a candidate's rank is the number of candidates with a
+  // larger key (blocks are distinct, so ranks are); then the forced target under the same budget
+  for (int k = tid; k < ncand; k += 256) {
+    const uint64_t key = dec_key(rho[k], cand[k]);
+    int rank = 0;
+    for (int o = 0; o < ncand; ++o) rank += dec_key(rho[o], cand[o]) > key;
+    if (rank < s.R) selb[rank] = cand[k];
+  }
+  __syncthreads();
   if (tid == 0) {
-    int nr = 0;
-    for (int k = 0; k < ncand; ++k) nr = s.R > 0 ? dec_insert(top, nr, s.R, dec_key(rho[k], cand[k])) : 0;
-    for (int r = 0; r < nr; ++r) selb[r] = dec_key_index(top[r]);
+    int nr = min(ncand, s.R);
     if (force && s.R > 0) {
       const int f = force[qrow];
       if (f >= 0 && f <= j - s.L) {
@@ -237,6 +307,17 @@ __global__ __launch_bounds__(256) void k_dec_attend(const T* __restrict__ Qn, co
   const float c = s.scale * kLog2eDec;
   const size_t rowbase = (size_t)bh * s.S;
   auto key_token = [&](int k) -> int { return k < nrk ? selb[k / s.blk] * s.blk + k % s.blk : lo + (k - nrk); };
+  // V rows of this lane's first VK keys (group kg = tid / 16 takes keys kg, kg + 16, ...) are requested
+  // together with the K rows of the scores
+  const int kg = tid >> 4, l = tid & 15;
+  float vv[VK][DL];
+#pragma unroll
+  for (int u = 0; u < VK; ++u) {
+    const int k = kg + u * KG;
+    const T* vr = V + (rowbase + key_token(k < nkeys ? k : 0)) * D + l * DL;
+#pragma unroll
+    for (int x = 0; x < DL; ++x) vv[u][x] = to_f(vr[x]);
+  }
   float mx = -INFINITY;
   for (int k = tid; k < nkeys; k += 256) {
     const T* kr = K + (rowbase + key_token(k)) * D;
@@ -267,22 +348,34 @@ __global__ __launch_bounds__(256) void k_dec_attend(const T* __restrict__ Qn, co
   if (lane == 0) wred[wave] = sum;
   __syncthreads();
   const float total = (wred[0] + wred[1]) + (wred[2] + wred[3]);
-  // o[d] = sum_k p_k V[k][d]: wave w takes keys w, w + 4, ...; lane d (and d + 64) one dimension
+  // o[d] = sum_k p_k V[k][d]: lane l of group kg holds dims [l·D/16, (l+1)·D/16) for keys kg, kg + 16,
+  // ...; the group partials are then added in group order
   {
-    float acc0 = 0.f, acc1 = 0.f;
-    for (int k = wave; k < nkeys; k += 4) {
-      const T* vr = V + (rowbase + key_token(k)) * D;
-      const float p = sc[k];
-      if (lane < D) acc0 = fmaf(p, to_f(vr[lane]), acc0);
-      if (D > 64) acc1 = fmaf(p, to_f(vr[lane + 64]), acc1);
+    float acc[DL];
+#pragma unroll
+    for (int x = 0; x < DL; ++x) acc[x] = 0.f;
+#pragma unroll
+    for (int u = 0; u < VK; ++u) {
+      const int k = kg + u * KG;
+      const float p = k < nkeys ? sc[k] : 0.f;
+#pragma unroll
+      for (int x = 0; x < DL; ++x) acc[x] = fmaf(p, vv[u][x], acc[x]);
     }
-    if (lane < D) part[wave][lane] = acc0;
-    if (D > 64) part[wave][lane + 64] = acc1;
+    for (int k = kg + VK * KG; k < nkeys; k += KG) {
+      const T* vr = V + (rowbase + key_token(k)) * D + l * DL;
+      const float p = sc[k];
+#pragma unroll
+      for (int x = 0; x < DL; ++x) acc[x] = fmaf(p, to_f(vr[x]), acc[x]);
+    }
+#pragma unroll
+    for (int x = 0; x < DL; ++x) part[kg][l * DL + x] = acc[x];
   }
   __syncthreads();
   if (tid < D) {
-    const float o = ((part[0][tid] + part[1][tid]) + (part[2][tid] + part[3][tid])) / total;
-    out[qrow * D + tid] = (T)o;
+    float o = 0.f;
+#pragma unroll
+    for (int g = 0; g < KG; ++g) o += part[g][tid];
+    out[qrow * D + tid] = (T)(o / total);
   }
 }
 
@@ -318,6 +411,14 @@ hipError_t dec_attend_t(const Shape& s, const void* q, const void* k, const void
 }
 
 }  // namespace
+
+hipError_t launch_ring_reset(int32_t* ring, long long records, int cap, hipStream_t st) {
+  long long blocks = (records * (cap + 1) + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(k_ring_reset, dim3((unsigned)blocks), dim3(256), 0, st, ring, records, cap);
+  return hipGetLastError();
+}
 
 hipError_t launch_decode_file(const Shape& s, const void* k_cache, const float* codebook, const float* bias,
                               const DecState& d, int target, hipStream_t st) {

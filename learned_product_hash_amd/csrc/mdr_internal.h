@@ -58,8 +58,8 @@ struct Buffers {
 
 // Streaming-decode state (one region of a caller-owned buffer each).
 struct DecState {
-  int32_t* ring;        // [B,H,A,cap] filed block ids; block n of an address sits in slot n % cap
-  int32_t* ring_n;      // [B,H,A] blocks filed per address so far
+  int32_t* ring;        // [B,H,A,cap+1]: blocks filed under the address so far, then cap slots;
+                        // the n-th block filed sits in slot n % cap
   int32_t* overflow;    // [B,H] blocks evicted so far
   int32_t* summarized;  // [B,H] blocks whose summary and address are in ksum / addr
   int32_t* filed;       // [B,H] blocks filed so far (blocks 0 .. filed - 1)
@@ -165,6 +165,7 @@ bool probe_fuses_post(const Shape& s);
 size_t probe_lds_bytes(const Shape& s);
 // Decode: file blocks [filed, target) of every (b,h) (summarising those not summarised yet), then
 // route and attend tokens pos .. pos + n_new - 1 (one query block).
+hipError_t launch_ring_reset(int32_t* ring, long long records, int cap, hipStream_t st);
 hipError_t launch_decode_file(const Shape& s, const void* k_cache, const float* codebook, const float* bias,
                               const DecState& d, int target, hipStream_t st);
 hipError_t launch_decode_attend(const Shape& s, const void* q_new, const void* k_cache, const void* v_cache,

@@ -126,14 +126,14 @@ def test_decode_state_size_and_view(mdr):
     n = mdr.mdr_decode_state_size(cfg)
     A = 16 * 16
     nb = 4096 // 64
-    assert n >= 8 * (A * 2 + A + nb) * 4 + 8 * nb * 64 * 4
+    assert n >= 8 * (A * 3 + nb) * 4 + 8 * nb * 64 * 4
     # (remote + local) * block above 4096 keys, or an invalid config: no state
     assert mdr.lib.mdr_decode_state_size(ctypes.byref(mdr.config(**_good(remote=16, local=60)))) == 0
     assert mdr.lib.mdr_decode_state_size(ctypes.byref(mdr.config(**_good(seq=4000)))) == 0
     v = mdr.MdrDecodeView()
     base = 1 << 20
     assert mdr.lib.mdr_decode_state_view(ctypes.byref(cfg), base, ctypes.byref(v)) == 0
-    ptrs = [v.ring, v.ring_n, v.overflow, v.summarized, v.filed, v.addr, v.ksum]
+    ptrs = [v.ring, v.overflow, v.summarized, v.filed, v.addr, v.ksum]
     assert ptrs == sorted(ptrs) and ptrs[0] == base and ptrs[-1] + nb * 64 * 4 * 8 <= base + n
     assert all(p % 256 == 0 for p in ptrs)
     assert mdr.lib.mdr_decode_state_view(ctypes.byref(cfg), base + 4, ctypes.byref(v)) == 1
