@@ -325,6 +325,38 @@ def attention_packed(q, k, v, sel_rows, block, local, tokens=None, scale=None, d
     return out
 
 
+def attention_lse2(q, k, sel_rows, block, local, tokens=None, scale=None) -> np.ndarray:
+    """Per token, log2 of sum_s 2^(scale * log2(e) * q_t . k_s) over its selected keys (float64): the
+    softmax normaliser in base 2 that the backward pass uses to recompute the weights."""
+    S, D = q.shape
+    toks = np.arange(S) if tokens is None else np.asarray(tokens, dtype=np.int64)
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    mask = selected_mask(np.asarray(sel_rows), toks, S, block, local)
+    scores = (np.asarray(q, dtype=np.float64)[toks] @ np.asarray(k, dtype=np.float64).T) * scale
+    scores = np.where(mask, scores, -np.inf)
+    mx = scores.max(axis=1)
+    return (mx + np.log(np.exp(scores - mx[:, None]).sum(axis=1))) / math.log(2.0)
+
+
+def attention_backward_dense(q, k, v, sel_rows, block, local, d_out, scale=None):
+    """Gradients of attention_dense over all tokens (the routing held fixed) for the upstream
+    gradient d_out, densely in float64.  With P the masked softmax of scale * q k^T and O = P v:
+    dV = P^T dO; dP = dO v^T; dS = P * (dP - rowsum(dO * O)); dQ = scale * dS k; dK = scale * dS^T q.
+    q, k, v, d_out [S, D]; sel_rows [S, R].  Returns (dq, dk, dv) [S, D] float64."""
+    S, D = q.shape
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    q64, k64, v64, do64 = (np.asarray(x, dtype=np.float64) for x in (q, k, v, d_out))
+    mask = selected_mask(np.asarray(sel_rows), np.arange(S), S, block, local)
+    scores = np.where(mask, (q64 @ k64.T) * scale, -np.inf)
+    p = np.exp(scores - scores.max(axis=1, keepdims=True))
+    p /= p.sum(axis=1, keepdims=True)
+    o = p @ v64
+    dv = p.T @ do64
+    dp = do64 @ v64.T
+    ds = p * (dp - (do64 * o).sum(axis=1, keepdims=True))
+    return scale * ds @ k64, scale * ds.T @ q64, dv
+
+
 # ---------------------------------------------------------------- core + mixer
 
 def routed_attention(q, k, v, codebook, bias, w, force=None, rdtype=np.float32):

@@ -321,3 +321,56 @@ def test_mixer_matches_brute_force():
         assert [[i for i in row if i >= 0] for row in r["sel"]] == bf["sel"]
         o[:, cols] = np.array(bf["out"])
     np.testing.assert_allclose(delta[0], o @ inp["wo"].astype(np.float64), rtol=0, atol=1e-11)
+
+
+def _routed_case(seed, seq=256):
+    w = synth.workload("tiny", seq=seq)
+    inp = synth.make_core_inputs(w, seed)
+    q, k, v = (inp[n][0, 0].astype(np.float64) for n in ("q", "k", "v"))
+    r = oracle.route_head(inp["q"][0, 0], inp["k"][0, 0], inp["codebook"][0], None, w)
+    return w, q, k, v, r["sel"]
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_attention_backward_matches_autograd(seed):
+    """The closed-form gradients against torch autograd through a dense masked softmax (float64)."""
+    w, q, k, v, sel = _routed_case(seed)
+    rng = np.random.default_rng(100 + seed)
+    d_out = rng.standard_normal(q.shape)
+    dq, dk, dv = oracle.attention_backward_dense(q, k, v, sel, w.block, w.local, d_out)
+    S, D = q.shape
+    tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    mask = torch.from_numpy(oracle.selected_mask(sel, np.arange(S), S, w.block, w.local))
+    scores = (tq @ tk.T) / math.sqrt(D)
+    out = torch.softmax(scores.masked_fill(~mask, float("-inf")), dim=-1) @ tv
+    out.backward(torch.from_numpy(d_out))
+    np.testing.assert_allclose(dq, tq.grad.numpy(), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(dk, tk.grad.numpy(), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(dv, tv.grad.numpy(), rtol=1e-10, atol=1e-12)
+
+
+def test_attention_backward_matches_finite_differences():
+    """Directional derivatives of <d_out, attention_dense> by central differences."""
+    w, q, k, v, sel = _routed_case(2, seq=128)
+    rng = np.random.default_rng(7)
+    d_out = rng.standard_normal(q.shape)
+    dq, dk, dv = oracle.attention_backward_dense(q, k, v, sel, w.block, w.local, d_out)
+    f = lambda q_, k_, v_: float((oracle.attention_dense(q_, k_, v_, sel, w.block, w.local) * d_out).sum())
+    h = 1e-6
+    for grad, which in ((dq, 0), (dk, 1), (dv, 2)):
+        u = rng.standard_normal(q.shape)
+        args_p = [q, k, v]
+        args_m = [q, k, v]
+        args_p[which] = args_p[which] + h * u
+        args_m[which] = args_m[which] - h * u
+        fd = (f(*args_p) - f(*args_m)) / (2 * h)
+        assert abs(fd - float((grad * u).sum())) <= 1e-6 * max(1.0, abs(fd))
+
+
+def test_attention_lse2_is_the_softmax_normaliser():
+    w, q, k, v, sel = _routed_case(3)
+    S, D = q.shape
+    lse2 = oracle.attention_lse2(q, k, sel, w.block, w.local)
+    mask = oracle.selected_mask(sel, np.arange(S), S, w.block, w.local)
+    direct = np.log2(np.where(mask, np.exp((q @ k.T) / math.sqrt(D)), 0.0).sum(axis=1))
+    np.testing.assert_allclose(lse2, direct, rtol=1e-12, atol=1e-12)
