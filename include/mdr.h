@@ -213,6 +213,34 @@ mdr_status mdr_stage_attend(const mdr_config* cfg, const void* q, const void* k,
                             const int32_t* sel, void* out, void* workspace, size_t workspace_bytes,
                             void* stream);
 
+/* mdr_stage_attend that also writes each token's softmax normaliser in base-2
+ * log form, the one saved tensor the backward below needs (the selected set is
+ * the other):
+ *   lse [B,H,S] fp32 out, or NULL (nothing written; the call is then
+ *   mdr_stage_attend): lse[t] = log2 sum_s 2^(c q_t.k_s) over the token's
+ *   selected keys, c = softmax_scale * log2(e).  Everything else as above. */
+mdr_status mdr_stage_attend_lse(const mdr_config* cfg, const void* q, const void* k, const void* v,
+                                const int32_t* sel, void* out, float* lse, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
+/* Gradient of the selected-set attention with the selection held fixed.  The
+ * pages leave training of the router open (remio.ai, "The 99.35% result does
+ * not prove language quality"); after selection the attention is an exact
+ * softmax (aitechinspire.com "Snapshot"), whose gradient this is:
+ *   P = 2^(c q.k - lse) over the selected keys, D_t = dO_t . O_t,
+ *   dV = P^T dO, dS = P (dO V^T - D), dQ = scale dS K, dK = scale dS^T Q.
+ *   q, k, v, sel  as passed to mdr_stage_attend_lse; out, lse its outputs;
+ *   d_out [B,H,S,D] the gradient of out (cfg->dtype);
+ *   dq, dk, dv [B,H,S,D] out (cfg->dtype), overwritten -- every row, including
+ *   keys no token selected (zero remote share);
+ *   workspace >= mdr_workspace_size bytes (its contents are overwritten).
+ * Sums are fp32; each remote block's share of dQ is rounded once to the io
+ * dtype before the slot-ordered sum.  Deterministic: no atomics. */
+mdr_status mdr_stage_attend_backward(const mdr_config* cfg, const void* q, const void* k, const void* v,
+                                     const int32_t* sel, const void* out, const float* lse,
+                                     const void* d_out, void* dq, void* dk, void* dv, void* workspace,
+                                     size_t workspace_bytes, void* stream);
+
 /* ---- streaming decode ----
  * Incremental routing for decoding (remio.ai, "What sparse attention
  * researchers should watch next", names it the open systems question).  Each

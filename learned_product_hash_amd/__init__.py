@@ -20,7 +20,8 @@ __all__ = [
     "LIB_PATH", "MdrError", "MdrConfig", "MdrRouting", "MDR_F32", "MDR_BF16", "config", "lib",
     "mdr_abi_version", "mdr_status_string", "mdr_check_config", "mdr_workspace_size",
     "mdr_routed_attention", "mdr_routed_attention_profiled", "mdr_mixer_forward", "mdr_stage_address", "mdr_stage_post",
-    "mdr_stage_probe_rerank", "mdr_stage_attend", "workspace", "routing_buffers",
+    "mdr_stage_probe_rerank", "mdr_stage_attend", "mdr_stage_attend_lse", "mdr_stage_attend_backward",
+    "workspace", "routing_buffers",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmdr.so")
@@ -76,6 +77,8 @@ _SIGS = {
     "mdr_stage_post": ([_cfgp, _vp, _vp, _vp, _vp, _vp], _i32),
     "mdr_stage_probe_rerank": ([_cfgp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp], _i32),
     "mdr_stage_attend": ([_cfgp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], _i32),
+    "mdr_stage_attend_lse": ([_cfgp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], _i32),
+    "mdr_stage_attend_backward": ([_cfgp] + [_vp] * 11 + [_sz, _vp], _i32),
     "mdr_decode_state_size": ([_cfgp], _sz),
     "mdr_decode_state_view": ([_cfgp, _vp, ctypes.POINTER(MdrDecodeView)], _i32),
     "mdr_decode_prime": ([_cfgp, _vp, _vp, _vp, ctypes.c_int32, _vp, _sz, _vp], _i32),
@@ -215,6 +218,19 @@ def mdr_stage_attend(cfg, q, k, v, sel, out, ws, stream=None):
     wp, wn = _ws(ws)
     _check(lib.mdr_stage_attend(ctypes.byref(cfg), _ptr(q), _ptr(k), _ptr(v), _ptr(sel), _ptr(out), wp, wn,
                                 _stream(stream)), "mdr_stage_attend")
+
+
+def mdr_stage_attend_lse(cfg, q, k, v, sel, out, lse, ws, stream=None):
+    wp, wn = _ws(ws)
+    _check(lib.mdr_stage_attend_lse(ctypes.byref(cfg), _ptr(q), _ptr(k), _ptr(v), _ptr(sel), _ptr(out), _ptr(lse),
+                                    wp, wn, _stream(stream)), "mdr_stage_attend_lse")
+
+
+def mdr_stage_attend_backward(cfg, q, k, v, sel, out, lse, d_out, dq, dk, dv, ws, stream=None):
+    wp, wn = _ws(ws)
+    _check(lib.mdr_stage_attend_backward(ctypes.byref(cfg), _ptr(q), _ptr(k), _ptr(v), _ptr(sel), _ptr(out),
+                                         _ptr(lse), _ptr(d_out), _ptr(dq), _ptr(dk), _ptr(dv), wp, wn,
+                                         _stream(stream)), "mdr_stage_attend_backward")
 
 
 # ---- streaming decode

@@ -95,6 +95,7 @@ size_t layout(const Shape& s, char* base, Buffers* b) {
   t.bins = (int32_t*)take(BH * (size_t)s.cells_per_bh * s.blk * 4);
   t.part_o = take(BH * s.S * s.R * s.D * e);
   t.part_ml = (float*)take(BH * s.S * s.R * 8);
+  t.dvec = (float*)take(BH * s.S * 4);
   if (s.W > 0) {
     const size_t qkv = BH * s.S * s.D * e;
     t.mq = take(qkv);
@@ -104,6 +105,7 @@ size_t layout(const Shape& s, char* base, Buffers* b) {
   } else {
     t.mq = t.mk = t.mv = t.mo = nullptr;
   }
+  t.lse = nullptr;
   if (b) *b = t;
   return off;
 }
@@ -331,8 +333,9 @@ mdr_status mdr_stage_probe_rerank(const mdr_config* cfg, const void* q, const fl
                                         nullptr, nullptr, (hipStream_t)stream));
 }
 
-mdr_status mdr_stage_attend(const mdr_config* cfg, const void* q, const void* k, const void* v, const int32_t* sel,
-                            void* out, void* workspace, size_t workspace_bytes, void* stream) {
+mdr_status mdr_stage_attend_lse(const mdr_config* cfg, const void* q, const void* k, const void* v,
+                                const int32_t* sel, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                                void* stream) {
   Shape s;
   mdr_status st = shape_from_config(cfg, false, &s);
   if (st != MDR_OK) return st;
@@ -342,12 +345,42 @@ mdr_status mdr_stage_attend(const mdr_config* cfg, const void* q, const void* k,
   Buffers b;
   st = check_workspace(s, workspace, workspace_bytes, &b);
   if (st != MDR_OK) return st;
+  b.lse = lse;
   hipStream_t hs = (hipStream_t)stream;
   if (s.R > 0 && s.ne > 0) {
     MDR_TRY(launch_fill(b.cellcnt, (long long)s.B * s.H * s.cells_per_bh, 0, hs));
     MDR_TRY(launch_pair_bin(s, sel, b.cellcnt, b.bins, hs));
   }
   MDR_TRY(launch_attend(s, q, k, v, sel, out, b, hs));
+  return MDR_OK;
+}
+
+mdr_status mdr_stage_attend(const mdr_config* cfg, const void* q, const void* k, const void* v, const int32_t* sel,
+                            void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  return mdr_stage_attend_lse(cfg, q, k, v, sel, out, nullptr, workspace, workspace_bytes, stream);
+}
+
+mdr_status mdr_stage_attend_backward(const mdr_config* cfg, const void* q, const void* k, const void* v,
+                                     const int32_t* sel, const void* out, const float* lse, const void* d_out,
+                                     void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                                     void* stream) {
+  Shape s;
+  mdr_status st = shape_from_config(cfg, false, &s);
+  if (st != MDR_OK) return st;
+  s.W = 0;
+  if (!q || !k || !v || !out || !lse || !d_out || !dq || !dk || !dv || (!sel && s.R > 0)) return MDR_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(d_out) || !aligned16(dq) ||
+      !aligned16(dk) || !aligned16(dv))
+    return MDR_ERR_INVALID_ARG;
+  Buffers b;
+  st = check_workspace(s, workspace, workspace_bytes, &b);
+  if (st != MDR_OK) return st;
+  hipStream_t hs = (hipStream_t)stream;
+  if (s.R > 0 && s.ne > 0) {
+    MDR_TRY(launch_fill(b.cellcnt, (long long)s.B * s.H * s.cells_per_bh, 0, hs));
+    MDR_TRY(launch_pair_bin_ordered(s, sel, b.cellcnt, b.bins, hs));
+  }
+  MDR_TRY(launch_attend_backward(s, q, k, v, sel, out, lse, d_out, dq, dk, dv, b, hs));
   return MDR_OK;
 }
 

@@ -54,6 +54,9 @@ struct Buffers {
   void* mk;
   void* mv;
   void* mo;
+  float* lse;          // [B,H,S] optional output of the attention: log2 of each token's softmax
+                       // normaliser sum_s 2^(scale log2(e) q.k_s) (nullptr: not written)
+  float* dvec;         // [B,H,S] backward: D_t = dO_t . O_t
 };
 
 // Streaming-decode state (one region of a caller-owned buffer each).
@@ -181,6 +184,15 @@ size_t remote_lds_bytes(const Shape& s);
 hipError_t launch_attend(const Shape& s, const void* q, const void* k, const void* v,
                          const int32_t* sel, void* out, const Buffers& b, hipStream_t st,
                          hipEvent_t* ev = nullptr);
+// The selection's pairs binned into cells in ascending token order within each cell (the cell
+// counters must be zero before the call).
+hipError_t launch_pair_bin_ordered(const Shape& s, const int32_t* sel, int32_t* cellcnt, int32_t* bins,
+                                   hipStream_t st);
+// Backward of the attention under a fixed selection (cellcnt / bins must hold the selection's
+// pairs; part_o receives the remote dQ shares, dvec the row dots).
+hipError_t launch_attend_backward(const Shape& s, const void* q, const void* k, const void* v, const int32_t* sel,
+                                  const void* out, const float* lse, const void* d_out, void* dq, void* dk, void* dv,
+                                  const Buffers& b, hipStream_t st);
 hipError_t launch_project_heads(const Shape& s, const void* x, const void* w, void* out, bool rope,
                                 hipStream_t st);
 hipError_t launch_project_out(const Shape& s, const void* o, const void* wo, void* delta,

@@ -357,6 +357,40 @@ def attention_backward_dense(q, k, v, sel_rows, block, local, d_out, scale=None)
     return scale * ds @ k64, scale * ds.T @ q64, dv
 
 
+def attention_backward_packed(q, k, v, sel_rows, block, local, d_out, scale=None):
+    """The gradients of attention_backward_dense, token by token over gathered keys only, so that it
+    runs at lengths where an S x S matrix does not fit.  Entry r of token t's row counts when
+    0 <= sel <= j - L and it repeats no earlier entry (the visible set is a set of blocks); the
+    local window is blocks j - L + 1 .. j up to t.  Per token: p = softmax over its keys, o = p v,
+    D = dO . o, ds = p (v dO - D); dq_t = scale ds k; dk += scale ds q_t; dv += p dO_t.
+    q, k, v, d_out [S, D]; sel_rows [S, R].  Returns (dq, dk, dv) [S, D] float64."""
+    S, D = q.shape
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    q64, k64, v64, do64 = (np.asarray(x, dtype=np.float64) for x in (q, k, v, d_out))
+    dq = np.zeros((S, D))
+    dk = np.zeros((S, D))
+    dv = np.zeros((S, D))
+    for t in range(S):
+        j = t // block
+        blocks = []
+        for i in sel_rows[t]:
+            i = int(i)
+            if 0 <= i <= j - local and i not in blocks:
+                blocks.append(i)
+        idx = [np.arange(i * block, (i + 1) * block) for i in blocks]
+        idx.append(np.arange(max(0, (j - local + 1) * block), t + 1))
+        idx = np.concatenate(idx)
+        s = (k64[idx] @ q64[t]) * scale
+        p = np.exp(s - s.max())
+        p /= p.sum()
+        o = p @ v64[idx]
+        ds = p * (v64[idx] @ do64[t] - do64[t] @ o)
+        dq[t] = scale * (ds @ k64[idx])
+        dk[idx] += scale * ds[:, None] * q64[t][None, :]
+        dv[idx] += p[:, None] * do64[t][None, :]
+    return dq, dk, dv
+
+
 # ---------------------------------------------------------------- core + mixer
 
 def routed_attention(q, k, v, codebook, bias, w, force=None, rdtype=np.float32):

@@ -12,6 +12,7 @@ from .gen import (  # noqa: F401
     Workload,
     bf16_round,
     make_core_inputs,
+    make_grad_inputs,
     make_mixer_inputs,
     workload,
 )

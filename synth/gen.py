@@ -192,6 +192,14 @@ def make_core_inputs(w: Workload, seed: int) -> dict:
     return out
 
 
+def make_grad_inputs(w: Workload, seed: int) -> np.ndarray:
+    """Upstream gradient of the attention output, d_out [B,H,S,D] ~ N(0, 1) (bf16-rounded for bf16
+    workloads), drawn from its own stream so the forward inputs of the same seed are unchanged."""
+    rng = np.random.default_rng([seed, 0x6772])
+    g = _normal(rng, (w.batch, w.heads, w.seq, w.head_dim))
+    return bf16_round(g) if w.dtype == "bf16" else g
+
+
 def make_mixer_inputs(w: Workload, seed: int) -> dict:
     """x [B,S,W], wq/wk/wv [W, H*D], wo [H*D, W] (std 1/sqrt(fan_in)), codebook, bias=None."""
     B, H, S, D, W = w.batch, w.heads, w.seq, w.head_dim, w.width

@@ -36,7 +36,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("mdr_routed_attention", "mdr_mixer_forward", "mdr_stage_address", "mdr_stage_post",
-              "mdr_stage_probe_rerank", "mdr_stage_attend", "mdr_workspace_size", "mdr_check_config"):
+              "mdr_stage_probe_rerank", "mdr_stage_attend", "mdr_stage_attend_lse", "mdr_stage_attend_backward",
+              "mdr_workspace_size", "mdr_check_config"):
         assert n in names
 
 
@@ -107,6 +108,14 @@ def test_entry_points_validate_before_launching(mdr):
     assert lib.mdr_routed_attention(c, p, p, p, p, None, None, p, None, p + 16, need, None) == 1
     assert lib.mdr_stage_attend(c, p, p, p, p, p, p, need - 1, None) == 3
     assert lib.mdr_stage_attend(c, p, p, p, None, p, p, need, None) == 1
+    assert lib.mdr_stage_attend_lse(c, p, p, p, p, p, p, p, need - 1, None) == 3
+    assert lib.mdr_stage_attend_lse(c, p, p, p, p, p + 4, p, p, need, None) == 1
+    bwd = lib.mdr_stage_attend_backward
+    assert bwd(c, p, p, p, p, p, None, p, p, p, p, p, need, None) == 1        # no lse
+    assert bwd(c, p, p, p, p, p, p, None, p, p, p, p, need, None) == 1        # no d_out
+    assert bwd(c, p, p, p, p, p, p, p, p + 8, p, p, p, need, None) == 1       # misaligned dq
+    assert bwd(c, p, p, p, None, p, p, p, p, p, p, p, need, None) == 1        # no selection with R > 0
+    assert bwd(c, p, p, p, p, p, p, p, p, p, p, p, need - 1, None) == 3
     assert lib.mdr_stage_post(c, None, p, p, p, None) == 1
     assert lib.mdr_stage_address(c, p, p, None, p + 4, p, None) == 1
     assert lib.mdr_stage_probe_rerank(c, p, p, None, p, p, p, None, None, None, None) == 1

@@ -374,3 +374,33 @@ def test_attention_lse2_is_the_softmax_normaliser():
     mask = oracle.selected_mask(sel, np.arange(S), S, w.block, w.local)
     direct = np.log2(np.where(mask, np.exp((q @ k.T) / math.sqrt(D)), 0.0).sum(axis=1))
     np.testing.assert_allclose(lse2, direct, rtol=1e-12, atol=1e-12)
+
+
+def _random_selection(rng, S, block, local, R, p_none=0.2, p_repeat=0.2):
+    """Entries in [-1, j - L] with some -1 and some repeated blocks (the shapes a selection can take)."""
+    sel = np.full((S, R), -1, dtype=np.int64)
+    for t in range(S):
+        hi = t // block - local
+        for r in range(R):
+            u = rng.random()
+            if hi < 0 or u < p_none:
+                continue
+            if r > 0 and u < p_none + p_repeat:
+                sel[t, r] = sel[t, rng.integers(0, r)]
+            else:
+                sel[t, r] = rng.integers(0, hi + 1)
+    return sel
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_attention_backward_packed_matches_dense(seed):
+    """The token-by-token gradients against the dense closed form, on a routed selection and on a
+    random one with empty and repeated entries."""
+    w, q, k, v, sel = _routed_case(seed)
+    rng = np.random.default_rng(200 + seed)
+    d_out = rng.standard_normal(q.shape)
+    for rows in (sel, _random_selection(rng, q.shape[0], w.block, w.local, 3)):
+        dense = oracle.attention_backward_dense(q, k, v, rows, w.block, w.local, d_out)
+        packed = oracle.attention_backward_packed(q, k, v, rows, w.block, w.local, d_out)
+        for a, b in zip(packed, dense):
+            np.testing.assert_allclose(a, b, rtol=1e-10, atol=1e-12)
