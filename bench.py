@@ -38,6 +38,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}  # MI355X dense, published (fp32: no fp32 MFMA figure; vector)
 KERNEL_SYMBOL = {  # substrings of the kernels' symbol names in rocprofv3 output
     "address": "k_address",
     "post": "k_post",
@@ -48,6 +49,12 @@ KERNEL_SYMBOL = {  # substrings of the kernels' symbol names in rocprofv3 output
 KERNEL_SOURCE = {
     "address": "mdr_route.hip", "post": "mdr_route.hip", "probe_rerank": "mdr_route.hip",
     "attn_remote": "mdr_attn.hip", "attn_local": "mdr_attn.hip",
+}
+BACKWARD_SYMBOL = {
+    "pair_bin": "k_pair_bin_ordered",
+    "bwd_dot": "k_bwd_dot",
+    "bwd_kv": "k_bwd_kv",
+    "bwd_q": "k_bwd_q",
 }
 CALIB_BYTES = 512 << 20
 HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000  # hipEventDisableSystemFence (hip_runtime_api.h)
@@ -70,6 +77,7 @@ def parse(argv=None):
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-sweep", action="store_true", help="skip the 4K-32K exponent sweep")
     ap.add_argument("--no-decode", action="store_true", help="skip the streaming-decode timing")
+    ap.add_argument("--no-backward", action="store_true", help="skip the attention-backward timing")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run one elementwise copy of 512 MiB first (counter calibration)")
     ap.add_argument("--cpu-heads", type=int, default=8)
@@ -388,6 +396,50 @@ def decode_bench(run, batch, steps=48, warmup=4):
             "alg_bytes_per_step": int(nbytes), "alg_gbps": round(nbytes / (ms * 1e-3) / 1e9, 1)}
 
 
+def backward_bench(run, hip, overhead, steps=20, warmup=3):
+    """The attention backward (dQ, dK, dV under the forward's selection) on the same workload, timed
+    per kernel with HIP events like the forward.  Compulsory bytes: Q, K, V, O, dO read and dQ, dK,
+    dV written once, plus the selection and the fp32 normaliser; algorithmic flops 10 D per visited
+    (query, key) pair (S, dP, dV, dK, dQ; the forward's S and PV count 4 D)."""
+    import torch
+
+    import synth
+
+    mdr, w = run.mdr, run.w
+    B, H, S, D, R = w.batch, w.heads, w.seq, w.head_dim, w.remote
+    e = 2 if w.dtype == "bf16" else 4
+    sel = run.rt["sel"]
+    g = torch.from_numpy(synth.make_grad_inputs(w, 1)).to("cuda").to(run.q.dtype)
+    out = torch.empty_like(run.q)
+    lse = torch.empty(B, H, S, dtype=torch.float32, device="cuda")
+    mdr.mdr_stage_attend_lse(run.cfg, run.q, run.k, run.v, sel, out, lse, run.ws)
+    dq, dk, dv = (torch.empty_like(run.q) for _ in range(3))
+    args = (run.cfg, run.q, run.k, run.v, sel, out, lse, g, dq, dk, dv)
+    for _ in range(warmup):
+        mdr.mdr_stage_attend_backward(*args, run.ws)
+    nk = mdr.MDR_BACKWARD_KERNELS
+    events = hip.create(steps * (nk + 1))
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        mdr.mdr_stage_attend_backward_profiled(*args, events[i * (nk + 1):(i + 1) * (nk + 1)], run.ws)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps
+    per = [max(0.0, sum(hip.elapsed_ms(events[i * (nk + 1) + k], events[i * (nk + 1) + k + 1])
+                        for i in range(steps)) / steps - overhead) for k in range(nk)]
+    hip.destroy(events)
+    pairs = int((sel >= 0).sum().item())
+    qkv = B * H * S * D * e
+    alg_bytes = 8 * qkv + B * H * S * (R * 4 + 4)
+    flops = 10 * D * attended_pairs(w, pairs)
+    total = sum(per)
+    return {"workload": describe(w) + ", upstream gradient ~ N(0, 1), the forward's own selection",
+            "ms_per_call": round(wall * 1e3, 4), "kernels_ms": {n: round(x, 5) for n, x in zip(mdr.BACKWARD_KERNELS, per)},
+            "alg_bytes": alg_bytes, "alg_flops": flops, "tokens_per_s": round(B * S / wall, 1),
+            "hbm_frac": round(alg_bytes / (total * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "mfma_frac": round(flops / (total * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS[w.dtype], 4)}
+
+
 def cpu_baseline(run, heads):
     """The oracle as it stands (routing + gathered fp64 attention), one thread, on a bounded sample."""
     import numpy as np
@@ -485,7 +537,25 @@ def summarize_rocprof(stats_csv, command, w, bench_log=None):
                 lines.append(f"| {k} (`{sym}`) | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                              f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
                              f"{float(r['Percentage']):.1f}% | {ev} |")
-    other = sum(float(r["Percentage"]) for r in rows if not any(sym in r["Name"] for sym in KERNEL_SYMBOL.values()))
+    bwd = {}
+    if bench_log:
+        for line in open(bench_log):
+            if line.startswith("{") and "backward" in json.loads(line):
+                bwd = {k: v * 1e3 for k, v in json.loads(line)["backward"]["kernels_ms"].items()}
+    bl = []
+    for k, sym in BACKWARD_SYMBOL.items():
+        for r in rows:
+            if sym in r["Name"]:
+                ev = f"{bwd[k]:.2f}" if k in bwd else "-"
+                bl.append(f"| {k} (`{sym}`) | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                          f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                          f"{float(r['Percentage']):.1f}% | {ev} |")
+    if bl:
+        lines += ["", "Backward (mdr_stage_attend_backward on the forward's selection):", "",
+                  "| kernel | calls | avg us | min us | max us | share of GPU time | bench.py HIP-event avg us |",
+                  "|---|---|---|---|---|---|---|"] + bl
+    known = list(KERNEL_SYMBOL.values()) + list(BACKWARD_SYMBOL.values())
+    other = sum(float(r["Percentage"]) for r in rows if not any(sym in r["Name"] for sym in known))
     lines += ["", f"Other kernels (input generation, torch copies, routing statistics): {other:.1f}% of GPU time.", ""]
     out = os.path.join(ROOT, "profiles", f"routed_attention_kernels_{w.name}_{w.seq // 1024}k.md")
     os.makedirs(os.path.dirname(out), exist_ok=True)
@@ -562,6 +632,8 @@ def main(argv=None):
     }
     if not a.no_decode and a.workload == "sweep":
         res["decode"] = [decode_bench(run, b) for b in (1, 16)]
+    if not a.no_backward:
+        res["backward"] = backward_bench(run, hip, ev_overhead)
     if not a.no_sweep and a.workload == "sweep":
         res["exponent"] = exponent_sweep(mdr, (4096, 8192, 16384, 32768), a.seed)
     if not a.no_cpu:

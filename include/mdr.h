@@ -241,6 +241,21 @@ mdr_status mdr_stage_attend_backward(const mdr_config* cfg, const void* q, const
                                      const void* d_out, void* dq, void* dk, void* dv, void* workspace,
                                      size_t workspace_bytes, void* stream);
 
+/* Kernels of the backward, in launch order: pair binning (with the counter
+ * fill before it; empty when R = 0 or nb <= L), row dots D, key blocks (dK,
+ * dV, remote dQ shares), query blocks (dQ). */
+#define MDR_BACKWARD_KERNELS 4
+
+/* Profiling form of mdr_stage_attend_backward: events[k] (hipEvent_t created
+ * by the caller) is recorded on `stream` just before the k-th stage above and
+ * events[MDR_BACKWARD_KERNELS] after the last.  A NULL `events` array or
+ * entry is rejected; everything else as in mdr_stage_attend_backward. */
+mdr_status mdr_stage_attend_backward_profiled(const mdr_config* cfg, const void* q, const void* k,
+                                              const void* v, const int32_t* sel, const void* out,
+                                              const float* lse, const void* d_out, void* dq, void* dk,
+                                              void* dv, void* workspace, size_t workspace_bytes,
+                                              void* const* events, void* stream);
+
 /* ---- streaming decode ----
  * Incremental routing for decoding (remio.ai, "What sparse attention
  * researchers should watch next", names it the open systems question).  Each

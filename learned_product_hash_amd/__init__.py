@@ -21,6 +21,7 @@ __all__ = [
     "mdr_abi_version", "mdr_status_string", "mdr_check_config", "mdr_workspace_size",
     "mdr_routed_attention", "mdr_routed_attention_profiled", "mdr_mixer_forward", "mdr_stage_address", "mdr_stage_post",
     "mdr_stage_probe_rerank", "mdr_stage_attend", "mdr_stage_attend_lse", "mdr_stage_attend_backward",
+    "mdr_stage_attend_backward_profiled", "MDR_BACKWARD_KERNELS", "BACKWARD_KERNELS",
     "workspace", "routing_buffers",
 ]
 
@@ -79,6 +80,7 @@ _SIGS = {
     "mdr_stage_attend": ([_cfgp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], _i32),
     "mdr_stage_attend_lse": ([_cfgp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], _i32),
     "mdr_stage_attend_backward": ([_cfgp] + [_vp] * 11 + [_sz, _vp], _i32),
+    "mdr_stage_attend_backward_profiled": ([_cfgp] + [_vp] * 11 + [_sz, ctypes.POINTER(_vp), _vp], _i32),
     "mdr_decode_state_size": ([_cfgp], _sz),
     "mdr_decode_state_view": ([_cfgp, _vp, ctypes.POINTER(MdrDecodeView)], _i32),
     "mdr_decode_prime": ([_cfgp, _vp, _vp, _vp, ctypes.c_int32, _vp, _sz, _vp], _i32),
@@ -231,6 +233,20 @@ def mdr_stage_attend_backward(cfg, q, k, v, sel, out, lse, d_out, dq, dk, dv, ws
     _check(lib.mdr_stage_attend_backward(ctypes.byref(cfg), _ptr(q), _ptr(k), _ptr(v), _ptr(sel), _ptr(out),
                                          _ptr(lse), _ptr(d_out), _ptr(dq), _ptr(dk), _ptr(dv), wp, wn,
                                          _stream(stream)), "mdr_stage_attend_backward")
+
+
+MDR_BACKWARD_KERNELS = 4
+BACKWARD_KERNELS = ("pair_bin", "bwd_dot", "bwd_kv", "bwd_q")
+
+
+def mdr_stage_attend_backward_profiled(cfg, q, k, v, sel, out, lse, d_out, dq, dk, dv, events, ws, stream=None):
+    """``events``: MDR_BACKWARD_KERNELS + 1 raw hipEvent_t handles (ints) created by the caller."""
+    wp, wn = _ws(ws)
+    arr = (_vp * (MDR_BACKWARD_KERNELS + 1))(*events)
+    _check(lib.mdr_stage_attend_backward_profiled(ctypes.byref(cfg), _ptr(q), _ptr(k), _ptr(v), _ptr(sel),
+                                                  _ptr(out), _ptr(lse), _ptr(d_out), _ptr(dq), _ptr(dk), _ptr(dv),
+                                                  wp, wn, arr, _stream(stream)),
+           "mdr_stage_attend_backward_profiled")
 
 
 # ---- streaming decode

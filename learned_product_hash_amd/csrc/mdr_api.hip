@@ -360,10 +360,9 @@ mdr_status mdr_stage_attend(const mdr_config* cfg, const void* q, const void* k,
   return mdr_stage_attend_lse(cfg, q, k, v, sel, out, nullptr, workspace, workspace_bytes, stream);
 }
 
-mdr_status mdr_stage_attend_backward(const mdr_config* cfg, const void* q, const void* k, const void* v,
-                                     const int32_t* sel, const void* out, const float* lse, const void* d_out,
-                                     void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
-                                     void* stream) {
+static mdr_status backward_core(const mdr_config* cfg, const void* q, const void* k, const void* v, const int32_t* sel,
+                                const void* out, const float* lse, const void* d_out, void* dq, void* dk, void* dv,
+                                void* workspace, size_t workspace_bytes, hipEvent_t* ev, void* stream) {
   Shape s;
   mdr_status st = shape_from_config(cfg, false, &s);
   if (st != MDR_OK) return st;
@@ -376,12 +375,32 @@ mdr_status mdr_stage_attend_backward(const mdr_config* cfg, const void* q, const
   st = check_workspace(s, workspace, workspace_bytes, &b);
   if (st != MDR_OK) return st;
   hipStream_t hs = (hipStream_t)stream;
+  if (ev) MDR_TRY(hipEventRecord(ev[0], hs));
   if (s.R > 0 && s.ne > 0) {
     MDR_TRY(launch_fill(b.cellcnt, (long long)s.B * s.H * s.cells_per_bh, 0, hs));
     MDR_TRY(launch_pair_bin_ordered(s, sel, b.cellcnt, b.bins, hs));
   }
-  MDR_TRY(launch_attend_backward(s, q, k, v, sel, out, lse, d_out, dq, dk, dv, b, hs));
+  MDR_TRY(launch_attend_backward(s, q, k, v, sel, out, lse, d_out, dq, dk, dv, b, hs, ev ? ev + 1 : nullptr));
+  if (ev) MDR_TRY(hipEventRecord(ev[MDR_BACKWARD_KERNELS], hs));
   return MDR_OK;
+}
+
+mdr_status mdr_stage_attend_backward(const mdr_config* cfg, const void* q, const void* k, const void* v,
+                                     const int32_t* sel, const void* out, const float* lse, const void* d_out,
+                                     void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                                     void* stream) {
+  return backward_core(cfg, q, k, v, sel, out, lse, d_out, dq, dk, dv, workspace, workspace_bytes, nullptr, stream);
+}
+
+mdr_status mdr_stage_attend_backward_profiled(const mdr_config* cfg, const void* q, const void* k, const void* v,
+                                              const int32_t* sel, const void* out, const float* lse,
+                                              const void* d_out, void* dq, void* dk, void* dv, void* workspace,
+                                              size_t workspace_bytes, void* const* events, void* stream) {
+  if (!events) return MDR_ERR_INVALID_ARG;
+  for (int i = 0; i <= MDR_BACKWARD_KERNELS; ++i)
+    if (!events[i]) return MDR_ERR_INVALID_ARG;
+  return backward_core(cfg, q, k, v, sel, out, lse, d_out, dq, dk, dv, workspace, workspace_bytes,
+                       (hipEvent_t*)events, stream);
 }
 
 // ---- streaming decode

@@ -338,18 +338,21 @@ __global__ __launch_bounds__(BLK * 4) void k_bwd_q(const T* __restrict__ Q, cons
 
 template <typename T, int D, int BLK>
 hipError_t bwd_impl(const Shape& s, const void* q, const void* k, const void* v, const int32_t* sel, const void* o,
-                    const float* lse, const void* d_o, void* dq, void* dk, void* dv, const Buffers& b, hipStream_t st) {
+                    const float* lse, const void* d_o, void* dq, void* dk, void* dv, const Buffers& b, hipStream_t st,
+                    hipEvent_t* ev) {
   const long long n = (long long)s.B * s.H * s.S;
   constexpr int LPT = D * (int)sizeof(T) / 16;
   const long long blocks = (n * LPT + 255) / 256;
+  hipError_t e;
+  if (ev && (e = hipEventRecord(ev[0], st)) != hipSuccess) return e;
   hipLaunchKernelGGL((k_bwd_dot<T, D>), dim3((unsigned)blocks), dim3(256), 0, st, (const T*)o, (const T*)d_o,
                      b.dvec, n);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if ((e = hipGetLastError()) != hipSuccess) return e;
   constexpr size_t kl = bwd_kv_lds<T, D, BLK>();
   if (kl > 65536 && (e = hipFuncSetAttribute((const void*)k_bwd_kv<T, D, BLK>,
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)kl)) != hipSuccess)
     return e;
+  if (ev && (e = hipEventRecord(ev[1], st)) != hipSuccess) return e;
   hipLaunchKernelGGL((k_bwd_kv<T, D, BLK>), dim3(s.nb, s.B * s.H), dim3(BLK * 4), kl, st, (const T*)q,
                      (const T*)k, (const T*)v, (const T*)d_o, lse, b.dvec, b.cellcnt, b.bins, (T*)b.part_o,
                      (T*)dk, (T*)dv, s);
@@ -358,6 +361,7 @@ hipError_t bwd_impl(const Shape& s, const void* q, const void* k, const void* v,
   if (ql > 65536 && (e = hipFuncSetAttribute((const void*)k_bwd_q<T, D, BLK>,
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)ql)) != hipSuccess)
     return e;
+  if (ev && (e = hipEventRecord(ev[2], st)) != hipSuccess) return e;
   hipLaunchKernelGGL((k_bwd_q<T, D, BLK>), dim3(s.nb, s.B * s.H), dim3(BLK * 4), ql, st, (const T*)q, (const T*)k,
                      (const T*)v, (const T*)d_o, lse, b.dvec, sel, (const T*)b.part_o, (T*)dq, s);
   return hipGetLastError();
@@ -365,22 +369,24 @@ hipError_t bwd_impl(const Shape& s, const void* q, const void* k, const void* v,
 
 template <typename T, int D>
 hipError_t bwd_blk(const Shape& s, const void* q, const void* k, const void* v, const int32_t* sel, const void* o,
-                   const float* lse, const void* d_o, void* dq, void* dk, void* dv, const Buffers& b, hipStream_t st) {
+                   const float* lse, const void* d_o, void* dq, void* dk, void* dv, const Buffers& b, hipStream_t st,
+                   hipEvent_t* ev) {
   switch (s.blk) {
-    case 32: return bwd_impl<T, D, 32>(s, q, k, v, sel, o, lse, d_o, dq, dk, dv, b, st);
-    case 64: return bwd_impl<T, D, 64>(s, q, k, v, sel, o, lse, d_o, dq, dk, dv, b, st);
-    case 128: return bwd_impl<T, D, 128>(s, q, k, v, sel, o, lse, d_o, dq, dk, dv, b, st);
+    case 32: return bwd_impl<T, D, 32>(s, q, k, v, sel, o, lse, d_o, dq, dk, dv, b, st, ev);
+    case 64: return bwd_impl<T, D, 64>(s, q, k, v, sel, o, lse, d_o, dq, dk, dv, b, st, ev);
+    case 128: return bwd_impl<T, D, 128>(s, q, k, v, sel, o, lse, d_o, dq, dk, dv, b, st, ev);
     default: return hipErrorInvalidValue;
   }
 }
 
 template <typename T>
 hipError_t bwd_d(const Shape& s, const void* q, const void* k, const void* v, const int32_t* sel, const void* o,
-                 const float* lse, const void* d_o, void* dq, void* dk, void* dv, const Buffers& b, hipStream_t st) {
+                 const float* lse, const void* d_o, void* dq, void* dk, void* dv, const Buffers& b, hipStream_t st,
+                 hipEvent_t* ev) {
   switch (s.D) {
-    case 32: return bwd_blk<T, 32>(s, q, k, v, sel, o, lse, d_o, dq, dk, dv, b, st);
-    case 64: return bwd_blk<T, 64>(s, q, k, v, sel, o, lse, d_o, dq, dk, dv, b, st);
-    case 128: return bwd_blk<T, 128>(s, q, k, v, sel, o, lse, d_o, dq, dk, dv, b, st);
+    case 32: return bwd_blk<T, 32>(s, q, k, v, sel, o, lse, d_o, dq, dk, dv, b, st, ev);
+    case 64: return bwd_blk<T, 64>(s, q, k, v, sel, o, lse, d_o, dq, dk, dv, b, st, ev);
+    case 128: return bwd_blk<T, 128>(s, q, k, v, sel, o, lse, d_o, dq, dk, dv, b, st, ev);
     default: return hipErrorInvalidValue;
   }
 }
@@ -399,9 +405,9 @@ hipError_t launch_pair_bin_ordered(const Shape& s, const int32_t* sel, int32_t* 
 
 hipError_t launch_attend_backward(const Shape& s, const void* q, const void* k, const void* v, const int32_t* sel,
                                   const void* out, const float* lse, const void* d_out, void* dq, void* dk, void* dv,
-                                  const Buffers& b, hipStream_t st) {
-  if (s.dtype == MDR_BF16) return bwd_d<bf16>(s, q, k, v, sel, out, lse, d_out, dq, dk, dv, b, st);
-  return bwd_d<float>(s, q, k, v, sel, out, lse, d_out, dq, dk, dv, b, st);
+                                  const Buffers& b, hipStream_t st, hipEvent_t* ev) {
+  if (s.dtype == MDR_BF16) return bwd_d<bf16>(s, q, k, v, sel, out, lse, d_out, dq, dk, dv, b, st, ev);
+  return bwd_d<float>(s, q, k, v, sel, out, lse, d_out, dq, dk, dv, b, st, ev);
 }
 
 }  // namespace mdr

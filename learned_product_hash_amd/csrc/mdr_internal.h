@@ -189,10 +189,11 @@ hipError_t launch_attend(const Shape& s, const void* q, const void* k, const voi
 hipError_t launch_pair_bin_ordered(const Shape& s, const int32_t* sel, int32_t* cellcnt, int32_t* bins,
                                    hipStream_t st);
 // Backward of the attention under a fixed selection (cellcnt / bins must hold the selection's
-// pairs; part_o receives the remote dQ shares, dvec the row dots).
+// pairs; part_o receives the remote dQ shares, dvec the row dots).  ev (optional, 3 entries):
+// recorded before the row-dot, key-block and query-block kernels.
 hipError_t launch_attend_backward(const Shape& s, const void* q, const void* k, const void* v, const int32_t* sel,
                                   const void* out, const float* lse, const void* d_out, void* dq, void* dk, void* dv,
-                                  const Buffers& b, hipStream_t st);
+                                  const Buffers& b, hipStream_t st, hipEvent_t* ev = nullptr);
 hipError_t launch_project_heads(const Shape& s, const void* x, const void* w, void* out, bool rope,
                                 hipStream_t st);
 hipError_t launch_project_out(const Shape& s, const void* o, const void* wo, void* delta,

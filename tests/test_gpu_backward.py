@@ -173,3 +173,31 @@ def test_backward_full_size_heads(gpu_lib):
     out, lse, (grads,) = run_backward(mdr, w, inp, sel, d_out)
     worst = check(w, inp, sel, d_out, out, lse, grads, heads=[(0, 0), (0, 5)], packed=True)
     print(f"full size: worst relative errors {worst}")
+
+
+def test_backward_profiled_form_gives_the_same_gradients(gpu_lib):
+    """The event-recording entry point runs the same kernels: bit-identical results."""
+    mdr = gpu_lib
+    w = small("tiny")
+    inp = synth.make_core_inputs(w, 6)
+    sel = run_core(mdr, w, inp)["sel"]
+    _, _, (plain,) = run_backward(mdr, w, inp, sel, synth.make_grad_inputs(w, 6))
+    cfg = cfg_of(mdr, w)
+    q, k, v = (dev(inp[n], io_dtype(w)) for n in ("q", "k", "v"))
+    sd, g = dev(sel), dev(synth.make_grad_inputs(w, 6), io_dtype(w))
+    out = torch.empty_like(q)
+    lse = torch.empty(w.batch, w.heads, w.seq, dtype=torch.float32, device="cuda")
+    ws = mdr.workspace(cfg)
+    mdr.mdr_stage_attend_lse(cfg, q, k, v, sd, out, lse, ws)
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    from bench import HipEvents
+
+    hip = HipEvents()
+    handles = hip.create(mdr.MDR_BACKWARD_KERNELS + 1)
+    mdr.mdr_stage_attend_backward_profiled(cfg, q, k, v, sd, out, lse, g, dq, dk, dv, handles, ws)
+    torch.cuda.synchronize()
+    times = [hip.elapsed_ms(handles[i], handles[i + 1]) for i in range(mdr.MDR_BACKWARD_KERNELS)]
+    hip.destroy(handles)
+    assert all(t >= 0 for t in times)
+    for n, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        assert np.array_equal(host(t), plain[n]), n
