@@ -9,7 +9,8 @@
 //   k_bwd_dot  D_t for every token.
 //   k_bwd_kv   one work-group per key block i, one wave per 16 of its keys: the entries that read
 //              block i -- the tokens of the local query blocks i .. i + L - 1 (causal on block i)
-//              and the remote (token, slot) pairs of its cells -- are staged 32 (or 16) at a time; each
+//              and the remote (token, slot) pairs of its cells -- are taken 64 (or fewer) at a time
+//              through a pipeline (pair lookup, row reads, products on three chunks at once); each
 //              wave recomputes S = Q K^T and dP = dO V^T for its keys with the entries as rows,
 //              then accumulates dV^T += dO^T P and dK^T += Q^T dS on MFMA (the score layout is
 //              the PV operand layout, as in the forward); for remote entries the waves also
@@ -101,50 +102,74 @@ hipError_t pair_bin_ordered(const Shape& s, const int32_t* sel, int32_t* cellcnt
   return hipGetLastError();
 }
 
-// Entries staged per chunk: 32, or 16 where 32 would not fit the 160 KiB of LDS.
+// Sizes of the key-block kernel: the entries of a block (local tokens, then the pairs of its cells
+// in cell order) are taken EC at a time -- 64, or fewer where that would not fit the 160 KiB of
+// LDS; the cell counts are scanned SEGC = NTHR * CPT cells at a time.
 template <typename T, int D, int BLK>
-constexpr int bwd_ec() {
-  return ((2 * BLK + 64) * Tile<T, D, BLK>::KST * (int)sizeof(T) + (4 * BLK + 1) * 4 + 1024 <= 160 * 1024) ? 32 : 16;
-}
+struct KvCfg {
+  using TL = Tile<T, D, BLK>;
+  static constexpr int NTHR = BLK * 4;
+  static constexpr int NW = BLK / 16;  // one wave per 16 keys
+  static constexpr int CPT = 4;
+  static constexpr int SEGC = NTHR * CPT;
+  static constexpr size_t lds(int ec) {
+    return (size_t)(2 * BLK + 2 * ec) * TL::KST * sizeof(T) + (size_t)2 * ec * 16 + (size_t)SEGC * 4;
+  }
+  static constexpr size_t LIM = 160 * 1024 - 256;
+  static constexpr int EC = lds(64) <= LIM ? 64 : lds(32) <= LIM ? 32 : 16;
+  static constexpr int SUB = EC < 32 ? EC : 32;  // entries per dK / dV product
+  static constexpr size_t LDS = lds(EC);
+};
+
+// The entries flow through a three-stage pipeline, one chunk of EC per stage and iteration:
+//   A  resolve: entry -> token (local) or pair id (remote: a binary search over the cell prefix, then
+//      the pair's slot in its cell), in registers of threads tid < EC;
+//   B  gather: the chunk's query and output-gradient rows, normaliser and row dot, in registers;
+//   C  products on the rows staged in LDS.
+// While chunk k is in C, chunk k+1's reads (B) and chunk k+2's pair lookups (A) are in flight.
+// bf16 with D <= 64 and 64-key blocks: held to three waves per SIMD (no spills at that budget), so
+// that three work-groups per CU hide each other's read latency.
+constexpr int kv_min_waves(int bytes, int D, int BLK) { return bytes == 2 && D <= 64 && BLK == 64 ? 3 : 1; }
 
 template <typename T, int D, int BLK>
-constexpr size_t bwd_kv_lds() {
-  constexpr int EC = bwd_ec<T, D, BLK>();
-  return (size_t)(2 * Tile<T, D, BLK>::K_ELEMS + 2 * Tile<T, D, EC>::K_ELEMS) * sizeof(T) + (size_t)(4 * BLK + 1) * 4;
-}
-
-template <typename T, int D, int BLK>
-__global__ __launch_bounds__(BLK * 4) void k_bwd_kv(const T* __restrict__ Q, const T* __restrict__ K,
+__global__ __launch_bounds__(BLK * 4) __attribute__((amdgpu_waves_per_eu(kv_min_waves((int)sizeof(T), D, BLK)))) void k_bwd_kv(const T* __restrict__ Q, const T* __restrict__ K,
                                                     const T* __restrict__ V, const T* __restrict__ dO,
                                                     const float* __restrict__ lse, const float* __restrict__ Dv,
                                                     const int32_t* __restrict__ cellcnt,
                                                     const int32_t* __restrict__ bins, T* __restrict__ dq_part,
                                                     T* __restrict__ dK, T* __restrict__ dV, Shape s) {
+  using C = KvCfg<T, D, BLK>;
   using TL = Tile<T, D, BLK>;
-  constexpr int EC = bwd_ec<T, D, BLK>();
-  using TE = Tile<T, D, EC>;
-  static_assert(!TL::bf || EC % 32 == 0, "bf16 products take the entries 32 at a time");
-  constexpr int NTHR = BLK * 4;
-  constexpr int NW = BLK / 16;  // one wave per 16 keys
-  constexpr int NCH = D / TL::VEC;
+  constexpr int EC = C::EC, SUB = C::SUB, NTHR = C::NTHR, NW = C::NW, CPT = C::CPT, SEGC = C::SEGC;
+  static_assert(!TL::bf || SUB == 32, "bf16 products take the entries 32 at a time");
+  static_assert(EC <= NTHR, "one resolving thread per entry of a chunk");
+  constexpr int NCH = D / TL::VEC;                      // 16-byte pieces per row
+  constexpr int RPT = (EC * NCH + NTHR - 1) / NTHR;     // pieces per thread per chunk and array
   extern __shared__ __align__(16) char lds_raw[];
   T* Ks = (T*)lds_raw;
   T* Vs = Ks + TL::K_ELEMS;
-  T* Qs = Vs + TL::V_ELEMS;   // [EC][KST] the chunk's query rows
-  T* dOs = Qs + TE::K_ELEMS;  // [EC][KST] the chunk's output-gradient rows
-  int* pre = (int*)(dOs + TE::K_ELEMS);  // [NTHR + 1] exclusive prefix of the counts of a run of cells
-  __shared__ int etok[EC], epair[EC];
-  __shared__ float else2[EC], edd[EC];
+  T* Qs = Vs + TL::V_ELEMS;              // [EC][KST] the chunk's query rows
+  T* dOs = Qs + EC * TL::KST;            // [EC][KST] the chunk's output-gradient rows
+  int* mtok = (int*)(dOs + EC * TL::KST);  // [2][EC] token of each entry (-1: none), by chunk parity
+  int* mpair = mtok + 2 * EC;              // [2][EC] pair id t R + r (-1: local entry)
+  float* mlse = (float*)(mpair + 2 * EC);  // [2][EC] log2 normaliser of the token
+  float* mdd = mlse + 2 * EC;              // [2][EC] D = dO . O of the token
+  int* pre = (int*)(mdd + 2 * EC);         // [SEGC] exclusive prefix of the cell counts of a segment
   __shared__ int scan_tmp[NW];
-  const int i = blockIdx.x, bh = blockIdx.y;
+  // block-major order: early blocks, which later tokens select most, start first
+  const int bhn = s.B * s.H;
+  const int i = blockIdx.x / bhn, bh = blockIdx.x % bhn;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int s4 = lane >> 4, r16 = lane & 15;
   const size_t rowbase = (size_t)bh * s.S;
-  for (int x = tid; x < BLK * NCH; x += NTHR) {
-    const int row = x / NCH, ch = x % NCH;
-    const size_t g = (rowbase + (size_t)i * BLK + row) * D + ch * TL::VEC;
-    *(uint4*)(Ks + row * TL::KST + ch * TL::VEC) = *(const uint4*)(K + g);
-    *(uint4*)(Vs + row * TL::VST + ch * TL::VEC) = *(const uint4*)(V + g);
+  const int nl = (min(i + s.L, s.nb) - i) * BLK;
+  const int ncell = (s.R > 0 && i < s.ne) ? s.ne - i : 0;
+  const long long row0 = (long long)bh * s.cells_per_bh + (ncell > 0 ? cell_row(i, s.ne) : 0);
+  const int nseg = ncell > 0 ? (ncell + SEGC - 1) / SEGC : 1;
+  {
+    KVRegs<T, D, BLK, NTHR> kv;
+    kv.load(K + (rowbase + (size_t)i * BLK) * D, V + (rowbase + (size_t)i * BLK) * D, tid);
+    kv.store(Ks, Vs, tid);
   }
   __syncthreads();
   // this wave's 16 keys as the MFMA operand held in registers (K for S, V for dP)
@@ -156,110 +181,161 @@ __global__ __launch_bounds__(BLK * 4) void k_bwd_kv(const T* __restrict__ Q, con
   f32x4 dk[TL::ND], dv[TL::ND];
 #pragma unroll
   for (int dt = 0; dt < TL::ND; ++dt) dk[dt] = dv[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // entries: segment -1 = the tokens of the local query blocks i .. i + L - 1; segment g >= 0 = the
-  // pairs of the cells g NTHR .. g NTHR + NTHR - 1 of block i (query blocks i + L + cell)
-  const int nl = (min(i + s.L, s.nb) - i) * BLK;
-  const int ncell = (s.R > 0 && i < s.ne) ? s.ne - i : 0;
-  const long long row0 = (long long)bh * s.cells_per_bh + (ncell > 0 ? cell_row(i, s.ne) : 0);
-  const int nseg = (ncell + NTHR - 1) / NTHR;
-  for (int seg = -1; seg < nseg; ++seg) {
-    int n_ent = nl, nc = 0;
-    const long long cbase = row0 + (long long)seg * NTHR;
-    if (seg >= 0) {
-      nc = min(NTHR, ncell - seg * NTHR);
-      const int v = tid < nc ? min(cellcnt[cbase + tid], BLK) : 0;
-      int tot;
-      const int ex = block_exclusive_scan<NTHR>(v, scan_tmp, &tot);
-      pre[tid] = ex;
-      n_ent = tot;
-      __syncthreads();
+  for (int seg = 0; seg < nseg; ++seg) {
+    // ---- cell counts of the segment (thread tid: cells tid CPT .. tid CPT + CPT - 1) and their prefix
+    const int cb = seg * SEGC;
+    const int nc = min(SEGC, ncell - cb);  // <= 0 when the block has no cells
+    int cnt[CPT], run = 0;
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+      const int cc = tid * CPT + u;
+      cnt[u] = cc < nc ? min(cellcnt[row0 + cb + cc], BLK) : 0;
+      run += cnt[u];
     }
-    for (int e0 = 0; e0 < n_ent; e0 += EC) {
-      // ---- stage the chunk: token, pair id, lse, D, then the query and output-gradient rows
+    int tot;
+    int ex = block_exclusive_scan<NTHR>(run, scan_tmp, &tot);
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+      pre[tid * CPT + u] = ex;
+      ex += cnt[u];
+    }
+    const int nloc = seg == 0 ? nl : 0;
+    const int ntot = nloc + tot;
+    const int nch = (ntot + EC - 1) / EC;
+    __syncthreads();
+    // ---- pipeline registers
+    int aT = -1, aP = -1;  // stage A of thread tid < EC: local token, or pair id (aT = -2)
+    u32x4 qr[RPT], gr[RPT];
+    float bl = 0.f, bd = 0.f;
+    auto stage_a = [&](int k) __attribute__((always_inline)) {
+      aT = -1;
+      aP = -1;
+      const int e = k * EC + tid;
+      if (tid < EC && e < ntot) {
+        if (e < nloc) {
+          aT = i * BLK + e;
+        } else {
+          const int er = e - nloc;
+          int lo = 0, hi = nc - 1;  // the last cell whose range starts at or before er
+          while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (pre[mid] <= er)
+              lo = mid;
+            else
+              hi = mid - 1;
+          }
+          aP = bins[(row0 + cb + lo) * BLK + (er - pre[lo])];
+          aT = -2;
+        }
+      }
+    };
+    auto commit_a = [&](int slot) __attribute__((always_inline)) {
       if (tid < EC) {
-        const int e = e0 + tid;
-        int t = -1, pid = -1;
-        if (e < n_ent) {
-          if (seg < 0) {
-            t = i * BLK + e;
-          } else {
-            int lo = 0, hi = nc - 1;  // the last cell whose range starts at or before e
-            while (lo < hi) {
-              const int mid = (lo + hi + 1) >> 1;
-              if (pre[mid] <= e)
-                lo = mid;
-              else
-                hi = mid - 1;
-            }
-            pid = bins[(cbase + lo) * BLK + (e - pre[lo])];
-            t = pid / s.R;
-          }
-        }
-        etok[tid] = t;
-        epair[tid] = pid;
-        else2[tid] = t >= 0 ? lse[rowbase + t] : 0.f;
-        edd[tid] = t >= 0 ? Dv[rowbase + t] : 0.f;
+        mtok[slot * EC + tid] = aT == -2 ? aP / s.R : aT;
+        mpair[slot * EC + tid] = aP;
       }
-      __syncthreads();
-      for (int x = tid; x < EC * NCH; x += NTHR) {
-        const int row = x / NCH, ch = x % NCH;
-        const int t = etok[row];
-        uint4 qv = make_uint4(0, 0, 0, 0), gv = make_uint4(0, 0, 0, 0);
-        if (t >= 0) {
-          qv = *(const uint4*)(Q + (rowbase + t) * D + ch * TL::VEC);
-          gv = *(const uint4*)(dO + (rowbase + t) * D + ch * TL::VEC);
+    };
+    auto stage_b = [&](int slot) __attribute__((always_inline)) {
+      const int* tk = mtok + slot * EC;
+#pragma unroll
+      for (int u = 0; u < RPT; ++u) {
+        const int x = u * NTHR + tid;
+        if ((EC * NCH) % NTHR == 0 || x < EC * NCH) {
+          const int t = tk[x / NCH];
+          const size_t g = (rowbase + (t >= 0 ? t : 0)) * D + (x % NCH) * TL::VEC;
+          const u32x4 z = {0u, 0u, 0u, 0u};
+          qr[u] = t >= 0 ? *(const u32x4*)(Q + g) : z;
+          gr[u] = t >= 0 ? *(const u32x4*)(dO + g) : z;
         }
-        *(uint4*)(Qs + row * TL::KST + ch * TL::VEC) = qv;
-        *(uint4*)(dOs + row * TL::KST + ch * TL::VEC) = gv;
       }
+      if (tid < EC) {
+        const int t = tk[tid];
+        bl = t >= 0 ? lse[rowbase + (t >= 0 ? t : 0)] : 0.f;
+        bd = t >= 0 ? Dv[rowbase + (t >= 0 ? t : 0)] : 0.f;
+      }
+    };
+    auto commit_b = [&](int slot) __attribute__((always_inline)) {
+#pragma unroll
+      for (int u = 0; u < RPT; ++u) {
+        const int x = u * NTHR + tid;
+        if ((EC * NCH) % NTHR == 0 || x < EC * NCH) {
+          const int row = x / NCH, ch = x % NCH;
+          *(u32x4*)(Qs + row * TL::KST + ch * TL::VEC) = qr[u];
+          *(u32x4*)(dOs + row * TL::KST + ch * TL::VEC) = gr[u];
+        }
+      }
+      if (tid < EC) {
+        mlse[slot * EC + tid] = bl;
+        mdd[slot * EC + tid] = bd;
+      }
+    };
+    if (nch > 0) {
+      stage_a(0);
+      commit_a(0);
       __syncthreads();
+      stage_b(0);
+      if (nch > 1) stage_a(1);
+    }
+    for (int k = 0; k < nch; ++k) {
+      const int cur = k & 1, nxt = cur ^ 1;
+      commit_b(cur);
+      if (k + 1 < nch) commit_a(nxt);
+      __syncthreads();
+      if (k + 1 < nch) stage_b(nxt);
+      if (k + 2 < nch) stage_a(k + 2);
+      const int* tk = mtok + cur * EC;
+      const int* pk = mpair + cur * EC;
+      const float* lk = mlse + cur * EC;
+      const float* dk_ = mdd + cur * EC;
       // ---- dV, dK of this wave's keys, entries as rows: lane (key r16) holds entries 16rt + 4s4 + k
-      {
-        f32x4 p[EC / 16], ds[EC / 16];
 #pragma unroll
-        for (int rt = 0; rt < EC / 16; ++rt) {
-          const f32x4 sc = score_tile<T, D, EC>(kf, Qs, rt, lane);
-          const f32x4 dp = score_tile<T, D, EC>(vf, dOs, rt, lane);
+      for (int h = 0; h < EC / SUB; ++h) {
+        const T* qh = Qs + h * SUB * TL::KST;
+        const T* gh = dOs + h * SUB * TL::KST;
+        f32x4 p[SUB / 16], ds[SUB / 16];
 #pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            const int e = 16 * rt + 4 * s4 + k;
-            const float pv = etok[e] >= key_tok ? fast_exp2(fmaf(sc[k], c, -else2[e])) : 0.f;
-            p[rt][k] = pv;
-            ds[rt][k] = pv * (dp[k] - edd[e]);
+        for (int rt = 0; rt < SUB / 16; ++rt) {
+          const f32x4 sc = score_tile<T, D, SUB>(kf, qh, rt, lane);
+          const f32x4 dp = score_tile<T, D, SUB>(vf, gh, rt, lane);
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk) {
+            const int e = h * SUB + 16 * rt + 4 * s4 + kk;
+            const float pv = tk[e] >= key_tok ? fast_exp2(fmaf(sc[kk], c, -lk[e])) : 0.f;
+            p[rt][kk] = pv;
+            ds[rt][kk] = pv * (dp[kk] - dk_[e]);
           }
         }
-        pv_block<T, D, EC>(dv, p, dOs, lane);
-        pv_block<T, D, EC>(dk, ds, Qs, lane);
+        pv_block<T, D, SUB>(dv, p, gh, lane);
+        pv_block<T, D, SUB>(dk, ds, qh, lane);
       }
       // ---- the remote entries' dQ shares, keys as rows: lane (entry 16g + r16) holds keys 16n + 4s4 + k
-      if (seg >= 0) {
-        for (int g = wave; g < EC / 16; g += NW) {
-          const int e = 16 * g + r16;
-          const int pid = epair[e];
-          QFrag<T, D> qf, gf;
-          load_q<T, D>(qf, Qs + e * TL::KST, lane);
-          load_q<T, D>(gf, dOs + e * TL::KST, lane);
-          const float le = else2[e], de = edd[e];
-          f32x4 dst[TL::NT];
+      for (int g = wave; g < EC / 16; g += NW) {
+        const int el = 16 * g + r16;
+        const int pid = pk[el];
+        if (__builtin_amdgcn_readfirstlane(__ballot(pid >= 0) != 0ull ? 1 : 0) == 0) continue;  // all local
+        QFrag<T, D> qf, gf;
+        load_q<T, D>(qf, Qs + el * TL::KST, lane);
+        load_q<T, D>(gf, dOs + el * TL::KST, lane);
+        const float le = lk[el], de = dk_[el];
+        f32x4 dst[TL::NT];
 #pragma unroll
-          for (int n = 0; n < TL::NT; ++n) {
-            const f32x4 sc = score_tile<T, D, BLK>(qf, Ks, n, lane);
-            const f32x4 dp = score_tile<T, D, BLK>(gf, Vs, n, lane);
+        for (int n = 0; n < TL::NT; ++n) {
+          const f32x4 sc = score_tile<T, D, BLK>(qf, Ks, n, lane);
+          const f32x4 dp = score_tile<T, D, BLK>(gf, Vs, n, lane);
 #pragma unroll
-            for (int k = 0; k < 4; ++k) dst[n][k] = fast_exp2(fmaf(sc[k], c, -le)) * (dp[k] - de);
-          }
-          f32x4 dq[TL::ND];
+          for (int kk = 0; kk < 4; ++kk) dst[n][kk] = fast_exp2(fmaf(sc[kk], c, -le)) * (dp[kk] - de);
+        }
+        f32x4 dq[TL::ND];
 #pragma unroll
-          for (int dt = 0; dt < TL::ND; ++dt) dq[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-          pv_block<T, D, BLK>(dq, dst, Ks, lane);
-          if (pid >= 0) {
-            const size_t pr = rowbase * s.R + pid;  // the pair (token, slot)
+        for (int dt = 0; dt < TL::ND; ++dt) dq[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        pv_block<T, D, BLK>(dq, dst, Ks, lane);
+        if (pid >= 0) {
+          const size_t pr = rowbase * s.R + pid;  // the pair (token, slot)
 #pragma unroll
-            for (int dt = 0; dt < TL::ND; ++dt) store4<T>(dq_part + pr * D + 16 * dt + 4 * s4, dq[dt], s.scale);
-          }
+          for (int dt = 0; dt < TL::ND; ++dt) store4<T>(dq_part + pr * D + 16 * dt + 4 * s4, dq[dt], s.scale);
         }
       }
-      __syncthreads();  // the chunk's staging is overwritten next
+      __syncthreads();  // chunk k's rows and metadata are overwritten next
     }
   }
   // ---- dV^T, dK^T: lane (key r16) holds d = 16dt + 4s4 + k
@@ -271,6 +347,9 @@ __global__ __launch_bounds__(BLK * 4) void k_bwd_kv(const T* __restrict__ Q, con
   }
 }
 
+// One work-group per query block, one wave per 16 of its tokens: dQ over the L local blocks
+// (recomputing P and dS; the next block's K / V read is in flight while the current one is used),
+// scaled, plus the remote blocks' shares in slot order.
 template <typename T, int D, int BLK>
 __global__ __launch_bounds__(BLK * 4) void k_bwd_q(const T* __restrict__ Q, const T* __restrict__ K,
                                                    const T* __restrict__ V, const T* __restrict__ dO,
@@ -282,12 +361,16 @@ __global__ __launch_bounds__(BLK * 4) void k_bwd_q(const T* __restrict__ Q, cons
   extern __shared__ __align__(16) char lds_raw[];
   T* Ks = (T*)lds_raw;
   T* Vs = Ks + TL::K_ELEMS;
-  const int j = blockIdx.x, bh = blockIdx.y;
+  const int wg = xcd_chunked(blockIdx.x, gridDim.x);  // query blocks of one head in order per XCD
+  const int j = wg % s.nb, bh = wg / s.nb;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int qi = wave * 16 + (lane & 15);
   const int t = j * BLK + qi;
   const int c4 = 4 * (lane >> 4);
   const size_t rowbase = (size_t)bh * s.S;
+  const int j0 = max(0, j - s.L + 1);
+  KVRegs<T, D, BLK, NTHR> kv;
+  kv.load(K + (rowbase + (size_t)j0 * BLK) * D, V + (rowbase + (size_t)j0 * BLK) * D, tid);
   QFrag<T, D> qf, gf;
   load_q<T, D>(qf, Q + (rowbase + t) * D, lane);
   load_q<T, D>(gf, dO + (rowbase + t) * D, lane);
@@ -296,15 +379,14 @@ __global__ __launch_bounds__(BLK * 4) void k_bwd_q(const T* __restrict__ Q, cons
   f32x4 dq[TL::ND];
 #pragma unroll
   for (int dt = 0; dt < TL::ND; ++dt) dq[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int j0 = max(0, j - s.L + 1);
   for (int jj = j0; jj <= j; ++jj) {
-    if (jj != j0) __syncthreads();
-    for (int x = tid; x < BLK * (D / TL::VEC); x += NTHR) {
-      const int row = x / (D / TL::VEC), ch = x % (D / TL::VEC);
-      *(uint4*)(Ks + row * TL::KST + ch * TL::VEC) = *(const uint4*)(K + (rowbase + (size_t)jj * BLK + row) * D + ch * TL::VEC);
-      *(uint4*)(Vs + row * TL::VST + ch * TL::VEC) = *(const uint4*)(V + (rowbase + (size_t)jj * BLK + row) * D + ch * TL::VEC);
-    }
+    if (jj != j0) __syncthreads();  // the previous block is no longer read
+    kv.store(Ks, Vs, tid);
     __syncthreads();
+    if (jj < j) {
+      const size_t nx = (rowbase + (size_t)(jj + 1) * BLK) * D;
+      kv.load(K + nx, V + nx, tid);
+    }
     f32x4 ds[TL::NT];
 #pragma unroll
     for (int n = 0; n < TL::NT; ++n) {
@@ -348,12 +430,13 @@ hipError_t bwd_impl(const Shape& s, const void* q, const void* k, const void* v,
   hipLaunchKernelGGL((k_bwd_dot<T, D>), dim3((unsigned)blocks), dim3(256), 0, st, (const T*)o, (const T*)d_o,
                      b.dvec, n);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  constexpr size_t kl = bwd_kv_lds<T, D, BLK>();
+  constexpr size_t kl = KvCfg<T, D, BLK>::LDS;
   if (kl > 65536 && (e = hipFuncSetAttribute((const void*)k_bwd_kv<T, D, BLK>,
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)kl)) != hipSuccess)
     return e;
   if (ev && (e = hipEventRecord(ev[1], st)) != hipSuccess) return e;
-  hipLaunchKernelGGL((k_bwd_kv<T, D, BLK>), dim3(s.nb, s.B * s.H), dim3(BLK * 4), kl, st, (const T*)q,
+  const unsigned nwg = (unsigned)((long long)s.nb * s.B * s.H);
+  hipLaunchKernelGGL((k_bwd_kv<T, D, BLK>), dim3(nwg), dim3(BLK * 4), kl, st, (const T*)q,
                      (const T*)k, (const T*)v, (const T*)d_o, lse, b.dvec, b.cellcnt, b.bins, (T*)b.part_o,
                      (T*)dk, (T*)dv, s);
   if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -362,7 +445,7 @@ hipError_t bwd_impl(const Shape& s, const void* q, const void* k, const void* v,
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)ql)) != hipSuccess)
     return e;
   if (ev && (e = hipEventRecord(ev[2], st)) != hipSuccess) return e;
-  hipLaunchKernelGGL((k_bwd_q<T, D, BLK>), dim3(s.nb, s.B * s.H), dim3(BLK * 4), ql, st, (const T*)q, (const T*)k,
+  hipLaunchKernelGGL((k_bwd_q<T, D, BLK>), dim3(nwg), dim3(BLK * 4), ql, st, (const T*)q, (const T*)k,
                      (const T*)v, (const T*)d_o, lse, b.dvec, sel, (const T*)b.part_o, (T*)dq, s);
   return hipGetLastError();
 }
