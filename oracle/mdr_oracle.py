@@ -151,6 +151,111 @@ def posting_view(lists: list, a: int, j: int, local: int, capacity: int) -> list
     return elig[::-1][:capacity]
 
 
+# ---------------------------------------------------------------- 3b. overflow redirect
+#
+# The pages name two ways to handle a full posting list -- drop the block or redirect it -- and warn
+# that either may hide relevant blocks (remio.ai, section "Monodratic turns sparse attention into a
+# retrieval decision"); they ask overflow stress tests to report dropped candidates and fallback
+# behaviour (same article, "What sparse attention researchers should watch next").  They fix no
+# redirect rule.  The reading taken here keeps the drop policy's views unchanged and only reuses
+# spare capacity:
+#   * a block's alternate address is its own address with one digit changed: in the subspace whose
+#     top two code logits are closest (smallest top1 - top2, ties to the smaller subspace), the
+#     runner-up code (second by logit desc, code asc) replaces the top code.  No alternate when C = 1.
+#   * a filed block leaves its primary view when the capacity-th newer block of the same address
+#     becomes eligible, at query block (that block) + L; at that moment it is filed, in time order,
+#     into its alternate address's redirect list.
+#   * the view of address a at query block j is the drop-policy view (newest `capacity` eligible
+#     primaries, newest first) followed, while slots remain, by the newest redirected blocks whose
+#     redirect time is <= j, newest first.
+
+def runner_up_codes(ksum: np.ndarray, codebook: np.ndarray, bias, rdtype=np.float32):
+    """Per block and subspace: the runner-up code (second by logit desc, code asc) [nb, G] (-1 when
+    C == 1) and the margin top1 - top2 evaluated in ``rdtype`` [nb, G] (inf when C == 1)."""
+    G, C, _ = codebook.shape
+    lg = code_logits(ksum, codebook, bias, rdtype)
+    nb = lg.shape[0]
+    second = np.full((nb, G), -1, dtype=np.int64)
+    margin = np.full((nb, G), INF)
+    if C == 1:
+        return second, margin
+    for i in range(nb):
+        for g in range(G):
+            order = sorted(range(C), key=lambda c: (-float(lg[i, g, c]), c))
+            second[i, g] = order[1]
+            margin[i, g] = float(rdtype(lg[i, g, order[0]]) - rdtype(lg[i, g, order[1]]))
+    return second, margin
+
+
+def alternate_addresses(codes: np.ndarray, second: np.ndarray, margin: np.ndarray, n_codes: int):
+    """Alternate address of each block [nb] (-1 when C == 1) and the gap between the smallest and the
+    next smallest subspace margin (the decision's own margin; inf with one subspace)."""
+    nb, G = codes.shape
+    alt = np.full(nb, -1, dtype=np.int64)
+    gap = np.full(nb, INF)
+    if n_codes == 1:
+        return alt, gap
+    for i in range(nb):
+        g_star = min(range(G), key=lambda g: (margin[i, g], g))
+        digits = list(codes[i])
+        digits[g_star] = int(second[i, g_star])
+        a = 0
+        for d in digits:
+            a = a * n_codes + d
+        alt[i] = a
+        if G > 1:
+            rest = sorted(margin[i, g] for g in range(G) if g != g_star)
+            gap[i] = rest[0] - margin[i, g_star]
+    return alt, gap
+
+
+def redirect_lists(lists: list, alt: np.ndarray, capacity: int, local: int) -> list:
+    """Per address, the blocks redirected into it as (time, block) in time order.  The block at
+    position k of list a leaves the primary view when the block at position k + capacity becomes
+    eligible, i.e. at query block lists[a][k + capacity] + L."""
+    rd = [[] for _ in range(len(lists))]
+    for lst in lists:
+        for k in range(len(lst) - capacity):
+            x = lst[k]
+            if alt[x] >= 0:
+                rd[int(alt[x])].append((lst[k + capacity] + local, x))
+    for r in rd:
+        r.sort()
+    return rd
+
+
+def posting_view_redirect(lists: list, rd: list, a: int, j: int, local: int, capacity: int) -> list:
+    """The drop-policy view of address a at query block j, then the newest redirected blocks with
+    time <= j (newest first) while slots remain."""
+    view = posting_view(lists, a, j, local, capacity)
+    room = capacity - len(view)
+    if room > 0:
+        arrived = [x for (tm, x) in rd[a] if tm <= j]
+        view = view + arrived[::-1][:room]
+    return view
+
+
+def redirect_overflow(lists: list, rd: list, capacity: int) -> int:
+    """Blocks no final view returns: the drop-policy overflow minus the redirected blocks that fill
+    spare slots at the last query block (every redirect happens by then)."""
+    shown = sum(min(max(0, capacity - len(lists[a])), len(rd[a])) for a in range(len(lists)))
+    return posting_overflow(lists, capacity) - shown
+
+
+def view_dropped(lists: list, rd, alt, a: int, j: int, local: int, capacity: int) -> int:
+    """Eligible blocks held by address a at query block j that its view does not return:
+    max(0, held - capacity).  Under drop, a holds its eligible primaries; under redirect, those
+    not yet redirected away (a block left behind without an alternate stays held and dropped),
+    plus the redirected blocks that have arrived."""
+    cutoff = j - local
+    elig = [i for i in lists[a] if i <= cutoff]
+    held = len(elig)
+    if rd is not None:
+        away = sum(1 for i in elig[:max(0, len(elig) - capacity)] if alt[i] >= 0)
+        held += sum(1 for (tm, _) in rd[a] if tm <= j) - away
+    return max(0, held - capacity)
+
+
 # ---------------------------------------------------------------- 4. probe, candidates, rerank
 
 def address_scores(mu: np.ndarray, n_codes: int) -> np.ndarray:
@@ -219,13 +324,14 @@ def apply_force(sel: list, f: int, j: int, local: int, remote: int):
 
 
 def route_head(q: np.ndarray, k: np.ndarray, codebook: np.ndarray, bias, w, force=None,
-               tokens=None, rdtype=np.float32) -> dict:
+               tokens=None, rdtype=np.float32, policy: str = "drop") -> dict:
     """Routing for one (batch, head).  q, k [S, D] post-RoPE; codebook [G, C, D]; bias [G, C] or None.
 
     ``w`` carries the sizes (block, codes, capacity, probes, cand_limit, remote,
     local).  ``tokens`` restricts the per-token steps to a subset (all by default).
     Returns the summaries, codes, addresses, posting lists, overflow, and per
-    token the probes, candidates, selection and decision margins.
+    token the probes, candidates, selection, capacity-dropped candidates and
+    decision margins.  ``policy`` is "drop" or "redirect" (section 3b).
     """
     S, D = q.shape
     blk, L, R, P = w.block, w.local, w.remote, w.probes
@@ -236,7 +342,16 @@ def route_head(q: np.ndarray, k: np.ndarray, codebook: np.ndarray, bias, w, forc
     codes, addr, addr_margin = block_addresses(ksum, codebook, bias, rdtype)
     lists = posting_lists(addr, A, L)
     off, idx = posting_csr(lists)
-    overflow = posting_overflow(lists, w.capacity)
+    alt = alt_gap = rd = None
+    if policy == "redirect":
+        second, margin32 = runner_up_codes(ksum, codebook, bias, rdtype)
+        alt, alt_gap = alternate_addresses(codes, second, margin32, C)
+        rd = redirect_lists(lists, alt, w.capacity, L)
+        overflow = redirect_overflow(lists, rd, w.capacity)
+    elif policy == "drop":
+        overflow = posting_overflow(lists, w.capacity)
+    else:
+        raise ValueError(f"unknown overflow policy {policy!r}")
 
     toks = np.arange(S) if tokens is None else np.asarray(tokens, dtype=np.int64)
     mu = code_logits(q[toks], codebook, bias, rdtype)             # [n, G, C]
@@ -246,13 +361,19 @@ def route_head(q: np.ndarray, k: np.ndarray, codebook: np.ndarray, bias, w, forc
     sel = np.full((n, R), -1, dtype=np.int64)
     sel_margin = np.full(n, INF)
     n_cand = np.zeros(n, dtype=np.int64)
+    n_drop = np.zeros(n, dtype=np.int64)
     cands_all = []
     force_ignored = 0
     for row, t in enumerate(toks):
         j = int(t) // blk
         cands = []
         for a in probes[row]:
-            cands += posting_view(lists, int(a), j, L, w.capacity)
+            if rd is None:
+                cands += posting_view(lists, int(a), j, L, w.capacity)
+            else:
+                cands += posting_view_redirect(lists, rd, int(a), j, L, w.capacity)
+            if j - L >= 0:
+                n_drop[row] += view_dropped(lists, rd, alt, int(a), j, L, w.capacity)
         cands = cands[:M]
         chosen, margin = rerank(q[t], ksum, cands, R, rdtype)
         if force is not None:
@@ -264,8 +385,8 @@ def route_head(q: np.ndarray, k: np.ndarray, codebook: np.ndarray, bias, w, forc
         cands_all.append(cands)
     return dict(ksum=ksum, codes=codes, addr=addr, addr_margin=addr_margin, lists=lists, off=off,
                 idx=idx, overflow=overflow, tokens=toks, probes=probes, probe_margin=probe_margin,
-                cands=cands_all, n_cand=n_cand, sel=sel, sel_margin=sel_margin,
-                force_ignored=force_ignored)
+                cands=cands_all, n_cand=n_cand, n_drop=n_drop, sel=sel, sel_margin=sel_margin,
+                force_ignored=force_ignored, alt=alt, alt_gap=alt_gap, rd=rd)
 
 
 # ---------------------------------------------------------------- 5. attention

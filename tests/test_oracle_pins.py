@@ -404,3 +404,140 @@ def test_attention_backward_packed_matches_dense(seed):
         packed = oracle.attention_backward_packed(q, k, v, rows, w.block, w.local, d_out)
         for a, b in zip(packed, dense):
             np.testing.assert_allclose(a, b, rtol=1e-10, atol=1e-12)
+
+
+# ---------------------------------------------------------------- overflow redirect
+
+def _simulate_rings(addr, alt, A, capacity, local):
+    """Step-by-step filing with a primary ring and a redirect ring per address (the streaming
+    formulation): at query block j the block j - L is filed; a full primary ring evicts its oldest
+    block into the redirect ring of that block's alternate address (or drops it).  Returns the
+    views {(a, j): list} under both policies and each block's eviction time."""
+    nb = len(addr)
+    prim = [[] for _ in range(A)]
+    redir = [[] for _ in range(A)]
+    evicted_at = {}
+    views_drop, views_redirect = {}, {}
+    for j in range(nb):
+        b = j - local
+        if b >= 0:
+            ring = prim[int(addr[b])]
+            ring.append(b)
+            if len(ring) > capacity:
+                x = ring.pop(0)
+                evicted_at[x] = j
+                if alt[x] >= 0:
+                    redir[int(alt[x])].append(x)
+        for a in range(A):
+            pv = prim[a][::-1]
+            views_drop[(a, j)] = pv
+            views_redirect[(a, j)] = pv + redir[a][::-1][:capacity - len(pv)]
+    return views_drop, views_redirect, evicted_at
+
+
+@pytest.mark.parametrize("seed,capacity,local", [(0, 1, 1), (1, 2, 2), (2, 3, 1), (3, 1, 3)])
+def test_redirect_views_match_the_ring_simulation(seed, capacity, local):
+    rng = np.random.default_rng(seed)
+    A, nb = 6, 40
+    addr = rng.integers(0, A, size=nb) if seed % 2 else np.minimum(rng.geometric(0.45, size=nb) - 1, A - 1)
+    alt = (addr + rng.integers(1, A, size=nb)) % A  # any address but the block's own
+    alt[rng.random(nb) < 0.15] = -1                  # some blocks without an alternate
+    lists = oracle.posting_lists(addr, A, local)
+    rd = oracle.redirect_lists(lists, alt, capacity, local)
+    vd, vr, ev = _simulate_rings(addr, alt, A, capacity, local)
+    for a in range(A):
+        for j in range(nb):
+            assert oracle.posting_view(lists, a, j, local, capacity) == vd[(a, j)], (a, j)
+            assert oracle.posting_view_redirect(lists, rd, a, j, local, capacity) == vr[(a, j)], (a, j)
+            # held blocks, from the simulation's eviction times
+            held = 0
+            for x in range(max(0, j - local + 1)):
+                gone = x in ev and ev[x] <= j
+                if addr[x] == a and not (gone and alt[x] >= 0):
+                    held += 1
+                if gone and alt[x] == a:
+                    held += 1
+            assert oracle.view_dropped(lists, rd, alt, a, j, local, capacity) == max(0, held - capacity)
+            assert oracle.view_dropped(lists, None, alt, a, j, local, capacity) == \
+                max(0, sum(1 for x in range(max(0, j - local + 1)) if addr[x] == a) - capacity)
+    final = set()
+    for a in range(A):
+        final |= set(vr[(a, nb - 1)])
+    assert oracle.redirect_overflow(lists, rd, capacity) == (nb - local) - len(final)
+    assert oracle.posting_overflow(lists, capacity) == (nb - local) - len({x for a in range(A) for x in vd[(a, nb - 1)]})
+
+
+def test_redirect_equals_drop_without_overflow():
+    rng = np.random.default_rng(9)
+    A, nb, cap, L = 8, 30, 8, 2
+    addr = rng.integers(0, A, size=nb)
+    addr[:] = np.arange(nb) % A  # at most 4 per address: nothing overflows
+    alt = (addr + 1) % A
+    lists = oracle.posting_lists(addr, A, L)
+    rd = oracle.redirect_lists(lists, alt, cap, L)
+    assert all(len(r) == 0 for r in rd)
+    for a in range(A):
+        for j in range(nb):
+            assert oracle.posting_view_redirect(lists, rd, a, j, L, cap) == oracle.posting_view(lists, a, j, L, cap)
+    assert oracle.redirect_overflow(lists, rd, cap) == 0
+
+
+def test_alternate_address_worked_example():
+    """Hand-computed logits (one-hot summary picks the codebook's first coordinate)."""
+    D = 4
+    cb = np.zeros((2, 3, D), dtype=np.float32)
+    cb[0, :, 0] = [3.0, 2.5, 1.0]  # subspace 0: top 0, runner-up 1, margin 0.5
+    cb[1, :, 0] = [0.25, 1.0, 0.875]  # subspace 1: top 1, runner-up 2, margin 0.125
+    ks = np.zeros((3, D), dtype=np.float32)
+    ks[0, 0] = 1.0
+    ks[1, 0] = 2.0            # margins scale: 1.0 and 0.25 -> still subspace 1
+    ks[2, 0] = -1.0           # logits negate: subspace 0 top 2 (-1.0), runner-up 1 (-2.5), margin 1.5;
+    #                           subspace 1 top 0 (-0.25), runner-up 2 (-0.875), margin 0.625
+    codes, addr, _ = oracle.block_addresses(ks, cb, None)
+    second, margin = oracle.runner_up_codes(ks, cb, None)
+    alt, gap = oracle.alternate_addresses(codes, second, margin, 3)
+    assert codes.tolist() == [[0, 1], [0, 1], [2, 0]]
+    assert second.tolist() == [[1, 2], [1, 2], [1, 2]]
+    np.testing.assert_allclose(margin, [[0.5, 0.125], [1.0, 0.25], [1.5, 0.625]])
+    assert addr.tolist() == [1, 1, 6]
+    assert alt.tolist() == [0 * 3 + 2, 0 * 3 + 2, 2 * 3 + 2]  # the low-margin subspace 1 changes
+    np.testing.assert_allclose(gap, [0.375, 0.75, 0.875])
+
+
+def test_alternate_address_ties():
+    """Equal top logits: margin 0, runner-up the larger tied code; equal margins: the smaller subspace."""
+    D = 2
+    cb = np.zeros((2, 3, D), dtype=np.float32)
+    cb[0, :, 0] = [1.0, 2.0, 2.0]   # top 1 (smaller of the tie), runner-up 2, margin 0
+    cb[1, :, 0] = [5.0, 5.0, 1.0]   # top 0, runner-up 1, margin 0
+    ks = np.array([[1.0, 0.0]], dtype=np.float32)
+    codes, addr, _ = oracle.block_addresses(ks, cb, None)
+    second, margin = oracle.runner_up_codes(ks, cb, None)
+    alt, _ = oracle.alternate_addresses(codes, second, margin, 3)
+    assert codes.tolist() == [[1, 0]] and second.tolist() == [[2, 1]]
+    assert alt.tolist() == [2 * 3 + 0]  # both margins 0: subspace 0 changes
+    one = np.zeros((1, 1, D), dtype=np.float32)
+    s1, m1 = oracle.runner_up_codes(ks, one, None)
+    a1, _ = oracle.alternate_addresses(np.zeros((1, 1), dtype=np.int64), s1, m1, 1)
+    assert a1.tolist() == [-1]
+
+
+def test_route_head_redirect_recovers_overflowed_blocks():
+    """Under skew with a small capacity, redirect drops fewer blocks than drop and returns at least
+    as many candidates overall; every view stays within capacity and holds eligible blocks only."""
+    w = synth.workload("skew", batch=1, heads=1, seq=4096, capacity=1)
+    inp = synth.make_core_inputs(w, 0)
+    args = (inp["q"][0, 0], inp["k"][0, 0], inp["codebook"][0], inp["bias"][0], w)
+    rdrop = oracle.route_head(*args, policy="drop")
+    rred = oracle.route_head(*args, policy="redirect")
+    assert rdrop["overflow"] > 0
+    assert rred["overflow"] < rdrop["overflow"]
+    assert rred["n_cand"].sum() >= rdrop["n_cand"].sum()
+    for row, t in enumerate(rred["tokens"]):
+        j = int(t) // w.block
+        c = rred["cands"][row]
+        assert all(0 <= i <= j - w.local for i in c)
+    for a in range(w.addresses):
+        for j in range(0, w.nblocks, 5):
+            v = oracle.posting_view_redirect(rred["lists"], rred["rd"], a, j, w.local, w.capacity)
+            assert len(v) <= w.capacity and len(set(v)) == len(v)
