@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define MDR_ABI_VERSION 1
+#define MDR_ABI_VERSION 2
 
 typedef enum {
   MDR_OK = 0,
@@ -72,6 +72,24 @@ typedef enum {
 } mdr_status;
 
 typedef enum { MDR_F32 = 0, MDR_BF16 = 1 } mdr_dtype;
+
+/* What a full posting list does with its overflow.  The pages name both
+ * options, dropping or redirecting blocks, and warn that either may hide
+ * relevant blocks (remio.ai, "Monodratic turns sparse attention into a
+ * retrieval decision"); they fix no redirect rule.
+ *   DROP      query block j reads from address a the newest `capacity`
+ *             eligible blocks (i <= j - L) filed under a, newest first.
+ *   REDIRECT  the same view, then, while slots remain, the newest blocks
+ *             redirected into a.  A block is redirected when it leaves its
+ *             own view: when the capacity-th newer block of its address
+ *             becomes eligible, i.e. at query block (that block) + L.  It
+ *             goes to its alternate address: its own address with, in the
+ *             subspace whose two best code logits are closest (fp32 top1 -
+ *             top2; ties to the smaller subspace), the runner-up code (ties to
+ *             the smaller code) in place of the best one.  Redirected blocks
+ *             are read newest arrival first.  Prefill entry points only (the
+ *             decode state rejects it with MDR_ERR_UNSUPPORTED). */
+typedef enum { MDR_OVERFLOW_DROP = 0, MDR_OVERFLOW_REDIRECT = 1 } mdr_overflow_policy;
 
 /* Sizes of one call.  nb = seq / block blocks per sequence.
  * Supported on gfx950: head_dim in {32, 64, 128}; block in {32, 64, 128};
@@ -96,14 +114,27 @@ typedef struct {
   int32_t dtype;       /* mdr_dtype */
   float rope_base;     /* mixer only: RoPE base (pairs (i, i + D/2), theta_i = base^(-2i/D)) */
   float softmax_scale; /* 0 => 1/sqrt(head_dim) */
+  int32_t overflow_policy; /* mdr_overflow_policy (0 = drop) */
 } mdr_config;
 
 /* Optional device outputs of the routing stages.  Any NULL member is kept in
- * the workspace instead.  Layouts:
+ * the workspace instead (n_drop: not computed).  Layouts:
  *   ksum [B,H,nb,D] fp32   addr [B,H,nb]        post_off [B,H,A+1]
  *   post_idx [B,H,nb] (CSR entries: the blocks of address a in ascending order
  *   at post_idx[post_off[a] .. post_off[a+1]); entries past post_off[A] are -1)
- *   overflow [B,H]          sel [B,H,S,R] (-1 padded)   n_cand [B,H,S] */
+ *   overflow [B,H]: blocks no view of the last query block returns
+ *   sel [B,H,S,R] (-1 padded)   n_cand [B,H,S]: candidates after the M cut
+ *   n_drop [B,H,S]: per token, summed over its probes, the eligible blocks a
+ *     probed address holds beyond its capacity (under REDIRECT an address
+ *     holds its primaries not redirected away plus the arrivals so far); the
+ *     pages ask overflow stress tests to report such dropped candidates
+ *     (remio.ai, "What sparse attention researchers should watch next")
+ * REDIRECT policy only (written when non-NULL, ignored under DROP):
+ *   alt [B,H,nb]: alternate address of each block
+ *   redir_off [B,H,A+1], redir_idx [B,H,nb], redir_time [B,H,nb]: per address
+ *     the blocks redirected into it in arrival order, at
+ *     redir_idx[redir_off[a] .. redir_off[a+1]), with redir_time the query
+ *     block at which each arrives; entries past redir_off[A] are -1. */
 typedef struct {
   float* ksum;
   int32_t* addr;
@@ -112,6 +143,11 @@ typedef struct {
   int32_t* overflow;
   int32_t* sel;
   int32_t* n_cand;
+  int32_t* n_drop;
+  int32_t* alt;
+  int32_t* redir_off;
+  int32_t* redir_idx;
+  int32_t* redir_time;
 } mdr_routing;
 
 /* MDR_ABI_VERSION of the built library. */
@@ -178,29 +214,40 @@ mdr_status mdr_mixer_forward(const mdr_config* cfg, const void* x, const void* w
  * attention into a retrieval decision": a product address combines the
  * decisions of several learned code components).
  *   k [B,H,S,D]; codebook [H,G,C,D]; code_bias [H,G,C] or NULL;
- *   ksum [B,H,nb,D] fp32 out; addr [B,H,nb] out. */
+ *   ksum [B,H,nb,D] fp32 out; addr [B,H,nb] out; alt [B,H,nb] out or NULL
+ *   (the alternate addresses of the REDIRECT policy; -1 when codes == 1). */
 mdr_status mdr_stage_address(const mdr_config* cfg, const void* k, const float* codebook,
-                             const float* code_bias, float* ksum, int32_t* addr, void* stream);
+                             const float* code_bias, float* ksum, int32_t* addr, int32_t* alt,
+                             void* stream);
 
 /* Bounded causal posting lists as CSR plus overflow counts (aitechinspire.com
  * "Snapshot": source blocks assigned to bounded causal posting lists; remio.ai
  * same section: a strict capacity bounds each list, overflow drops blocks).
  *   addr [B,H,nb] in (values must lie in [0, A)); post_off [B,H,A+1],
- *   post_idx [B,H,nb], overflow [B,H] out. */
-mdr_status mdr_stage_post(const mdr_config* cfg, const int32_t* addr, int32_t* post_off,
-                          int32_t* post_idx, int32_t* overflow, void* stream);
+ *   post_idx [B,H,nb], overflow [B,H] out.  Under REDIRECT also alt
+ *   [B,H,nb] in (values in [0, A), or -1 for none) and the redirect lists
+ *   redir_off, redir_idx, redir_time out (layouts as in mdr_routing); under
+ *   DROP those four may be NULL and are ignored. */
+mdr_status mdr_stage_post(const mdr_config* cfg, const int32_t* addr, const int32_t* alt,
+                          int32_t* post_off, int32_t* post_idx, int32_t* redir_off,
+                          int32_t* redir_idx, int32_t* redir_time, int32_t* overflow, void* stream);
 
 /* Query probe, candidate gathering and rerank to R remote blocks
  * (aitechinspire.com "Snapshot": each query probes product addresses,
  * reranks returned candidates and selects a fixed number of remote blocks).
  *   q [B,H,S,D]; codebook, code_bias as above; ksum [B,H,nb,D] fp32;
  *   post_off [B,H,A+1], post_idx [B,H,nb] (CSR as produced by
- *   mdr_stage_post); force [B,H,S] or NULL; sel [B,H,S,R] out;
- *   n_cand [B,H,S] out or NULL. */
+ *   mdr_stage_post); redir_off, redir_idx, redir_time as produced by
+ *   mdr_stage_post (REDIRECT; ignored under DROP); force [B,H,S] or NULL;
+ *   sel [B,H,S,R] out; n_cand [B,H,S] out or NULL; n_drop [B,H,S] out or
+ *   NULL (its count assumes every block has an alternate when codes > 1,
+ *   as the library's alternates do). */
 mdr_status mdr_stage_probe_rerank(const mdr_config* cfg, const void* q, const float* codebook,
                                   const float* code_bias, const float* ksum, const int32_t* post_off,
-                                  const int32_t* post_idx, const int32_t* force, int32_t* sel,
-                                  int32_t* n_cand, void* stream);
+                                  const int32_t* post_idx, const int32_t* redir_off,
+                                  const int32_t* redir_idx, const int32_t* redir_time,
+                                  const int32_t* force, int32_t* sel, int32_t* n_cand,
+                                  int32_t* n_drop, void* stream);
 
 /* Exact causal softmax over the selected remote blocks plus the L local blocks
  * (aitechinspire.com "Snapshot" and "What's the core idea?": no approximation

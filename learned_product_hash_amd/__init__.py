@@ -29,6 +29,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmdr.so")
 
 MDR_OK, MDR_ERR_INVALID_ARG, MDR_ERR_UNSUPPORTED, MDR_ERR_WORKSPACE, MDR_ERR_HIP = range(5)
 MDR_F32, MDR_BF16 = 0, 1
+MDR_OVERFLOW_DROP, MDR_OVERFLOW_REDIRECT = 0, 1
 
 
 class MdrError(RuntimeError):
@@ -41,12 +42,13 @@ class MdrConfig(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "batch", "seq", "heads", "head_dim", "width", "block", "subspaces", "codes", "capacity",
         "probes", "max_cand", "remote", "local", "dtype")] + [
-        ("rope_base", ctypes.c_float), ("softmax_scale", ctypes.c_float)]
+        ("rope_base", ctypes.c_float), ("softmax_scale", ctypes.c_float), ("overflow_policy", ctypes.c_int32)]
 
 
 class MdrRouting(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
-        "ksum", "addr", "post_off", "post_idx", "overflow", "sel", "n_cand")]
+        "ksum", "addr", "post_off", "post_idx", "overflow", "sel", "n_cand", "n_drop", "alt", "redir_off",
+        "redir_idx", "redir_time")]
 
 
 class MdrDecodeView(ctypes.Structure):
@@ -74,9 +76,9 @@ _SIGS = {
     "mdr_routed_attention_profiled": ([_cfgp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _rtp, _vp, _sz,
                                        ctypes.POINTER(_vp), _vp], _i32),
     "mdr_mixer_forward": ([_cfgp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _rtp, _vp, _sz, _vp], _i32),
-    "mdr_stage_address": ([_cfgp, _vp, _vp, _vp, _vp, _vp, _vp], _i32),
-    "mdr_stage_post": ([_cfgp, _vp, _vp, _vp, _vp, _vp], _i32),
-    "mdr_stage_probe_rerank": ([_cfgp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp], _i32),
+    "mdr_stage_address": ([_cfgp] + [_vp] * 7, _i32),
+    "mdr_stage_post": ([_cfgp] + [_vp] * 9, _i32),
+    "mdr_stage_probe_rerank": ([_cfgp] + [_vp] * 14, _i32),
     "mdr_stage_attend": ([_cfgp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], _i32),
     "mdr_stage_attend_lse": ([_cfgp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], _i32),
     "mdr_stage_attend_backward": ([_cfgp] + [_vp] * 11 + [_sz, _vp], _i32),
@@ -94,10 +96,13 @@ for _name, (_args, _res) in _SIGS.items():
 
 
 def config(**fields) -> MdrConfig:
-    """An MdrConfig with unspecified fields zero (dtype accepts "f32"/"bf16")."""
+    """An MdrConfig with unspecified fields zero (dtype accepts "f32"/"bf16", overflow_policy
+    "drop"/"redirect")."""
     f = dict(fields)
     if isinstance(f.get("dtype"), str):
         f["dtype"] = {"f32": MDR_F32, "bf16": MDR_BF16}[f["dtype"]]
+    if isinstance(f.get("overflow_policy"), str):
+        f["overflow_policy"] = {"drop": MDR_OVERFLOW_DROP, "redirect": MDR_OVERFLOW_REDIRECT}[f["overflow_policy"]]
     return MdrConfig(**f)
 
 
@@ -164,7 +169,11 @@ def routing_buffers(cfg: MdrConfig, device="cuda") -> dict:
     return dict(ksum=torch.empty(B, H, nb, D, dtype=torch.float32, device=device),
                 addr=torch.empty(B, H, nb, **i32), post_off=torch.empty(B, H, A + 1, **i32),
                 post_idx=torch.empty(B, H, nb, **i32), overflow=torch.empty(B, H, **i32),
-                sel=torch.empty(B, H, S, cfg.remote, **i32), n_cand=torch.empty(B, H, S, **i32))
+                sel=torch.empty(B, H, S, cfg.remote, **i32), n_cand=torch.empty(B, H, S, **i32),
+                n_drop=torch.empty(B, H, S, **i32),
+                **(dict(alt=torch.empty(B, H, nb, **i32), redir_off=torch.empty(B, H, A + 1, **i32),
+                        redir_idx=torch.empty(B, H, nb, **i32), redir_time=torch.empty(B, H, nb, **i32))
+                   if cfg.overflow_policy == MDR_OVERFLOW_REDIRECT else {}))
 
 
 def _ws(ws):
@@ -199,20 +208,23 @@ def mdr_mixer_forward(cfg, x, wq, wk, wv, wo, codebook, code_bias, delta, routin
                                  _stream(stream)), "mdr_mixer_forward")
 
 
-def mdr_stage_address(cfg, k, codebook, code_bias, ksum, addr, stream=None):
+def mdr_stage_address(cfg, k, codebook, code_bias, ksum, addr, alt=None, stream=None):
     _check(lib.mdr_stage_address(ctypes.byref(cfg), _ptr(k), _ptr(codebook), _ptr(code_bias), _ptr(ksum),
-                                 _ptr(addr), _stream(stream)), "mdr_stage_address")
+                                 _ptr(addr), _ptr(alt), _stream(stream)), "mdr_stage_address")
 
 
-def mdr_stage_post(cfg, addr, post_off, post_idx, overflow, stream=None):
-    _check(lib.mdr_stage_post(ctypes.byref(cfg), _ptr(addr), _ptr(post_off), _ptr(post_idx), _ptr(overflow),
+def mdr_stage_post(cfg, addr, post_off, post_idx, overflow, alt=None, redir_off=None, redir_idx=None,
+                   redir_time=None, stream=None):
+    _check(lib.mdr_stage_post(ctypes.byref(cfg), _ptr(addr), _ptr(alt), _ptr(post_off), _ptr(post_idx),
+                              _ptr(redir_off), _ptr(redir_idx), _ptr(redir_time), _ptr(overflow),
                               _stream(stream)), "mdr_stage_post")
 
 
 def mdr_stage_probe_rerank(cfg, q, codebook, code_bias, ksum, post_off, post_idx, force, sel, n_cand=None,
-                           stream=None):
+                           redir_off=None, redir_idx=None, redir_time=None, n_drop=None, stream=None):
     _check(lib.mdr_stage_probe_rerank(ctypes.byref(cfg), _ptr(q), _ptr(codebook), _ptr(code_bias), _ptr(ksum),
-                                      _ptr(post_off), _ptr(post_idx), _ptr(force), _ptr(sel), _ptr(n_cand),
+                                      _ptr(post_off), _ptr(post_idx), _ptr(redir_off), _ptr(redir_idx),
+                                      _ptr(redir_time), _ptr(force), _ptr(sel), _ptr(n_cand), _ptr(n_drop),
                                       _stream(stream)), "mdr_stage_probe_rerank")
 
 

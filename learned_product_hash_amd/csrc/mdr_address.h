@@ -41,12 +41,15 @@ struct AddressLds {
 // All 256 threads of the work-group call it (it contains barriers).  The codebook rows are
 // requested together with the key rows: four adjacent lanes share one code (each a quarter of D,
 // added in a fixed order), and one wave takes each subspace's argmax with a butterfly over
-// (logit, code).  Writes ksum[bh, i, :] and addr[bh, i].
+// (logit, code).  Writes ksum[bh, i, :] and addr[bh, i], and when `alt` is given the block's
+// alternate address: in the subspace with the smallest fp32 margin top1 - top2 (ties to the
+// smaller subspace) the runner-up code (the best of the others, smaller code on ties) replaces the
+// top code; -1 when C == 1.
 template <typename T, int D>
 __device__ __forceinline__ void block_address(const T* __restrict__ K, const float* __restrict__ cb,
                                               const float* __restrict__ bias, float* __restrict__ ksum,
                                               int32_t* __restrict__ addr, int i, int bh, AddressLds<T, D>& sm,
-                                              const Shape& s) {
+                                              const Shape& s, int32_t* __restrict__ alt = nullptr) {
   constexpr int VEC = Vec16<T>::n;
   constexpr int NCH = AddressLds<T, D>::NCH;
   constexpr int RG = AddressLds<T, D>::RG;
@@ -103,10 +106,13 @@ __device__ __forceinline__ void block_address(const T* __restrict__ K, const flo
   __syncthreads();
   if (tid < 64) {
     int a = 0;
+    float best_m = INFINITY;
+    int gs = -1, dc = 0;  // subspace of the smallest margin, runner-up code minus top code
     for (int g = 0; g < s.G; ++g) {
       // lanes 0..C-1 hold the subspace's logits; the butterfly keeps the larger logit, the
       // smaller code on ties
-      float v = lane < s.C ? sm.logit[g * s.C + lane] : -INFINITY;
+      const float lv = lane < s.C ? sm.logit[g * s.C + lane] : -INFINITY;
+      float v = lv;
       int c = lane < s.C ? lane : 0x7fffffff;
 #pragma unroll
       for (int x = 32; x >= 1; x >>= 1) {
@@ -118,8 +124,34 @@ __device__ __forceinline__ void block_address(const T* __restrict__ K, const flo
         }
       }
       a = a * s.C + c;
+      if (alt) {
+        float v2 = (lane < s.C && lane != c) ? lv : -INFINITY;
+        int c2 = (lane < s.C && lane != c) ? lane : 0x7fffffff;
+#pragma unroll
+        for (int x = 32; x >= 1; x >>= 1) {
+          const float ov = __shfl_xor(v2, x);
+          const int oc = __shfl_xor(c2, x);
+          if (ov > v2 || (ov == v2 && oc < c2)) {
+            v2 = ov;
+            c2 = oc;
+          }
+        }
+        const float m = v - v2;  // +inf when C == 1
+        if (m < best_m) {
+          best_m = m;
+          gs = g;
+          dc = c2 - c;
+        }
+      }
     }
-    if (tid == 0) addr[(size_t)bh * s.nb + i] = a;
+    if (tid == 0) {
+      addr[(size_t)bh * s.nb + i] = a;
+      if (alt) {
+        int pw = 1;  // place value of subspace gs (subspace 0 most significant)
+        for (int g = gs + 1; g < s.G; ++g) pw *= s.C;
+        alt[(size_t)bh * s.nb + i] = gs >= 0 ? a + dc * pw : -1;
+      }
+    }
   }
 }
 

@@ -18,6 +18,7 @@ mdr_status shape_from_config(const mdr_config* cfg, bool mixer, Shape* out) {
     return MDR_ERR_INVALID_ARG;
   if (c.seq % c.block != 0) return MDR_ERR_INVALID_ARG;
   if (c.dtype != MDR_F32 && c.dtype != MDR_BF16) return MDR_ERR_INVALID_ARG;
+  if (c.overflow_policy != MDR_OVERFLOW_DROP && c.overflow_policy != MDR_OVERFLOW_REDIRECT) return MDR_ERR_INVALID_ARG;
   if (!(c.softmax_scale >= 0.f) || isinf(c.softmax_scale)) return MDR_ERR_INVALID_ARG;
   if (mixer && (c.width < 1 || !(c.rope_base > 0.f) || isinf(c.rope_base))) return MDR_ERR_INVALID_ARG;
   if (c.head_dim != 32 && c.head_dim != 64 && c.head_dim != 128) return MDR_ERR_UNSUPPORTED;
@@ -57,6 +58,7 @@ mdr_status shape_from_config(const mdr_config* cfg, bool mixer, Shape* out) {
   s.dtype = c.dtype;
   s.scale = c.softmax_scale > 0.f ? c.softmax_scale : 1.0f / sqrtf((float)c.head_dim);
   s.rope_base = c.rope_base;
+  s.policy = c.overflow_policy;
   const long long ne = nb > c.local ? nb - c.local : 0;
   s.ne = (int)ne;
   s.cells_per_bh = ne * (ne + 1) / 2;
@@ -68,6 +70,7 @@ mdr_status shape_from_config(const mdr_config* cfg, bool mixer, Shape* out) {
   s.fixed_probe = probe_fixed_shape(s);
   if (probe_lds_bytes(s) > 160 * 1024) return MDR_ERR_UNSUPPORTED;
   if (s.R > 0 && ne > 0 && remote_lds_bytes(s) > 160 * 1024) return MDR_ERR_UNSUPPORTED;
+  if (s.policy == MDR_OVERFLOW_REDIRECT && ((long long)s.A + 2 * ne) * 4 > 160 * 1024) return MDR_ERR_UNSUPPORTED;
   *out = s;
   return MDR_OK;
 }
@@ -96,6 +99,15 @@ size_t layout(const Shape& s, char* base, Buffers* b) {
   t.part_o = take(BH * s.S * s.R * s.D * e);
   t.part_ml = (float*)take(BH * s.S * s.R * 8);
   t.dvec = (float*)take(BH * s.S * 4);
+  if (s.policy == MDR_OVERFLOW_REDIRECT) {
+    t.alt = (int32_t*)take(BH * s.nb * 4);
+    t.roff = (int32_t*)take(BH * (s.A + 1) * 4);
+    t.ridx = (int32_t*)take(BH * s.nb * 4);
+    t.rtime = (int32_t*)take(BH * s.nb * 4);
+  } else {
+    t.alt = t.roff = t.ridx = t.rtime = nullptr;
+  }
+  t.ndrop = nullptr;
   if (s.W > 0) {
     const size_t qkv = BH * s.S * s.D * e;
     t.mq = take(qkv);
@@ -135,6 +147,7 @@ mdr_status decode_shape(const mdr_config* cfg, Shape* out) {
   if (st != MDR_OK) return st;
   s.W = 0;
   if ((long long)(s.R + s.L) * s.blk > kDecMaxKeys || s.M > kDecMaxCand) return MDR_ERR_UNSUPPORTED;
+  if (s.policy != MDR_OVERFLOW_DROP) return MDR_ERR_UNSUPPORTED;
   *out = s;
   return MDR_OK;
 }
@@ -180,6 +193,13 @@ void apply_routing(const mdr_routing* r, Buffers* b) {
   if (r->overflow) b->overflow = r->overflow;
   if (r->sel) b->sel = r->sel;
   if (r->n_cand) b->ncand = r->n_cand;
+  b->ndrop = r->n_drop;
+  if (b->alt) {  // redirect policy
+    if (r->alt) b->alt = r->alt;
+    if (r->redir_off) b->roff = r->redir_off;
+    if (r->redir_idx) b->ridx = r->redir_idx;
+    if (r->redir_time) b->rtime = r->redir_time;
+  }
 }
 
 bool routing_aligned(const mdr_routing* r) {
@@ -192,16 +212,20 @@ mdr_status run_core(const Shape& s, const void* q, const void* k, const void* v,
                     const int32_t* force, void* out, const Buffers& b, hipStream_t st, hipEvent_t* ev = nullptr) {
   const bool remote = s.R > 0 && s.ne > 0;
   if (ev) MDR_TRY(hipEventRecord(ev[0], st));
-  MDR_TRY(launch_address(s, k, cb, bias, b.ksum, b.addr, remote ? b.cellcnt : nullptr, st));
+  const bool redirect = s.policy == MDR_OVERFLOW_REDIRECT;
+  MDR_TRY(launch_address(s, k, cb, bias, b.ksum, b.addr, remote ? b.cellcnt : nullptr, st, 0, -1,
+                         redirect ? b.alt : nullptr));
   if (ev) MDR_TRY(hipEventRecord(ev[1], st));
   // the posting lists are built inside the probe kernel where a specialised probe exists (the post
-  // interval of a profiled call is then empty)
-  const bool fused = probe_fuses_post(s);
+  // interval of a profiled call is then empty); the redirect lists need the whole CSR first
+  const bool fused = probe_fuses_post(s) && !redirect;
   if (!fused) MDR_TRY(launch_post(s, b.addr, b.off, b.idx, b.overflow, st));
+  if (redirect) MDR_TRY(launch_post_redirect(s, b.addr, b.alt, b.off, b.idx, b.roff, b.ridx, b.rtime, b.overflow, st));
   if (ev) MDR_TRY(hipEventRecord(ev[2], st));
   const FusedPost fp{b.addr, b.off, b.idx, b.overflow};
+  const ProbeExtra ex{redirect ? b.roff : nullptr, b.ridx, b.rtime, b.ndrop};
   MDR_TRY(launch_probe_rerank(s, q, cb, bias, b.ksum, b.off, b.idx, force, b.sel, b.ncand,
-                              remote ? b.cellcnt : nullptr, remote ? b.bins : nullptr, st, fused ? &fp : nullptr));
+                              remote ? b.cellcnt : nullptr, remote ? b.bins : nullptr, st, fused ? &fp : nullptr, ex));
   MDR_TRY(launch_attend(s, q, k, v, b.sel, out, b, st, ev ? ev + 3 : nullptr));
   if (ev) MDR_TRY(hipEventRecord(ev[MDR_CORE_KERNELS], st));
   return MDR_OK;
@@ -302,35 +326,46 @@ mdr_status mdr_mixer_forward(const mdr_config* cfg, const void* x, const void* w
 }
 
 mdr_status mdr_stage_address(const mdr_config* cfg, const void* k, const float* codebook, const float* code_bias,
-                             float* ksum, int32_t* addr, void* stream) {
+                             float* ksum, int32_t* addr, int32_t* alt, void* stream) {
   Shape s;
   mdr_status st = shape_from_config(cfg, false, &s);
   if (st != MDR_OK) return st;
   if (!k || !codebook || !ksum || !addr) return MDR_ERR_INVALID_ARG;
   if (!aligned16(k) || !aligned16(ksum)) return MDR_ERR_INVALID_ARG;
-  return hip_status(launch_address(s, k, codebook, code_bias, ksum, addr, nullptr, (hipStream_t)stream));
+  return hip_status(launch_address(s, k, codebook, code_bias, ksum, addr, nullptr, (hipStream_t)stream, 0, -1, alt));
 }
 
-mdr_status mdr_stage_post(const mdr_config* cfg, const int32_t* addr, int32_t* post_off, int32_t* post_idx,
+mdr_status mdr_stage_post(const mdr_config* cfg, const int32_t* addr, const int32_t* alt, int32_t* post_off,
+                          int32_t* post_idx, int32_t* redir_off, int32_t* redir_idx, int32_t* redir_time,
                           int32_t* overflow, void* stream) {
   Shape s;
   mdr_status st = shape_from_config(cfg, false, &s);
   if (st != MDR_OK) return st;
   if (!addr || !post_off || !post_idx || !overflow) return MDR_ERR_INVALID_ARG;
-  return hip_status(launch_post(s, addr, post_off, post_idx, overflow, (hipStream_t)stream));
+  const bool redirect = s.policy == MDR_OVERFLOW_REDIRECT;
+  if (redirect && (!alt || !redir_off || !redir_idx || !redir_time)) return MDR_ERR_INVALID_ARG;
+  hipStream_t hs = (hipStream_t)stream;
+  MDR_TRY(launch_post(s, addr, post_off, post_idx, overflow, hs));
+  if (redirect)
+    MDR_TRY(launch_post_redirect(s, addr, alt, post_off, post_idx, redir_off, redir_idx, redir_time, overflow, hs));
+  return MDR_OK;
 }
 
 mdr_status mdr_stage_probe_rerank(const mdr_config* cfg, const void* q, const float* codebook,
                                   const float* code_bias, const float* ksum, const int32_t* post_off,
-                                  const int32_t* post_idx, const int32_t* force, int32_t* sel, int32_t* n_cand,
-                                  void* stream) {
+                                  const int32_t* post_idx, const int32_t* redir_off, const int32_t* redir_idx,
+                                  const int32_t* redir_time, const int32_t* force, int32_t* sel, int32_t* n_cand,
+                                  int32_t* n_drop, void* stream) {
   Shape s;
   mdr_status st = shape_from_config(cfg, false, &s);
   if (st != MDR_OK) return st;
   if (!q || !codebook || !ksum || !post_off || !post_idx || (!sel && s.R > 0)) return MDR_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(ksum)) return MDR_ERR_INVALID_ARG;
+  const bool redirect = s.policy == MDR_OVERFLOW_REDIRECT;
+  if (redirect && (!redir_off || !redir_idx || !redir_time)) return MDR_ERR_INVALID_ARG;
+  const ProbeExtra ex{redirect ? redir_off : nullptr, redir_idx, redir_time, n_drop};
   return hip_status(launch_probe_rerank(s, q, codebook, code_bias, ksum, post_off, post_idx, force, sel, n_cand,
-                                        nullptr, nullptr, (hipStream_t)stream));
+                                        nullptr, nullptr, (hipStream_t)stream, nullptr, ex));
 }
 
 mdr_status mdr_stage_attend_lse(const mdr_config* cfg, const void* q, const void* k, const void* v,

@@ -33,6 +33,7 @@ struct Shape {
   int split;        // remote work-groups per block
   int csr_lds;      // probe stage stages the posting-list CSR in LDS
   int fixed_probe;  // probe stage uses its compile-time specialisation for these sizes
+  int policy;       // mdr_overflow_policy
 };
 
 constexpr int kProbeThreads = 128;  // query tokens per probe work-group (one per lane)
@@ -57,6 +58,20 @@ struct Buffers {
   float* lse;          // [B,H,S] optional output of the attention: log2 of each token's softmax
                        // normaliser sum_s 2^(scale log2(e) q.k_s) (nullptr: not written)
   float* dvec;         // [B,H,S] backward: D_t = dO_t . O_t
+  int32_t* alt;        // [B,H,nb] alternate address of each block (redirect policy)
+  int32_t* roff;       // [B,H,A+1] redirect lists: per address, blocks redirected into it
+  int32_t* ridx;       // [B,H,nb]  (block ids, in arrival order; -1 beyond the last)
+  int32_t* rtime;      // [B,H,nb]  (the query block at which each arrives; -1 beyond the last)
+  int32_t* ndrop;      // [B,H,S] optional: candidates the probed lists held but did not return
+};
+
+// Redirect lists and the dropped-candidate output of the probe stage (all null under the drop
+// policy without diagnostics).
+struct ProbeExtra {
+  const int32_t* roff;
+  const int32_t* ridx;
+  const int32_t* rtime;
+  int32_t* ndrop;
 };
 
 // Streaming-decode state (one region of a caller-owned buffer each).
@@ -147,8 +162,11 @@ __device__ inline int block_exclusive_scan(int v, int* tmp, int* total) {
 // Launchers (return hipGetLastError()).
 // cell_zero (optional): the address kernel of block i clears the cell counters of row i.
 // Blocks [i0, i0 + n) (n < 0: to the end).
+// alt (optional): also the alternate address of each block (runner-up code of its lowest-margin
+// subspace).
 hipError_t launch_address(const Shape& s, const void* k, const float* codebook, const float* bias,
-                          float* ksum, int32_t* addr, int32_t* cell_zero, hipStream_t st, int i0 = 0, int n = -1);
+                          float* ksum, int32_t* addr, int32_t* cell_zero, hipStream_t st, int i0 = 0, int n = -1,
+                          int32_t* alt = nullptr);
 hipError_t launch_post(const Shape& s, const int32_t* addr, int32_t* off, int32_t* idx,
                        int32_t* overflow, hipStream_t st);
 // Posting lists built inside the probe kernel (from the block addresses) instead of read: every
@@ -162,7 +180,13 @@ struct FusedPost {
 hipError_t launch_probe_rerank(const Shape& s, const void* q, const float* codebook, const float* bias,
                                const float* ksum, const int32_t* off, const int32_t* idx,
                                const int32_t* force, int32_t* sel, int32_t* ncand, int32_t* cellcnt,
-                               int32_t* bins, hipStream_t st, const FusedPost* fuse = nullptr);
+                               int32_t* bins, hipStream_t st, const FusedPost* fuse = nullptr,
+                               const ProbeExtra& ex = ProbeExtra{nullptr, nullptr, nullptr, nullptr});
+// Redirect lists from the posting CSR and the alternates; overwrites overflow with the blocks no
+// final view returns.
+hipError_t launch_post_redirect(const Shape& s, const int32_t* addr, const int32_t* alt, const int32_t* off,
+                                const int32_t* idx, int32_t* roff, int32_t* ridx, int32_t* rtime,
+                                int32_t* overflow, hipStream_t st);
 // True when launch_probe_rerank accepts `fuse` for this shape (the compile-time specialised probe).
 bool probe_fuses_post(const Shape& s);
 size_t probe_lds_bytes(const Shape& s);

@@ -30,7 +30,7 @@ template <typename T, int D>
 __global__ __launch_bounds__(256) void k_address(const T* __restrict__ K, const float* __restrict__ cb,
                                                  const float* __restrict__ bias, float* __restrict__ ksum,
                                                  int32_t* __restrict__ addr, int32_t* __restrict__ cell_zero,
-                                                 int i0, Shape s) {
+                                                 int32_t* __restrict__ alt, int i0, Shape s) {
   __shared__ AddressLds<T, D> sm;
   const int i = i0 + blockIdx.x;
   const int bh = blockIdx.y;
@@ -38,7 +38,7 @@ __global__ __launch_bounds__(256) void k_address(const T* __restrict__ K, const 
     int32_t* row = cell_zero + (size_t)bh * s.cells_per_bh + cell_row(i, s.ne);
     for (int c = threadIdx.x; c < s.ne - i; c += 256) row[c] = 0;
   }
-  block_address<T, D>(K, cb, bias, ksum, addr, i, bh, sm, s);
+  block_address<T, D>(K, cb, bias, ksum, addr, i, bh, sm, s, alt);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -124,6 +124,112 @@ __global__ __launch_bounds__(256) void k_post(const int32_t* __restrict__ addr, 
 }
 
 // ---------------------------------------------------------------------------------------------
+// Redirect lists of one (b,h), for the overflow policy that redirects.  The block at position k of
+// list a leaves the primary view when the block y at position k + capacity becomes eligible (query
+// block y + L) and then arrives in the redirect list of its alternate address.  A block evicts at
+// most one other, so arrivals are indexed by the evicting block y and ordered by it; a stable
+// counting sort by alternate address (one ballot per address bit, as in k_post) keeps that order
+// within each list.  overflow = the drop policy's overflow minus the redirected blocks that fill
+// spare slots of their lists at the last query block.
+__global__ __launch_bounds__(256) void k_post_redirect(const int32_t* __restrict__ addr,
+                                                       const int32_t* __restrict__ alt,
+                                                       const int32_t* __restrict__ off,
+                                                       const int32_t* __restrict__ idx, int32_t* __restrict__ roff,
+                                                       int32_t* __restrict__ ridx, int32_t* __restrict__ rtime,
+                                                       int32_t* __restrict__ overflow, Shape s) {
+  extern __shared__ int rsm[];
+  const int A = s.A, ne = s.ne;
+  int* hist = rsm;         // [A] arrivals per address, then the scatter cursors
+  int* key = hist + A;     // [ne] alternate address of the block evicted by block y (-1: none)
+  int* evb = key + ne;     // [ne] the block evicted by block y
+  __shared__ int part[4];
+  const int tid = threadIdx.x;
+  const int bh = blockIdx.x;
+  const int32_t* offp = off + (size_t)bh * (A + 1);
+  const int32_t* idxp = idx + (size_t)bh * s.nb;
+  const int32_t* ad = addr + (size_t)bh * s.nb;
+  const int32_t* al = alt + (size_t)bh * s.nb;
+  for (int a = tid; a < A; a += 256) hist[a] = 0;
+  for (int y = tid; y < ne; y += 256) key[y] = -1;
+  __syncthreads();
+  const int total = min(offp[A], ne);
+  for (int q = tid; q < total; q += 256) {
+    const int y = idxp[q];
+    if (y < 0 || y >= ne) continue;
+    const int a = ad[y];
+    if (a < 0 || a >= A || q - s.cap < offp[a]) continue;
+    const int x = idxp[q - s.cap];
+    const int b = (x >= 0 && x < ne) ? al[x] : -1;
+    if (b >= 0 && b < A) {
+      key[y] = b;
+      evb[y] = x;
+      atomicAdd(&hist[b], 1);
+    }
+  }
+  __syncthreads();
+  const int seg = (A + 255) / 256;
+  const int a0 = min(A, tid * seg), a1 = min(A, a0 + seg);
+  int sum = 0, over = 0, shown = 0;
+  for (int a = a0; a < a1; ++a) {
+    const int np = offp[a + 1] - offp[a];
+    sum += hist[a];
+    over += max(0, np - s.cap);
+    shown += min(max(0, s.cap - np), hist[a]);
+  }
+  int tot_over = 0, tot_shown = 0, tot = 0;
+  block_exclusive_scan<256>(over, part, &tot_over);
+  block_exclusive_scan<256>(shown, part, &tot_shown);
+  int run = block_exclusive_scan<256>(sum, part, &tot);
+  int32_t* ro = roff + (size_t)bh * (A + 1);
+  if (tid == 0) {
+    overflow[bh] = tot_over - tot_shown;
+    ro[A] = tot;
+  }
+  for (int a = a0; a < a1; ++a) {
+    const int v = hist[a];
+    ro[a] = run;
+    hist[a] = run;
+    run += v;
+  }
+  __syncthreads();
+  int32_t* oi = ridx + (size_t)bh * s.nb;
+  int32_t* ot = rtime + (size_t)bh * s.nb;
+  if (tid < kWave) {
+    const int lane = tid;
+    int nbits = 0;
+    while ((1 << nbits) < A) ++nbits;
+    const unsigned long long lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    for (int c0 = 0; c0 < ne; c0 += kWave) {
+      const int y = c0 + lane;
+      int k = y < ne ? key[y] : -1;
+      const bool valid = k >= 0;
+      if (!valid) k = 0;
+      unsigned long long same = __ballot(valid);
+      for (int b = 0; b < nbits; ++b) {
+        const bool bit = (k >> b) & 1;
+        const unsigned long long m1 = __ballot(bit);
+        same &= bit ? m1 : ~m1;
+      }
+      if (valid) {
+        const int rank = __popcll(same & lt);
+        const int count = __popcll(same);
+        const int cur = hist[k];
+        oi[cur + rank] = evb[y];
+        ot[cur + rank] = y + s.L;
+        __builtin_amdgcn_wave_barrier();
+        if (rank == count - 1) hist[k] = cur + count;
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
+  }
+  __syncthreads();
+  for (int i = tot + tid; i < s.nb; i += 256) {
+    oi[i] = -1;
+    ot[i] = -1;
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
 // Probe + rerank.  A work-group of kProbeThreads lanes handles as many consecutive query tokens of
 // one (b,h), one token per lane for the ranking steps (per-lane scratch lives in LDS, laid out
 // [slot][lane] so lanes never conflict):
@@ -143,7 +249,7 @@ __global__ __launch_bounds__(kProbeThreads) void k_probe_rerank(
     const T* __restrict__ Q, const float* __restrict__ cb, const float* __restrict__ bias,
     const float* __restrict__ ksum, const int32_t* __restrict__ off, const int32_t* __restrict__ idx,
     const int32_t* __restrict__ force, int32_t* __restrict__ sel, int32_t* __restrict__ ncand,
-    int32_t* __restrict__ cellcnt, int32_t* __restrict__ bins, Shape s) {
+    int32_t* __restrict__ cellcnt, int32_t* __restrict__ bins, ProbeExtra ex, Shape s) {
   constexpr int NT = kProbeThreads;
   extern __shared__ __align__(16) float smem[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -298,11 +404,14 @@ __global__ __launch_bounds__(kProbeThreads) void k_probe_rerank(
     tpa[pos * NT + tid] = a;
   }
 
-  // ---- candidates in probe rank order, rerank by <q_t, summary>
-  int nc = 0, nr = 0;
-  if (cutoff >= 0 && R > 0) {
+  // ---- candidates in probe rank order (each probe's view: its newest `capacity` eligible
+  // primaries, then, under the redirect policy, the newest arrivals of its redirect list while slots
+  // remain), cut at M; rerank by <q_t, summary>.  Dropped candidates: per probe, the eligible
+  // blocks the list holds beyond its capacity.
+  int nc = 0, nr = 0, ndr = 0;
+  if (cutoff >= 0) {
     float qv[D];
-    {
+    if (R > 0) {
       const T* qp = Q + ((size_t)bh * s.S + t) * D;
       constexpr int VEC = Vec16<T>::n;
 #pragma unroll
@@ -313,7 +422,42 @@ __global__ __launch_bounds__(kProbeThreads) void k_probe_rerank(
       }
     }
     const float* ksh = ksum + (size_t)bh * s.nb * D;
-    for (int p = 0; p < np && nc < s.M; ++p) {
+    const int32_t* roffp = ex.roff ? ex.roff + (size_t)bh * (A + 1) : nullptr;
+    const int32_t* ridxp = ex.roff ? ex.ridx + (size_t)bh * s.nb : nullptr;
+    const int32_t* rtimep = ex.roff ? ex.rtime + (size_t)bh * s.nb : nullptr;
+    auto consider = [&](int i) {
+      ++nc;
+      const float4* kr = (const float4*)(ksh + (size_t)i * D);
+      float rho = 0.f;
+#pragma unroll
+      for (int c = 0; c < D / 4; ++c) {
+        const float4 kv = kr[c];
+        rho = fmaf(kv.x, qv[4 * c + 0], rho);
+        rho = fmaf(kv.y, qv[4 * c + 1], rho);
+        rho = fmaf(kv.z, qv[4 * c + 2], rho);
+        rho = fmaf(kv.w, qv[4 * c + 3], rho);
+      }
+      int pos;
+      if (nr == R) {
+        const float wv = trv[(R - 1) * NT + tid];
+        const int wi = tri[(R - 1) * NT + tid];
+        if (!(rho > wv || (rho == wv && i < wi))) return;
+        pos = R - 1;
+      } else {
+        pos = nr++;
+      }
+      while (pos > 0) {
+        const float pvv = trv[(pos - 1) * NT + tid];
+        const int pi = tri[(pos - 1) * NT + tid];
+        if (!(rho > pvv || (rho == pvv && i < pi))) break;
+        trv[pos * NT + tid] = pvv;
+        tri[pos * NT + tid] = pi;
+        --pos;
+      }
+      trv[pos * NT + tid] = rho;
+      tri[pos * NT + tid] = i;
+    };
+    for (int p = 0; p < np; ++p) {
       const int a = tpa[p * NT + tid];
       const int lo = offp[a], hi = offp[a + 1];
       int l0 = lo, l1 = hi;  // first entry > cutoff
@@ -324,40 +468,26 @@ __global__ __launch_bounds__(kProbeThreads) void k_probe_rerank(
         else
           l1 = mid;
       }
-      const int take = min(min(s.cap, l0 - lo), s.M - nc);
-      for (int e = 0; e < take; ++e) {
-        const int i = idxp[l0 - 1 - e];
-        ++nc;
-        const float4* kr = (const float4*)(ksh + (size_t)i * D);
-        float rho = 0.f;
-#pragma unroll
-        for (int c = 0; c < D / 4; ++c) {
-          const float4 kv = kr[c];
-          rho = fmaf(kv.x, qv[4 * c + 0], rho);
-          rho = fmaf(kv.y, qv[4 * c + 1], rho);
-          rho = fmaf(kv.z, qv[4 * c + 2], rho);
-          rho = fmaf(kv.w, qv[4 * c + 3], rho);
+      const int nprim = l0 - lo, tp = min(s.cap, nprim);
+      const int take = R > 0 ? min(tp, s.M - nc) : 0;
+      for (int e = 0; e < take; ++e) consider(idxp[l0 - 1 - e]);
+      int narr = 0;
+      if (roffp) {
+        const int rlo = roffp[a];
+        int r0 = rlo, r1 = roffp[a + 1];  // first arrival after query block j
+        while (r0 < r1) {
+          const int mid = (r0 + r1) >> 1;
+          if (rtimep[mid] <= j)
+            r0 = mid + 1;
+          else
+            r1 = mid;
         }
-        int pos;
-        if (nr == R) {
-          const float wv = trv[(R - 1) * NT + tid];
-          const int wi = tri[(R - 1) * NT + tid];
-          if (!(rho > wv || (rho == wv && i < wi))) continue;
-          pos = R - 1;
-        } else {
-          pos = nr++;
-        }
-        while (pos > 0) {
-          const float pvv = trv[(pos - 1) * NT + tid];
-          const int pi = tri[(pos - 1) * NT + tid];
-          if (!(rho > pvv || (rho == pvv && i < pi))) break;
-          trv[pos * NT + tid] = pvv;
-          tri[pos * NT + tid] = pi;
-          --pos;
-        }
-        trv[pos * NT + tid] = rho;
-        tri[pos * NT + tid] = i;
+        narr = r0 - rlo;
+        const int taker = R > 0 ? min(min(s.cap - tp, narr), s.M - nc) : 0;
+        for (int e = 0; e < taker; ++e) consider(ridxp[r0 - 1 - e]);
       }
+      // held: the primaries not redirected away (every block has an alternate when C > 1) plus arrivals
+      ndr += max(0, (roffp && C > 1 ? tp : nprim) + narr - s.cap);
     }
   }
   if (force && R > 0) {
@@ -376,6 +506,7 @@ __global__ __launch_bounds__(kProbeThreads) void k_probe_rerank(
   int32_t* srow = sel + ((size_t)bh * s.S + t) * R;
   for (int r = 0; r < R; ++r) srow[r] = r < nr ? tri[r * NT + tid] : -1;
   if (ncand) ncand[(size_t)bh * s.S + t] = nc;
+  if (ex.ndrop) ex.ndrop[(size_t)bh * s.S + t] = ndr;
   if (bins)
     for (int r = 0; r < nr; ++r) record_pair(cellcnt, bins, s, bh, tri[r * NT + tid], j, t, r);
 }
@@ -513,7 +644,7 @@ __global__ __launch_bounds__(kProbeThreads) __attribute__((amdgpu_waves_per_eu(p
     const T* __restrict__ Q, const float* __restrict__ cb, const float* __restrict__ bias,
     const float* __restrict__ ksum, const int32_t* __restrict__ off, const int32_t* __restrict__ idx,
     const int32_t* __restrict__ force, int32_t* __restrict__ sel, int32_t* __restrict__ ncand,
-    int32_t* __restrict__ cellcnt, int32_t* __restrict__ bins, FusedPost fp, Shape s) {
+    int32_t* __restrict__ cellcnt, int32_t* __restrict__ bins, FusedPost fp, ProbeExtra ex, Shape s) {
   constexpr int NT = kProbeThreads;
   static_assert(NT % 64 == 0, "whole waves of 64 tokens");
   constexpr bool BF = std::is_same<T, bf16>::value;
@@ -707,14 +838,21 @@ __global__ __launch_bounds__(kProbeThreads) __attribute__((amdgpu_waves_per_eu(p
 #pragma unroll
   for (int p = 0; p < P; ++p) tpa[p] = key_index(tpk[p]);
   // ---- candidate ranges: probe p contributes the `take[p]` newest entries <= cutoff of its list,
-  // ending at CSR position lim[p] (exclusive), until M candidates
-  int lim[P], take[P];
-  int nc = 0;
+  // ending at CSR position lim[p] (exclusive), then (redirect policy) the `rtake[p]` newest arrivals
+  // of its redirect list up to query block j, ending at rlim[p], until M candidates.  Dropped
+  // candidates: per probe, the eligible blocks the list holds beyond its capacity.
+  int lim[P], take[P], rlim[P], rtake[P];
+  int nc = 0, ndr = 0;
+  const int32_t* roffp = ex.roff ? ex.roff + (size_t)bh * (A + 1) : nullptr;
+  const int32_t* ridxp = ex.roff ? ex.ridx + (size_t)bh * s.nb : nullptr;
+  const int32_t* rtimep = ex.roff ? ex.rtime + (size_t)bh * s.nb : nullptr;
 #pragma unroll
   for (int p = 0; p < P; ++p) {
     take[p] = 0;
     lim[p] = 0;
-    if (active && cutoff >= 0 && R > 0) {
+    rtake[p] = 0;
+    rlim[p] = 0;
+    if (active && cutoff >= 0) {
       const int a = tpa[p];
       const int lo = offp[a], hi = offp[a + 1];
       int l0 = lo, l1 = hi;  // first entry > cutoff
@@ -725,10 +863,30 @@ __global__ __launch_bounds__(kProbeThreads) __attribute__((amdgpu_waves_per_eu(p
         else
           l1 = mid;
       }
-      const int tk = min(min(s.cap, l0 - lo), s.M - nc);
+      const int nprim = l0 - lo, tp = min(s.cap, nprim);
+      const int tk = R > 0 ? min(tp, s.M - nc) : 0;
       take[p] = tk > 0 ? tk : 0;
       lim[p] = l0;
       nc += take[p];
+      int narr = 0;
+      if (roffp) {
+        const int rlo = roffp[a];
+        int r0 = rlo, r1 = roffp[a + 1];  // first arrival after query block j
+        while (r0 < r1) {
+          const int mid = (r0 + r1) >> 1;
+          if (rtimep[mid] <= j)
+            r0 = mid + 1;
+          else
+            r1 = mid;
+        }
+        narr = r0 - rlo;
+        const int tr = R > 0 ? min(min(s.cap - tp, narr), s.M - nc) : 0;
+        rtake[p] = tr > 0 ? tr : 0;
+        rlim[p] = r0;
+        nc += rtake[p];
+      }
+      // held: the primaries not redirected away (every block has an alternate when C > 1) plus arrivals
+      ndr += max(0, (roffp && C > 1 ? tp : nprim) + narr - s.cap);
     }
   }
   // ---- the work-group's candidates as one list (token-major) in LDS, in the place of mu
@@ -740,8 +898,10 @@ __global__ __launch_bounds__(kProbeThreads) __attribute__((amdgpu_waves_per_eu(p
   {
     int k = base;
 #pragma unroll
-    for (int p = 0; p < P; ++p)
+    for (int p = 0; p < P; ++p) {
       for (int e = 0; e < take[p]; ++e) clist[k++] = (tid << 16) | idxp[lim[p] - 1 - e];
+      for (int e = 0; e < rtake[p]; ++e) clist[k++] = (tid << 16) | ridxp[rlim[p] - 1 - e];
+    }
   }
   lds_barrier();
   // ---- rerank scores: LPT adjacent lanes share a token (token wave*64 + (64/LPT)m + lane/LPT,
@@ -842,6 +1002,7 @@ __global__ __launch_bounds__(kProbeThreads) __attribute__((amdgpu_waves_per_eu(p
 #pragma unroll
     for (int r = 0; r < R; ++r) srow[r] = r < nr ? tri[r] : -1;
     if (ncand) ncand[(size_t)bh * s.S + t] = nc;
+    if (ex.ndrop) ex.ndrop[(size_t)bh * s.S + t] = ndr;
   }
   if (!bins) return;  // uniform
   // ---- file each selected pair in its (remote block i, query block j) cell.  The work-group owns
@@ -883,18 +1044,18 @@ __global__ __launch_bounds__(kProbeThreads) __attribute__((amdgpu_waves_per_eu(p
 
 template <typename T>
 hipError_t address_dispatch(const Shape& s, const void* k, const float* cb, const float* bias, float* ksum,
-                            int32_t* addr, int32_t* cnt, int i0, int n, hipStream_t st) {
+                            int32_t* addr, int32_t* cnt, int32_t* alt, int i0, int n, hipStream_t st) {
   if (n <= 0) return hipSuccess;
   dim3 grid(n, s.B * s.H);
   switch (s.D) {
     case 32:
-      hipLaunchKernelGGL((k_address<T, 32>), grid, dim3(256), 0, st, (const T*)k, cb, bias, ksum, addr, cnt, i0, s);
+      hipLaunchKernelGGL((k_address<T, 32>), grid, dim3(256), 0, st, (const T*)k, cb, bias, ksum, addr, cnt, alt, i0, s);
       break;
     case 64:
-      hipLaunchKernelGGL((k_address<T, 64>), grid, dim3(256), 0, st, (const T*)k, cb, bias, ksum, addr, cnt, i0, s);
+      hipLaunchKernelGGL((k_address<T, 64>), grid, dim3(256), 0, st, (const T*)k, cb, bias, ksum, addr, cnt, alt, i0, s);
       break;
     case 128:
-      hipLaunchKernelGGL((k_address<T, 128>), grid, dim3(256), 0, st, (const T*)k, cb, bias, ksum, addr, cnt, i0, s);
+      hipLaunchKernelGGL((k_address<T, 128>), grid, dim3(256), 0, st, (const T*)k, cb, bias, ksum, addr, cnt, alt, i0, s);
       break;
     default:
       return hipErrorInvalidValue;
@@ -906,7 +1067,7 @@ template <typename T, int D, int G, int C, int P, int R, bool FUSED>
 hipError_t probe_fixed_launch_t(const Shape& s, const void* q, const float* cb, const float* bias, const float* ksum,
                                 const int32_t* off, const int32_t* idx, const int32_t* force, int32_t* sel,
                                 int32_t* ncand, int32_t* cellcnt, int32_t* bins, const FusedPost& fp,
-                                hipStream_t st) {
+                                const ProbeExtra& ex, hipStream_t st) {
   dim3 grid((s.S + kProbeThreads - 1) / kProbeThreads, s.B * s.H);
   const size_t lds = probe_lds_bytes(s);
   if (lds > 65536) {
@@ -915,7 +1076,7 @@ hipError_t probe_fixed_launch_t(const Shape& s, const void* q, const float* cb, 
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL((k_probe_fixed<T, D, G, C, P, R, FUSED>), grid, dim3(kProbeThreads), lds, st, (const T*)q, cb,
-                     bias, ksum, off, idx, force, sel, ncand, cellcnt, bins, fp, s);
+                     bias, ksum, off, idx, force, sel, ncand, cellcnt, bins, fp, ex, s);
   return hipGetLastError();
 }
 
@@ -923,13 +1084,13 @@ template <typename T, int D, int G, int C, int P, int R>
 hipError_t probe_fixed_launch(const Shape& s, const void* q, const float* cb, const float* bias, const float* ksum,
                               const int32_t* off, const int32_t* idx, const int32_t* force, int32_t* sel,
                               int32_t* ncand, int32_t* cellcnt, int32_t* bins, const FusedPost* fuse,
-                              hipStream_t st) {
+                              const ProbeExtra& ex, hipStream_t st) {
   if (fuse)
     return probe_fixed_launch_t<T, D, G, C, P, R, true>(s, q, cb, bias, ksum, off, idx, force, sel, ncand, cellcnt,
-                                                         bins, *fuse, st);
+                                                         bins, *fuse, ex, st);
   const FusedPost none{nullptr, nullptr, nullptr, nullptr};
   return probe_fixed_launch_t<T, D, G, C, P, R, false>(s, q, cb, bias, ksum, off, idx, force, sel, ncand, cellcnt,
-                                                        bins, none, st);
+                                                        bins, none, ex, st);
 }
 
 // Shapes with a compile-time specialisation (the five workload families); others use k_probe_rerank.
@@ -944,11 +1105,11 @@ template <typename T>
 hipError_t probe_dispatch(const Shape& s, const void* q, const float* cb, const float* bias, const float* ksum,
                           const int32_t* off, const int32_t* idx, const int32_t* force, int32_t* sel,
                           int32_t* ncand, int32_t* cellcnt, int32_t* bins, const FusedPost* fuse,
-                          hipStream_t st) {
+                          const ProbeExtra& ex, hipStream_t st) {
 #define MDR_FIXED(TT, DD, GG, CC, PP, RR)                                                                        \
   if (std::is_same<T, TT>::value && s.D == DD && s.G == GG && s.C == CC && s.P == PP && s.R == RR && s.fixed_probe) \
     return probe_fixed_launch<TT, DD, GG, CC, PP, RR>(s, q, cb, bias, ksum, off, idx, force, sel, ncand, cellcnt, \
-                                                      bins, fuse, st);
+                                                      bins, fuse, ex, st);
   MDR_PROBE_FIXED_SHAPES(MDR_FIXED)
 #undef MDR_FIXED
   if (fuse) return hipErrorInvalidValue;  // only the specialised probe builds the lists itself
@@ -968,15 +1129,15 @@ hipError_t probe_dispatch(const Shape& s, const void* q, const float* cb, const 
   switch (s.D) {
     case 32:
       hipLaunchKernelGGL((k_probe_rerank<T, 32>), grid, dim3(kProbeThreads), lds, st, (const T*)q, cb, bias, ksum,
-                         off, idx, force, sel, ncand, cellcnt, bins, s);
+                         off, idx, force, sel, ncand, cellcnt, bins, ex, s);
       break;
     case 64:
       hipLaunchKernelGGL((k_probe_rerank<T, 64>), grid, dim3(kProbeThreads), lds, st, (const T*)q, cb, bias, ksum,
-                         off, idx, force, sel, ncand, cellcnt, bins, s);
+                         off, idx, force, sel, ncand, cellcnt, bins, ex, s);
       break;
     default:
       hipLaunchKernelGGL((k_probe_rerank<T, 128>), grid, dim3(kProbeThreads), lds, st, (const T*)q, cb, bias,
-                         ksum, off, idx, force, sel, ncand, cellcnt, bins, s);
+                         ksum, off, idx, force, sel, ncand, cellcnt, bins, ex, s);
       break;
   }
   return hipGetLastError();
@@ -985,10 +1146,11 @@ hipError_t probe_dispatch(const Shape& s, const void* q, const float* cb, const 
 }  // namespace
 
 hipError_t launch_address(const Shape& s, const void* k, const float* codebook, const float* bias, float* ksum,
-                          int32_t* addr, int32_t* cell_zero, hipStream_t st, int i0, int n) {
+                          int32_t* addr, int32_t* cell_zero, hipStream_t st, int i0, int n, int32_t* alt) {
   if (n < 0) n = s.nb - i0;
-  if (s.dtype == MDR_BF16) return address_dispatch<bf16>(s, k, codebook, bias, ksum, addr, cell_zero, i0, n, st);
-  return address_dispatch<float>(s, k, codebook, bias, ksum, addr, cell_zero, i0, n, st);
+  if (s.dtype == MDR_BF16)
+    return address_dispatch<bf16>(s, k, codebook, bias, ksum, addr, cell_zero, alt, i0, n, st);
+  return address_dispatch<float>(s, k, codebook, bias, ksum, addr, cell_zero, alt, i0, n, st);
 }
 
 bool probe_fixed_shape(const Shape& s) {
@@ -1024,10 +1186,25 @@ hipError_t launch_post(const Shape& s, const int32_t* addr, int32_t* off, int32_
 hipError_t launch_probe_rerank(const Shape& s, const void* q, const float* codebook, const float* bias,
                                const float* ksum, const int32_t* off, const int32_t* idx, const int32_t* force,
                                int32_t* sel, int32_t* ncand, int32_t* cellcnt, int32_t* bins, hipStream_t st,
-                               const FusedPost* fuse) {
+                               const FusedPost* fuse, const ProbeExtra& ex) {
+  if (fuse && ex.roff) return hipErrorInvalidValue;  // redirect lists need the whole CSR first
   if (s.dtype == MDR_BF16)
-    return probe_dispatch<bf16>(s, q, codebook, bias, ksum, off, idx, force, sel, ncand, cellcnt, bins, fuse, st);
-  return probe_dispatch<float>(s, q, codebook, bias, ksum, off, idx, force, sel, ncand, cellcnt, bins, fuse, st);
+    return probe_dispatch<bf16>(s, q, codebook, bias, ksum, off, idx, force, sel, ncand, cellcnt, bins, fuse, ex, st);
+  return probe_dispatch<float>(s, q, codebook, bias, ksum, off, idx, force, sel, ncand, cellcnt, bins, fuse, ex, st);
+}
+
+hipError_t launch_post_redirect(const Shape& s, const int32_t* addr, const int32_t* alt, const int32_t* off,
+                                const int32_t* idx, int32_t* roff, int32_t* ridx, int32_t* rtime,
+                                int32_t* overflow, hipStream_t st) {
+  const size_t lds = ((size_t)s.A + 2 * (size_t)s.ne) * 4;
+  if (lds > 65536) {
+    hipError_t e = hipFuncSetAttribute((const void*)k_post_redirect, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(k_post_redirect, dim3(s.B * s.H), dim3(256), lds, st, addr, alt, off, idx, roff, ridx, rtime,
+                     overflow, s);
+  return hipGetLastError();
 }
 
 bool probe_fuses_post(const Shape& s) {

@@ -187,6 +187,17 @@ def runner_up_codes(ksum: np.ndarray, codebook: np.ndarray, bias, rdtype=np.floa
     return second, margin
 
 
+def runner_up_gap(ksum: np.ndarray, codebook: np.ndarray, bias, rdtype=np.float32) -> np.ndarray:
+    """Per block and subspace, second - third largest logit [nb, G] (inf when C < 3): how close the
+    runner-up choice itself is to a tie."""
+    G, C, _ = codebook.shape
+    lg = code_logits(ksum, codebook, bias, rdtype)
+    if C < 3:
+        return np.full(lg.shape[:2], INF)
+    srt = np.sort(lg.astype(np.float64), axis=2)
+    return srt[..., -2] - srt[..., -3]
+
+
 def alternate_addresses(codes: np.ndarray, second: np.ndarray, margin: np.ndarray, n_codes: int):
     """Alternate address of each block [nb] (-1 when C == 1) and the gap between the smallest and the
     next smallest subspace margin (the decision's own margin; inf with one subspace)."""

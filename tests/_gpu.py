@@ -17,10 +17,11 @@ NEAR = 1e-4
 TOL = {"f32": 1e-5, "bf16": 2e-2}
 
 
-def cfg_of(mdr, w):
+def cfg_of(mdr, w, policy="drop"):
     return mdr.config(batch=w.batch, seq=w.seq, heads=w.heads, head_dim=w.head_dim, width=w.width, block=w.block,
                       subspaces=w.subspaces, codes=w.codes, capacity=w.capacity, probes=w.probes,
-                      max_cand=w.max_cand, remote=w.remote, local=w.local, dtype=w.dtype, rope_base=w.rope_base)
+                      max_cand=w.max_cand, remote=w.remote, local=w.local, dtype=w.dtype, rope_base=w.rope_base,
+                      overflow_policy=policy)
 
 
 def io_dtype(w):
@@ -40,9 +41,9 @@ def host(t):
     return t.detach().float().cpu().numpy() if t.is_floating_point() else t.detach().cpu().numpy()
 
 
-def run_core(mdr, w, inp, force=None):
+def run_core(mdr, w, inp, force=None, policy="drop"):
     """mdr_routed_attention with every routing output requested; returns host arrays."""
-    cfg = cfg_of(mdr, w)
+    cfg = cfg_of(mdr, w, policy)
     dt = io_dtype(w)
     q, k, v = (dev(inp[n], dt) for n in ("q", "k", "v"))
     cb = dev(inp["codebook"], torch.float32)

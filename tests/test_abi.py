@@ -45,7 +45,7 @@ def test_library_exports_every_declared_symbol(mdr):
     lib = ctypes.CDLL(LIB)
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert mdr.mdr_abi_version() == 1
+    assert mdr.mdr_abi_version() == 2
 
 
 def _good(**over):
@@ -77,6 +77,7 @@ def test_valid_configs_pass(mdr):
     (dict(probes=0), 1),
     (dict(remote=-1), 1),
     (dict(dtype=7), 1),
+    (dict(overflow_policy=2), 1),
     (dict(probes=300, codes=16), 1),  # more probes than addresses (A = 256)
     (dict(head_dim=48), 2),
     (dict(block=16), 2),
@@ -116,9 +117,15 @@ def test_entry_points_validate_before_launching(mdr):
     assert bwd(c, p, p, p, p, p, p, p, p + 8, p, p, p, need, None) == 1       # misaligned dq
     assert bwd(c, p, p, p, None, p, p, p, p, p, p, p, need, None) == 1        # no selection with R > 0
     assert bwd(c, p, p, p, p, p, p, p, p, p, p, p, need - 1, None) == 3
-    assert lib.mdr_stage_post(c, None, p, p, p, None) == 1
-    assert lib.mdr_stage_address(c, p, p, None, p + 4, p, None) == 1
-    assert lib.mdr_stage_probe_rerank(c, p, p, None, p, p, p, None, None, None, None) == 1
+    assert lib.mdr_stage_post(c, None, None, p, p, None, None, None, p, None) == 1
+    assert lib.mdr_stage_address(c, p, p, None, p + 4, p, None, None) == 1
+    assert lib.mdr_stage_probe_rerank(c, p, p, None, p, p, p, None, None, None, None, None, None, None, None) == 1
+    red = mdr.config(**_good(overflow_policy="redirect"))
+    cr = ctypes.byref(red)
+    assert mdr.mdr_check_config(red) == 0
+    assert lib.mdr_stage_post(cr, p, None, p, p, p, p, p, p, None) == 1        # redirect needs alt
+    assert lib.mdr_stage_post(cr, p, p, p, p, None, p, p, p, None) == 1        # and the redirect lists
+    assert lib.mdr_stage_probe_rerank(cr, p, p, None, p, p, p, None, p, p, None, p, None, None, None) == 1
     mix = mdr.config(**_good(width=0))
     assert lib.mdr_mixer_forward(ctypes.byref(mix), p, p, p, p, p, p, None, p, None, p, 1 << 40, None) == 1
     assert mdr.mdr_status_string(3) == "MDR_ERR_WORKSPACE"
@@ -164,3 +171,14 @@ def test_decode_entry_points_validate_before_launching(mdr):
     assert lib.mdr_decode_step(c, p, p, p, p, None, None, 10, 0, p, None, p, n, None) == 1
     assert lib.mdr_decode_step(c, p, p, p, p, None, None, 10, 1, p + 2, None, p, n, None) == 1  # misaligned out
     assert lib.mdr_decode_step(c, p, p, p, p, None, None, 10, 1, p, None, p + 16, n, None) == 1  # state alignment
+
+
+def test_redirect_policy_is_prefill_only(mdr):
+    """The decode state has no redirect lists: a redirect config is rejected before any launch."""
+    red = mdr.config(**_good(overflow_policy="redirect"))
+    assert mdr.mdr_check_config(red) == 0
+    with pytest.raises(mdr.MdrError) as e:
+        mdr.mdr_decode_state_size(red)
+    assert e.value.status == 2
+    drop = mdr.mdr_workspace_size(mdr.config(**_good()))
+    assert mdr.mdr_workspace_size(red) > drop  # alternates and redirect lists
