@@ -18,7 +18,7 @@ against 8 TB/s), every kernel's time and bytes, the fitted timing exponent over
 
     python bench.py --ingest-pmc FETCH.csv WRITE.csv
 turns two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of
-``python bench.py --steps 3 --warmup 1 --calib-copy --no-cpu --no-sweep`` into
+``python bench.py --steps 3 --warmup 1 --calib-copy --no-cpu --no-sweep --no-decode --no-backward --no-stress`` into
 profiles/traffic_<workload>.json (per-launch HBM bytes of every kernel,
 scaled by what the counters read for a plain elementwise copy of known size).
 """
@@ -60,9 +60,9 @@ CALIB_BYTES = 512 << 20
 HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000  # hipEventDisableSystemFence (hip_runtime_api.h)
 PMC_COMMANDS = [  # run from the repository root on one MI355X, TMPDIR=/tmp
     "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmcf -o f -- "
-    "python3 bench.py --steps 3 --warmup 1 --calib-copy --no-cpu --no-sweep",
+    "python3 bench.py --steps 3 --warmup 1 --calib-copy --no-cpu --no-sweep --no-decode --no-backward --no-stress",
     "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmcw -o w -- "
-    "python3 bench.py --steps 3 --warmup 1 --calib-copy --no-cpu --no-sweep",
+    "python3 bench.py --steps 3 --warmup 1 --calib-copy --no-cpu --no-sweep --no-decode --no-backward --no-stress",
 ]
 
 
@@ -78,6 +78,7 @@ def parse(argv=None):
     ap.add_argument("--no-sweep", action="store_true", help="skip the 4K-32K exponent sweep")
     ap.add_argument("--no-decode", action="store_true", help="skip the streaming-decode timing")
     ap.add_argument("--no-backward", action="store_true", help="skip the attention-backward timing")
+    ap.add_argument("--no-stress", action="store_true", help="skip the overflow stress test")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run one elementwise copy of 512 MiB first (counter calibration)")
     ap.add_argument("--cpu-heads", type=int, default=8)
@@ -154,22 +155,24 @@ def describe(w):
 class Run:
     """Device inputs, workspace and routing buffers of one workload."""
 
-    def __init__(self, mdr, w, seed):
+    def __init__(self, mdr, w, seed, policy="drop", bias=None, inputs=None):
         import torch
 
         import synth
 
         self.w = w
         self.mdr = mdr
-        inp = synth.make_core_inputs(w, seed)
+        inp = synth.make_core_inputs(w, seed) if inputs is None else inputs
         dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
         self.q, self.k, self.v = (torch.from_numpy(inp[n]).to("cuda").to(dt) for n in ("q", "k", "v"))
         self.cb = torch.from_numpy(inp["codebook"]).cuda()
-        self.bias = None if inp["bias"] is None else torch.from_numpy(inp["bias"]).cuda()
+        b = inp["bias"] if bias is None else bias
+        self.bias = None if b is None else torch.from_numpy(b).cuda()
         self.out = torch.empty_like(self.q)
         self.cfg = mdr.config(batch=w.batch, seq=w.seq, heads=w.heads, head_dim=w.head_dim, block=w.block,
                               subspaces=w.subspaces, codes=w.codes, capacity=w.capacity, probes=w.probes,
-                              max_cand=w.max_cand, remote=w.remote, local=w.local, dtype=w.dtype)
+                              max_cand=w.max_cand, remote=w.remote, local=w.local, dtype=w.dtype,
+                              overflow_policy=policy)
         self.ws = mdr.workspace(self.cfg)
         self.rt = mdr.routing_buffers(self.cfg)
         self.inputs = inp
@@ -440,6 +443,72 @@ def backward_bench(run, hip, overhead, steps=20, warmup=3):
             "mfma_frac": round(flops / (total * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS[w.dtype], 4)}
 
 
+def overflow_stress(mdr, seed, steps=20, warmup=3):
+    """The overflow stress test the pages ask for (remio.ai, "What sparse attention researchers
+    should watch next"): skewed code biases -kappa ln(c + 1) send many blocks and queries to few
+    addresses; for the drop and redirect policies report overflow, dropped candidates per token,
+    candidates per token, the step time's spread, and route recall of a planted block.
+      skew shape:   B2 H8 S16384 D128 block 64, 3x8 codes, capacity 8, P6, R8, bf16, kappa 0 .. 1
+      recall shape: B16 H4 S2048 D64 block 64, 2x8 codes, capacity 2, P16, M5, R2, fp32; route recall =
+                    share of the last query block's tokens whose selection holds the planted block."""
+    import numpy as np
+    import torch
+
+    import synth
+
+    def timed(run):
+        for _ in range(warmup):
+            run.step()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        torch.cuda.synchronize()
+        ev[0].record()
+        for i in range(steps):
+            run.step()
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        ms = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(steps)])
+        return [round(float(x), 4) for x in np.percentile(ms, [10, 50, 90])] + [round(float(ms.max()), 4)]
+
+    out = {"skew": [], "recall": []}
+    ws = make_workload("skew", 0)
+    ws = __import__("dataclasses").replace(ws, batch=2, heads=8)
+    inp = synth.make_core_inputs(ws, seed)
+    for kappa in (0.0, 0.11, 0.5, 1.0):
+        bias = synth.zipf_code_bias(ws.heads, ws.subspaces, ws.codes, kappa)
+        row = {"kappa": kappa}
+        for policy in ("drop", "redirect"):
+            run = Run(mdr, ws, seed, policy, bias=bias, inputs=inp)
+            q = timed(run)
+            rt = run.rt
+            row[policy] = {"overflow": int(rt["overflow"].sum().item()),
+                           "dropped_per_token": round(float(rt["n_drop"].float().mean().item()), 3),
+                           "cand_per_token": round(float(rt["n_cand"].float().mean().item()), 3),
+                           "step_ms_p10_p50_p90_max": q}
+            del run
+        out["skew"].append(row)
+    wr = __import__("dataclasses").replace(make_workload("recall", 0), capacity=2)
+    inp = synth.make_core_inputs(wr, seed)
+    planted = torch.from_numpy(inp["planted"]).cuda().long()
+    last = slice((wr.nblocks - 1) * wr.block, wr.seq)
+    for kappa in (0.0, 0.5, 1.0, 2.0):
+        bias = synth.zipf_code_bias(wr.heads, wr.subspaces, wr.codes, kappa)
+        row = {"kappa": kappa}
+        for policy in ("drop", "redirect"):
+            run = Run(mdr, wr, seed, policy, bias=bias, inputs=inp)
+            run.step()
+            torch.cuda.synchronize()
+            sel = run.rt["sel"][:, :, last].long()
+            hit = (sel == planted[:, None, None, None]).any(dim=-1)
+            row[policy] = {"route_recall": round(float(hit.float().mean().item()), 4),
+                           "overflow": int(run.rt["overflow"].sum().item()),
+                           "dropped_per_token": round(float(run.rt["n_drop"].float().mean().item()), 3)}
+            del run
+        out["recall"].append(row)
+    out["note"] = ("synthetic keys and untrained random codebooks: the recall figures describe the overflow "
+                   "mechanism, not the pages' trained-router result")
+    return out
+
+
 def cpu_baseline(run, heads):
     """The oracle as it stands (routing + gathered fp64 attention), one thread, on a bounded sample."""
     import numpy as np
@@ -634,6 +703,8 @@ def main(argv=None):
         res["decode"] = [decode_bench(run, b) for b in (1, 16)]
     if not a.no_backward:
         res["backward"] = backward_bench(run, hip, ev_overhead)
+    if not a.no_stress and a.workload == "sweep":
+        res["overflow_stress"] = overflow_stress(mdr, a.seed)
     if not a.no_sweep and a.workload == "sweep":
         res["exponent"] = exponent_sweep(mdr, (4096, 8192, 16384, 32768), a.seed)
     if not a.no_cpu:

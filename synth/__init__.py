@@ -15,4 +15,5 @@ from .gen import (  # noqa: F401
     make_grad_inputs,
     make_mixer_inputs,
     workload,
+    zipf_code_bias,
 )

@@ -118,6 +118,14 @@ def bf16_round(x: np.ndarray) -> np.ndarray:
     return x
 
 
+def zipf_code_bias(H: int, G: int, C: int, kappa: float) -> np.ndarray:
+    """Code bias -kappa * ln(c + 1) for every head and subspace [H, G, C] float32: the larger kappa,
+    the more the low codes (and so a few addresses) attract blocks and queries."""
+    c = np.arange(C, dtype=np.float64)
+    row = (-kappa * np.log(c + 1.0)).astype(np.float32)
+    return np.broadcast_to(row, (H, G, C)).copy()
+
+
 def _normal(rng, shape, std=1.0):
     a = rng.standard_normal(size=shape, dtype=np.float32)
     if std != 1.0:
@@ -179,9 +187,7 @@ def make_core_inputs(w: Workload, seed: int) -> dict:
             k[:, h] += np.repeat(push.astype(np.float32), blk, axis=0)[None]
         out["target_addr"] = target
     elif w.plant == "zipf":
-        c = np.arange(C, dtype=np.float64)
-        row = (-w.zipf_kappa * np.log(c + 1.0)).astype(np.float32)
-        bias = np.broadcast_to(row, (H, G, C)).copy()
+        bias = zipf_code_bias(H, G, C, w.zipf_kappa)
     elif w.plant != "none":
         raise ValueError(f"unknown plant {w.plant!r}")
     if w.dtype == "bf16":
