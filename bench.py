@@ -50,6 +50,10 @@ KERNEL_SOURCE = {
     "address": "mdr_route.hip", "post": "mdr_route.hip", "probe_rerank": "mdr_route.hip",
     "attn_remote": "mdr_attn.hip", "attn_local": "mdr_attn.hip",
 }
+MIXER_SYMBOL = {
+    "qkv (fused projections + RoPE + summaries + addresses)": "k_qkv",
+    "output projection": "k_gemm",
+}
 BACKWARD_SYMBOL = {
     "pair_bin": "k_pair_bin_ordered",
     "bwd_dot": "k_bwd_dot",
@@ -79,6 +83,10 @@ def parse(argv=None):
     ap.add_argument("--no-decode", action="store_true", help="skip the streaming-decode timing")
     ap.add_argument("--no-backward", action="store_true", help="skip the attention-backward timing")
     ap.add_argument("--no-stress", action="store_true", help="skip the overflow stress test")
+    ap.add_argument("--no-mixer", action="store_true", help="skip the mixer timing")
+    ap.add_argument("--mixer-only", action="store_true", help="time the mixer alone and print its JSON")
+    ap.add_argument("--profile-name", default="routed_attention_kernels",
+                    help="with --summarize-rocprof: file name stem of the summary under profiles/")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run one elementwise copy of 512 MiB first (counter calibration)")
     ap.add_argument("--cpu-heads", type=int, default=8)
@@ -509,6 +517,46 @@ def overflow_stress(mdr, seed, steps=20, warmup=3):
     return out
 
 
+def mixer_bench(mdr, hip, seed, steps=20, warmup=3):
+    """The stateless mixer [B, S, W] -> delta on the 32K sweep shape with width H*D = 512: the fused
+    Q/K/V projection (RoPE, block summaries and addresses in its epilogue), the core, the output
+    projection.  Timed per call with HIP events; projection flops 2 * B*S * W * 3HD (+ 2 * B*S * HD * W)."""
+    import dataclasses
+
+    import torch
+
+    import synth
+
+    w = dataclasses.replace(make_workload("sweep", 0), width=512)
+    inp = synth.make_mixer_inputs(w, seed)
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    t = {n: torch.from_numpy(inp[n]).to("cuda").to(dt) for n in ("x", "wq", "wk", "wv", "wo")}
+    cb = torch.from_numpy(inp["codebook"]).cuda()
+    cfg = mdr.config(batch=w.batch, seq=w.seq, heads=w.heads, head_dim=w.head_dim, width=w.width, block=w.block,
+                     subspaces=w.subspaces, codes=w.codes, capacity=w.capacity, probes=w.probes,
+                     max_cand=w.max_cand, remote=w.remote, local=w.local, dtype=w.dtype, rope_base=w.rope_base)
+    ws = mdr.workspace(cfg)
+    delta = torch.empty_like(t["x"])
+    call = lambda: mdr.mdr_mixer_forward(cfg, t["x"], t["wq"], t["wk"], t["wv"], t["wo"], cb, None, delta, None, ws)
+    for _ in range(warmup):
+        call()
+    ev = hip.create(2)
+    stream = torch.cuda.current_stream().cuda_stream
+    torch.cuda.synchronize()
+    hip.record(ev[0], stream)
+    for _ in range(steps):
+        call()
+    hip.record(ev[1], stream)
+    torch.cuda.synchronize()
+    ms = hip.elapsed_ms(ev[0], ev[1]) / steps
+    hip.destroy(ev)
+    M, HD = w.batch * w.seq, w.heads * w.head_dim
+    return {"workload": f"mixer B{w.batch} S{w.seq} W{w.width} H{w.heads} D{w.head_dim} block{w.block} "
+                        f"{w.subspaces}x{w.codes} codes cap{w.capacity} P{w.probes} R{w.remote} L{w.local} {w.dtype}",
+            "ms_per_call": round(ms, 4), "tokens_per_s": round(M / (ms * 1e-3), 1),
+            "projection_flops": 2 * M * w.width * 3 * HD + 2 * M * HD * w.width}
+
+
 def cpu_baseline(run, heads):
     """The oracle as it stands (routing + gathered fp64 attention), one thread, on a bounded sample."""
     import numpy as np
@@ -586,7 +634,7 @@ def ingest_pmc(fetch_csv, write_csv, w):
 
 # ----------------------------------------------------------------------------- main
 
-def summarize_rocprof(stats_csv, command, w, bench_log=None):
+def summarize_rocprof(stats_csv, command, w, bench_log=None, stem="routed_attention_kernels"):
     """Short markdown table of the library's kernels from a rocprofv3 kernel_stats.csv, with the
     HIP-event averages bench.py printed in the same run (bench_log: its stdout) beside them."""
     rows = list(csv.DictReader(open(stats_csv)))
@@ -623,10 +671,20 @@ def summarize_rocprof(stats_csv, command, w, bench_log=None):
         lines += ["", "Backward (mdr_stage_attend_backward on the forward's selection):", "",
                   "| kernel | calls | avg us | min us | max us | share of GPU time | bench.py HIP-event avg us |",
                   "|---|---|---|---|---|---|---|"] + bl
-    known = list(KERNEL_SYMBOL.values()) + list(BACKWARD_SYMBOL.values())
+    ml = []
+    for k, sym in MIXER_SYMBOL.items():
+        for r in rows:
+            if sym in r["Name"]:
+                ml.append(f"| {k} (`{sym}`) | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                          f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                          f"{float(r['Percentage']):.1f}% |")
+    if ml:
+        lines += ["", "Mixer (mdr_mixer_forward at width 512; its core kernels are counted in the table above):", "",
+                  "| kernel | calls | avg us | min us | max us | share of GPU time |", "|---|---|---|---|---|---|"] + ml
+    known = list(KERNEL_SYMBOL.values()) + list(BACKWARD_SYMBOL.values()) + list(MIXER_SYMBOL.values())
     other = sum(float(r["Percentage"]) for r in rows if not any(sym in r["Name"] for sym in known))
     lines += ["", f"Other kernels (input generation, torch copies, routing statistics): {other:.1f}% of GPU time.", ""]
-    out = os.path.join(ROOT, "profiles", f"routed_attention_kernels_{w.name}_{w.seq // 1024}k.md")
+    out = os.path.join(ROOT, "profiles", f"{stem}_{w.name}_{w.seq // 1024}k.md")
     os.makedirs(os.path.dirname(out), exist_ok=True)
     open(out, "w").write("\n".join(lines))
     print(open(out).read())
@@ -639,7 +697,7 @@ def main(argv=None):
         ingest_pmc(*a.ingest_pmc, w)
         return 0
     if a.summarize_rocprof:
-        summarize_rocprof(*a.summarize_rocprof, w, a.bench_log)
+        summarize_rocprof(*a.summarize_rocprof, w, a.bench_log, a.profile_name)
         return 0
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print(json.dumps({"error": "this build runs on one GPU only: the path shards over (batch, head) with no "
@@ -652,6 +710,9 @@ def main(argv=None):
 
     torch.cuda.init()
     hip = HipEvents()
+    if a.mixer_only:
+        print(json.dumps({"mixer": mixer_bench(mdr, hip, a.seed)}))
+        return 0
     if a.calib_copy:
         src = torch.empty(CALIB_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
         dst = torch.empty_like(src)
@@ -703,6 +764,8 @@ def main(argv=None):
         res["decode"] = [decode_bench(run, b) for b in (1, 16)]
     if not a.no_backward:
         res["backward"] = backward_bench(run, hip, ev_overhead)
+    if not a.no_mixer and a.workload == "sweep":
+        res["mixer"] = mixer_bench(mdr, hip, a.seed)
     if not a.no_stress and a.workload == "sweep":
         res["overflow_stress"] = overflow_stress(mdr, a.seed)
     if not a.no_sweep and a.workload == "sweep":

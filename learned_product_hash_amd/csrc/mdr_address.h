@@ -38,31 +38,23 @@ struct AddressLds {
   float logit[kMaxCodesTotal];
 };
 
-// All 256 threads of the work-group call it (it contains barriers).  The codebook rows are
-// requested together with the key rows: four adjacent lanes share one code (each a quarter of D,
-// added in a fixed order), and one wave takes each subspace's argmax with a butterfly over
-// (logit, code).  Writes ksum[bh, i, :] and addr[bh, i], and when `alt` is given the block's
-// alternate address: in the subspace with the smallest fp32 margin top1 - top2 (ties to the
-// smaller subspace) the runner-up code (the best of the others, smaller code on ties) replaces the
-// top code; -1 when C == 1.
-template <typename T, int D>
-__device__ __forceinline__ void block_address(const T* __restrict__ K, const float* __restrict__ cb,
-                                              const float* __restrict__ bias, float* __restrict__ ksum,
-                                              int32_t* __restrict__ addr, int i, int bh, AddressLds<T, D>& sm,
-                                              const Shape& s, int32_t* __restrict__ alt = nullptr) {
-  constexpr int VEC = Vec16<T>::n;
-  constexpr int NCH = AddressLds<T, D>::NCH;
-  constexpr int RG = AddressLds<T, D>::RG;
-  constexpr int LPC = 256 / kMaxCodesTotal;  // lanes per code
-  constexpr int DPL = D / LPC;               // codebook dims per lane
+// The codebook slice one thread of a 256-thread work-group holds for the logits: four adjacent
+// lanes share one code cc (of the G*C codes of head h), each a quarter of D.  Requested early so
+// that it arrives while the keys are read.
+template <int D>
+struct CodeSlice {
+  static constexpr int LPC = 256 / kMaxCodesTotal;  // lanes per code
+  static constexpr int DPL = D / LPC;               // codebook dims per lane
   static_assert(DPL % 4 == 0, "whole float4 per lane");
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int h = bh % s.H;
-  const int GC = s.G * s.C;
-  // codebook slice of this lane: code cc, dims [part * DPL, (part + 1) * DPL)
-  const int cc = tid / LPC, part = tid % LPC;
   float w[DPL];
-  {
+  float bv;
+  int cc, part;
+  __device__ __forceinline__ void load(const float* __restrict__ cb, const float* __restrict__ bias, int h,
+                                       const Shape& s) {
+    const int tid = threadIdx.x;
+    const int GC = s.G * s.C;
+    cc = tid / LPC;
+    part = tid % LPC;
     const float* wr = cb + ((size_t)h * GC + (cc < GC ? cc : 0)) * D + part * DPL;
 #pragma unroll
     for (int d = 0; d < DPL; d += 4) {
@@ -72,8 +64,99 @@ __device__ __forceinline__ void block_address(const T* __restrict__ K, const flo
       w[d + 2] = v.z;
       w[d + 3] = v.w;
     }
+    bv = (bias && cc < GC) ? bias[h * GC + cc] : 0.f;
   }
-  const float bv = (bias && cc < GC) ? bias[h * GC + cc] : 0.f;
+};
+
+// Address (and optional alternate) of one block from its summary kbar (LDS, D floats): the code
+// logits <codebook[h,g,c], kbar> + bias (the four lanes of a code each add a quarter of D in a fixed
+// order), then one wave takes each subspace's argmax with a butterfly over (logit, code).  All 256
+// threads call it (it contains a barrier); `logit` is LDS scratch of kMaxCodesTotal floats.  Thread
+// 0 writes *addr_out and, when given, *alt_out: in the subspace with the smallest fp32 margin
+// top1 - top2 (ties to the smaller subspace) the runner-up code (the best of the others, smaller
+// code on ties) replaces the top code; -1 when C == 1.
+template <int D>
+__device__ __forceinline__ void address_from_summary(const CodeSlice<D>& cs, const float* kbar, float* logit,
+                                                     int32_t* __restrict__ addr_out, int32_t* __restrict__ alt_out,
+                                                     const Shape& s) {
+  constexpr int LPC = CodeSlice<D>::LPC, DPL = CodeSlice<D>::DPL;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int GC = s.G * s.C;
+  {
+    float acc = 0.f;
+#pragma unroll
+    for (int d = 0; d < DPL; ++d) acc = fmaf(cs.w[d], kbar[cs.part * DPL + d], acc);
+#pragma unroll
+    for (int x = 1; x < LPC; x <<= 1) acc += __shfl_xor(acc, x);
+    if (cs.part == 0 && cs.cc < GC) logit[cs.cc] = acc + cs.bv;
+  }
+  __syncthreads();
+  if (tid < 64) {
+    int a = 0;
+    float best_m = INFINITY;
+    int gs = -1, dc = 0;  // subspace of the smallest margin, runner-up code minus top code
+    for (int g = 0; g < s.G; ++g) {
+      // lanes 0..C-1 hold the subspace's logits; the butterfly keeps the larger logit, the
+      // smaller code on ties
+      const float lv = lane < s.C ? logit[g * s.C + lane] : -INFINITY;
+      float v = lv;
+      int c = lane < s.C ? lane : 0x7fffffff;
+#pragma unroll
+      for (int x = 32; x >= 1; x >>= 1) {
+        const float ov = __shfl_xor(v, x);
+        const int oc = __shfl_xor(c, x);
+        if (ov > v || (ov == v && oc < c)) {
+          v = ov;
+          c = oc;
+        }
+      }
+      a = a * s.C + c;
+      if (alt_out) {
+        float v2 = (lane < s.C && lane != c) ? lv : -INFINITY;
+        int c2 = (lane < s.C && lane != c) ? lane : 0x7fffffff;
+#pragma unroll
+        for (int x = 32; x >= 1; x >>= 1) {
+          const float ov = __shfl_xor(v2, x);
+          const int oc = __shfl_xor(c2, x);
+          if (ov > v2 || (ov == v2 && oc < c2)) {
+            v2 = ov;
+            c2 = oc;
+          }
+        }
+        const float m = v - v2;  // +inf when C == 1
+        if (m < best_m) {
+          best_m = m;
+          gs = g;
+          dc = c2 - c;
+        }
+      }
+    }
+    if (tid == 0) {
+      *addr_out = a;
+      if (alt_out) {
+        int pw = 1;  // place value of subspace gs (subspace 0 most significant)
+        for (int g = gs + 1; g < s.G; ++g) pw *= s.C;
+        *alt_out = gs >= 0 ? a + dc * pw : -1;
+      }
+    }
+  }
+}
+
+// All 256 threads of the work-group call it (it contains barriers).  The codebook rows are
+// requested together with the key rows.  Writes ksum[bh, i, :] and addr[bh, i], and when `alt` is
+// given the block's alternate address (see address_from_summary).
+template <typename T, int D>
+__device__ __forceinline__ void block_address(const T* __restrict__ K, const float* __restrict__ cb,
+                                              const float* __restrict__ bias, float* __restrict__ ksum,
+                                              int32_t* __restrict__ addr, int i, int bh, AddressLds<T, D>& sm,
+                                              const Shape& s, int32_t* __restrict__ alt = nullptr) {
+  constexpr int VEC = Vec16<T>::n;
+  constexpr int NCH = AddressLds<T, D>::NCH;
+  constexpr int RG = AddressLds<T, D>::RG;
+  const int tid = threadIdx.x;
+  const int h = bh % s.H;
+  CodeSlice<D> cs;
+  cs.load(cb, bias, h, s);
   const T* base = K + ((size_t)bh * s.S + (size_t)i * s.blk) * D;
   const int ch = tid % NCH, rg = tid / NCH;
   float acc4[VEC];
@@ -95,64 +178,8 @@ __device__ __forceinline__ void block_address(const T* __restrict__ K, const flo
     ksum[((size_t)bh * s.nb + i) * D + tid] = m;
   }
   __syncthreads();
-  {
-    float acc = 0.f;
-#pragma unroll
-    for (int d = 0; d < DPL; ++d) acc = fmaf(w[d], sm.kbar[part * DPL + d], acc);
-#pragma unroll
-    for (int x = 1; x < LPC; x <<= 1) acc += __shfl_xor(acc, x);
-    if (part == 0 && cc < GC) sm.logit[cc] = acc + bv;
-  }
-  __syncthreads();
-  if (tid < 64) {
-    int a = 0;
-    float best_m = INFINITY;
-    int gs = -1, dc = 0;  // subspace of the smallest margin, runner-up code minus top code
-    for (int g = 0; g < s.G; ++g) {
-      // lanes 0..C-1 hold the subspace's logits; the butterfly keeps the larger logit, the
-      // smaller code on ties
-      const float lv = lane < s.C ? sm.logit[g * s.C + lane] : -INFINITY;
-      float v = lv;
-      int c = lane < s.C ? lane : 0x7fffffff;
-#pragma unroll
-      for (int x = 32; x >= 1; x >>= 1) {
-        const float ov = __shfl_xor(v, x);
-        const int oc = __shfl_xor(c, x);
-        if (ov > v || (ov == v && oc < c)) {
-          v = ov;
-          c = oc;
-        }
-      }
-      a = a * s.C + c;
-      if (alt) {
-        float v2 = (lane < s.C && lane != c) ? lv : -INFINITY;
-        int c2 = (lane < s.C && lane != c) ? lane : 0x7fffffff;
-#pragma unroll
-        for (int x = 32; x >= 1; x >>= 1) {
-          const float ov = __shfl_xor(v2, x);
-          const int oc = __shfl_xor(c2, x);
-          if (ov > v2 || (ov == v2 && oc < c2)) {
-            v2 = ov;
-            c2 = oc;
-          }
-        }
-        const float m = v - v2;  // +inf when C == 1
-        if (m < best_m) {
-          best_m = m;
-          gs = g;
-          dc = c2 - c;
-        }
-      }
-    }
-    if (tid == 0) {
-      addr[(size_t)bh * s.nb + i] = a;
-      if (alt) {
-        int pw = 1;  // place value of subspace gs (subspace 0 most significant)
-        for (int g = gs + 1; g < s.G; ++g) pw *= s.C;
-        alt[(size_t)bh * s.nb + i] = gs >= 0 ? a + dc * pw : -1;
-      }
-    }
-  }
+  address_from_summary<D>(cs, sm.kbar, sm.logit, addr + (size_t)bh * s.nb + i,
+                          alt ? alt + (size_t)bh * s.nb + i : nullptr, s);
 }
 
 }  // namespace mdr

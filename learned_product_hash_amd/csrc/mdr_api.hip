@@ -114,8 +114,9 @@ size_t layout(const Shape& s, char* base, Buffers* b) {
     t.mk = take(qkv);
     t.mv = take(qkv);
     t.mo = take(qkv);
+    t.mwt = take(4 * (size_t)s.W * s.H * s.D * e);
   } else {
-    t.mq = t.mk = t.mv = t.mo = nullptr;
+    t.mq = t.mk = t.mv = t.mo = t.mwt = nullptr;
   }
   t.lse = nullptr;
   if (b) *b = t;
@@ -208,13 +209,17 @@ bool routing_aligned(const mdr_routing* r) {
 
 // The four stages of the core on post-RoPE q, k, v already in device memory.
 // ev (optional, MDR_CORE_KERNELS + 1 entries): recorded before each kernel and after the last.
+// have_address: the summaries, addresses (and alternates) and cleared cell counters are already in
+// the buffers (the mixer's fused projection wrote them).
 mdr_status run_core(const Shape& s, const void* q, const void* k, const void* v, const float* cb, const float* bias,
-                    const int32_t* force, void* out, const Buffers& b, hipStream_t st, hipEvent_t* ev = nullptr) {
+                    const int32_t* force, void* out, const Buffers& b, hipStream_t st, hipEvent_t* ev = nullptr,
+                    bool have_address = false) {
   const bool remote = s.R > 0 && s.ne > 0;
   if (ev) MDR_TRY(hipEventRecord(ev[0], st));
   const bool redirect = s.policy == MDR_OVERFLOW_REDIRECT;
-  MDR_TRY(launch_address(s, k, cb, bias, b.ksum, b.addr, remote ? b.cellcnt : nullptr, st, 0, -1,
-                         redirect ? b.alt : nullptr));
+  if (!have_address)
+    MDR_TRY(launch_address(s, k, cb, bias, b.ksum, b.addr, remote ? b.cellcnt : nullptr, st, 0, -1,
+                           redirect ? b.alt : nullptr));
   if (ev) MDR_TRY(hipEventRecord(ev[1], st));
   // the posting lists are built inside the probe kernel where a specialised probe exists (the post
   // interval of a profiled call is then empty); the redirect lists need the whole CSR first
@@ -316,12 +321,20 @@ mdr_status mdr_mixer_forward(const mdr_config* cfg, const void* x, const void* w
   if (st != MDR_OK) return st;
   apply_routing(routing, &b);
   hipStream_t hs = (hipStream_t)stream;
-  MDR_TRY(launch_project_heads(s, x, wq, b.mq, true, hs));
-  MDR_TRY(launch_project_heads(s, x, wk, b.mk, true, hs));
-  MDR_TRY(launch_project_heads(s, x, wv, b.mv, false, hs));
-  st = run_core(s, b.mq, b.mk, b.mv, codebook, code_bias, nullptr, b.mo, b, hs);
+  const bool fused = qkv_fuses_address(s);
+  if (fused) {
+    const bool remote = s.R > 0 && s.ne > 0;
+    MDR_TRY(launch_qkv_fused(s, x, wq, wk, wv, b.mq, b.mk, b.mv, codebook, code_bias, b.ksum, b.addr,
+                             s.policy == MDR_OVERFLOW_REDIRECT ? b.alt : nullptr, remote ? b.cellcnt : nullptr,
+                             b.mwt, hs));
+  } else {
+    MDR_TRY(launch_project_heads(s, x, wq, b.mq, true, hs));
+    MDR_TRY(launch_project_heads(s, x, wk, b.mk, true, hs));
+    MDR_TRY(launch_project_heads(s, x, wv, b.mv, false, hs));
+  }
+  st = run_core(s, b.mq, b.mk, b.mv, codebook, code_bias, nullptr, b.mo, b, hs, nullptr, fused);
   if (st != MDR_OK) return st;
-  MDR_TRY(launch_project_out(s, b.mo, wo, delta, hs));
+  MDR_TRY(launch_project_out(s, b.mo, wo, delta, b.mwt, hs));
   return MDR_OK;
 }
 

@@ -55,6 +55,7 @@ struct Buffers {
   void* mk;
   void* mv;
   void* mo;
+  void* mwt;           // mixer: Wq, Wk, Wv transposed ([H*D][W] each), then Wo transposed ([W][H*D])
   float* lse;          // [B,H,S] optional output of the attention: log2 of each token's softmax
                        // normaliser sum_s 2^(scale log2(e) q.k_s) (nullptr: not written)
   float* dvec;         // [B,H,S] backward: D_t = dO_t . O_t
@@ -220,7 +221,15 @@ hipError_t launch_attend_backward(const Shape& s, const void* q, const void* k, 
                                   const Buffers& b, hipStream_t st, hipEvent_t* ev = nullptr);
 hipError_t launch_project_heads(const Shape& s, const void* x, const void* w, void* out, bool rope,
                                 hipStream_t st);
-hipError_t launch_project_out(const Shape& s, const void* o, const void* wo, void* delta,
+// wt (optional): workspace for the transposed weights (4 * W * H * D elements); without it the
+// simple tiled product is used.
+hipError_t launch_project_out(const Shape& s, const void* o, const void* wo, void* delta, void* wt,
                               hipStream_t st);
+// Q, K, V projections with RoPE, block summaries and addresses (and alternates when alt is given)
+// fused into one launch; cell_zero (optional) as for launch_address.  Only when qkv_fuses_address.
+bool qkv_fuses_address(const Shape& s);
+hipError_t launch_qkv_fused(const Shape& s, const void* x, const void* wq, const void* wk, const void* wv, void* q,
+                            void* k, void* v, const float* cb, const float* bias, float* ksum, int32_t* addr,
+                            int32_t* alt, int32_t* cell_zero, void* wt, hipStream_t st);
 
 }  // namespace mdr

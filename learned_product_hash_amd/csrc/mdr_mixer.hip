@@ -10,6 +10,13 @@
 //            [B,H,S,D] layout (as a [B*S, H*D] matrix) and C written to it.
 //   k_rope   in place on [B,H,S,D]: pairs (i, i + D/2) rotate by pos * base^(-2i/D); the angle
 //            and its sine/cosine are taken in double so fp32 outputs keep full precision.
+//   k_mm     C = A B with register-prefetched 64 x NT tiles; as the fused projection it computes Q, K
+//            and V in one launch and, in its epilogue, applies RoPE to Q and K, stores whole rows, and
+//            for K forms each block's summary (the mean of the block's stored key rows) and its
+//            product address -- the address stage of the core then has nothing left to do (blocks of
+//            up to 64 tokens and widths divisible by 8; otherwise k_gemm, k_rope and the address
+//            kernel); as the output projection it reads the head-split O directly.
+#include "mdr_address.h"
 #include "mdr_internal.h"
 
 #include <type_traits>
@@ -17,6 +24,8 @@
 namespace mdr {
 
 namespace {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 struct HeadMap {
   int S, H, D;
@@ -114,6 +123,291 @@ __global__ __launch_bounds__(256) void k_rope(T* __restrict__ X, long long rows,
   }
 }
 
+// C = A B on MFMA for 64 x NT output tiles, 256 threads (2 x 2 waves of 32 x NT/2), contraction
+// steps of KT (64 bf16 / 32 fp32): the next step's A and B tiles are read into registers while the
+// current step is multiplied out of LDS.  B is passed transposed ([n][k], k contiguous: the mixer
+// transposes its weights once per call), so both tiles are plain 16-byte row copies into LDS.  The
+// tile then goes through LDS once more so that every row leaves as 16-byte vectors.
+//   AHEADS  A is the head-split [B,H,S,D] layout read as a [B*S, H*D] matrix
+//   QKV     three products at once (B0/B1/B2 = Wq/Wk/Wv, C0/C1/C2 = Q/K/V in [B,H,S,D]); the
+//           epilogue applies RoPE to Q and K and, for K, forms each block's summary from the stored
+//           rows and its product address (and alternate) with address_from_summary
+// Requires Kd % (16 / sizeof(T)) == 0 and Nm % NT == 0 (with NT % D == 0 for QKV).
+struct QkvEpilogue {
+  const float* cb;
+  const float* bias;
+  float* ksum;
+  int32_t* addr;
+  int32_t* alt;
+  int32_t* cell_zero;
+};
+
+template <typename T, int NT, bool AHEADS, bool QKV, int D>
+__global__ __launch_bounds__(256) void k_mm(const T* __restrict__ A, const T* __restrict__ B0,
+                                            const T* __restrict__ B1, const T* __restrict__ B2, T* __restrict__ C0,
+                                            T* __restrict__ C1, T* __restrict__ C2, int M, int Nm, int Kd, HeadMap hm,
+                                            QkvEpilogue ep, Shape s) {
+  constexpr bool bf = std::is_same<T, bf16>::value;
+  constexpr int VEC = 16 / (int)sizeof(T);
+  constexpr int KT = bf ? 64 : 32;
+  constexpr int KS = KT + VEC;                 // LDS row stride: 16 bytes of padding
+  constexpr int TJ = NT / 32;                  // 16-column tiles per wave
+  constexpr int AR = 64 * KT / VEC / 256;      // A vectors per thread per step
+  constexpr int BR = KT * NT / VEC / 256;      // B vectors per thread per step
+  static_assert(AR >= 1 && BR >= 1 && 64 * KT / VEC % 256 == 0 && KT * NT / VEC % 256 == 0, "whole vectors");
+  constexpr int CST = NT + 1;                  // output tile row stride (floats)
+  constexpr size_t STAGE = (size_t)(64 + NT) * KS * sizeof(T);
+  constexpr size_t EPIB = (size_t)64 * CST * 4;
+  __shared__ __align__(16) char smem[STAGE > EPIB ? STAGE : EPIB];
+  T* As = (T*)smem;
+  T* Bt = As + 64 * KS;
+  float* Cs = (float*)smem;  // after the main loop
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int m0 = blockIdx.x * 64;
+  const int ng = blockIdx.y * NT;
+  const int which = QKV ? ng / Nm : 0, n0 = QKV ? ng % Nm : ng;
+  const T* Bm = which == 0 ? B0 : which == 1 ? B1 : B2;
+  T* Cm = which == 0 ? C0 : which == 1 ? C1 : C2;
+  const int wm = (wave >> 1) * 32, wn = (wave & 1) * (NT / 2);
+  const int sl = lane >> 4, r = lane & 15;
+  f32x4 acc[2][TJ];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < TJ; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  u32x4 ar[AR], br[BR];
+  auto gload = [&](int k0) __attribute__((always_inline)) {
+    const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int u = 0; u < AR; ++u) {
+      const int c = u * 256 + tid;
+      const int row = c / (KT / VEC), cv = c % (KT / VEC);
+      const int m = m0 + row, kk = k0 + cv * VEC;
+      const bool ok = m < M && kk < Kd;
+      const size_t off = AHEADS ? hm(ok ? m : 0, ok ? kk : 0) : (size_t)(ok ? m : 0) * Kd + (ok ? kk : 0);
+      ar[u] = ok ? *(const u32x4*)(A + off) : z;
+    }
+#pragma unroll
+    for (int u = 0; u < BR; ++u) {
+      const int c = u * 256 + tid;
+      const int row = c / (KT / VEC), cv = c % (KT / VEC);
+      const int kk = k0 + cv * VEC;
+      const bool ok = kk < Kd;
+      br[u] = ok ? *(const u32x4*)(Bm + (size_t)(n0 + row) * Kd + (ok ? kk : 0)) : z;
+    }
+  };
+  auto lstore = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < AR; ++u) {
+      const int c = u * 256 + tid;
+      const int row = c / (KT / VEC), cv = c % (KT / VEC);
+      *(u32x4*)(As + row * KS + cv * VEC) = ar[u];
+    }
+#pragma unroll
+    for (int u = 0; u < BR; ++u) {
+      const int c = u * 256 + tid;
+      const int row = c / (KT / VEC), cv = c % (KT / VEC);
+      *(u32x4*)(Bt + row * KS + cv * VEC) = br[u];
+    }
+  };
+  gload(0);
+  for (int k0 = 0; k0 < Kd; k0 += KT) {
+    lstore();
+    __syncthreads();
+    if (k0 + KT < Kd) gload(k0 + KT);  // in flight during this step's products
+#pragma unroll
+    for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+      for (int tj = 0; tj < TJ; ++tj) {
+        const T* arow = As + (wm + 16 * ti + r) * KS;
+        const T* brow = Bt + (wn + 16 * tj + r) * KS;
+        if constexpr (bf) {
+#pragma unroll
+          for (int ks = 0; ks < KT / 32; ++ks) {
+            const bf16x8 a = *(const bf16x8*)(arow + 32 * ks + 8 * sl);
+            const bf16x8 b = *(const bf16x8*)(brow + 32 * ks + 8 * sl);
+            acc[ti][tj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[ti][tj], 0, 0, 0);
+          }
+        } else {
+#pragma unroll
+          for (int kk = 0; kk < KT / 4; ++kk)
+            acc[ti][tj] = __builtin_amdgcn_mfma_f32_16x16x4f32(arow[4 * kk + sl], brow[4 * kk + sl], acc[ti][tj], 0, 0, 0);
+        }
+      }
+    __syncthreads();
+  }
+  // ---- the tile into LDS (lane holds rows 4(l/16) + k, column l%16 of each 16x16 tile)
+#pragma unroll
+  for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+    for (int tj = 0; tj < TJ; ++tj)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) Cs[(wm + 16 * ti + 4 * sl + k) * CST + wn + 16 * tj + r] = acc[ti][tj][k];
+  __syncthreads();
+  if constexpr (QKV) {
+    if (which < 2) {
+      // RoPE on pairs (d, d + D/2) of each head in the tile, at the token's position in its sequence:
+      // the frequencies base^(-2i/D) and the angle pos * theta in double, the angle reduced to
+      // [-pi, pi] in double, then sine / cosine in float
+      __shared__ double theta[D / 2];
+      if (tid < D / 2) theta[tid] = pow((double)s.rope_base, -2.0 * tid / D);
+      __syncthreads();
+      constexpr double kTwoPi = 6.283185307179586476925286766559;
+      for (int e = tid; e < 64 * (NT / 2); e += 256) {
+        const int row = e / (NT / 2), pc = e % (NT / 2);
+        const int hc = pc / (D / 2), i = pc % (D / 2);
+        const int col = hc * D + i;
+        const int pos = (m0 + row) % s.S;
+        const double ang = (double)pos * theta[i];
+        const double red = fma(-rint(ang * (1.0 / kTwoPi)), kTwoPi, ang);
+        float sv, c;
+        sincosf((float)red, &sv, &c);
+        const float x1 = Cs[row * CST + col], x2 = Cs[row * CST + col + D / 2];
+        Cs[row * CST + col] = x1 * c - x2 * sv;
+        Cs[row * CST + col + D / 2] = x2 * c + x1 * sv;
+      }
+      __syncthreads();
+    }
+  }
+  // ---- whole rows out as 16-byte vectors; the stored (rounded) values stay in LDS
+  for (int e = tid; e < 64 * (NT / VEC); e += 256) {
+    const int row = e / (NT / VEC), cv = e % (NT / VEC);
+    const int m = m0 + row;
+    T v[VEC];
+#pragma unroll
+    for (int x = 0; x < VEC; ++x) {
+      v[x] = (T)Cs[row * CST + cv * VEC + x];
+      Cs[row * CST + cv * VEC + x] = (float)v[x];
+    }
+    if (m < M) {
+      const int n = n0 + cv * VEC;
+      size_t off;
+      if constexpr (QKV) {
+        const int b = m / s.S, t = m % s.S, h = n / D;
+        off = (((size_t)b * s.H + h) * s.S + t) * D + n % D;
+      } else {
+        off = (size_t)m * Nm + n;
+      }
+      *(u32x4*)(Cm + off) = *(const u32x4*)v;
+    }
+  }
+  if constexpr (QKV) {
+    if (which != 1) return;  // uniform for the work-group
+    __shared__ float kbar[D];
+    __shared__ float logit[kMaxCodesTotal];
+    __syncthreads();
+    // ---- K: each (head, block) in the tile: summary = mean of its stored key rows (added in row
+    // order), then its product address (and alternate)
+    for (int hc = 0; hc < NT / D; ++hc) {
+      const int h = (n0 + hc * D) / D;
+      CodeSlice<D> cs;
+      cs.load(ep.cb, ep.bias, h, s);
+      for (int u = 0; u < 64 / s.blk; ++u) {
+        const int mb = m0 + u * s.blk;  // first row of the block (blocks never straddle sequences)
+        if (mb >= M) break;             // uniform
+        const int b = mb / s.S, i = (mb % s.S) / s.blk;
+        const int bh = b * s.H + h;
+        if (tid < D) {
+          float a = 0.f;
+          for (int rr = 0; rr < s.blk; ++rr) a += Cs[(u * s.blk + rr) * CST + hc * D + tid];
+          const float mval = a / (float)s.blk;
+          kbar[tid] = mval;
+          ep.ksum[((size_t)bh * s.nb + i) * D + tid] = mval;
+        }
+        if (ep.cell_zero && i < s.ne) {
+          int32_t* crow = ep.cell_zero + (size_t)bh * s.cells_per_bh + cell_row(i, s.ne);
+          for (int c = tid; c < s.ne - i; c += 256) crow[c] = 0;
+        }
+        __syncthreads();
+        address_from_summary<D>(cs, kbar, logit, ep.addr + (size_t)bh * s.nb + i,
+                                ep.alt ? ep.alt + (size_t)bh * s.nb + i : nullptr, s);
+        __syncthreads();  // kbar and logit are rewritten next
+      }
+    }
+  }
+}
+
+// out[c][r] = in[r][c] for an R x Cc matrix, through a padded 32 x 32 LDS tile.
+template <typename T>
+__global__ __launch_bounds__(256) void k_transpose(const T* __restrict__ in, T* __restrict__ out, int R, int Cc) {
+  __shared__ T tile[32][33];
+  const int c0 = blockIdx.x * 32, r0 = blockIdx.y * 32;
+  const int tx = threadIdx.x % 32, ty = threadIdx.x / 32;
+  for (int y = ty; y < 32; y += 8)
+    if (r0 + y < R && c0 + tx < Cc) tile[y][tx] = in[(size_t)(r0 + y) * Cc + c0 + tx];
+  __syncthreads();
+  for (int y = ty; y < 32; y += 8)
+    if (c0 + y < Cc && r0 + tx < R) out[(size_t)(c0 + y) * R + r0 + tx] = tile[tx][y];
+}
+
+template <typename T>
+hipError_t transpose(const void* in, void* out, int R, int Cc, hipStream_t st) {
+  hipLaunchKernelGGL(k_transpose<T>, dim3((Cc + 31) / 32, (R + 31) / 32), dim3(256), 0, st, (const T*)in, (T*)out, R,
+                     Cc);
+  return hipGetLastError();
+}
+
+// Largest output tile width (128, 64, 32) dividing Nm and, for the fused projection, holding whole
+// heads; 0 when none.
+int mm_tile(int Nm, int D, bool qkv) {
+  for (int nt = 128; nt >= 32; nt >>= 1)
+    if (Nm % nt == 0 && (!qkv || nt % D == 0)) return nt;
+  return 0;
+}
+
+template <typename T, int NT, int D>
+hipError_t qkv_launch(const Shape& s, const void* x, const void* wq, const void* wk, const void* wv, void* q, void* k,
+                      void* v, const QkvEpilogue& ep, void* wt, hipStream_t st) {
+  const int M = s.B * s.S, Nm = s.H * s.D;
+  HeadMap hm{s.S, s.H, s.D};
+  T* t0 = (T*)wt;
+  T* t1 = t0 + (size_t)Nm * s.W;
+  T* t2 = t1 + (size_t)Nm * s.W;
+  hipError_t e;
+  if ((e = transpose<T>(wq, t0, s.W, Nm, st)) != hipSuccess) return e;
+  if ((e = transpose<T>(wk, t1, s.W, Nm, st)) != hipSuccess) return e;
+  if ((e = transpose<T>(wv, t2, s.W, Nm, st)) != hipSuccess) return e;
+  hipLaunchKernelGGL((k_mm<T, NT, false, true, D>), dim3((M + 63) / 64, 3 * Nm / NT), dim3(256), 0, st, (const T*)x,
+                     t0, t1, t2, (T*)q, (T*)k, (T*)v, M, Nm, s.W, hm, ep, s);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t qkv_fused_d(const Shape& s, const void* x, const void* wq, const void* wk, const void* wv, void* q, void* k,
+                       void* v, const QkvEpilogue& ep, void* wt, hipStream_t st) {
+  switch (mm_tile(s.H * s.D, D, true)) {
+    case 128: return qkv_launch<T, 128, D>(s, x, wq, wk, wv, q, k, v, ep, wt, st);
+    case 64: if constexpr (D <= 64) return qkv_launch<T, 64, D>(s, x, wq, wk, wv, q, k, v, ep, wt, st); break;
+    case 32: if constexpr (D <= 32) return qkv_launch<T, 32, D>(s, x, wq, wk, wv, q, k, v, ep, wt, st); break;
+    default: break;
+  }
+  return hipErrorInvalidValue;
+}
+
+template <typename T>
+hipError_t qkv_fused(const Shape& s, const void* x, const void* wq, const void* wk, const void* wv, void* q, void* k,
+                     void* v, const QkvEpilogue& ep, void* wt, hipStream_t st) {
+  switch (s.D) {
+    case 32: return qkv_fused_d<T, 32>(s, x, wq, wk, wv, q, k, v, ep, wt, st);
+    case 64: return qkv_fused_d<T, 64>(s, x, wq, wk, wv, q, k, v, ep, wt, st);
+    case 128: return qkv_fused_d<T, 128>(s, x, wq, wk, wv, q, k, v, ep, wt, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <typename T, int NT>
+hipError_t out_launch(const Shape& s, const void* o, const void* wo, void* delta, void* wt, hipStream_t st) {
+  const int M = s.B * s.S, Nm = s.W, Kd = s.H * s.D;
+  HeadMap hm{s.S, s.H, s.D};
+  const QkvEpilogue none{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
+  T* t = (T*)wt + 3 * (size_t)Kd * s.W;  // after the three projection weights
+  hipError_t e = transpose<T>(wo, t, Kd, Nm, st);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((k_mm<T, NT, true, false, 0>), dim3((M + 63) / 64, Nm / NT), dim3(256), 0, st, (const T*)o,
+                     t, t, t, (T*)delta, (T*)delta, (T*)delta, M, Nm, Kd, hm, none, s);
+  return hipGetLastError();
+}
+
 template <typename T>
 hipError_t project_heads(const Shape& s, const void* x, const void* w, void* out, bool rope, hipStream_t st) {
   const int M = s.B * s.S, N = s.H * s.D, Kd = s.W;
@@ -131,7 +425,13 @@ hipError_t project_heads(const Shape& s, const void* x, const void* w, void* out
 }
 
 template <typename T>
-hipError_t project_out(const Shape& s, const void* o, const void* wo, void* delta, hipStream_t st) {
+hipError_t project_out(const Shape& s, const void* o, const void* wo, void* delta, void* wt, hipStream_t st) {
+  switch (wt ? mm_tile(s.W, 0, false) : 0) {
+    case 128: return out_launch<T, 128>(s, o, wo, delta, wt, st);
+    case 64: return out_launch<T, 64>(s, o, wo, delta, wt, st);
+    case 32: return out_launch<T, 32>(s, o, wo, delta, wt, st);
+    default: break;
+  }
   const int M = s.B * s.S, N = s.W, Kd = s.H * s.D;
   HeadMap hm{s.S, s.H, s.D};
   hipLaunchKernelGGL((k_gemm<T, true, false>), dim3((N + 63) / 64, (M + 63) / 64), dim3(256), 0, st, (const T*)o,
@@ -146,9 +446,20 @@ hipError_t launch_project_heads(const Shape& s, const void* x, const void* w, vo
   return project_heads<float>(s, x, w, out, rope, st);
 }
 
-hipError_t launch_project_out(const Shape& s, const void* o, const void* wo, void* delta, hipStream_t st) {
-  if (s.dtype == MDR_BF16) return project_out<bf16>(s, o, wo, delta, st);
-  return project_out<float>(s, o, wo, delta, st);
+bool qkv_fuses_address(const Shape& s) { return s.blk <= 64 && s.W % 8 == 0 && mm_tile(s.H * s.D, s.D, true) > 0; }
+
+hipError_t launch_qkv_fused(const Shape& s, const void* x, const void* wq, const void* wk, const void* wv, void* q,
+                            void* k, void* v, const float* cb, const float* bias, float* ksum, int32_t* addr,
+                            int32_t* alt, int32_t* cell_zero, void* wt, hipStream_t st) {
+  if (!qkv_fuses_address(s)) return hipErrorInvalidValue;
+  const QkvEpilogue ep{cb, bias, ksum, addr, alt, cell_zero};
+  if (s.dtype == MDR_BF16) return qkv_fused<bf16>(s, x, wq, wk, wv, q, k, v, ep, wt, st);
+  return qkv_fused<float>(s, x, wq, wk, wv, q, k, v, ep, wt, st);
+}
+
+hipError_t launch_project_out(const Shape& s, const void* o, const void* wo, void* delta, void* wt, hipStream_t st) {
+  if (s.dtype == MDR_BF16) return project_out<bf16>(s, o, wo, delta, wt, st);
+  return project_out<float>(s, o, wo, delta, wt, st);
 }
 
 }  // namespace mdr

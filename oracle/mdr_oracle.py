@@ -573,23 +573,37 @@ def mixer_qkv(x, wq, wk, wv, w):
     return q, k, v
 
 
-def mixer_forward(x, wq, wk, wv, wo, codebook, bias, w, sel_override=None, rdtype=np.float32):
+def round_to_bf16(a) -> np.ndarray:
+    """Each value rounded to the nearest bfloat16 (8 significand bits; ties to even), returned as
+    float64: keep the top 16 bits of the float32 pattern after adding half an ulp of the kept part
+    (0x7FFF plus the lowest kept bit).  Finite inputs only."""
+    f = np.ascontiguousarray(np.asarray(a, dtype=np.float32))
+    u = f.view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
+    return u.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+def mixer_forward(x, wq, wk, wv, wo, codebook, bias, w, sel_override=None, rdtype=np.float32, io_dtype="f32",
+                  policy="drop"):
     """Stateless [B, S, W] -> attention delta [B, S, W] (float64), plus the routes.
 
-    Routing reads Q and K rounded to ``rdtype``; attention uses them in float64.
-    ``sel_override`` [B, H, S, R] replaces the oracle's own selection (so the
-    attention and output projection can be checked on another router's choice).
+    Q, K, V are held in the io dtype between the projections and the core (the core's own inputs):
+    with ``io_dtype`` "bf16" they are rounded to bfloat16 first.  Routing reads Q and K rounded to
+    ``rdtype``; attention uses them in float64.  ``sel_override`` [B, H, S, R] replaces the oracle's
+    own selection (so the attention and output projection can be checked on another router's choice).
     """
     B, S, _ = x.shape
     H, D = w.heads, w.head_dim
     q, k, v = mixer_qkv(x, wq, wk, wv, w)
+    if io_dtype == "bf16":
+        q, k, v = round_to_bf16(q), round_to_bf16(k), round_to_bf16(v)
     o = np.zeros((B, H, S, D))
     routes = []
     for b in range(B):
         rb = []
         for h in range(H):
             r = route_head(q[b, h].astype(rdtype), k[b, h].astype(rdtype), codebook[h],
-                           None if bias is None else bias[h], w, rdtype=rdtype)
+                           None if bias is None else bias[h], w, rdtype=rdtype, policy=policy)
             sel = r["sel"] if sel_override is None else np.asarray(sel_override[b, h])
             o[b, h] = attention_dense(q[b, h], k[b, h], v[b, h], sel, w.block, w.local)
             rb.append(r)

@@ -1,0 +1,92 @@
+"""The stateless mixer on the GPU against the oracle, through mdr_mixer_forward: the fused Q/K/V
+projection (RoPE, block summaries and addresses in its epilogue; blocks of up to 64 tokens and a
+width divisible by 8) and the unfused path (k_gemm, k_rope, the address kernel) for the rest.
+
+Q, K, V are held in the io dtype between the projection and the core, so the oracle rounds them the
+same way (oracle.mixer_forward, io_dtype).  Checks: block summaries (fp32 1e-5 relative; bf16 2e-3
+relative: the fused epilogue averages the stored bf16 rows, the oracle the same rounded rows in fp32
+from an fp64 product, so only bf16 rounding flips of single elements differ), addresses and
+alternates under the near-tie rule, selections under the near-tie rule, and the delta with the GPU's
+selection (1e-5 fp32 / 2e-2 bf16).
+"""
+
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tests._gpu import NEAR, TOL, cfg_of, compare_selection, dev, host, io_dtype
+
+pytestmark = pytest.mark.gpu
+
+BASE = synth.workload("tiny")
+CASES = {
+    # fused: fp32, D32, block 32, width 64 (the tiny mixer)
+    "tiny": dict(),
+    # fused: bf16, D64, block 64, 2x16 codes
+    "bf16_d64": dict(batch=1, heads=4, seq=2048, head_dim=64, block=64, width=256, subspaces=2, codes=16,
+                     capacity=4, probes=4, dtype="bf16"),
+    # fused: block 32 with seq % 64 == 32, so one 64-row tile holds the last block of one sequence and
+    # the first block of the next
+    "straddle": dict(batch=2, heads=2, seq=1056, head_dim=32, block=32, width=96),
+    # fused + redirect policy: bf16, D128, 3x8 codes, capacity 1 and a skewing code bias (lists
+    # overflow), alternates in the epilogue
+    "redirect": dict(batch=1, heads=2, seq=2048, head_dim=128, block=64, width=128, subspaces=3, codes=8,
+                     capacity=1, probes=6, remote=4, dtype="bf16", zipf_kappa=1.0),
+    # unfused: block 128
+    "block128": dict(batch=1, heads=2, seq=1024, head_dim=128, block=128, width=128, codes=8, capacity=4,
+                     probes=4),
+    # unfused: width not a multiple of 8
+    "width60": dict(batch=1, heads=2, seq=512, head_dim=32, block=32, width=60),
+}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_mixer_matches_oracle(gpu_lib, name):
+    mdr = gpu_lib
+    w = dataclasses.replace(BASE, **CASES[name])
+    policy = "redirect" if name == "redirect" else "drop"
+    inp = synth.make_mixer_inputs(w, 0)
+    cfg = cfg_of(mdr, w, policy)
+    dt = io_dtype(w)
+    t = {n: dev(inp[n], dt) for n in ("x", "wq", "wk", "wv", "wo")}
+    cb = dev(inp["codebook"], torch.float32)
+    bias = synth.zipf_code_bias(w.heads, w.subspaces, w.codes, w.zipf_kappa) if w.zipf_kappa else None
+    delta = torch.empty_like(t["x"])
+    rt = mdr.routing_buffers(cfg)
+    mdr.mdr_mixer_forward(cfg, t["x"], t["wq"], t["wk"], t["wv"], t["wo"], cb,
+                          None if bias is None else dev(bias), delta, rt, mdr.workspace(cfg))
+    torch.cuda.synchronize()
+    res = {n: host(v) for n, v in rt.items()}
+    ref, routes = oracle.mixer_forward(inp["x"], inp["wq"], inp["wk"], inp["wv"], inp["wo"], inp["codebook"], bias,
+                                       w, sel_override=res["sel"], io_dtype=w.dtype, policy=policy)
+    near_a = near_s = 0
+    ktol = 1e-5 if w.dtype == "f32" else 2e-3
+    for b in range(w.batch):
+        for h in range(w.heads):
+            r = routes[b][h]
+            scale = max(1.0, float(np.abs(r["ksum"]).max()))
+            np.testing.assert_allclose(res["ksum"][b, h], r["ksum"], rtol=0, atol=ktol * scale)
+            sure = r["addr_margin"].min(axis=1) > NEAR
+            near_a += int((~sure).sum())
+            assert np.array_equal(res["addr"][b, h][sure], r["addr"][sure]), (b, h)
+            if policy == "redirect":
+                bh_ = None if bias is None else bias[h]
+                second, margin = oracle.runner_up_codes(r["ksum"], inp["codebook"][h], bh_)
+                alt, gap = oracle.alternate_addresses(r["codes"], second, margin, w.codes)
+                gap2 = oracle.runner_up_gap(r["ksum"], inp["codebook"][h], bh_)
+                g_star = np.array([min(range(w.subspaces), key=lambda g: (margin[i, g], g))
+                                   for i in range(w.nblocks)])
+                ok = sure & (gap > NEAR) & (gap2[np.arange(w.nblocks), g_star] > NEAR)
+                assert np.array_equal(res["alt"][b, h][ok], alt[ok]), (b, h)
+            if np.all(sure[: max(0, w.nblocks - w.local)]):
+                near_s += compare_selection(r, res["sel"][b, h])
+    err = float(np.abs(host(delta) - ref).max())
+    print(f"{name}: address near-ties {near_a}, selection near-ties {near_s}, max abs err {err:.3g}, "
+          f"overflow {int(res['overflow'].sum())}")
+    assert err <= TOL[w.dtype]
+    if name == "redirect":
+        assert int(res["overflow"].sum()) >= 0 and int(res["redir_off"][..., -1].sum()) > 0

@@ -541,3 +541,18 @@ def test_route_head_redirect_recovers_overflowed_blocks():
         for j in range(0, w.nblocks, 5):
             v = oracle.posting_view_redirect(rred["lists"], rred["rd"], a, j, w.local, w.capacity)
             assert len(v) <= w.capacity and len(set(v)) == len(v)
+
+
+def test_round_to_bf16_matches_torch():
+    """The oracle's bfloat16 rounding against torch's conversion (round to nearest even), including
+    exact ties, values at the bf16 grid and negative numbers."""
+    rng = np.random.default_rng(11)
+    a = rng.standard_normal(4096).astype(np.float32) * np.float32(3.0)
+    grid = torch.tensor(a).to(torch.bfloat16).float().numpy()
+    _, e = np.frexp(grid)                                       # |grid| = m 2^e, 0.5 <= m < 1
+    ulp = np.ldexp(np.float32(1.0), e - 8).astype(np.float32)  # bf16 spacing at grid
+    ties = (grid + np.sign(grid) * ulp * np.float32(0.5)).astype(np.float32)  # exactly half way
+    assert np.all(np.abs(ties - grid) == ulp / 2)
+    for x in (a, grid, ties, -ties):
+        ref = torch.tensor(x).to(torch.bfloat16).double().numpy()
+        np.testing.assert_array_equal(oracle.round_to_bf16(x), ref)
