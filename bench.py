@@ -18,7 +18,8 @@ against 8 TB/s), every kernel's time and bytes, the fitted timing exponent over
 
     python bench.py --ingest-pmc FETCH.csv WRITE.csv
 turns two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of
-``python bench.py --steps 3 --warmup 1 --calib-copy --no-cpu --no-sweep --no-decode --no-backward --no-stress`` into
+``python bench.py --steps 3 --warmup 1 --calib-copy --no-cpu --no-sweep --no-decode --no-backward --no-stress
+--no-mixer`` into
 profiles/traffic_<workload>.json (per-launch HBM bytes of every kernel,
 scaled by what the counters read for a plain elementwise copy of known size).
 """
@@ -64,9 +65,9 @@ CALIB_BYTES = 512 << 20
 HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000  # hipEventDisableSystemFence (hip_runtime_api.h)
 PMC_COMMANDS = [  # run from the repository root on one MI355X, TMPDIR=/tmp
     "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmcf -o f -- "
-    "python3 bench.py --steps 3 --warmup 1 --calib-copy --no-cpu --no-sweep --no-decode --no-backward --no-stress",
+    "python3 bench.py --steps 3 --warmup 1 --calib-copy --no-cpu --no-sweep --no-decode --no-backward --no-stress --no-mixer",
     "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmcw -o w -- "
-    "python3 bench.py --steps 3 --warmup 1 --calib-copy --no-cpu --no-sweep --no-decode --no-backward --no-stress",
+    "python3 bench.py --steps 3 --warmup 1 --calib-copy --no-cpu --no-sweep --no-decode --no-backward --no-stress --no-mixer",
 ]
 
 
