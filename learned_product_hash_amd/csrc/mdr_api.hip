@@ -95,7 +95,7 @@ size_t layout(const Shape& s, char* base, Buffers* b) {
   t.sel = (int32_t*)take(BH * s.S * s.R * 4);
   t.ncand = (int32_t*)take(BH * s.S * 4);
   t.cellcnt = (int32_t*)take(BH * (size_t)s.cells_per_bh * 4);
-  t.bins = (int32_t*)take(BH * (size_t)s.cells_per_bh * s.blk * 4);
+  t.bins = (int32_t*)take(BH * (size_t)s.cells_per_bh * (s.blk + kCellDense) * 4);
   t.part_o = take(BH * s.S * s.R * s.D * e);
   t.part_ml = (float*)take(BH * s.S * s.R * 8);
   t.dvec = (float*)take(BH * s.S * 4);

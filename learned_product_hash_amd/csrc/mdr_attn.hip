@@ -114,7 +114,7 @@ __global__ __launch_bounds__(kRemoteWaves * 64) void k_attn_remote(const T* __re
       else
         hi = mid - 1;
     }
-    return bins[(row0 + lo) * BLK + (pidx - pre[lo])];
+    return cell_pair(bins, s, row0 + lo, pidx - pre[lo]);
   };
   int it = blockIdx.z;
   if (it * PER_IT + wave * 16 >= total) return;  // this wave has no pairs at all (no barriers below)

@@ -86,7 +86,7 @@ __global__ __launch_bounds__(BLK) void k_pair_bin_ordered(const int32_t* __restr
     }
     pos += __popc(m[tid / 32] & ((1u << (tid % 32)) - 1u));
     const long long cell = (long long)bh * s.cells_per_bh + cell_row(i, s.ne) + (j - i - s.L);
-    bins[cell * BLK + pos] = t * s.R + r;
+    *cell_slot(bins, s, cell, pos) = t * s.R + r;
     if (pos == 0) cellcnt[cell] = tot;
   }
 }
@@ -224,7 +224,7 @@ __global__ __launch_bounds__(BLK * 4) __attribute__((amdgpu_waves_per_eu(kv_min_
             else
               hi = mid - 1;
           }
-          aP = bins[(row0 + cb + lo) * BLK + (er - pre[lo])];
+          aP = cell_pair(bins, s, row0 + cb + lo, er - pre[lo]);
           aT = -2;
         }
       }

@@ -48,7 +48,8 @@ struct Buffers {
   int32_t* sel;
   int32_t* ncand;
   int32_t* cellcnt;    // [B,H,cells] pairs per (remote block i, query block j) cell
-  int32_t* bins;       // [B,H,cells,blk] (t*R + r) of the pairs of each cell
+  int32_t* bins;       // (t*R + r) of the pairs of each cell: a dense [B,H,cells,kCellDense] table of
+                       // the first slots, then [B,H,cells,blk] rows (see cell_slot)
   void* part_o;        // [B,H,S,R,D] remote partial outputs (normalised), io dtype
   float* part_ml;      // [B,H,S,R,2] remote partial (max in log2 units, sum)
   void* mq;            // mixer: Q, K, V, O in [B,H,S,D]
@@ -105,13 +106,27 @@ __device__ inline bool sel_entry_valid(const int32_t* row, int r, int j, int L) 
   return true;
 }
 
+// Where slot pos of a cell's pair list lives.  Cells hold 1.3 pairs on average and a row of a
+// block's cells is read front to back, so the first kCellDense slots of every cell sit in a dense
+// table ([cells][kCellDense], consecutive cells on shared cache lines) at the start of the bins
+// region; slots kCellDense .. blk - 1 sit in full-width rows ([cells][blk]) after it.
+constexpr int kCellDense = 4;
+__host__ __device__ inline long long cells_total(const Shape& s) { return (long long)s.B * s.H * s.cells_per_bh; }
+__device__ inline int32_t* cell_slot(int32_t* bins, const Shape& s, long long cell, int pos) {
+  return pos < kCellDense ? bins + cell * kCellDense + pos
+                          : bins + cells_total(s) * kCellDense + cell * s.blk + pos;
+}
+__device__ inline int32_t cell_pair(const int32_t* __restrict__ bins, const Shape& s, long long cell, int pos) {
+  return pos < kCellDense ? bins[cell * kCellDense + pos] : bins[cells_total(s) * kCellDense + cell * s.blk + pos];
+}
+
 // Append pair (t, r) of query block j to the cell (i, j).  Only the work-group that owns query
 // block j touches the cell, so its counter sees at most blk atomic adds.
 __device__ inline void record_pair(int32_t* cellcnt, int32_t* bins, const Shape& s, int bh, int i, int j, int t,
                                    int r) {
   const long long cell = (long long)bh * s.cells_per_bh + cell_row(i, s.ne) + (j - i - s.L);
   const int pos = atomicAdd(&cellcnt[cell], 1);
-  if (pos < s.blk) bins[cell * s.blk + pos] = t * s.R + r;
+  if (pos < s.blk) *cell_slot(bins, s, cell, pos) = t * s.R + r;
 }
 
 // Work-groups are handed to the 8 XCDs of the chip in turn (linear id mod 8), and each XCD has its

@@ -1023,7 +1023,7 @@ __global__ __launch_bounds__(kProbeThreads) __attribute__((amdgpu_waves_per_eu(p
           const int i = tri[r];
           const int pos = atomicAdd(&cnt[(j - jb) * s.ne + i], 1);
           const long long cell = (long long)bh * s.cells_per_bh + cell_row(i, s.ne) + (j - i - s.L);
-          if (pos < s.blk) bins[cell * s.blk + pos] = t * s.R + r;
+          if (pos < s.blk) *cell_slot(bins, s, cell, pos) = t * s.R + r;
         }
       }
     }
