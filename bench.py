@@ -51,9 +51,10 @@ KERNEL_SOURCE = {
     "address": "mdr_route.hip", "post": "mdr_route.hip", "probe_rerank": "mdr_route.hip",
     "attn_remote": "mdr_attn.hip", "attn_local": "mdr_attn.hip",
 }
-MIXER_SYMBOL = {
-    "qkv (fused projections + RoPE + summaries + addresses)": "k_qkv",
-    "output projection": "k_gemm",
+MIXER_SYMBOL = {  # every listed substring must occur in the (mangled) kernel name
+    "qkv (fused projections + RoPE + summaries + addresses)": ("k_mm", "Lb0ELb1E"),
+    "output projection": ("k_mm", "Lb1ELb0E"),
+    "weight transposes": ("k_transpose",),
 }
 BACKWARD_SYMBOL = {
     "pair_bin": "k_pair_bin_ordered",
@@ -673,16 +674,16 @@ def summarize_rocprof(stats_csv, command, w, bench_log=None, stem="routed_attent
                   "| kernel | calls | avg us | min us | max us | share of GPU time | bench.py HIP-event avg us |",
                   "|---|---|---|---|---|---|---|"] + bl
     ml = []
-    for k, sym in MIXER_SYMBOL.items():
+    for k, subs in MIXER_SYMBOL.items():
         for r in rows:
-            if sym in r["Name"]:
-                ml.append(f"| {k} (`{sym}`) | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+            if all(x in r["Name"] for x in subs):
+                ml.append(f"| {k} (`{subs[0]}`) | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                           f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
                           f"{float(r['Percentage']):.1f}% |")
     if ml:
         lines += ["", "Mixer (mdr_mixer_forward at width 512; its core kernels are counted in the table above):", "",
                   "| kernel | calls | avg us | min us | max us | share of GPU time |", "|---|---|---|---|---|---|"] + ml
-    known = list(KERNEL_SYMBOL.values()) + list(BACKWARD_SYMBOL.values()) + list(MIXER_SYMBOL.values())
+    known = list(KERNEL_SYMBOL.values()) + list(BACKWARD_SYMBOL.values()) + [v[0] for v in MIXER_SYMBOL.values()]
     other = sum(float(r["Percentage"]) for r in rows if not any(sym in r["Name"] for sym in known))
     lines += ["", f"Other kernels (input generation, torch copies, routing statistics): {other:.1f}% of GPU time.", ""]
     out = os.path.join(ROOT, "profiles", f"{stem}_{w.name}_{w.seq // 1024}k.md")

@@ -123,7 +123,7 @@ __global__ __launch_bounds__(256) void k_rope(T* __restrict__ X, long long rows,
   }
 }
 
-// C = A B on MFMA for 64 x NT output tiles, 256 threads (2 x 2 waves of 32 x NT/2), contraction
+// C = A B on MFMA for MT x NT output tiles, 256 threads (2 x 2 waves of MT/2 x NT/2), contraction
 // steps of KT (64 bf16 / 32 fp32): the next step's A and B tiles are read into registers while the
 // current step is multiplied out of LDS.  B is passed transposed ([n][k], k contiguous: the mixer
 // transposes its weights once per call), so both tiles are plain 16-byte row copies into LDS.  The
@@ -142,7 +142,7 @@ struct QkvEpilogue {
   int32_t* cell_zero;
 };
 
-template <typename T, int NT, bool AHEADS, bool QKV, int D>
+template <typename T, int MT, int NT, bool AHEADS, bool QKV, int D>
 __global__ __launch_bounds__(256) void k_mm(const T* __restrict__ A, const T* __restrict__ B0,
                                             const T* __restrict__ B1, const T* __restrict__ B2, T* __restrict__ C0,
                                             T* __restrict__ C1, T* __restrict__ C2, int M, int Nm, int Kd, HeadMap hm,
@@ -151,28 +151,29 @@ __global__ __launch_bounds__(256) void k_mm(const T* __restrict__ A, const T* __
   constexpr int VEC = 16 / (int)sizeof(T);
   constexpr int KT = bf ? 64 : 32;
   constexpr int KS = KT + VEC;                 // LDS row stride: 16 bytes of padding
+  constexpr int TI = MT / 32;                  // 16-row tiles per wave (waves split MT in halves)
   constexpr int TJ = NT / 32;                  // 16-column tiles per wave
-  constexpr int AR = 64 * KT / VEC / 256;      // A vectors per thread per step
+  constexpr int AR = MT * KT / VEC / 256;      // A vectors per thread per step
   constexpr int BR = KT * NT / VEC / 256;      // B vectors per thread per step
-  static_assert(AR >= 1 && BR >= 1 && 64 * KT / VEC % 256 == 0 && KT * NT / VEC % 256 == 0, "whole vectors");
-  constexpr int CST = NT + 1;                  // output tile row stride (floats)
-  constexpr size_t STAGE = (size_t)(64 + NT) * KS * sizeof(T);
+  static_assert(AR >= 1 && BR >= 1 && MT * KT / VEC % 256 == 0 && KT * NT / VEC % 256 == 0, "whole vectors");
+  constexpr int CST = NT + 1;                  // output rows of 64 at a time (floats)
+  constexpr size_t STAGE = (size_t)(MT + NT) * KS * sizeof(T);
   constexpr size_t EPIB = (size_t)64 * CST * 4;
   __shared__ __align__(16) char smem[STAGE > EPIB ? STAGE : EPIB];
   T* As = (T*)smem;
-  T* Bt = As + 64 * KS;
+  T* Bt = As + MT * KS;
   float* Cs = (float*)smem;  // after the main loop
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int m0 = blockIdx.x * 64;
+  const int m0 = blockIdx.x * MT;
   const int ng = blockIdx.y * NT;
   const int which = QKV ? ng / Nm : 0, n0 = QKV ? ng % Nm : ng;
   const T* Bm = which == 0 ? B0 : which == 1 ? B1 : B2;
   T* Cm = which == 0 ? C0 : which == 1 ? C1 : C2;
-  const int wm = (wave >> 1) * 32, wn = (wave & 1) * (NT / 2);
+  const int wm = (wave >> 1) * (MT / 2), wn = (wave & 1) * (NT / 2);
   const int sl = lane >> 4, r = lane & 15;
-  f32x4 acc[2][TJ];
+  f32x4 acc[TI][TJ];
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int a = 0; a < TI; ++a)
 #pragma unroll
     for (int b = 0; b < TJ; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
   u32x4 ar[AR], br[BR];
@@ -216,112 +217,130 @@ __global__ __launch_bounds__(256) void k_mm(const T* __restrict__ A, const T* __
     __syncthreads();
     if (k0 + KT < Kd) gload(k0 + KT);  // in flight during this step's products
 #pragma unroll
-    for (int ti = 0; ti < 2; ++ti)
+    for (int ks = 0; ks < (bf ? KT / 32 : KT / 4); ++ks) {
+      // the step's operand fragments of this wave, each used for TJ (A) or TI (B) products
+      if constexpr (bf) {
+        bf16x8 af[TI], bfr[TJ];
 #pragma unroll
-      for (int tj = 0; tj < TJ; ++tj) {
-        const T* arow = As + (wm + 16 * ti + r) * KS;
-        const T* brow = Bt + (wn + 16 * tj + r) * KS;
-        if constexpr (bf) {
+        for (int ti = 0; ti < TI; ++ti) af[ti] = *(const bf16x8*)(As + (wm + 16 * ti + r) * KS + 32 * ks + 8 * sl);
 #pragma unroll
-          for (int ks = 0; ks < KT / 32; ++ks) {
-            const bf16x8 a = *(const bf16x8*)(arow + 32 * ks + 8 * sl);
-            const bf16x8 b = *(const bf16x8*)(brow + 32 * ks + 8 * sl);
-            acc[ti][tj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[ti][tj], 0, 0, 0);
-          }
-        } else {
+        for (int tj = 0; tj < TJ; ++tj) bfr[tj] = *(const bf16x8*)(Bt + (wn + 16 * tj + r) * KS + 32 * ks + 8 * sl);
 #pragma unroll
-          for (int kk = 0; kk < KT / 4; ++kk)
-            acc[ti][tj] = __builtin_amdgcn_mfma_f32_16x16x4f32(arow[4 * kk + sl], brow[4 * kk + sl], acc[ti][tj], 0, 0, 0);
-        }
-      }
-    __syncthreads();
-  }
-  // ---- the tile into LDS (lane holds rows 4(l/16) + k, column l%16 of each 16x16 tile)
+        for (int ti = 0; ti < TI; ++ti)
 #pragma unroll
-  for (int ti = 0; ti < 2; ++ti)
-#pragma unroll
-    for (int tj = 0; tj < TJ; ++tj)
-#pragma unroll
-      for (int k = 0; k < 4; ++k) Cs[(wm + 16 * ti + 4 * sl + k) * CST + wn + 16 * tj + r] = acc[ti][tj][k];
-  __syncthreads();
-  if constexpr (QKV) {
-    if (which < 2) {
-      // RoPE on pairs (d, d + D/2) of each head in the tile, at the token's position in its sequence:
-      // the frequencies base^(-2i/D) and the angle pos * theta in double, the angle reduced to
-      // [-pi, pi] in double, then sine / cosine in float
-      __shared__ double theta[D / 2];
-      if (tid < D / 2) theta[tid] = pow((double)s.rope_base, -2.0 * tid / D);
-      __syncthreads();
-      constexpr double kTwoPi = 6.283185307179586476925286766559;
-      for (int e = tid; e < 64 * (NT / 2); e += 256) {
-        const int row = e / (NT / 2), pc = e % (NT / 2);
-        const int hc = pc / (D / 2), i = pc % (D / 2);
-        const int col = hc * D + i;
-        const int pos = (m0 + row) % s.S;
-        const double ang = (double)pos * theta[i];
-        const double red = fma(-rint(ang * (1.0 / kTwoPi)), kTwoPi, ang);
-        float sv, c;
-        sincosf((float)red, &sv, &c);
-        const float x1 = Cs[row * CST + col], x2 = Cs[row * CST + col + D / 2];
-        Cs[row * CST + col] = x1 * c - x2 * sv;
-        Cs[row * CST + col + D / 2] = x2 * c + x1 * sv;
-      }
-      __syncthreads();
-    }
-  }
-  // ---- whole rows out as 16-byte vectors; the stored (rounded) values stay in LDS
-  for (int e = tid; e < 64 * (NT / VEC); e += 256) {
-    const int row = e / (NT / VEC), cv = e % (NT / VEC);
-    const int m = m0 + row;
-    T v[VEC];
-#pragma unroll
-    for (int x = 0; x < VEC; ++x) {
-      v[x] = (T)Cs[row * CST + cv * VEC + x];
-      Cs[row * CST + cv * VEC + x] = (float)v[x];
-    }
-    if (m < M) {
-      const int n = n0 + cv * VEC;
-      size_t off;
-      if constexpr (QKV) {
-        const int b = m / s.S, t = m % s.S, h = n / D;
-        off = (((size_t)b * s.H + h) * s.S + t) * D + n % D;
+          for (int tj = 0; tj < TJ; ++tj)
+            acc[ti][tj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[ti], bfr[tj], acc[ti][tj], 0, 0, 0);
       } else {
-        off = (size_t)m * Nm + n;
+        float af[TI], bfr[TJ];
+#pragma unroll
+        for (int ti = 0; ti < TI; ++ti) af[ti] = As[(wm + 16 * ti + r) * KS + 4 * ks + sl];
+#pragma unroll
+        for (int tj = 0; tj < TJ; ++tj) bfr[tj] = Bt[(wn + 16 * tj + r) * KS + 4 * ks + sl];
+#pragma unroll
+        for (int ti = 0; ti < TI; ++ti)
+#pragma unroll
+          for (int tj = 0; tj < TJ; ++tj)
+            acc[ti][tj] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[ti], bfr[tj], acc[ti][tj], 0, 0, 0);
       }
-      *(u32x4*)(Cm + off) = *(const u32x4*)v;
     }
-  }
-  if constexpr (QKV) {
-    if (which != 1) return;  // uniform for the work-group
-    __shared__ float kbar[D];
-    __shared__ float logit[kMaxCodesTotal];
     __syncthreads();
-    // ---- K: each (head, block) in the tile: summary = mean of its stored key rows (added in row
-    // order), then its product address (and alternate)
-    for (int hc = 0; hc < NT / D; ++hc) {
-      const int h = (n0 + hc * D) / D;
-      CodeSlice<D> cs;
-      cs.load(ep.cb, ep.bias, h, s);
-      for (int u = 0; u < 64 / s.blk; ++u) {
-        const int mb = m0 + u * s.blk;  // first row of the block (blocks never straddle sequences)
-        if (mb >= M) break;             // uniform
-        const int b = mb / s.S, i = (mb % s.S) / s.blk;
-        const int bh = b * s.H + h;
-        if (tid < D) {
-          float a = 0.f;
-          for (int rr = 0; rr < s.blk; ++rr) a += Cs[(u * s.blk + rr) * CST + hc * D + tid];
-          const float mval = a / (float)s.blk;
-          kbar[tid] = mval;
-          ep.ksum[((size_t)bh * s.nb + i) * D + tid] = mval;
-        }
-        if (ep.cell_zero && i < s.ne) {
-          int32_t* crow = ep.cell_zero + (size_t)bh * s.cells_per_bh + cell_row(i, s.ne);
-          for (int c = tid; c < s.ne - i; c += 256) crow[c] = 0;
+  }
+  // ---- epilogue, 64 rows at a time through LDS (lane holds rows 4(l/16) + k, column l%16 of each
+  // 16x16 tile)
+  [[maybe_unused]] double* theta = nullptr;
+  if constexpr (QKV) {
+    __shared__ double th[D / 2];  // RoPE frequencies base^(-2i/D), in double
+    if (tid < D / 2) th[tid] = pow((double)s.rope_base, -2.0 * tid / D);
+    theta = th;
+  }
+  for (int hf = 0; hf < MT / 64; ++hf) {
+    const int mh = m0 + hf * 64;
+    if (hf > 0) __syncthreads();  // the previous rows are no longer read
+    if (wm / 64 == hf) {
+#pragma unroll
+      for (int ti = 0; ti < TI; ++ti)
+#pragma unroll
+        for (int tj = 0; tj < TJ; ++tj)
+#pragma unroll
+          for (int k = 0; k < 4; ++k) Cs[(wm % 64 + 16 * ti + 4 * sl + k) * CST + wn + 16 * tj + r] = acc[ti][tj][k];
+    }
+    __syncthreads();
+    if constexpr (QKV) {
+      if (which < 2) {
+        // RoPE on pairs (d, d + D/2) of each head in the tile, at the token's position in its sequence:
+        // the angle pos * theta in double, reduced to [-pi, pi] in double, then sine / cosine in float
+        constexpr double kTwoPi = 6.283185307179586476925286766559;
+        for (int e = tid; e < 64 * (NT / 2); e += 256) {
+          const int row = e / (NT / 2), pc = e % (NT / 2);
+          const int hc = pc / (D / 2), i = pc % (D / 2);
+          const int col = hc * D + i;
+          const int pos = (mh + row) % s.S;
+          const double ang = (double)pos * theta[i];
+          const double red = fma(-rint(ang * (1.0 / kTwoPi)), kTwoPi, ang);
+          float sv, c;
+          sincosf((float)red, &sv, &c);
+          const float x1 = Cs[row * CST + col], x2 = Cs[row * CST + col + D / 2];
+          Cs[row * CST + col] = x1 * c - x2 * sv;
+          Cs[row * CST + col + D / 2] = x2 * c + x1 * sv;
         }
         __syncthreads();
-        address_from_summary<D>(cs, kbar, logit, ep.addr + (size_t)bh * s.nb + i,
-                                ep.alt ? ep.alt + (size_t)bh * s.nb + i : nullptr, s);
-        __syncthreads();  // kbar and logit are rewritten next
+      }
+    }
+    // ---- whole rows out as 16-byte vectors; the stored (rounded) values stay in LDS
+    for (int e = tid; e < 64 * (NT / VEC); e += 256) {
+      const int row = e / (NT / VEC), cv = e % (NT / VEC);
+      const int m = mh + row;
+      T v[VEC];
+#pragma unroll
+      for (int x = 0; x < VEC; ++x) {
+        v[x] = (T)Cs[row * CST + cv * VEC + x];
+        Cs[row * CST + cv * VEC + x] = (float)v[x];
+      }
+      if (m < M) {
+        const int n = n0 + cv * VEC;
+        size_t off;
+        if constexpr (QKV) {
+          const int b = m / s.S, t = m % s.S, h = n / D;
+          off = (((size_t)b * s.H + h) * s.S + t) * D + n % D;
+        } else {
+          off = (size_t)m * Nm + n;
+        }
+        *(u32x4*)(Cm + off) = *(const u32x4*)v;
+      }
+    }
+    if constexpr (QKV) {
+      if (which == 1) {  // uniform for the work-group
+        __shared__ float kbar[D];
+        __shared__ float logit[kMaxCodesTotal];
+        __syncthreads();
+        // ---- K: each (head, block) in these rows: summary = mean of its stored key rows (added in
+        // row order), then its product address (and alternate)
+        for (int hc = 0; hc < NT / D; ++hc) {
+          const int h = (n0 + hc * D) / D;
+          CodeSlice<D> cs;
+          cs.load(ep.cb, ep.bias, h, s);
+          for (int u = 0; u < 64 / s.blk; ++u) {
+            const int mb = mh + u * s.blk;  // first row of the block (blocks never straddle sequences)
+            if (mb >= M) break;             // uniform
+            const int b = mb / s.S, i = (mb % s.S) / s.blk;
+            const int bh = b * s.H + h;
+            if (tid < D) {
+              float a = 0.f;
+              for (int rr = 0; rr < s.blk; ++rr) a += Cs[(u * s.blk + rr) * CST + hc * D + tid];
+              const float mval = a / (float)s.blk;
+              kbar[tid] = mval;
+              ep.ksum[((size_t)bh * s.nb + i) * D + tid] = mval;
+            }
+            if (ep.cell_zero && i < s.ne) {
+              int32_t* crow = ep.cell_zero + (size_t)bh * s.cells_per_bh + cell_row(i, s.ne);
+              for (int c = tid; c < s.ne - i; c += 256) crow[c] = 0;
+            }
+            __syncthreads();
+            address_from_summary<D>(cs, kbar, logit, ep.addr + (size_t)bh * s.nb + i,
+                                    ep.alt ? ep.alt + (size_t)bh * s.nb + i : nullptr, s);
+            __syncthreads();  // kbar and logit are rewritten next
+          }
+        }
       }
     }
   }
@@ -347,6 +366,12 @@ hipError_t transpose(const void* in, void* out, int R, int Cc, hipStream_t st) {
   return hipGetLastError();
 }
 
+// The output projection over at least this many rows uses 128-row tiles (64 x 64 per wave: half the
+// LDS operand reads per flop of 64-row tiles; 45 -> 40 us at 32K x 512 x 512).  The fused projection
+// keeps 64-row tiles: at 128 rows its registers allow two waves per SIMD and it ran slower
+// (143 -> 172 us).
+constexpr int kBigM = 16384;
+
 // Largest output tile width (128, 64, 32) dividing Nm and, for the fused projection, holding whole
 // heads; 0 when none.
 int mm_tile(int Nm, int D, bool qkv) {
@@ -367,8 +392,8 @@ hipError_t qkv_launch(const Shape& s, const void* x, const void* wq, const void*
   if ((e = transpose<T>(wq, t0, s.W, Nm, st)) != hipSuccess) return e;
   if ((e = transpose<T>(wk, t1, s.W, Nm, st)) != hipSuccess) return e;
   if ((e = transpose<T>(wv, t2, s.W, Nm, st)) != hipSuccess) return e;
-  hipLaunchKernelGGL((k_mm<T, NT, false, true, D>), dim3((M + 63) / 64, 3 * Nm / NT), dim3(256), 0, st, (const T*)x,
-                     t0, t1, t2, (T*)q, (T*)k, (T*)v, M, Nm, s.W, hm, ep, s);
+  hipLaunchKernelGGL((k_mm<T, 64, NT, false, true, D>), dim3((M + 63) / 64, 3 * Nm / NT), dim3(256), 0, st,
+                     (const T*)x, t0, t1, t2, (T*)q, (T*)k, (T*)v, M, Nm, s.W, hm, ep, s);
   return hipGetLastError();
 }
 
@@ -403,8 +428,12 @@ hipError_t out_launch(const Shape& s, const void* o, const void* wo, void* delta
   T* t = (T*)wt + 3 * (size_t)Kd * s.W;  // after the three projection weights
   hipError_t e = transpose<T>(wo, t, Kd, Nm, st);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_mm<T, NT, true, false, 0>), dim3((M + 63) / 64, Nm / NT), dim3(256), 0, st, (const T*)o,
-                     t, t, t, (T*)delta, (T*)delta, (T*)delta, M, Nm, Kd, hm, none, s);
+  if (M >= kBigM)
+    hipLaunchKernelGGL((k_mm<T, 128, NT, true, false, 0>), dim3((M + 127) / 128, Nm / NT), dim3(256), 0, st,
+                       (const T*)o, t, t, t, (T*)delta, (T*)delta, (T*)delta, M, Nm, Kd, hm, none, s);
+  else
+    hipLaunchKernelGGL((k_mm<T, 64, NT, true, false, 0>), dim3((M + 63) / 64, Nm / NT), dim3(256), 0, st,
+                       (const T*)o, t, t, t, (T*)delta, (T*)delta, (T*)delta, M, Nm, Kd, hm, none, s);
   return hipGetLastError();
 }
 

@@ -90,3 +90,40 @@ def test_mixer_matches_oracle(gpu_lib, name):
     assert err <= TOL[w.dtype]
     if name == "redirect":
         assert int(res["overflow"].sum()) >= 0 and int(res["redir_off"][..., -1].sum()) > 0
+
+
+def test_mixer_large_tiles(gpu_lib):
+    """16384 rows: the output projection takes its 128-row tiles.  Summaries and addresses of every
+    block against the oracle's projections, and the delta on sampled tokens (gathered attention with
+    the GPU's selection, then the output projection)."""
+    mdr = gpu_lib
+    w = dataclasses.replace(BASE, batch=1, heads=2, seq=16384, head_dim=64, block=64, width=256, subspaces=2,
+                            codes=16, capacity=4, probes=4, dtype="bf16")
+    inp = synth.make_mixer_inputs(w, 1)
+    cfg = cfg_of(mdr, w)
+    t = {n: dev(inp[n], torch.bfloat16) for n in ("x", "wq", "wk", "wv", "wo")}
+    cb = dev(inp["codebook"], torch.float32)
+    delta = torch.empty_like(t["x"])
+    rt = mdr.routing_buffers(cfg)
+    mdr.mdr_mixer_forward(cfg, t["x"], t["wq"], t["wk"], t["wv"], t["wo"], cb, None, delta, rt, mdr.workspace(cfg))
+    torch.cuda.synchronize()
+    res = {n: host(v) for n, v in rt.items()}
+    q, k, v = (oracle.round_to_bf16(a) for a in oracle.mixer_qkv(inp["x"], inp["wq"], inp["wk"], inp["wv"], w))
+    rng = np.random.default_rng(3)
+    toks = np.sort(rng.choice(w.seq, size=64, replace=False))
+    o = np.zeros((len(toks), w.heads * w.head_dim))
+    near = 0
+    for h in range(w.heads):
+        ks = oracle.block_summaries(k[0, h].astype(np.float32), w.block)
+        scale = max(1.0, float(np.abs(ks).max()))
+        np.testing.assert_allclose(res["ksum"][0, h], ks, rtol=0, atol=2e-3 * scale)
+        _, addr, margin = oracle.block_addresses(ks, inp["codebook"][h], None)
+        sure = margin.min(axis=1) > NEAR
+        near += int((~sure).sum())
+        assert np.array_equal(res["addr"][0, h][sure], addr[sure]), h
+        o[:, h * w.head_dim:(h + 1) * w.head_dim] = oracle.attention_packed(
+            q[0, h], k[0, h], v[0, h], res["sel"][0, h][toks], w.block, w.local, tokens=toks)
+    ref = o @ inp["wo"].astype(np.float64)
+    err = float(np.abs(host(delta)[0, toks] - ref).max())
+    print(f"large tiles: address near-ties {near}, sampled delta max abs err {err:.3g}")
+    assert err <= TOL["bf16"]
