@@ -32,6 +32,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -240,10 +241,21 @@ def stage_bytes(w):
 
 
 def source_digest(kernel):
-    """Digest of the kernel's source file and the shared device header it includes."""
+    """Digest of the kernel's source file and every project header it includes (transitively)."""
+    csrc = os.path.join(ROOT, "learned_product_hash_amd", "csrc")
+    seen, todo = [], [KERNEL_SOURCE[kernel]]
+    while todo:
+        f = todo.pop(0)
+        if f in seen:
+            continue
+        seen.append(f)
+        path = os.path.join(csrc, f) if f != "mdr.h" else os.path.join(ROOT, "include", f)
+        text = open(path, "rb").read()
+        todo += [m.decode() for m in re.findall(rb'#include "([^"]+)"', text)]
     h = hashlib.sha256()
-    for f in (KERNEL_SOURCE[kernel], "mdr_internal.h"):
-        h.update(open(os.path.join(ROOT, "learned_product_hash_amd", "csrc", f), "rb").read())
+    for f in sorted(seen):
+        path = os.path.join(csrc, f) if f != "mdr.h" else os.path.join(ROOT, "include", f)
+        h.update(open(path, "rb").read())
     return h.hexdigest()[:16]
 
 

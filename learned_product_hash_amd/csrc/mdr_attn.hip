@@ -61,7 +61,26 @@ __global__ __launch_bounds__(256) void k_pair_bin(const int32_t* __restrict__ se
 // split c % splits): each wave gathers 16 pairs' queries, S^T = K Q^T and O^T = V^T P^T run on
 // MFMA, and every pair's softmax partial is stored at [token][slot].  The next iteration's pair
 // ids and query rows are loaded before the current one is computed.
+//
+// Each cell's dense slots are read together with its count, so the first pair ids of every cell
+// are known when the scan ends: they are written to an LDS pair list in pair order and a pair's id
+// is then one LDS read.  Pairs past a cell's dense slots, or past the list's capacity, take the
+// other route (the cell by binary search over the prefix, then the id from the cell's row).
 constexpr int kRemoteWaves = 8;
+
+// Capacity of the remote kernel's LDS pair list: what is left of the LDS once the work-groups
+// that the K/V tile and the cell prefix allow (at most four: 32 waves per CU) have their share,
+// at most 2048 and a multiple of 64.  Host and device compute it from the same values.
+__host__ __device__ inline int remote_pair_cap(size_t kv_bytes, int ne) {
+  const size_t lim = 159 * 1024;  // 160 KiB less a margin for the static scratch
+  const size_t base = kv_bytes + (size_t)(ne + 1) * 4;
+  if (base >= lim) return 0;
+  size_t nwg = lim / base;
+  if (nwg > 4) nwg = 4;
+  size_t cap = (lim / nwg - base) / 4;
+  if (cap > 2048) cap = 2048;
+  return (int)(cap & ~(size_t)63);
+}
 
 template <typename T, int D, int BLK>
 __global__ __launch_bounds__(kRemoteWaves * 64) void k_attn_remote(const T* __restrict__ Q, const T* __restrict__ K,
@@ -76,7 +95,9 @@ __global__ __launch_bounds__(kRemoteWaves * 64) void k_attn_remote(const T* __re
   extern __shared__ __align__(16) char lds_raw[];
   T* Ks = (T*)lds_raw;
   T* Vx = Ks + TL::K_ELEMS;
-  int* pre = (int*)(Vx + TL::V_ELEMS);  // [ncell + 1] exclusive prefix of the cell counts
+  int* pre = (int*)(Vx + TL::V_ELEMS);  // [ne + 1] exclusive prefix of the cell counts
+  int* plist = pre + s.ne + 1;           // [pcap] pair ids in pair order (-2: read from the cell row)
+  const int pcap = remote_pair_cap(TL::LDS_BYTES, s.ne);
   __shared__ int scan_tmp[kRemoteWaves];
   const int i = blockIdx.x, bh = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -89,10 +110,22 @@ __global__ __launch_bounds__(kRemoteWaves * 64) void k_attn_remote(const T* __re
   int run = 0;
   for (int c0 = 0; c0 < ncell; c0 += NTHR) {
     const int c = c0 + tid;
-    const int v = c < ncell ? min(cellcnt[row0 + c], BLK) : 0;
+    int v = 0;
+    int4 dense = make_int4(-1, -1, -1, -1);
+    if (c < ncell) {  // the count and the dense slots in one round trip
+      v = cellcnt[row0 + c];
+      dense = *(const int4*)(bins + (row0 + c) * kCellDense);
+      v = min(v, BLK);
+    }
     int tot;
     const int ex = block_exclusive_scan<NTHR>(v, scan_tmp, &tot);
-    if (c < ncell) pre[c] = run + ex;
+    if (c < ncell) {
+      const int b0 = run + ex;
+      pre[c] = b0;
+      const int n = min(v, pcap - b0);  // entries of this cell that fall inside the list
+      for (int p = 0; p < n; ++p)
+        plist[b0 + p] = p == 0 ? dense.x : p == 1 ? dense.y : p == 2 ? dense.z : p == 3 ? dense.w : -2;
+    }
     run += tot;
   }
   if (tid == 0) pre[ncell] = run;
@@ -106,6 +139,10 @@ __global__ __launch_bounds__(kRemoteWaves * 64) void k_attn_remote(const T* __re
   auto pair_at = [&](int it) __attribute__((always_inline)) -> int {
     const int pidx = it * PER_IT + wave * 16 + (lane & 15);
     if (pidx >= total) return -1;
+    if (pidx < pcap) {
+      const int p = plist[pidx];
+      if (p != -2) return p;
+    }
     int lo = 0, hi = ncell - 1;  // the cell whose range holds pidx
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
@@ -392,7 +429,7 @@ hipError_t launch_pair_bin(const Shape& s, const int32_t* sel, int32_t* cellcnt,
 
 size_t remote_lds_bytes(const Shape& s) {
   const size_t kv = s.dtype == MDR_BF16 ? remote_lds_t<bf16>(s) : remote_lds_t<float>(s);
-  return kv + (size_t)(s.ne + 1) * 4;
+  return kv + (size_t)(s.ne + 1) * 4 + (size_t)remote_pair_cap(kv, s.ne) * 4;
 }
 
 hipError_t launch_attend(const Shape& s, const void* q, const void* k, const void* v, const int32_t* sel, void* out,

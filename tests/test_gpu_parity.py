@@ -321,3 +321,43 @@ def test_generic_probe_kernel(gpu_lib, name, over):
             ref = attention_rows(w, inp, res["sel"][b, h], b, h, None, dense=w.seq <= 4096)
             assert np.abs(res["out"][b, h] - ref).max() <= TOL[w.dtype]
     print(f"{name} {over}: selection near-ties {near}")
+
+
+def hot_block_selection(w, seed):
+    """Every eligible token selects block 0 in slot 0; each other slot holds a seeded random eligible
+    block (blocks 1 .. j - L, none twice for one token, as the router selects) or nothing."""
+    rng = np.random.default_rng(seed)
+    B, H, S, R = w.batch, w.heads, w.seq, w.remote
+    j = np.arange(S) // w.block
+    sel = np.full((B, H, S, R), -1, dtype=np.int32)
+    sel[:, :, j >= w.local, 0] = 0
+    for r in range(1, R):
+        x = rng.integers(1, np.maximum(j - w.local + 1, 2), size=(B, H, S))
+        keep = (j - w.local >= 1) & (rng.random((B, H, S)) < 0.7) & np.all(sel[..., :r] != x[..., None], axis=-1)
+        sel[..., r] = np.where(keep, x, -1)
+    return sel
+
+
+@pytest.mark.parametrize("name", ["sweep", "long"])
+def test_stage_attend_hot_block(gpu_lib, name):
+    """A block that every eligible token selects: its pairs outnumber the remote kernel's LDS pair list
+    (the rest are found by the cell prefix), and each of its cells is full (slots past the dense table
+    are read from the cell rows)."""
+    mdr = gpu_lib
+    w = small(name)
+    inp = synth.make_core_inputs(w, 7)
+    sel = hot_block_selection(w, 7)
+    cfg = cfg_of(mdr, w)
+    dt = io_dtype(w)
+    q, k, v = (dev(inp[n], dt) for n in ("q", "k", "v"))
+    out = torch.empty_like(q)
+    mdr.mdr_stage_attend(cfg, q, k, v, dev(sel), out, mdr.workspace(cfg))
+    torch.cuda.synchronize()
+    out = host(out)
+    err = 0.0
+    for b in range(w.batch):
+        for h in range(w.heads):
+            ref = attention_rows(w, inp, sel[b, h], b, h, None, dense=w.seq <= 4096)
+            err = max(err, float(np.abs(out[b, h] - ref).max()))
+    print(f"{name}: block 0 pairs per head {int((sel[0, 0] == 0).sum())}, max abs err {err:.3g}")
+    assert err <= TOL[w.dtype]
