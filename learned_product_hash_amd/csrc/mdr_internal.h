@@ -37,6 +37,7 @@ struct Shape {
 };
 
 constexpr int kProbeThreads = 128;  // query tokens per probe work-group (one per lane)
+constexpr int kProbeFixedThreads = 256;  // the same for the compile-time specialised probe
 
 // Device buffers of one call (workspace regions or caller-provided outputs).
 struct Buffers {

@@ -640,12 +640,12 @@ __device__ inline int operand_dim(int s4, int x) {
 constexpr int probe_min_waves(int bytes, int D, int C) { return bytes == 2 && D <= 64 && C <= 16 ? 4 : 1; }
 
 template <typename T, int D, int G, int C, int P, int R, bool FUSED>
-__global__ __launch_bounds__(kProbeThreads) __attribute__((amdgpu_waves_per_eu(probe_min_waves((int)sizeof(T), D, C)))) void k_probe_fixed(
+__global__ __launch_bounds__(kProbeFixedThreads) __attribute__((amdgpu_waves_per_eu(probe_min_waves((int)sizeof(T), D, C)))) void k_probe_fixed(
     const T* __restrict__ Q, const float* __restrict__ cb, const float* __restrict__ bias,
     const float* __restrict__ ksum, const int32_t* __restrict__ off, const int32_t* __restrict__ idx,
     const int32_t* __restrict__ force, int32_t* __restrict__ sel, int32_t* __restrict__ ncand,
     int32_t* __restrict__ cellcnt, int32_t* __restrict__ bins, FusedPost fp, ProbeExtra ex, Shape s) {
-  constexpr int NT = kProbeThreads;
+  constexpr int NT = kProbeFixedThreads;
   static_assert(NT % 64 == 0, "whole waves of 64 tokens");
   constexpr bool BF = std::is_same<T, bf16>::value;
   constexpr int CP = (C + 15) & ~15;
@@ -890,7 +890,7 @@ __global__ __launch_bounds__(kProbeThreads) __attribute__((amdgpu_waves_per_eu(p
     }
   }
   // ---- the work-group's candidates as one list (token-major) in LDS, in the place of mu
-  __shared__ int scan_tmp[kProbeThreads / 64];
+  __shared__ int scan_tmp[NT / 64];
   int total;
   const int base = block_exclusive_scan<NT>(nc, scan_tmp, &total);
   int* clist = (int*)smem;                // [total] (local token << 16) | block
@@ -1068,14 +1068,14 @@ hipError_t probe_fixed_launch_t(const Shape& s, const void* q, const float* cb, 
                                 const int32_t* off, const int32_t* idx, const int32_t* force, int32_t* sel,
                                 int32_t* ncand, int32_t* cellcnt, int32_t* bins, const FusedPost& fp,
                                 const ProbeExtra& ex, hipStream_t st) {
-  dim3 grid((s.S + kProbeThreads - 1) / kProbeThreads, s.B * s.H);
+  dim3 grid((s.S + kProbeFixedThreads - 1) / kProbeFixedThreads, s.B * s.H);
   const size_t lds = probe_lds_bytes(s);
   if (lds > 65536) {
     hipError_t e = hipFuncSetAttribute((const void*)k_probe_fixed<T, D, G, C, P, R, FUSED>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((k_probe_fixed<T, D, G, C, P, R, FUSED>), grid, dim3(kProbeThreads), lds, st, (const T*)q, cb,
+  hipLaunchKernelGGL((k_probe_fixed<T, D, G, C, P, R, FUSED>), grid, dim3(kProbeFixedThreads), lds, st, (const T*)q, cb,
                      bias, ksum, off, idx, force, sel, ncand, cellcnt, bins, fp, ex, s);
   return hipGetLastError();
 }
@@ -1168,7 +1168,7 @@ size_t probe_lds_bytes(const Shape& s) {
   const int CP = (s.C + 15) & ~15;
   if (s.fixed_probe) {
     // mu rows during the logits, then the work-group's candidate list (block ids and scores)
-    const size_t mu_w = (size_t)kProbeThreads * (s.G * CP + 1), pairs_w = (size_t)kProbeThreads * s.M * 2;
+    const size_t mu_w = (size_t)kProbeFixedThreads * (s.G * CP + 1), pairs_w = (size_t)kProbeFixedThreads * s.M * 2;
     return ((mu_w > pairs_w ? mu_w : pairs_w) + (s.csr_lds ? (size_t)(s.A + 1 + s.ne) : 0)) * 4;
   }
   const int Pg = s.P < s.C ? s.P : s.C;
@@ -1210,7 +1210,7 @@ hipError_t launch_post_redirect(const Shape& s, const int32_t* addr, const int32
 bool probe_fuses_post(const Shape& s) {
   // the fixed probe stages the addresses and list cursors in its mu region
   const int CP = (s.C + 15) & ~15;
-  return s.fixed_probe && (long long)s.ne + s.A <= (long long)kProbeThreads * (s.G * CP + 1);
+  return s.fixed_probe && (long long)s.ne + s.A <= (long long)kProbeFixedThreads * (s.G * CP + 1);
 }
 
 }  // namespace mdr
