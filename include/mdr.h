@@ -189,8 +189,9 @@ mdr_status mdr_routed_attention(const mdr_config* cfg, const void* q, const void
  * events[k] (a hipEvent_t created by the caller) is recorded just before the
  * k-th kernel of the core path and events[MDR_CORE_KERNELS] after the last one.
  * A kernel a configuration does not need (attn_remote when R = 0 or nb <= L)
- * gets two adjacent events.  Everything else is as in
- * mdr_routed_attention; a NULL `events` array is rejected. */
+ * gets two adjacent events.  A NULL entry records nothing at that point (so a
+ * caller can time one kernel alone); a NULL `events` array is rejected.
+ * Everything else is as in mdr_routed_attention. */
 mdr_status mdr_routed_attention_profiled(const mdr_config* cfg, const void* q, const void* k, const void* v,
                                          const float* codebook, const float* code_bias, const int32_t* force,
                                          void* out, const mdr_routing* routing, void* workspace,
@@ -295,8 +296,9 @@ mdr_status mdr_stage_attend_backward(const mdr_config* cfg, const void* q, const
 
 /* Profiling form of mdr_stage_attend_backward: events[k] (hipEvent_t created
  * by the caller) is recorded on `stream` just before the k-th stage above and
- * events[MDR_BACKWARD_KERNELS] after the last.  A NULL `events` array or
- * entry is rejected; everything else as in mdr_stage_attend_backward. */
+ * events[MDR_BACKWARD_KERNELS] after the last.  A NULL entry records nothing
+ * at that point; a NULL `events` array is rejected.  Everything else as in
+ * mdr_stage_attend_backward. */
 mdr_status mdr_stage_attend_backward_profiled(const mdr_config* cfg, const void* q, const void* k,
                                               const void* v, const int32_t* sel, const void* out,
                                               const float* lse, const void* d_out, void* dq, void* dk,

@@ -215,24 +215,24 @@ mdr_status run_core(const Shape& s, const void* q, const void* k, const void* v,
                     const int32_t* force, void* out, const Buffers& b, hipStream_t st, hipEvent_t* ev = nullptr,
                     bool have_address = false) {
   const bool remote = s.R > 0 && s.ne > 0;
-  if (ev) MDR_TRY(hipEventRecord(ev[0], st));
+  MDR_TRY(mark_event(ev, 0, st));
   const bool redirect = s.policy == MDR_OVERFLOW_REDIRECT;
   if (!have_address)
     MDR_TRY(launch_address(s, k, cb, bias, b.ksum, b.addr, remote ? b.cellcnt : nullptr, st, 0, -1,
                            redirect ? b.alt : nullptr));
-  if (ev) MDR_TRY(hipEventRecord(ev[1], st));
+  MDR_TRY(mark_event(ev, 1, st));
   // the posting lists are built inside the probe kernel where a specialised probe exists (the post
   // interval of a profiled call is then empty); the redirect lists need the whole CSR first
   const bool fused = probe_fuses_post(s) && !redirect;
   if (!fused) MDR_TRY(launch_post(s, b.addr, b.off, b.idx, b.overflow, st));
   if (redirect) MDR_TRY(launch_post_redirect(s, b.addr, b.alt, b.off, b.idx, b.roff, b.ridx, b.rtime, b.overflow, st));
-  if (ev) MDR_TRY(hipEventRecord(ev[2], st));
+  MDR_TRY(mark_event(ev, 2, st));
   const FusedPost fp{b.addr, b.off, b.idx, b.overflow};
   const ProbeExtra ex{redirect ? b.roff : nullptr, b.ridx, b.rtime, b.ndrop};
   MDR_TRY(launch_probe_rerank(s, q, cb, bias, b.ksum, b.off, b.idx, force, b.sel, b.ncand,
                               remote ? b.cellcnt : nullptr, remote ? b.bins : nullptr, st, fused ? &fp : nullptr, ex));
   MDR_TRY(launch_attend(s, q, k, v, b.sel, out, b, st, ev ? ev + 3 : nullptr));
-  if (ev) MDR_TRY(hipEventRecord(ev[MDR_CORE_KERNELS], st));
+  MDR_TRY(mark_event(ev, MDR_CORE_KERNELS, st));
   return MDR_OK;
 }
 
@@ -294,8 +294,6 @@ mdr_status mdr_routed_attention_profiled(const mdr_config* cfg, const void* q, c
   if (st != MDR_OK) return st;
   s.W = 0;
   if (!q || !k || !v || !codebook || !out || !events) return MDR_ERR_INVALID_ARG;
-  for (int i = 0; i <= MDR_CORE_KERNELS; ++i)
-    if (!events[i]) return MDR_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(codebook) ||
       !routing_aligned(routing))
     return MDR_ERR_INVALID_ARG;
@@ -423,13 +421,13 @@ static mdr_status backward_core(const mdr_config* cfg, const void* q, const void
   st = check_workspace(s, workspace, workspace_bytes, &b);
   if (st != MDR_OK) return st;
   hipStream_t hs = (hipStream_t)stream;
-  if (ev) MDR_TRY(hipEventRecord(ev[0], hs));
+  MDR_TRY(mark_event(ev, 0, hs));
   if (s.R > 0 && s.ne > 0) {
     MDR_TRY(launch_fill(b.cellcnt, (long long)s.B * s.H * s.cells_per_bh, 0, hs));
     MDR_TRY(launch_pair_bin_ordered(s, sel, b.cellcnt, b.bins, hs));
   }
   MDR_TRY(launch_attend_backward(s, q, k, v, sel, out, lse, d_out, dq, dk, dv, b, hs, ev ? ev + 1 : nullptr));
-  if (ev) MDR_TRY(hipEventRecord(ev[MDR_BACKWARD_KERNELS], hs));
+  MDR_TRY(mark_event(ev, MDR_BACKWARD_KERNELS, hs));
   return MDR_OK;
 }
 
@@ -445,8 +443,6 @@ mdr_status mdr_stage_attend_backward_profiled(const mdr_config* cfg, const void*
                                               const void* d_out, void* dq, void* dk, void* dv, void* workspace,
                                               size_t workspace_bytes, void* const* events, void* stream) {
   if (!events) return MDR_ERR_INVALID_ARG;
-  for (int i = 0; i <= MDR_BACKWARD_KERNELS; ++i)
-    if (!events[i]) return MDR_ERR_INVALID_ARG;
   return backward_core(cfg, q, k, v, sel, out, lse, d_out, dq, dk, dv, workspace, workspace_bytes,
                        (hipEvent_t*)events, stream);
 }

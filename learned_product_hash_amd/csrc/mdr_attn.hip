@@ -355,7 +355,7 @@ hipError_t attend_impl(const Shape& s, const void* q, const void* k, const void*
   const size_t lds = TL::LDS_BYTES;
   const bool remote = s.R > 0 && s.ne > 0;
   hipError_t e;
-  if (ev && (e = hipEventRecord(ev[0], st)) != hipSuccess) return e;
+  if ((e = mark_event(ev, 0, st)) != hipSuccess) return e;
   if (remote) {
     const size_t rl = remote_lds_bytes(s);
     if (rl > 65536 && (e = hipFuncSetAttribute((const void*)k_attn_remote<T, D, BLK>,
@@ -366,7 +366,7 @@ hipError_t attend_impl(const Shape& s, const void* q, const void* k, const void*
                        (const T*)k, (const T*)v, b.cellcnt, b.bins, (T*)b.part_o, b.part_ml, s);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  if (ev && (e = hipEventRecord(ev[1], st)) != hipSuccess) return e;
+  if ((e = mark_event(ev, 1, st)) != hipSuccess) return e;
   return s.R >= 2   ? launch_local<T, D, BLK, 2>(s, q, k, v, sel, out, b, st)
          : s.R == 1 ? launch_local<T, D, BLK, 1>(s, q, k, v, sel, out, b, st)
                     : launch_local<T, D, BLK, 0>(s, q, k, v, sel, out, b, st);

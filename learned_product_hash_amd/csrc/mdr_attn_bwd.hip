@@ -426,7 +426,7 @@ hipError_t bwd_impl(const Shape& s, const void* q, const void* k, const void* v,
   constexpr int LPT = D * (int)sizeof(T) / 16;
   const long long blocks = (n * LPT + 255) / 256;
   hipError_t e;
-  if (ev && (e = hipEventRecord(ev[0], st)) != hipSuccess) return e;
+  if ((e = mark_event(ev, 0, st)) != hipSuccess) return e;
   hipLaunchKernelGGL((k_bwd_dot<T, D>), dim3((unsigned)blocks), dim3(256), 0, st, (const T*)o, (const T*)d_o,
                      b.dvec, n);
   if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -434,7 +434,7 @@ hipError_t bwd_impl(const Shape& s, const void* q, const void* k, const void* v,
   if (kl > 65536 && (e = hipFuncSetAttribute((const void*)k_bwd_kv<T, D, BLK>,
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)kl)) != hipSuccess)
     return e;
-  if (ev && (e = hipEventRecord(ev[1], st)) != hipSuccess) return e;
+  if ((e = mark_event(ev, 1, st)) != hipSuccess) return e;
   const unsigned nwg = (unsigned)((long long)s.nb * s.B * s.H);
   hipLaunchKernelGGL((k_bwd_kv<T, D, BLK>), dim3(nwg), dim3(BLK * 4), kl, st, (const T*)q,
                      (const T*)k, (const T*)v, (const T*)d_o, lse, b.dvec, b.cellcnt, b.bins, (T*)b.part_o,
@@ -444,7 +444,7 @@ hipError_t bwd_impl(const Shape& s, const void* q, const void* k, const void* v,
   if (ql > 65536 && (e = hipFuncSetAttribute((const void*)k_bwd_q<T, D, BLK>,
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)ql)) != hipSuccess)
     return e;
-  if (ev && (e = hipEventRecord(ev[2], st)) != hipSuccess) return e;
+  if ((e = mark_event(ev, 2, st)) != hipSuccess) return e;
   hipLaunchKernelGGL((k_bwd_q<T, D, BLK>), dim3(nwg), dim3(BLK * 4), ql, st, (const T*)q, (const T*)k,
                      (const T*)v, (const T*)d_o, lse, b.dvec, sel, (const T*)b.part_o, (T*)dq, s);
   return hipGetLastError();

@@ -176,6 +176,12 @@ __device__ inline int block_exclusive_scan(int v, int* tmp, int* total) {
   return before + x - v;
 }
 
+// Profiling events: entry i of an optional event array is recorded on the stream when present
+// (a null array or a null entry records nothing).
+inline hipError_t mark_event(hipEvent_t* ev, int i, hipStream_t st) {
+  return ev && ev[i] ? hipEventRecord(ev[i], st) : hipSuccess;
+}
+
 // Launchers (return hipGetLastError()).
 // cell_zero (optional): the address kernel of block i clears the cell counters of row i.
 // Blocks [i0, i0 + n) (n < 0: to the end).

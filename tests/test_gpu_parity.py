@@ -361,3 +361,34 @@ def test_stage_attend_hot_block(gpu_lib, name):
             err = max(err, float(np.abs(out[b, h] - ref).max()))
     print(f"{name}: block 0 pairs per head {int((sel[0, 0] == 0).sum())}, max abs err {err:.3g}")
     assert err <= TOL[w.dtype]
+
+
+@pytest.mark.parametrize("marked", [None, 2, 3])
+def test_profiled_form_gives_the_same_results(gpu_lib, marked):
+    """mdr_routed_attention_profiled with every event, or with events around one kernel only (null
+    entries elsewhere), runs the same kernels: results bit for bit those of the plain call, and
+    every recorded interval is non-negative."""
+    mdr = gpu_lib
+    w = small("recall", batch=2)
+    inp = synth.make_core_inputs(w, 8)
+    plain = run_core(mdr, w, inp)
+    cfg = cfg_of(mdr, w)
+    q, k, v = (dev(inp[n], io_dtype(w)) for n in ("q", "k", "v"))
+    out = torch.empty_like(q)
+    rt = mdr.routing_buffers(cfg)
+    from bench import HipEvents
+
+    hip = HipEvents()
+    nk = mdr.MDR_CORE_KERNELS
+    handles = hip.create(nk + 1)
+    events = list(handles) if marked is None else [
+        handles[i] if i in (marked, marked + 1) else None for i in range(nk + 1)]
+    mdr.mdr_routed_attention_profiled(cfg, q, k, v, dev(inp["codebook"], torch.float32), None, None, out, events,
+                                      rt, mdr.workspace(cfg))
+    torch.cuda.synchronize()
+    pairs = [(i, i + 1) for i in range(nk)] if marked is None else [(marked, marked + 1)]
+    assert all(hip.elapsed_ms(handles[a], handles[b]) >= 0 for a, b in pairs)
+    hip.destroy(handles)
+    assert np.array_equal(host(out), plain["out"])
+    for n, t in rt.items():
+        assert np.array_equal(host(t), plain[n]), n
