@@ -276,13 +276,27 @@ def load_traffic(w, kernel):
     return k["bytes_per_launch"]
 
 
-def attention_stage(w, t_att):
+def selected_set_bytes(w, pairs):
+    """What a per-query gather with no reuse across queries would read and write: per (token, head)
+    q, o and the local window's K/V (L blocks amortised per query block: L * D * 2e per token), plus
+    blk K/V rows per selected remote (token, slot) pair."""
+    e = 2 if w.dtype == "bf16" else 4
+    return w.batch * w.heads * w.seq * (2 * w.head_dim * e + w.local * w.head_dim * 2 * e) + \
+        pairs * w.block * w.head_dim * 2 * e
+
+
+def attention_stage(w, t_att, pairs):
     """The selected-set attention (remote + local kernels) against the HBM peak, two ways:
     (i) compulsory bytes (Q, K, V, O once + sel) / time; (ii) measured HBM bytes (FETCH_SIZE +
-    WRITE_SIZE of both kernels, when counters for these sources exist) / time."""
+    WRITE_SIZE of both kernels, when counters for these sources exist) / time; and (iii) the
+    selected-set bytes of a gather without reuse / time, which counts cache-served and regrouped
+    re-reads and so is not an HBM bandwidth."""
     alg = stage_bytes(w)
+    sel_b = selected_set_bytes(w, pairs)
     out = {"ms": round(t_att, 5), "alg_bytes": alg,
-           "frac_of_hbm_peak": round(alg / (t_att * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+           "frac_of_hbm_peak": round(alg / (t_att * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+           "selected_set_bytes": sel_b,
+           "selected_set_gbps_not_hbm": round(sel_b / (t_att * 1e-3) / 1e9, 1)}
     tr = [load_traffic(w, k) for k in ("attn_remote", "attn_local")]
     if all(t is not None for t in tr):
         gbps = sum(tr) / (t_att * 1e-3) / 1e9
@@ -805,7 +819,7 @@ def main(argv=None):
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": None if traffic is None else round(traffic)},
         "kernels": kernels,
-        "attention_stage": attention_stage(w, t_att),
+        "attention_stage": attention_stage(w, t_att, st["pairs"]),
         "plain_entry_point_ms_per_step": round(plain / a.steps * 1e3, 4),
         "event_overhead_ms": round(ev_overhead, 5),
         "profiled_step_ms_p10_p50_p90": run.step_quantiles,
