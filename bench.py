@@ -21,7 +21,7 @@ against 8 TB/s), every kernel's time and bytes, the fitted timing exponent over
     python bench.py --ingest-pmc FETCH.csv WRITE.csv
 turns two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of
 ``python bench.py --steps 3 --warmup 1 --calib-copy --no-cpu --no-sweep --no-decode --no-backward --no-stress
---no-mixer`` into
+--no-mixer --no-cold`` into
 profiles/traffic_<workload>.json (per-launch HBM bytes of every kernel,
 scaled by what the counters read for a plain elementwise copy of known size).
 """
@@ -69,9 +69,9 @@ CALIB_BYTES = 512 << 20
 HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000  # hipEventDisableSystemFence (hip_runtime_api.h)
 PMC_COMMANDS = [  # run from the repository root on one MI355X, TMPDIR=/tmp
     "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmcf -o f -- "
-    "python3 bench.py --steps 3 --warmup 1 --calib-copy --no-cpu --no-sweep --no-decode --no-backward --no-stress --no-mixer",
+    "python3 bench.py --steps 3 --warmup 1 --calib-copy --no-cpu --no-sweep --no-decode --no-backward --no-stress --no-mixer --no-cold",
     "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmcw -o w -- "
-    "python3 bench.py --steps 3 --warmup 1 --calib-copy --no-cpu --no-sweep --no-decode --no-backward --no-stress --no-mixer",
+    "python3 bench.py --steps 3 --warmup 1 --calib-copy --no-cpu --no-sweep --no-decode --no-backward --no-stress --no-mixer --no-cold",
 ]
 
 
@@ -89,6 +89,7 @@ def parse(argv=None):
     ap.add_argument("--no-backward", action="store_true", help="skip the attention-backward timing")
     ap.add_argument("--no-stress", action="store_true", help="skip the overflow stress test")
     ap.add_argument("--no-mixer", action="store_true", help="skip the mixer timing")
+    ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache steps")
     ap.add_argument("--mixer-only", action="store_true", help="time the mixer alone and print its JSON")
     ap.add_argument("--profile-name", default="routed_attention_kernels",
                     help="with --summarize-rocprof: file name stem of the summary under profiles/")
@@ -368,6 +369,33 @@ def timed_region(run, hip, steps, warmup):
     dom_ms = max(0.0, sum(hip.elapsed_ms(marks[2 * s], marks[2 * s + 1]) for s in range(steps)) / steps - overhead)
     hip.destroy(marks)
     return wall, per, overhead, dom, dom_ms
+
+
+def cold_region(run, hip, steps, overhead):
+    """Steps with the caches cold: before each step a 512 MiB buffer is written (twice the 256 MB
+    last-level cache of the chip, so neither it nor the L2s hold the inputs), outside the events
+    that bracket the step.  Returns the p10 / p50 / p90 step time and each kernel's average (ms)."""
+    import numpy as np
+    import torch
+
+    nk = run.mdr.MDR_CORE_KERNELS
+    flush = torch.empty(512 * 2**20 // 4, dtype=torch.float32, device="cuda")
+    events = hip.create(steps * (nk + 1))
+    for s in range(steps):
+        flush.fill_(float(s))
+        run.step(events[s * (nk + 1):(s + 1) * (nk + 1)])
+    torch.cuda.synchronize()
+    per = [0.0] * nk
+    totals = []
+    for s in range(steps):
+        ev = events[s * (nk + 1):(s + 1) * (nk + 1)]
+        for i in range(nk):
+            per[i] += hip.elapsed_ms(ev[i], ev[i + 1])
+        totals.append(hip.elapsed_ms(ev[0], ev[nk]))
+    hip.destroy(events)
+    del flush
+    q = [round(float(x), 4) for x in np.percentile(totals, [10, 50, 90])]
+    return q, [max(0.0, p / steps - overhead) for p in per]
 
 
 def plain_region(run, steps):
@@ -787,6 +815,7 @@ def main(argv=None):
     run = Run(mdr, w, a.seed)
     wall, per, ev_overhead, dom_i, dom_ms = timed_region(run, hip, a.steps, a.warmup)
     plain = plain_region(run, a.steps)
+    cold_q, cold_per = (None, None) if a.no_cold else cold_region(run, hip, min(a.steps, 20), ev_overhead)
     st = run.routing_stats()
     names = list(mdr.CORE_KERNELS)
     abytes = algorithmic_bytes(w, st)
@@ -823,6 +852,10 @@ def main(argv=None):
         "plain_entry_point_ms_per_step": round(plain / a.steps * 1e3, 4),
         "event_overhead_ms": round(ev_overhead, 5),
         "profiled_step_ms_p10_p50_p90": run.step_quantiles,
+        "cold_caches": None if cold_q is None else {
+            "note": "a 512 MiB write before each step evicts the last-level cache and the L2s; the step is "
+                    "bracketed by events, the write is not",
+            "step_ms_p10_p50_p90": cold_q, "kernels_ms": {n: round(ms, 5) for n, ms in zip(names, cold_per)}},
         "routing": st,
     }
     if not a.no_decode and a.workload == "sweep":
