@@ -1007,8 +1007,9 @@ __global__ __launch_bounds__(kProbeFixedThreads) __attribute__((amdgpu_waves_per
   if (!bins) return;  // uniform
   // ---- file each selected pair in its (remote block i, query block j) cell.  The work-group owns
   // the cells of its query blocks, so when they fit (in the place of mu) it counts them in LDS, stores
-  // each pair at the slot that count gives, and then writes the non-zero counts (the address kernel
-  // has cleared all of them); otherwise it appends with global atomics.
+  // each pair at the slot that count gives, and then the thread that filed a cell's first pair writes
+  // the cell's count (the address kernel has cleared all of them); otherwise it appends with global
+  // atomics.
   const int nqb = NT / s.blk;  // whole query blocks per work-group
   if (nqb * s.ne <= NT * MST) {
     int* cnt = (int*)mu;  // [nqb][ne]
@@ -1016,25 +1017,27 @@ __global__ __launch_bounds__(kProbeFixedThreads) __attribute__((amdgpu_waves_per
     for (int c = tid; c < nqb * s.ne; c += NT) cnt[c] = 0;
     lds_barrier();
     const int jb = tbase / s.blk;
+    const long long cbase = (long long)bh * s.cells_per_bh + j - s.L;  // cell (i, j) = cbase + cell_row(i) - i
+    uint32_t first = 0;  // bit r: this token filed the first pair of slot r's cell
     if (active) {
 #pragma unroll
       for (int r = 0; r < RK; ++r) {
         if (r < nr) {
           const int i = tri[r];
           const int pos = atomicAdd(&cnt[(j - jb) * s.ne + i], 1);
-          const long long cell = (long long)bh * s.cells_per_bh + cell_row(i, s.ne) + (j - i - s.L);
+          const long long cell = cbase + cell_row(i, s.ne) - i;
           if (pos < s.blk) *cell_slot(bins, s, cell, pos) = t * s.R + r;
+          if (pos == 0) first |= 1u << r;
         }
       }
     }
     lds_barrier();
-    for (int c = tid; c < nqb * s.ne; c += NT) {
-      const int n = cnt[c];
-      if (n > 0) {
-        const int jj = jb + c / s.ne, i = c % s.ne;
-        cellcnt[(long long)bh * s.cells_per_bh + cell_row(i, s.ne) + (jj - i - s.L)] = n;
+#pragma unroll
+    for (int r = 0; r < RK; ++r)
+      if (first >> r & 1u) {
+        const int i = tri[r];
+        cellcnt[cbase + cell_row(i, s.ne) - i] = cnt[(j - jb) * s.ne + i];
       }
-    }
   } else if (active) {
 #pragma unroll
     for (int r = 0; r < RK; ++r)
