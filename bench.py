@@ -243,8 +243,16 @@ def stage_bytes(w):
     return 4 * BH * w.seq * w.head_dim * e + BH * w.seq * w.remote * 4
 
 
+def strip_comments(text):
+    """C++ source without its comments and blank lines (a comment edit does not change a kernel)."""
+    text = re.sub(rb"/\*.*?\*/", b"", text, flags=re.S)
+    text = re.sub(rb"//[^\n]*", b"", text)
+    return b"\n".join(line.rstrip() for line in text.split(b"\n") if line.strip())
+
+
 def source_digest(kernel):
-    """Digest of the kernel's source file and every project header it includes (transitively)."""
+    """Digest of the code (comments stripped) of the kernel's source file and every project header
+    it includes (transitively)."""
     csrc = os.path.join(ROOT, "learned_product_hash_amd", "csrc")
     seen, todo = [], [KERNEL_SOURCE[kernel]]
     while todo:
@@ -258,7 +266,7 @@ def source_digest(kernel):
     h = hashlib.sha256()
     for f in sorted(seen):
         path = os.path.join(csrc, f) if f != "mdr.h" else os.path.join(ROOT, "include", f)
-        h.update(open(path, "rb").read())
+        h.update(strip_comments(open(path, "rb").read()))
     return h.hexdigest()[:16]
 
 

@@ -14,9 +14,10 @@
 //                  block j) -- by the probe kernel, or by k_pair_bin when a selection is passed in;
 //                  only the work-group owning query block j writes a cell, so no counter is hot
 //   k_attn_remote  one work-group per selected block (split when blocks are heavy): the block's
-//                  K/V is staged in LDS once, its pairs are walked 64 at a time, the pairs'
-//                  queries are gathered, S^T = K Q^T and O^T = V^T P^T run on MFMA, and each
-//                  pair's softmax partial (max, sum, normalised output) is stored
+//                  K/V is staged in LDS once, its pair ids go to an LDS list during the cell scan,
+//                  its pairs are walked 128 at a time (16 per wave), the pairs' queries are
+//                  gathered, S^T = K Q^T and O^T = V^T P^T run on MFMA, and each pair's softmax
+//                  partial (max, sum, normalised output) is stored
 //   k_attn_local   one work-group per query block: the L local blocks through LDS on MFMA with
 //                  the causal mask on the diagonal block and an online softmax, then the
 //                  remote partials of each token are merged in slot order and O is written.

@@ -3,6 +3,8 @@
 //   k_post           causal posting lists (histogram, wavefront scan, stable scatter) + overflow
 //   k_probe_rerank   per query token: probe scores, top-P addresses, candidate views,
 //                    rerank against the block summaries, top-R selection (+ forced target)
+//   k_probe_fixed    the same with the routing sizes fixed at compile time; it also builds the
+//                    posting lists in LDS and files the selected pairs into their cells
 //
 // The method (remio.ai, "Monodratic claims learned routing can make sparse causal attention
 // more selective", section "Monodratic turns sparse attention into a retrieval decision";
@@ -636,7 +638,7 @@ __device__ inline int operand_dim(int s4, int x) {
   return BF ? 32 * (x >> 3) + 8 * s4 + (x & 7) : s4 * (D / 4) + x;
 }
 
-// Small bf16 shapes keep four waves per SIMD, so that eight 128-token work-groups share a CU.
+// Small bf16 shapes keep four waves per SIMD, so that four 256-token work-groups share a CU.
 constexpr int probe_min_waves(int bytes, int D, int C) { return bytes == 2 && D <= 64 && C <= 16 ? 4 : 1; }
 
 template <typename T, int D, int G, int C, int P, int R, bool FUSED>
