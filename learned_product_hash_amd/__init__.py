@@ -1,5 +1,6 @@
-"""Python binding of libmdr.so, the gfx950 HIP library for the forward pass of
-Monodratic routed sparse causal attention.
+"""Python binding of libmdr.so, the gfx950 HIP library of Monodratic routed sparse
+causal attention: the routed forward path, the stateless mixer around it, the
+streaming decode step, and the attention backward under a fixed selection.
 
 Argument marshalling only: every step of the path runs in the library's HIP
 kernels.  torch supplies device memory and streams; it is imported before the
@@ -17,11 +18,14 @@ import os
 import torch  # noqa: F401  (loads the HIP runtime the library must share)
 
 __all__ = [
-    "LIB_PATH", "MdrError", "MdrConfig", "MdrRouting", "MDR_F32", "MDR_BF16", "config", "lib",
+    "LIB_PATH", "MdrError", "MdrConfig", "MdrRouting", "MdrDecodeView", "MDR_F32", "MDR_BF16",
+    "MDR_OVERFLOW_DROP", "MDR_OVERFLOW_REDIRECT", "config", "lib",
     "mdr_abi_version", "mdr_status_string", "mdr_check_config", "mdr_workspace_size",
-    "mdr_routed_attention", "mdr_routed_attention_profiled", "mdr_mixer_forward", "mdr_stage_address", "mdr_stage_post",
+    "mdr_routed_attention", "mdr_routed_attention_profiled", "MDR_CORE_KERNELS", "CORE_KERNELS",
+    "mdr_mixer_forward", "mdr_stage_address", "mdr_stage_post",
     "mdr_stage_probe_rerank", "mdr_stage_attend", "mdr_stage_attend_lse", "mdr_stage_attend_backward",
     "mdr_stage_attend_backward_profiled", "MDR_BACKWARD_KERNELS", "BACKWARD_KERNELS",
+    "mdr_decode_state_size", "decode_state", "mdr_decode_state_view", "mdr_decode_prime", "mdr_decode_step",
     "workspace", "routing_buffers",
 ]
 

@@ -48,6 +48,14 @@ def test_library_exports_every_declared_symbol(mdr):
     assert mdr.mdr_abi_version() == 2
 
 
+def test_binding_has_every_declared_entry_point(mdr):
+    """The Python binding is the thin layer over the C ABI: one function of the same name per
+    declared entry point."""
+    for name in declared_functions():
+        assert callable(getattr(mdr, name, None)), name
+        assert name in mdr.__all__, name
+
+
 def _good(**over):
     f = dict(batch=1, seq=4096, heads=8, head_dim=64, block=64, subspaces=2, codes=16, capacity=2, probes=4,
              remote=2, local=2, dtype="bf16")
