@@ -267,18 +267,38 @@ __global__ __launch_bounds__(256) void k_mm(const T* __restrict__ A, const T* __
     __syncthreads();
     if constexpr (QKV) {
       if (which < 2) {
-        // RoPE on pairs (d, d + D/2) of each head in the tile, at the token's position in its sequence:
-        // the angle pos * theta in double, reduced to [-pi, pi] in double, then sine / cosine in float
+        // RoPE on pairs (d, d + D/2) of each head in the tile, at the token's position in its sequence.
+        // A thread keeps one pair column and walks the rows RSTEP apart.  Its first row's angle
+        // pos * theta is formed in double, reduced to [-pi, pi] in double, and its sine / cosine taken
+        // in float; each further row rotates that (cosine, sine) by the angle of RSTEP positions (a
+        // few float ulps per step, at most 64 / RSTEP - 1 steps), unless the rows cross into the next
+        // sequence, where the angle is formed afresh.
         constexpr double kTwoPi = 6.283185307179586476925286766559;
-        for (int e = tid; e < 64 * (NT / 2); e += 256) {
-          const int row = e / (NT / 2), pc = e % (NT / 2);
-          const int hc = pc / (D / 2), i = pc % (D / 2);
-          const int col = hc * D + i;
-          const int pos = (mh + row) % s.S;
-          const double ang = (double)pos * theta[i];
+        constexpr int PCN = NT / 2;        // pair columns per row of the tile
+        constexpr int RSTEP = 256 / PCN;   // rows between a thread's consecutive elements
+        static_assert(256 % PCN == 0 && RSTEP <= 32, "whole rows per pass");
+        const int pc = tid % PCN;
+        const int hc = pc / (D / 2), i = pc % (D / 2);
+        const int col = hc * D + i;
+        auto angle = [&](int p, float* sv, float* c) __attribute__((always_inline)) {
+          const double ang = (double)p * theta[i];
           const double red = fma(-rint(ang * (1.0 / kTwoPi)), kTwoPi, ang);
-          float sv, c;
-          sincosf((float)red, &sv, &c);
+          sincosf((float)red, sv, c);
+        };
+        float sstep, cstep;
+        angle(RSTEP, &sstep, &cstep);
+        float sv = 0.f, c = 1.f;
+        int pos = -1;
+        for (int row = tid / PCN; row < 64; row += RSTEP) {
+          if (pos >= 0 && pos + RSTEP < s.S) {
+            pos += RSTEP;
+            const float c2 = c * cstep - sv * sstep;
+            sv = fmaf(sv, cstep, c * sstep);
+            c = c2;
+          } else {
+            pos = (mh + row) % s.S;
+            angle(pos, &sv, &c);
+          }
           const float x1 = Cs[row * CST + col], x2 = Cs[row * CST + col + D / 2];
           Cs[row * CST + col] = x1 * c - x2 * sv;
           Cs[row * CST + col + D / 2] = x2 * c + x1 * sv;
