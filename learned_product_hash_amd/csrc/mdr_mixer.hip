@@ -306,26 +306,33 @@ __global__ __launch_bounds__(256) void k_mm(const T* __restrict__ A, const T* __
         __syncthreads();
       }
     }
-    // ---- whole rows out as 16-byte vectors; the stored (rounded) values stay in LDS
-    for (int e = tid; e < 64 * (NT / VEC); e += 256) {
-      const int row = e / (NT / VEC), cv = e % (NT / VEC);
+    // ---- the rows out as 16-byte vectors.  Thread tid keeps row tid % 64 and takes its column
+    // chunks tid / 64, + 4, ...: the 64 lanes of a read are 64 rows (an odd row stride), so the reads
+    // hit distinct banks.  The K tile's stored (rounded) values stay in LDS for its summaries.
+    {
+      const int row = tid % 64;
       const int m = mh + row;
-      T v[VEC];
-#pragma unroll
-      for (int x = 0; x < VEC; ++x) {
-        v[x] = (T)Cs[row * CST + cv * VEC + x];
-        Cs[row * CST + cv * VEC + x] = (float)v[x];
+      [[maybe_unused]] int b = 0, t = 0;
+      if constexpr (QKV) {
+        b = m / s.S;
+        t = m % s.S;
       }
-      if (m < M) {
-        const int n = n0 + cv * VEC;
-        size_t off;
-        if constexpr (QKV) {
-          const int b = m / s.S, t = m % s.S, h = n / D;
-          off = (((size_t)b * s.H + h) * s.S + t) * D + n % D;
-        } else {
-          off = (size_t)m * Nm + n;
+      for (int cv = tid / 64; cv < NT / VEC; cv += 4) {
+        T v[VEC];
+#pragma unroll
+        for (int x = 0; x < VEC; ++x) {
+          v[x] = (T)Cs[row * CST + cv * VEC + x];
+          if (QKV && which == 1) Cs[row * CST + cv * VEC + x] = (float)v[x];
         }
-        *(u32x4*)(Cm + off) = *(const u32x4*)v;
+        if (m < M) {
+          const int n = n0 + cv * VEC;
+          size_t off;
+          if constexpr (QKV)
+            off = (((size_t)b * s.H + n / D) * s.S + t) * D + n % D;
+          else
+            off = (size_t)m * Nm + n;
+          *(u32x4*)(Cm + off) = *(const u32x4*)v;
+        }
       }
     }
     if constexpr (QKV) {
