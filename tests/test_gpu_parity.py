@@ -392,3 +392,32 @@ def test_profiled_form_gives_the_same_results(gpu_lib, marked):
     assert np.array_equal(host(out), plain["out"])
     for n, t in rt.items():
         assert np.array_equal(host(t), plain[n]), n
+
+
+@pytest.mark.parametrize("case", ["routing_limits", "block_limit"])
+def test_size_limits(gpu_lib, case):
+    """The largest sizes the library accepts.  routing_limits: 4 subspaces of 8 codes (4096
+    addresses, the address limit), 16 probes and 16 remote blocks (both limits), through the
+    generic probe kernel, checked on every token.  block_limit: 8192 blocks of 32 tokens (262144
+    tokens, the block limit), checked on sampled tokens."""
+    mdr = gpu_lib
+    if case == "routing_limits":
+        w = synth.workload("tiny", seq=16384, subspaces=4, codes=8, capacity=2, probes=16, remote=16, local=1)
+        toks = None
+    else:
+        w = synth.workload("tiny", seq=8192 * 32, capacity=4, probes=2, remote=2)
+        rng = np.random.default_rng(11)
+        toks = np.unique(np.concatenate([rng.choice(w.seq, 64, replace=False), [0, w.seq - 1]]))
+    assert mdr.mdr_check_config(cfg_of(mdr, w)) == 0
+    inp = synth.make_core_inputs(w, 4)
+    res = run_core(mdr, w, inp)
+    q, k, v = (inp[n][0, 0] for n in ("q", "k", "v"))
+    compare_addresses(w, inp, res["addr"][0, 0], 0, 0)
+    r = oracle.route_head(q, k, inp["codebook"][0], None, w, tokens=toks)
+    near = compare_selection(r, res["sel"][0, 0], rows=toks)
+    rows = np.arange(w.seq) if toks is None else toks
+    ref = attention_rows(w, inp, res["sel"][0, 0][rows], 0, 0, toks)
+    err = float(np.abs(res["out"][0, 0][rows] - ref).max())
+    print(f"{case}: {w.nblocks} blocks, {w.addresses} addresses, P{w.probes} R{w.remote}, "
+          f"selection near-ties {near}, max abs err {err:.3g}")
+    assert err <= TOL[w.dtype]
