@@ -32,7 +32,6 @@ import argparse
 import csv
 import hashlib
 import json
-import math
 import os
 import re
 import sys

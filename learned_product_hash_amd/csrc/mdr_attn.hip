@@ -352,8 +352,6 @@ hipError_t launch_local(const Shape& s, const void* q, const void* k, const void
 template <typename T, int D, int BLK>
 hipError_t attend_impl(const Shape& s, const void* q, const void* k, const void* v, const int32_t* sel, void* out,
                        const Buffers& b, hipStream_t st, hipEvent_t* ev) {
-  using TL = Tile<T, D, BLK>;
-  const size_t lds = TL::LDS_BYTES;
   const bool remote = s.R > 0 && s.ne > 0;
   hipError_t e;
   if ((e = mark_event(ev, 0, st)) != hipSuccess) return e;
