@@ -799,7 +799,7 @@ def main(argv=None):
         summarize_rocprof(*a.summarize_rocprof, w, a.bench_log, a.profile_name)
         return 0
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print(json.dumps({"error": "this build runs on one GPU only: the path shards over (batch, head) with no "
+        print(json.dumps({"error": "the benchmark runs on one GPU only: the path shards over (batch, head) with no "
                                    "communication, so N GPUs would each run this benchmark on their own share; "
                                    "run with --gpus 1"}))
         return 2
