@@ -81,6 +81,22 @@ __device__ inline f32x4 score_tile(const QFrag<T, D>& qf, const T* Ks, int n, in
   return acc;
 }
 
+// Transposing LDS read (ds_read_b64_tr_b16): within each group of 16 lanes, local lane l receives
+// in slot k the (l % 4)-th 16-bit value at the address that local lane 4k + l / 4 supplies.  So if
+// lane r supplies row r / 4 of a 4-row tile, columns 4 (r % 4) .. + 3, lane r receives the four
+// rows' values in column r (rows 0..3 in slots 0..3); the layout was checked on gfx950 with an
+// in-bounds probe.  tile: the tile's first row and column (LDS, bf16), stride: row stride in
+// elements (a multiple of 4); the values go to slots at .. at + 3 of a.
+__device__ __forceinline__ void tr_keys4(bf16x8& a, int at, const bf16* tile, int stride, int r) {
+  typedef short v4i16 __attribute__((ext_vector_type(4)));
+  const bf16* src = tile + (r >> 2) * stride + 4 * (r & 3);
+  const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(src));
+  bf16x4 w;
+  __builtin_memcpy(&w, &v, 8);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) a[at + e] = w[e];
+}
+
 // O^T += V^T P^T over one block; p[n][k] = P^T[16n + 4(l/16) + k][l%16].  For bf16 the MFMA's
 // k-slot 8(l/16) + e stands for key 32pp + 4(l/16) + e (e < 4) or 32pp + 16 + 4(l/16) + e - 4 (e >= 4),
 // the same permutation on both operands, so P needs no shuffle.
@@ -99,15 +115,11 @@ __device__ inline void pv_block(f32x4 (&o)[D / 16], const f32x4 (&p)[BLK / 16], 
       }
 #pragma unroll
       for (int dt = 0; dt < D / 16; ++dt) {
-        // V^T[d][key] for the 8 keys of this lane's k-slots: 32pp + 4s + {0..3} and + 16 + {0..3};
-        // with a 144-byte row stride the four lane groups (s) hit disjoint bank windows
-        const bf16* vc = Vx + (32 * pp + 4 * s) * TL::VST + 16 * dt + r;
+        // V^T[d][key] for the 8 keys of this lane's k-slots (32pp + 4s + {0..3} and + 16 + {0..3}) at
+        // d = 16dt + r, by two transposing LDS reads
         bf16x8 a;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          a[e] = vc[e * TL::VST];
-          a[4 + e] = vc[(16 + e) * TL::VST];
-        }
+        tr_keys4(a, 0, Vx + (32 * pp + 4 * s) * TL::VST + 16 * dt, TL::VST, r);
+        tr_keys4(a, 4, Vx + (32 * pp + 16 + 4 * s) * TL::VST + 16 * dt, TL::VST, r);
         o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, o[dt], 0, 0, 0);
       }
     }
