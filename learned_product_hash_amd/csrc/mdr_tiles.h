@@ -15,8 +15,12 @@ constexpr float kLog2e = 1.4426950408889634f;
 template <typename T, int D, int BLK>
 struct Tile {
   static constexpr bool bf = std::is_same<T, bf16>::value;
-  static constexpr int KST = bf ? D + 8 : D + 4;     // K rows in LDS (elements)
-  static constexpr int VST = KST;                    // V rows in LDS (elements), row-major like K
+  // K and V rows in LDS (elements), row-major.  For bf16 the row stride is D + 16 elements: the eight
+  // rows that half a wave's transposing reads (tr_keys4) touch then fall in disjoint bank windows.
+  // One stride for both, since score_tile also takes V rows (the backward's dP = dO V^T).
+  static constexpr int KST = bf ? D + 16 : D + 4;
+  static constexpr int VST = KST;
+  static_assert(VST == KST, "score_tile reads V rows with the K stride");
   static constexpr int K_ELEMS = BLK * KST;
   static constexpr int V_ELEMS = BLK * VST;
   static constexpr int NQF = bf ? D / 32 : D / 4;    // query operand registers
