@@ -545,6 +545,50 @@ __device__ inline void insert_key(uint64_t (&top)[K], uint64_t x) {
   }
 }
 
+// The same ranks with 32-bit keys: the value's order-preserving bits with the low B bits given to the
+// complemented index.  One unsigned compare then ranks (value desc, index asc) exactly as long as no
+// two ranked values agree above those B bits.  top[0..K) is kept sorted (best first, empty slots 0)
+// by a median-of-three network: the new rank k is the median of the old ranks k and k-1 and x.
+constexpr int key_bits(int n) {
+  int b = 0;
+  while ((1 << b) < n) ++b;
+  return b;
+}
+__device__ inline uint32_t order_bits(float v) {
+  const uint32_t u = __float_as_uint(v);
+  return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);  // ~u if negative, else the sign bit set
+}
+template <int B>
+__device__ inline uint32_t packed_key(float v, int idx) {
+  constexpr uint32_t mask = (1u << B) - 1u;
+  return (order_bits(v) & ~mask) | (mask - (uint32_t)idx);
+}
+template <int B>
+__device__ inline int packed_index(uint32_t k) {
+  constexpr uint32_t mask = (1u << B) - 1u;
+  return (int)(mask - (k & mask));
+}
+__device__ inline uint32_t med3_u32(uint32_t a, uint32_t b, uint32_t c) {
+  uint32_t r;
+  asm("v_med3_u32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+template <int K>
+__device__ inline void insert_packed(uint32_t (&top)[K], uint32_t x) {
+#pragma unroll
+  for (int k = K - 1; k >= 1; --k) top[k] = med3_u32(top[k], x, top[k - 1]);
+  top[0] = max(top[0], x);
+}
+// The first K-1 packed ranks are the exact ones when no two neighbours among the K kept keys share
+// their value bits (so that every one of them is alone in its group of equal truncated values).
+template <int K, int B>
+__device__ inline bool packed_exact(const uint32_t (&top)[K]) {
+  bool ok = true;
+#pragma unroll
+  for (int k = 0; k + 1 < K; ++k) ok &= top[k + 1] == 0u || ((top[k] ^ top[k + 1]) >> B) != 0u;
+  return ok;
+}
+
 template <int G, int PG>
 struct RankSpace {
   static constexpr int count() {
@@ -794,29 +838,42 @@ __global__ __launch_bounds__(kProbeFixedThreads) __attribute__((amdgpu_waves_per
   const int cutoff = j - s.L;
   const float* mrow = mu + tid * MST;
 
-  // ---- top-PG codes of every subspace by (mu desc, code asc)
+  // ---- top-PG codes of every subspace by (mu desc, code asc): packed 32-bit keys, one more kept
+  // than used to see the boundary; a token whose packed ranks might differ from the exact ones
+  // ranks that subspace again with 64-bit keys.  mu is read back from LDS for the kept codes.
+  constexpr int CB = key_bits(C);
+  constexpr int KG = PG < C ? PG + 1 : PG;
   int tcode[G][PG];
   float tval[G][PG];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    uint64_t top[PG];
+    uint32_t top[KG];
 #pragma unroll
-    for (int p = 0; p < PG; ++p) top[p] = 0;
+    for (int p = 0; p < KG; ++p) top[p] = 0;
 #pragma unroll
-    for (int c = 0; c < C; ++c) insert_key<PG>(top, rank_key(mrow[g * CP + c], c));
+    for (int c = 0; c < C; ++c) insert_packed<KG>(top, packed_key<CB>(mrow[g * CP + c], c));
+    if (packed_exact<KG, CB>(top)) {
 #pragma unroll
-    for (int p = 0; p < PG; ++p) {
-      tcode[g][p] = key_index(top[p]);
-      tval[g][p] = key_value(top[p]);
+      for (int p = 0; p < PG; ++p) tcode[g][p] = packed_index<CB>(top[p]);
+    } else {
+      uint64_t top64[PG];
+#pragma unroll
+      for (int p = 0; p < PG; ++p) top64[p] = 0;
+#pragma unroll
+      for (int c = 0; c < C; ++c) insert_key<PG>(top64, rank_key(mrow[g * CP + c], c));
+#pragma unroll
+      for (int p = 0; p < PG; ++p) tcode[g][p] = key_index(top64[p]);
     }
+#pragma unroll
+    for (int p = 0; p < PG; ++p) tval[g][p] = mrow[g * CP + tcode[g][p]];
   }
-  // ---- rank vectors with prod (k_g + 1) <= P, top-P addresses by (sigma desc, address asc)
-  uint64_t tpk[P];
-#pragma unroll
-  for (int p = 0; p < P; ++p) tpk[p] = 0;
+  // ---- rank vectors with prod (k_g + 1) <= P, top-P addresses by (sigma desc, address asc); packed
+  // keys when the address takes few bits, with the same boundary check and 64-bit fallback
   constexpr int NCOMB = RankSpace<G, PG>::count();
-#pragma unroll
-  for (int kc = 0; kc < NCOMB; ++kc) {
+  constexpr int AB = G * CB;
+  constexpr bool PACK_A = AB <= 12;
+  constexpr int KP = P + 1;
+  auto combo = [&](int kc, float& sig, int& a) -> bool {
     int rem = kc, prod = 1;
     int rk[G];
 #pragma unroll
@@ -825,20 +882,48 @@ __global__ __launch_bounds__(kProbeFixedThreads) __attribute__((amdgpu_waves_per
       rem /= PG;
       prod *= rk[g] + 1;
     }
-    if (prod <= P) {
-      float sig = tval[0][rk[0]];
-      int a = tcode[0][rk[0]];
+    sig = tval[0][rk[0]];
+    a = tcode[0][rk[0]];
 #pragma unroll
-      for (int g = 1; g < G; ++g) {
-        sig += tval[g][rk[g]];
-        a = a * C + tcode[g][rk[g]];
-      }
-      insert_key<P>(tpk, rank_key(sig, a));
+    for (int g = 1; g < G; ++g) {
+      sig += tval[g][rk[g]];
+      a = a * C + tcode[g][rk[g]];
     }
-  }
-  int tpa[P];
+    return prod <= P;
+  };
+  auto exact_addresses = [&](int (&out)[P]) {
+    uint64_t tpk[P];
 #pragma unroll
-  for (int p = 0; p < P; ++p) tpa[p] = key_index(tpk[p]);
+    for (int p = 0; p < P; ++p) tpk[p] = 0;
+#pragma unroll
+    for (int kc = 0; kc < NCOMB; ++kc) {
+      float sig;
+      int a;
+      if (combo(kc, sig, a)) insert_key<P>(tpk, rank_key(sig, a));
+    }
+#pragma unroll
+    for (int p = 0; p < P; ++p) out[p] = key_index(tpk[p]);
+  };
+  int tpa[P];
+  if constexpr (PACK_A) {
+    uint32_t tpk[KP];
+#pragma unroll
+    for (int p = 0; p < KP; ++p) tpk[p] = 0;
+#pragma unroll
+    for (int kc = 0; kc < NCOMB; ++kc) {
+      float sig;
+      int a;
+      if (combo(kc, sig, a)) insert_packed<KP>(tpk, packed_key<AB>(sig, a));
+    }
+    if (packed_exact<KP, AB>(tpk)) {
+#pragma unroll
+      for (int p = 0; p < P; ++p) tpa[p] = packed_index<AB>(tpk[p]);
+    } else {
+      exact_addresses(tpa);
+    }
+  } else {
+    exact_addresses(tpa);
+  }
   // ---- candidate ranges: probe p contributes the `take[p]` newest entries <= cutoff of its list,
   // ending at CSR position lim[p] (exclusive), then (redirect policy) the `rtake[p]` newest arrivals
   // of its redirect list up to query block j, ending at rlim[p], until M candidates.  Dropped
