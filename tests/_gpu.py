@@ -98,3 +98,16 @@ def small(name, **over):
     kw = dict(sizes[name])
     kw.update(over)
     return synth.workload(name, **kw)
+
+
+def integer_inputs(w, seed):
+    """Core inputs rounded to small integers: every code logit, summary and rerank score is then exact
+    on both sides, so ties are frequent and decided by the index rules alone."""
+    inp = dict(synth.make_core_inputs(w, seed))
+    for n in ("q", "k"):
+        inp[n] = np.clip(np.rint(inp[n]), -2, 2).astype(inp[n].dtype)
+    cb = inp["codebook"]
+    inp["codebook"] = np.clip(np.rint(cb / np.abs(cb).max() * 2), -2, 2).astype(cb.dtype)
+    if inp["bias"] is not None:
+        inp["bias"] = np.rint(inp["bias"]).astype(inp["bias"].dtype)
+    return inp

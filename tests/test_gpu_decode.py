@@ -15,7 +15,7 @@ import torch
 
 import oracle
 import synth
-from tests._gpu import NEAR, TOL, cfg_of, compare_selection, dev, host, io_dtype, run_core, small
+from tests._gpu import NEAR, TOL, cfg_of, compare_selection, dev, host, integer_inputs, io_dtype, run_core, small
 
 pytestmark = pytest.mark.gpu
 
@@ -105,6 +105,30 @@ def test_decode_matches_oracle(gpu_lib, name, n0, chunk):
         assert view["overflow"].sum() > 0
     print(f"{name}: decoded {w.seq - n0} tokens, selection near-ties {near}, max abs err {err:.3g}, "
           f"overflow {view['overflow'].sum()}")
+
+
+@pytest.mark.parametrize("name,n0,chunk,cap", [("tiny", 100, 1, 1), ("recall", 1000, 7, None), ("sweep", 3000, 1, None)])
+def test_decode_integer_scores_exactly(gpu_lib, name, n0, chunk, cap):
+    """Integer-valued inputs make every score exact on both sides: each decoded token's selection
+    must equal the oracle's, ties included, with no near-tie allowance."""
+    mdr = gpu_lib
+    over = {"recall": dict(batch=2), "sweep": dict(seq=4096)}.get(name, {})
+    if cap is not None:
+        over["capacity"] = cap
+    w = small(name, **over)
+    inp = integer_inputs(w, 4)
+    out, sel, view = decode_run(mdr, w, inp, n0, chunk)
+    toks = np.arange(n0, w.seq)
+    ties = 0
+    for b in range(w.batch):
+        for h in range(w.heads):
+            r = oracle.route_head(inp["q"][b, h], inp["k"][b, h], inp["codebook"][h],
+                                  None if inp["bias"] is None else inp["bias"][h], w, tokens=toks)
+            assert np.array_equal(sel[b, h], r["sel"]), (b, h)
+            assert view["overflow"][b, h] == oracle.posting_overflow(r["lists"], w.capacity)
+            ties += int(((r["probe_margin"] <= NEAR) | (r["sel_margin"] <= NEAR)).sum())
+    assert np.isfinite(out).all()
+    print(f"{name}: decoded {w.seq - n0} tokens, tied rankings {ties}, overflow {view['overflow'].sum()}, all matched")
 
 
 def test_decode_matches_prefill_kernels(gpu_lib):

@@ -13,7 +13,7 @@ import torch
 import oracle
 import synth
 from tests._gpu import (NEAR, TOL, attention_rows, cfg_of, compare_addresses, compare_selection, dev, host,
-                        io_dtype, run_core, small)
+                        integer_inputs, io_dtype, run_core, small)
 
 pytestmark = pytest.mark.gpu
 
@@ -106,40 +106,29 @@ def test_stage_probe_rerank_on_oracle_index(gpu_lib, name):
     print(f"{name}: probe/rerank near-tie tokens {near} of {B * H * S}")
 
 
-def integer_inputs(w, seed):
-    """Core inputs rounded to small integers: every code logit, summary and rerank score is then exact
-    on both sides, so ties are frequent and decided by the index rules alone."""
-    inp = dict(synth.make_core_inputs(w, seed))
-    for n in ("q", "k"):
-        inp[n] = np.clip(np.rint(inp[n]), -2, 2).astype(inp[n].dtype)
-    cb = inp["codebook"]
-    inp["codebook"] = np.clip(np.rint(cb / np.abs(cb).max() * 2), -2, 2).astype(cb.dtype)
-    if inp["bias"] is not None:
-        inp["bias"] = np.rint(inp["bias"]).astype(inp["bias"].dtype)
-    return inp
-
-
-@pytest.mark.parametrize("name", NAMES)
-def test_integer_scores_route_exactly(gpu_lib, name):
+@pytest.mark.parametrize("name,policy,cap", [(n, "drop", None) for n in NAMES] +
+                         [(n, "redirect", 1) for n in ("tiny", "recall", "skew")])
+def test_integer_scores_route_exactly(gpu_lib, name, policy, cap):
     """With exact scores the routing must equal the oracle's on every token, ties included (no
-    near-tie allowance): the code, address and candidate rankings break ties by the lower index."""
+    near-tie allowance): the code, address and candidate rankings break ties by the lower index.
+    Capacity 1 under the redirect policy makes lists overflow and redirect."""
     mdr = gpu_lib
-    w = small(name)
+    w = small(name) if cap is None else small(name, capacity=cap)
     inp = integer_inputs(w, 4)
-    res = run_core(mdr, w, inp, force=inp.get("force"))
+    res = run_core(mdr, w, inp, force=inp.get("force"), policy=policy)
     ties = 0
     for b in range(w.batch):
         for h in range(w.heads):
             f = None if inp.get("force") is None else inp["force"][b, h]
             r = oracle.route_head(inp["q"][b, h], inp["k"][b, h], inp["codebook"][h],
-                                  None if inp["bias"] is None else inp["bias"][h], w, f)
+                                  None if inp["bias"] is None else inp["bias"][h], w, f, policy=policy)
             ks = oracle.block_summaries(inp["k"][b, h], w.block)
             _, addr, _ = oracle.block_addresses(ks, inp["codebook"][h], None if inp["bias"] is None else inp["bias"][h])
             assert np.array_equal(res["addr"][b, h], addr), (b, h)
             assert res["overflow"][b, h] == r["overflow"]
             assert np.array_equal(res["sel"][b, h], r["sel"]), (b, h)
             ties += int(((r["probe_margin"] <= NEAR) | (r["sel_margin"] <= NEAR)).sum())
-    print(f"{name}: tokens with tied rankings {ties}, all matched")
+    print(f"{name} {policy}: tokens with tied rankings {ties}, overflow {int(res['overflow'].sum())}, all matched")
 
 
 @pytest.mark.parametrize("name", NAMES)
