@@ -142,6 +142,12 @@ struct QkvEpilogue {
   int32_t* cell_zero;
 };
 
+// One direct global-to-LDS load of 16 bytes per lane: lane l's bytes land at lds + 16 l (lds uniform
+// over the wave).
+__device__ __forceinline__ void lds_load16(const void* src, char* lds) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+}
+
 template <typename T, int MT, int NT, bool AHEADS, bool QKV, int D>
 __global__ __launch_bounds__(256) void k_mm(const T* __restrict__ A, const T* __restrict__ B0,
                                             const T* __restrict__ B1, const T* __restrict__ B2, T* __restrict__ C0,
@@ -159,7 +165,11 @@ __global__ __launch_bounds__(256) void k_mm(const T* __restrict__ A, const T* __
   constexpr int CST = NT + 1;                  // output rows of 64 at a time (floats)
   constexpr size_t STAGE = (size_t)(MT + NT) * KS * sizeof(T);
   constexpr size_t EPIB = (size_t)64 * CST * 4;
-  __shared__ __align__(16) char smem[STAGE > EPIB ? STAGE : EPIB];
+  constexpr int DRB = KT * (int)sizeof(T);  // bytes of a row per contraction step (direct path)
+  static_assert(DRB == 128, "eight 16-byte chunks per row and step");
+  constexpr size_t DSTAGE = (size_t)(MT + NT) * DRB;
+  constexpr size_t SM0 = STAGE > EPIB ? STAGE : EPIB;
+  __shared__ __align__(16) char smem[SM0 > 2 * DSTAGE ? SM0 : 2 * DSTAGE];
   T* As = (T*)smem;
   T* Bt = As + MT * KS;
   float* Cs = (float*)smem;  // after the main loop
@@ -211,39 +221,105 @@ __global__ __launch_bounds__(256) void k_mm(const T* __restrict__ A, const T* __
       *(u32x4*)(Bt + row * KS + cv * VEC) = br[u];
     }
   };
-  gload(0);
-  for (int k0 = 0; k0 < Kd; k0 += KT) {
-    lstore();
-    __syncthreads();
-    if (k0 + KT < Kd) gload(k0 + KT);  // in flight during this step's products
+  if (Kd % KT == 0) {
+    // ---- two LDS stages filled by direct global-to-LDS loads: a wave's 16-byte load per lane fills
+    // eight consecutive 128-byte rows of a stage (lane l lands at byte 16 l), one contraction step of
+    // a row per 128 bytes.  Lane l of such a load fetches the row's chunk (l % 8) ^ (row % 8), so
+    // chunk c of a row sits in slot c ^ (row % 8): the 16 rows of an operand fragment then spread
+    // over all banks.  Rows past M read row M - 1 (never stored).  Step s + 1 is requested right after
+    // the barrier that opens step s, so it arrives while step s is multiplied.
+    constexpr int NG = (MT + NT) / 8;  // 8-row groups per stage
+    static_assert(NG % 4 == 0, "whole groups per wave");
+    char* sb = smem;
+    auto dload = [&](int k0, char* buf) __attribute__((always_inline)) {
 #pragma unroll
-    for (int ks = 0; ks < (bf ? KT / 32 : KT / 4); ++ks) {
-      // the step's operand fragments of this wave, each used for TJ (A) or TI (B) products
-      if constexpr (bf) {
-        bf16x8 af[TI], bfr[TJ];
+      for (int u = 0; u < NG / 4; ++u) {
+        const int g = u * 4 + wave;
+        const int row = 8 * g + (lane >> 3);
+        const int kk = k0 + (((lane & 7) ^ (row & 7)) * VEC);
+        const T* src;
+        if (8 * g < MT) {  // uniform: a group is all A rows or all B rows
+          const int m = min(m0 + row, M - 1);
+          src = A + (AHEADS ? hm(m, kk) : (size_t)m * Kd + kk);
+        } else {
+          src = Bm + (size_t)(n0 + row - MT) * Kd + kk;
+        }
+        lds_load16(src, buf + g * 8 * DRB);
+      }
+    };
+    auto frag = [&](const char* buf, int row, int chunk) -> const char* {
+      return buf + row * DRB + ((chunk ^ (row & 7)) << 4);
+    };
+    const int nst = Kd / KT;
+    dload(0, sb);
+    for (int st = 0; st < nst; ++st) {
+      const char* cur = sb + (st & 1) * DSTAGE;
+      __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of step st are in LDS
+      __syncthreads();                // everyone's are; step st - 1 is multiplied everywhere
+      if (st + 1 < nst) dload((st + 1) * KT, sb + ((st + 1) & 1) * DSTAGE);
 #pragma unroll
-        for (int ti = 0; ti < TI; ++ti) af[ti] = *(const bf16x8*)(As + (wm + 16 * ti + r) * KS + 32 * ks + 8 * sl);
+      for (int ks = 0; ks < (bf ? KT / 32 : KT / 4); ++ks) {
+        if constexpr (bf) {
+          bf16x8 af[TI], bfr[TJ];
 #pragma unroll
-        for (int tj = 0; tj < TJ; ++tj) bfr[tj] = *(const bf16x8*)(Bt + (wn + 16 * tj + r) * KS + 32 * ks + 8 * sl);
+          for (int ti = 0; ti < TI; ++ti) af[ti] = *(const bf16x8*)frag(cur, wm + 16 * ti + r, 4 * ks + sl);
 #pragma unroll
-        for (int ti = 0; ti < TI; ++ti)
+          for (int tj = 0; tj < TJ; ++tj) bfr[tj] = *(const bf16x8*)frag(cur, MT + wn + 16 * tj + r, 4 * ks + sl);
 #pragma unroll
-          for (int tj = 0; tj < TJ; ++tj)
-            acc[ti][tj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[ti], bfr[tj], acc[ti][tj], 0, 0, 0);
-      } else {
-        float af[TI], bfr[TJ];
+          for (int ti = 0; ti < TI; ++ti)
 #pragma unroll
-        for (int ti = 0; ti < TI; ++ti) af[ti] = As[(wm + 16 * ti + r) * KS + 4 * ks + sl];
+            for (int tj = 0; tj < TJ; ++tj)
+              acc[ti][tj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[ti], bfr[tj], acc[ti][tj], 0, 0, 0);
+        } else {
+          float af[TI], bfr[TJ];
 #pragma unroll
-        for (int tj = 0; tj < TJ; ++tj) bfr[tj] = Bt[(wn + 16 * tj + r) * KS + 4 * ks + sl];
+          for (int ti = 0; ti < TI; ++ti) af[ti] = *(const float*)(frag(cur, wm + 16 * ti + r, ks) + 4 * sl);
 #pragma unroll
-        for (int ti = 0; ti < TI; ++ti)
+          for (int tj = 0; tj < TJ; ++tj) bfr[tj] = *(const float*)(frag(cur, MT + wn + 16 * tj + r, ks) + 4 * sl);
 #pragma unroll
-          for (int tj = 0; tj < TJ; ++tj)
-            acc[ti][tj] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[ti], bfr[tj], acc[ti][tj], 0, 0, 0);
+          for (int ti = 0; ti < TI; ++ti)
+#pragma unroll
+            for (int tj = 0; tj < TJ; ++tj)
+              acc[ti][tj] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[ti], bfr[tj], acc[ti][tj], 0, 0, 0);
+        }
       }
     }
-    __syncthreads();
+    __syncthreads();  // the epilogue reuses the stages
+  } else {
+    gload(0);
+    for (int k0 = 0; k0 < Kd; k0 += KT) {
+      lstore();
+      __syncthreads();
+      if (k0 + KT < Kd) gload(k0 + KT);  // in flight during this step's products
+  #pragma unroll
+      for (int ks = 0; ks < (bf ? KT / 32 : KT / 4); ++ks) {
+        // the step's operand fragments of this wave, each used for TJ (A) or TI (B) products
+        if constexpr (bf) {
+          bf16x8 af[TI], bfr[TJ];
+  #pragma unroll
+          for (int ti = 0; ti < TI; ++ti) af[ti] = *(const bf16x8*)(As + (wm + 16 * ti + r) * KS + 32 * ks + 8 * sl);
+  #pragma unroll
+          for (int tj = 0; tj < TJ; ++tj) bfr[tj] = *(const bf16x8*)(Bt + (wn + 16 * tj + r) * KS + 32 * ks + 8 * sl);
+  #pragma unroll
+          for (int ti = 0; ti < TI; ++ti)
+  #pragma unroll
+            for (int tj = 0; tj < TJ; ++tj)
+              acc[ti][tj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[ti], bfr[tj], acc[ti][tj], 0, 0, 0);
+        } else {
+          float af[TI], bfr[TJ];
+  #pragma unroll
+          for (int ti = 0; ti < TI; ++ti) af[ti] = As[(wm + 16 * ti + r) * KS + 4 * ks + sl];
+  #pragma unroll
+          for (int tj = 0; tj < TJ; ++tj) bfr[tj] = Bt[(wn + 16 * tj + r) * KS + 4 * ks + sl];
+  #pragma unroll
+          for (int ti = 0; ti < TI; ++ti)
+  #pragma unroll
+            for (int tj = 0; tj < TJ; ++tj)
+              acc[ti][tj] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[ti], bfr[tj], acc[ti][tj], 0, 0, 0);
+        }
+      }
+      __syncthreads();
+    }
   }
   // ---- epilogue, 64 rows at a time through LDS (lane holds rows 4(l/16) + k, column l%16 of each
   // 16x16 tile)
