@@ -36,6 +36,12 @@ CASES = {
     # overflow), alternates in the epilogue
     "redirect": dict(batch=1, heads=2, seq=2048, head_dim=128, block=64, width=128, subspaces=3, codes=8,
                      capacity=1, probes=6, remote=4, dtype="bf16", zipf_kappa=1.0),
+    # fused bf16 with width 96: the projection's contraction (96) is not a whole number of 64-wide
+    # steps, so it takes the register-staged loop; the output projection (64) takes the direct loop
+    "bf16_w96": dict(batch=1, heads=2, seq=1024, head_dim=32, block=32, width=96, dtype="bf16"),
+    # fused, one sequence of 1056 tokens: the last 64-row tile holds 32 rows (rows past the end read
+    # the last row and are never stored)
+    "row_tail": dict(batch=1, heads=2, seq=1056, head_dim=32, block=32, width=96),
     # unfused: block 128
     "block128": dict(batch=1, heads=2, seq=1024, head_dim=128, block=128, width=128, codes=8, capacity=4,
                      probes=4),
