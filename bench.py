@@ -8,15 +8,16 @@ probe + rerank, selected-set attention -- over the scaling-sweep workload at
 remote + 2 local blocks, bf16 Q/K/V with fp32 routing and softmax, balanced
 addresses), with inputs already resident in HBM.  An untimed pass of K calls
 of the library's profiling entry point, with an event before every kernel,
-gives each kernel's average duration and names the dominant one; the timed
-region is then K consecutive calls of the same entry point, bracketed by
-torch.cuda.synchronize(), with events on the call's stream around the dominant
-kernel only, whose average over that region is the roofline's duration.
+gives each kernel's average duration; the timed region is then K consecutive
+calls of the same entry point, bracketed by torch.cuda.synchronize(), with
+events on the call's stream around the selected-set attention stage only (its
+kernels run last), whose average over that region is the roofline's duration.
 
 Prints one JSON line: tokens/s (B*S*K / wall time), the roofline of the
-dominant kernel (its algorithmic bytes per launch / its average duration,
-against 8 TB/s), every kernel's time and bytes, the fitted timing exponent over
-4K-32K, and the CPU oracle timed on a bounded sample of the same workload.
+attention stage (its compulsory bytes -- Q, K, V and O once plus the selection
+-- per call / its average duration, against 8 TB/s), every kernel's time, the
+memory split, the fitted timing exponent over 4K-32K, and the CPU oracle timed
+on the host's cores over a bounded sample of the same workload.
 
     python bench.py --ingest-pmc FETCH.csv WRITE.csv
 turns two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of
@@ -215,8 +216,10 @@ class Run:
                     n_cand_mean=float(self.rt["n_cand"].float().mean().item()))
 
 
-def algorithmic_bytes(w, st):
-    """Bytes each kernel must move per launch (compulsory traffic of its contract, each byte once)."""
+def design_bytes(w, st):
+    """Bytes each kernel moves per launch by this design's own data flow (each byte once), including what the
+    design adds beyond the method's compulsory bytes (per-pair query gathers, the remote partials' round
+    trip, pair lists).  Reported per kernel; the roofline uses the stage's compulsory bytes instead."""
     e = 2 if w.dtype == "bf16" else 4
     B, H, S, D, nb, blk = w.batch, w.heads, w.seq, w.head_dim, w.nblocks, w.block
     A, R, G, C = w.addresses, w.remote, w.subspaces, w.codes
@@ -293,23 +296,23 @@ def selected_set_bytes(w, pairs):
         pairs * w.block * w.head_dim * 2 * e
 
 
-def attention_stage(w, t_att, pairs):
-    """The selected-set attention (remote + local kernels) against the HBM peak, two ways:
-    (i) compulsory bytes (Q, K, V, O once + sel) / time; (ii) measured HBM bytes (FETCH_SIZE +
-    WRITE_SIZE of both kernels, when counters for these sources exist) / time; and (iii) the
-    selected-set bytes of a gather without reuse / time, which counts cache-served and regrouped
-    re-reads and so is not an HBM bandwidth."""
+def attention_stage(w, t_att, pairs, stage_names):
+    """The selected-set attention stage against the HBM peak, three ways: (i) compulsory bytes (Q, K, V,
+    O once + sel) / time -- the roofline's fraction; (ii) L2-to-fabric bytes (FETCH_SIZE + WRITE_SIZE of
+    the stage's kernels, when counters for these sources exist) / time, an upper bound on what HBM served
+    (the 256 MB last-level cache serves part of it); (iii) the selected-set bytes of a gather without reuse
+    / time, which counts cache-served and regrouped re-reads and so is not an HBM bandwidth."""
     alg = stage_bytes(w)
     sel_b = selected_set_bytes(w, pairs)
     out = {"ms": round(t_att, 5), "alg_bytes": alg,
            "frac_of_hbm_peak": round(alg / (t_att * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
            "selected_set_bytes": sel_b,
            "selected_set_gbps_not_hbm": round(sel_b / (t_att * 1e-3) / 1e9, 1)}
-    tr = [load_traffic(w, k) for k in ("attn_remote", "attn_local")]
+    tr = [load_traffic(w, k) for k in stage_names]
     if all(t is not None for t in tr):
         gbps = sum(tr) / (t_att * 1e-3) / 1e9
-        out.update(measured_bytes=round(sum(tr)), measured_gbps=round(gbps, 1),
-                   measured_frac_of_hbm_peak=round(gbps / HBM_PEAK_GBPS, 4))
+        out.update(l2_fabric_bytes=round(sum(tr)), l2_fabric_gbps=round(gbps, 1),
+                   l2_fabric_over_compulsory=round(sum(tr) / alg, 3))
     return out
 
 
@@ -331,11 +334,18 @@ def event_overhead(hip, steps):
     return overhead
 
 
+def stage_span(names):
+    """Event indices bracketing the selected-set attention stage (mdr_sel_attn): the kernels whose names
+    start with "attn_", which run last in the core path."""
+    idx = [i for i, n in enumerate(names) if n.startswith("attn_")]
+    return idx[0], idx[-1] + 1
+
+
 def timed_region(run, hip, steps, warmup):
     """W warm-up steps; then K steps with an event before every kernel (untimed: every kernel's
-    average, and which kernel dominates); then the timed region, K steps with events around the
-    dominant kernel only, so that the step rate carries two events instead of six.  Returns the
-    timed wall time, the per-kernel averages, the event cost, the dominant kernel's index and its
+    average); then the timed region, K steps with events around the attention stage only (its
+    first kernel to the end of its last), so that the step rate carries two events instead of one per
+    kernel.  Returns the timed wall time, the per-kernel averages, the event cost and the stage's
     average over the timed region."""
     import numpy as np
     import torch
@@ -360,12 +370,12 @@ def timed_region(run, hip, steps, warmup):
     run.step_quantiles = [round(float(x), 4) for x in np.percentile(totals, [10, 50, 90])]
     overhead = event_overhead(hip, steps)
     per = [max(0.0, p / steps - overhead) for p in per]
-    dom = int(np.argmax(per))
+    a, b = stage_span(list(mdr.CORE_KERNELS))
     marks = hip.create(2 * steps)
     arrays = []
     for s in range(steps):
         arr = [None] * (nk + 1)
-        arr[dom], arr[dom + 1] = marks[2 * s], marks[2 * s + 1]
+        arr[a], arr[b] = marks[2 * s], marks[2 * s + 1]
         arrays.append(arr)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -373,9 +383,9 @@ def timed_region(run, hip, steps, warmup):
         run.step(arrays[s])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    dom_ms = max(0.0, sum(hip.elapsed_ms(marks[2 * s], marks[2 * s + 1]) for s in range(steps)) / steps - overhead)
+    stage_ms = max(0.0, sum(hip.elapsed_ms(marks[2 * s], marks[2 * s + 1]) for s in range(steps)) / steps - overhead)
     hip.destroy(marks)
-    return wall, per, overhead, dom, dom_ms
+    return wall, per, overhead, stage_ms
 
 
 def cold_region(run, hip, steps, overhead):
@@ -649,28 +659,70 @@ def mixer_bench(mdr, hip, seed, steps=20, warmup=3):
             "projection_flops": 2 * M * w.width * 3 * HD + 2 * M * HD * w.width}
 
 
-def cpu_baseline(run, heads):
-    """The oracle as it stands (routing + gathered fp64 attention), one thread, on a bounded sample."""
+_CPU_JOB = {}  # the workload and its inputs, set before the worker processes are forked
+
+
+def _cpu_task(task):
+    """One share of the CPU baseline: routing (with its head's index build) and gathered fp64 attention for
+    a contiguous token range of one head, on one thread."""
     import numpy as np
     from threadpoolctl import threadpool_limits
 
     import oracle
 
-    w, inp = run.w, run.inputs
-    heads = min(heads, w.heads)
-    t0 = time.perf_counter()
+    h, t0, t1 = task
+    w, inp = _CPU_JOB["w"], _CPU_JOB["inputs"]
+    q, k, v = (inp[n][0, h] for n in ("q", "k", "v"))
+    bias = None if inp["bias"] is None else inp["bias"][h]
+    toks = np.arange(t0, t1)
     with threadpool_limits(1):
-        for h in range(heads):
-            q, k, v = (inp[n][0, h] for n in ("q", "k", "v"))
-            bias = None if inp["bias"] is None else inp["bias"][h]
-            r = oracle.route_head(q, k, inp["codebook"][h], bias, w)
-            oracle.attention_packed(q, k, v, r["sel"], w.block, w.local)
+        r = oracle.route_head(q, k, inp["codebook"][h], bias, w, tokens=toks)
+        oracle.attention_packed(q, k, v, r["sel"], w.block, w.local, tokens=toks)
+    return t1 - t0
+
+
+def host_cpu():
+    """(usable cores for the pool, cores this process may run on, CPU model name)."""
+    avail = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return max(1, min(avail, 16)), avail, model
+
+
+def cpu_baseline(w, inputs, heads):
+    """The oracle as it stands (routing + gathered fp64 attention) on the host's cores: a pool of forked
+    worker processes (one BLAS thread each) over (head, token range) shares of the sample, so every core
+    has work; then the same oracle on one thread over one head, for the per-core rate.  Runs before the
+    process initialises the GPU, so forking is safe."""
+    import multiprocessing as mp
+
+    heads = min(heads, w.heads)
+    cores, avail, model = host_cpu()
+    parts = max(1, -(-cores // heads))
+    bounds = [(w.seq * p) // parts for p in range(parts + 1)]
+    tasks = [(h, bounds[p], bounds[p + 1]) for h in range(heads) for p in range(parts)]
+    _CPU_JOB.update(w=w, inputs=inputs)
+    t0 = time.perf_counter()
+    with mp.get_context("fork").Pool(cores) as pool:
+        done = sum(pool.map(_cpu_task, tasks, chunksize=1))
     dt = time.perf_counter() - t0
-    pairs = heads * w.seq
-    return {"value": round(pairs / w.heads / dt, 2), "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"batch 0, heads 0-{heads - 1} of {w.heads}, all {w.seq} tokens each (routing incl. the "
-                      f"index build of those heads + gathered fp64 attention); tokens/s counts a token as all "
-                      f"{w.heads} heads; {dt:.1f} s on one thread"}
+    t1 = time.perf_counter()
+    _cpu_task((0, 0, w.seq))
+    dt1 = time.perf_counter() - t1
+    return {"value": round(done / w.heads / dt, 2), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "cpu_model": model, "host_cpus_visible": avail,
+            "one_thread_tokens_per_s": round(w.seq / w.heads / dt1, 2),
+            "sample": f"batch 0, heads 0-{heads - 1} of {w.heads}, all {w.seq} tokens each, split into {len(tasks)} "
+                      f"(head, token range) shares over {cores} forked worker processes (one BLAS thread each); "
+                      f"each share routes its tokens (with its head's index build) and runs gathered fp64 "
+                      f"attention; tokens/s counts a token as all {w.heads} heads; {dt:.1f} s wall. "
+                      f"One thread, head 0 alone: {dt1:.1f} s"}
 
 
 # ----------------------------------------------------------------------------- PMC ingest
@@ -734,9 +786,11 @@ def summarize_rocprof(stats_csv, command, w, bench_log=None, stem="routed_attent
     if bench_log:
         for line in open(bench_log):
             if line.startswith("{"):
-                ks = json.loads(line).get("kernels", {})
+                rec = json.loads(line)
+                ks = rec.get("kernels", {})
                 events = {k: v["ms"] * 1e3 for k, v in ks.items()}
-                timed = next(((k, v["ms_timed_region"] * 1e3) for k, v in ks.items() if "ms_timed_region" in v), None)
+                if "roofline" in rec:
+                    timed = (rec["roofline"]["kernel"], rec["roofline"]["ms_timed_region"] * 1e3)
     lines = [f"# rocprofv3 kernel statistics: routed attention, {describe(w)}", "",
              "Command (run from the repository root on one MI355X):", "", f"    {command}", "",
              "| kernel | calls | avg us | min us | max us | share of GPU time | bench.py HIP-event avg us |",
@@ -749,10 +803,14 @@ def summarize_rocprof(stats_csv, command, w, bench_log=None, stem="routed_attent
                              f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
                              f"{float(r['Percentage']):.1f}% | {ev} |")
     if timed:
-        avg = next((float(r["AverageNs"]) / 1e3 for r in rows if KERNEL_SYMBOL[timed[0]] in r["Name"]), None)
+        stage = [k for k in KERNEL_SYMBOL if k.startswith("attn_")]
+        avgs = [next((float(r["AverageNs"]) / 1e3 for r in rows if KERNEL_SYMBOL[k] in r["Name"]), None)
+                for k in stage]
+        tot = sum(avgs) if all(x is not None for x in avgs) else None
         lines += ["", f"The HIP-event column is bench.py's pass with an event before every kernel.  In its timed "
-                      f"region (events around the dominant kernel only) `{timed[0]}` averaged {timed[1]:.2f} us"
-                      + (f" (rocprofv3, every launch in the run: {avg:.2f} us)." if avg else ".")]
+                      f"region (events around the attention stage only) {timed[0]} averaged {timed[1]:.2f} us"
+                      + (f"; rocprofv3, every launch in the run, sums the stage's kernels to {tot:.2f} us." if tot
+                         else ".")]
     bwd = {}
     if bench_log:
         for line in open(bench_log):
@@ -789,6 +847,22 @@ def summarize_rocprof(stats_csv, command, w, bench_log=None, stem="routed_attent
     print(open(out).read())
 
 
+def memory_split(mdr, w, cfg):
+    """Device memory of one call, split the way the pages ask (remio.ai, "What sparse attention
+    researchers should watch next": weights, routing buffers, posting lists and K/V reported apart)."""
+    e = 2 if w.dtype == "bf16" else 4
+    BH = w.batch * w.heads
+    parts = mdr.workspace_breakdown(cfg)
+    row = BH * w.seq * w.head_dim * e
+    return {"weights_and_codebook": w.heads * w.subspaces * w.codes * (w.head_dim + 1) * 4,
+            "k_v": 2 * row, "q_and_out": 2 * row,
+            "posting_lists": parts["posting_lists"],
+            "routing_buffers": {k: parts[k] for k in ("summaries", "selection", "pair_lists", "partials")},
+            "backward_scratch": parts["backward"], "workspace_total": parts["total"],
+            "note": "bytes; the workspace is caller-owned and sized by mdr_workspace_size; weights are the "
+                    "fp32 codebook and bias (the core takes post-RoPE Q/K/V, so it has no projection weights)"}
+
+
 def main(argv=None):
     a = parse(argv)
     w = make_workload(a.workload, a.seq)
@@ -803,6 +877,14 @@ def main(argv=None):
                                    "communication, so N GPUs would each run this benchmark on their own share; "
                                    "run with --gpus 1"}))
         return 2
+    import synth
+
+    inputs = None
+    cpu = None
+    if not a.no_cpu and not a.mixer_only:
+        # the CPU baseline forks worker processes, so it runs before anything touches the GPU
+        inputs = synth.make_core_inputs(w, a.seed)
+        cpu = cpu_baseline(w, inputs, a.cpu_heads)
     import torch
 
     import learned_product_hash_amd as mdr
@@ -819,22 +901,22 @@ def main(argv=None):
         torch.neg(src, out=dst)
         torch.cuda.synchronize()
         del src, dst
-    run = Run(mdr, w, a.seed)
-    wall, per, ev_overhead, dom_i, dom_ms = timed_region(run, hip, a.steps, a.warmup)
+    run = Run(mdr, w, a.seed, inputs=inputs)
+    wall, per, ev_overhead, stage_ms = timed_region(run, hip, a.steps, a.warmup)
     plain = plain_region(run, a.steps)
     cold_q, cold_per = (None, None) if a.no_cold else cold_region(run, hip, min(a.steps, 20), ev_overhead)
     st = run.routing_stats()
     names = list(mdr.CORE_KERNELS)
-    abytes = algorithmic_bytes(w, st)
+    dbytes = design_bytes(w, st)
     kernels = {}
     for n, ms in zip(names, per):
-        kernels[n] = {"ms": round(ms, 5), "alg_bytes": abytes[n],
-                      "alg_gbps": round(abytes[n] / (ms * 1e-3) / 1e9, 1) if ms > 0 else None}
-    dom = names[dom_i]
-    kernels[dom]["ms_timed_region"] = round(dom_ms, 5)
-    achieved = abytes[dom] / (dom_ms * 1e-3) / 1e9
-    traffic = load_traffic(w, dom)
-    t_att = sum(kernels[n]["ms"] for n in ("attn_remote", "attn_local"))
+        kernels[n] = {"ms": round(ms, 5), "design_bytes": dbytes.get(n),
+                      "design_gbps": round(dbytes[n] / (ms * 1e-3) / 1e9, 1) if ms > 0 and n in dbytes else None}
+    stage_names = [n for n in names if n.startswith("attn_")]
+    alg = stage_bytes(w)
+    achieved = alg / (stage_ms * 1e-3) / 1e9
+    tr = [load_traffic(w, n) for n in stage_names]
+    traffic = None if any(t is None for t in tr) else round(sum(tr))
     tokens = w.batch * w.seq
     res = {
         "metric": "routed-attention tokens/sec at 32K seq; achieved HBM GB/s vs peak",
@@ -851,11 +933,17 @@ def main(argv=None):
         "data": "synthetic (seeded Gaussian Q/K/V with balanced planted block addresses)",
         "config": {"workload": describe(w), "global_batch": w.batch, "seq_len": w.seq, "heads": w.heads,
                    "head_dim": w.head_dim, "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": None if traffic is None else round(traffic)},
+        "roofline": {"bound": "hbm", "kernel": "mdr_sel_attn (" + " + ".join(stage_names) + ")",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                     "alg_bytes": alg, "ms_timed_region": round(stage_ms, 5),
+                     "note": "achieved = compulsory bytes of the stage (Q, K, V and O once, plus the selection) / "
+                             "the stage's average duration over the timed region (HIP events on the call's stream "
+                             "before its first kernel and after its last); traffic = FETCH_SIZE + WRITE_SIZE of the "
+                             "stage's kernels per call, calibrated on a plain copy: bytes between the L2s and the "
+                             "fabric, served by HBM or the 256 MB last-level cache, so an upper bound on DRAM bytes"},
         "kernels": kernels,
-        "attention_stage": attention_stage(w, t_att, st["pairs"]),
+        "attention_stage": attention_stage(w, stage_ms, st["pairs"], stage_names),
         "plain_entry_point_ms_per_step": round(plain / a.steps * 1e3, 4),
         "event_overhead_ms": round(ev_overhead, 5),
         "profiled_step_ms_p10_p50_p90": run.step_quantiles,
@@ -864,6 +952,7 @@ def main(argv=None):
                     "bracketed by events, the write is not",
             "step_ms_p10_p50_p90": cold_q, "kernels_ms": {n: round(ms, 5) for n, ms in zip(names, cold_per)}},
         "routing": st,
+        "memory": memory_split(mdr, w, run.cfg),
     }
     if not a.no_decode and a.workload == "sweep":
         res["decode"] = [decode_bench(run, b) for b in (1, 16)]
@@ -875,8 +964,8 @@ def main(argv=None):
         res["overflow_stress"] = overflow_stress(mdr, a.seed)
     if not a.no_sweep and a.workload == "sweep":
         res["exponent"] = exponent_sweep(mdr, (4096, 8192, 16384, 32768), a.seed)
-    if not a.no_cpu:
-        res["cpu_baseline"] = cpu_baseline(run, a.cpu_heads)
+    if cpu is not None:
+        res["cpu_baseline"] = cpu
     print(json.dumps(res))
     return 0
 

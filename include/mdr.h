@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define MDR_ABI_VERSION 2
+#define MDR_ABI_VERSION 3
 
 typedef enum {
   MDR_OK = 0,
@@ -163,6 +163,24 @@ mdr_status mdr_check_config(const mdr_config* cfg);
 /* Host-only: bytes of device workspace every entry point below needs for `cfg`
  * (mdr_mixer_forward included when cfg->width > 0).  *bytes is set on MDR_OK. */
 mdr_status mdr_workspace_size(const mdr_config* cfg, size_t* bytes);
+
+/* Host-only: how the workspace of cfg divides, in bytes.  The pages ask memory
+ * to be reported split into weights, routing buffers, posting lists and K/V
+ * (remio.ai, "What sparse attention researchers should watch next"); the
+ * caller-owned tensors (Q, K, V, out, codebook, bias, projection weights) are
+ * not part of the workspace and not counted here.  Regions are 256-byte
+ * aligned, so the parts sum to `total` (== mdr_workspace_size). */
+typedef struct {
+  size_t summaries;     /* block key summaries, addresses (and alternates) */
+  size_t posting_lists; /* posting-list CSR, redirect lists, overflow counts */
+  size_t selection;     /* sel and n_cand of the workspace copy */
+  size_t pair_lists;    /* the selected (token, slot) pairs binned by remote block */
+  size_t partials;      /* remote softmax partials (output rows and normalisers) */
+  size_t backward;      /* backward-only scratch */
+  size_t mixer;         /* mixer-only scratch: projected Q, K, V, O and transposed weights */
+  size_t total;
+} mdr_workspace_parts;
+mdr_status mdr_workspace_breakdown(const mdr_config* cfg, mdr_workspace_parts* parts);
 
 /* The routed attention core on post-RoPE inputs (the whole path: addressing,
  * posting lists, probe + rerank, selected-set attention).

@@ -20,7 +20,8 @@ import torch  # noqa: F401  (loads the HIP runtime the library must share)
 __all__ = [
     "LIB_PATH", "MdrError", "MdrConfig", "MdrRouting", "MdrDecodeView", "MDR_F32", "MDR_BF16",
     "MDR_OVERFLOW_DROP", "MDR_OVERFLOW_REDIRECT", "config", "lib",
-    "mdr_abi_version", "mdr_status_string", "mdr_check_config", "mdr_workspace_size",
+    "mdr_abi_version", "mdr_status_string", "mdr_check_config", "mdr_workspace_size", "MdrWorkspaceParts",
+    "mdr_workspace_breakdown", "workspace_breakdown",
     "mdr_routed_attention", "mdr_routed_attention_profiled", "MDR_CORE_KERNELS", "CORE_KERNELS",
     "mdr_mixer_forward", "mdr_stage_address", "mdr_stage_post",
     "mdr_stage_probe_rerank", "mdr_stage_attend", "mdr_stage_attend_lse", "mdr_stage_attend_backward",
@@ -55,6 +56,11 @@ class MdrRouting(ctypes.Structure):
         "redir_idx", "redir_time")]
 
 
+class MdrWorkspaceParts(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in (
+        "summaries", "posting_lists", "selection", "pair_lists", "partials", "backward", "mixer", "total")]
+
+
 class MdrDecodeView(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "ring", "overflow", "summarized", "filed", "addr", "ksum")]
@@ -76,6 +82,7 @@ _SIGS = {
     "mdr_status_string": ([_i32], ctypes.c_char_p),
     "mdr_check_config": ([_cfgp], _i32),
     "mdr_workspace_size": ([_cfgp, ctypes.POINTER(_sz)], _i32),
+    "mdr_workspace_breakdown": ([_cfgp, ctypes.POINTER(MdrWorkspaceParts)], _i32),
     "mdr_routed_attention": ([_cfgp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _rtp, _vp, _sz, _vp], _i32),
     "mdr_routed_attention_profiled": ([_cfgp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _rtp, _vp, _sz,
                                        ctypes.POINTER(_vp), _vp], _i32),
@@ -157,6 +164,18 @@ def mdr_workspace_size(cfg: MdrConfig) -> int:
     n = _sz(0)
     _check(lib.mdr_workspace_size(ctypes.byref(cfg), ctypes.byref(n)), "mdr_workspace_size")
     return n.value
+
+
+def mdr_workspace_breakdown(cfg: MdrConfig) -> MdrWorkspaceParts:
+    p = MdrWorkspaceParts()
+    _check(lib.mdr_workspace_breakdown(ctypes.byref(cfg), ctypes.byref(p)), "mdr_workspace_breakdown")
+    return p
+
+
+def workspace_breakdown(cfg: MdrConfig) -> dict:
+    """mdr_workspace_breakdown as a dict of byte counts."""
+    p = mdr_workspace_breakdown(cfg)
+    return {n: getattr(p, n) for n, _ in MdrWorkspaceParts._fields_}
 
 
 def workspace(cfg: MdrConfig, device="cuda") -> torch.Tensor:

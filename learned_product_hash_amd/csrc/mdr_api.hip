@@ -77,30 +77,44 @@ mdr_status shape_from_config(const mdr_config* cfg, bool mixer, Shape* out) {
 
 size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Workspace regions; with base == nullptr only the size is computed.
-size_t layout(const Shape& s, char* base, Buffers* b) {
+// Workspace regions; with base == nullptr only the size is computed.  parts (optional) receives the
+// bytes of each group of regions.
+size_t layout(const Shape& s, char* base, Buffers* b, mdr_workspace_parts* parts = nullptr) {
   const size_t BH = (size_t)s.B * s.H, e = s.dtype == MDR_BF16 ? 2 : 4;
   size_t off = 0;
+  mdr_workspace_parts pt;
+  memset(&pt, 0, sizeof(pt));
+  size_t* group = &pt.summaries;
   auto take = [&](size_t bytes) -> char* {
     char* p = base ? base + off : nullptr;
-    off += align_up(bytes ? bytes : 4);
+    const size_t n = align_up(bytes ? bytes : 4);
+    off += n;
+    *group += n;
     return p;
   };
   Buffers t;
+  group = &pt.summaries;
   t.ksum = (float*)take(BH * s.nb * s.D * 4);
   t.addr = (int32_t*)take(BH * s.nb * 4);
+  group = &pt.posting_lists;
   t.off = (int32_t*)take(BH * (s.A + 1) * 4);
   t.idx = (int32_t*)take(BH * s.nb * 4);
   t.overflow = (int32_t*)take(BH * 4);
+  group = &pt.selection;
   t.sel = (int32_t*)take(BH * s.S * s.R * 4);
   t.ncand = (int32_t*)take(BH * s.S * 4);
+  group = &pt.pair_lists;
   t.cellcnt = (int32_t*)take(BH * (size_t)s.cells_per_bh * 4);
   t.bins = (int32_t*)take(BH * (size_t)s.cells_per_bh * (s.blk + kCellDense) * 4);
+  group = &pt.partials;
   t.part_o = take(BH * s.S * s.R * s.D * e);
   t.part_ml = (float*)take(BH * s.S * s.R * 8);
+  group = &pt.backward;
   t.dvec = (float*)take(BH * s.S * 4);
   if (s.policy == MDR_OVERFLOW_REDIRECT) {
+    group = &pt.summaries;
     t.alt = (int32_t*)take(BH * s.nb * 4);
+    group = &pt.posting_lists;
     t.roff = (int32_t*)take(BH * (s.A + 1) * 4);
     t.ridx = (int32_t*)take(BH * s.nb * 4);
     t.rtime = (int32_t*)take(BH * s.nb * 4);
@@ -109,6 +123,7 @@ size_t layout(const Shape& s, char* base, Buffers* b) {
   }
   t.ndrop = nullptr;
   if (s.W > 0) {
+    group = &pt.mixer;
     const size_t qkv = BH * s.S * s.D * e;
     t.mq = take(qkv);
     t.mk = take(qkv);
@@ -120,6 +135,8 @@ size_t layout(const Shape& s, char* base, Buffers* b) {
   }
   t.lse = nullptr;
   if (b) *b = t;
+  pt.total = off;
+  if (parts) *parts = pt;
   return off;
 }
 
@@ -264,6 +281,15 @@ mdr_status mdr_workspace_size(const mdr_config* cfg, size_t* bytes) {
   const mdr_status st = shape_from_config(cfg, cfg && cfg->width > 0, &s);
   if (st != MDR_OK) return st;
   *bytes = layout(s, nullptr, nullptr);
+  return MDR_OK;
+}
+
+mdr_status mdr_workspace_breakdown(const mdr_config* cfg, mdr_workspace_parts* parts) {
+  if (!parts) return MDR_ERR_INVALID_ARG;
+  Shape s;
+  const mdr_status st = shape_from_config(cfg, cfg && cfg->width > 0, &s);
+  if (st != MDR_OK) return st;
+  layout(s, nullptr, nullptr, parts);
   return MDR_OK;
 }
 

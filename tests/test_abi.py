@@ -45,7 +45,7 @@ def test_library_exports_every_declared_symbol(mdr):
     lib = ctypes.CDLL(LIB)
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert mdr.mdr_abi_version() == 2
+    assert mdr.mdr_abi_version() == 3
 
 
 def test_binding_has_every_declared_entry_point(mdr):
@@ -143,6 +143,18 @@ def test_workspace_grows_with_the_mixer_buffers(mdr):
     core = mdr.mdr_workspace_size(mdr.config(**_good()))
     mixer = mdr.mdr_workspace_size(mdr.config(**_good(width=512, rope_base=10000.0)))
     assert mixer > core
+
+
+def test_workspace_breakdown_sums_to_the_workspace_size(mdr):
+    for over in ({}, dict(width=512, rope_base=10000.0), dict(overflow_policy="redirect"), dict(remote=0)):
+        cfg = mdr.config(**_good(**over))
+        parts = mdr.workspace_breakdown(cfg)
+        assert parts["total"] == mdr.mdr_workspace_size(cfg)
+        assert sum(v for k, v in parts.items() if k != "total") == parts["total"]
+        assert (parts["mixer"] > 0) == ("width" in over)
+        assert all(v % 256 == 0 for v in parts.values())
+    with pytest.raises(mdr.MdrError):
+        mdr.workspace_breakdown(mdr.config(**_good(seq=4000)))
 
 
 def test_decode_state_size_and_view(mdr):

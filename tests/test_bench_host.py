@@ -36,14 +36,33 @@ def test_selected_set_bytes_formula():
     assert bench.selected_set_bytes(w, pairs) == 8 * 32768 * per_token + pairs * 64 * 64 * 2 * 2
 
 
-def test_algorithmic_bytes_of_the_attention_kernels():
+def test_design_bytes_of_the_attention_kernels():
     w = synth.workload("sweep")
     st = {"pairs": 436000, "blocks_used": 4046}
-    ab = bench.algorithmic_bytes(w, st)
+    ab = bench.design_bytes(w, st)
     qkv = 8 * 32768 * 64 * 2
     # the local kernel: Q, its K/V window and O once, the selection, and one partial per pair
     assert ab["attn_local"] == 4 * qkv + 8 * 32768 * 2 * 4 + st["pairs"] * (64 * 2 + 8)
     assert all(v > 0 for v in ab.values())
+
+
+def test_stage_span_brackets_the_attention_kernels():
+    names = ["address", "post", "probe_rerank", "attn_bin", "attn_remote", "attn_local"]
+    assert bench.stage_span(names) == (3, 6)
+    assert bench.stage_span(["address", "probe_rerank", "attn_local"]) == (2, 3)
+
+
+def test_cpu_baseline_uses_every_usable_core():
+    """The oracle timed over a process pool: the shares cover every token of every sampled head once, and
+    the record states the cores used, the CPU model and the one-thread rate beside the pool's."""
+    w = synth.workload("tiny")
+    inp = synth.make_core_inputs(w, 0)
+    cores, avail, model = bench.host_cpu()
+    assert 1 <= cores <= 16 and cores <= avail and model
+    r = bench.cpu_baseline(w, inp, 8)
+    assert r["cores"] == cores and r["kind"] == "oracle" and r["cpu_model"] == model
+    assert r["value"] > 0 and r["one_thread_tokens_per_s"] > 0
+    assert str(cores) in r["sample"]
 
 
 def test_strip_comments():
