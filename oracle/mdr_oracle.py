@@ -335,14 +335,17 @@ def apply_force(sel: list, f: int, j: int, local: int, remote: int):
 
 
 def route_head(q: np.ndarray, k: np.ndarray, codebook: np.ndarray, bias, w, force=None,
-               tokens=None, rdtype=np.float32, policy: str = "drop") -> dict:
+               tokens=None, rdtype=np.float32, policy: str = "drop", addr=None, alt=None) -> dict:
     """Routing for one (batch, head).  q, k [S, D] post-RoPE; codebook [G, C, D]; bias [G, C] or None.
 
     ``w`` carries the sizes (block, codes, capacity, probes, cand_limit, remote,
     local).  ``tokens`` restricts the per-token steps to a subset (all by default).
     Returns the summaries, codes, addresses, posting lists, overflow, and per
     token the probes, candidates, selection, capacity-dropped candidates and
-    decision margins.  ``policy`` is "drop" or "redirect" (section 3b).
+    decision margins.  ``policy`` is "drop" or "redirect" (section 3b).  ``addr`` [nb], when given,
+    replaces the computed block addresses (so the posting lists, probes and rerank can be checked on
+    another implementation's addresses); the summaries, codes and margins are still this oracle's.
+    ``alt`` [nb] likewise replaces the alternate addresses of the redirect policy.
     """
     S, D = q.shape
     blk, L, R, P = w.block, w.local, w.remote, w.probes
@@ -350,13 +353,15 @@ def route_head(q: np.ndarray, k: np.ndarray, codebook: np.ndarray, bias, w, forc
     A = C ** G
     M = w.cand_limit
     ksum = block_summaries(k, blk, rdtype)
-    codes, addr, addr_margin = block_addresses(ksum, codebook, bias, rdtype)
+    codes, own_addr, addr_margin = block_addresses(ksum, codebook, bias, rdtype)
+    addr = own_addr if addr is None else np.asarray(addr, dtype=np.int64)
     lists = posting_lists(addr, A, L)
     off, idx = posting_csr(lists)
     alt = alt_gap = rd = None
     if policy == "redirect":
         second, margin32 = runner_up_codes(ksum, codebook, bias, rdtype)
-        alt, alt_gap = alternate_addresses(codes, second, margin32, C)
+        own_alt, alt_gap = alternate_addresses(codes, second, margin32, C)
+        alt = own_alt if alt is None else np.asarray(alt, dtype=np.int64)
         rd = redirect_lists(lists, alt, w.capacity, L)
         overflow = redirect_overflow(lists, rd, w.capacity)
     elif policy == "drop":

@@ -24,7 +24,9 @@ def _dot(a, b):
 def brute_routed_attention(q, k, v, codebook, bias, w, force=None):
     """q, k, v: lists [S][D] of floats; codebook [G][C][D]; bias [G][C] or None.
 
-    Returns dict(addr, overflow, sel (list of lists), out (list [S][D])).
+    Returns dict(addr, overflow, sel (list of lists), out (list [S][D])) and the raw scores behind every
+    decision: logits [nb][G][C] of the block summaries, probe_scores [S][A] of every product address,
+    cand_scores [S] (the rerank score of each candidate, in candidate order).
     """
     S, D = len(q), len(q[0])
     blk, L, R, P, cap, M = w.block, w.local, w.remote, w.probes, w.capacity, w.cand_limit
@@ -39,6 +41,7 @@ def brute_routed_attention(q, k, v, codebook, bias, w, force=None):
     for i in range(nb):
         ksum.append([sum(k[i * blk + r][d] for r in range(blk)) / blk for d in range(D)])
 
+    logits = [[[logit(ksum[i], g, c) for c in range(C)] for g in range(G)] for i in range(nb)]
     addr = []
     for i in range(nb):
         a = 0
@@ -53,7 +56,7 @@ def brute_routed_attention(q, k, v, codebook, bias, w, force=None):
 
     rings = [deque() for _ in range(A)]
     evicted = 0
-    sels, outs = [], []
+    sels, outs, probe_scores, cand_scores = [], [], [], []
     for t in range(S):
         j = t // blk
         if t % blk == 0 and j - L >= 0:
@@ -88,6 +91,8 @@ def brute_routed_attention(q, k, v, codebook, bias, w, force=None):
             cands.extend(reversed(rings[a]))
         cands = cands[:M]
         rho = {i: _dot(q[t], ksum[i]) for i in cands}
+        probe_scores.append(score)
+        cand_scores.append([rho[i] for i in cands])
         sel, pool = [], list(cands)
         for _ in range(min(R, len(pool))):
             best = pool[0]
@@ -111,7 +116,70 @@ def brute_routed_attention(q, k, v, codebook, bias, w, force=None):
         z = sum(e)
         outs.append([sum(e[n] * v[s][d] for n, s in enumerate(keys)) / z for d in range(D)])
         sels.append(sel)
-    return dict(addr=addr, overflow=evicted, sel=sels, out=outs)
+    return dict(addr=addr, overflow=evicted, sel=sels, out=outs, logits=logits, probe_scores=probe_scores,
+                cand_scores=cand_scores)
+
+
+def _largest_first(values):
+    """The values sorted largest first, by insertion."""
+    out = []
+    for x in values:
+        out.append(x)
+        n = len(out) - 1
+        while n > 0 and out[n - 1] < x:
+            out[n] = out[n - 1]
+            n -= 1
+        out[n] = x
+    return out
+
+
+def top_gap(values, keep):
+    """Smallest difference between neighbours among the `keep` largest values (inf with fewer than two):
+    how close a ranking of the top `keep - 1` values, and its boundary with the next, comes to a tie."""
+    s = _largest_first(values)[:keep]
+    gaps = [s[n] - s[n + 1] for n in range(len(s) - 1)]
+    return min(gaps) if gaps else math.inf
+
+
+def brute_margins(bf, w):
+    """The decision margins of one brute-force routing run, each from a full sort of the scores it ranks:
+      addr_margin [nb][G]   best minus second-best logit of each subspace (inf with one code)
+      second_gap  [nb][G]   second minus third-best logit (inf with fewer than three codes)
+      probe_margin [S]      smallest neighbour gap among the min(P + 1, A) best address scores
+      sel_margin [S]        smallest neighbour gap among the min(R + 1, n) best candidate scores
+                            (inf without candidates or with R = 0)
+      alt_gap [nb]          with G > 1, the second-smallest subspace margin minus the smallest (which
+                            subspace the alternate address changes); inf with one subspace"""
+    G = w.subspaces
+    A = w.codes ** G
+    addr_margin, second_gap, alt_gap = [], [], []
+    for lg in bf["logits"]:
+        am = [top_gap(lg[g], 2) if len(lg[g]) > 1 else math.inf for g in range(G)]
+        addr_margin.append(am)
+        sg = []
+        for g in range(G):
+            s = _largest_first(lg[g])
+            sg.append(s[1] - s[2] if len(s) > 2 else math.inf)
+        second_gap.append(sg)
+        if G > 1 and w.codes > 1:
+            srt = _largest_first([-m for m in am])
+            alt_gap.append(srt[0] - srt[1])
+        else:
+            alt_gap.append(math.inf)
+    probe_margin = [top_gap(sc, min(w.probes + 1, A)) for sc in bf["probe_scores"]]
+    sel_margin = [top_gap(cs, min(w.remote + 1, len(cs))) if cs and w.remote > 0 else math.inf
+                  for cs in bf["cand_scores"]]
+    return dict(addr_margin=addr_margin, second_gap=second_gap, probe_margin=probe_margin, sel_margin=sel_margin,
+                alt_gap=alt_gap)
+
+
+def brute_posting_csr(addr, n_addr, local):
+    """CSR of the posting lists by counting: off[a] = number of filed blocks (i < nb - L) with an address
+    below a; the entries of address a are its filed blocks in ascending order."""
+    filed = range(max(0, len(addr) - local))
+    off = [sum(1 for i in filed if addr[i] < a) for a in range(n_addr + 1)]
+    idx = [i for a in range(n_addr) for i in filed if addr[i] == a]
+    return off, idx
 
 
 def brute_rope(x, base):

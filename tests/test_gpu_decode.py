@@ -15,7 +15,8 @@ import torch
 
 import oracle
 import synth
-from tests._gpu import NEAR, TOL, cfg_of, compare_selection, dev, host, integer_inputs, io_dtype, run_core, small
+from tests._gpu import (NEAR, TOL, cfg_of, compare_addresses, compare_selection, dev, host, integer_inputs, io_dtype,
+                        run_core, small)
 
 pytestmark = pytest.mark.gpu
 
@@ -54,6 +55,16 @@ def decode_run(mdr, w, inp, n0, chunk, force=None):
     return host(torch.cat(outs, dim=2)), host(torch.cat(sels, dim=2)), view
 
 
+def compare_addresses_prefix(w, inp, addr_g, b, h):
+    """compare_addresses on the first len(addr_g) blocks (those the decode state has filed)."""
+    ks = oracle.block_summaries(inp["k"][b, h], w.block)
+    bias = None if inp["bias"] is None else inp["bias"][h]
+    _, own, _ = oracle.block_addresses(ks, inp["codebook"][h], bias)
+    full = own.copy()
+    full[:len(addr_g)] = addr_g
+    return compare_addresses(w, inp, full, b, h)
+
+
 def check_against_oracle(w, inp, n0, out, sel, view, force=None):
     toks = np.arange(n0, w.seq)
     near = 0
@@ -64,19 +75,28 @@ def check_against_oracle(w, inp, n0, out, sel, view, force=None):
         for h in range(w.heads):
             bias = None if inp["bias"] is None else inp["bias"][h]
             f = None if force is None else force[b, h]
-            r = oracle.route_head(inp["q"][b, h], inp["k"][b, h], inp["codebook"][h], bias, w, f, tokens=toks)
-            sure_addr = r["addr_margin"].min(axis=1) > NEAR
             filed = max(0, last_j - w.local + 1)
-            if np.all(sure_addr[:filed]):
-                # the rings hold the prefill views of the last query block
-                assert view["filed"][b, h] == filed
-                assert view["overflow"][b, h] == oracle.posting_overflow(r["lists"], w.capacity)
-                for a in range(A):
-                    n = int(view["ring_n"][b, h, a])
-                    assert n == len(r["lists"][a]), (b, h, a)
-                    ring = [int(view["ring"][b, h, a, (n - 1 - e) % w.capacity]) for e in range(min(n, w.capacity))]
-                    assert ring == oracle.posting_view(r["lists"], a, last_j, w.local, w.capacity), (b, h, a)
-                near += compare_selection(r, sel[b, h])
+            # the decode state's addresses (near-ties allowed), then the oracle routed on them
+            addr_g = np.asarray(view["addr"][b, h][:filed])
+            na = compare_addresses_prefix(w, inp, addr_g, b, h)
+            ad = None
+            if na:
+                ad = np.zeros(w.nblocks, dtype=np.int64)
+                ad[:filed] = addr_g
+                ks = oracle.block_summaries(inp["k"][b, h], w.block)
+                _, own, _ = oracle.block_addresses(ks, inp["codebook"][h], bias)
+                ad[filed:] = own[filed:]  # blocks never filed: their addresses do not matter
+            r = oracle.route_head(inp["q"][b, h], inp["k"][b, h], inp["codebook"][h], bias, w, f, tokens=toks,
+                                  addr=ad)
+            # the rings hold the prefill views of the last query block
+            assert view["filed"][b, h] == filed
+            assert view["overflow"][b, h] == oracle.posting_overflow(r["lists"], w.capacity)
+            for a in range(A):
+                n = int(view["ring_n"][b, h, a])
+                assert n == len(r["lists"][a]), (b, h, a)
+                ring = [int(view["ring"][b, h, a, (n - 1 - e) % w.capacity]) for e in range(min(n, w.capacity))]
+                assert ring == oracle.posting_view(r["lists"], a, last_j, w.local, w.capacity), (b, h, a)
+            near += compare_selection(r, sel[b, h], w=w, inp=inp, b=b, h=h, force=f)
             ref = oracle.attention_packed(inp["q"][b, h], inp["k"][b, h], inp["v"][b, h], sel[b, h], w.block,
                                           w.local, tokens=toks)
             err = max(err, float(np.abs(out[b, h] - ref).max()))

@@ -18,7 +18,7 @@ import torch
 
 import oracle
 import synth
-from tests._gpu import NEAR, TOL, cfg_of, compare_selection, dev, host, io_dtype
+from tests._gpu import NEAR, TOL, cfg_of, check_head_routing, compare_selection, dev, host, io_dtype
 
 pytestmark = pytest.mark.gpu
 
@@ -71,25 +71,18 @@ def test_mixer_matches_oracle(gpu_lib, name):
                                        w, sel_override=res["sel"], io_dtype=w.dtype, policy=policy)
     near_a = near_s = 0
     ktol = 1e-5 if w.dtype == "f32" else 2e-3
+    q, k, _ = oracle.mixer_qkv(inp["x"], inp["wq"], inp["wk"], inp["wv"], w)
+    if w.dtype == "bf16":
+        q, k = oracle.round_to_bf16(q), oracle.round_to_bf16(k)
+    heads_inp = {"q": q.astype(np.float32), "k": k.astype(np.float32), "codebook": inp["codebook"], "bias": bias}
     for b in range(w.batch):
         for h in range(w.heads):
             r = routes[b][h]
             scale = max(1.0, float(np.abs(r["ksum"]).max()))
             np.testing.assert_allclose(res["ksum"][b, h], r["ksum"], rtol=0, atol=ktol * scale)
-            sure = r["addr_margin"].min(axis=1) > NEAR
-            near_a += int((~sure).sum())
-            assert np.array_equal(res["addr"][b, h][sure], r["addr"][sure]), (b, h)
-            if policy == "redirect":
-                bh_ = None if bias is None else bias[h]
-                second, margin = oracle.runner_up_codes(r["ksum"], inp["codebook"][h], bh_)
-                alt, gap = oracle.alternate_addresses(r["codes"], second, margin, w.codes)
-                gap2 = oracle.runner_up_gap(r["ksum"], inp["codebook"][h], bh_)
-                g_star = np.array([min(range(w.subspaces), key=lambda g: (margin[i, g], g))
-                                   for i in range(w.nblocks)])
-                ok = sure & (gap > NEAR) & (gap2[np.arange(w.nblocks), g_star] > NEAR)
-                assert np.array_equal(res["alt"][b, h][ok], alt[ok]), (b, h)
-            if np.all(sure[: max(0, w.nblocks - w.local)]):
-                near_s += compare_selection(r, res["sel"][b, h])
+            na, ns = check_head_routing(w, heads_inp, res, b, h, policy=policy)
+            near_a += na
+            near_s += ns
     err = float(np.abs(host(delta) - ref).max())
     print(f"{name}: address near-ties {near_a}, selection near-ties {near_s}, max abs err {err:.3g}, "
           f"overflow {int(res['overflow'].sum())}")

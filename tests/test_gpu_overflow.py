@@ -15,7 +15,7 @@ import torch
 
 import oracle
 import synth
-from tests._gpu import NEAR, cfg_of, compare_selection, dev, host, io_dtype, run_core, small
+from tests._gpu import NEAR, cfg_of, check_head_routing, compare_selection, dev, host, io_dtype, run_core, small
 
 pytestmark = pytest.mark.gpu
 
@@ -52,37 +52,17 @@ def test_redirect_end_to_end(gpu_lib, name, over, seed):
     w = small(name, **over)
     inp = synth.make_core_inputs(w, seed)
     res = run_core(mdr, w, inp, policy="redirect")
-    routes = oracle_routes(w, inp, "redirect")
-    A = w.addresses
-    full = near_alt = near_sel = 0
+    near_up = near_sel = 0
     over_total = 0
     for b in range(w.batch):
         for h in range(w.heads):
-            r = routes[b][h]
-            sure = alt_sure(w, inp, r, b, h)
-            near_alt += int((~sure).sum())
-            assert np.array_equal(res["alt"][b, h][sure], r["alt"][sure]), (b, h)
-            if not np.all((r["addr_margin"].min(axis=1) > NEAR)[: w.nblocks - w.local]) or \
-                    not np.all(sure[: w.nblocks - w.local]):
-                continue
-            full += 1
-            over_total += r["overflow"]
-            assert res["overflow"][b, h] == r["overflow"], (b, h)
-            ro, ri, rt = res["redir_off"][b, h], res["redir_idx"][b, h], res["redir_time"][b, h]
-            n = 0
-            for a in range(A):
-                got = [(int(rt[k]), int(ri[k])) for k in range(ro[a], ro[a + 1])]
-                assert got == r["rd"][a], (b, h, a)
-                n += len(got)
-            assert ro[A] == n and np.all(ri[n:] == -1) and np.all(rt[n:] == -1)
-            near_sel += compare_selection(r, res["sel"][b, h])
-            sure_p = r["probe_margin"] > NEAR
-            assert np.array_equal(res["n_drop"][b, h][sure_p], r["n_drop"][sure_p]), (b, h)
-            assert np.array_equal(res["n_cand"][b, h][sure_p], r["n_cand"][sure_p]), (b, h)
-    assert full > 0, "no (b, h) without near-ties to compare whole lists on"
+            nu, ns = check_head_routing(w, inp, res, b, h, policy="redirect")
+            near_up += nu
+            near_sel += ns
+            over_total += int(res["overflow"][b, h])
     assert over_total > 0 or name == "recall"
-    print(f"{name} {over}: {full} heads compared in full, alternate near-ties {near_alt}, "
-          f"selection near-ties {near_sel}, overflow {over_total}")
+    print(f"{name} {over}: every head compared (on the GPU's addresses and alternates where they hold "
+          f"near-ties: {near_up}), selection near-ties {near_sel} (validated), overflow {over_total}")
 
 
 @pytest.mark.parametrize("name,over", CASES[:3])
@@ -92,16 +72,11 @@ def test_drop_policy_dropped_candidates(gpu_lib, name, over):
     w = small(name, **over)
     inp = synth.make_core_inputs(w, 1)
     res = run_core(mdr, w, inp)
-    routes = oracle_routes(w, inp, "drop")
     total = 0
     for b in range(w.batch):
         for h in range(w.heads):
-            r = routes[b][h]
-            if not np.all(r["addr_margin"].min(axis=1) > NEAR):
-                continue
-            sure_p = r["probe_margin"] > NEAR
-            assert np.array_equal(res["n_drop"][b, h][sure_p], r["n_drop"][sure_p]), (b, h)
-            total += int(r["n_drop"].sum())
+            check_head_routing(w, inp, res, b, h)  # n_drop on every probe-sure token, every head
+            total += int(res["n_drop"][b, h].sum())
     assert total > 0
     print(f"{name} {over}: dropped candidates {total}")
 
@@ -180,7 +155,7 @@ def test_staged_redirect_on_oracle_upstream(gpu_lib, name, over):
     for b in range(B):
         for h in range(H):
             r = routes[b][h]
-            near += compare_selection(r, sel[b, h])
+            near += compare_selection(r, sel[b, h], w=w, inp=inp, b=b, h=h, policy="redirect")
             sure = r["probe_margin"] > NEAR
             assert np.array_equal(ncand[b, h][sure], r["n_cand"][sure])
             assert np.array_equal(ndrop[b, h][sure], r["n_drop"][sure])

@@ -12,8 +12,8 @@ import torch
 
 import oracle
 import synth
-from tests._gpu import (NEAR, TOL, attention_rows, cfg_of, compare_addresses, compare_selection, dev, host,
-                        integer_inputs, io_dtype, run_core, small)
+from tests._gpu import (NEAR, TOL, attention_rows, cfg_of, check_head_routing, compare_addresses, compare_selection,
+                        dev, host, integer_inputs, io_dtype, route_for, run_core, small)
 
 pytestmark = pytest.mark.gpu
 
@@ -100,7 +100,8 @@ def test_stage_probe_rerank_on_oracle_index(gpu_lib, name):
     for b in range(B):
         for h in range(H):
             r = routes[b][h]
-            near += compare_selection(r, sel[b, h])
+            near += compare_selection(r, sel[b, h], w=w, inp=inp, b=b, h=h,
+                                      force=None if force is None else force[b, h])
             sure = r["probe_margin"] > NEAR
             assert np.array_equal(ncand[b, h][sure], r["n_cand"][sure])
     print(f"{name}: probe/rerank near-tie tokens {near} of {B * H * S}")
@@ -166,21 +167,13 @@ def test_routed_attention_end_to_end(gpu_lib, name):
     err = 0.0
     for b in range(w.batch):
         for h in range(w.heads):
-            na = compare_addresses(w, inp, res["addr"][b, h], b, h)
+            na, ns = check_head_routing(w, inp, res, b, h, force=inp.get("force"))
             near_a += na
-            f = None if inp.get("force") is None else inp["force"][b, h]
-            r = oracle.route_head(inp["q"][b, h], inp["k"][b, h], inp["codebook"][h],
-                                  None if inp["bias"] is None else inp["bias"][h], w, f)
-            if na == 0:
-                assert res["overflow"][b, h] == r["overflow"]
-                assert np.array_equal(res["post_off"][b, h], r["off"])
-                n_filed = len(r["idx"])
-                assert np.array_equal(res["post_idx"][b, h][:n_filed], r["idx"])
-                assert np.all(res["post_idx"][b, h][n_filed:] == -1)
-                near_s += compare_selection(r, res["sel"][b, h])
+            near_s += ns
             ref = attention_rows(w, inp, res["sel"][b, h], b, h, None, dense=w.seq <= 4096)
             err = max(err, float(np.abs(res["out"][b, h] - ref).max()))
-    print(f"{name}: address near-ties {near_a}, selection near-ties {near_s}, max abs err {err:.3g}")
+    print(f"{name}: address near-ties {near_a}, selection near-ties {near_s} (each checked for validity), "
+          f"max abs err {err:.3g}")
     assert err <= TOL[w.dtype]
 
 
@@ -251,9 +244,7 @@ def test_edge_cases(gpu_lib, over):
     res = run_core(mdr, w, inp)
     for b in range(w.batch):
         for h in range(w.heads):
-            r = oracle.route_head(inp["q"][b, h], inp["k"][b, h], inp["codebook"][h], None, w)
-            compare_addresses(w, inp, res["addr"][b, h], b, h)
-            compare_selection(r, res["sel"][b, h])
+            check_head_routing(w, inp, res, b, h)
             ref = attention_rows(w, inp, res["sel"][b, h], b, h, None, dense=True)
             assert np.abs(res["out"][b, h] - ref).max() <= TOL[w.dtype]
 
@@ -304,24 +295,22 @@ def test_full_size_sampled(gpu_lib, name):
     res = run_core(mdr, w, inp)
     rng = np.random.default_rng(7)
     heads = [(b, h) for b in range(w.batch) for h in range(w.heads)]
+    near_a = {}
     for b, h in heads:
-        ks = oracle.block_summaries(inp["k"][b, h], w.block)
-        bias = None if inp["bias"] is None else inp["bias"][h]
-        _, addr, margin = oracle.block_addresses(ks, inp["codebook"][h], bias)
-        if margin.min() > NEAR:
-            assert np.array_equal(res["addr"][b, h], addr)
-            lists = oracle.posting_lists(addr, w.addresses, w.local)
-            assert res["overflow"][b, h] == oracle.posting_overflow(lists, w.capacity)
+        near_a[b, h] = compare_addresses(w, inp, res["addr"][b, h], b, h)
+        lists = oracle.posting_lists(res["addr"][b, h], w.addresses, w.local)  # on the GPU's addresses
+        assert res["overflow"][b, h] == oracle.posting_overflow(lists, w.capacity)
     picks = [heads[i] for i in rng.choice(len(heads), size=min(4, len(heads)), replace=False)]
     err = 0.0
+    near = 0
     for b, h in picks:
         toks = np.unique(np.concatenate([rng.choice(w.seq, 96, replace=False), [0, w.block - 1, w.seq - 1]]))
-        r = oracle.route_head(inp["q"][b, h], inp["k"][b, h], inp["codebook"][h],
-                              None if inp["bias"] is None else inp["bias"][h], w, tokens=toks)
-        compare_selection(r, res["sel"][b, h], rows=toks)
+        _, ns = check_head_routing(w, inp, res, b, h, tokens=toks)
+        near += ns
         ref = attention_rows(w, inp, res["sel"][b, h][toks], b, h, toks)
         err = max(err, float(np.abs(res["out"][b, h][toks] - ref).max()))
-    print(f"{name} full size: overflow total {int(res['overflow'].sum())}, "
+    print(f"{name} full size: overflow total {int(res['overflow'].sum())}, address near-ties "
+          f"{sum(near_a.values())}, sampled selection near-ties {near}, "
           f"R_eff {float((res['sel'] >= 0).sum(-1).mean()):.3f}, sampled max abs err {err:.3g}")
     assert err <= TOL[w.dtype]
 
@@ -338,11 +327,7 @@ def test_generic_probe_kernel(gpu_lib, name, over):
     near = 0
     for b in range(w.batch):
         for h in range(w.heads):
-            if compare_addresses(w, inp, res["addr"][b, h], b, h):
-                continue
-            r = oracle.route_head(inp["q"][b, h], inp["k"][b, h], inp["codebook"][h],
-                                  None if inp["bias"] is None else inp["bias"][h], w)
-            near += compare_selection(r, res["sel"][b, h])
+            near += check_head_routing(w, inp, res, b, h)[1]
             ref = attention_rows(w, inp, res["sel"][b, h], b, h, None, dense=w.seq <= 4096)
             assert np.abs(res["out"][b, h] - ref).max() <= TOL[w.dtype]
     print(f"{name} {over}: selection near-ties {near}")
@@ -436,10 +421,7 @@ def test_size_limits(gpu_lib, case):
     assert mdr.mdr_check_config(cfg_of(mdr, w)) == 0
     inp = synth.make_core_inputs(w, 4)
     res = run_core(mdr, w, inp)
-    q, k, v = (inp[n][0, 0] for n in ("q", "k", "v"))
-    compare_addresses(w, inp, res["addr"][0, 0], 0, 0)
-    r = oracle.route_head(q, k, inp["codebook"][0], None, w, tokens=toks)
-    near = compare_selection(r, res["sel"][0, 0], rows=toks)
+    _, near = check_head_routing(w, inp, res, 0, 0, tokens=toks)
     rows = np.arange(w.seq) if toks is None else toks
     ref = attention_rows(w, inp, res["sel"][0, 0][rows], 0, 0, toks)
     err = float(np.abs(res["out"][0, 0][rows] - ref).max())

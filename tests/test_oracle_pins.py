@@ -556,3 +556,147 @@ def test_round_to_bf16_matches_torch():
     for x in (a, grid, ties, -ties):
         ref = torch.tensor(x).to(torch.bfloat16).double().numpy()
         np.testing.assert_array_equal(oracle.round_to_bf16(x), ref)
+
+
+# ---------------------------------------------------------------- decision margins
+#
+# The margins decide which GPU decisions the parity tests compare exactly (a decision whose margin is at
+# most 1e-4 may legitimately come out either way in fp32).  They are pinned here against margins taken
+# from a full sort of the raw scores the brute force computes, on dyadic inputs where every score is exact.
+
+def margin_mismatches(w, q, k, cb, b, rdtype=np.float32):
+    """Every disagreement between the oracle's margins, posting CSR and runner-up gaps and the brute force's."""
+    from tests._brute import brute_margins, brute_posting_csr
+
+    bad = []
+    r = oracle.route_head(q, k, cb, b, w, rdtype=rdtype)
+    bf = brute_routed_attention(q.tolist(), k.tolist(), np.zeros_like(q).tolist(), cb.tolist(),
+                                None if b is None else b.tolist(), w)
+    bm = brute_margins(bf, w)
+    if r["addr_margin"].tolist() != bm["addr_margin"]:
+        bad.append("addr_margin")
+    if r["probe_margin"].tolist() != bm["probe_margin"]:
+        bad.append("probe_margin")
+    if r["sel_margin"].tolist() != bm["sel_margin"]:
+        bad.append("sel_margin")
+    gap = oracle.runner_up_gap(r["ksum"], cb, b, rdtype)
+    if gap.tolist() != bm["second_gap"]:
+        bad.append("runner_up_gap")
+    second, m32 = oracle.runner_up_codes(r["ksum"], cb, b, rdtype)
+    _, alt_gap = oracle.alternate_addresses(r["codes"], second, m32, w.codes)
+    if alt_gap.tolist() != bm["alt_gap"]:
+        bad.append("alt_gap")
+    off, idx = brute_posting_csr(bf["addr"], w.addresses, w.local)
+    if r["off"].tolist() != off or r["idx"].tolist() != idx:
+        bad.append("posting_csr")
+    return bad
+
+
+@pytest.mark.parametrize("case", range(len(SMALL)))
+@pytest.mark.parametrize("seed", [0, 1, 2])
+@pytest.mark.parametrize("rdtype", [np.float32, np.float64])
+def test_margins_match_brute_force_sorts(case, seed, rdtype):
+    w = _w(**SMALL[case])
+    q, k, v, cb, b = _dyadic_inputs(w, seed, bias=(seed == 1))
+    assert margin_mismatches(w, q, k, cb, b, rdtype) == []
+
+
+def test_margins_count_inner_rank_gaps():
+    """Hand cases whose closest gap lies inside the kept ranks, not at the boundary with the first one
+    left out: the probe margin over address scores 10, 9.75, 5, 1 with P = 2 is 0.25 (between the first
+    and second probe), not 4.75; the rerank margin over candidate scores 8, 7.5, 7.375, 0 with R = 2 is
+    0.125; with R = 3 it is still 0.125 (ranks 2-3), not 7.375 (the boundary)."""
+    top, m = oracle.top_probes(np.array([[1.0, 10.0, 5.0, 9.75]]), 2)
+    assert top.tolist() == [[1, 3]] and m.tolist() == [0.25]
+    top, m = oracle.top_probes(np.array([[4.0, 3.0, 2.5, 0.0]]), 3)  # boundary 2.5 | 0 is 2.5, inner 0.5
+    assert top.tolist() == [[0, 1, 2]] and m.tolist() == [0.5]
+    D = 4
+    ks = np.zeros((4, D), dtype=np.float32)
+    ks[:, 0] = [8.0, 7.5, 7.375, 0.0]
+    q = np.array([1.0, 0.0, 0.0, 0.0], dtype=np.float32)
+    sel, m = oracle.rerank(q, ks, [3, 2, 1, 0], 2)
+    assert sel == [0, 1] and m == 0.125
+    sel, m = oracle.rerank(q, ks, [3, 2, 1, 0], 3)
+    assert sel == [0, 1, 2] and m == 0.125
+    sel, m = oracle.rerank(q, ks, [3, 0], 2)  # fewer candidates than R + 1: the gap between the two
+    assert sel == [0, 3] and m == 8.0
+    # block addresses: logits 3, 2.875, 1 in subspace 0 -> margin 0.125; runner-up gap 1.875
+    cb = np.zeros((1, 3, D), dtype=np.float32)
+    cb[0, :, 0] = [2.875, 3.0, 1.0]
+    one = np.zeros((1, D), dtype=np.float32)
+    one[0, 0] = 1.0
+    codes, addr, margin = oracle.block_addresses(one, cb, None)
+    assert codes.tolist() == [[1]] and margin.tolist() == [[0.125]]
+    assert oracle.runner_up_gap(one, cb, None).tolist() == [[1.875]]
+
+
+# Seeded mistakes, each a plausible slip in one margin function, planted in the oracle on the CPU: the pin
+# above must catch every one of them.
+def _probe_boundary_only(sigma, probes):
+    order = np.argsort(-sigma, axis=-1, kind="stable")
+    s = np.take_along_axis(sigma, order, axis=-1).astype(np.float64)
+    n = min(probes, sigma.shape[-1] - 1)
+    return order[..., :probes], s[..., n - 1] - s[..., n]
+
+
+def _probe_inner_only(sigma, probes):
+    order = np.argsort(-sigma, axis=-1, kind="stable")
+    s = np.take_along_axis(sigma, order[..., :probes], axis=-1).astype(np.float64)
+    m = (s[..., :-1] - s[..., 1:]).min(axis=-1) if probes > 1 else np.full(sigma.shape[:-1], oracle.INF)
+    return order[..., :probes], m
+
+
+def _rerank_boundary_only(q_t, ksum, cands, remote, rdtype=np.float32):
+    if not cands or remote == 0:
+        return [], oracle.INF
+    rho = np.asarray(ksum[cands], dtype=rdtype) @ np.asarray(q_t, dtype=rdtype)
+    order = sorted(range(len(cands)), key=lambda n: (-float(rho[n]), cands[n]))
+    top = [float(rho[n]) for n in order[:remote + 1]]
+    return [cands[n] for n in order[:remote]], (top[-2] - top[-1]) if len(top) > 1 else oracle.INF
+
+
+def _addresses_wrong_margin(ksum, codebook, bias, rdtype=np.float32):
+    codes, addr, margin = _ORIG["block_addresses"](ksum, codebook, bias, rdtype)
+    lg = oracle.code_logits(ksum, codebook, bias, rdtype)
+    srt = np.sort(lg, axis=2).astype(np.float64)
+    return codes, addr, srt[..., -1] - srt[..., 0]  # best minus worst instead of best minus second
+
+
+def _alternates_wrong_gap(codes, second, margin, n_codes):
+    alt, gap = _ORIG["alternate_addresses"](codes, second, margin, n_codes)
+    return alt, np.where(np.isfinite(gap), margin.max(axis=1) - margin.min(axis=1), gap)  # largest, not next
+
+
+def _csr_descending(lists):
+    off, idx = _ORIG["posting_csr"](lists)
+    return off, np.concatenate([idx[off[a]:off[a + 1]][::-1] for a in range(len(lists))]).astype(np.int64)
+
+
+def _runner_up_gap_wrong(ksum, codebook, bias, rdtype=np.float32):
+    lg = oracle.code_logits(ksum, codebook, bias, rdtype)
+    srt = np.sort(lg.astype(np.float64), axis=2)
+    return srt[..., -1] - srt[..., -2]  # first minus second instead of second minus third
+
+
+_ORIG = {n: getattr(oracle.mdr_oracle, n) for n in ("block_addresses", "posting_csr", "alternate_addresses")}
+
+
+@pytest.mark.parametrize("name,fn,field", [
+    ("top_probes", _probe_boundary_only, "probe_margin"),
+    ("top_probes", _probe_inner_only, "probe_margin"),
+    ("rerank", _rerank_boundary_only, "sel_margin"),
+    ("block_addresses", _addresses_wrong_margin, "addr_margin"),
+    ("posting_csr", _csr_descending, "posting_csr"),
+    ("runner_up_gap", _runner_up_gap_wrong, "runner_up_gap"),
+    ("alternate_addresses", _alternates_wrong_gap, "alt_gap"),
+])
+def test_margin_pins_catch_planted_mistakes(monkeypatch, name, fn, field):
+    monkeypatch.setattr(oracle.mdr_oracle, name, fn)
+    monkeypatch.setattr(oracle, name, fn)
+    found = set()
+    for case in range(len(SMALL)):
+        w = _w(**SMALL[case])
+        for seed in (0, 1, 2):
+            q, k, v, cb, b = _dyadic_inputs(w, seed, bias=(seed == 1))
+            found.update(margin_mismatches(w, q, k, cb, b))
+    assert field in found
