@@ -471,8 +471,11 @@ __global__ __launch_bounds__(kProbeThreads) void k_probe_rerank(
           l1 = mid;
       }
       const int nprim = l0 - lo, tp = min(s.cap, nprim);
-      const int take = R > 0 ? min(tp, s.M - nc) : 0;
-      for (int e = 0; e < take; ++e) consider(idxp[l0 - 1 - e]);
+      const int take = min(tp, s.M - nc);  // with R = 0 the candidates are counted, not scored
+      if (R > 0)
+        for (int e = 0; e < take; ++e) consider(idxp[l0 - 1 - e]);
+      else
+        nc += take;
       int narr = 0;
       if (roffp) {
         const int rlo = roffp[a];
@@ -485,8 +488,11 @@ __global__ __launch_bounds__(kProbeThreads) void k_probe_rerank(
             r1 = mid;
         }
         narr = r0 - rlo;
-        const int taker = R > 0 ? min(min(s.cap - tp, narr), s.M - nc) : 0;
-        for (int e = 0; e < taker; ++e) consider(ridxp[r0 - 1 - e]);
+        const int taker = min(min(s.cap - tp, narr), s.M - nc);
+        if (R > 0)
+          for (int e = 0; e < taker; ++e) consider(ridxp[r0 - 1 - e]);
+        else
+          nc += taker;
       }
       // held: the primaries not redirected away (every block has an alternate when C > 1) plus arrivals
       ndr += max(0, (roffp && C > 1 ? tp : nprim) + narr - s.cap);
