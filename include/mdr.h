@@ -199,6 +199,22 @@ mdr_status mdr_routed_attention(const mdr_config* cfg, const void* q, const void
                                 void* out, const mdr_routing* routing, void* workspace,
                                 size_t workspace_bytes, void* stream);
 
+/* mdr_routed_attention without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Its workspace is a static device array
+ * of MDR_NOALLOC_SCRATCH_BYTES inside the library, one copy per GPU, held
+ * until the process ends; the call allocates nothing.  A configuration whose
+ * workspace (mdr_workspace_size) exceeds it returns MDR_ERR_WORKSPACE before
+ * anything is launched.  Every call on a GPU shares that GPU's array, so calls
+ * that overlap in time on one GPU (other streams, other host threads) race and
+ * must be serialised by the caller.  The first call on each device looks up
+ * that device's copy (a host-side lookup, no allocation).  Everything else is
+ * as in mdr_routed_attention, with identical results. */
+#define MDR_NOALLOC_SCRATCH_BYTES (64u << 20)
+mdr_status mdr_routed_attention_noalloc(const mdr_config* cfg, const void* q, const void* k, const void* v,
+                                        const float* codebook, const float* code_bias, const int32_t* force,
+                                        void* out, const mdr_routing* routing, void* stream);
+
 /* Kernels of the core path, in launch order (the profiling form below records
  * an event before each and one after the last). */
 #define MDR_CORE_KERNELS 5 /* address, post, probe_rerank, attn_remote, attn_local */

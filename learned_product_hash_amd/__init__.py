@@ -23,6 +23,7 @@ __all__ = [
     "mdr_abi_version", "mdr_status_string", "mdr_check_config", "mdr_workspace_size", "MdrWorkspaceParts",
     "mdr_workspace_breakdown", "workspace_breakdown",
     "mdr_routed_attention", "mdr_routed_attention_profiled", "MDR_CORE_KERNELS", "CORE_KERNELS",
+    "mdr_routed_attention_noalloc", "MDR_NOALLOC_SCRATCH_BYTES",
     "mdr_mixer_forward", "mdr_stage_address", "mdr_stage_post",
     "mdr_stage_probe_rerank", "mdr_stage_attend", "mdr_stage_attend_lse", "mdr_stage_attend_backward",
     "mdr_stage_attend_backward_profiled", "MDR_BACKWARD_KERNELS", "BACKWARD_KERNELS",
@@ -86,6 +87,7 @@ _SIGS = {
     "mdr_routed_attention": ([_cfgp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _rtp, _vp, _sz, _vp], _i32),
     "mdr_routed_attention_profiled": ([_cfgp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _rtp, _vp, _sz,
                                        ctypes.POINTER(_vp), _vp], _i32),
+    "mdr_routed_attention_noalloc": ([_cfgp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _rtp, _vp], _i32),
     "mdr_mixer_forward": ([_cfgp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _rtp, _vp, _sz, _vp], _i32),
     "mdr_stage_address": ([_cfgp] + [_vp] * 7, _i32),
     "mdr_stage_post": ([_cfgp] + [_vp] * 9, _i32),
@@ -208,6 +210,16 @@ def mdr_routed_attention(cfg, q, k, v, codebook, code_bias, force, out, routing=
     _check(lib.mdr_routed_attention(ctypes.byref(cfg), _ptr(q), _ptr(k), _ptr(v), _ptr(codebook),
                                     _ptr(code_bias), _ptr(force), _ptr(out), _routing(routing), wp, wn,
                                     _stream(stream)), "mdr_routed_attention")
+
+
+MDR_NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def mdr_routed_attention_noalloc(cfg, q, k, v, codebook, code_bias, force, out, routing=None, stream=None):
+    """mdr_routed_attention on the library's static per-GPU scratch (no workspace argument)."""
+    _check(lib.mdr_routed_attention_noalloc(ctypes.byref(cfg), _ptr(q), _ptr(k), _ptr(v), _ptr(codebook),
+                                            _ptr(code_bias), _ptr(force), _ptr(out), _routing(routing),
+                                            _stream(stream)), "mdr_routed_attention_noalloc")
 
 
 MDR_CORE_KERNELS = 5

@@ -4,6 +4,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "mdr_internal.h"
 
 using namespace mdr;
@@ -306,6 +308,63 @@ mdr_status mdr_routed_attention(const mdr_config* cfg, const void* q, const void
     return MDR_ERR_INVALID_ARG;
   Buffers b;
   st = check_workspace(s, workspace, workspace_bytes, &b);
+  if (st != MDR_OK) return st;
+  apply_routing(routing, &b);
+  return run_core(s, q, k, v, codebook, code_bias, force, out, b, (hipStream_t)stream);
+}
+
+}  // extern "C"
+
+// ---- the entry point that allocates nothing: its workspace is a file-scope device array, one copy per
+// GPU, held until the process ends.  Host code never passes `scratch` itself (on the host that name is
+// only a stand-in, not a device address): each device's copy is looked up once with
+// hipGetSymbolAddress, with that device current, and that address is used from then on.
+namespace mdr {
+constexpr size_t kNoAllocScratchBytes = (size_t)MDR_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) char scratch[kNoAllocScratchBytes];
+}  // namespace mdr
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// This device's copy of the scratch array (looked up on the first call on the device).
+mdr_status scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MDR_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MDR_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MDR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+mdr_status mdr_routed_attention_noalloc(const mdr_config* cfg, const void* q, const void* k, const void* v,
+                                        const float* codebook, const float* code_bias, const int32_t* force,
+                                        void* out, const mdr_routing* routing, void* stream) {
+  Shape s;
+  mdr_status st = shape_from_config(cfg, false, &s);
+  if (st != MDR_OK) return st;
+  s.W = 0;
+  if (!q || !k || !v || !codebook || !out) return MDR_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(codebook) ||
+      !routing_aligned(routing))
+    return MDR_ERR_INVALID_ARG;
+  if (layout(s, nullptr, nullptr) > kNoAllocScratchBytes) return MDR_ERR_WORKSPACE;
+  void* ws = nullptr;
+  st = scratch_address(&ws);
+  if (st != MDR_OK) return st;
+  Buffers b;
+  st = check_workspace(s, ws, kNoAllocScratchBytes, &b);
   if (st != MDR_OK) return st;
   apply_routing(routing, &b);
   return run_core(s, q, k, v, codebook, code_bias, force, out, b, (hipStream_t)stream);

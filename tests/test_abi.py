@@ -157,6 +157,24 @@ def test_workspace_breakdown_sums_to_the_workspace_size(mdr):
         mdr.workspace_breakdown(mdr.config(**_good(seq=4000)))
 
 
+def test_noalloc_validates_before_touching_the_device(mdr):
+    """The entry point without a workspace checks the configuration and its scratch limit on the host:
+    a workspace beyond MDR_NOALLOC_SCRATCH_BYTES is MDR_ERR_WORKSPACE, nothing launched."""
+    text = open(HEADER).read()
+    assert "#define MDR_NOALLOC_SCRATCH_BYTES (64u << 20)" in text
+    assert mdr.MDR_NOALLOC_SCRATCH_BYTES == 64 << 20
+    big = mdr.config(**_good(seq=32768))
+    assert mdr.mdr_workspace_size(big) > mdr.MDR_NOALLOC_SCRATCH_BYTES
+    fake = 1 << 20  # aligned non-null pointers: never dereferenced, the call returns first
+    for cfg, status in ((big, 3), (mdr.config(**_good(seq=4000)), 1)):
+        with pytest.raises(mdr.MdrError) as e:
+            mdr.mdr_routed_attention_noalloc(cfg, fake, fake, fake, fake, None, None, fake, stream=0)
+        assert e.value.status == status
+    with pytest.raises(mdr.MdrError) as e:  # a null input
+        mdr.mdr_routed_attention_noalloc(mdr.config(**_good()), None, fake, fake, fake, None, None, fake, stream=0)
+    assert e.value.status == 1
+
+
 def test_decode_state_size_and_view(mdr):
     cfg = mdr.config(**_good())
     n = mdr.mdr_decode_state_size(cfg)
