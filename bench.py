@@ -47,12 +47,13 @@ KERNEL_SYMBOL = {  # substrings of the kernels' symbol names in rocprofv3 output
     "address": "k_address",
     "post": "k_post",
     "probe_rerank": "k_probe",
+    "attn_bin": "k_pair_scatter",
     "attn_remote": "k_attn_remote",
     "attn_local": "k_attn_local",
 }
 KERNEL_SOURCE = {
     "address": "mdr_route.hip", "post": "mdr_route.hip", "probe_rerank": "mdr_route.hip",
-    "attn_remote": "mdr_attn.hip", "attn_local": "mdr_attn.hip",
+    "attn_bin": "mdr_pairs.hip", "attn_remote": "mdr_attn.hip", "attn_local": "mdr_attn.hip",
 }
 MIXER_SYMBOL = {  # every listed substring must occur in the (mangled) kernel name
     "qkv (fused projections + RoPE + summaries + addresses)": ("k_mm", "Lb0ELb1E"),
@@ -228,12 +229,15 @@ def design_bytes(w, st):
     qkv = BH * S * D * e
     cb = H * G * C * D * 4
     pairs, used = st["pairs"], st["blocks_used"]
-    part = D * e + 8
+    part = D * e + 4  # a remote partial: normalised output row and its log2 normaliser
+    tbin = ((S + 15) // 16 + 255) // 256 * 256  # tokens per range of the pair binning
+    ng = (S + tbin - 1) // tbin
     return {
         "address": qkv + BH * nb * D * 4 + 2 * BH * nb * 4 + cb,
         "post": BH * nb * 4 + BH * (A + 1) * 4 + BH * nb * 4 + BH * 4,
-        "probe_rerank": qkv + cb + BH * (A + 1 + nb) * 4 + BH * nb * D * 4 + BH * S * (R + 1) * 4 + pairs * 12,
-        "attn_remote": pairs * (D * e + 4 + part) + used * 2 * blk * D * e + BH * (ne * (ne + 1) // 2) * 4,
+        "probe_rerank": qkv + cb + BH * (A + 1 + nb) * 4 + BH * nb * D * 4 + BH * S * (R + 1) * 4,
+        "attn_bin": BH * S * R * 4 + BH * ng * ne * 4 + pairs * 4 + BH * (ne + 1) * 4,
+        "attn_remote": pairs * (4 + D * e + part) + used * 2 * blk * D * e,
         "attn_local": 4 * qkv + BH * S * R * 4 + pairs * part,
     }
 

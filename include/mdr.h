@@ -217,13 +217,14 @@ mdr_status mdr_routed_attention_noalloc(const mdr_config* cfg, const void* q, co
 
 /* Kernels of the core path, in launch order (the profiling form below records
  * an event before each and one after the last). */
-#define MDR_CORE_KERNELS 5 /* address, post, probe_rerank, attn_remote, attn_local */
+#define MDR_CORE_KERNELS 6 /* address, post, probe_rerank, attn_bin, attn_remote, attn_local */
 
 /* Profiling form of mdr_routed_attention, for timing each kernel on `stream`:
  * events[k] (a hipEvent_t created by the caller) is recorded just before the
  * k-th kernel of the core path and events[MDR_CORE_KERNELS] after the last one.
- * A kernel a configuration does not need (attn_remote when R = 0 or nb <= L)
- * gets two adjacent events.  A NULL entry records nothing at that point (so a
+ * attn_bin groups the selected (token, slot) pairs by remote block for
+ * attn_remote.  A kernel a configuration does not need (attn_bin and
+ * attn_remote when R = 0 or nb <= L) gets two adjacent events.  A NULL entry records nothing at that point (so a
  * caller can time one kernel alone); a NULL `events` array is rejected.
  * Everything else is as in mdr_routed_attention. */
 mdr_status mdr_routed_attention_profiled(const mdr_config* cfg, const void* q, const void* k, const void* v,
@@ -323,9 +324,9 @@ mdr_status mdr_stage_attend_backward(const mdr_config* cfg, const void* q, const
                                      const void* d_out, void* dq, void* dk, void* dv, void* workspace,
                                      size_t workspace_bytes, void* stream);
 
-/* Kernels of the backward, in launch order: pair binning (with the counter
- * fill before it; empty when R = 0 or nb <= L), row dots D, key blocks (dK,
- * dV, remote dQ shares), query blocks (dQ). */
+/* Kernels of the backward, in launch order: pair binning (counter fill, count
+ * and scatter; empty when R = 0 or nb <= L), row dots D, key blocks (dK, dV,
+ * remote dQ shares), query blocks (dQ). */
 #define MDR_BACKWARD_KERNELS 4
 
 /* Profiling form of mdr_stage_attend_backward: events[k] (hipEvent_t created

@@ -222,8 +222,8 @@ def mdr_routed_attention_noalloc(cfg, q, k, v, codebook, code_bias, force, out, 
                                             _stream(stream)), "mdr_routed_attention_noalloc")
 
 
-MDR_CORE_KERNELS = 5
-CORE_KERNELS = ("address", "post", "probe_rerank", "attn_remote", "attn_local")
+MDR_CORE_KERNELS = 6
+CORE_KERNELS = ("address", "post", "probe_rerank", "attn_bin", "attn_remote", "attn_local")
 
 
 def mdr_routed_attention_profiled(cfg, q, k, v, codebook, code_bias, force, out, events, routing=None, ws=None,

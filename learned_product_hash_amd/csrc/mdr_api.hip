@@ -63,15 +63,21 @@ mdr_status shape_from_config(const mdr_config* cfg, bool mixer, Shape* out) {
   s.policy = c.overflow_policy;
   const long long ne = nb > c.local ? nb - c.local : 0;
   s.ne = (int)ne;
-  s.cells_per_bh = ne * (ne + 1) / 2;
-  // split heavy blocks over several remote work-groups when blocks average several iterations
-  const long long avg_pairs = ne > 0 ? (long long)c.seq * c.remote / ne : 0;
-  long long split = avg_pairs / 512;
-  s.split = (int)(split < 1 ? 1 : split > 8 ? 8 : split);
+  // pair binning: at most kMaxBinRanges token ranges per (b,h), each a whole number of 256-token probe
+  // work-groups; remote work items of kItemPairs pairs, at most one partial item per block
+  const long long tb = ((c.seq + kMaxBinRanges - 1) / kMaxBinRanges + 255) / 256 * 256;
+  s.tbin = (int)tb;
+  s.ng = (int)((c.seq + tb - 1) / tb);
+  const long long pairs = (long long)c.seq * c.remote;
+  const long long items = ne + (pairs + kItemPairs - 1) / kItemPairs;
+  if (pairs >= (1LL << 31) || items * c.batch * c.heads >= (1LL << 31)) return MDR_ERR_UNSUPPORTED;
+  s.max_items = (int)items;
+  s.pin = (c.batch * c.heads) % kXcds == 0;
   s.csr_lds = ((long long)s.A + 1 + ne) * 4 <= 16384;
   s.fixed_probe = probe_fixed_shape(s);
   if (probe_lds_bytes(s) > 160 * 1024) return MDR_ERR_UNSUPPORTED;
-  if (s.R > 0 && ne > 0 && remote_lds_bytes(s) > 160 * 1024) return MDR_ERR_UNSUPPORTED;
+  if (s.R > 0 && ne > 0 && (remote_lds_bytes(s) > 160 * 1024 || pair_scatter_lds_bytes(s) > 160 * 1024))
+    return MDR_ERR_UNSUPPORTED;
   if (s.policy == MDR_OVERFLOW_REDIRECT && ((long long)s.A + 2 * ne) * 4 > 160 * 1024) return MDR_ERR_UNSUPPORTED;
   *out = s;
   return MDR_OK;
@@ -106,11 +112,13 @@ size_t layout(const Shape& s, char* base, Buffers* b, mdr_workspace_parts* parts
   t.sel = (int32_t*)take(BH * s.S * s.R * 4);
   t.ncand = (int32_t*)take(BH * s.S * 4);
   group = &pt.pair_lists;
-  t.cellcnt = (int32_t*)take(BH * (size_t)s.cells_per_bh * 4);
-  t.bins = (int32_t*)take(BH * (size_t)s.cells_per_bh * (s.blk + kCellDense) * 4);
+  t.phist = (int32_t*)take(BH * s.ng * s.ne * 4);
+  t.poff = (int32_t*)take(BH * (s.ne + 1) * 4);
+  t.plist = (int32_t*)take(BH * s.S * s.R * 4);
+  t.items = (int2*)take(BH * (size_t)s.max_items * 8);
   group = &pt.partials;
   t.part_o = take(BH * s.S * s.R * s.D * e);
-  t.part_ml = (float*)take(BH * s.S * s.R * 8);
+  t.part_lse = (float*)take(BH * s.S * s.R * 4);
   group = &pt.backward;
   t.dvec = (float*)take(BH * s.S * 4);
   if (s.policy == MDR_OVERFLOW_REDIRECT) {
@@ -237,7 +245,7 @@ mdr_status run_core(const Shape& s, const void* q, const void* k, const void* v,
   MDR_TRY(mark_event(ev, 0, st));
   const bool redirect = s.policy == MDR_OVERFLOW_REDIRECT;
   if (!have_address)
-    MDR_TRY(launch_address(s, k, cb, bias, b.ksum, b.addr, remote ? b.cellcnt : nullptr, st, 0, -1,
+    MDR_TRY(launch_address(s, k, cb, bias, b.ksum, b.addr, remote ? b.phist : nullptr, st, 0, -1,
                            redirect ? b.alt : nullptr));
   MDR_TRY(mark_event(ev, 1, st));
   // the posting lists are built inside the probe kernel where a specialised probe exists (the post
@@ -249,8 +257,10 @@ mdr_status run_core(const Shape& s, const void* q, const void* k, const void* v,
   const FusedPost fp{b.addr, b.off, b.idx, b.overflow};
   const ProbeExtra ex{redirect ? b.roff : nullptr, b.ridx, b.rtime, b.ndrop};
   MDR_TRY(launch_probe_rerank(s, q, cb, bias, b.ksum, b.off, b.idx, force, b.sel, b.ncand,
-                              remote ? b.cellcnt : nullptr, remote ? b.bins : nullptr, st, fused ? &fp : nullptr, ex));
-  MDR_TRY(launch_attend(s, q, k, v, b.sel, out, b, st, ev ? ev + 3 : nullptr));
+                              remote ? b.phist : nullptr, st, fused ? &fp : nullptr, ex));
+  MDR_TRY(mark_event(ev, 3, st));
+  MDR_TRY(launch_pair_scatter(s, b.sel, b.phist, b.poff, b.plist, b.items, st));
+  MDR_TRY(launch_attend(s, q, k, v, b.sel, out, b, st, ev ? ev + 4 : nullptr));
   MDR_TRY(mark_event(ev, MDR_CORE_KERNELS, st));
   return MDR_OK;
 }
@@ -408,7 +418,7 @@ mdr_status mdr_mixer_forward(const mdr_config* cfg, const void* x, const void* w
   if (fused) {
     const bool remote = s.R > 0 && s.ne > 0;
     MDR_TRY(launch_qkv_fused(s, x, wq, wk, wv, b.mq, b.mk, b.mv, codebook, code_bias, b.ksum, b.addr,
-                             s.policy == MDR_OVERFLOW_REDIRECT ? b.alt : nullptr, remote ? b.cellcnt : nullptr,
+                             s.policy == MDR_OVERFLOW_REDIRECT ? b.alt : nullptr, remote ? b.phist : nullptr,
                              b.mwt, hs));
   } else {
     MDR_TRY(launch_project_heads(s, x, wq, b.mq, true, hs));
@@ -461,7 +471,7 @@ mdr_status mdr_stage_probe_rerank(const mdr_config* cfg, const void* q, const fl
   if (redirect && (!redir_off || !redir_idx || !redir_time)) return MDR_ERR_INVALID_ARG;
   const ProbeExtra ex{redirect ? redir_off : nullptr, redir_idx, redir_time, n_drop};
   return hip_status(launch_probe_rerank(s, q, codebook, code_bias, ksum, post_off, post_idx, force, sel, n_cand,
-                                        nullptr, nullptr, (hipStream_t)stream, nullptr, ex));
+                                        nullptr, (hipStream_t)stream, nullptr, ex));
 }
 
 mdr_status mdr_stage_attend_lse(const mdr_config* cfg, const void* q, const void* k, const void* v,
@@ -479,8 +489,9 @@ mdr_status mdr_stage_attend_lse(const mdr_config* cfg, const void* q, const void
   b.lse = lse;
   hipStream_t hs = (hipStream_t)stream;
   if (s.R > 0 && s.ne > 0) {
-    MDR_TRY(launch_fill(b.cellcnt, (long long)s.B * s.H * s.cells_per_bh, 0, hs));
-    MDR_TRY(launch_pair_bin(s, sel, b.cellcnt, b.bins, hs));
+    MDR_TRY(launch_fill(b.phist, (long long)s.B * s.H * s.ng * s.ne, 0, hs));
+    MDR_TRY(launch_pair_count(s, sel, b.phist, hs));
+    MDR_TRY(launch_pair_scatter(s, sel, b.phist, b.poff, b.plist, b.items, hs));
   }
   MDR_TRY(launch_attend(s, q, k, v, sel, out, b, hs));
   return MDR_OK;
@@ -508,8 +519,9 @@ static mdr_status backward_core(const mdr_config* cfg, const void* q, const void
   hipStream_t hs = (hipStream_t)stream;
   MDR_TRY(mark_event(ev, 0, hs));
   if (s.R > 0 && s.ne > 0) {
-    MDR_TRY(launch_fill(b.cellcnt, (long long)s.B * s.H * s.cells_per_bh, 0, hs));
-    MDR_TRY(launch_pair_bin_ordered(s, sel, b.cellcnt, b.bins, hs));
+    MDR_TRY(launch_fill(b.phist, (long long)s.B * s.H * s.ng * s.ne, 0, hs));
+    MDR_TRY(launch_pair_count(s, sel, b.phist, hs));
+    MDR_TRY(launch_pair_scatter(s, sel, b.phist, b.poff, b.plist, b.items, hs));
   }
   MDR_TRY(launch_attend_backward(s, q, k, v, sel, out, lse, d_out, dq, dk, dv, b, hs, ev ? ev + 1 : nullptr));
   MDR_TRY(mark_event(ev, MDR_BACKWARD_KERNELS, hs));

@@ -10,14 +10,13 @@
 // Routing is per query token, so the remote blocks of neighbouring tokens differ.  Reading
 // each token's remote blocks separately would move every block many times, so the remote part
 // is regrouped by block:
-//   pairs          each selected (token, slot) pair is appended to the cell (remote block i, query
-//                  block j) -- by the probe kernel, or by k_pair_bin when a selection is passed in;
-//                  only the work-group owning query block j writes a cell, so no counter is hot
-//   k_attn_remote  one work-group per selected block (split when blocks are heavy): the block's
-//                  K/V is staged in LDS once, its pair ids go to an LDS list during the cell scan,
-//                  its pairs are walked 128 at a time (16 per wave), the pairs' queries are
-//                  gathered, S^T = K Q^T and O^T = V^T P^T run on MFMA, and each pair's softmax
-//                  partial (max, sum, normalised output) is stored
+//   pairs          the selected (token, slot) pairs are binned by remote block (mdr_pairs.hip): each
+//                  block's list in ascending token order, cut into work items of kItemPairs pairs
+//   k_attn_remote  one work-group per work item: the block's K/V is staged in LDS, the item's pairs
+//                  go 16 per wave, their queries are gathered, S^T = K Q^T and O^T = V^T P^T run on
+//                  MFMA, and each pair's softmax partial (normalised output, log2 normaliser) is
+//                  stored at [token][slot].  The items of one (b,h) run on one XCD when the heads
+//                  divide evenly, so that head's query rows and partials share that XCD's L2
 //   k_attn_local   one work-group per query block: the L local blocks through LDS on MFMA with
 //                  the causal mask on the diagonal block and an online softmax, then the
 //                  remote partials of each token are merged in slot order and O is written.
@@ -45,160 +44,81 @@ __global__ __launch_bounds__(256) void k_fill(int32_t* p, long long n, int32_t v
   for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long long)gridDim.x * 256) p[i] = value;
 }
 
-__global__ __launch_bounds__(256) void k_pair_bin(const int32_t* __restrict__ sel, int32_t* __restrict__ cellcnt,
-                                                  int32_t* __restrict__ bins, Shape s) {
-  const int t = blockIdx.x * 256 + threadIdx.x;
-  const int bh = blockIdx.y;
-  if (t >= s.S) return;
-  const int j = t / s.blk;
-  const int32_t* row = sel + ((size_t)bh * s.S + t) * s.R;
-  for (int r = 0; r < s.R; ++r)
-    if (sel_entry_valid(row, r, j, s.L)) record_pair(cellcnt, bins, s, bh, row[r], j, t, r);
-}
-
-// One work-group per (remote block i, split): the pairs of block i are the concatenation of its
-// cells (i, j), j = i + L .. nb - 1.  The work-group scans the cell counts into LDS, stages the
-// block's K/V in LDS once, and walks its pairs kRemoteWaves * 16 at a time (iteration c goes to
-// split c % splits): each wave gathers 16 pairs' queries, S^T = K Q^T and O^T = V^T P^T run on
-// MFMA, and every pair's softmax partial is stored at [token][slot].  The next iteration's pair
-// ids and query rows are loaded before the current one is computed.
-//
-// Each cell's dense slots are read together with its count, so the first pair ids of every cell
-// are known when the scan ends: they are written to an LDS pair list in pair order and a pair's id
-// is then one LDS read.  Pairs past a cell's dense slots, or past the list's capacity, take the
-// other route (the cell by binary search over the prefix, then the id from the cell's row).
-constexpr int kRemoteWaves = 8;
-
-// Capacity of the remote kernel's LDS pair list: what is left of the LDS once the work-groups
-// that the K/V tile and the cell prefix allow (at most four: 32 waves per CU) have their share,
-// at most 2048 and a multiple of 64.  Host and device compute it from the same values.
-__host__ __device__ inline int remote_pair_cap(size_t kv_bytes, int ne) {
-  const size_t lim = 159 * 1024;  // 160 KiB less a margin for the static scratch
-  const size_t base = kv_bytes + (size_t)(ne + 1) * 4;
-  if (base >= lim) return 0;
-  size_t nwg = lim / base;
-  if (nwg > 4) nwg = 4;
-  size_t cap = (lim / nwg - base) / 4;
-  if (cap > 2048) cap = 2048;
-  return (int)(cap & ~(size_t)63);
-}
+// One work-group per remote work item: kItemPairs pairs (or fewer) of one block's pair list, 16 per
+// wave.  The item, then the block's K/V and the pairs' ids, then the pairs' query rows: three dependent
+// reads ahead of the products.
+constexpr int kRemoteWaves = kItemPairs / 16;
 
 template <typename T, int D, int BLK>
 __global__ __launch_bounds__(kRemoteWaves * 64) void k_attn_remote(const T* __restrict__ Q, const T* __restrict__ K,
                                                                    const T* __restrict__ V,
-                                                                   const int32_t* __restrict__ cellcnt,
-                                                                   const int32_t* __restrict__ bins,
-                                                                   T* __restrict__ part_o, float* __restrict__ part_ml,
+                                                                   const int32_t* __restrict__ plist,
+                                                                   const int2* __restrict__ items,
+                                                                   T* __restrict__ part_o, float* __restrict__ part_lse,
                                                                    Shape s) {
   using TL = Tile<T, D, BLK>;
   constexpr int NTHR = kRemoteWaves * 64;
-  constexpr int PER_IT = kRemoteWaves * 16;
   extern __shared__ __align__(16) char lds_raw[];
   T* Ks = (T*)lds_raw;
   T* Vx = Ks + TL::K_ELEMS;
-  int* pre = (int*)(Vx + TL::V_ELEMS);  // [ne + 1] exclusive prefix of the cell counts
-  int* plist = pre + s.ne + 1;           // [pcap] pair ids in pair order (-2: read from the cell row)
-  const int pcap = remote_pair_cap(TL::LDS_BYTES, s.ne);
-  __shared__ int scan_tmp[kRemoteWaves];
-  const int i = blockIdx.x, bh = blockIdx.y;
+  // work item k of (b,h); pinned: work-group ids cycle over the XCDs, so (b,h) = id % 8 + 8 (...) keeps
+  // every item of one (b,h) on one XCD
+  const int id = blockIdx.x;
+  int bh, k;
+  if (s.pin) {
+    const int m = id / kXcds;
+    bh = id % kXcds + kXcds * (m / s.max_items);
+    k = m % s.max_items;
+  } else {
+    bh = id / s.max_items;
+    k = id % s.max_items;
+  }
+  if (bh >= s.B * s.H) return;
+  const int2 it = items[(size_t)bh * s.max_items + k];
+  if (it.x < 0) return;  // past the last item (uniform for the work-group)
+  const int i = it.x & 0xffff, n = it.x >> 16;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int ncell = s.ne - i;
-  const long long row0 = (long long)bh * s.cells_per_bh + cell_row(i, s.ne);
   const size_t rowbase = (size_t)bh * s.S;
-  // the block's K/V is requested before the cell counts are scanned
   KVRegs<T, D, BLK, NTHR> kv;
   kv.load(K + (rowbase + (size_t)i * BLK) * D, V + (rowbase + (size_t)i * BLK) * D, tid);
-  int run = 0;
-  for (int c0 = 0; c0 < ncell; c0 += NTHR) {
-    const int c = c0 + tid;
-    int v = 0;
-    int4 dense = make_int4(-1, -1, -1, -1);
-    if (c < ncell) {  // the count and the dense slots in one round trip
-      v = cellcnt[row0 + c];
-      dense = *(const int4*)(bins + (row0 + c) * kCellDense);
-      v = min(v, BLK);
-    }
-    int tot;
-    const int ex = block_exclusive_scan<NTHR>(v, scan_tmp, &tot);
-    if (c < ncell) {
-      const int b0 = run + ex;
-      pre[c] = b0;
-      const int n = min(v, pcap - b0);  // entries of this cell that fall inside the list
-      for (int p = 0; p < n; ++p)
-        plist[b0 + p] = p == 0 ? dense.x : p == 1 ? dense.y : p == 2 ? dense.z : p == 3 ? dense.w : -2;
-    }
-    run += tot;
-  }
-  if (tid == 0) pre[ncell] = run;
-  const int total = run;
-  const int nit = (total + PER_IT - 1) / PER_IT;
-  if ((int)blockIdx.z >= nit) return;  // uniform for the work-group
+  const int e = wave * 16 + (lane & 15);
+  int pid = e < n ? plist[rowbase * s.R + it.y + e] : -1;
+  if ((unsigned)pid >= (unsigned)(s.S * s.R)) pid = -1;  // only ids of this (b,h) are ever gathered
+  QFrag<T, D> qf;
+  load_q<T, D>(qf, Q + (rowbase + (pid < 0 ? 0 : pid / s.R)) * D, lane);
   kv.store(Ks, Vx, tid);
   __syncthreads();
+  if (wave * 16 >= n) return;  // no pairs for this wave (no barriers below)
+  // softmax in base 2 with the scale folded in: p = 2^(c s - c max s), c = scale * log2(e) > 0
   const float c = s.scale * kLog2e;
-  // pair id of this lane's slot in iteration it (-1 when past the end)
-  auto pair_at = [&](int it) __attribute__((always_inline)) -> int {
-    const int pidx = it * PER_IT + wave * 16 + (lane & 15);
-    if (pidx >= total) return -1;
-    if (pidx < pcap) {
-      const int p = plist[pidx];
-      if (p != -2) return p;
+  f32x4 p[TL::NT];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int nn = 0; nn < TL::NT; ++nn) {
+    p[nn] = score_tile<T, D, BLK>(qf, Ks, nn, lane);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) mx = fmaxf(mx, p[nn][kk]);
+  }
+  mx = c * wave_max16(mx);
+  float sum = 0.f;
+#pragma unroll
+  for (int nn = 0; nn < TL::NT; ++nn)
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      p[nn][kk] = fast_exp2(fmaf(p[nn][kk], c, -mx));
+      sum += p[nn][kk];
     }
-    int lo = 0, hi = ncell - 1;  // the cell whose range holds pidx
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (pre[mid] <= pidx)
-        lo = mid;
-      else
-        hi = mid - 1;
-    }
-    return cell_pair(bins, s, row0 + lo, pidx - pre[lo]);
-  };
-  int it = blockIdx.z;
-  if (it * PER_IT + wave * 16 >= total) return;  // this wave has no pairs at all (no barriers below)
-  // software pipeline over this wave's iterations: the next pair id is requested before the current
-  // tile is scored and its query row right after, so neither read waits on the other's round trip
-  int cur = pair_at(it);
-  QFrag<T, D> qf;
-  load_q<T, D>(qf, Q + (rowbase + (cur < 0 ? 0 : cur / s.R)) * D, lane);
-  for (; it < nit; it += gridDim.z) {
-    const int nx = it + (int)gridDim.z;
-    const bool more = nx < nit && nx * PER_IT + wave * 16 < total;  // uniform per wave
-    const int nxt = more ? pair_at(nx) : -1;
-    // softmax in base 2 with the scale folded in: p = 2^(c s - c max s), c = scale * log2(e) > 0
-    f32x4 p[TL::NT];
-    float mx = -INFINITY;
+  sum = wave_sum16(sum);
+  f32x4 o[TL::ND];
 #pragma unroll
-    for (int n = 0; n < TL::NT; ++n) {
-      p[n] = score_tile<T, D, BLK>(qf, Ks, n, lane);
+  for (int dt = 0; dt < TL::ND; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  pv_block<T, D, BLK>(o, p, Vx, lane);
+  if (pid >= 0) {
+    const size_t pr = rowbase * s.R + pid;  // the pair (token, slot)
+    const float inv = 1.f / sum;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) mx = fmaxf(mx, p[n][k]);
-    }
-    mx = c * wave_max16(mx);
-    float sum = 0.f;
-#pragma unroll
-    for (int n = 0; n < TL::NT; ++n)
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        p[n][k] = fast_exp2(fmaf(p[n][k], c, -mx));
-        sum += p[n][k];
-      }
-    sum = wave_sum16(sum);
-    f32x4 o[TL::ND];
-#pragma unroll
-    for (int dt = 0; dt < TL::ND; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    pv_block<T, D, BLK>(o, p, Vx, lane);
-    if (more) load_q<T, D>(qf, Q + (rowbase + (nxt < 0 ? 0 : nxt / s.R)) * D, lane);
-    if (cur >= 0) {
-      const int t = cur / s.R, r = cur % s.R;
-      const size_t pr = (rowbase + t) * s.R + r;
-      const float inv = 1.f / sum;
-#pragma unroll
-      for (int dt = 0; dt < TL::ND; ++dt) store4<T>(part_o + pr * D + 16 * dt + 4 * (lane >> 4), o[dt], inv);
-      if ((lane >> 4) == 0) *(float2*)(part_ml + 2 * pr) = make_float2(mx, sum);
-    }
-    if (!more) break;
-    cur = nxt;
+    for (int dt = 0; dt < TL::ND; ++dt) store4<T>(part_o + pr * D + 16 * dt + 4 * (lane >> 4), o[dt], inv);
+    if ((lane >> 4) == 0) part_lse[pr] = mx + log2f(sum);
   }
 }
 
@@ -215,7 +135,7 @@ constexpr int local_min_waves(int bytes, int D) { return bytes == 2 && D <= 64 ?
 template <typename T, int D, int BLK, int RS>
 __global__ __launch_bounds__(BLK * 4) __attribute__((amdgpu_waves_per_eu(local_min_waves((int)sizeof(T), D)))) void k_attn_local(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, const int32_t* __restrict__ sel,
-    const T* __restrict__ part_o, const float* __restrict__ part_ml, T* __restrict__ out,
+    const T* __restrict__ part_o, const float* __restrict__ part_lse, T* __restrict__ out,
     float* __restrict__ lse, Shape s) {
   using TL = Tile<T, D, BLK>;
   constexpr int NTHR = BLK * 4;
@@ -240,13 +160,13 @@ __global__ __launch_bounds__(BLK * 4) __attribute__((amdgpu_waves_per_eu(local_m
   const int32_t* row = sel + (rowbase + t) * s.R;
   constexpr int RA = RS > 0 ? RS : 1;
   int sr[RA];
-  float2 pml[RA];
+  float plse[RA];
   Raw4<T> praw[RA][TL::ND];
 #pragma unroll
   for (int r = 0; r < RS; ++r) {
     const size_t pr = (rowbase + t) * s.R + r;
     sr[r] = row[r];
-    pml[r] = *(const float2*)(part_ml + 2 * pr);
+    plse[r] = part_lse[pr];
 #pragma unroll
     for (int dt = 0; dt < TL::ND; ++dt) praw[r][dt] = *(const Raw4<T>*)(part_o + pr * D + 16 * dt + c4);
   }
@@ -305,11 +225,12 @@ __global__ __launch_bounds__(BLK * 4) __attribute__((amdgpu_waves_per_eu(local_m
     block_step(std::true_type{}, j);
   }
   // merge the remote partials in slot order: entry r counts when 0 <= sel <= j - L and it does not
-  // repeat an earlier entry of the row
-  auto merge = [&](float2 ml, const Raw4<T> (&po)[TL::ND]) __attribute__((always_inline)) {
-    const float mnew = fmaxf(m, ml.x);
+  // repeat an earlier entry of the row.  A partial with normalised output o_r and log2 normaliser
+  // lse_r carries the weight 2^lse_r.
+  auto merge = [&](float lr, const Raw4<T> (&po)[TL::ND]) __attribute__((always_inline)) {
+    const float mnew = fmaxf(m, lr);
     const float a = fast_exp2(m - mnew);
-    const float b = fast_exp2(ml.x - mnew) * ml.y;
+    const float b = fast_exp2(lr - mnew);
 #pragma unroll
     for (int dt = 0; dt < TL::ND; ++dt) o[dt] = o[dt] * a + unpack4<T>(po[dt]) * b;
     l = l * a + b;
@@ -320,7 +241,7 @@ __global__ __launch_bounds__(BLK * 4) __attribute__((amdgpu_waves_per_eu(local_m
     bool ok = sr[r] >= 0 && sr[r] <= j - s.L;
 #pragma unroll
     for (int p = 0; p < r; ++p) ok = ok && sr[p] != sr[r];
-    if (ok) merge(pml[r], praw[r]);
+    if (ok) merge(plse[r], praw[r]);
   }
   for (int r = RS; r < s.R; ++r) {
     if (!sel_entry_valid(row, r, j, s.L)) continue;
@@ -328,7 +249,7 @@ __global__ __launch_bounds__(BLK * 4) __attribute__((amdgpu_waves_per_eu(local_m
     Raw4<T> po[TL::ND];
 #pragma unroll
     for (int dt = 0; dt < TL::ND; ++dt) po[dt] = *(const Raw4<T>*)(part_o + pr * D + 16 * dt + c4);
-    merge(*(const float2*)(part_ml + 2 * pr), po);
+    merge(part_lse[pr], po);
   }
   const float inv = 1.f / l;
 #pragma unroll
@@ -345,7 +266,7 @@ hipError_t launch_local(const Shape& s, const void* q, const void* k, const void
                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)) != hipSuccess)
     return e;
   hipLaunchKernelGGL((k_attn_local<T, D, BLK, RS>), dim3(s.nb * s.B * s.H), dim3(BLK * 4), lds, st, (const T*)q,
-                     (const T*)k, (const T*)v, sel, (const T*)b.part_o, b.part_ml, (T*)out, b.lse, s);
+                     (const T*)k, (const T*)v, sel, (const T*)b.part_o, b.part_lse, (T*)out, b.lse, s);
   return hipGetLastError();
 }
 
@@ -360,9 +281,9 @@ hipError_t attend_impl(const Shape& s, const void* q, const void* k, const void*
     if (rl > 65536 && (e = hipFuncSetAttribute((const void*)k_attn_remote<T, D, BLK>,
                                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)rl)) != hipSuccess)
       return e;
-    hipLaunchKernelGGL((k_attn_remote<T, D, BLK>), dim3(s.ne, s.B * s.H, s.split), dim3(kRemoteWaves * 64), rl, st,
-                       (const T*)q,
-                       (const T*)k, (const T*)v, b.cellcnt, b.bins, (T*)b.part_o, b.part_ml, s);
+    const long long bh_pad = s.pin ? ((long long)s.B * s.H + kXcds - 1) / kXcds * kXcds : (long long)s.B * s.H;
+    hipLaunchKernelGGL((k_attn_remote<T, D, BLK>), dim3((unsigned)(bh_pad * s.max_items)), dim3(kRemoteWaves * 64),
+                       rl, st, (const T*)q, (const T*)k, (const T*)v, b.plist, b.items, (T*)b.part_o, b.part_lse, s);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if ((e = mark_event(ev, 1, st)) != hipSuccess) return e;
@@ -421,14 +342,8 @@ hipError_t launch_fill(int32_t* p, long long n, int32_t value, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_pair_bin(const Shape& s, const int32_t* sel, int32_t* cellcnt, int32_t* bins, hipStream_t st) {
-  hipLaunchKernelGGL(k_pair_bin, dim3((s.S + 255) / 256, s.B * s.H), dim3(256), 0, st, sel, cellcnt, bins, s);
-  return hipGetLastError();
-}
-
 size_t remote_lds_bytes(const Shape& s) {
-  const size_t kv = s.dtype == MDR_BF16 ? remote_lds_t<bf16>(s) : remote_lds_t<float>(s);
-  return kv + (size_t)(s.ne + 1) * 4 + (size_t)remote_pair_cap(kv, s.ne) * 4;
+  return s.dtype == MDR_BF16 ? remote_lds_t<bf16>(s) : remote_lds_t<float>(s);
 }
 
 hipError_t launch_attend(const Shape& s, const void* q, const void* k, const void* v, const int32_t* sel, void* out,

@@ -9,7 +9,8 @@
 //   k_bwd_dot  D_t for every token.
 //   k_bwd_kv   one work-group per key block i, one wave per 16 of its keys: the entries that read
 //              block i -- the tokens of the local query blocks i .. i + L - 1 (causal on block i)
-//              and the remote (token, slot) pairs of its cells -- are taken 64 (or fewer) at a time
+//              and the remote (token, slot) pairs of its pair list (mdr_pairs.hip: ascending token
+//              order, so every sum adds its terms in one fixed order) -- are taken 64 (or fewer) at a time
 //              through a pipeline (pair lookup, row reads, products on three chunks at once); each
 //              wave recomputes S = Q K^T and dP = dO V^T for its keys with the entries as rows,
 //              then accumulates dV^T += dO^T P and dK^T += Q^T dS on MFMA (the score layout is
@@ -47,73 +48,15 @@ __global__ __launch_bounds__(256) void k_bwd_dot(const T* __restrict__ O, const 
   if (t < n && l == 0) Dv[t] = a;
 }
 
-// Pairs binned into cells in a fixed order (ascending token within each cell), so that the
-// gradient sums below always add the same terms in the same order.  One work-group per query block
-// j, one thread per token: each eligible block the token selects gets the token's bit in a BLK-bit
-// mask in LDS (atomic OR, so the result does not depend on timing), and the token's place in the
-// cell (i, j) is the number of set bits below its own.  Cells left empty keep the count zero from
-// the fill that precedes this kernel.
-template <int BLK>
-__global__ __launch_bounds__(BLK) void k_pair_bin_ordered(const int32_t* __restrict__ sel,
-                                                          int32_t* __restrict__ cellcnt, int32_t* __restrict__ bins,
-                                                          Shape s) {
-  constexpr int NWORD = BLK / 32;
-  extern __shared__ uint32_t masks[];  // [ne][NWORD]: the tokens of this query block selecting block i
-  const int j = blockIdx.x, bh = blockIdx.y;
-  if (j < s.L) return;  // no eligible block for the whole query block
-  const int tid = threadIdx.x;
-  const int t = j * BLK + tid;
-  const int32_t* row = sel + ((size_t)bh * s.S + t) * s.R;
-  uint32_t used = 0;  // bit r: entry r counts (eligible, first of a repeat)
-  for (int r = 0; r < s.R; ++r)
-    if (sel_entry_valid(row, r, j, s.L)) used |= 1u << r;
-  for (int r = 0; r < s.R; ++r)
-    if (used >> r & 1)
-      for (int w = 0; w < NWORD; ++w) masks[row[r] * NWORD + w] = 0;
-  __syncthreads();
-  for (int r = 0; r < s.R; ++r)
-    if (used >> r & 1) atomicOr(&masks[row[r] * NWORD + tid / 32], 1u << (tid % 32));
-  __syncthreads();
-  for (int r = 0; r < s.R; ++r) {
-    if (!(used >> r & 1)) continue;
-    const int i = row[r];
-    const uint32_t* m = masks + i * NWORD;
-    int pos = 0, tot = 0;
-    for (int w = 0; w < NWORD; ++w) {
-      const int c = __popc(m[w]);
-      tot += c;
-      if (w < tid / 32) pos += c;
-    }
-    pos += __popc(m[tid / 32] & ((1u << (tid % 32)) - 1u));
-    const long long cell = (long long)bh * s.cells_per_bh + cell_row(i, s.ne) + (j - i - s.L);
-    *cell_slot(bins, s, cell, pos) = t * s.R + r;
-    if (pos == 0) cellcnt[cell] = tot;
-  }
-}
-
-template <int BLK>
-hipError_t pair_bin_ordered(const Shape& s, const int32_t* sel, int32_t* cellcnt, int32_t* bins, hipStream_t st) {
-  const size_t lds = (size_t)s.ne * (BLK / 32) * 4;
-  hipError_t e;
-  if (lds > 65536 && (e = hipFuncSetAttribute((const void*)k_pair_bin_ordered<BLK>,
-                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)) != hipSuccess)
-    return e;
-  hipLaunchKernelGGL(k_pair_bin_ordered<BLK>, dim3(s.nb, s.B * s.H), dim3(BLK), lds, st, sel, cellcnt, bins, s);
-  return hipGetLastError();
-}
-
-// Sizes of the key-block kernel: the entries of a block (local tokens, then the pairs of its cells
-// in cell order) are taken EC at a time -- 64, or fewer where that would not fit the 160 KiB of
-// LDS; the cell counts are scanned SEGC = NTHR * CPT cells at a time.
+// Sizes of the key-block kernel: the entries of a block (local tokens, then its pair list) are taken
+// EC at a time -- 64, or fewer where that would not fit the 160 KiB of LDS.
 template <typename T, int D, int BLK>
 struct KvCfg {
   using TL = Tile<T, D, BLK>;
   static constexpr int NTHR = BLK * 4;
   static constexpr int NW = BLK / 16;  // one wave per 16 keys
-  static constexpr int CPT = 4;
-  static constexpr int SEGC = NTHR * CPT;
   static constexpr size_t lds(int ec) {
-    return (size_t)(2 * BLK + 2 * ec) * TL::KST * sizeof(T) + (size_t)2 * ec * 16 + (size_t)SEGC * 4;
+    return (size_t)(2 * BLK + 2 * ec) * TL::KST * sizeof(T) + (size_t)2 * ec * 16;
   }
   static constexpr size_t LIM = 160 * 1024 - 256;
   static constexpr int EC = lds(64) <= LIM ? 64 : lds(32) <= LIM ? 32 : 16;
@@ -122,8 +65,8 @@ struct KvCfg {
 };
 
 // The entries flow through a three-stage pipeline, one chunk of EC per stage and iteration:
-//   A  resolve: entry -> token (local) or pair id (remote: a binary search over the cell prefix, then
-//      the pair's slot in its cell), in registers of threads tid < EC;
+//   A  resolve: entry -> token (local) or pair id (remote: the entry's slot of the block's pair list),
+//      in registers of threads tid < EC;
 //   B  gather: the chunk's query and output-gradient rows, normaliser and row dot, in registers;
 //   C  products on the rows staged in LDS.
 // While chunk k is in C, chunk k+1's reads (B) and chunk k+2's pair lookups (A) are in flight.
@@ -135,12 +78,12 @@ template <typename T, int D, int BLK>
 __global__ __launch_bounds__(BLK * 4) __attribute__((amdgpu_waves_per_eu(kv_min_waves((int)sizeof(T), D, BLK)))) void k_bwd_kv(const T* __restrict__ Q, const T* __restrict__ K,
                                                     const T* __restrict__ V, const T* __restrict__ dO,
                                                     const float* __restrict__ lse, const float* __restrict__ Dv,
-                                                    const int32_t* __restrict__ cellcnt,
-                                                    const int32_t* __restrict__ bins, T* __restrict__ dq_part,
+                                                    const int32_t* __restrict__ poff,
+                                                    const int32_t* __restrict__ plist, T* __restrict__ dq_part,
                                                     T* __restrict__ dK, T* __restrict__ dV, Shape s) {
   using C = KvCfg<T, D, BLK>;
   using TL = Tile<T, D, BLK>;
-  constexpr int EC = C::EC, SUB = C::SUB, NTHR = C::NTHR, NW = C::NW, CPT = C::CPT, SEGC = C::SEGC;
+  constexpr int EC = C::EC, SUB = C::SUB, NTHR = C::NTHR, NW = C::NW;
   static_assert(!TL::bf || SUB == 32, "bf16 products take the entries 32 at a time");
   static_assert(EC <= NTHR, "one resolving thread per entry of a chunk");
   constexpr int NCH = D / TL::VEC;                      // 16-byte pieces per row
@@ -154,8 +97,6 @@ __global__ __launch_bounds__(BLK * 4) __attribute__((amdgpu_waves_per_eu(kv_min_
   int* mpair = mtok + 2 * EC;              // [2][EC] pair id t R + r (-1: local entry)
   float* mlse = (float*)(mpair + 2 * EC);  // [2][EC] log2 normaliser of the token
   float* mdd = mlse + 2 * EC;              // [2][EC] D = dO . O of the token
-  int* pre = (int*)(mdd + 2 * EC);         // [SEGC] exclusive prefix of the cell counts of a segment
-  __shared__ int scan_tmp[NW];
   // block-major order: early blocks, which later tokens select most, start first
   const int bhn = s.B * s.H;
   const int i = blockIdx.x / bhn, bh = blockIdx.x % bhn;
@@ -163,9 +104,13 @@ __global__ __launch_bounds__(BLK * 4) __attribute__((amdgpu_waves_per_eu(kv_min_
   const int s4 = lane >> 4, r16 = lane & 15;
   const size_t rowbase = (size_t)bh * s.S;
   const int nl = (min(i + s.L, s.nb) - i) * BLK;
-  const int ncell = (s.R > 0 && i < s.ne) ? s.ne - i : 0;
-  const long long row0 = (long long)bh * s.cells_per_bh + (ncell > 0 ? cell_row(i, s.ne) : 0);
-  const int nseg = ncell > 0 ? (ncell + SEGC - 1) / SEGC : 1;
+  int p0 = 0, npair = 0;  // this block's pair list: plist[p0 .. p0 + npair)
+  if (s.R > 0 && i < s.ne) {
+    const int32_t* po = poff + (size_t)bh * (s.ne + 1) + i;
+    p0 = po[0];
+    npair = po[1] - p0;
+  }
+  const int32_t* pl = plist + rowbase * s.R + p0;
   {
     KVRegs<T, D, BLK, NTHR> kv;
     kv.load(K + (rowbase + (size_t)i * BLK) * D, V + (rowbase + (size_t)i * BLK) * D, tid);
@@ -181,28 +126,10 @@ __global__ __launch_bounds__(BLK * 4) __attribute__((amdgpu_waves_per_eu(kv_min_
   f32x4 dk[TL::ND], dv[TL::ND];
 #pragma unroll
   for (int dt = 0; dt < TL::ND; ++dt) dk[dt] = dv[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int seg = 0; seg < nseg; ++seg) {
-    // ---- cell counts of the segment (thread tid: cells tid CPT .. tid CPT + CPT - 1) and their prefix
-    const int cb = seg * SEGC;
-    const int nc = min(SEGC, ncell - cb);  // <= 0 when the block has no cells
-    int cnt[CPT], run = 0;
-#pragma unroll
-    for (int u = 0; u < CPT; ++u) {
-      const int cc = tid * CPT + u;
-      cnt[u] = cc < nc ? min(cellcnt[row0 + cb + cc], BLK) : 0;
-      run += cnt[u];
-    }
-    int tot;
-    int ex = block_exclusive_scan<NTHR>(run, scan_tmp, &tot);
-#pragma unroll
-    for (int u = 0; u < CPT; ++u) {
-      pre[tid * CPT + u] = ex;
-      ex += cnt[u];
-    }
-    const int nloc = seg == 0 ? nl : 0;
-    const int ntot = nloc + tot;
+  {
+    const int nloc = nl;
+    const int ntot = nloc + npair;
     const int nch = (ntot + EC - 1) / EC;
-    __syncthreads();
     // ---- pipeline registers
     int aT = -1, aP = -1;  // stage A of thread tid < EC: local token, or pair id (aT = -2)
     u32x4 qr[RPT], gr[RPT];
@@ -215,17 +142,9 @@ __global__ __launch_bounds__(BLK * 4) __attribute__((amdgpu_waves_per_eu(kv_min_
         if (e < nloc) {
           aT = i * BLK + e;
         } else {
-          const int er = e - nloc;
-          int lo = 0, hi = nc - 1;  // the last cell whose range starts at or before er
-          while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (pre[mid] <= er)
-              lo = mid;
-            else
-              hi = mid - 1;
-          }
-          aP = cell_pair(bins, s, row0 + cb + lo, er - pre[lo]);
-          aT = -2;
+          aP = pl[e - nloc];
+          if ((unsigned)aP >= (unsigned)(s.S * s.R)) aP = -1;  // only ids of this (b,h) are ever gathered
+          aT = aP < 0 ? -1 : -2;
         }
       }
     };
@@ -437,7 +356,7 @@ hipError_t bwd_impl(const Shape& s, const void* q, const void* k, const void* v,
   if ((e = mark_event(ev, 1, st)) != hipSuccess) return e;
   const unsigned nwg = (unsigned)((long long)s.nb * s.B * s.H);
   hipLaunchKernelGGL((k_bwd_kv<T, D, BLK>), dim3(nwg), dim3(BLK * 4), kl, st, (const T*)q,
-                     (const T*)k, (const T*)v, (const T*)d_o, lse, b.dvec, b.cellcnt, b.bins, (T*)b.part_o,
+                     (const T*)k, (const T*)v, (const T*)d_o, lse, b.dvec, b.poff, b.plist, (T*)b.part_o,
                      (T*)dk, (T*)dv, s);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const size_t ql = Tile<T, D, BLK>::LDS_BYTES;
@@ -475,16 +394,6 @@ hipError_t bwd_d(const Shape& s, const void* q, const void* k, const void* v, co
 }
 
 }  // namespace
-
-hipError_t launch_pair_bin_ordered(const Shape& s, const int32_t* sel, int32_t* cellcnt, int32_t* bins,
-                                   hipStream_t st) {
-  switch (s.blk) {
-    case 32: return pair_bin_ordered<32>(s, sel, cellcnt, bins, st);
-    case 64: return pair_bin_ordered<64>(s, sel, cellcnt, bins, st);
-    case 128: return pair_bin_ordered<128>(s, sel, cellcnt, bins, st);
-    default: return hipErrorInvalidValue;
-  }
-}
 
 hipError_t launch_attend_backward(const Shape& s, const void* q, const void* k, const void* v, const int32_t* sel,
                                   const void* out, const float* lse, const void* d_out, void* dq, void* dk, void* dv,

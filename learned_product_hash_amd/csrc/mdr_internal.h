@@ -15,7 +15,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
-constexpr int kPairsPerChunk = 64;  // (query, slot) pairs one remote work-group handles
+constexpr int kItemPairs = 128;     // (token, slot) pairs of one remote work item: 8 waves of 16
+constexpr int kMaxBinRanges = 16;   // token ranges per (b,h) of the pair binning
 constexpr int kMaxProbes = 16;
 constexpr int kMaxRemote = 16;
 constexpr int kMaxSubspaces = 4;
@@ -29,8 +30,10 @@ struct Shape {
   float scale;      // softmax scale (1/sqrt(D) unless given)
   float rope_base;  // mixer only
   int ne;           // blocks that some query block can see: nb - L (or 0)
-  long long cells_per_bh;  // (remote block i, query block j) cells with j >= i + L: ne (ne + 1) / 2
-  int split;        // remote work-groups per block
+  int ng;           // token ranges of the pair binning per (b,h): tokens [g tbin, (g + 1) tbin)
+  int tbin;         // tokens per range, a multiple of 256 (every probe work-group lies in one range)
+  int max_items;    // remote work items per (b,h), an upper bound: ne + ceil(S R / kItemPairs)
+  int pin;          // remote work of (b,h) runs on XCD bh % 8 (when B H is a multiple of 8)
   int csr_lds;      // probe stage stages the posting-list CSR in LDS
   int fixed_probe;  // probe stage uses its compile-time specialisation for these sizes
   int policy;       // mdr_overflow_policy
@@ -48,11 +51,12 @@ struct Buffers {
   int32_t* overflow;
   int32_t* sel;
   int32_t* ncand;
-  int32_t* cellcnt;    // [B,H,cells] pairs per (remote block i, query block j) cell
-  int32_t* bins;       // (t*R + r) of the pairs of each cell: a dense [B,H,cells,kCellDense] table of
-                       // the first slots, then [B,H,cells,blk] rows (see cell_slot)
+  int32_t* phist;      // [B,H,ng,ne] pairs of token range g that selected block i
+  int32_t* poff;       // [B,H,ne+1] the pair lists of the blocks: block i's at plist[poff[i], poff[i+1])
+  int32_t* plist;      // [B,H,S*R] pair ids t*R + r, grouped by remote block, ascending within a block
+  int2* items;         // [B,H,max_items] remote work items: {block | pairs << 16, first pair}, -1 past the end
   void* part_o;        // [B,H,S,R,D] remote partial outputs (normalised), io dtype
-  float* part_ml;      // [B,H,S,R,2] remote partial (max in log2 units, sum)
+  float* part_lse;     // [B,H,S,R] remote partial: log2 of its softmax normaliser (scaled exponent units)
   void* mq;            // mixer: Q, K, V, O in [B,H,S,D]
   void* mk;
   void* mv;
@@ -90,13 +94,6 @@ struct DecState {
 constexpr int kDecMaxKeys = 4096;  // (R + L) * block keys per decoded token
 constexpr int kDecMaxCand = 1024;  // candidates per decoded token
 
-// The cells of remote block i are (i, j) for j = i + L .. nb - 1, stored contiguously; a cell
-// holds the pairs of query block j that selected block i (at most blk of them).
-__host__ __device__ inline long long cell_row(int i, int ne) {
-  const long long ii = i;
-  return ii * ne - ii * (ii - 1) / 2;
-}
-
 // Selection entry r of a token in query block j is used iff it is an eligible block
 // (0 <= i <= j - L) not repeated by an earlier entry of the same token.
 __device__ inline bool sel_entry_valid(const int32_t* row, int r, int j, int L) {
@@ -107,28 +104,44 @@ __device__ inline bool sel_entry_valid(const int32_t* row, int r, int j, int L) 
   return true;
 }
 
-// Where slot pos of a cell's pair list lives.  Cells hold 1.3 pairs on average and a row of a
-// block's cells is read front to back, so the first kCellDense slots of every cell sit in a dense
-// table ([cells][kCellDense], consecutive cells on shared cache lines) at the start of the bins
-// region; slots kCellDense .. blk - 1 sit in full-width rows ([cells][blk]) after it.
-constexpr int kCellDense = 4;
-__host__ __device__ inline long long cells_total(const Shape& s) { return (long long)s.B * s.H * s.cells_per_bh; }
-__device__ inline int32_t* cell_slot(int32_t* bins, const Shape& s, long long cell, int pos) {
-  return pos < kCellDense ? bins + cell * kCellDense + pos
-                          : bins + cells_total(s) * kCellDense + cell * s.blk + pos;
-}
-__device__ inline int32_t cell_pair(const int32_t* __restrict__ bins, const Shape& s, long long cell, int pos) {
-  return pos < kCellDense ? bins[cell * kCellDense + pos] : bins[cells_total(s) * kCellDense + cell * s.blk + pos];
+// Pair binning.  The counters phist are cleared column by column: the work-group that summarises block
+// i clears entry i of every token range of its (b,h).
+__device__ inline void clear_pair_counts(int32_t* phist, const Shape& s, int bh, int i, int tid, int nthreads) {
+  if (i >= s.ne) return;
+  int32_t* col = phist + (size_t)bh * s.ng * s.ne + i;
+  for (int g = tid; g < s.ng; g += nthreads) col[(size_t)g * s.ne] = 0;
 }
 
-// Append pair (t, r) of query block j to the cell (i, j).  Only the work-group that owns query
-// block j touches the cell, so its counter sees at most blk atomic adds.
-__device__ inline void record_pair(int32_t* cellcnt, int32_t* bins, const Shape& s, int bh, int i, int j, int t,
-                                   int r) {
-  const long long cell = (long long)bh * s.cells_per_bh + cell_row(i, s.ne) + (j - i - s.L);
-  const int pos = atomicAdd(&cellcnt[cell], 1);
-  if (pos < s.blk) *cell_slot(bins, s, cell, pos) = t * s.R + r;
-}
+// Adds the pairs a work-group of NT threads selected to the counters of its token range: each thread
+// passes its pairs' blocks to add(); an LDS histogram (cnt, ne ints, or nullptr when the blocks do not
+// fit: then every pair is one device-scope atomic) collects them, then each non-empty block is one
+// device-scope atomic add.  Every thread of the work-group must call begin() and end().
+template <int NT>
+struct PairCounter {
+  int* cnt;
+  int32_t* dst;  // phist row of this (b,h, range)
+  int ne;
+  __device__ void begin() {  // cnt may alias LDS the work-group used before: every such use is done first
+    __syncthreads();
+    if (cnt)
+      for (int i = threadIdx.x; i < ne; i += NT) cnt[i] = 0;
+    __syncthreads();
+  }
+  __device__ void add(int i) {
+    if (cnt)
+      atomicAdd(&cnt[i], 1);
+    else
+      atomicAdd(&dst[i], 1);
+  }
+  __device__ void end() {
+    __syncthreads();
+    if (cnt)
+      for (int i = threadIdx.x; i < ne; i += NT) {
+        const int c = cnt[i];
+        if (c) atomicAdd(&dst[i], c);
+      }
+  }
+};
 
 // Work-groups are handed to the 8 XCDs of the chip in turn (linear id mod 8), and each XCD has its
 // own L2.  xcd_chunked(id, n) renumbers the n work-groups of a 1-D grid so that each XCD receives a
@@ -183,12 +196,12 @@ inline hipError_t mark_event(hipEvent_t* ev, int i, hipStream_t st) {
 }
 
 // Launchers (return hipGetLastError()).
-// cell_zero (optional): the address kernel of block i clears the cell counters of row i.
+// pair_zero (optional): the address kernel of block i clears column i of the pair counters.
 // Blocks [i0, i0 + n) (n < 0: to the end).
 // alt (optional): also the alternate address of each block (runner-up code of its lowest-margin
 // subspace).
 hipError_t launch_address(const Shape& s, const void* k, const float* codebook, const float* bias,
-                          float* ksum, int32_t* addr, int32_t* cell_zero, hipStream_t st, int i0 = 0, int n = -1,
+                          float* ksum, int32_t* addr, int32_t* pair_zero, hipStream_t st, int i0 = 0, int n = -1,
                           int32_t* alt = nullptr);
 hipError_t launch_post(const Shape& s, const int32_t* addr, int32_t* off, int32_t* idx,
                        int32_t* overflow, hipStream_t st);
@@ -200,10 +213,11 @@ struct FusedPost {
   int32_t* idx;
   int32_t* overflow;
 };
+// phist (optional): the selected pairs are counted per (token range, remote block) for the binning.
 hipError_t launch_probe_rerank(const Shape& s, const void* q, const float* codebook, const float* bias,
                                const float* ksum, const int32_t* off, const int32_t* idx,
-                               const int32_t* force, int32_t* sel, int32_t* ncand, int32_t* cellcnt,
-                               int32_t* bins, hipStream_t st, const FusedPost* fuse = nullptr,
+                               const int32_t* force, int32_t* sel, int32_t* ncand, int32_t* phist,
+                               hipStream_t st, const FusedPost* fuse = nullptr,
                                const ProbeExtra& ex = ProbeExtra{nullptr, nullptr, nullptr, nullptr});
 // Redirect lists from the posting CSR and the alternates; overwrites overflow with the blocks no
 // final view returns.
@@ -224,20 +238,22 @@ hipError_t launch_decode_attend(const Shape& s, const void* q_new, const void* k
                                 hipStream_t st);
 bool probe_fixed_shape(const Shape& s);
 hipError_t launch_fill(int32_t* p, long long n, int32_t value, hipStream_t st);
-hipError_t launch_pair_bin(const Shape& s, const int32_t* sel, int32_t* cellcnt, int32_t* bins,
-                           hipStream_t st);
+// Pair binning of a selection: launch_pair_count adds its pairs to the counters (which must be zero:
+// launch_fill, or the address kernel's clearing); launch_pair_scatter turns the counts into the
+// per-block lists (poff, plist: stable, ascending token within a block) and the remote work items.
+hipError_t launch_pair_count(const Shape& s, const int32_t* sel, int32_t* phist, hipStream_t st);
+hipError_t launch_pair_scatter(const Shape& s, const int32_t* sel, const int32_t* phist, int32_t* poff,
+                               int32_t* plist, int2* items, hipStream_t st);
+size_t pair_scatter_lds_bytes(const Shape& s);
 size_t remote_lds_bytes(const Shape& s);
-// ev (optional, 2 entries): recorded before attn_remote and attn_local.
+// The attention of a selection whose pairs are binned (poff / plist / items).  ev (optional, 2 entries):
+// recorded before attn_remote and attn_local.
 hipError_t launch_attend(const Shape& s, const void* q, const void* k, const void* v,
                          const int32_t* sel, void* out, const Buffers& b, hipStream_t st,
                          hipEvent_t* ev = nullptr);
-// The selection's pairs binned into cells in ascending token order within each cell (the cell
-// counters must be zero before the call).
-hipError_t launch_pair_bin_ordered(const Shape& s, const int32_t* sel, int32_t* cellcnt, int32_t* bins,
-                                   hipStream_t st);
-// Backward of the attention under a fixed selection (cellcnt / bins must hold the selection's
-// pairs; part_o receives the remote dQ shares, dvec the row dots).  ev (optional, 3 entries):
-// recorded before the row-dot, key-block and query-block kernels.
+// Backward of the attention under a fixed selection (poff / plist must hold the selection's pairs;
+// part_o receives the remote dQ shares, dvec the row dots).  ev (optional, 3 entries): recorded before
+// the row-dot, key-block and query-block kernels.
 hipError_t launch_attend_backward(const Shape& s, const void* q, const void* k, const void* v, const int32_t* sel,
                                   const void* out, const float* lse, const void* d_out, void* dq, void* dk, void* dv,
                                   const Buffers& b, hipStream_t st, hipEvent_t* ev = nullptr);
@@ -248,10 +264,10 @@ hipError_t launch_project_heads(const Shape& s, const void* x, const void* w, vo
 hipError_t launch_project_out(const Shape& s, const void* o, const void* wo, void* delta, void* wt,
                               hipStream_t st);
 // Q, K, V projections with RoPE, block summaries and addresses (and alternates when alt is given)
-// fused into one launch; cell_zero (optional) as for launch_address.  Only when qkv_fuses_address.
+// fused into one launch; pair_zero (optional) as for launch_address.  Only when qkv_fuses_address.
 bool qkv_fuses_address(const Shape& s);
 hipError_t launch_qkv_fused(const Shape& s, const void* x, const void* wq, const void* wk, const void* wv, void* q,
                             void* k, void* v, const float* cb, const float* bias, float* ksum, int32_t* addr,
-                            int32_t* alt, int32_t* cell_zero, void* wt, hipStream_t st);
+                            int32_t* alt, int32_t* pair_zero, void* wt, hipStream_t st);
 
 }  // namespace mdr

@@ -139,7 +139,7 @@ struct QkvEpilogue {
   float* ksum;
   int32_t* addr;
   int32_t* alt;
-  int32_t* cell_zero;
+  int32_t* pair_zero;
 };
 
 // One direct global-to-LDS load of 16 bytes per lane: lane l's bytes land at lds + 16 l (lds uniform
@@ -434,10 +434,7 @@ __global__ __launch_bounds__(256) void k_mm(const T* __restrict__ A, const T* __
               kbar[tid] = mval;
               ep.ksum[((size_t)bh * s.nb + i) * D + tid] = mval;
             }
-            if (ep.cell_zero && i < s.ne) {
-              int32_t* crow = ep.cell_zero + (size_t)bh * s.cells_per_bh + cell_row(i, s.ne);
-              for (int c = tid; c < s.ne - i; c += 256) crow[c] = 0;
-            }
+            if (ep.pair_zero) clear_pair_counts(ep.pair_zero, s, bh, i, tid, 256);
             __syncthreads();
             address_from_summary<D>(cs, kbar, logit, ep.addr + (size_t)bh * s.nb + i,
                                     ep.alt ? ep.alt + (size_t)bh * s.nb + i : nullptr, s);
@@ -582,9 +579,9 @@ bool qkv_fuses_address(const Shape& s) { return s.blk <= 64 && s.W % 8 == 0 && m
 
 hipError_t launch_qkv_fused(const Shape& s, const void* x, const void* wq, const void* wk, const void* wv, void* q,
                             void* k, void* v, const float* cb, const float* bias, float* ksum, int32_t* addr,
-                            int32_t* alt, int32_t* cell_zero, void* wt, hipStream_t st) {
+                            int32_t* alt, int32_t* pair_zero, void* wt, hipStream_t st) {
   if (!qkv_fuses_address(s)) return hipErrorInvalidValue;
-  const QkvEpilogue ep{cb, bias, ksum, addr, alt, cell_zero};
+  const QkvEpilogue ep{cb, bias, ksum, addr, alt, pair_zero};
   if (s.dtype == MDR_BF16) return qkv_fused<bf16>(s, x, wq, wk, wv, q, k, v, ep, wt, st);
   return qkv_fused<float>(s, x, wq, wk, wv, q, k, v, ep, wt, st);
 }

@@ -4,7 +4,8 @@
 //   k_probe_rerank   per query token: probe scores, top-P addresses, candidate views,
 //                    rerank against the block summaries, top-R selection (+ forced target)
 //   k_probe_fixed    the same with the routing sizes fixed at compile time; it also builds the
-//                    posting lists in LDS and files the selected pairs into their cells
+//                    posting lists in LDS
+// Both count the selected pairs per (token range, remote block) for the binning of the attention.
 //
 // The method (remio.ai, "Monodratic claims learned routing can make sparse causal attention
 // more selective", section "Monodratic turns sparse attention into a retrieval decision";
@@ -27,19 +28,16 @@ namespace {
 // ---------------------------------------------------------------------------------------------
 // Block key summaries and product addresses: one work-group of 256 threads per (b,h, block); the
 // arithmetic is block_address() (mdr_address.h), shared with the decode path.  The work-group of
-// block i also clears the cell counters of row i when asked.
+// block i also clears column i of the pair counters when asked.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void k_address(const T* __restrict__ K, const float* __restrict__ cb,
                                                  const float* __restrict__ bias, float* __restrict__ ksum,
-                                                 int32_t* __restrict__ addr, int32_t* __restrict__ cell_zero,
+                                                 int32_t* __restrict__ addr, int32_t* __restrict__ pair_zero,
                                                  int32_t* __restrict__ alt, int i0, Shape s) {
   __shared__ AddressLds<T, D> sm;
   const int i = i0 + blockIdx.x;
   const int bh = blockIdx.y;
-  if (cell_zero && i < s.ne) {
-    int32_t* row = cell_zero + (size_t)bh * s.cells_per_bh + cell_row(i, s.ne);
-    for (int c = threadIdx.x; c < s.ne - i; c += 256) row[c] = 0;
-  }
+  if (pair_zero) clear_pair_counts(pair_zero, s, bh, i, threadIdx.x, 256);
   block_address<T, D>(K, cb, bias, ksum, addr, i, bh, sm, s, alt);
 }
 
@@ -245,13 +243,14 @@ __global__ __launch_bounds__(256) void k_post_redirect(const int32_t* __restrict
 //   candidates= for each probe in rank order, the newest `capacity` CSR entries <= j - L,
 //               newest first, until M candidates
 //   selection = top-R candidates by <q_t, summary_i>, ties to the smaller block
-// Optionally each selected (token, slot) pair is appended to the cell (block, query block).
+// Optionally the selected (token, slot) pairs are counted per (token range, remote block) for the
+// binning of the attention.
 template <typename T, int D>
 __global__ __launch_bounds__(kProbeThreads) void k_probe_rerank(
     const T* __restrict__ Q, const float* __restrict__ cb, const float* __restrict__ bias,
     const float* __restrict__ ksum, const int32_t* __restrict__ off, const int32_t* __restrict__ idx,
     const int32_t* __restrict__ force, int32_t* __restrict__ sel, int32_t* __restrict__ ncand,
-    int32_t* __restrict__ cellcnt, int32_t* __restrict__ bins, ProbeExtra ex, Shape s) {
+    int32_t* __restrict__ phist, ProbeExtra ex, Shape s) {
   constexpr int NT = kProbeThreads;
   extern __shared__ __align__(16) float smem[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -333,7 +332,9 @@ __global__ __launch_bounds__(kProbeThreads) void k_probe_rerank(
     }
   }
   __syncthreads();
-  if (t >= s.S) return;  // no barriers below
+  const bool active = t < s.S;
+  int nr = 0;
+  if (active) {  // no barriers inside
   const int j = t / s.blk;
   const int cutoff = j - s.L;
   const float* mrow = mu + tid * MST;
@@ -410,7 +411,7 @@ __global__ __launch_bounds__(kProbeThreads) void k_probe_rerank(
   // primaries, then, under the redirect policy, the newest arrivals of its redirect list while slots
   // remain), cut at M; rerank by <q_t, summary>.  Dropped candidates: per probe, the eligible
   // blocks the list holds beyond its capacity.
-  int nc = 0, nr = 0, ndr = 0;
+  int nc = 0, ndr = 0;
   if (cutoff >= 0) {
     float qv[D];
     if (R > 0) {
@@ -515,8 +516,15 @@ __global__ __launch_bounds__(kProbeThreads) void k_probe_rerank(
   for (int r = 0; r < R; ++r) srow[r] = r < nr ? tri[r * NT + tid] : -1;
   if (ncand) ncand[(size_t)bh * s.S + t] = nc;
   if (ex.ndrop) ex.ndrop[(size_t)bh * s.S + t] = ndr;
-  if (bins)
-    for (int r = 0; r < nr; ++r) record_pair(cellcnt, bins, s, bh, tri[r * NT + tid], j, t, r);
+  }  // active
+  if (!phist) return;  // uniform
+  // ---- count the selected pairs of this work-group's token range per remote block (LDS histogram in the
+  // place of mu when it fits)
+  PairCounter<NT> pc{s.ne <= NT * MST ? (int*)mu : nullptr, phist + ((size_t)bh * s.ng + tbase / s.tbin) * s.ne,
+                     s.ne};
+  pc.begin();
+  for (int r = 0; r < nr; ++r) pc.add(tri[r * NT + tid]);
+  pc.end();
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -779,7 +787,7 @@ __global__ __launch_bounds__(kProbeFixedThreads) __attribute__((amdgpu_waves_per
     const T* __restrict__ Q, const float* __restrict__ cb, const float* __restrict__ bias,
     const float* __restrict__ ksum, const int32_t* __restrict__ off, const int32_t* __restrict__ idx,
     const int32_t* __restrict__ force, int32_t* __restrict__ sel, int32_t* __restrict__ ncand,
-    int32_t* __restrict__ cellcnt, int32_t* __restrict__ bins, FusedPost fp, ProbeExtra ex, Shape s) {
+    int32_t* __restrict__ phist, FusedPost fp, ProbeExtra ex, Shape s) {
   constexpr int NT = kProbeFixedThreads;
   static_assert(NT % 64 == 0, "whole waves of 64 tokens");
   constexpr bool BF = std::is_same<T, bf16>::value;
@@ -1186,45 +1194,18 @@ __global__ __launch_bounds__(kProbeFixedThreads) __attribute__((amdgpu_waves_per
     if (ncand) ncand[(size_t)bh * s.S + t] = nc;
     if (ex.ndrop) ex.ndrop[(size_t)bh * s.S + t] = ndr;
   }
-  if (!bins) return;  // uniform
-  // ---- file each selected pair in its (remote block i, query block j) cell.  The work-group owns
-  // the cells of its query blocks, so when they fit (in the place of mu) it counts them in LDS, stores
-  // each pair at the slot that count gives, and then the thread that filed a cell's first pair writes
-  // the cell's count (the address kernel has cleared all of them); otherwise it appends with global
-  // atomics.
-  const int nqb = NT / s.blk;  // whole query blocks per work-group
-  if (nqb * s.ne <= NT * MST) {
-    int* cnt = (int*)mu;  // [nqb][ne]
-    lds_barrier();      // every rho / clist read is done
-    for (int c = tid; c < nqb * s.ne; c += NT) cnt[c] = 0;
-    lds_barrier();
-    const int jb = tbase / s.blk;
-    const long long cbase = (long long)bh * s.cells_per_bh + j - s.L;  // cell (i, j) = cbase + cell_row(i) - i
-    uint32_t first = 0;  // bit r: this token filed the first pair of slot r's cell
-    if (active) {
-#pragma unroll
-      for (int r = 0; r < RK; ++r) {
-        if (r < nr) {
-          const int i = tri[r];
-          const int pos = atomicAdd(&cnt[(j - jb) * s.ne + i], 1);
-          const long long cell = cbase + cell_row(i, s.ne) - i;
-          if (pos < s.blk) *cell_slot(bins, s, cell, pos) = t * s.R + r;
-          if (pos == 0) first |= 1u << r;
-        }
-      }
-    }
-    lds_barrier();
+  if (!phist) return;  // uniform
+  // ---- count the selected pairs of this work-group's token range per remote block (LDS histogram in the
+  // place of mu when it fits)
+  PairCounter<NT> pc{s.ne <= NT * MST ? (int*)mu : nullptr, phist + ((size_t)bh * s.ng + tbase / s.tbin) * s.ne,
+                     s.ne};
+  pc.begin();
+  if (active) {
 #pragma unroll
     for (int r = 0; r < RK; ++r)
-      if (first >> r & 1u) {
-        const int i = tri[r];
-        cellcnt[cbase + cell_row(i, s.ne) - i] = cnt[(j - jb) * s.ne + i];
-      }
-  } else if (active) {
-#pragma unroll
-    for (int r = 0; r < RK; ++r)
-      if (r < nr) record_pair(cellcnt, bins, s, bh, tri[r], j, t, r);
+      if (r < nr) pc.add(tri[r]);
   }
+  pc.end();
 }
 
 template <typename T>
@@ -1251,7 +1232,7 @@ hipError_t address_dispatch(const Shape& s, const void* k, const float* cb, cons
 template <typename T, int D, int G, int C, int P, int R, bool FUSED>
 hipError_t probe_fixed_launch_t(const Shape& s, const void* q, const float* cb, const float* bias, const float* ksum,
                                 const int32_t* off, const int32_t* idx, const int32_t* force, int32_t* sel,
-                                int32_t* ncand, int32_t* cellcnt, int32_t* bins, const FusedPost& fp,
+                                int32_t* ncand, int32_t* phist, const FusedPost& fp,
                                 const ProbeExtra& ex, hipStream_t st) {
   dim3 grid((s.S + kProbeFixedThreads - 1) / kProbeFixedThreads, s.B * s.H);
   const size_t lds = probe_lds_bytes(s);
@@ -1261,21 +1242,21 @@ hipError_t probe_fixed_launch_t(const Shape& s, const void* q, const float* cb, 
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL((k_probe_fixed<T, D, G, C, P, R, FUSED>), grid, dim3(kProbeFixedThreads), lds, st, (const T*)q, cb,
-                     bias, ksum, off, idx, force, sel, ncand, cellcnt, bins, fp, ex, s);
+                     bias, ksum, off, idx, force, sel, ncand, phist, fp, ex, s);
   return hipGetLastError();
 }
 
 template <typename T, int D, int G, int C, int P, int R>
 hipError_t probe_fixed_launch(const Shape& s, const void* q, const float* cb, const float* bias, const float* ksum,
                               const int32_t* off, const int32_t* idx, const int32_t* force, int32_t* sel,
-                              int32_t* ncand, int32_t* cellcnt, int32_t* bins, const FusedPost* fuse,
+                              int32_t* ncand, int32_t* phist, const FusedPost* fuse,
                               const ProbeExtra& ex, hipStream_t st) {
   if (fuse)
-    return probe_fixed_launch_t<T, D, G, C, P, R, true>(s, q, cb, bias, ksum, off, idx, force, sel, ncand, cellcnt,
-                                                         bins, *fuse, ex, st);
+    return probe_fixed_launch_t<T, D, G, C, P, R, true>(s, q, cb, bias, ksum, off, idx, force, sel, ncand, phist,
+                                                         *fuse, ex, st);
   const FusedPost none{nullptr, nullptr, nullptr, nullptr};
-  return probe_fixed_launch_t<T, D, G, C, P, R, false>(s, q, cb, bias, ksum, off, idx, force, sel, ncand, cellcnt,
-                                                        bins, none, ex, st);
+  return probe_fixed_launch_t<T, D, G, C, P, R, false>(s, q, cb, bias, ksum, off, idx, force, sel, ncand, phist,
+                                                        none, ex, st);
 }
 
 // Shapes with a compile-time specialisation (the five workload families); others use k_probe_rerank.
@@ -1289,12 +1270,12 @@ hipError_t probe_fixed_launch(const Shape& s, const void* q, const float* cb, co
 template <typename T>
 hipError_t probe_dispatch(const Shape& s, const void* q, const float* cb, const float* bias, const float* ksum,
                           const int32_t* off, const int32_t* idx, const int32_t* force, int32_t* sel,
-                          int32_t* ncand, int32_t* cellcnt, int32_t* bins, const FusedPost* fuse,
+                          int32_t* ncand, int32_t* phist, const FusedPost* fuse,
                           const ProbeExtra& ex, hipStream_t st) {
 #define MDR_FIXED(TT, DD, GG, CC, PP, RR)                                                                        \
   if (std::is_same<T, TT>::value && s.D == DD && s.G == GG && s.C == CC && s.P == PP && s.R == RR && s.fixed_probe) \
-    return probe_fixed_launch<TT, DD, GG, CC, PP, RR>(s, q, cb, bias, ksum, off, idx, force, sel, ncand, cellcnt, \
-                                                      bins, fuse, ex, st);
+    return probe_fixed_launch<TT, DD, GG, CC, PP, RR>(s, q, cb, bias, ksum, off, idx, force, sel, ncand, phist,  \
+                                                      fuse, ex, st);
   MDR_PROBE_FIXED_SHAPES(MDR_FIXED)
 #undef MDR_FIXED
   if (fuse) return hipErrorInvalidValue;  // only the specialised probe builds the lists itself
@@ -1314,15 +1295,15 @@ hipError_t probe_dispatch(const Shape& s, const void* q, const float* cb, const 
   switch (s.D) {
     case 32:
       hipLaunchKernelGGL((k_probe_rerank<T, 32>), grid, dim3(kProbeThreads), lds, st, (const T*)q, cb, bias, ksum,
-                         off, idx, force, sel, ncand, cellcnt, bins, ex, s);
+                         off, idx, force, sel, ncand, phist, ex, s);
       break;
     case 64:
       hipLaunchKernelGGL((k_probe_rerank<T, 64>), grid, dim3(kProbeThreads), lds, st, (const T*)q, cb, bias, ksum,
-                         off, idx, force, sel, ncand, cellcnt, bins, ex, s);
+                         off, idx, force, sel, ncand, phist, ex, s);
       break;
     default:
       hipLaunchKernelGGL((k_probe_rerank<T, 128>), grid, dim3(kProbeThreads), lds, st, (const T*)q, cb, bias,
-                         ksum, off, idx, force, sel, ncand, cellcnt, bins, ex, s);
+                         ksum, off, idx, force, sel, ncand, phist, ex, s);
       break;
   }
   return hipGetLastError();
@@ -1331,11 +1312,11 @@ hipError_t probe_dispatch(const Shape& s, const void* q, const float* cb, const 
 }  // namespace
 
 hipError_t launch_address(const Shape& s, const void* k, const float* codebook, const float* bias, float* ksum,
-                          int32_t* addr, int32_t* cell_zero, hipStream_t st, int i0, int n, int32_t* alt) {
+                          int32_t* addr, int32_t* pair_zero, hipStream_t st, int i0, int n, int32_t* alt) {
   if (n < 0) n = s.nb - i0;
   if (s.dtype == MDR_BF16)
-    return address_dispatch<bf16>(s, k, codebook, bias, ksum, addr, cell_zero, alt, i0, n, st);
-  return address_dispatch<float>(s, k, codebook, bias, ksum, addr, cell_zero, alt, i0, n, st);
+    return address_dispatch<bf16>(s, k, codebook, bias, ksum, addr, pair_zero, alt, i0, n, st);
+  return address_dispatch<float>(s, k, codebook, bias, ksum, addr, pair_zero, alt, i0, n, st);
 }
 
 bool probe_fixed_shape(const Shape& s) {
@@ -1370,12 +1351,12 @@ hipError_t launch_post(const Shape& s, const int32_t* addr, int32_t* off, int32_
 
 hipError_t launch_probe_rerank(const Shape& s, const void* q, const float* codebook, const float* bias,
                                const float* ksum, const int32_t* off, const int32_t* idx, const int32_t* force,
-                               int32_t* sel, int32_t* ncand, int32_t* cellcnt, int32_t* bins, hipStream_t st,
+                               int32_t* sel, int32_t* ncand, int32_t* phist, hipStream_t st,
                                const FusedPost* fuse, const ProbeExtra& ex) {
   if (fuse && ex.roff) return hipErrorInvalidValue;  // redirect lists need the whole CSR first
   if (s.dtype == MDR_BF16)
-    return probe_dispatch<bf16>(s, q, codebook, bias, ksum, off, idx, force, sel, ncand, cellcnt, bins, fuse, ex, st);
-  return probe_dispatch<float>(s, q, codebook, bias, ksum, off, idx, force, sel, ncand, cellcnt, bins, fuse, ex, st);
+    return probe_dispatch<bf16>(s, q, codebook, bias, ksum, off, idx, force, sel, ncand, phist, fuse, ex, st);
+  return probe_dispatch<float>(s, q, codebook, bias, ksum, off, idx, force, sel, ncand, phist, fuse, ex, st);
 }
 
 hipError_t launch_post_redirect(const Shape& s, const int32_t* addr, const int32_t* alt, const int32_t* off,

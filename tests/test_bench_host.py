@@ -42,7 +42,9 @@ def test_design_bytes_of_the_attention_kernels():
     ab = bench.design_bytes(w, st)
     qkv = 8 * 32768 * 64 * 2
     # the local kernel: Q, its K/V window and O once, the selection, and one partial per pair
-    assert ab["attn_local"] == 4 * qkv + 8 * 32768 * 2 * 4 + st["pairs"] * (64 * 2 + 8)
+    assert ab["attn_local"] == 4 * qkv + 8 * 32768 * 2 * 4 + st["pairs"] * (64 * 2 + 4)
+    # the binning: the selection, the per-range counts (16 ranges of 2048 tokens x 510 blocks), the lists
+    assert ab["attn_bin"] == 8 * 32768 * 2 * 4 + 8 * 16 * 510 * 4 + st["pairs"] * 4 + 8 * 511 * 4
     assert all(v > 0 for v in ab.values())
 
 
