@@ -114,8 +114,8 @@ size_t layout(const Shape& s, char* base, Buffers* b, mdr_workspace_parts* parts
   group = &pt.pair_lists;
   t.phist = (int32_t*)take(BH * s.ng * s.ne * 4);
   t.poff = (int32_t*)take(BH * (s.ne + 1) * 4);
-  t.plist = (int32_t*)take(BH * s.S * s.R * 4);
-  t.items = (int2*)take(BH * (size_t)s.max_items * 8);
+  t.ioff = (int32_t*)take(BH * (s.ne + 1) * 4);
+  t.items = (int32_t*)take(BH * (size_t)s.max_items * kItemInts * 4);
   group = &pt.partials;
   t.part_o = take(BH * s.S * s.R * s.D * e);
   t.part_lse = (float*)take(BH * s.S * s.R * 4);
@@ -259,7 +259,7 @@ mdr_status run_core(const Shape& s, const void* q, const void* k, const void* v,
   MDR_TRY(launch_probe_rerank(s, q, cb, bias, b.ksum, b.off, b.idx, force, b.sel, b.ncand,
                               remote ? b.phist : nullptr, st, fused ? &fp : nullptr, ex));
   MDR_TRY(mark_event(ev, 3, st));
-  MDR_TRY(launch_pair_scatter(s, b.sel, b.phist, b.poff, b.plist, b.items, st));
+  MDR_TRY(launch_pair_scatter(s, b.sel, b.phist, b.poff, b.ioff, b.items, st));
   MDR_TRY(launch_attend(s, q, k, v, b.sel, out, b, st, ev ? ev + 4 : nullptr));
   MDR_TRY(mark_event(ev, MDR_CORE_KERNELS, st));
   return MDR_OK;
@@ -491,7 +491,7 @@ mdr_status mdr_stage_attend_lse(const mdr_config* cfg, const void* q, const void
   if (s.R > 0 && s.ne > 0) {
     MDR_TRY(launch_fill(b.phist, (long long)s.B * s.H * s.ng * s.ne, 0, hs));
     MDR_TRY(launch_pair_count(s, sel, b.phist, hs));
-    MDR_TRY(launch_pair_scatter(s, sel, b.phist, b.poff, b.plist, b.items, hs));
+    MDR_TRY(launch_pair_scatter(s, sel, b.phist, b.poff, b.ioff, b.items, hs));
   }
   MDR_TRY(launch_attend(s, q, k, v, sel, out, b, hs));
   return MDR_OK;
@@ -521,7 +521,7 @@ static mdr_status backward_core(const mdr_config* cfg, const void* q, const void
   if (s.R > 0 && s.ne > 0) {
     MDR_TRY(launch_fill(b.phist, (long long)s.B * s.H * s.ng * s.ne, 0, hs));
     MDR_TRY(launch_pair_count(s, sel, b.phist, hs));
-    MDR_TRY(launch_pair_scatter(s, sel, b.phist, b.poff, b.plist, b.items, hs));
+    MDR_TRY(launch_pair_scatter(s, sel, b.phist, b.poff, b.ioff, b.items, hs));
   }
   MDR_TRY(launch_attend_backward(s, q, k, v, sel, out, lse, d_out, dq, dk, dv, b, hs, ev ? ev + 1 : nullptr));
   MDR_TRY(mark_event(ev, MDR_BACKWARD_KERNELS, hs));

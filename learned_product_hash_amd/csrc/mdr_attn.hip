@@ -11,7 +11,7 @@
 // each token's remote blocks separately would move every block many times, so the remote part
 // is regrouped by block:
 //   pairs          the selected (token, slot) pairs are binned by remote block (mdr_pairs.hip): each
-//                  block's list in ascending token order, cut into work items of kItemPairs pairs
+//                  block's list in ascending token order, cut into work items of kItemPairs pair ids
 //   k_attn_remote  one work-group per work item: the block's K/V is staged in LDS, the item's pairs
 //                  go 16 per wave, their queries are gathered, S^T = K Q^T and O^T = V^T P^T run on
 //                  MFMA, and each pair's softmax partial (normalised output, log2 normaliser) is
@@ -45,15 +45,14 @@ __global__ __launch_bounds__(256) void k_fill(int32_t* p, long long n, int32_t v
 }
 
 // One work-group per remote work item: kItemPairs pairs (or fewer) of one block's pair list, 16 per
-// wave.  The item, then the block's K/V and the pairs' ids, then the pairs' query rows: three dependent
-// reads ahead of the products.
+// wave.  The item record (block and pair ids in one read), then the block's K/V and the pairs' query
+// rows: two dependent reads ahead of the products.
 constexpr int kRemoteWaves = kItemPairs / 16;
 
 template <typename T, int D, int BLK>
 __global__ __launch_bounds__(kRemoteWaves * 64) void k_attn_remote(const T* __restrict__ Q, const T* __restrict__ K,
                                                                    const T* __restrict__ V,
-                                                                   const int32_t* __restrict__ plist,
-                                                                   const int2* __restrict__ items,
+                                                                   const int32_t* __restrict__ items,
                                                                    T* __restrict__ part_o, float* __restrict__ part_lse,
                                                                    Shape s) {
   using TL = Tile<T, D, BLK>;
@@ -74,16 +73,17 @@ __global__ __launch_bounds__(kRemoteWaves * 64) void k_attn_remote(const T* __re
     k = id % s.max_items;
   }
   if (bh >= s.B * s.H) return;
-  const int2 it = items[(size_t)bh * s.max_items + k];
-  if (it.x < 0) return;  // past the last item (uniform for the work-group)
-  const int i = it.x & 0xffff, n = it.x >> 16;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int e = wave * 16 + (lane & 15);
+  const int32_t* rec = items + ((size_t)bh * s.max_items + k) * kItemInts;
+  const int hdr = rec[0];
+  int pid = rec[kItemHead + e];
+  if (hdr < 0) return;  // past the last item (uniform for the work-group)
+  const int i = hdr & 0xffff, n = hdr >> 16;
+  if (e >= n || (unsigned)pid >= (unsigned)(s.S * s.R)) pid = -1;  // only ids of this (b,h) are ever gathered
   const size_t rowbase = (size_t)bh * s.S;
   KVRegs<T, D, BLK, NTHR> kv;
   kv.load(K + (rowbase + (size_t)i * BLK) * D, V + (rowbase + (size_t)i * BLK) * D, tid);
-  const int e = wave * 16 + (lane & 15);
-  int pid = e < n ? plist[rowbase * s.R + it.y + e] : -1;
-  if ((unsigned)pid >= (unsigned)(s.S * s.R)) pid = -1;  // only ids of this (b,h) are ever gathered
   QFrag<T, D> qf;
   load_q<T, D>(qf, Q + (rowbase + (pid < 0 ? 0 : pid / s.R)) * D, lane);
   kv.store(Ks, Vx, tid);
@@ -283,7 +283,7 @@ hipError_t attend_impl(const Shape& s, const void* q, const void* k, const void*
       return e;
     const long long bh_pad = s.pin ? ((long long)s.B * s.H + kXcds - 1) / kXcds * kXcds : (long long)s.B * s.H;
     hipLaunchKernelGGL((k_attn_remote<T, D, BLK>), dim3((unsigned)(bh_pad * s.max_items)), dim3(kRemoteWaves * 64),
-                       rl, st, (const T*)q, (const T*)k, (const T*)v, b.plist, b.items, (T*)b.part_o, b.part_lse, s);
+                       rl, st, (const T*)q, (const T*)k, (const T*)v, b.items, (T*)b.part_o, b.part_lse, s);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if ((e = mark_event(ev, 1, st)) != hipSuccess) return e;

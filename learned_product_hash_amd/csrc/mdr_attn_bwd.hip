@@ -79,7 +79,8 @@ __global__ __launch_bounds__(BLK * 4) __attribute__((amdgpu_waves_per_eu(kv_min_
                                                     const T* __restrict__ V, const T* __restrict__ dO,
                                                     const float* __restrict__ lse, const float* __restrict__ Dv,
                                                     const int32_t* __restrict__ poff,
-                                                    const int32_t* __restrict__ plist, T* __restrict__ dq_part,
+                                                    const int32_t* __restrict__ ioff,
+                                                    const int32_t* __restrict__ items, T* __restrict__ dq_part,
                                                     T* __restrict__ dK, T* __restrict__ dV, Shape s) {
   using C = KvCfg<T, D, BLK>;
   using TL = Tile<T, D, BLK>;
@@ -104,13 +105,13 @@ __global__ __launch_bounds__(BLK * 4) __attribute__((amdgpu_waves_per_eu(kv_min_
   const int s4 = lane >> 4, r16 = lane & 15;
   const size_t rowbase = (size_t)bh * s.S;
   const int nl = (min(i + s.L, s.nb) - i) * BLK;
-  int p0 = 0, npair = 0;  // this block's pair list: plist[p0 .. p0 + npair)
+  int npair = 0, it0 = 0;  // this block's list: npair pairs in the work items from it0 on, in order
   if (s.R > 0 && i < s.ne) {
     const int32_t* po = poff + (size_t)bh * (s.ne + 1) + i;
-    p0 = po[0];
-    npair = po[1] - p0;
+    npair = po[1] - po[0];
+    it0 = ioff[(size_t)bh * (s.ne + 1) + i];
   }
-  const int32_t* pl = plist + rowbase * s.R + p0;
+  const int32_t* recs = items + ((size_t)bh * s.max_items + it0) * kItemInts;
   {
     KVRegs<T, D, BLK, NTHR> kv;
     kv.load(K + (rowbase + (size_t)i * BLK) * D, V + (rowbase + (size_t)i * BLK) * D, tid);
@@ -142,7 +143,8 @@ __global__ __launch_bounds__(BLK * 4) __attribute__((amdgpu_waves_per_eu(kv_min_
         if (e < nloc) {
           aT = i * BLK + e;
         } else {
-          aP = pl[e - nloc];
+          const int er = e - nloc;
+          aP = recs[(size_t)(er / kItemPairs) * kItemInts + kItemHead + er % kItemPairs];
           if ((unsigned)aP >= (unsigned)(s.S * s.R)) aP = -1;  // only ids of this (b,h) are ever gathered
           aT = aP < 0 ? -1 : -2;
         }
@@ -356,7 +358,7 @@ hipError_t bwd_impl(const Shape& s, const void* q, const void* k, const void* v,
   if ((e = mark_event(ev, 1, st)) != hipSuccess) return e;
   const unsigned nwg = (unsigned)((long long)s.nb * s.B * s.H);
   hipLaunchKernelGGL((k_bwd_kv<T, D, BLK>), dim3(nwg), dim3(BLK * 4), kl, st, (const T*)q,
-                     (const T*)k, (const T*)v, (const T*)d_o, lse, b.dvec, b.poff, b.plist, (T*)b.part_o,
+                     (const T*)k, (const T*)v, (const T*)d_o, lse, b.dvec, b.poff, b.ioff, b.items, (T*)b.part_o,
                      (T*)dk, (T*)dv, s);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const size_t ql = Tile<T, D, BLK>::LDS_BYTES;

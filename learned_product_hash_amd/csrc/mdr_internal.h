@@ -16,6 +16,10 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
 constexpr int kItemPairs = 128;     // (token, slot) pairs of one remote work item: 8 waves of 16
+// A remote work item is one record of kItemInts ints: [0] = block | (pairs << 16) (-1 past the last item),
+// [kItemHead + e] = the pair id t*R + r of its e-th pair, in list order (ascending token).
+constexpr int kItemHead = 4;
+constexpr int kItemInts = kItemHead + kItemPairs;
 constexpr int kMaxBinRanges = 16;   // token ranges per (b,h) of the pair binning
 constexpr int kMaxProbes = 16;
 constexpr int kMaxRemote = 16;
@@ -52,9 +56,9 @@ struct Buffers {
   int32_t* sel;
   int32_t* ncand;
   int32_t* phist;      // [B,H,ng,ne] pairs of token range g that selected block i
-  int32_t* poff;       // [B,H,ne+1] the pair lists of the blocks: block i's at plist[poff[i], poff[i+1])
-  int32_t* plist;      // [B,H,S*R] pair ids t*R + r, grouped by remote block, ascending within a block
-  int2* items;         // [B,H,max_items] remote work items: {block | pairs << 16, first pair}, -1 past the end
+  int32_t* poff;       // [B,H,ne+1] pairs selecting blocks < i (block i's list has poff[i+1] - poff[i] pairs)
+  int32_t* ioff;       // [B,H,ne+1] work items of blocks < i (block i's list is in items ioff[i] .. ioff[i+1])
+  int32_t* items;      // [B,H,max_items,kItemInts] remote work items: each block's pair list in pieces
   void* part_o;        // [B,H,S,R,D] remote partial outputs (normalised), io dtype
   float* part_lse;     // [B,H,S,R] remote partial: log2 of its softmax normaliser (scaled exponent units)
   void* mq;            // mixer: Q, K, V, O in [B,H,S,D]
@@ -240,18 +244,18 @@ bool probe_fixed_shape(const Shape& s);
 hipError_t launch_fill(int32_t* p, long long n, int32_t value, hipStream_t st);
 // Pair binning of a selection: launch_pair_count adds its pairs to the counters (which must be zero:
 // launch_fill, or the address kernel's clearing); launch_pair_scatter turns the counts into the
-// per-block lists (poff, plist: stable, ascending token within a block) and the remote work items.
+// per-block lists, cut into the remote work items (stable: ascending token within a block).
 hipError_t launch_pair_count(const Shape& s, const int32_t* sel, int32_t* phist, hipStream_t st);
 hipError_t launch_pair_scatter(const Shape& s, const int32_t* sel, const int32_t* phist, int32_t* poff,
-                               int32_t* plist, int2* items, hipStream_t st);
+                               int32_t* ioff, int32_t* items, hipStream_t st);
 size_t pair_scatter_lds_bytes(const Shape& s);
 size_t remote_lds_bytes(const Shape& s);
-// The attention of a selection whose pairs are binned (poff / plist / items).  ev (optional, 2 entries):
+// The attention of a selection whose pairs are binned (items).  ev (optional, 2 entries):
 // recorded before attn_remote and attn_local.
 hipError_t launch_attend(const Shape& s, const void* q, const void* k, const void* v,
                          const int32_t* sel, void* out, const Buffers& b, hipStream_t st,
                          hipEvent_t* ev = nullptr);
-// Backward of the attention under a fixed selection (poff / plist must hold the selection's pairs;
+// Backward of the attention under a fixed selection (poff / ioff / items must hold the selection's pairs;
 // part_o receives the remote dQ shares, dvec the row dots).  ev (optional, 3 entries): recorded before
 // the row-dot, key-block and query-block kernels.
 hipError_t launch_attend_backward(const Shape& s, const void* q, const void* k, const void* v, const int32_t* sel,

@@ -10,8 +10,8 @@
 //   scatter  k_pair_scatter, one work-group per (range, b,h): the totals over all ranges give each
 //            block's list offset (poff), the counts of the earlier ranges this range's first slot per
 //            block; its waves then file their pairs in ascending pair id (t R + r) with ballot ranks, so
-//            every list is in ascending token order whatever the timing.  The work-groups also write the
-//            remote work items: each block's list cut into pieces of kItemPairs pairs.
+//            every list is in ascending token order whatever the timing.  The lists are stored as the
+//            remote work items: each block's list cut into records of kItemPairs pair ids.
 #include "mdr_internal.h"
 
 namespace mdr {
@@ -24,10 +24,10 @@ constexpr int kBinThreads = 256;
 // LDS by all threads at once, then the waves that file pairs count and file them from LDS.  Those waves'
 // count and cursor rows share the LDS with two rows of per-block values and the staged blocks.
 constexpr int kScatterThreads = 1024;
-constexpr int kSubPairs = 8192;
-constexpr int kScatterLdsInts = 36 * 1024;  // 144 KiB
+constexpr int kSubPairs = 4096;
+constexpr int kScatterLdsInts = 37 * 1024;  // 148 KiB
 __host__ __device__ inline int scatter_waves(int ne) {
-  const int w = (kScatterLdsInts - kSubPairs) / ne - 2;
+  const int w = (kScatterLdsInts - kSubPairs) / ne - 3;
   return w > kScatterThreads / 64 ? kScatterThreads / 64 : w;
 }
 
@@ -50,8 +50,8 @@ __global__ __launch_bounds__(kBinThreads) void k_pair_count(const int32_t* __res
 
 __global__ __launch_bounds__(kScatterThreads) void k_pair_scatter(const int32_t* __restrict__ sel,
                                                               const int32_t* __restrict__ phist,
-                                                              int32_t* __restrict__ poff, int32_t* __restrict__ plist,
-                                                              int2* __restrict__ items, Shape s) {
+                                                              int32_t* __restrict__ poff, int32_t* __restrict__ ioff,
+                                                              int32_t* __restrict__ items, Shape s) {
   extern __shared__ int sm[];
   __shared__ int scan_tmp[kScatterThreads / 64];
   const int ne = s.ne, g = blockIdx.x, bh = blockIdx.y;
@@ -59,8 +59,24 @@ __global__ __launch_bounds__(kScatterThreads) void k_pair_scatter(const int32_t*
   const int nwf = scatter_waves(ne);
   int* base = sm;            // [ne] the next free slot per block of this range
   int* start = base + ne;    // [ne] pairs per block, then each block's list offset
-  int* wc = start + ne;      // [nwf][ne] per-wave counts, then per-wave cursors
+  int* istart = start + ne;  // [ne] each block's first work item
+  int* wc = istart + ne;     // [nwf][ne] per-wave counts, then per-wave cursors
   int* keys = wc + nwf * ne; // [kSubPairs] the blocks of the piece's pairs (-1: entry not used)
+  // this range's tokens, kSubPairs / R at a time (all of a token's pairs in one piece); the first piece's
+  // entries are requested before the counts, so the two reads overlap
+  const int tfirst = g * s.tbin, tlast = min(s.S, tfirst + s.tbin);
+  const int tps = kSubPairs / s.R;  // tokens per piece
+  const int32_t* selh = sel + (size_t)bh * s.S * s.R;
+  int v[kSubPairs / kScatterThreads];
+  auto load_piece = [&](int t0) __attribute__((always_inline)) {  // contiguous: pair p is selh[t0 R + p]
+    const int np = min(tps, tlast - t0) * s.R;
+#pragma unroll
+    for (int u = 0; u < kSubPairs / kScatterThreads; ++u) {
+      const int x = u * kScatterThreads + tid;
+      v[u] = x < np ? selh[(size_t)t0 * s.R + x] : -1;
+    }
+  };
+  load_piece(tfirst);
   const int32_t* ph = phist + (size_t)bh * s.ng * ne;
   for (int i = tid; i < ne; i += kScatterThreads) {
     int v[kMaxBinRanges];  // every range's count requested at once
@@ -88,40 +104,37 @@ __global__ __launch_bounds__(kScatterThreads) void k_pair_scatter(const int32_t*
   int run = block_exclusive_scan<kScatterThreads>(sum, scan_tmp, &total);
   int irun = block_exclusive_scan<kScatterThreads>(isum, scan_tmp, &itot);
   int32_t* po = poff + (size_t)bh * (ne + 1);
-  int2* it = items + (size_t)bh * s.max_items;
+  int32_t* io = ioff + (size_t)bh * (ne + 1);
+  int32_t* it = items + (size_t)bh * s.max_items * kItemInts;
   for (int a = a0; a < a1; ++a) {
     const int tot = start[a];
     const int ni = (tot + kItemPairs - 1) / kItemPairs;
-    if (g == 0) po[a] = run;
+    if (g == 0) {
+      po[a] = run;
+      io[a] = irun;
+    }
     if (a % s.ng == g)
-      for (int k = 0; k < ni; ++k)
-        it[irun + k] = make_int2(a | (min(kItemPairs, tot - k * kItemPairs) << 16), run + k * kItemPairs);
+      for (int k = 0; k < ni; ++k) it[(size_t)(irun + k) * kItemInts] = a | (min(kItemPairs, tot - k * kItemPairs) << 16);
+    istart[a] = irun;
     irun += ni;
     base[a] += run;
     start[a] = run;
     run += tot;
   }
-  if (g == 0 && tid == 0) po[ne] = total;
-  for (int k = itot + g * kScatterThreads + tid; k < s.max_items; k += kScatterThreads * s.ng) it[k] = make_int2(-1, 0);
-  // this range's tokens, kSubPairs / R at a time (all of a token's pairs in one piece); within a piece,
-  // pair p (pair id (t0 + p / R) R + p % R) goes to wave p / share
-  const int tfirst = g * s.tbin, tlast = min(s.S, tfirst + s.tbin);
-  const int tps = kSubPairs / s.R;  // tokens per piece
-  const int32_t* selh = sel + (size_t)bh * s.S * s.R;
-  int32_t* out = plist + (size_t)bh * s.S * s.R;
+  if (g == 0 && tid == 0) {
+    po[ne] = total;
+    io[ne] = itot;
+  }
+  for (int k = itot + g * kScatterThreads + tid; k < s.max_items; k += kScatterThreads * s.ng)
+    it[(size_t)k * kItemInts] = -1;
+  // within a piece, pair p (pair id (t0 + p / R) R + p % R) goes to wave p / share
   int nbits = 0;
   while ((1 << nbits) < ne) ++nbits;
   const unsigned long long lt = lane == 0 ? 0ull : (~0ull >> (64 - lane));
   for (int t0 = tfirst; t0 < tlast; t0 += tps) {
     const int nt = min(tps, tlast - t0), np = nt * s.R;
     const int share = ((np + nwf - 1) / nwf + 63) & ~63;
-    // the piece's entries, all requested at once (contiguous: pair p is selh[t0 R + p])
-    int v[kSubPairs / kScatterThreads];
-#pragma unroll
-    for (int u = 0; u < kSubPairs / kScatterThreads; ++u) {
-      const int x = u * kScatterThreads + tid;
-      v[u] = x < np ? selh[(size_t)t0 * s.R + x] : -1;
-    }
+    if (t0 != tfirst) load_piece(t0);  // the piece's entries, all requested at once
     __syncthreads();  // the previous piece is filed: its keys and the counts are free
 #pragma unroll
     for (int u = 0; u < kSubPairs / kScatterThreads; ++u) keys[u * kScatterThreads + tid] = v[u];
@@ -174,7 +187,10 @@ __global__ __launch_bounds__(kScatterThreads) void k_pair_scatter(const int32_t*
           const int rank = __popcll(same & lt);
           const int count = __popcll(same);
           const int cur = cw[i];
-          if ((unsigned)(cur + rank) < (unsigned)(s.S * s.R)) out[cur + rank] = t0 * s.R + p;
+          const int pos = cur + rank - start[i];  // the pair's place in block i's list
+          const int rec = istart[i] + pos / kItemPairs;
+          if (pos >= 0 && rec < s.max_items)
+            it[(size_t)rec * kItemInts + kItemHead + pos % kItemPairs] = t0 * s.R + p;
           __builtin_amdgcn_wave_barrier();
           if (rank == count - 1) cw[i] = cur + count;
         }
@@ -189,7 +205,7 @@ __global__ __launch_bounds__(kScatterThreads) void k_pair_scatter(const int32_t*
 size_t pair_scatter_lds_bytes(const Shape& s) {
   if (s.ne <= 0) return 0;
   if (scatter_waves(s.ne) < 1) return (size_t)1 << 30;  // never: ne <= 8192 leaves room for two waves
-  return ((size_t)(2 + scatter_waves(s.ne)) * s.ne + kSubPairs) * 4;
+  return ((size_t)(3 + scatter_waves(s.ne)) * s.ne + kSubPairs) * 4;
 }
 
 hipError_t launch_pair_count(const Shape& s, const int32_t* sel, int32_t* phist, hipStream_t st) {
@@ -200,7 +216,7 @@ hipError_t launch_pair_count(const Shape& s, const int32_t* sel, int32_t* phist,
 }
 
 hipError_t launch_pair_scatter(const Shape& s, const int32_t* sel, const int32_t* phist, int32_t* poff,
-                               int32_t* plist, int2* items, hipStream_t st) {
+                               int32_t* ioff, int32_t* items, hipStream_t st) {
   if (s.R <= 0 || s.ne <= 0) return hipSuccess;
   const size_t lds = pair_scatter_lds_bytes(s);
   if (lds > 65536) {
@@ -208,7 +224,7 @@ hipError_t launch_pair_scatter(const Shape& s, const int32_t* sel, const int32_t
                                        (int)lds);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(k_pair_scatter, dim3(s.ng, s.B * s.H), dim3(kScatterThreads), lds, st, sel, phist, poff, plist,
+  hipLaunchKernelGGL(k_pair_scatter, dim3(s.ng, s.B * s.H), dim3(kScatterThreads), lds, st, sel, phist, poff, ioff,
                      items, s);
   return hipGetLastError();
 }
