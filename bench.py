@@ -60,8 +60,8 @@ MIXER_SYMBOL = {  # every listed substring must occur in the (mangled) kernel na
     "output projection": ("k_mm", "Lb1ELb0E"),
     "weight transposes": ("k_transpose",),
 }
-BACKWARD_SYMBOL = {
-    "pair_bin": "k_pair_bin_ordered",
+BACKWARD_SYMBOL = {  # the backward's binning also runs k_pair_scatter, listed with the forward's kernels
+    "pair_bin (count)": "k_pair_count",
     "bwd_dot": "k_bwd_dot",
     "bwd_kv": "k_bwd_kv",
     "bwd_q": "k_bwd_q",
