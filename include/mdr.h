@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define MDR_ABI_VERSION 3
+#define MDR_ABI_VERSION 4
 
 typedef enum {
   MDR_OK = 0,
@@ -134,7 +134,23 @@ typedef struct {
  *   redir_off [B,H,A+1], redir_idx [B,H,nb], redir_time [B,H,nb]: per address
  *     the blocks redirected into it in arrival order, at
  *     redir_idx[redir_off[a] .. redir_off[a+1]), with redir_time the query
- *     block at which each arrives; entries past redir_off[A] are -1. */
+ *     block at which each arrives; entries past redir_off[A] are -1.
+ * Routing diagnostics (each written when non-NULL).  The pages ask for the
+ * selected remote blocks per query to be logged and checked against a dense
+ * selected-mask oracle (aitechinspire.com, "Practical notes for tinkerers");
+ * these outputs let a caller tell which decisions were close to a tie (all
+ * fp32, in the kernels' own summation order):
+ *   probes [B,H,S,P]: each token's probed addresses, best first
+ *   sel_score [B,H,S,R]: <q_t, summary_i> of each selected block (-inf for -1
+ *     padding, NaN for a forced block that was not among the candidates)
+ *   probe_margin [B,H,S]: the smallest gap between neighbouring address scores
+ *     among the min(P + 1, A) best (+inf with fewer than two)
+ *   sel_margin [B,H,S]: the smallest gap between neighbouring rerank scores
+ *     among the min(R + 1, candidates) best (+inf with fewer than two)
+ *   addr_margin [B,H,nb]: per block, the smallest best-minus-second code logit
+ *     over its subspaces (+inf when codes == 1)
+ *   Asking for any of the first four runs the probe with one more address and
+ *   candidate ranked; the routing itself is identical either way. */
 typedef struct {
   float* ksum;
   int32_t* addr;
@@ -148,6 +164,11 @@ typedef struct {
   int32_t* redir_off;
   int32_t* redir_idx;
   int32_t* redir_time;
+  int32_t* probes;
+  float* sel_score;
+  float* probe_margin;
+  float* sel_margin;
+  float* addr_margin;
 } mdr_routing;
 
 /* MDR_ABI_VERSION of the built library. */

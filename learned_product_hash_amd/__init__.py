@@ -54,7 +54,7 @@ class MdrConfig(ctypes.Structure):
 class MdrRouting(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "ksum", "addr", "post_off", "post_idx", "overflow", "sel", "n_cand", "n_drop", "alt", "redir_off",
-        "redir_idx", "redir_time")]
+        "redir_idx", "redir_time", "probes", "sel_score", "probe_margin", "sel_margin", "addr_margin")]
 
 
 class MdrWorkspaceParts(ctypes.Structure):
@@ -185,13 +185,20 @@ def workspace(cfg: MdrConfig, device="cuda") -> torch.Tensor:
     return torch.empty(max(1, mdr_workspace_size(cfg)), dtype=torch.uint8, device=device)
 
 
-def routing_buffers(cfg: MdrConfig, device="cuda") -> dict:
-    """Device tensors for every routing output of ``cfg``."""
+def routing_buffers(cfg: MdrConfig, device="cuda", diag=False) -> dict:
+    """Device tensors for every routing output of ``cfg`` (with ``diag`` also the routing diagnostics:
+    probes, selection scores and the decision margins)."""
     B, H, S, D = cfg.batch, cfg.heads, cfg.seq, cfg.head_dim
     nb = S // cfg.block
     A = cfg.codes ** cfg.subspaces
     i32 = dict(dtype=torch.int32, device=device)
-    return dict(ksum=torch.empty(B, H, nb, D, dtype=torch.float32, device=device),
+    f32 = dict(dtype=torch.float32, device=device)
+    extra = {}
+    if diag:
+        extra = dict(probes=torch.empty(B, H, S, cfg.probes, **i32), sel_score=torch.empty(B, H, S, cfg.remote, **f32),
+                     probe_margin=torch.empty(B, H, S, **f32), sel_margin=torch.empty(B, H, S, **f32),
+                     addr_margin=torch.empty(B, H, nb, **f32))
+    return dict(**extra, ksum=torch.empty(B, H, nb, D, dtype=torch.float32, device=device),
                 addr=torch.empty(B, H, nb, **i32), post_off=torch.empty(B, H, A + 1, **i32),
                 post_idx=torch.empty(B, H, nb, **i32), overflow=torch.empty(B, H, **i32),
                 sel=torch.empty(B, H, S, cfg.remote, **i32), n_cand=torch.empty(B, H, S, **i32),

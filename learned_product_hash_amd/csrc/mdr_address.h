@@ -74,11 +74,12 @@ struct CodeSlice {
 // threads call it (it contains a barrier); `logit` is LDS scratch of kMaxCodesTotal floats.  Thread
 // 0 writes *addr_out and, when given, *alt_out: in the subspace with the smallest fp32 margin
 // top1 - top2 (ties to the smaller subspace) the runner-up code (the best of the others, smaller
-// code on ties) replaces the top code; -1 when C == 1.
+// code on ties) replaces the top code; -1 when C == 1.  margin_out (optional) receives that smallest
+// margin (+inf when C == 1): how close the address came to a tie.
 template <int D>
 __device__ __forceinline__ void address_from_summary(const CodeSlice<D>& cs, const float* kbar, float* logit,
                                                      int32_t* __restrict__ addr_out, int32_t* __restrict__ alt_out,
-                                                     const Shape& s) {
+                                                     const Shape& s, float* __restrict__ margin_out = nullptr) {
   constexpr int LPC = CodeSlice<D>::LPC, DPL = CodeSlice<D>::DPL;
   const int tid = threadIdx.x, lane = tid & 63;
   const int GC = s.G * s.C;
@@ -111,7 +112,7 @@ __device__ __forceinline__ void address_from_summary(const CodeSlice<D>& cs, con
         }
       }
       a = a * s.C + c;
-      if (alt_out) {
+      if (alt_out || margin_out) {
         float v2 = (lane < s.C && lane != c) ? lv : -INFINITY;
         int c2 = (lane < s.C && lane != c) ? lane : 0x7fffffff;
 #pragma unroll
@@ -133,6 +134,7 @@ __device__ __forceinline__ void address_from_summary(const CodeSlice<D>& cs, con
     }
     if (tid == 0) {
       *addr_out = a;
+      if (margin_out) *margin_out = best_m;
       if (alt_out) {
         int pw = 1;  // place value of subspace gs (subspace 0 most significant)
         for (int g = gs + 1; g < s.G; ++g) pw *= s.C;
@@ -149,7 +151,8 @@ template <typename T, int D>
 __device__ __forceinline__ void block_address(const T* __restrict__ K, const float* __restrict__ cb,
                                               const float* __restrict__ bias, float* __restrict__ ksum,
                                               int32_t* __restrict__ addr, int i, int bh, AddressLds<T, D>& sm,
-                                              const Shape& s, int32_t* __restrict__ alt = nullptr) {
+                                              const Shape& s, int32_t* __restrict__ alt = nullptr,
+                                              float* __restrict__ margin = nullptr) {
   constexpr int VEC = Vec16<T>::n;
   constexpr int NCH = AddressLds<T, D>::NCH;
   constexpr int RG = AddressLds<T, D>::RG;
@@ -179,7 +182,8 @@ __device__ __forceinline__ void block_address(const T* __restrict__ K, const flo
   }
   __syncthreads();
   address_from_summary<D>(cs, sm.kbar, sm.logit, addr + (size_t)bh * s.nb + i,
-                          alt ? alt + (size_t)bh * s.nb + i : nullptr, s);
+                          alt ? alt + (size_t)bh * s.nb + i : nullptr, s,
+                          margin ? margin + (size_t)bh * s.nb + i : nullptr);
 }
 
 }  // namespace mdr

@@ -132,6 +132,9 @@ size_t layout(const Shape& s, char* base, Buffers* b, mdr_workspace_parts* parts
     t.alt = t.roff = t.ridx = t.rtime = nullptr;
   }
   t.ndrop = nullptr;
+  t.amargin = nullptr;
+  t.probes = nullptr;
+  t.sel_score = t.pmargin = t.smargin = nullptr;
   if (s.W > 0) {
     group = &pt.mixer;
     const size_t qkv = BH * s.S * s.D * e;
@@ -222,6 +225,11 @@ void apply_routing(const mdr_routing* r, Buffers* b) {
   if (r->sel) b->sel = r->sel;
   if (r->n_cand) b->ncand = r->n_cand;
   b->ndrop = r->n_drop;
+  b->amargin = r->addr_margin;
+  b->probes = r->probes;
+  b->sel_score = r->sel_score;
+  b->pmargin = r->probe_margin;
+  b->smargin = r->sel_margin;
   if (b->alt) {  // redirect policy
     if (r->alt) b->alt = r->alt;
     if (r->redir_off) b->roff = r->redir_off;
@@ -246,7 +254,7 @@ mdr_status run_core(const Shape& s, const void* q, const void* k, const void* v,
   const bool redirect = s.policy == MDR_OVERFLOW_REDIRECT;
   if (!have_address)
     MDR_TRY(launch_address(s, k, cb, bias, b.ksum, b.addr, remote ? b.phist : nullptr, st, 0, -1,
-                           redirect ? b.alt : nullptr));
+                           redirect ? b.alt : nullptr, b.amargin));
   MDR_TRY(mark_event(ev, 1, st));
   // the posting lists are built inside the probe kernel where a specialised probe exists (the post
   // interval of a profiled call is then empty); the redirect lists need the whole CSR first
@@ -255,7 +263,8 @@ mdr_status run_core(const Shape& s, const void* q, const void* k, const void* v,
   if (redirect) MDR_TRY(launch_post_redirect(s, b.addr, b.alt, b.off, b.idx, b.roff, b.ridx, b.rtime, b.overflow, st));
   MDR_TRY(mark_event(ev, 2, st));
   const FusedPost fp{b.addr, b.off, b.idx, b.overflow};
-  const ProbeExtra ex{redirect ? b.roff : nullptr, b.ridx, b.rtime, b.ndrop};
+  const ProbeExtra ex{redirect ? b.roff : nullptr, b.ridx, b.rtime, b.ndrop, b.probes, b.sel_score, b.pmargin,
+                      b.smargin};
   MDR_TRY(launch_probe_rerank(s, q, cb, bias, b.ksum, b.off, b.idx, force, b.sel, b.ncand,
                               remote ? b.phist : nullptr, st, fused ? &fp : nullptr, ex));
   MDR_TRY(mark_event(ev, 3, st));
@@ -419,7 +428,7 @@ mdr_status mdr_mixer_forward(const mdr_config* cfg, const void* x, const void* w
     const bool remote = s.R > 0 && s.ne > 0;
     MDR_TRY(launch_qkv_fused(s, x, wq, wk, wv, b.mq, b.mk, b.mv, codebook, code_bias, b.ksum, b.addr,
                              s.policy == MDR_OVERFLOW_REDIRECT ? b.alt : nullptr, remote ? b.phist : nullptr,
-                             b.mwt, hs));
+                             b.mwt, hs, b.amargin));
   } else {
     MDR_TRY(launch_project_heads(s, x, wq, b.mq, true, hs));
     MDR_TRY(launch_project_heads(s, x, wk, b.mk, true, hs));

@@ -74,15 +74,24 @@ struct Buffers {
   int32_t* ridx;       // [B,H,nb]  (block ids, in arrival order; -1 beyond the last)
   int32_t* rtime;      // [B,H,nb]  (the query block at which each arrives; -1 beyond the last)
   int32_t* ndrop;      // [B,H,S] optional: candidates the probed lists held but did not return
+  float* amargin;      // [B,H,nb] optional: each block's smallest code-logit margin
+  int32_t* probes;     // optional probe diagnostics (see ProbeExtra)
+  float* sel_score;
+  float* pmargin;
+  float* smargin;
 };
 
-// Redirect lists and the dropped-candidate output of the probe stage (all null under the drop
-// policy without diagnostics).
+// Redirect lists and the optional per-token outputs of the probe stage beyond the selection (all null
+// under the drop policy without diagnostics).
 struct ProbeExtra {
   const int32_t* roff;
   const int32_t* ridx;
   const int32_t* rtime;
   int32_t* ndrop;
+  int32_t* probes = nullptr;    // [B,H,S,P] the probed addresses in rank order
+  float* sel_score = nullptr;   // [B,H,S,R] rerank score of each selected block
+  float* pmargin = nullptr;     // [B,H,S] smallest neighbour gap of the P + 1 best address scores
+  float* smargin = nullptr;     // [B,H,S] smallest neighbour gap of the R + 1 best candidate scores
 };
 
 // Streaming-decode state (one region of a caller-owned buffer each).
@@ -203,10 +212,10 @@ inline hipError_t mark_event(hipEvent_t* ev, int i, hipStream_t st) {
 // pair_zero (optional): the address kernel of block i clears column i of the pair counters.
 // Blocks [i0, i0 + n) (n < 0: to the end).
 // alt (optional): also the alternate address of each block (runner-up code of its lowest-margin
-// subspace).
+// subspace).  amargin (optional): each block's smallest top1 - top2 code-logit margin.
 hipError_t launch_address(const Shape& s, const void* k, const float* codebook, const float* bias,
                           float* ksum, int32_t* addr, int32_t* pair_zero, hipStream_t st, int i0 = 0, int n = -1,
-                          int32_t* alt = nullptr);
+                          int32_t* alt = nullptr, float* amargin = nullptr);
 hipError_t launch_post(const Shape& s, const int32_t* addr, int32_t* off, int32_t* idx,
                        int32_t* overflow, hipStream_t st);
 // Posting lists built inside the probe kernel (from the block addresses) instead of read: every
@@ -272,6 +281,6 @@ hipError_t launch_project_out(const Shape& s, const void* o, const void* wo, voi
 bool qkv_fuses_address(const Shape& s);
 hipError_t launch_qkv_fused(const Shape& s, const void* x, const void* wq, const void* wk, const void* wv, void* q,
                             void* k, void* v, const float* cb, const float* bias, float* ksum, int32_t* addr,
-                            int32_t* alt, int32_t* pair_zero, void* wt, hipStream_t st);
+                            int32_t* alt, int32_t* pair_zero, void* wt, hipStream_t st, float* amargin = nullptr);
 
 }  // namespace mdr

@@ -140,6 +140,7 @@ struct QkvEpilogue {
   int32_t* addr;
   int32_t* alt;
   int32_t* pair_zero;
+  float* amargin;
 };
 
 // One direct global-to-LDS load of 16 bytes per lane: lane l's bytes land at lds + 16 l (lds uniform
@@ -437,7 +438,8 @@ __global__ __launch_bounds__(256) void k_mm(const T* __restrict__ A, const T* __
             if (ep.pair_zero) clear_pair_counts(ep.pair_zero, s, bh, i, tid, 256);
             __syncthreads();
             address_from_summary<D>(cs, kbar, logit, ep.addr + (size_t)bh * s.nb + i,
-                                    ep.alt ? ep.alt + (size_t)bh * s.nb + i : nullptr, s);
+                                    ep.alt ? ep.alt + (size_t)bh * s.nb + i : nullptr, s,
+                                    ep.amargin ? ep.amargin + (size_t)bh * s.nb + i : nullptr);
             __syncthreads();  // kbar and logit are rewritten next
           }
         }
@@ -579,9 +581,9 @@ bool qkv_fuses_address(const Shape& s) { return s.blk <= 64 && s.W % 8 == 0 && m
 
 hipError_t launch_qkv_fused(const Shape& s, const void* x, const void* wq, const void* wk, const void* wv, void* q,
                             void* k, void* v, const float* cb, const float* bias, float* ksum, int32_t* addr,
-                            int32_t* alt, int32_t* pair_zero, void* wt, hipStream_t st) {
+                            int32_t* alt, int32_t* pair_zero, void* wt, hipStream_t st, float* amargin) {
   if (!qkv_fuses_address(s)) return hipErrorInvalidValue;
-  const QkvEpilogue ep{cb, bias, ksum, addr, alt, pair_zero};
+  const QkvEpilogue ep{cb, bias, ksum, addr, alt, pair_zero, amargin};
   if (s.dtype == MDR_BF16) return qkv_fused<bf16>(s, x, wq, wk, wv, q, k, v, ep, wt, st);
   return qkv_fused<float>(s, x, wq, wk, wv, q, k, v, ep, wt, st);
 }

@@ -33,12 +33,13 @@ template <typename T, int D>
 __global__ __launch_bounds__(256) void k_address(const T* __restrict__ K, const float* __restrict__ cb,
                                                  const float* __restrict__ bias, float* __restrict__ ksum,
                                                  int32_t* __restrict__ addr, int32_t* __restrict__ pair_zero,
-                                                 int32_t* __restrict__ alt, int i0, Shape s) {
+                                                 int32_t* __restrict__ alt, float* __restrict__ amargin, int i0,
+                                                 Shape s) {
   __shared__ AddressLds<T, D> sm;
   const int i = i0 + blockIdx.x;
   const int bh = blockIdx.y;
   if (pair_zero) clear_pair_counts(pair_zero, s, bh, i, threadIdx.x, 256);
-  block_address<T, D>(K, cb, bias, ksum, addr, i, bh, sm, s, alt);
+  block_address<T, D>(K, cb, bias, ksum, addr, i, bh, sm, s, alt, amargin);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -260,14 +261,22 @@ __global__ __launch_bounds__(kProbeThreads) void k_probe_rerank(
   const int C = s.C, G = s.G, P = s.P, R = s.R, A = s.A;
   const int CP = (C + 15) & ~15;
   const int MST = G * CP + 4;
-  const int Pg = min(P, C);
+  // with diagnostics one more address and candidate are ranked, for the margins at the boundaries: the
+  // P + 1 best addresses come from the min(P + 1, C) best codes per subspace and the rank vectors with
+  // prod (k_g + 1) <= P + 1
+  const bool diag = ex.probes || ex.sel_score || ex.pmargin || ex.smargin;
+  const int Pl = diag ? P + 1 : P;                   // rank-vector bound and address list length
+  const int KPl = min(Pl, A);
+  const int Rl = diag ? R + 1 : R;                   // candidate list length
+  const int Pg = min(Pl, C);
+  const int PgM = min(P + 1, C);                     // LDS is laid out for the diagnostics sizes
   float* mu = smem;                                  // [NT][MST]
-  int* tcode = (int*)(mu + NT * MST);                // [G*Pg][NT]
-  float* tpv = (float*)(tcode + G * Pg * NT);        // [P][NT]
-  int* tpa = (int*)(tpv + P * NT);                   // [P][NT]
-  float* trv = (float*)(tpa + P * NT);               // [R][NT]
-  int* tri = (int*)(trv + R * NT);                   // [R][NT]
-  int* csr = tri + R * NT;                           // off [A+1], idx [ne] when staged
+  int* tcode = (int*)(mu + NT * MST);                // [G*PgM][NT]
+  float* tpv = (float*)(tcode + G * PgM * NT);       // [P+1][NT]
+  int* tpa = (int*)(tpv + (P + 1) * NT);             // [P+1][NT]
+  float* trv = (float*)(tpa + (P + 1) * NT);         // [R+1][NT]
+  int* tri = (int*)(trv + (R + 1) * NT);             // [R+1][NT]
+  int* csr = tri + (R + 1) * NT;                     // off [A+1], idx [ne] when staged
   const int32_t* offp = off + (size_t)bh * (A + 1);
   const int32_t* idxp = idx + (size_t)bh * s.nb;
   if (s.csr_lds) {
@@ -359,7 +368,7 @@ __global__ __launch_bounds__(kProbeThreads) void k_probe_rerank(
       pc = bc;
     }
   }
-  // ---- score the rank vectors with prod (k_g + 1) <= P, keep the top-P addresses
+  // ---- score the rank vectors with prod (k_g + 1) <= Pl, keep the top-Pl addresses
   int ncomb = 1;
   for (int g = 0; g < G; ++g) ncomb *= Pg;
   int np = 0;
@@ -374,7 +383,7 @@ __global__ __launch_bounds__(kProbeThreads) void k_probe_rerank(
         prod *= rk[g] + 1;
       }
     }
-    if (prod > P) continue;
+    if (prod > Pl) continue;
     int c0 = tcode[rk[0] * NT + tid];
     float sig = mrow[c0];
     int a = c0;
@@ -387,11 +396,11 @@ __global__ __launch_bounds__(kProbeThreads) void k_probe_rerank(
       }
     }
     int pos;
-    if (np == P) {
-      const float wv = tpv[(P - 1) * NT + tid];
-      const int wa = tpa[(P - 1) * NT + tid];
+    if (np == KPl) {
+      const float wv = tpv[(KPl - 1) * NT + tid];
+      const int wa = tpa[(KPl - 1) * NT + tid];
       if (!(sig > wv || (sig == wv && a < wa))) continue;
-      pos = P - 1;
+      pos = KPl - 1;
     } else {
       pos = np++;
     }
@@ -441,11 +450,11 @@ __global__ __launch_bounds__(kProbeThreads) void k_probe_rerank(
         rho = fmaf(kv.w, qv[4 * c + 3], rho);
       }
       int pos;
-      if (nr == R) {
-        const float wv = trv[(R - 1) * NT + tid];
-        const int wi = tri[(R - 1) * NT + tid];
+      if (nr == Rl) {
+        const float wv = trv[(Rl - 1) * NT + tid];
+        const int wi = tri[(Rl - 1) * NT + tid];
         if (!(rho > wv || (rho == wv && i < wi))) return;
-        pos = R - 1;
+        pos = Rl - 1;
       } else {
         pos = nr++;
       }
@@ -460,7 +469,7 @@ __global__ __launch_bounds__(kProbeThreads) void k_probe_rerank(
       trv[pos * NT + tid] = rho;
       tri[pos * NT + tid] = i;
     };
-    for (int p = 0; p < np; ++p) {
+    for (int p = 0; p < min(np, P); ++p) {
       const int a = tpa[p * NT + tid];
       const int lo = offp[a], hi = offp[a + 1];
       int l0 = lo, l1 = hi;  // first entry > cutoff
@@ -499,23 +508,39 @@ __global__ __launch_bounds__(kProbeThreads) void k_probe_rerank(
       ndr += max(0, (roffp && C > 1 ? tp : nprim) + narr - s.cap);
     }
   }
+  const int nrank = nr;  // ranked candidates kept (up to Rl)
+  nr = min(nr, R);
+  int fslot = -1;        // the slot a forced block took
   if (force && R > 0) {
     const int f = force[(size_t)bh * s.S + t];
     if (f >= 0 && f <= cutoff) {
       bool present = false;
       for (int r = 0; r < nr; ++r) present |= (tri[r * NT + tid] == f);
-      if (!present) {
-        if (nr < R)
-          tri[(nr++) * NT + tid] = f;
-        else
-          tri[(R - 1) * NT + tid] = f;
+      if (!present) {  // the forced block goes to its slot once the diagnostics have read the ranking
+        fslot = nr < R ? nr : R - 1;
+        if (nr < R) ++nr;
       }
     }
   }
-  int32_t* srow = sel + ((size_t)bh * s.S + t) * R;
+  const size_t tt = (size_t)bh * s.S + t;
+  if (diag) {
+    if (ex.probes)
+      for (int p = 0; p < P; ++p) ex.probes[tt * P + p] = tpa[p * NT + tid];
+    float pm = INFINITY;
+    for (int p = 0; p + 1 < np; ++p) pm = fminf(pm, tpv[p * NT + tid] - tpv[(p + 1) * NT + tid]);
+    if (ex.pmargin) ex.pmargin[tt] = pm;
+    float sm = INFINITY;
+    for (int r = 0; r + 1 < nrank && r < R; ++r) sm = fminf(sm, trv[r * NT + tid] - trv[(r + 1) * NT + tid]);
+    if (ex.smargin) ex.smargin[tt] = R > 0 ? sm : INFINITY;
+    if (ex.sel_score)
+      for (int r = 0; r < R; ++r)
+        ex.sel_score[tt * R + r] = r >= nr ? -INFINITY : r == fslot ? NAN : trv[r * NT + tid];
+  }
+  if (fslot >= 0) tri[fslot * NT + tid] = force[(size_t)bh * s.S + t];
+  int32_t* srow = sel + tt * R;
   for (int r = 0; r < R; ++r) srow[r] = r < nr ? tri[r * NT + tid] : -1;
-  if (ncand) ncand[(size_t)bh * s.S + t] = nc;
-  if (ex.ndrop) ex.ndrop[(size_t)bh * s.S + t] = ndr;
+  if (ncand) ncand[tt] = nc;
+  if (ex.ndrop) ex.ndrop[tt] = ndr;
   }  // active
   if (!phist) return;  // uniform
   // ---- count the selected pairs of this work-group's token range per remote block (LDS histogram in the
@@ -782,7 +807,9 @@ __device__ inline int operand_dim(int s4, int x) {
 // Small bf16 shapes keep four waves per SIMD, so that four 256-token work-groups share a CU.
 constexpr int probe_min_waves(int bytes, int D, int C) { return bytes == 2 && D <= 64 && C <= 16 ? 4 : 1; }
 
-template <typename T, int D, int G, int C, int P, int R, bool FUSED>
+constexpr int cpow(int b, int e) { return e == 0 ? 1 : b * cpow(b, e - 1); }
+
+template <typename T, int D, int G, int C, int P, int R, bool FUSED, bool DIAG>
 __global__ __launch_bounds__(kProbeFixedThreads) __attribute__((amdgpu_waves_per_eu(probe_min_waves((int)sizeof(T), D, C)))) void k_probe_fixed(
     const T* __restrict__ Q, const float* __restrict__ cb, const float* __restrict__ bias,
     const float* __restrict__ ksum, const int32_t* __restrict__ off, const int32_t* __restrict__ idx,
@@ -1008,7 +1035,55 @@ __global__ __launch_bounds__(kProbeFixedThreads) __attribute__((amdgpu_waves_per
     for (int p = 0; p < P; ++p) out[p] = key_index(tpk[p]);
   };
   int tpa[P];
-  if constexpr (PACK_A) {
+  float pmarg = INFINITY;  // diagnostics: smallest gap between neighbouring scores of the P + 1 best addresses
+  if constexpr (DIAG) {
+    // exact (value desc, index asc) ranks over every code and rank vector that can reach the P + 1 best
+    // addresses: min(P + 1, C) codes per subspace, rank vectors with prod (k_g + 1) <= P + 1
+    constexpr int PX = P + 1 < C ? P + 1 : C;
+    constexpr int NCX = RankSpace<G, PX>::count();
+    constexpr int KX = P + 1 < cpow(C, G) ? P + 1 : cpow(C, G);
+    int xcode[G][PX];
+    float xval[G][PX];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      uint64_t t64[PX];
+#pragma unroll
+      for (int p = 0; p < PX; ++p) t64[p] = 0;
+#pragma unroll
+      for (int c = 0; c < C; ++c) insert_key<PX>(t64, rank_key(mrow[g * CP + c], c));
+#pragma unroll
+      for (int p = 0; p < PX; ++p) {
+        xcode[g][p] = key_index(t64[p]);
+        xval[g][p] = mrow[g * CP + xcode[g][p]];
+      }
+    }
+    uint64_t tpk[KX];
+#pragma unroll
+    for (int p = 0; p < KX; ++p) tpk[p] = 0;
+#pragma unroll
+    for (int kc = 0; kc < NCX; ++kc) {
+      int rem = kc, prod = 1;
+      int rk[G];
+#pragma unroll
+      for (int g = G - 1; g >= 0; --g) {
+        rk[g] = rem % PX;
+        rem /= PX;
+        prod *= rk[g] + 1;
+      }
+      float sig = xval[0][rk[0]];
+      int a = xcode[0][rk[0]];
+#pragma unroll
+      for (int g = 1; g < G; ++g) {
+        sig += xval[g][rk[g]];
+        a = a * C + xcode[g][rk[g]];
+      }
+      if (prod <= P + 1) insert_key<KX>(tpk, rank_key(sig, a));
+    }
+#pragma unroll
+    for (int p = 0; p < P; ++p) tpa[p] = key_index(tpk[p]);
+#pragma unroll
+    for (int p = 0; p + 1 < KX; ++p) pmarg = fminf(pmarg, key_value(tpk[p]) - key_value(tpk[p + 1]));
+  } else if constexpr (PACK_A) {
     uint32_t tpk[KP];
 #pragma unroll
     for (int p = 0; p < KP; ++p) tpk[p] = 0;
@@ -1163,16 +1238,18 @@ __global__ __launch_bounds__(kProbeFixedThreads) __attribute__((amdgpu_waves_per
   lds_barrier();
   // ---- top-R of the token's candidates by (score desc, block asc)
   constexpr int RK = R > 0 ? R : 1;
+  constexpr int RKX = DIAG ? RK + 1 : RK;  // diagnostics: one more, for the margin at the boundary
   int tri[RK];
   int nr = 0;
   if (active) {
-    uint64_t trk[RK];
+    uint64_t trk[RKX];
 #pragma unroll
-    for (int r = 0; r < RK; ++r) trk[r] = 0;
-    for (int k = base; k < base + nc; ++k) insert_key<RK>(trk, rank_key(rho[k], clist[k] & 0xffff));
+    for (int r = 0; r < RKX; ++r) trk[r] = 0;
+    for (int k = base; k < base + nc; ++k) insert_key<RKX>(trk, rank_key(rho[k], clist[k] & 0xffff));
 #pragma unroll
     for (int r = 0; r < RK; ++r) tri[r] = key_index(trk[r]);
     nr = nc < R ? nc : R;
+    int fslot = -1;  // the slot a forced block took
     if (force && R > 0) {
       const int f = fv;
       if (f >= 0 && f <= cutoff) {
@@ -1185,6 +1262,7 @@ __global__ __launch_bounds__(kProbeFixedThreads) __attribute__((amdgpu_waves_per
           for (int r = 0; r < RK; ++r)
             if (r == slot) tri[r] = f;
           nr = nr < R ? nr + 1 : R;
+          fslot = slot;
         }
       }
     }
@@ -1193,6 +1271,22 @@ __global__ __launch_bounds__(kProbeFixedThreads) __attribute__((amdgpu_waves_per
     for (int r = 0; r < R; ++r) srow[r] = r < nr ? tri[r] : -1;
     if (ncand) ncand[(size_t)bh * s.S + t] = nc;
     if (ex.ndrop) ex.ndrop[(size_t)bh * s.S + t] = ndr;
+    if constexpr (DIAG) {
+      const size_t tt = (size_t)bh * s.S + t;
+      if (ex.probes)
+#pragma unroll
+        for (int p = 0; p < P; ++p) ex.probes[tt * P + p] = tpa[p];
+      if (ex.pmargin) ex.pmargin[tt] = pmarg;
+      float smarg = INFINITY;
+#pragma unroll
+      for (int r = 0; r + 1 < RKX; ++r)
+        if (r + 1 < nc && r < R) smarg = fminf(smarg, key_value(trk[r]) - key_value(trk[r + 1]));
+      if (ex.smargin) ex.smargin[tt] = R > 0 ? smarg : INFINITY;
+      if (ex.sel_score)
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+          ex.sel_score[tt * R + r] = r >= nr ? -INFINITY : r == fslot ? NAN : key_value(trk[r]);
+    }
   }
   if (!phist) return;  // uniform
   // ---- count the selected pairs of this work-group's token range per remote block (LDS histogram in the
@@ -1210,18 +1304,18 @@ __global__ __launch_bounds__(kProbeFixedThreads) __attribute__((amdgpu_waves_per
 
 template <typename T>
 hipError_t address_dispatch(const Shape& s, const void* k, const float* cb, const float* bias, float* ksum,
-                            int32_t* addr, int32_t* cnt, int32_t* alt, int i0, int n, hipStream_t st) {
+                            int32_t* addr, int32_t* cnt, int32_t* alt, float* am, int i0, int n, hipStream_t st) {
   if (n <= 0) return hipSuccess;
   dim3 grid(n, s.B * s.H);
   switch (s.D) {
     case 32:
-      hipLaunchKernelGGL((k_address<T, 32>), grid, dim3(256), 0, st, (const T*)k, cb, bias, ksum, addr, cnt, alt, i0, s);
+      hipLaunchKernelGGL((k_address<T, 32>), grid, dim3(256), 0, st, (const T*)k, cb, bias, ksum, addr, cnt, alt, am, i0, s);
       break;
     case 64:
-      hipLaunchKernelGGL((k_address<T, 64>), grid, dim3(256), 0, st, (const T*)k, cb, bias, ksum, addr, cnt, alt, i0, s);
+      hipLaunchKernelGGL((k_address<T, 64>), grid, dim3(256), 0, st, (const T*)k, cb, bias, ksum, addr, cnt, alt, am, i0, s);
       break;
     case 128:
-      hipLaunchKernelGGL((k_address<T, 128>), grid, dim3(256), 0, st, (const T*)k, cb, bias, ksum, addr, cnt, alt, i0, s);
+      hipLaunchKernelGGL((k_address<T, 128>), grid, dim3(256), 0, st, (const T*)k, cb, bias, ksum, addr, cnt, alt, am, i0, s);
       break;
     default:
       return hipErrorInvalidValue;
@@ -1229,7 +1323,7 @@ hipError_t address_dispatch(const Shape& s, const void* k, const float* cb, cons
   return hipGetLastError();
 }
 
-template <typename T, int D, int G, int C, int P, int R, bool FUSED>
+template <typename T, int D, int G, int C, int P, int R, bool FUSED, bool DIAG>
 hipError_t probe_fixed_launch_t(const Shape& s, const void* q, const float* cb, const float* bias, const float* ksum,
                                 const int32_t* off, const int32_t* idx, const int32_t* force, int32_t* sel,
                                 int32_t* ncand, int32_t* phist, const FusedPost& fp,
@@ -1237,11 +1331,11 @@ hipError_t probe_fixed_launch_t(const Shape& s, const void* q, const float* cb, 
   dim3 grid((s.S + kProbeFixedThreads - 1) / kProbeFixedThreads, s.B * s.H);
   const size_t lds = probe_lds_bytes(s);
   if (lds > 65536) {
-    hipError_t e = hipFuncSetAttribute((const void*)k_probe_fixed<T, D, G, C, P, R, FUSED>,
+    hipError_t e = hipFuncSetAttribute((const void*)k_probe_fixed<T, D, G, C, P, R, FUSED, DIAG>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((k_probe_fixed<T, D, G, C, P, R, FUSED>), grid, dim3(kProbeFixedThreads), lds, st, (const T*)q, cb,
+  hipLaunchKernelGGL((k_probe_fixed<T, D, G, C, P, R, FUSED, DIAG>), grid, dim3(kProbeFixedThreads), lds, st, (const T*)q, cb,
                      bias, ksum, off, idx, force, sel, ncand, phist, fp, ex, s);
   return hipGetLastError();
 }
@@ -1251,12 +1345,17 @@ hipError_t probe_fixed_launch(const Shape& s, const void* q, const float* cb, co
                               const int32_t* off, const int32_t* idx, const int32_t* force, int32_t* sel,
                               int32_t* ncand, int32_t* phist, const FusedPost* fuse,
                               const ProbeExtra& ex, hipStream_t st) {
-  if (fuse)
-    return probe_fixed_launch_t<T, D, G, C, P, R, true>(s, q, cb, bias, ksum, off, idx, force, sel, ncand, phist,
-                                                         *fuse, ex, st);
+  const bool diag = ex.probes || ex.sel_score || ex.pmargin || ex.smargin;
   const FusedPost none{nullptr, nullptr, nullptr, nullptr};
-  return probe_fixed_launch_t<T, D, G, C, P, R, false>(s, q, cb, bias, ksum, off, idx, force, sel, ncand, phist,
-                                                        none, ex, st);
+  if (fuse)
+    return diag ? probe_fixed_launch_t<T, D, G, C, P, R, true, true>(s, q, cb, bias, ksum, off, idx, force, sel,
+                                                                     ncand, phist, *fuse, ex, st)
+                : probe_fixed_launch_t<T, D, G, C, P, R, true, false>(s, q, cb, bias, ksum, off, idx, force, sel,
+                                                                      ncand, phist, *fuse, ex, st);
+  return diag ? probe_fixed_launch_t<T, D, G, C, P, R, false, true>(s, q, cb, bias, ksum, off, idx, force, sel, ncand,
+                                                                    phist, none, ex, st)
+              : probe_fixed_launch_t<T, D, G, C, P, R, false, false>(s, q, cb, bias, ksum, off, idx, force, sel,
+                                                                     ncand, phist, none, ex, st);
 }
 
 // Shapes with a compile-time specialisation (the five workload families); others use k_probe_rerank.
@@ -1312,11 +1411,12 @@ hipError_t probe_dispatch(const Shape& s, const void* q, const float* cb, const 
 }  // namespace
 
 hipError_t launch_address(const Shape& s, const void* k, const float* codebook, const float* bias, float* ksum,
-                          int32_t* addr, int32_t* pair_zero, hipStream_t st, int i0, int n, int32_t* alt) {
+                          int32_t* addr, int32_t* pair_zero, hipStream_t st, int i0, int n, int32_t* alt,
+                          float* amargin) {
   if (n < 0) n = s.nb - i0;
   if (s.dtype == MDR_BF16)
-    return address_dispatch<bf16>(s, k, codebook, bias, ksum, addr, pair_zero, alt, i0, n, st);
-  return address_dispatch<float>(s, k, codebook, bias, ksum, addr, pair_zero, alt, i0, n, st);
+    return address_dispatch<bf16>(s, k, codebook, bias, ksum, addr, pair_zero, alt, amargin, i0, n, st);
+  return address_dispatch<float>(s, k, codebook, bias, ksum, addr, pair_zero, alt, amargin, i0, n, st);
 }
 
 bool probe_fixed_shape(const Shape& s) {
@@ -1337,8 +1437,9 @@ size_t probe_lds_bytes(const Shape& s) {
     const size_t mu_w = (size_t)kProbeFixedThreads * (s.G * CP + 1), pairs_w = (size_t)kProbeFixedThreads * s.M * 2;
     return ((mu_w > pairs_w ? mu_w : pairs_w) + (s.csr_lds ? (size_t)(s.A + 1 + s.ne) : 0)) * 4;
   }
-  const int Pg = s.P < s.C ? s.P : s.C;
-  const size_t words = (size_t)kProbeThreads * (s.G * CP + 4) + (size_t)kProbeThreads * (s.G * Pg + 2 * s.P + 2 * s.R) +
+  const int Pg = s.P + 1 < s.C ? s.P + 1 : s.C;  // laid out for the diagnostics sizes (P + 1, R + 1)
+  const size_t words = (size_t)kProbeThreads * (s.G * CP + 4) +
+                       (size_t)kProbeThreads * (s.G * Pg + 2 * (s.P + 1) + 2 * (s.R + 1)) +
                        (s.csr_lds ? (size_t)(s.A + 1 + s.ne) : 0);
   return words * 4;
 }

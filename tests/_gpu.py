@@ -41,8 +41,9 @@ def host(t):
     return t.detach().float().cpu().numpy() if t.is_floating_point() else t.detach().cpu().numpy()
 
 
-def run_core(mdr, w, inp, force=None, policy="drop"):
-    """mdr_routed_attention with every routing output requested; returns host arrays."""
+def run_core(mdr, w, inp, force=None, policy="drop", diag=True):
+    """mdr_routed_attention with every routing output requested (with ``diag`` also the routing
+    diagnostics: probes, scores, margins); returns host arrays."""
     cfg = cfg_of(mdr, w, policy)
     dt = io_dtype(w)
     q, k, v = (dev(inp[n], dt) for n in ("q", "k", "v"))
@@ -50,7 +51,7 @@ def run_core(mdr, w, inp, force=None, policy="drop"):
     bias = None if inp["bias"] is None else dev(inp["bias"], torch.float32)
     f = None if force is None else dev(force)
     out = torch.empty_like(q)
-    rt = mdr.routing_buffers(cfg)
+    rt = mdr.routing_buffers(cfg, diag=diag)
     ws = mdr.workspace(cfg)
     mdr.mdr_routed_attention(cfg, q, k, v, cb, bias, f, out, rt, ws)
     torch.cuda.synchronize()

@@ -45,7 +45,7 @@ def test_library_exports_every_declared_symbol(mdr):
     lib = ctypes.CDLL(LIB)
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert mdr.mdr_abi_version() == 3
+    assert mdr.mdr_abi_version() == 4
 
 
 def test_binding_has_every_declared_entry_point(mdr):

@@ -177,6 +177,59 @@ def test_routed_attention_end_to_end(gpu_lib, name):
     assert err <= TOL[w.dtype]
 
 
+@pytest.mark.parametrize("name", NAMES)
+def test_diagnostics_leave_routing_unchanged(gpu_lib, name):
+    """Asking for the routing diagnostics runs the probe with one more address and candidate ranked;
+    every other output must be bit-identical to the run without them."""
+    mdr = gpu_lib
+    w = small(name)
+    inp = synth.make_core_inputs(w, 5)
+    a = run_core(mdr, w, inp, force=inp.get("force"), diag=False)
+    b = run_core(mdr, w, inp, force=inp.get("force"), diag=True)
+    for n in a:
+        assert np.array_equal(a[n], b[n]), n
+
+
+@pytest.mark.parametrize("name", NAMES)
+def test_diagnostics_match_the_oracle(gpu_lib, name):
+    """The GPU's probes equal the oracle's wherever the probe margin exceeds NEAR; its selection scores,
+    probe, rerank and address margins equal the oracle's up to fp32 summation order (where the oracle's
+    routing is the GPU's: no address near-tie in the head)."""
+    mdr = gpu_lib
+    w = small(name)
+    inp = synth.make_core_inputs(w, 6)
+    res = run_core(mdr, w, inp)
+    checked = 0
+    for b in range(w.batch):
+        for h in range(w.heads):
+            na = compare_addresses(w, inp, res["addr"][b, h], b, h)
+            r = route_for(w, inp, b, h, addr=res["addr"][b, h] if na else None)
+            am = res["addr_margin"][b, h]
+            np.testing.assert_allclose(am, r["addr_margin"].min(axis=1), rtol=1e-4, atol=1e-4)
+            sure = r["probe_margin"] > NEAR
+            assert np.array_equal(res["probes"][b, h][sure], r["probes"][sure])
+            pm, om = res["probe_margin"][b, h], r["probe_margin"]
+            fin = np.isfinite(om)
+            assert np.array_equal(np.isfinite(pm), fin)
+            np.testing.assert_allclose(pm[fin], om[fin], rtol=1e-4, atol=1e-4)
+            sure &= r["sel_margin"] > NEAR
+            sm, osm = res["sel_margin"][b, h], r["sel_margin"]
+            fin = np.isfinite(osm) & sure
+            np.testing.assert_allclose(sm[fin], osm[fin], rtol=1e-4, atol=1e-4)
+            q = inp["q"][b, h].astype(np.float32)
+            for t in np.nonzero(sure)[0]:
+                sel = r["sel"][t]
+                for k in range(w.remote):
+                    if sel[k] < 0:
+                        assert res["sel_score"][b, h, t, k] == -np.inf
+                    else:
+                        ref = float(np.asarray(r["ksum"][sel[k]], np.float32) @ q[t])
+                        assert abs(res["sel_score"][b, h, t, k] - ref) <= 1e-4 * max(1.0, abs(ref)), (t, k)
+                checked += 1
+    print(f"{name}: diagnostics checked on {checked} tokens")
+    assert checked > 0
+
+
 def test_recall_forced_target_full_batch(gpu_lib):
     """All 16 sequences of the recall workload; forcing the planted block puts it into every selection of
     the last query block under the same budget R."""
