@@ -203,6 +203,15 @@ typedef struct {
 } mdr_workspace_parts;
 mdr_status mdr_workspace_breakdown(const mdr_config* cfg, mdr_workspace_parts* parts);
 
+/* Host-only self-check of the kernels' index arithmetic for cfg: the functions
+ * the kernels use to map a work-group to its work and to address their buffers
+ * are run over every launch index of cfg's kernels (and over extreme
+ * distributions of the selected pairs), and each result is checked against the
+ * workspace region it addresses (also: regions aligned, disjoint, inside the
+ * workspace).  Returns MDR_OK, or MDR_ERR_INVALID_ARG with a description in msg
+ * (msg_len bytes, may be 0).  Touches no device. */
+mdr_status mdr_selfcheck_indices(const mdr_config* cfg, char* msg, size_t msg_len);
+
 /* The routed attention core on post-RoPE inputs (the whole path: addressing,
  * posting lists, probe + rerank, selected-set attention).
  *   q, k, v    [B,H,S,D] in cfg->dtype

@@ -21,7 +21,7 @@ __all__ = [
     "LIB_PATH", "MdrError", "MdrConfig", "MdrRouting", "MdrDecodeView", "MDR_F32", "MDR_BF16",
     "MDR_OVERFLOW_DROP", "MDR_OVERFLOW_REDIRECT", "config", "lib",
     "mdr_abi_version", "mdr_status_string", "mdr_check_config", "mdr_workspace_size", "MdrWorkspaceParts",
-    "mdr_workspace_breakdown", "workspace_breakdown",
+    "mdr_workspace_breakdown", "workspace_breakdown", "mdr_selfcheck_indices",
     "mdr_routed_attention", "mdr_routed_attention_profiled", "MDR_CORE_KERNELS", "CORE_KERNELS",
     "mdr_routed_attention_noalloc", "MDR_NOALLOC_SCRATCH_BYTES",
     "mdr_mixer_forward", "mdr_stage_address", "mdr_stage_post",
@@ -84,6 +84,7 @@ _SIGS = {
     "mdr_check_config": ([_cfgp], _i32),
     "mdr_workspace_size": ([_cfgp, ctypes.POINTER(_sz)], _i32),
     "mdr_workspace_breakdown": ([_cfgp, ctypes.POINTER(MdrWorkspaceParts)], _i32),
+    "mdr_selfcheck_indices": ([_cfgp, ctypes.c_char_p, _sz], _i32),
     "mdr_routed_attention": ([_cfgp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _rtp, _vp, _sz, _vp], _i32),
     "mdr_routed_attention_profiled": ([_cfgp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _rtp, _vp, _sz,
                                        ctypes.POINTER(_vp), _vp], _i32),
@@ -178,6 +179,16 @@ def workspace_breakdown(cfg: MdrConfig) -> dict:
     """mdr_workspace_breakdown as a dict of byte counts."""
     p = mdr_workspace_breakdown(cfg)
     return {n: getattr(p, n) for n, _ in MdrWorkspaceParts._fields_}
+
+
+def mdr_selfcheck_indices(cfg: MdrConfig) -> str:
+    """Host-only check of the kernels' index arithmetic for ``cfg``; returns "" when every index is in
+    bounds, else the first violation."""
+    buf = ctypes.create_string_buffer(256)
+    st = lib.mdr_selfcheck_indices(ctypes.byref(cfg), buf, 256)
+    if st not in (MDR_OK, MDR_ERR_INVALID_ARG):
+        raise MdrError(st, "mdr_selfcheck_indices")
+    return buf.value.decode() if st != MDR_OK else ""
 
 
 def workspace(cfg: MdrConfig, device="cuda") -> torch.Tensor:

@@ -1,6 +1,7 @@
 // C ABI of the routed-attention library: host-side validation, workspace planning and the
 // launch sequences.  No entry point allocates memory or keeps state between calls.
 #include <math.h>
+#include <stdio.h>
 #include <stdlib.h>
 #include <string.h>
 
@@ -87,15 +88,25 @@ size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Workspace regions; with base == nullptr only the size is computed.  parts (optional) receives the
 // bytes of each group of regions.
-size_t layout(const Shape& s, char* base, Buffers* b, mdr_workspace_parts* parts = nullptr) {
+// Requested size of each region (for the index self-check).
+struct Region {
+  const char* p;
+  size_t bytes;
+};
+constexpr int kMaxRegions = 64;
+
+size_t layout(const Shape& s, char* base, Buffers* b, mdr_workspace_parts* parts = nullptr, Region* regs = nullptr,
+              int* nregs = nullptr) {
   const size_t BH = (size_t)s.B * s.H, e = s.dtype == MDR_BF16 ? 2 : 4;
   size_t off = 0;
   mdr_workspace_parts pt;
   memset(&pt, 0, sizeof(pt));
   size_t* group = &pt.summaries;
+  int nr = 0;
   auto take = [&](size_t bytes) -> char* {
     char* p = base ? base + off : nullptr;
     const size_t n = align_up(bytes ? bytes : 4);
+    if (regs && nr < kMaxRegions) regs[nr++] = Region{p, bytes};
     off += n;
     *group += n;
     return p;
@@ -150,6 +161,7 @@ size_t layout(const Shape& s, char* base, Buffers* b, mdr_workspace_parts* parts
   if (b) *b = t;
   pt.total = off;
   if (parts) *parts = pt;
+  if (nregs) *nregs = nr;
   return off;
 }
 
@@ -551,6 +563,129 @@ mdr_status mdr_stage_attend_backward_profiled(const mdr_config* cfg, const void*
   if (!events) return MDR_ERR_INVALID_ARG;
   return backward_core(cfg, q, k, v, sel, out, lse, d_out, dq, dk, dv, workspace, workspace_bytes,
                        (hipEvent_t*)events, stream);
+}
+
+// ---- host self-check of the kernels' index arithmetic
+
+namespace {
+
+struct Checker {
+  char* msg;
+  size_t len;
+  bool ok = true;
+  void fail(const char* what, long long a, long long b) {
+    if (ok && msg && len) snprintf(msg, len, "%s: %lld outside [0, %lld)", what, a, b);
+    ok = false;
+  }
+  // index idx (in elements of esize bytes) must address inside the region of `bytes` bytes
+  void in(const char* what, long long idx, long long n) {
+    if (idx < 0 || idx >= n) fail(what, idx, n);
+  }
+};
+
+size_t region_bytes(const Region* regs, int nr, const void* p) {
+  for (int r = 0; r < nr; ++r)
+    if (regs[r].p == p) return regs[r].bytes;
+  return 0;
+}
+
+}  // namespace
+
+mdr_status mdr_selfcheck_indices(const mdr_config* cfg, char* msg, size_t msg_len) {
+  Shape s;
+  mdr_status st = shape_from_config(cfg, cfg && cfg->width > 0, &s);
+  if (st != MDR_OK) return st;
+  if (msg && msg_len) msg[0] = 0;
+  Region regs[kMaxRegions];
+  int nr = 0;
+  Buffers b;
+  char* const base = (char*)((uintptr_t)1 << 40);  // never dereferenced: only offsets are compared
+  const size_t total = layout(s, base, &b, nullptr, regs, &nr);
+  Checker ck{msg, msg_len};
+  const long long BH = (long long)s.B * s.H;
+  const long long rows = BH * s.S;  // rows of Q, K, V, O
+  // workspace regions: 256-byte aligned, in order, inside the workspace
+  for (int r = 0; r < nr; ++r) {
+    const long long o = (long long)(regs[r].p - base);
+    if (o % 256) ck.fail("region alignment", o % 256, 1);
+    ck.in("region end", o + (long long)regs[r].bytes - 1, (long long)total);
+    if (r + 1 < nr && o + (long long)regs[r].bytes > (long long)(regs[r + 1].p - base))
+      ck.fail("region overlap", o + (long long)regs[r].bytes, (long long)(regs[r + 1].p - base));
+  }
+  const bool remote = s.R > 0 && s.ne > 0;
+  if (remote) {
+    const long long n_items = (long long)(region_bytes(regs, nr, b.items) / 4);
+    const long long n_phist = (long long)(region_bytes(regs, nr, b.phist) / 4);
+    const long long n_plse = (long long)(region_bytes(regs, nr, b.part_lse) / 4);
+    const long long n_po = (long long)(region_bytes(regs, nr, b.part_o) / (s.dtype == MDR_BF16 ? 2 : 4));
+    const long long n_poff = (long long)(region_bytes(regs, nr, b.poff) / 4);
+    // remote kernel: every work-group id maps to one (b,h, item) or to none; every item is covered once
+    const long long grid = remote_grid(s);
+    char* seen = (char*)calloc((size_t)(BH * s.max_items), 1);
+    if (!seen) return MDR_ERR_UNSUPPORTED;
+    for (long long id = 0; id < grid && ck.ok; ++id) {
+      int bh, k;
+      remote_work_of(s, id, &bh, &k);
+      if (bh >= BH) continue;
+      ck.in("remote item", k, s.max_items);
+      ck.in("remote (b,h)", bh, BH);
+      if (!ck.ok) break;
+      if (seen[(size_t)bh * s.max_items + k]++) ck.fail("remote item mapped twice", k, s.max_items);
+      ck.in("item record", (long long)(item_record(s, bh, k) + kItemInts - 1), n_items);
+      // any block the item may name, any pair id it may hold
+      ck.in("remote K/V row", (long long)(block_row(s, bh, s.ne - 1) + s.blk - 1), rows);
+      ck.in("partial normaliser", (long long)partial_index(s, bh, s.S * s.R - 1), n_plse);
+      ck.in("partial row", (long long)(partial_index(s, bh, s.S * s.R - 1) * s.D + s.D - 1), n_po);
+    }
+    for (long long x = 0; x < BH * s.max_items && ck.ok; ++x)
+      if (!seen[x]) ck.fail("remote item never run", x, BH * s.max_items);
+    free(seen);
+    // pair counts: probe (256- and 128-token work-groups), count and scatter work-groups
+    for (int bh = 0; bh < BH && ck.ok; ++bh) {
+      for (int t0 = 0; t0 < s.S; t0 += kProbeThreads) ck.in("pair counts row", (long long)(pair_counts_row(s, bh, t0) + s.ne - 1), n_phist);
+      for (int g = 0; g < s.ng; ++g) {
+        ck.in("scatter range", (long long)g * s.tbin, s.S);
+        ck.in("scatter counts row", (long long)(pair_counts_row(s, bh, g * s.tbin) + s.ne - 1), n_phist);
+      }
+      ck.in("block offsets", (long long)bh * (s.ne + 1) + s.ne, n_poff);
+    }
+    // item slots under extreme count distributions of one (b,h): every pair in one block, one pair per
+    // block with the rest in the last, and an even spread
+    const long long pairs = (long long)s.S * s.R;
+    for (int dist = 0; dist < 3 && ck.ok; ++dist) {
+      long long istart = 0;
+      for (int i = 0; i < s.ne && ck.ok; ++i) {
+        long long cnt = dist == 0 ? (i == s.ne - 1 ? pairs : 0)
+                        : dist == 1 ? (i == s.ne - 1 ? pairs - (s.ne - 1) : 1)
+                                    : pairs / s.ne + (i < pairs % s.ne ? 1 : 0);
+        if (cnt < 0) cnt = 0;
+        const long long ni = (cnt + kItemPairs - 1) / kItemPairs;
+        if (ni > 0) {
+          ck.in("work items of a block", istart + ni - 1, s.max_items);
+          ck.in("item pair slot", (long long)item_pair_slot(s, (int)BH - 1, (int)istart, (int)cnt - 1), n_items);
+        }
+        istart += ni;
+      }
+    }
+  }
+  // query-block kernels (local attention, backward dQ): a bijection onto (b,h, j), windows inside
+  {
+    const int n = (int)(BH * s.nb);
+    char* seen = (char*)calloc((size_t)n, 1);
+    if (!seen) return MDR_ERR_UNSUPPORTED;
+    for (int id = 0; id < n && ck.ok; ++id) {
+      int bh, j;
+      query_block_of(s, id, n, &bh, &j);
+      ck.in("query block", (long long)bh * s.nb + j, n);
+      if (!ck.ok) break;
+      if (seen[(size_t)bh * s.nb + j]++) ck.fail("query block mapped twice", j, s.nb);
+      const int j0 = j - s.L + 1 > 0 ? j - s.L + 1 : 0;
+      ck.in("local window first row", (long long)block_row(s, bh, j0), rows);
+      ck.in("local window last row", (long long)(block_row(s, bh, j) + s.blk - 1), rows);
+    }
+    free(seen);
+  }
+  return ck.ok ? MDR_OK : MDR_ERR_INVALID_ARG;
 }
 
 // ---- streaming decode

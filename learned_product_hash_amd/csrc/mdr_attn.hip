@@ -60,22 +60,13 @@ __global__ __launch_bounds__(kRemoteWaves * 64) void k_attn_remote(const T* __re
   extern __shared__ __align__(16) char lds_raw[];
   T* Ks = (T*)lds_raw;
   T* Vx = Ks + TL::K_ELEMS;
-  // work item k of (b,h); pinned: work-group ids cycle over the XCDs, so (b,h) = id % 8 + 8 (...) keeps
-  // every item of one (b,h) on one XCD
-  const int id = blockIdx.x;
+  // work item k of (b,h) (its items on one XCD when pinned)
   int bh, k;
-  if (s.pin) {
-    const int m = id / kXcds;
-    bh = id % kXcds + kXcds * (m / s.max_items);
-    k = m % s.max_items;
-  } else {
-    bh = id / s.max_items;
-    k = id % s.max_items;
-  }
+  remote_work_of(s, blockIdx.x, &bh, &k);
   if (bh >= s.B * s.H) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int e = wave * 16 + (lane & 15);
-  const int32_t* rec = items + ((size_t)bh * s.max_items + k) * kItemInts;
+  const int32_t* rec = items + item_record(s, bh, k);
   const int hdr = rec[0];
   int pid = rec[kItemHead + e];
   if (hdr < 0) return;  // past the last item (uniform for the work-group)
@@ -83,7 +74,7 @@ __global__ __launch_bounds__(kRemoteWaves * 64) void k_attn_remote(const T* __re
   if (e >= n || (unsigned)pid >= (unsigned)(s.S * s.R)) pid = -1;  // only ids of this (b,h) are ever gathered
   const size_t rowbase = (size_t)bh * s.S;
   KVRegs<T, D, BLK, NTHR> kv;
-  kv.load(K + (rowbase + (size_t)i * BLK) * D, V + (rowbase + (size_t)i * BLK) * D, tid);
+  kv.load(K + block_row(s, bh, i) * D, V + block_row(s, bh, i) * D, tid);
   QFrag<T, D> qf;
   load_q<T, D>(qf, Q + (rowbase + (pid < 0 ? 0 : pid / s.R)) * D, lane);
   kv.store(Ks, Vx, tid);
@@ -114,7 +105,7 @@ __global__ __launch_bounds__(kRemoteWaves * 64) void k_attn_remote(const T* __re
   for (int dt = 0; dt < TL::ND; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   pv_block<T, D, BLK>(o, p, Vx, lane);
   if (pid >= 0) {
-    const size_t pr = rowbase * s.R + pid;  // the pair (token, slot)
+    const size_t pr = partial_index(s, bh, pid);  // the pair (token, slot)
     const float inv = 1.f / sum;
 #pragma unroll
     for (int dt = 0; dt < TL::ND; ++dt) store4<T>(part_o + pr * D + 16 * dt + 4 * (lane >> 4), o[dt], inv);
@@ -142,8 +133,8 @@ __global__ __launch_bounds__(BLK * 4) __attribute__((amdgpu_waves_per_eu(local_m
   extern __shared__ __align__(16) char lds_raw[];
   T* Ks = (T*)lds_raw;
   T* Vx = Ks + TL::K_ELEMS;
-  const int wg = xcd_chunked(blockIdx.x, gridDim.x);  // query blocks of one head in order per XCD
-  const int j = wg % s.nb, bh = wg / s.nb;
+  int j, bh;
+  query_block_of(s, blockIdx.x, gridDim.x, &bh, &j);  // query blocks of one head in order per XCD
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int qi = wave * 16 + (lane & 15);
   const int t = j * BLK + qi;
@@ -281,8 +272,7 @@ hipError_t attend_impl(const Shape& s, const void* q, const void* k, const void*
     if (rl > 65536 && (e = hipFuncSetAttribute((const void*)k_attn_remote<T, D, BLK>,
                                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)rl)) != hipSuccess)
       return e;
-    const long long bh_pad = s.pin ? ((long long)s.B * s.H + kXcds - 1) / kXcds * kXcds : (long long)s.B * s.H;
-    hipLaunchKernelGGL((k_attn_remote<T, D, BLK>), dim3((unsigned)(bh_pad * s.max_items)), dim3(kRemoteWaves * 64),
+    hipLaunchKernelGGL((k_attn_remote<T, D, BLK>), dim3((unsigned)remote_grid(s)), dim3(kRemoteWaves * 64),
                        rl, st, (const T*)q, (const T*)k, (const T*)v, b.items, (T*)b.part_o, b.part_lse, s);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }

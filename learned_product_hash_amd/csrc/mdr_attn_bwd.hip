@@ -111,7 +111,7 @@ __global__ __launch_bounds__(BLK * 4) __attribute__((amdgpu_waves_per_eu(kv_min_
     npair = po[1] - po[0];
     it0 = ioff[(size_t)bh * (s.ne + 1) + i];
   }
-  const int32_t* recs = items + ((size_t)bh * s.max_items + it0) * kItemInts;
+  const int32_t* recs = items + item_record(s, bh, it0);
   {
     KVRegs<T, D, BLK, NTHR> kv;
     kv.load(K + (rowbase + (size_t)i * BLK) * D, V + (rowbase + (size_t)i * BLK) * D, tid);
@@ -282,8 +282,8 @@ __global__ __launch_bounds__(BLK * 4) void k_bwd_q(const T* __restrict__ Q, cons
   extern __shared__ __align__(16) char lds_raw[];
   T* Ks = (T*)lds_raw;
   T* Vs = Ks + TL::K_ELEMS;
-  const int wg = xcd_chunked(blockIdx.x, gridDim.x);  // query blocks of one head in order per XCD
-  const int j = wg % s.nb, bh = wg / s.nb;
+  int j, bh;
+  query_block_of(s, blockIdx.x, gridDim.x, &bh, &j);  // query blocks of one head in order per XCD
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int qi = wave * 16 + (lane & 15);
   const int t = j * BLK + qi;

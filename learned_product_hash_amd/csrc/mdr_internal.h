@@ -117,11 +117,70 @@ __device__ inline bool sel_entry_valid(const int32_t* row, int r, int j, int L) 
   return true;
 }
 
+// Work-groups are handed to the 8 XCDs of the chip in turn (linear id mod 8), and each XCD has its
+// own L2.  xcd_chunked(id, n) renumbers the n work-groups of a 1-D grid so that each XCD receives a
+// contiguous run of logical indices, in order: neighbours that share data (adjacent query blocks
+// reading the same K/V block) then run on the same XCD at about the same time.  A bijection on
+// [0, n) for any n.
+constexpr int kXcds = 8;
+__host__ __device__ inline int xcd_chunked(int id, int n) {
+  const int x = id % kXcds, k = id / kXcds;
+  const int q = n / kXcds, r = n % kXcds;
+  return x * q + (x < r ? x : r) + k;
+}
+
+// ---- index arithmetic shared by the kernels and the host self-check (mdr_selfcheck_indices), which
+// runs these same functions over every launch index of a configuration and checks each result
+// against the buffer it addresses.
+
+// The remote kernel's work-group id -> (b,h, work item).  Pinned: ids cycle over the XCDs, so
+// (b,h) = id % 8 + 8 (id / 8 / max_items) keeps every item of one (b,h) on one XCD.  bh >= B H: no work.
+__host__ __device__ inline void remote_work_of(const Shape& s, long long id, int* bh, int* k) {
+  if (s.pin) {
+    const long long m = id / kXcds;
+    *bh = (int)(id % kXcds + kXcds * (m / s.max_items));
+    *k = (int)(m % s.max_items);
+  } else {
+    *bh = (int)(id / s.max_items);
+    *k = (int)(id % s.max_items);
+  }
+}
+__host__ __device__ inline long long remote_grid(const Shape& s) {
+  const long long bh = (long long)s.B * s.H;
+  return (s.pin ? (bh + kXcds - 1) / kXcds * kXcds : bh) * s.max_items;
+}
+// First int of work item k's record of (b,h); pair slot of the pos-th pair of a block whose first item
+// is istart.
+__host__ __device__ inline size_t item_record(const Shape& s, int bh, int k) {
+  return ((size_t)bh * s.max_items + k) * kItemInts;
+}
+__host__ __device__ inline size_t item_pair_slot(const Shape& s, int bh, int istart, int pos) {
+  return item_record(s, bh, istart + pos / kItemPairs) + kItemHead + pos % kItemPairs;
+}
+// Row of pair counts of the token range holding token t0, of (b,h).
+__host__ __device__ inline size_t pair_counts_row(const Shape& s, int bh, int t0) {
+  return ((size_t)bh * s.ng + t0 / s.tbin) * s.ne;
+}
+// First key row of block i of (b,h); the (token, slot) pair pid's partial (times D for its output row).
+__host__ __device__ inline size_t block_row(const Shape& s, int bh, int i) {
+  return (size_t)bh * s.S + (size_t)i * s.blk;
+}
+__host__ __device__ inline size_t partial_index(const Shape& s, int bh, int pid) {
+  return (size_t)bh * s.S * s.R + pid;
+}
+// The query-block kernels' work-group id -> ((b,h), query block j), query blocks of one head in order
+// per XCD.
+__host__ __device__ inline void query_block_of(const Shape& s, int id, int n, int* bh, int* j) {
+  const int wg = xcd_chunked(id, n);
+  *j = wg % s.nb;
+  *bh = wg / s.nb;
+}
+
 // Pair binning.  The counters phist are cleared column by column: the work-group that summarises block
 // i clears entry i of every token range of its (b,h).
 __device__ inline void clear_pair_counts(int32_t* phist, const Shape& s, int bh, int i, int tid, int nthreads) {
   if (i >= s.ne) return;
-  int32_t* col = phist + (size_t)bh * s.ng * s.ne + i;
+  int32_t* col = phist + pair_counts_row(s, bh, 0) + i;
   for (int g = tid; g < s.ng; g += nthreads) col[(size_t)g * s.ne] = 0;
 }
 
@@ -155,18 +214,6 @@ struct PairCounter {
       }
   }
 };
-
-// Work-groups are handed to the 8 XCDs of the chip in turn (linear id mod 8), and each XCD has its
-// own L2.  xcd_chunked(id, n) renumbers the n work-groups of a 1-D grid so that each XCD receives a
-// contiguous run of logical indices, in order: neighbours that share data (adjacent query blocks
-// reading the same K/V block) then run on the same XCD at about the same time.  A bijection on
-// [0, n) for any n.
-constexpr int kXcds = 8;
-__device__ inline int xcd_chunked(int id, int n) {
-  const int x = id % kXcds, k = id / kXcds;
-  const int q = n / kXcds, r = n % kXcds;
-  return x * q + min(x, r) + k;
-}
 
 // Work-group barrier that orders LDS accesses only: global loads still in flight stay in flight
 // across it (the fences are restricted to the local address space).  Used where a barrier

@@ -37,7 +37,7 @@ __global__ __launch_bounds__(kBinThreads) void k_pair_count(const int32_t* __res
   const int bh = blockIdx.y;
   const int t0 = blockIdx.x * kBinThreads;
   const int t = t0 + threadIdx.x;
-  PairCounter<kBinThreads> pc{cnt, phist + ((size_t)bh * s.ng + t0 / s.tbin) * s.ne, s.ne};
+  PairCounter<kBinThreads> pc{cnt, phist + pair_counts_row(s, bh, t0), s.ne};
   pc.begin();
   if (t < s.S) {
     const int j = t / s.blk;
@@ -77,7 +77,7 @@ __global__ __launch_bounds__(kScatterThreads) void k_pair_scatter(const int32_t*
     }
   };
   load_piece(tfirst);
-  const int32_t* ph = phist + (size_t)bh * s.ng * ne;
+  const int32_t* ph = phist + pair_counts_row(s, bh, 0);
   for (int i = tid; i < ne; i += kScatterThreads) {
     int v[kMaxBinRanges];  // every range's count requested at once
 #pragma unroll
@@ -105,7 +105,7 @@ __global__ __launch_bounds__(kScatterThreads) void k_pair_scatter(const int32_t*
   int irun = block_exclusive_scan<kScatterThreads>(isum, scan_tmp, &itot);
   int32_t* po = poff + (size_t)bh * (ne + 1);
   int32_t* io = ioff + (size_t)bh * (ne + 1);
-  int32_t* it = items + (size_t)bh * s.max_items * kItemInts;
+  int32_t* it = items + item_record(s, bh, 0);
   for (int a = a0; a < a1; ++a) {
     const int tot = start[a];
     const int ni = (tot + kItemPairs - 1) / kItemPairs;
@@ -188,9 +188,8 @@ __global__ __launch_bounds__(kScatterThreads) void k_pair_scatter(const int32_t*
           const int count = __popcll(same);
           const int cur = cw[i];
           const int pos = cur + rank - start[i];  // the pair's place in block i's list
-          const int rec = istart[i] + pos / kItemPairs;
-          if (pos >= 0 && rec < s.max_items)
-            it[(size_t)rec * kItemInts + kItemHead + pos % kItemPairs] = t0 * s.R + p;
+          if (pos >= 0 && istart[i] + pos / kItemPairs < s.max_items)
+            items[item_pair_slot(s, bh, istart[i], pos)] = t0 * s.R + p;
           __builtin_amdgcn_wave_barrier();
           if (rank == count - 1) cw[i] = cur + count;
         }

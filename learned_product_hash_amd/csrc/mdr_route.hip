@@ -545,7 +545,7 @@ __global__ __launch_bounds__(kProbeThreads) void k_probe_rerank(
   if (!phist) return;  // uniform
   // ---- count the selected pairs of this work-group's token range per remote block (LDS histogram in the
   // place of mu when it fits)
-  PairCounter<NT> pc{s.ne <= NT * MST ? (int*)mu : nullptr, phist + ((size_t)bh * s.ng + tbase / s.tbin) * s.ne,
+  PairCounter<NT> pc{s.ne <= NT * MST ? (int*)mu : nullptr, phist + pair_counts_row(s, bh, tbase),
                      s.ne};
   pc.begin();
   for (int r = 0; r < nr; ++r) pc.add(tri[r * NT + tid]);
@@ -1291,7 +1291,7 @@ __global__ __launch_bounds__(kProbeFixedThreads) __attribute__((amdgpu_waves_per
   if (!phist) return;  // uniform
   // ---- count the selected pairs of this work-group's token range per remote block (LDS histogram in the
   // place of mu when it fits)
-  PairCounter<NT> pc{s.ne <= NT * MST ? (int*)mu : nullptr, phist + ((size_t)bh * s.ng + tbase / s.tbin) * s.ne,
+  PairCounter<NT> pc{s.ne <= NT * MST ? (int*)mu : nullptr, phist + pair_counts_row(s, bh, tbase),
                      s.ne};
   pc.begin();
   if (active) {
