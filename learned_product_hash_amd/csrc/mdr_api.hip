@@ -640,9 +640,9 @@ mdr_status mdr_selfcheck_indices(const mdr_config* cfg, char* msg, size_t msg_le
     for (long long x = 0; x < BH * s.max_items && ck.ok; ++x)
       if (!seen[x]) ck.fail("remote item never run", x, BH * s.max_items);
     free(seen);
-    // pair counts: probe (256- and 128-token work-groups), count and scatter work-groups
+    // pair counts: probe (every 64-token group: 256-, 128- or 64-token work-groups), count and scatter work-groups
     for (int bh = 0; bh < BH && ck.ok; ++bh) {
-      for (int t0 = 0; t0 < s.S; t0 += kProbeThreads) ck.in("pair counts row", (long long)(pair_counts_row(s, bh, t0) + s.ne - 1), n_phist);
+      for (int t0 = 0; t0 < s.S; t0 += 64) ck.in("pair counts row", (long long)(pair_counts_row(s, bh, t0) + s.ne - 1), n_phist);
       for (int g = 0; g < s.ng; ++g) {
         ck.in("scatter range", (long long)g * s.tbin, s.S);
         ck.in("scatter counts row", (long long)(pair_counts_row(s, bh, g * s.tbin) + s.ne - 1), n_phist);

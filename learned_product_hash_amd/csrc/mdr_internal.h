@@ -123,6 +123,7 @@ __device__ inline bool sel_entry_valid(const int32_t* row, int r, int j, int L) 
 // reading the same K/V block) then run on the same XCD at about the same time.  A bijection on
 // [0, n) for any n.
 constexpr int kXcds = 8;
+constexpr int kCUs = 256;  // compute units of the chip (32 per XCD)
 __host__ __device__ inline int xcd_chunked(int id, int n) {
   const int x = id % kXcds, k = id / kXcds;
   const int q = n / kXcds, r = n % kXcds;
@@ -286,7 +287,10 @@ hipError_t launch_post_redirect(const Shape& s, const int32_t* addr, const int32
                                 int32_t* overflow, hipStream_t st);
 // True when launch_probe_rerank accepts `fuse` for this shape (the compile-time specialised probe).
 bool probe_fuses_post(const Shape& s);
-size_t probe_lds_bytes(const Shape& s);
+bool probe_fuses_post_nt(const Shape& s, int nt);
+// Query tokens per work-group of the routing path's probe (256, or 128 / 64 on small grids).
+int probe_fixed_tokens(const Shape& s);
+size_t probe_lds_bytes(const Shape& s, int nt = kProbeFixedThreads);
 // Decode: file blocks [filed, target) of every (b,h) (summarising those not summarised yet), then
 // route and attend tokens pos .. pos + n_new - 1 (one query block).
 hipError_t launch_ring_reset(int32_t* ring, long long records, int cap, hipStream_t st);

@@ -809,14 +809,13 @@ constexpr int probe_min_waves(int bytes, int D, int C) { return bytes == 2 && D 
 
 constexpr int cpow(int b, int e) { return e == 0 ? 1 : b * cpow(b, e - 1); }
 
-template <typename T, int D, int G, int C, int P, int R, bool FUSED, bool DIAG>
-__global__ __launch_bounds__(kProbeFixedThreads) __attribute__((amdgpu_waves_per_eu(probe_min_waves((int)sizeof(T), D, C)))) void k_probe_fixed(
+template <typename T, int D, int G, int C, int P, int R, bool FUSED, bool DIAG, int NT>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(probe_min_waves((int)sizeof(T), D, C)))) void k_probe_fixed(
     const T* __restrict__ Q, const float* __restrict__ cb, const float* __restrict__ bias,
     const float* __restrict__ ksum, const int32_t* __restrict__ off, const int32_t* __restrict__ idx,
     const int32_t* __restrict__ force, int32_t* __restrict__ sel, int32_t* __restrict__ ncand,
     int32_t* __restrict__ phist, FusedPost fp, ProbeExtra ex, Shape s) {
-  constexpr int NT = kProbeFixedThreads;
-  static_assert(NT % 64 == 0, "whole waves of 64 tokens");
+  static_assert(NT % 64 == 0 && NT <= kProbeFixedThreads, "whole waves of 64 tokens");
   constexpr bool BF = std::is_same<T, bf16>::value;
   constexpr int CP = (C + 15) & ~15;
   constexpr int MST = G * CP + 1;  // odd stride: each lane's row starts in its own bank
@@ -1323,21 +1322,41 @@ hipError_t address_dispatch(const Shape& s, const void* k, const float* cb, cons
   return hipGetLastError();
 }
 
+template <typename T, int D, int G, int C, int P, int R, bool FUSED, bool DIAG, int NT>
+hipError_t probe_fixed_launch_nt(const Shape& s, const void* q, const float* cb, const float* bias, const float* ksum,
+                                 const int32_t* off, const int32_t* idx, const int32_t* force, int32_t* sel,
+                                 int32_t* ncand, int32_t* phist, const FusedPost& fp,
+                                 const ProbeExtra& ex, hipStream_t st) {
+  dim3 grid((s.S + NT - 1) / NT, s.B * s.H);
+  const size_t lds = probe_lds_bytes(s, NT);
+  if (lds > 65536) {
+    hipError_t e = hipFuncSetAttribute((const void*)k_probe_fixed<T, D, G, C, P, R, FUSED, DIAG, NT>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((k_probe_fixed<T, D, G, C, P, R, FUSED, DIAG, NT>), grid, dim3(NT), lds, st, (const T*)q, cb,
+                     bias, ksum, off, idx, force, sel, ncand, phist, fp, ex, s);
+  return hipGetLastError();
+}
+
+// The routing path's probe (lists built in the kernel, no diagnostics) also comes with 128- and 64-token
+// work-groups, for grids that 256-token groups would leave short of two per CU; the others keep 256.
 template <typename T, int D, int G, int C, int P, int R, bool FUSED, bool DIAG>
 hipError_t probe_fixed_launch_t(const Shape& s, const void* q, const float* cb, const float* bias, const float* ksum,
                                 const int32_t* off, const int32_t* idx, const int32_t* force, int32_t* sel,
                                 int32_t* ncand, int32_t* phist, const FusedPost& fp,
                                 const ProbeExtra& ex, hipStream_t st) {
-  dim3 grid((s.S + kProbeFixedThreads - 1) / kProbeFixedThreads, s.B * s.H);
-  const size_t lds = probe_lds_bytes(s);
-  if (lds > 65536) {
-    hipError_t e = hipFuncSetAttribute((const void*)k_probe_fixed<T, D, G, C, P, R, FUSED, DIAG>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
+  if constexpr (FUSED && !DIAG) {
+    const int nt = probe_fixed_tokens(s);
+    if (nt == 64)
+      return probe_fixed_launch_nt<T, D, G, C, P, R, FUSED, DIAG, 64>(s, q, cb, bias, ksum, off, idx, force, sel,
+                                                                      ncand, phist, fp, ex, st);
+    if (nt == 128)
+      return probe_fixed_launch_nt<T, D, G, C, P, R, FUSED, DIAG, 128>(s, q, cb, bias, ksum, off, idx, force, sel,
+                                                                       ncand, phist, fp, ex, st);
   }
-  hipLaunchKernelGGL((k_probe_fixed<T, D, G, C, P, R, FUSED, DIAG>), grid, dim3(kProbeFixedThreads), lds, st, (const T*)q, cb,
-                     bias, ksum, off, idx, force, sel, ncand, phist, fp, ex, s);
-  return hipGetLastError();
+  return probe_fixed_launch_nt<T, D, G, C, P, R, FUSED, DIAG, kProbeFixedThreads>(
+      s, q, cb, bias, ksum, off, idx, force, sel, ncand, phist, fp, ex, st);
 }
 
 template <typename T, int D, int G, int C, int P, int R>
@@ -1379,7 +1398,7 @@ hipError_t probe_dispatch(const Shape& s, const void* q, const float* cb, const 
 #undef MDR_FIXED
   if (fuse) return hipErrorInvalidValue;  // only the specialised probe builds the lists itself
   dim3 grid((s.S + kProbeThreads - 1) / kProbeThreads, s.B * s.H);
-  const size_t lds = probe_lds_bytes(s);
+  const size_t lds = probe_lds_bytes(s, kProbeThreads);
   const void* fn = nullptr;
   switch (s.D) {
     case 32: fn = (const void*)k_probe_rerank<T, 32>; break;
@@ -1430,11 +1449,11 @@ bool probe_fixed_shape(const Shape& s) {
   return false;
 }
 
-size_t probe_lds_bytes(const Shape& s) {
+size_t probe_lds_bytes(const Shape& s, int nt) {
   const int CP = (s.C + 15) & ~15;
   if (s.fixed_probe) {
     // mu rows during the logits, then the work-group's candidate list (block ids and scores)
-    const size_t mu_w = (size_t)kProbeFixedThreads * (s.G * CP + 1), pairs_w = (size_t)kProbeFixedThreads * s.M * 2;
+    const size_t mu_w = (size_t)nt * (s.G * CP + 1), pairs_w = (size_t)nt * s.M * 2;
     return ((mu_w > pairs_w ? mu_w : pairs_w) + (s.csr_lds ? (size_t)(s.A + 1 + s.ne) : 0)) * 4;
   }
   const int Pg = s.P + 1 < s.C ? s.P + 1 : s.C;  // laid out for the diagnostics sizes (P + 1, R + 1)
@@ -1474,10 +1493,19 @@ hipError_t launch_post_redirect(const Shape& s, const int32_t* addr, const int32
   return hipGetLastError();
 }
 
-bool probe_fuses_post(const Shape& s) {
+bool probe_fuses_post(const Shape& s) { return probe_fuses_post_nt(s, kProbeFixedThreads); }
+
+bool probe_fuses_post_nt(const Shape& s, int nt) {
   // the fixed probe stages the addresses and list cursors in its mu region
   const int CP = (s.C + 15) & ~15;
-  return s.fixed_probe && (long long)s.ne + s.A <= (long long)kProbeFixedThreads * (s.G * CP + 1);
+  return s.fixed_probe && (long long)s.ne + s.A <= (long long)nt * (s.G * CP + 1);
+}
+
+int probe_fixed_tokens(const Shape& s) {
+  int nt = kProbeFixedThreads;
+  while (nt > 64 && (long long)s.B * s.H * ((s.S + nt - 1) / nt) < 2LL * kCUs && probe_fuses_post_nt(s, nt / 2))
+    nt /= 2;
+  return nt;
 }
 
 }  // namespace mdr

@@ -177,12 +177,13 @@ def test_routed_attention_end_to_end(gpu_lib, name):
     assert err <= TOL[w.dtype]
 
 
-@pytest.mark.parametrize("name", NAMES)
-def test_diagnostics_leave_routing_unchanged(gpu_lib, name):
-    """Asking for the routing diagnostics runs the probe with one more address and candidate ranked;
-    every other output must be bit-identical to the run without them."""
+@pytest.mark.parametrize("name,over", [(n, {}) for n in NAMES] + [("sweep", dict(seq=8192))])
+def test_diagnostics_leave_routing_unchanged(gpu_lib, name, over):
+    """Asking for the routing diagnostics runs the probe with one more address and candidate ranked, in
+    256-token work-groups; without them small grids take 64-token (the test sizes) or 128-token (sweep
+    at 8K) work-groups.  Every other output must be bit-identical between the two runs."""
     mdr = gpu_lib
-    w = small(name)
+    w = small(name, **over)
     inp = synth.make_core_inputs(w, 5)
     a = run_core(mdr, w, inp, force=inp.get("force"), diag=False)
     b = run_core(mdr, w, inp, force=inp.get("force"), diag=True)
