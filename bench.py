@@ -69,9 +69,9 @@ BACKWARD_SYMBOL = {  # the backward's binning also runs k_pair_scatter, listed w
 CALIB_BYTES = 512 << 20
 HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000  # hipEventDisableSystemFence (hip_runtime_api.h)
 PMC_COMMANDS = [  # run from the repository root on one MI355X, TMPDIR=/tmp
-    "rocprofv3 --pmc FETCH_SIZE --output-format csv -d rocprof_out/pmcf -o f -- "
+    "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmcf -o f -- "
     "python3 bench.py --steps 3 --warmup 1 --calib-copy --no-cpu --no-sweep --no-decode --no-backward --no-stress --no-mixer --no-cold",
-    "rocprofv3 --pmc WRITE_SIZE --output-format csv -d rocprof_out/pmcw -o w -- "
+    "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmcw -o w -- "
     "python3 bench.py --steps 3 --warmup 1 --calib-copy --no-cpu --no-sweep --no-decode --no-backward --no-stress --no-mixer --no-cold",
 ]
 

@@ -254,9 +254,9 @@ bool routing_aligned(const mdr_routing* r) {
   return !r || aligned16(r->ksum);
 }
 
-// The four stages of the core on post-RoPE q, k, v already in device memory.
+// The stages of the core on post-RoPE q, k, v already in device memory.
 // ev (optional, MDR_CORE_KERNELS + 1 entries): recorded before each kernel and after the last.
-// have_address: the summaries, addresses (and alternates) and cleared cell counters are already in
+// have_address: the summaries, addresses (and alternates) and cleared pair counts are already in
 // the buffers (the mixer's fused projection wrote them).
 mdr_status run_core(const Shape& s, const void* q, const void* k, const void* v, const float* cb, const float* bias,
                     const int32_t* force, void* out, const Buffers& b, hipStream_t st, hipEvent_t* ev = nullptr,

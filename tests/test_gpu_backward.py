@@ -129,16 +129,16 @@ def test_backward_random_selection(gpu_lib, name, over):
 
 
 def test_backward_every_token_selects_one_block(gpu_lib):
-    """Full cells: every token selects block 0 (and block 1), so each cell of those blocks holds a
-    whole query block of pairs, and block 0 has more cells than one scan of the kernel covers."""
+    """Every token selects block 0 (and block 1): those blocks' pair lists hold a pair of nearly every
+    token and span many work items."""
     mdr = gpu_lib
-    w = small("tiny", seq=8192)  # 256 blocks of 32: 254 cells for block 0, scanned 128 at a time
+    w = small("tiny", seq=8192)  # 256 blocks of 32: about 8,100 pairs for block 0, 64 work items
     inp = synth.make_core_inputs(w, 2)
     sel = np.zeros((1, 1, w.seq, w.remote), dtype=np.int32)
     sel[..., 1] = 1
     d_out = synth.make_grad_inputs(w, 2)
     out, lse, (grads,) = run_backward(mdr, w, inp, sel, d_out)
-    print(f"full cells: worst relative errors {check(w, inp, sel, d_out, out, lse, grads, packed=True)}")
+    print(f"one hot block: worst relative errors {check(w, inp, sel, d_out, out, lse, grads, packed=True)}")
 
 
 @pytest.mark.parametrize("over", [dict(remote=0), dict(seq=64)])

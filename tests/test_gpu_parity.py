@@ -404,9 +404,8 @@ def hot_block_selection(w, seed):
 
 @pytest.mark.parametrize("name", ["sweep", "long"])
 def test_stage_attend_hot_block(gpu_lib, name):
-    """A block that every eligible token selects: its pairs outnumber the remote kernel's LDS pair list
-    (the rest are found by the cell prefix), and each of its cells is full (slots past the dense table
-    are read from the cell rows)."""
+    """A block that every eligible token selects: its pair list spans many work items of the remote
+    kernel, while the other slots spread over random blocks with short lists."""
     mdr = gpu_lib
     w = small(name)
     inp = synth.make_core_inputs(w, 7)
