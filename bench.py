@@ -458,8 +458,9 @@ def exponent_sweep(mdr, seqs, seed):
     slope_work = float(np.polyfit(np.log([r["attended"] for r in rows]), lt, 1)[0])
     return dict(seqs=[r["seq"] for r in rows], ms=[round(r["ms"], 4) for r in rows],
                 R_eff=[round(r["R_eff"], 3) for r in rows], overflow=[r["overflow"] for r in rows],
-                attended_pairs=[r["attended"] for r in rows], slope_vs_seq=round(slope, 3),
-                slope_vs_attended_pairs=round(slope_work, 3),
+                attended_pairs=[r["attended"] for r in rows],
+                ps_per_attended_pair=[round(r["ms"] * 1e9 / r["attended"], 2) for r in rows],
+                slope_vs_seq=round(slope, 3), slope_vs_attended_pairs=round(slope_work, 3),
                 note="context only: the pages report 0.993 for their packed CPU routing over 4K-32K "
                      "(fixed, balanced setup; CPU hardware not stated)")
 

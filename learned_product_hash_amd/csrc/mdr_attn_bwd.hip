@@ -22,6 +22,8 @@
 #include "mdr_internal.h"
 #include "mdr_tiles.h"
 
+#include <type_traits>
+
 namespace mdr {
 namespace {
 
@@ -208,27 +210,39 @@ __global__ __launch_bounds__(BLK * 4) __attribute__((amdgpu_waves_per_eu(kv_min_
       const int* pk = mpair + cur * EC;
       const float* lk = mlse + cur * EC;
       const float* dk_ = mdd + cur * EC;
-      // ---- dV, dK of this wave's keys, entries as rows: lane (key r16) holds entries 16rt + 4s4 + k
+      // ---- dV, dK of this wave's keys, entries as rows: lane (key r16) holds entries 16rt + 4s4 + k.
+      // Only entries below BLK (the tokens of query block i) can precede a key of block i; every later
+      // entry is a later token, and an unused entry (token -1) has zero query and gradient rows and a
+      // zero normaliser and row dot, so whatever weight it gets it adds exactly zero.  The causal test
+      // is therefore made only in chunks that hold entries below BLK.
+      auto products = [&](auto masked_tag) __attribute__((always_inline)) {
+        constexpr bool MASKED = decltype(masked_tag)::value;
 #pragma unroll
-      for (int h = 0; h < EC / SUB; ++h) {
-        const T* qh = Qs + h * SUB * TL::KST;
-        const T* gh = dOs + h * SUB * TL::KST;
-        f32x4 p[SUB / 16], ds[SUB / 16];
+        for (int h = 0; h < EC / SUB; ++h) {
+          const T* qh = Qs + h * SUB * TL::KST;
+          const T* gh = dOs + h * SUB * TL::KST;
+          f32x4 p[SUB / 16], ds[SUB / 16];
 #pragma unroll
-        for (int rt = 0; rt < SUB / 16; ++rt) {
-          const f32x4 sc = score_tile<T, D, SUB>(kf, qh, rt, lane);
-          const f32x4 dp = score_tile<T, D, SUB>(vf, gh, rt, lane);
+          for (int rt = 0; rt < SUB / 16; ++rt) {
+            const f32x4 sc = score_tile<T, D, SUB>(kf, qh, rt, lane);
+            const f32x4 dp = score_tile<T, D, SUB>(vf, gh, rt, lane);
 #pragma unroll
-          for (int kk = 0; kk < 4; ++kk) {
-            const int e = h * SUB + 16 * rt + 4 * s4 + kk;
-            const float pv = tk[e] >= key_tok ? fast_exp2(fmaf(sc[kk], c, -lk[e])) : 0.f;
-            p[rt][kk] = pv;
-            ds[rt][kk] = pv * (dp[kk] - dk_[e]);
+            for (int kk = 0; kk < 4; ++kk) {
+              const int e = h * SUB + 16 * rt + 4 * s4 + kk;
+              const float ex = fast_exp2(fmaf(sc[kk], c, -lk[e]));
+              const float pv = !MASKED || tk[e] >= key_tok ? ex : 0.f;
+              p[rt][kk] = pv;
+              ds[rt][kk] = pv * (dp[kk] - dk_[e]);
+            }
           }
+          pv_block<T, D, SUB>(dv, p, gh, lane);
+          pv_block<T, D, SUB>(dk, ds, qh, lane);
         }
-        pv_block<T, D, SUB>(dv, p, gh, lane);
-        pv_block<T, D, SUB>(dk, ds, qh, lane);
-      }
+      };
+      if (k * EC < BLK)
+        products(std::true_type{});
+      else
+        products(std::false_type{});
       // ---- the remote entries' dQ shares, keys as rows: lane (entry 16g + r16) holds keys 16n + 4s4 + k
       for (int g = wave; g < EC / 16; g += NW) {
         const int el = 16 * g + r16;
