@@ -283,10 +283,15 @@ __global__ __launch_bounds__(BLK * 4) __attribute__((amdgpu_waves_per_eu(kv_min_
 }
 
 // One work-group per query block, one wave per 16 of its tokens: dQ over the L local blocks
-// (recomputing P and dS; the next block's K / V read is in flight while the current one is used),
-// scaled, plus the remote blocks' shares in slot order.
-template <typename T, int D, int BLK>
-__global__ __launch_bounds__(BLK * 4) void k_bwd_q(const T* __restrict__ Q, const T* __restrict__ K,
+// (recomputing P and dS; the next block's K / V read is in flight while the current one is used; only
+// the diagonal block needs the causal test), scaled, plus the remote blocks' shares in slot order.  The
+// first RS = min(R, 1) shares are requested at entry with the query and gradient rows (their addresses
+// do not depend on the selection; an unused one is ignored); a second would not fit four waves per SIMD
+// without spilling, and measured no faster.
+constexpr int q_min_waves(int bytes, int D) { return bytes == 2 && D <= 64 ? 4 : 1; }
+
+template <typename T, int D, int BLK, int RS>
+__global__ __launch_bounds__(BLK * 4) __attribute__((amdgpu_waves_per_eu(q_min_waves((int)sizeof(T), D)))) void k_bwd_q(const T* __restrict__ Q, const T* __restrict__ K,
                                                    const T* __restrict__ V, const T* __restrict__ dO,
                                                    const float* __restrict__ lse, const float* __restrict__ Dv,
                                                    const int32_t* __restrict__ sel, const T* __restrict__ dq_part,
@@ -310,11 +315,23 @@ __global__ __launch_bounds__(BLK * 4) void k_bwd_q(const T* __restrict__ Q, cons
   load_q<T, D>(qf, Q + (rowbase + t) * D, lane);
   load_q<T, D>(gf, dO + (rowbase + t) * D, lane);
   const float lt = lse[rowbase + t], dt_ = Dv[rowbase + t];
+  const int32_t* row = sel + (rowbase + t) * s.R;
+  constexpr int RA = RS > 0 ? RS : 1;
+  int sr[RA];
+  Raw4<T> praw[RA][TL::ND];
+#pragma unroll
+  for (int r = 0; r < RS; ++r) {
+    const size_t pr = (rowbase + t) * s.R + r;
+    sr[r] = row[r];
+#pragma unroll
+    for (int dt = 0; dt < TL::ND; ++dt) praw[r][dt] = *(const Raw4<T>*)(dq_part + pr * D + 16 * dt + c4);
+  }
   const float c = s.scale * kLog2e;
   f32x4 dq[TL::ND];
 #pragma unroll
   for (int dt = 0; dt < TL::ND; ++dt) dq[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int jj = j0; jj <= j; ++jj) {
+  auto block_step = [&](auto diag_tag, int jj) __attribute__((always_inline)) {
+    constexpr bool DIAG = decltype(diag_tag)::value;
     if (jj != j0) __syncthreads();  // the previous block is no longer read
     kv.store(Ks, Vs, tid);
     __syncthreads();
@@ -329,18 +346,33 @@ __global__ __launch_bounds__(BLK * 4) void k_bwd_q(const T* __restrict__ Q, cons
       const f32x4 dp = score_tile<T, D, BLK>(gf, Vs, n, lane);
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const bool vis = jj < j || 16 * n + c4 + k <= qi;
-        const float pv = vis ? fast_exp2(fmaf(sc[k], c, -lt)) : 0.f;
+        const float ex = fast_exp2(fmaf(sc[k], c, -lt));
+        const float pv = !DIAG || 16 * n + c4 + k <= qi ? ex : 0.f;
         ds[n][k] = pv * (dp[k] - dt_);
       }
     }
     pv_block<T, D, BLK>(dq, ds, Ks, lane);
+  };
+  if (s.L == 2 && j >= 1) {
+    block_step(std::false_type{}, j - 1);
+    block_step(std::true_type{}, j);
+  } else {
+    for (int jj = j0; jj < j; ++jj) block_step(std::false_type{}, jj);
+    block_step(std::true_type{}, j);
   }
   // the remote shares in slot order (entries used by the forward: 0 <= sel <= j - L, first of a repeat)
-  const int32_t* row = sel + (rowbase + t) * s.R;
 #pragma unroll
   for (int dt = 0; dt < TL::ND; ++dt) dq[dt] *= s.scale;
-  for (int r = 0; r < s.R; ++r) {
+#pragma unroll
+  for (int r = 0; r < RS; ++r) {
+    bool ok = sr[r] >= 0 && sr[r] <= j - s.L;
+#pragma unroll
+    for (int p = 0; p < r; ++p) ok = ok && sr[p] != sr[r];
+    if (ok)
+#pragma unroll
+      for (int dt = 0; dt < TL::ND; ++dt) dq[dt] += unpack4<T>(praw[r][dt]);
+  }
+  for (int r = RS; r < s.R; ++r) {
     if (!sel_entry_valid(row, r, j, s.L)) continue;
     const size_t pr = (rowbase + t) * s.R + r;
 #pragma unroll
@@ -351,6 +383,19 @@ __global__ __launch_bounds__(BLK * 4) void k_bwd_q(const T* __restrict__ Q, cons
   }
 #pragma unroll
   for (int dt = 0; dt < TL::ND; ++dt) store4<T>(dQ + (rowbase + t) * D + 16 * dt + c4, dq[dt], 1.f);
+}
+
+template <typename T, int D, int BLK, int RS>
+hipError_t launch_bwd_q(const Shape& s, const void* q, const void* k, const void* v, const void* d_o, const float* lse,
+                        const int32_t* sel, void* dq, const Buffers& b, long long nwg, hipStream_t st) {
+  const size_t ql = Tile<T, D, BLK>::LDS_BYTES;
+  hipError_t e;
+  if (ql > 65536 && (e = hipFuncSetAttribute((const void*)k_bwd_q<T, D, BLK, RS>,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)ql)) != hipSuccess)
+    return e;
+  hipLaunchKernelGGL((k_bwd_q<T, D, BLK, RS>), dim3((unsigned)nwg), dim3(BLK * 4), ql, st, (const T*)q,
+                     (const T*)k, (const T*)v, (const T*)d_o, lse, b.dvec, sel, (const T*)b.part_o, (T*)dq, s);
+  return hipGetLastError();
 }
 
 template <typename T, int D, int BLK>
@@ -375,14 +420,9 @@ hipError_t bwd_impl(const Shape& s, const void* q, const void* k, const void* v,
                      (const T*)k, (const T*)v, (const T*)d_o, lse, b.dvec, b.poff, b.ioff, b.items, (T*)b.part_o,
                      (T*)dk, (T*)dv, s);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  const size_t ql = Tile<T, D, BLK>::LDS_BYTES;
-  if (ql > 65536 && (e = hipFuncSetAttribute((const void*)k_bwd_q<T, D, BLK>,
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)ql)) != hipSuccess)
-    return e;
   if ((e = mark_event(ev, 2, st)) != hipSuccess) return e;
-  hipLaunchKernelGGL((k_bwd_q<T, D, BLK>), dim3(nwg), dim3(BLK * 4), ql, st, (const T*)q, (const T*)k,
-                     (const T*)v, (const T*)d_o, lse, b.dvec, sel, (const T*)b.part_o, (T*)dq, s);
-  return hipGetLastError();
+  return s.R >= 1 ? launch_bwd_q<T, D, BLK, 1>(s, q, k, v, d_o, lse, sel, dq, b, nwg, st)
+                    : launch_bwd_q<T, D, BLK, 0>(s, q, k, v, d_o, lse, sel, dq, b, nwg, st);
 }
 
 template <typename T, int D>
