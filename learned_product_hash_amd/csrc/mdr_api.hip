@@ -510,7 +510,6 @@ mdr_status mdr_stage_attend_lse(const mdr_config* cfg, const void* q, const void
   b.lse = lse;
   hipStream_t hs = (hipStream_t)stream;
   if (s.R > 0 && s.ne > 0) {
-    MDR_TRY(launch_fill(b.phist, (long long)s.B * s.H * s.ng * s.ne, 0, hs));
     MDR_TRY(launch_pair_count(s, sel, b.phist, hs));
     MDR_TRY(launch_pair_scatter(s, sel, b.phist, b.poff, b.ioff, b.items, hs));
   }
@@ -540,7 +539,6 @@ static mdr_status backward_core(const mdr_config* cfg, const void* q, const void
   hipStream_t hs = (hipStream_t)stream;
   MDR_TRY(mark_event(ev, 0, hs));
   if (s.R > 0 && s.ne > 0) {
-    MDR_TRY(launch_fill(b.phist, (long long)s.B * s.H * s.ng * s.ne, 0, hs));
     MDR_TRY(launch_pair_count(s, sel, b.phist, hs));
     MDR_TRY(launch_pair_scatter(s, sel, b.phist, b.poff, b.ioff, b.items, hs));
   }

@@ -302,9 +302,10 @@ hipError_t launch_decode_attend(const Shape& s, const void* q_new, const void* k
                                 hipStream_t st);
 bool probe_fixed_shape(const Shape& s);
 hipError_t launch_fill(int32_t* p, long long n, int32_t value, hipStream_t st);
-// Pair binning of a selection: launch_pair_count adds its pairs to the counters (which must be zero:
-// launch_fill, or the address kernel's clearing); launch_pair_scatter turns the counts into the
-// per-block lists, cut into the remote work items (stable: ascending token within a block).
+// Pair binning of a selection: launch_pair_count writes every token range's row of counts (the probe
+// kernels count their own selections instead, into counters the address kernel clears);
+// launch_pair_scatter turns the counts into the per-block lists, cut into the remote work items
+// (stable: ascending token within a block).
 hipError_t launch_pair_count(const Shape& s, const int32_t* sel, int32_t* phist, hipStream_t st);
 hipError_t launch_pair_scatter(const Shape& s, const int32_t* sel, const int32_t* phist, int32_t* poff,
                                int32_t* ioff, int32_t* items, hipStream_t st);

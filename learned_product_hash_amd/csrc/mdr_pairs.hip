@@ -6,7 +6,8 @@
 // that chose it, so the pairs are first grouped by block -- a stable counting sort in space linear in the
 // sequence:
 //   counts   per (b,h), token range g (tbin tokens) and remote block i, the number of valid pairs: the
-//            probe kernels count their own selections; k_pair_count counts a selection passed in
+//            probe kernels count their own selections; k_pair_count counts a selection passed in, one
+//            work-group per range writing its whole row (so the counters need no clearing first)
 //   scatter  k_pair_scatter, one work-group per (range, b,h): the totals over all ranges give each
 //            block's list offset (poff), the counts of the earlier ranges this range's first slot per
 //            block; its waves then file their pairs in ascending pair id (t R + r) with ballot ranks, so
@@ -18,7 +19,7 @@ namespace mdr {
 
 namespace {
 
-constexpr int kBinThreads = 256;
+constexpr int kCountThreads = 1024;
 
 // The scatter work-group takes its range's pairs kSubPairs at a time: their blocks (or -1) are staged in
 // LDS by all threads at once, then the waves that file pairs count and file them from LDS.  Those waves'
@@ -31,21 +32,22 @@ __host__ __device__ inline int scatter_waves(int ne) {
   return w > kScatterThreads / 64 ? kScatterThreads / 64 : w;
 }
 
-__global__ __launch_bounds__(kBinThreads) void k_pair_count(const int32_t* __restrict__ sel,
-                                                            int32_t* __restrict__ phist, Shape s) {
+__global__ __launch_bounds__(kCountThreads) void k_pair_count(const int32_t* __restrict__ sel,
+                                                              int32_t* __restrict__ phist, Shape s) {
   extern __shared__ int cnt[];  // [ne]
-  const int bh = blockIdx.y;
-  const int t0 = blockIdx.x * kBinThreads;
-  const int t = t0 + threadIdx.x;
-  PairCounter<kBinThreads> pc{cnt, phist + pair_counts_row(s, bh, t0), s.ne};
-  pc.begin();
-  if (t < s.S) {
+  const int g = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
+  for (int i = tid; i < s.ne; i += kCountThreads) cnt[i] = 0;
+  __syncthreads();
+  const int tfirst = g * s.tbin, tlast = min(s.S, tfirst + s.tbin);
+  for (int t = tfirst + tid; t < tlast; t += kCountThreads) {
     const int j = t / s.blk;
     const int32_t* row = sel + ((size_t)bh * s.S + t) * s.R;
     for (int r = 0; r < s.R; ++r)
-      if (sel_entry_valid(row, r, j, s.L)) pc.add(row[r]);
+      if (sel_entry_valid(row, r, j, s.L)) atomicAdd(&cnt[row[r]], 1);
   }
-  pc.end();
+  __syncthreads();
+  int32_t* dst = phist + pair_counts_row(s, bh, tfirst);
+  for (int i = tid; i < s.ne; i += kCountThreads) dst[i] = cnt[i];
 }
 
 __global__ __launch_bounds__(kScatterThreads) void k_pair_scatter(const int32_t* __restrict__ sel,
@@ -209,8 +211,7 @@ size_t pair_scatter_lds_bytes(const Shape& s) {
 
 hipError_t launch_pair_count(const Shape& s, const int32_t* sel, int32_t* phist, hipStream_t st) {
   if (s.R <= 0 || s.ne <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_pair_count, dim3((s.S + kBinThreads - 1) / kBinThreads, s.B * s.H), dim3(kBinThreads),
-                     (size_t)s.ne * 4, st, sel, phist, s);
+  hipLaunchKernelGGL(k_pair_count, dim3(s.ng, s.B * s.H), dim3(kCountThreads), (size_t)s.ne * 4, st, sel, phist, s);
   return hipGetLastError();
 }
 
