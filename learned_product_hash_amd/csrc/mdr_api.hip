@@ -436,9 +436,12 @@ mdr_status mdr_mixer_forward(const mdr_config* cfg, const void* x, const void* w
   apply_routing(routing, &b);
   hipStream_t hs = (hipStream_t)stream;
   const bool fused = qkv_fuses_address(s);
+  // the fused projection reads Wq, Wk, Wv transposed, the tiled output projection Wo
+  const int tfirst = fused ? 0 : 3, tlast = project_out_tiled(s) ? 4 : 3;
+  MDR_TRY(launch_transpose_weights(s, wq, wk, wv, wo, b.mwt, tfirst, tlast - tfirst, hs));
   if (fused) {
     const bool remote = s.R > 0 && s.ne > 0;
-    MDR_TRY(launch_qkv_fused(s, x, wq, wk, wv, b.mq, b.mk, b.mv, codebook, code_bias, b.ksum, b.addr,
+    MDR_TRY(launch_qkv_fused(s, x, b.mq, b.mk, b.mv, codebook, code_bias, b.ksum, b.addr,
                              s.policy == MDR_OVERFLOW_REDIRECT ? b.alt : nullptr, remote ? b.phist : nullptr,
                              b.mwt, hs, b.amargin));
   } else {

@@ -324,15 +324,22 @@ hipError_t launch_attend_backward(const Shape& s, const void* q, const void* k, 
                                   const Buffers& b, hipStream_t st, hipEvent_t* ev = nullptr);
 hipError_t launch_project_heads(const Shape& s, const void* x, const void* w, void* out, bool rope,
                                 hipStream_t st);
-// wt (optional): workspace for the transposed weights (4 * W * H * D elements); without it the
-// simple tiled product is used.
+// wt (optional): the transposed weights (4 * W * H * D elements, launch_transpose_weights); without it
+// the simple tiled product is used.
 hipError_t launch_project_out(const Shape& s, const void* o, const void* wo, void* delta, void* wt,
                               hipStream_t st);
+// True when launch_project_out with wt takes the tiled product on the transposed Wo.
+bool project_out_tiled(const Shape& s);
+// The mixer's weights transposed into wt in one launch: matrices first .. first + count - 1 of
+// (Wq, Wk, Wv, Wo), matrix z at wt + z W H D (k-contiguous rows for the tiled products).
+hipError_t launch_transpose_weights(const Shape& s, const void* wq, const void* wk, const void* wv, const void* wo,
+                                    void* wt, int first, int count, hipStream_t st);
 // Q, K, V projections with RoPE, block summaries and addresses (and alternates when alt is given)
-// fused into one launch; pair_zero (optional) as for launch_address.  Only when qkv_fuses_address.
+// fused into one launch, on the weights launch_transpose_weights wrote to wt; pair_zero (optional) as
+// for launch_address.  Only when qkv_fuses_address.
 bool qkv_fuses_address(const Shape& s);
-hipError_t launch_qkv_fused(const Shape& s, const void* x, const void* wq, const void* wk, const void* wv, void* q,
-                            void* k, void* v, const float* cb, const float* bias, float* ksum, int32_t* addr,
-                            int32_t* alt, int32_t* pair_zero, void* wt, hipStream_t st, float* amargin = nullptr);
+hipError_t launch_qkv_fused(const Shape& s, const void* x, void* q, void* k, void* v, const float* cb,
+                            const float* bias, float* ksum, int32_t* addr, int32_t* alt, int32_t* pair_zero,
+                            const void* wt, hipStream_t st, float* amargin = nullptr);
 
 }  // namespace mdr

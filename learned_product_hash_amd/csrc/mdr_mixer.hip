@@ -448,10 +448,18 @@ __global__ __launch_bounds__(256) void k_mm(const T* __restrict__ A, const T* __
   }
 }
 
-// out[c][r] = in[r][c] for an R x Cc matrix, through a padded 32 x 32 LDS tile.
+// The mixer's weights transposed into the workspace in one launch: matrix z = first + blockIdx.z of
+// (Wq, Wk, Wv: W x N; Wo: N x W) goes to wt + z N W, out[c][r] = in[r][c], through a padded 32 x 32
+// LDS tile; tiles past a matrix's edge do nothing.
 template <typename T>
-__global__ __launch_bounds__(256) void k_transpose(const T* __restrict__ in, T* __restrict__ out, int R, int Cc) {
+__global__ __launch_bounds__(256) void k_transpose(const T* __restrict__ w0, const T* __restrict__ w1,
+                                                   const T* __restrict__ w2, const T* __restrict__ w3,
+                                                   T* __restrict__ wt, int W, int N, int first) {
   __shared__ T tile[32][33];
+  const int z = first + blockIdx.z;
+  const T* in = z == 0 ? w0 : z == 1 ? w1 : z == 2 ? w2 : w3;
+  const int R = z < 3 ? W : N, Cc = z < 3 ? N : W;
+  T* out = wt + (size_t)z * N * W;
   const int c0 = blockIdx.x * 32, r0 = blockIdx.y * 32;
   const int tx = threadIdx.x % 32, ty = threadIdx.x / 32;
   for (int y = ty; y < 32; y += 8)
@@ -462,9 +470,12 @@ __global__ __launch_bounds__(256) void k_transpose(const T* __restrict__ in, T* 
 }
 
 template <typename T>
-hipError_t transpose(const void* in, void* out, int R, int Cc, hipStream_t st) {
-  hipLaunchKernelGGL(k_transpose<T>, dim3((Cc + 31) / 32, (R + 31) / 32), dim3(256), 0, st, (const T*)in, (T*)out, R,
-                     Cc);
+hipError_t transpose_weights(const Shape& s, const void* wq, const void* wk, const void* wv, const void* wo, void* wt,
+                             int first, int count, hipStream_t st) {
+  if (count <= 0) return hipSuccess;
+  const int W = s.W, N = s.H * s.D, side = (W > N ? W : N) + 31;
+  hipLaunchKernelGGL(k_transpose<T>, dim3(side / 32, side / 32, count), dim3(256), 0, st, (const T*)wq,
+                     (const T*)wk, (const T*)wv, (const T*)wo, (T*)wt, W, N, first);
   return hipGetLastError();
 }
 
@@ -483,41 +494,37 @@ int mm_tile(int Nm, int D, bool qkv) {
 }
 
 template <typename T, int NT, int D>
-hipError_t qkv_launch(const Shape& s, const void* x, const void* wq, const void* wk, const void* wv, void* q, void* k,
-                      void* v, const QkvEpilogue& ep, void* wt, hipStream_t st) {
+hipError_t qkv_launch(const Shape& s, const void* x, void* q, void* k, void* v, const QkvEpilogue& ep, const void* wt,
+                      hipStream_t st) {
   const int M = s.B * s.S, Nm = s.H * s.D;
   HeadMap hm{s.S, s.H, s.D};
-  T* t0 = (T*)wt;
-  T* t1 = t0 + (size_t)Nm * s.W;
-  T* t2 = t1 + (size_t)Nm * s.W;
-  hipError_t e;
-  if ((e = transpose<T>(wq, t0, s.W, Nm, st)) != hipSuccess) return e;
-  if ((e = transpose<T>(wk, t1, s.W, Nm, st)) != hipSuccess) return e;
-  if ((e = transpose<T>(wv, t2, s.W, Nm, st)) != hipSuccess) return e;
+  const T* t0 = (const T*)wt;  // Wq, Wk, Wv transposed by launch_transpose_weights
+  const T* t1 = t0 + (size_t)Nm * s.W;
+  const T* t2 = t1 + (size_t)Nm * s.W;
   hipLaunchKernelGGL((k_mm<T, 64, NT, false, true, D>), dim3((M + 63) / 64, 3 * Nm / NT), dim3(256), 0, st,
                      (const T*)x, t0, t1, t2, (T*)q, (T*)k, (T*)v, M, Nm, s.W, hm, ep, s);
   return hipGetLastError();
 }
 
 template <typename T, int D>
-hipError_t qkv_fused_d(const Shape& s, const void* x, const void* wq, const void* wk, const void* wv, void* q, void* k,
-                       void* v, const QkvEpilogue& ep, void* wt, hipStream_t st) {
+hipError_t qkv_fused_d(const Shape& s, const void* x, void* q, void* k, void* v, const QkvEpilogue& ep, const void* wt,
+                       hipStream_t st) {
   switch (mm_tile(s.H * s.D, D, true)) {
-    case 128: return qkv_launch<T, 128, D>(s, x, wq, wk, wv, q, k, v, ep, wt, st);
-    case 64: if constexpr (D <= 64) return qkv_launch<T, 64, D>(s, x, wq, wk, wv, q, k, v, ep, wt, st); break;
-    case 32: if constexpr (D <= 32) return qkv_launch<T, 32, D>(s, x, wq, wk, wv, q, k, v, ep, wt, st); break;
+    case 128: return qkv_launch<T, 128, D>(s, x, q, k, v, ep, wt, st);
+    case 64: if constexpr (D <= 64) return qkv_launch<T, 64, D>(s, x, q, k, v, ep, wt, st); break;
+    case 32: if constexpr (D <= 32) return qkv_launch<T, 32, D>(s, x, q, k, v, ep, wt, st); break;
     default: break;
   }
   return hipErrorInvalidValue;
 }
 
 template <typename T>
-hipError_t qkv_fused(const Shape& s, const void* x, const void* wq, const void* wk, const void* wv, void* q, void* k,
-                     void* v, const QkvEpilogue& ep, void* wt, hipStream_t st) {
+hipError_t qkv_fused(const Shape& s, const void* x, void* q, void* k, void* v, const QkvEpilogue& ep, const void* wt,
+                     hipStream_t st) {
   switch (s.D) {
-    case 32: return qkv_fused_d<T, 32>(s, x, wq, wk, wv, q, k, v, ep, wt, st);
-    case 64: return qkv_fused_d<T, 64>(s, x, wq, wk, wv, q, k, v, ep, wt, st);
-    case 128: return qkv_fused_d<T, 128>(s, x, wq, wk, wv, q, k, v, ep, wt, st);
+    case 32: return qkv_fused_d<T, 32>(s, x, q, k, v, ep, wt, st);
+    case 64: return qkv_fused_d<T, 64>(s, x, q, k, v, ep, wt, st);
+    case 128: return qkv_fused_d<T, 128>(s, x, q, k, v, ep, wt, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -527,9 +534,7 @@ hipError_t out_launch(const Shape& s, const void* o, const void* wo, void* delta
   const int M = s.B * s.S, Nm = s.W, Kd = s.H * s.D;
   HeadMap hm{s.S, s.H, s.D};
   const QkvEpilogue none{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
-  T* t = (T*)wt + 3 * (size_t)Kd * s.W;  // after the three projection weights
-  hipError_t e = transpose<T>(wo, t, Kd, Nm, st);
-  if (e != hipSuccess) return e;
+  const T* t = (const T*)wt + 3 * (size_t)Kd * s.W;  // Wo transposed, after the three projection weights
   if (M >= kBigM)
     hipLaunchKernelGGL((k_mm<T, 128, NT, true, false, 0>), dim3((M + 127) / 128, Nm / NT), dim3(256), 0, st,
                        (const T*)o, t, t, t, (T*)delta, (T*)delta, (T*)delta, M, Nm, Kd, hm, none, s);
@@ -579,13 +584,21 @@ hipError_t launch_project_heads(const Shape& s, const void* x, const void* w, vo
 
 bool qkv_fuses_address(const Shape& s) { return s.blk <= 64 && s.W % 8 == 0 && mm_tile(s.H * s.D, s.D, true) > 0; }
 
-hipError_t launch_qkv_fused(const Shape& s, const void* x, const void* wq, const void* wk, const void* wv, void* q,
-                            void* k, void* v, const float* cb, const float* bias, float* ksum, int32_t* addr,
-                            int32_t* alt, int32_t* pair_zero, void* wt, hipStream_t st, float* amargin) {
+hipError_t launch_qkv_fused(const Shape& s, const void* x, void* q, void* k, void* v, const float* cb,
+                            const float* bias, float* ksum, int32_t* addr, int32_t* alt, int32_t* pair_zero,
+                            const void* wt, hipStream_t st, float* amargin) {
   if (!qkv_fuses_address(s)) return hipErrorInvalidValue;
   const QkvEpilogue ep{cb, bias, ksum, addr, alt, pair_zero, amargin};
-  if (s.dtype == MDR_BF16) return qkv_fused<bf16>(s, x, wq, wk, wv, q, k, v, ep, wt, st);
-  return qkv_fused<float>(s, x, wq, wk, wv, q, k, v, ep, wt, st);
+  if (s.dtype == MDR_BF16) return qkv_fused<bf16>(s, x, q, k, v, ep, wt, st);
+  return qkv_fused<float>(s, x, q, k, v, ep, wt, st);
+}
+
+bool project_out_tiled(const Shape& s) { return mm_tile(s.W, 0, false) != 0; }
+
+hipError_t launch_transpose_weights(const Shape& s, const void* wq, const void* wk, const void* wv, const void* wo,
+                                    void* wt, int first, int count, hipStream_t st) {
+  if (s.dtype == MDR_BF16) return transpose_weights<bf16>(s, wq, wk, wv, wo, wt, first, count, st);
+  return transpose_weights<float>(s, wq, wk, wv, wo, wt, first, count, st);
 }
 
 hipError_t launch_project_out(const Shape& s, const void* o, const void* wo, void* delta, void* wt, hipStream_t st) {
