@@ -120,8 +120,9 @@ __global__ __launch_bounds__(kRemoteWaves * 64) void k_attn_remote(const T* __re
 // depend on the selection; unused ones are ignored).  RS is a template argument so that these
 // reads form one straight-line block the compiler need not wait on early.
 
-// bf16 tiles with D <= 64 are held to four waves per SIMD (four 256-thread work-groups per CU).
-constexpr int local_min_waves(int bytes, int D) { return bytes == 2 && D <= 64 ? 4 : 1; }
+// bf16 tiles are held to four waves per SIMD with D <= 64 (four 256-thread work-groups per CU) and to
+// two with D = 128 (left free, that shape took one wave per SIMD).
+constexpr int local_min_waves(int bytes, int D) { return bytes == 2 ? (D <= 64 ? 4 : 2) : 1; }
 
 template <typename T, int D, int BLK, int RS>
 __global__ __launch_bounds__(BLK * 4) __attribute__((amdgpu_waves_per_eu(local_min_waves((int)sizeof(T), D)))) void k_attn_local(
