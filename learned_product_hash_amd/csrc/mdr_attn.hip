@@ -124,7 +124,7 @@ __global__ __launch_bounds__(kRemoteWaves * 64) void k_attn_remote(const T* __re
 // two with D = 128 (left free, that shape took one wave per SIMD).
 constexpr int local_min_waves(int bytes, int D) { return bytes == 2 ? (D <= 64 ? 4 : 2) : 1; }
 
-template <typename T, int D, int BLK, int RS>
+template <typename T, int D, int BLK, int RS, bool TAIL>
 __global__ __launch_bounds__(BLK * 4) __attribute__((amdgpu_waves_per_eu(local_min_waves((int)sizeof(T), D)))) void k_attn_local(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, const int32_t* __restrict__ sel,
     const T* __restrict__ part_o, const float* __restrict__ part_lse, T* __restrict__ out,
@@ -235,13 +235,38 @@ __global__ __launch_bounds__(BLK * 4) __attribute__((amdgpu_waves_per_eu(local_m
     for (int p = 0; p < r; ++p) ok = ok && sr[p] != sr[r];
     if (ok) merge(plse[r], praw[r]);
   }
-  for (int r = RS; r < s.R; ++r) {
-    if (!sel_entry_valid(row, r, j, s.L)) continue;
-    const size_t pr = (rowbase + t) * s.R + r;
-    Raw4<T> po[TL::ND];
+  if constexpr (TAIL) {
+    // slots RS .. R-1 (R > RS): the whole row is read at once, then the used slots' partials two at a
+    // time, both requested before either is merged
+    int sx[kMaxRemote];
 #pragma unroll
-    for (int dt = 0; dt < TL::ND; ++dt) po[dt] = *(const Raw4<T>*)(part_o + pr * D + 16 * dt + c4);
-    merge(part_lse[pr], po);
+    for (int r = 0; r < kMaxRemote; ++r) sx[r] = r < s.R ? row[r] : -1;
+    auto used = [&](int r) -> bool {
+      bool ok = sx[r] >= 0 && sx[r] <= j - s.L;
+#pragma unroll
+      for (int p = 0; p < kMaxRemote; ++p) ok = ok && (p >= r || sx[p] != sx[r]);
+      return ok;
+    };
+#pragma unroll
+    for (int r = RS; r < kMaxRemote; r += 2) {
+      if (r >= s.R) break;
+      const bool u0 = used(r), u1 = r + 1 < s.R && used(r + 1);
+      const size_t pr = (rowbase + t) * s.R + r;
+      Raw4<T> pa[TL::ND], pb[TL::ND];
+      float la = 0.f, lb = 0.f;
+      if (u0) {
+#pragma unroll
+        for (int dt = 0; dt < TL::ND; ++dt) pa[dt] = *(const Raw4<T>*)(part_o + pr * D + 16 * dt + c4);
+        la = part_lse[pr];
+      }
+      if (u1) {
+#pragma unroll
+        for (int dt = 0; dt < TL::ND; ++dt) pb[dt] = *(const Raw4<T>*)(part_o + (pr + 1) * D + 16 * dt + c4);
+        lb = part_lse[pr + 1];
+      }
+      if (u0) merge(la, pa);
+      if (u1) merge(lb, pb);
+    }
   }
   const float inv = 1.f / l;
 #pragma unroll
@@ -249,15 +274,15 @@ __global__ __launch_bounds__(BLK * 4) __attribute__((amdgpu_waves_per_eu(local_m
   if (lse && c4 == 0) lse[rowbase + t] = m + log2f(l);
 }
 
-template <typename T, int D, int BLK, int RS>
+template <typename T, int D, int BLK, int RS, bool TAIL = false>
 hipError_t launch_local(const Shape& s, const void* q, const void* k, const void* v, const int32_t* sel, void* out,
                         const Buffers& b, hipStream_t st) {
   const size_t lds = Tile<T, D, BLK>::LDS_BYTES;
   hipError_t e;
-  if (lds > 65536 && (e = hipFuncSetAttribute((const void*)k_attn_local<T, D, BLK, RS>,
+  if (lds > 65536 && (e = hipFuncSetAttribute((const void*)k_attn_local<T, D, BLK, RS, TAIL>,
                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)) != hipSuccess)
     return e;
-  hipLaunchKernelGGL((k_attn_local<T, D, BLK, RS>), dim3(s.nb * s.B * s.H), dim3(BLK * 4), lds, st, (const T*)q,
+  hipLaunchKernelGGL((k_attn_local<T, D, BLK, RS, TAIL>), dim3(s.nb * s.B * s.H), dim3(BLK * 4), lds, st, (const T*)q,
                      (const T*)k, (const T*)v, sel, (const T*)b.part_o, b.part_lse, (T*)out, b.lse, s);
   return hipGetLastError();
 }
@@ -278,7 +303,8 @@ hipError_t attend_impl(const Shape& s, const void* q, const void* k, const void*
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if ((e = mark_event(ev, 1, st)) != hipSuccess) return e;
-  return s.R >= 2   ? launch_local<T, D, BLK, 2>(s, q, k, v, sel, out, b, st)
+  return s.R > 2    ? launch_local<T, D, BLK, 2, true>(s, q, k, v, sel, out, b, st)
+         : s.R == 2 ? launch_local<T, D, BLK, 2>(s, q, k, v, sel, out, b, st)
          : s.R == 1 ? launch_local<T, D, BLK, 1>(s, q, k, v, sel, out, b, st)
                     : launch_local<T, D, BLK, 0>(s, q, k, v, sel, out, b, st);
 }
