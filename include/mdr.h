@@ -354,9 +354,9 @@ mdr_status mdr_stage_attend_backward(const mdr_config* cfg, const void* q, const
                                      const void* d_out, void* dq, void* dk, void* dv, void* workspace,
                                      size_t workspace_bytes, void* stream);
 
-/* Kernels of the backward, in launch order: pair binning (counter fill, count
- * and scatter; empty when R = 0 or nb <= L), row dots D, key blocks (dK, dV,
- * remote dQ shares), query blocks (dQ). */
+/* Stages of the backward, in launch order: pair binning (count and scatter;
+ * empty when R = 0 or nb <= L), row dots D, key blocks (dK, dV, remote dQ
+ * shares), query blocks (dQ). */
 #define MDR_BACKWARD_KERNELS 4
 
 /* Profiling form of mdr_stage_attend_backward: events[k] (hipEvent_t created
