@@ -126,3 +126,42 @@ def test_mixer_large_tiles(gpu_lib):
     err = float(np.abs(host(delta)[0, toks] - ref).max())
     print(f"large tiles: address near-ties {near}, sampled delta max abs err {err:.3g}")
     assert err <= TOL["bf16"]
+
+
+def test_mixer_full_size_sampled(gpu_lib):
+    """The benchmark's mixer at full size in its launch configuration (B1 S32768 W512, 8 heads of 64,
+    bf16): summaries and addresses of every block against the oracle's projections, routing of sampled
+    tokens of every head under the near-tie rule (on the GPU's addresses where a head has an address
+    near-tie), and the delta on those tokens (gathered attention with the GPU's selection, then the
+    output projection)."""
+    mdr = gpu_lib
+    w = dataclasses.replace(synth.workload("sweep", seq=32768), width=512)
+    inp = synth.make_mixer_inputs(w, 0)
+    cfg = cfg_of(mdr, w)
+    t = {n: dev(inp[n], torch.bfloat16) for n in ("x", "wq", "wk", "wv", "wo")}
+    cb = dev(inp["codebook"], torch.float32)
+    delta = torch.empty_like(t["x"])
+    rt = mdr.routing_buffers(cfg)
+    mdr.mdr_mixer_forward(cfg, t["x"], t["wq"], t["wk"], t["wv"], t["wo"], cb, None, delta, rt, mdr.workspace(cfg))
+    torch.cuda.synchronize()
+    res = {n: host(v) for n, v in rt.items()}
+    q, k, v = (oracle.round_to_bf16(a) for a in oracle.mixer_qkv(inp["x"], inp["wq"], inp["wk"], inp["wv"], w))
+    heads_inp = {"q": q.astype(np.float32), "k": k.astype(np.float32), "codebook": inp["codebook"], "bias": None}
+    rng = np.random.default_rng(11)
+    toks = np.unique(np.concatenate([rng.choice(w.seq, size=96, replace=False), [0, w.block - 1, w.seq - 1]]))
+    o = np.zeros((len(toks), w.heads * w.head_dim))
+    near_a = near_s = 0
+    for h in range(w.heads):
+        ks = oracle.block_summaries(k[0, h].astype(np.float32), w.block)
+        scale = max(1.0, float(np.abs(ks).max()))
+        np.testing.assert_allclose(res["ksum"][0, h], ks, rtol=0, atol=2e-3 * scale)
+        na, ns = check_head_routing(w, heads_inp, res, 0, h, tokens=toks)
+        near_a += na
+        near_s += ns
+        o[:, h * w.head_dim:(h + 1) * w.head_dim] = oracle.attention_packed(
+            q[0, h], k[0, h], v[0, h], res["sel"][0, h][toks], w.block, w.local, tokens=toks)
+    ref = o @ inp["wo"].astype(np.float64)
+    err = float(np.abs(host(delta)[0, toks] - ref).max())
+    print(f"mixer full size: address near-ties {near_a}, sampled selection near-ties {near_s}, "
+          f"sampled delta max abs err {err:.3g}")
+    assert err <= TOL["bf16"]
