@@ -112,11 +112,13 @@ def check_against_oracle(w, inp, n0, out, sel, view, force=None):
     ("sweep", 3000, 1),     # bf16, balanced addresses
     ("skew", 15900, 16),    # bf16, D128, zipf-biased codes at 16K: hot rings overflow
     ("long", 5000, 64),     # bf16, D128 block 128, R4
+    ("sweep_full", 32704, 1),  # the benchmark's decode: 32K context, 8 heads, one token per call
 ])
 def test_decode_matches_oracle(gpu_lib, name, n0, chunk):
     mdr = gpu_lib
     over = {"tiny_cap1": dict(capacity=1), "recall": dict(batch=2), "sweep": dict(seq=4096),
-            "skew": dict(batch=1, heads=2, seq=16384), "long": dict(heads=1, seq=8192)}.get(name, {})
+            "skew": dict(batch=1, heads=2, seq=16384), "long": dict(heads=1, seq=8192),
+            "sweep_full": dict(seq=32768)}.get(name, {})
     w = small(name.split("_")[0], **over)
     inp = synth.make_core_inputs(w, 0)
     out, sel, view = decode_run(mdr, w, inp, n0, chunk)
