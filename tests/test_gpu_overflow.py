@@ -15,7 +15,8 @@ import torch
 
 import oracle
 import synth
-from tests._gpu import NEAR, cfg_of, check_head_routing, compare_selection, dev, host, io_dtype, run_core, small
+from tests._gpu import (NEAR, TOL, attention_rows, cfg_of, check_head_routing, compare_selection, dev, host, io_dtype,
+                        run_core, small)
 
 pytestmark = pytest.mark.gpu
 
@@ -174,3 +175,30 @@ def test_redirect_without_overflow_equals_drop(gpu_lib):
         for n in ("sel", "n_cand", "n_drop", "overflow", "addr"):
             assert np.array_equal(a[n], b[n]), n
         np.testing.assert_array_equal(a["out"], b["out"])
+
+
+@pytest.mark.parametrize("policy", ["drop", "redirect"])
+def test_stress_full_size_sampled(gpu_lib, policy):
+    """The benchmark's overflow-stress shape at full size and its strongest skew (B2 H8 S16384 D128, 3x8
+    codes, capacity 8, P6, R8, code bias -ln(c + 1)): every head's addresses, posting lists, overflow
+    (and redirect lists) against the oracle, the routing of sampled tokens under the near-tie rule, and
+    their attention rows with the GPU's selection."""
+    mdr = gpu_lib
+    w = small("skew", batch=2, heads=8, seq=16384, zipf_kappa=1.0)
+    inp = synth.make_core_inputs(w, 0)
+    res = run_core(mdr, w, inp, policy=policy)
+    rng = np.random.default_rng(5)
+    toks = np.unique(np.concatenate([rng.choice(w.seq, 64, replace=False), [0, w.block - 1, w.seq - 1]]))
+    near_up = near_sel = 0
+    err = 0.0
+    for b in range(w.batch):
+        for h in range(w.heads):
+            nu, ns = check_head_routing(w, inp, res, b, h, policy=policy, tokens=toks)
+            near_up += nu
+            near_sel += ns
+            ref = attention_rows(w, inp, res["sel"][b, h][toks], b, h, toks)
+            err = max(err, float(np.abs(res["out"][b, h][toks] - ref).max()))
+    print(f"stress {policy}: overflow {int(res['overflow'].sum())}, upstream near-ties {near_up}, sampled "
+          f"selection near-ties {near_sel}, sampled max abs err {err:.3g}")
+    assert int(res["overflow"].sum()) > 0
+    assert err <= TOL[w.dtype]
