@@ -15,8 +15,9 @@
 //              wave recomputes S = Q K^T and dP = dO V^T for its keys with the entries as rows,
 //              then accumulates dV^T += dO^T P and dK^T += Q^T dS on MFMA (the score layout is
 //              the PV operand layout, as in the forward); for remote entries the waves also
-//              compute, with the keys as rows, the pair's share of dQ (scale dS K over block i)
-//              and store it in the pair's partial slot.  dK, dV are written once, no atomics.
+//              compute the pair's share of dQ (scale dS K over block i), from the chunk's dS left
+//              in LDS where it fits (else recomputed with the keys as rows), and store it in the
+//              pair's partial slot.  dK, dV are written once, no atomics.
 //   k_bwd_q    one work-group per query block: dQ of the local window (recomputed), plus the
 //              remote shares in slot order.
 #include "mdr_internal.h"
@@ -52,6 +53,13 @@ __global__ __launch_bounds__(256) void k_bwd_dot(const T* __restrict__ O, const 
 
 // Sizes of the key-block kernel: the entries of a block (local tokens, then its pair list) are taken
 // EC at a time -- 64, or fewer where that would not fit the 160 KiB of LDS.
+//
+// The remote entries' dQ shares need dS with the keys as the contraction.  For bf16 with D <= 64, where
+// one more BLK x EC tile fits without lowering the number of work-groups the LDS allows per CU
+// (DS_LDS), each wave leaves its 16 keys' rows of dS^T in that tile (the bf16 values the dK product
+// uses), and each share is one product over the block's keys read back from it with transposing
+// reads; otherwise each share recomputes S and dP with the keys as rows.  (With D = 128 the kernel is
+// at its register limit and the tile's stores made it spill: 2.75 -> 4.0 ms on 128K tokens.)
 template <typename T, int D, int BLK>
 struct KvCfg {
   using TL = Tile<T, D, BLK>;
@@ -63,7 +71,14 @@ struct KvCfg {
   static constexpr size_t LIM = 160 * 1024 - 256;
   static constexpr int EC = lds(64) <= LIM ? 64 : lds(32) <= LIM ? 32 : 16;
   static constexpr int SUB = EC < 32 ? EC : 32;  // entries per dK / dV product
-  static constexpr size_t LDS = lds(EC);
+  // dS^T tile [BLK][DSS] (keys as rows): with rows EC + 16 elements apart, the eight rows that half a
+  // wave's transposing reads touch fall in disjoint bank windows (as for the K/V tiles)
+  static constexpr int DSS = EC + 16;
+  static constexpr size_t DS_BYTES = (size_t)BLK * DSS * sizeof(T);
+  static constexpr int per_cu(size_t b) { return (int)((size_t)160 * 1024 / b); }
+  static constexpr bool DS_LDS =
+      TL::bf && D <= 64 && lds(EC) + DS_BYTES <= LIM && per_cu(lds(EC) + DS_BYTES) >= per_cu(lds(EC));
+  static constexpr size_t LDS = lds(EC) + (DS_LDS ? DS_BYTES : 0);
 };
 
 // The entries flow through a three-stage pipeline, one chunk of EC per stage and iteration:
@@ -96,7 +111,8 @@ __global__ __launch_bounds__(BLK * 4) __attribute__((amdgpu_waves_per_eu(kv_min_
   T* Vs = Ks + TL::K_ELEMS;
   T* Qs = Vs + TL::V_ELEMS;              // [EC][KST] the chunk's query rows
   T* dOs = Qs + EC * TL::KST;            // [EC][KST] the chunk's output-gradient rows
-  int* mtok = (int*)(dOs + EC * TL::KST);  // [2][EC] token of each entry (-1: none), by chunk parity
+  T* dsT = dOs + EC * TL::KST;           // [BLK][DSS] dS^T of the chunk, keys as rows (DS_LDS)
+  int* mtok = (int*)(dsT + (C::DS_LDS ? BLK * C::DSS : 0));  // [2][EC] token of each entry (-1: none), by chunk parity
   int* mpair = mtok + 2 * EC;              // [2][EC] pair id t R + r (-1: local entry)
   float* mlse = (float*)(mpair + 2 * EC);  // [2][EC] log2 normaliser of the token
   float* mdd = mlse + 2 * EC;              // [2][EC] D = dO . O of the token
@@ -214,7 +230,10 @@ __global__ __launch_bounds__(BLK * 4) __attribute__((amdgpu_waves_per_eu(kv_min_
       // Only entries below BLK (the tokens of query block i) can precede a key of block i; every later
       // entry is a later token, and an unused entry (token -1) has zero query and gradient rows and a
       // zero normaliser and row dot, so whatever weight it gets it adds exactly zero.  The causal test
-      // is therefore made only in chunks that hold entries below BLK.
+      // is therefore made only in chunks that hold entries below BLK.  In a chunk with remote entries
+      // (DS_LDS) each lane also leaves its key's four dS values of each row tile in dsT, in bf16 as
+      // the dK product takes them.
+      const bool has_remote = npair > 0 && (k + 1) * EC > nloc;
       auto products = [&](auto masked_tag) __attribute__((always_inline)) {
         constexpr bool MASKED = decltype(masked_tag)::value;
 #pragma unroll
@@ -234,6 +253,12 @@ __global__ __launch_bounds__(BLK * 4) __attribute__((amdgpu_waves_per_eu(kv_min_
               p[rt][kk] = pv;
               ds[rt][kk] = pv * (dp[kk] - dk_[e]);
             }
+            if constexpr (C::DS_LDS) {
+              if (has_remote) {
+                const bf16x4 w = {(bf16)ds[rt][0], (bf16)ds[rt][1], (bf16)ds[rt][2], (bf16)ds[rt][3]};
+                *(bf16x4*)(dsT + (16 * wave + r16) * C::DSS + h * SUB + 16 * rt + 4 * s4) = w;
+              }
+            }
           }
           pv_block<T, D, SUB>(dv, p, gh, lane);
           pv_block<T, D, SUB>(dk, ds, qh, lane);
@@ -243,31 +268,53 @@ __global__ __launch_bounds__(BLK * 4) __attribute__((amdgpu_waves_per_eu(kv_min_
         products(std::true_type{});
       else
         products(std::false_type{});
-      // ---- the remote entries' dQ shares, keys as rows: lane (entry 16g + r16) holds keys 16n + 4s4 + k
-      for (int g = wave; g < EC / 16; g += NW) {
-        const int el = 16 * g + r16;
-        const int pid = pk[el];
-        if (__builtin_amdgcn_readfirstlane(__ballot(pid >= 0) != 0ull ? 1 : 0) == 0) continue;  // all local
-        QFrag<T, D> qf, gf;
-        load_q<T, D>(qf, Qs + el * TL::KST, lane);
-        load_q<T, D>(gf, dOs + el * TL::KST, lane);
-        const float le = lk[el], de = dk_[el];
-        f32x4 dst[TL::NT];
-#pragma unroll
-        for (int n = 0; n < TL::NT; ++n) {
-          const f32x4 sc = score_tile<T, D, BLK>(qf, Ks, n, lane);
-          const f32x4 dp = score_tile<T, D, BLK>(gf, Vs, n, lane);
-#pragma unroll
-          for (int kk = 0; kk < 4; ++kk) dst[n][kk] = fast_exp2(fmaf(sc[kk], c, -le)) * (dp[kk] - de);
-        }
+      // ---- the remote entries' dQ shares (scale dS K over block i): lane (entry 16g + r16) takes dS of
+      // keys 16n + 4s4 + k, read back from dsT or recomputed with the keys as rows
+      auto store_share = [&](int pid, const auto& dst) __attribute__((always_inline)) {
         f32x4 dq[TL::ND];
 #pragma unroll
         for (int dt = 0; dt < TL::ND; ++dt) dq[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        pv_block<T, D, BLK>(dq, dst, Ks, lane);
+        if constexpr (C::DS_LDS)
+          pv_block_bf16<D, BLK>(dq, dst, Ks, lane);
+        else
+          pv_block<T, D, BLK>(dq, dst, Ks, lane);
         if (pid >= 0) {
           const size_t pr = rowbase * s.R + pid;  // the pair (token, slot)
 #pragma unroll
           for (int dt = 0; dt < TL::ND; ++dt) store4<T>(dq_part + pr * D + 16 * dt + 4 * s4, dq[dt], s.scale);
+        }
+      };
+      if constexpr (C::DS_LDS) {
+        if (has_remote) {
+          __syncthreads();  // every wave's dS columns are in dsT
+          for (int g = wave; g < EC / 16; g += NW) {
+            const int el = 16 * g + r16;
+            const int pid = pk[el];
+            if (__builtin_amdgcn_readfirstlane(__ballot(pid >= 0) != 0ull ? 1 : 0) == 0) continue;  // all local
+            bf16x4 dst[TL::NT];  // dS^T[16n + 4s4 + k][el], column el of four rows per transposing read
+#pragma unroll
+            for (int n = 0; n < TL::NT; ++n) dst[n] = tr_col4(dsT + (16 * n + 4 * s4) * C::DSS + 16 * g, C::DSS, r16);
+            store_share(pid, dst);
+          }
+        }
+      } else {
+        for (int g = wave; g < EC / 16; g += NW) {
+          const int el = 16 * g + r16;
+          const int pid = pk[el];
+          if (__builtin_amdgcn_readfirstlane(__ballot(pid >= 0) != 0ull ? 1 : 0) == 0) continue;  // all local
+          QFrag<T, D> qf, gf;
+          load_q<T, D>(qf, Qs + el * TL::KST, lane);
+          load_q<T, D>(gf, dOs + el * TL::KST, lane);
+          const float le = lk[el], de = dk_[el];
+          f32x4 dst[TL::NT];  // dS^T[16n + 4s4 + k][el]
+#pragma unroll
+          for (int n = 0; n < TL::NT; ++n) {
+            const f32x4 sc = score_tile<T, D, BLK>(qf, Ks, n, lane);
+            const f32x4 dp = score_tile<T, D, BLK>(gf, Vs, n, lane);
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) dst[n][kk] = fast_exp2(fmaf(sc[kk], c, -le)) * (dp[kk] - de);
+          }
+          store_share(pid, dst);
         }
       }
       __syncthreads();  // chunk k's rows and metadata are overwritten next

@@ -90,13 +90,17 @@ __device__ inline f32x4 score_tile(const QFrag<T, D>& qf, const T* Ks, int n, in
 // lane r supplies row r / 4 of a 4-row tile, columns 4 (r % 4) .. + 3, lane r receives the four
 // rows' values in column r (rows 0..3 in slots 0..3); the layout was checked on gfx950 with an
 // in-bounds probe.  tile: the tile's first row and column (LDS, bf16), stride: row stride in
-// elements (a multiple of 4); the values go to slots at .. at + 3 of a.
-__device__ __forceinline__ void tr_keys4(bf16x8& a, int at, const bf16* tile, int stride, int r) {
+// elements (a multiple of 4); tr_keys4 puts the values in slots at .. at + 3 of a.
+__device__ __forceinline__ bf16x4 tr_col4(const bf16* tile, int stride, int r) {
   typedef short v4i16 __attribute__((ext_vector_type(4)));
   const bf16* src = tile + (r >> 2) * stride + 4 * (r & 3);
   const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(src));
   bf16x4 w;
   __builtin_memcpy(&w, &v, 8);
+  return w;
+}
+__device__ __forceinline__ void tr_keys4(bf16x8& a, int at, const bf16* tile, int stride, int r) {
+  const bf16x4 w = tr_col4(tile, stride, r);
 #pragma unroll
   for (int e = 0; e < 4; ++e) a[at + e] = w[e];
 }
@@ -181,6 +185,29 @@ __device__ inline f32x4 unpack4(const Raw4<T>& r) {
   } else {
     const float4 v = *(const float4*)&r;
     return f32x4{v.x, v.y, v.z, v.w};
+  }
+}
+
+// pv_block for bf16 with P^T already in bf16, four values per sub-tile: p[n] = P^T[16n + 4(l/16) + 0..3][l%16].
+template <int D, int BLK>
+__device__ inline void pv_block_bf16(f32x4 (&o)[D / 16], const bf16x4 (&p)[BLK / 16], const bf16* Vx, int lane) {
+  using TL = Tile<bf16, D, BLK>;
+  const int s = lane >> 4, r = lane & 15;
+#pragma unroll
+  for (int pp = 0; pp < BLK / 32; ++pp) {
+    bf16x8 b;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      b[k] = p[2 * pp][k];
+      b[4 + k] = p[2 * pp + 1][k];
+    }
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) {
+      bf16x8 a;
+      tr_keys4(a, 0, Vx + (32 * pp + 4 * s) * TL::VST + 16 * dt, TL::VST, r);
+      tr_keys4(a, 4, Vx + (32 * pp + 16 + 4 * s) * TL::VST + 16 * dt, TL::VST, r);
+      o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, o[dt], 0, 0, 0);
+    }
   }
 }
 
