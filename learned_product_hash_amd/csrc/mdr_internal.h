@@ -290,7 +290,9 @@ bool probe_fuses_post(const Shape& s);
 bool probe_fuses_post_nt(const Shape& s, int nt);
 // Query tokens per work-group of the routing path's probe (256, or 128 / 64 on small grids).
 int probe_fixed_tokens(const Shape& s);
-size_t probe_lds_bytes(const Shape& s, int nt = kProbeFixedThreads);
+// LDS of the probe kernel (the generic kernel, or the fixed one with nt threads and, when diag, the
+// diagnostics outputs; the default is the largest form).
+size_t probe_lds_bytes(const Shape& s, int nt = kProbeFixedThreads, bool diag = true);
 // Decode: file blocks [filed, target) of every (b,h) (summarising those not summarised yet), then
 // route and attend tokens pos .. pos + n_new - 1 (one query block).
 hipError_t launch_ring_reset(int32_t* ring, long long records, int cap, hipStream_t st);

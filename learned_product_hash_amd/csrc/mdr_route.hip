@@ -828,8 +828,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(probe_min_wa
   const int tbase = blockIdx.x * NT;
   const int t = tbase + tid;
   const int A = s.A;
-  float* mu = smem;                                       // [NT][MST]
-  int* csr = (int*)(smem + max(NT * MST, NT * s.M * 2));  // off [A+1], idx [ne]
+  constexpr int RK = R > 0 ? R : 1;
+  // the mu rows, later the candidate list and then (diagnostics) the scores or (routing) the top-R keys
+  float* mu = smem;  // [NT][MST]
+  int* csr = (int*)(smem + max(NT * MST, DIAG ? NT * s.M * 2 : NT * (s.M + 2 * RK)));  // off [A+1], idx [ne]
   // ---- the addresses (or the CSR) of this (b,h), first 8 per lane
   const int32_t* og = off + (size_t)bh * (A + 1);
   const int32_t* ig = idx + (size_t)bh * s.nb;
@@ -1157,8 +1159,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(probe_min_wa
   __shared__ int scan_tmp[NT / 64];
   int total;
   const int base = block_exclusive_scan<NT>(nc, scan_tmp, &total);
-  int* clist = (int*)smem;                // [total] (local token << 16) | block
-  float* rho = smem + NT * s.M;           // [total]
+  int* clist = (int*)smem;                          // [total] (local token << 16) | block
+  float* rho = smem + NT * s.M;                     // [total] scores (diagnostics)
+  uint64_t* topk = (uint64_t*)(smem + NT * s.M);    // [NT][RK] each token's top-R keys (routing)
   {
     int k = base;
 #pragma unroll
@@ -1172,7 +1175,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(probe_min_wa
   // m = 0..LPT-1); lane o = lane%LPT takes dims 4*LPT*c + 4o + e, so the group reads 16*LPT contiguous
   // bytes of a summary per load.  Several candidates are in flight at a time; the partial dots are
   // added in a fixed order (xor 1, 2, ...).  The query slices are read again (from L2) rather than
-  // kept live through the selection above, the next token's while the current one is scored.
+  // kept live through the selection above, the next token's while the current one is scored.  The
+  // routing variant ranks each score into the token's top-R right away (the group's lanes hold the same
+  // list) and leaves only the R keys in LDS; the diagnostics variant, which needs every candidate's
+  // score, stores them all.
   {
     constexpr int LPT = 4;
     constexpr int NC4 = D / (4 * LPT);   // float4 per candidate per lane
@@ -1208,11 +1214,16 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(probe_min_wa
         }
       }
       if (m + 1 < LPT) q_slice(m + 1, qnext);
+      uint64_t tk[RK];
+#pragma unroll
+      for (int r = 0; r < RK; ++r) tk[r] = 0;
       for (int k0 = 0; k0 < n0; k0 += UB) {
         float4 kv[UB][NC4];
+        int iu[UB];
 #pragma unroll
         for (int u = 0; u < UB; ++u) {
           const int i = clist[b0 + (k0 + u < n0 ? k0 + u : k0)] & 0xffff;
+          iu[u] = i;
           const float* kr = ksh + (size_t)i * D + 4 * lo;
 #pragma unroll
           for (int c = 0; c < NC4; ++c) kv[u][c] = *(const float4*)(kr + 4 * LPT * c);
@@ -1229,22 +1240,37 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(probe_min_wa
           }
 #pragma unroll
           for (int x = 1; x < LPT; x <<= 1) a += __shfl_xor(a, x);
-          if (lo == 0 && k0 + u < n0) rho[b0 + k0 + u] = a;
+          if constexpr (DIAG) {
+            if (lo == 0 && k0 + u < n0) rho[b0 + k0 + u] = a;
+          } else {
+            if (k0 + u < n0) insert_key<RK>(tk, rank_key(a, iu[u]));
+          }
         }
+      }
+      if constexpr (!DIAG) {
+        if (lo == 0)
+#pragma unroll
+          for (int r = 0; r < RK; ++r) topk[(wave * 64 + src) * RK + r] = tk[r];
       }
     }
   }
   lds_barrier();
-  // ---- top-R of the token's candidates by (score desc, block asc)
-  constexpr int RK = R > 0 ? R : 1;
+  // ---- top-R of the token's candidates by (score desc, block asc): ranked here from the scores
+  // (diagnostics), or as ranked in the rerank (the order of insertion does not change a top list under
+  // this total order)
   constexpr int RKX = DIAG ? RK + 1 : RK;  // diagnostics: one more, for the margin at the boundary
   int tri[RK];
   int nr = 0;
   if (active) {
     uint64_t trk[RKX];
+    if constexpr (DIAG) {
 #pragma unroll
-    for (int r = 0; r < RKX; ++r) trk[r] = 0;
-    for (int k = base; k < base + nc; ++k) insert_key<RKX>(trk, rank_key(rho[k], clist[k] & 0xffff));
+      for (int r = 0; r < RKX; ++r) trk[r] = 0;
+      for (int k = base; k < base + nc; ++k) insert_key<RKX>(trk, rank_key(rho[k], clist[k] & 0xffff));
+    } else {
+#pragma unroll
+      for (int r = 0; r < RK; ++r) trk[r] = topk[tid * RK + r];
+    }
 #pragma unroll
     for (int r = 0; r < RK; ++r) tri[r] = key_index(trk[r]);
     nr = nc < R ? nc : R;
@@ -1328,7 +1354,7 @@ hipError_t probe_fixed_launch_nt(const Shape& s, const void* q, const float* cb,
                                  int32_t* ncand, int32_t* phist, const FusedPost& fp,
                                  const ProbeExtra& ex, hipStream_t st) {
   dim3 grid((s.S + NT - 1) / NT, s.B * s.H);
-  const size_t lds = probe_lds_bytes(s, NT);
+  const size_t lds = probe_lds_bytes(s, NT, DIAG);
   if (lds > 65536) {
     hipError_t e = hipFuncSetAttribute((const void*)k_probe_fixed<T, D, G, C, P, R, FUSED, DIAG, NT>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -1340,7 +1366,8 @@ hipError_t probe_fixed_launch_nt(const Shape& s, const void* q, const float* cb,
 }
 
 // The routing path's probe (lists built in the kernel, no diagnostics) also comes with 128- and 64-token
-// work-groups, for grids that 256-token groups would leave short of two per CU; the others keep 256.
+// work-groups, for shapes whose LDS holds more waves of the smaller groups and for grids that 256-token
+// groups would leave short of two per CU; the others keep 256.
 template <typename T, int D, int G, int C, int P, int R, bool FUSED, bool DIAG>
 hipError_t probe_fixed_launch_t(const Shape& s, const void* q, const float* cb, const float* bias, const float* ksum,
                                 const int32_t* off, const int32_t* idx, const int32_t* force, int32_t* sel,
@@ -1449,11 +1476,13 @@ bool probe_fixed_shape(const Shape& s) {
   return false;
 }
 
-size_t probe_lds_bytes(const Shape& s, int nt) {
+size_t probe_lds_bytes(const Shape& s, int nt, bool diag) {
   const int CP = (s.C + 15) & ~15;
   if (s.fixed_probe) {
-    // mu rows during the logits, then the work-group's candidate list (block ids and scores)
-    const size_t mu_w = (size_t)nt * (s.G * CP + 1), pairs_w = (size_t)nt * s.M * 2;
+    // mu rows during the logits, then the work-group's candidate list (block ids) and either the
+    // candidates' scores (diagnostics) or each token's top-R keys (two words each)
+    const size_t mu_w = (size_t)nt * (s.G * CP + 1);
+    const size_t pairs_w = diag ? (size_t)nt * s.M * 2 : (size_t)nt * (s.M + 2 * (s.R > 0 ? s.R : 1));
     return ((mu_w > pairs_w ? mu_w : pairs_w) + (s.csr_lds ? (size_t)(s.A + 1 + s.ne) : 0)) * 4;
   }
   const int Pg = s.P + 1 < s.C ? s.P + 1 : s.C;  // laid out for the diagnostics sizes (P + 1, R + 1)
@@ -1502,7 +1531,18 @@ bool probe_fuses_post_nt(const Shape& s, int nt) {
 }
 
 int probe_fixed_tokens(const Shape& s) {
+  // first the size whose work-groups keep the most waves resident as far as the LDS goes (160 KiB per
+  // CU, allocated in 512-byte granules with room for the kernel's few static words; counted up to
+  // four waves per SIMD, ties to the larger size, which builds the lists fewer times)...
+  auto lds_waves = [&](int nt) {
+    const size_t wg = (probe_lds_bytes(s, nt, false) + 64 + 511) / 512 * 512;
+    const long long w = (long long)(160 * 1024 / wg) * (nt / 64);
+    return w < 16 ? w : 16;
+  };
   int nt = kProbeFixedThreads;
+  for (int c = kProbeFixedThreads / 2; c >= 64 && probe_fuses_post_nt(s, c); c /= 2)
+    if (lds_waves(c) > lds_waves(nt)) nt = c;
+  // ...then smaller ones while the grid would give fewer than two work-groups per CU
   while (nt > 64 && (long long)s.B * s.H * ((s.S + nt - 1) / nt) < 2LL * kCUs && probe_fuses_post_nt(s, nt / 2))
     nt /= 2;
   return nt;

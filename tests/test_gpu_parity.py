@@ -177,11 +177,15 @@ def test_routed_attention_end_to_end(gpu_lib, name):
     assert err <= TOL[w.dtype]
 
 
-@pytest.mark.parametrize("name,over", [(n, {}) for n in NAMES] + [("sweep", dict(seq=8192))])
+@pytest.mark.parametrize("name,over", [(n, {}) for n in NAMES] + [("sweep", dict(seq=8192)),
+                                                                   ("long", dict(heads=8)),
+                                                                   ("skew", dict(batch=8, heads=8))])
 def test_diagnostics_leave_routing_unchanged(gpu_lib, name, over):
     """Asking for the routing diagnostics runs the probe with one more address and candidate ranked, in
-    256-token work-groups; without them small grids take 64-token (the test sizes) or 128-token (sweep
-    at 8K) work-groups.  Every other output must be bit-identical between the two runs."""
+    256-token work-groups, every candidate's score kept in LDS; without them the rerank keeps only each
+    token's top-R, and small grids take 64-token (the test sizes) or 128-token (sweep at 8K) work-groups,
+    the long shape 128-token ones (its LDS holds more of them; 8 heads at 8K) and the skew shape at 8 x 8
+    heads 256-token ones.  Every other output must be bit-identical between the two runs."""
     mdr = gpu_lib
     w = small(name, **over)
     inp = synth.make_core_inputs(w, 5)
