@@ -10,8 +10,9 @@ addresses), with inputs already resident in HBM.  An untimed pass of K calls
 of the library's profiling entry point, with an event before every kernel,
 gives each kernel's average duration; the timed region is then K consecutive
 calls of the same entry point, bracketed by torch.cuda.synchronize(), with
-events on the call's stream around the selected-set attention stage only (its
-kernels run last), whose average over that region is the roofline's duration.
+events on the call's stream around the selected-set attention stage only (the
+remote and local attention kernels, which run last), whose average over that
+region is the roofline's duration.
 
 Prints one JSON line: tokens/s (B*S*K / wall time), the roofline of the
 attention stage (its compulsory bytes -- Q, K, V and O once plus the selection
@@ -51,6 +52,10 @@ KERNEL_SYMBOL = {  # substrings of the kernels' symbol names in rocprofv3 output
     "attn_remote": "k_attn_remote",
     "attn_local": "k_attn_local",
 }
+# The selected-set attention stage (mdr_sel_attn) of the roofline: the remote partials and the local window
+# with the merge.  The pair binning that feeds it (attn_bin, the selection turned into per-block pair lists)
+# is timed with it and reported beside it (attention_stage.with_binning).
+STAGE_KERNELS = ("attn_remote", "attn_local")
 KERNEL_SOURCE = {
     "address": "mdr_route.hip", "post": "mdr_route.hip", "probe_rerank": "mdr_route.hip",
     "attn_bin": "mdr_pairs.hip", "attn_remote": "mdr_attn.hip", "attn_local": "mdr_attn.hip",
@@ -300,12 +305,13 @@ def selected_set_bytes(w, pairs):
         pairs * w.block * w.head_dim * 2 * e
 
 
-def attention_stage(w, t_att, pairs, stage_names):
+def attention_stage(w, t_att, pairs, stage_names, t_bin=None):
     """The selected-set attention stage against the HBM peak, three ways: (i) compulsory bytes (Q, K, V,
     O once + sel) / time -- the roofline's fraction; (ii) L2-to-fabric bytes (FETCH_SIZE + WRITE_SIZE of
     the stage's kernels, when counters for these sources exist) / time, an upper bound on what HBM served
     (the 256 MB last-level cache serves part of it); (iii) the selected-set bytes of a gather without reuse
-    / time, which counts cache-served and regrouped re-reads and so is not an HBM bandwidth."""
+    / time, which counts cache-served and regrouped re-reads and so is not an HBM bandwidth.  With t_bin
+    (the pair binning's average), (i) and (ii) again for the stage together with the binning that feeds it."""
     alg = stage_bytes(w)
     sel_b = selected_set_bytes(w, pairs)
     out = {"ms": round(t_att, 5), "alg_bytes": alg,
@@ -317,6 +323,14 @@ def attention_stage(w, t_att, pairs, stage_names):
         gbps = sum(tr) / (t_att * 1e-3) / 1e9
         out.update(l2_fabric_bytes=round(sum(tr)), l2_fabric_gbps=round(gbps, 1),
                    l2_fabric_over_compulsory=round(sum(tr) / alg, 3))
+    if t_bin is not None:
+        t = t_att + t_bin
+        wb = {"kernels": ["attn_bin", *stage_names], "ms": round(t, 5),
+              "frac_of_hbm_peak": round(alg / (t * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+        trb = [load_traffic(w, k) for k in ("attn_bin", *stage_names)]
+        if all(x is not None for x in trb):
+            wb.update(l2_fabric_bytes=round(sum(trb)), l2_fabric_over_compulsory=round(sum(trb) / alg, 3))
+        out["with_binning"] = wb
     return out
 
 
@@ -339,9 +353,9 @@ def event_overhead(hip, steps):
 
 
 def stage_span(names):
-    """Event indices bracketing the selected-set attention stage (mdr_sel_attn): the kernels whose names
-    start with "attn_", which run last in the core path."""
-    idx = [i for i, n in enumerate(names) if n.startswith("attn_")]
+    """Event indices bracketing the selected-set attention stage (mdr_sel_attn): the STAGE_KERNELS, which
+    run last in the core path."""
+    idx = [i for i, n in enumerate(names) if n in STAGE_KERNELS]
     return idx[0], idx[-1] + 1
 
 
@@ -808,7 +822,7 @@ def summarize_rocprof(stats_csv, command, w, bench_log=None, stem="routed_attent
                              f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
                              f"{float(r['Percentage']):.1f}% | {ev} |")
     if timed:
-        stage = [k for k in KERNEL_SYMBOL if k.startswith("attn_")]
+        stage = list(STAGE_KERNELS)
         avgs = [next((float(r["AverageNs"]) / 1e3 for r in rows if KERNEL_SYMBOL[k] in r["Name"]), None)
                 for k in stage]
         tot = sum(avgs) if all(x is not None for x in avgs) else None
@@ -917,7 +931,7 @@ def main(argv=None):
     for n, ms in zip(names, per):
         kernels[n] = {"ms": round(ms, 5), "design_bytes": dbytes.get(n),
                       "design_gbps": round(dbytes[n] / (ms * 1e-3) / 1e9, 1) if ms > 0 and n in dbytes else None}
-    stage_names = [n for n in names if n.startswith("attn_")]
+    stage_names = [n for n in names if n in STAGE_KERNELS]
     alg = stage_bytes(w)
     achieved = alg / (stage_ms * 1e-3) / 1e9
     tr = [load_traffic(w, n) for n in stage_names]
@@ -946,9 +960,11 @@ def main(argv=None):
                              "the stage's average duration over the timed region (HIP events on the call's stream "
                              "before its first kernel and after its last); traffic = FETCH_SIZE + WRITE_SIZE of the "
                              "stage's kernels per call, calibrated on a plain copy: bytes between the L2s and the "
-                             "fabric, served by HBM or the 256 MB last-level cache, so an upper bound on DRAM bytes"},
+                             "fabric, served by HBM or the 256 MB last-level cache, so an upper bound on DRAM bytes. "
+                             "The pair binning that feeds the stage (attn_bin) is in attention_stage.with_binning"},
         "kernels": kernels,
-        "attention_stage": attention_stage(w, stage_ms, st["pairs"], stage_names),
+        "attention_stage": attention_stage(w, stage_ms, st["pairs"], stage_names,
+                                           kernels["attn_bin"]["ms"] if "attn_bin" in kernels else None),
         "plain_entry_point_ms_per_step": round(plain / a.steps * 1e3, 4),
         "event_overhead_ms": round(ev_overhead, 5),
         "profiled_step_ms_p10_p50_p90": run.step_quantiles,

@@ -50,7 +50,7 @@ def test_design_bytes_of_the_attention_kernels():
 
 def test_stage_span_brackets_the_attention_kernels():
     names = ["address", "post", "probe_rerank", "attn_bin", "attn_remote", "attn_local"]
-    assert bench.stage_span(names) == (3, 6)
+    assert bench.stage_span(names) == (4, 6)
     assert bench.stage_span(["address", "probe_rerank", "attn_local"]) == (2, 3)
 
 
