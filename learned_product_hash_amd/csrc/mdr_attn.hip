@@ -113,12 +113,12 @@ __global__ __launch_bounds__(kRemoteWaves * 64) void k_attn_remote(const T* __re
   }
 }
 
-// One work-group per query block: local blocks + merge of the remote partials.  Every read that
-// does not depend on another is issued at the start: the query rows, the first local block of K/V
-// (held in registers until the LDS takes it; each later block is read while the previous one is
-// scored), the selection row and the first RS = min(R, 2) remote partials (their addresses do not
-// depend on the selection; unused ones are ignored).  RS is a template argument so that these
-// reads form one straight-line block the compiler need not wait on early.
+// One work-group per query block: local blocks + merge of the remote partials.  The selection row,
+// the first local block of K/V (held in registers until the LDS takes it; each later block is read
+// while the previous one is scored) and the query rows are read at the start; with the last (diagonal)
+// block, the partials of the row's first RS = min(R, 2) entries are requested, only for the entries
+// the token uses, so that no unused partial row is fetched.  RS is a template
+// argument so that these reads form one straight-line block the compiler need not wait on early.
 
 // bf16 tiles are held to four waves per SIMD with D <= 64 (four 256-thread work-groups per CU) and to
 // two with D = 128 (left free, that shape took one wave per SIMD).
@@ -142,26 +142,34 @@ __global__ __launch_bounds__(BLK * 4) __attribute__((amdgpu_waves_per_eu(local_m
   const int c4 = 4 * (lane >> 4);
   const size_t rowbase = (size_t)bh * s.S;
   const int j0 = max(0, j - s.L + 1);
+  const int32_t* row = sel + (rowbase + t) * s.R;
+  constexpr int RA = RS > 0 ? RS : 1;
+  int sr[RA];
+#pragma unroll
+  for (int r = 0; r < RS; ++r) sr[r] = row[r];
   KVRegs<T, D, BLK, NTHR> kv;
   kv.load(K + (rowbase + (size_t)j0 * BLK) * D, V + (rowbase + (size_t)j0 * BLK) * D, tid);
   QFrag<T, D> qf;
   load_q<T, D>(qf, Q + (rowbase + t) * D, lane);
-  // reads complete in issue order: keep the K/V and query reads ahead of the partials, which are
-  // needed last
-  __builtin_amdgcn_sched_barrier(0);
-  const int32_t* row = sel + (rowbase + t) * s.R;
-  constexpr int RA = RS > 0 ? RS : 1;
-  int sr[RA];
+  // the first RS partials are requested with the diagonal block, only those of used entries: entry r
+  // counts when 0 <= sel <= j - L and it does not repeat an earlier entry of the row
+  bool use[RA];
   float plse[RA];
   Raw4<T> praw[RA][TL::ND];
+  auto request_partials = [&]() __attribute__((always_inline)) {
 #pragma unroll
-  for (int r = 0; r < RS; ++r) {
-    const size_t pr = (rowbase + t) * s.R + r;
-    sr[r] = row[r];
-    plse[r] = part_lse[pr];
+    for (int r = 0; r < RS; ++r) {
+      bool ok = sr[r] >= 0 && sr[r] <= j - s.L;
 #pragma unroll
-    for (int dt = 0; dt < TL::ND; ++dt) praw[r][dt] = *(const Raw4<T>*)(part_o + pr * D + 16 * dt + c4);
-  }
+      for (int p = 0; p < r; ++p) ok = ok && sr[p] != sr[r];
+      use[r] = ok;
+      const size_t pr = (rowbase + t) * s.R + r;
+      plse[r] = ok ? part_lse[pr] : 0.f;
+#pragma unroll
+      for (int dt = 0; dt < TL::ND; ++dt)
+        praw[r][dt] = ok ? *(const Raw4<T>*)(part_o + pr * D + 16 * dt + c4) : Raw4<T>{};
+    }
+  };
   const float c = s.scale * kLog2e;
   float m = -INFINITY, l = 0.f;
   f32x4 o[TL::ND];
@@ -178,6 +186,7 @@ __global__ __launch_bounds__(BLK * 4) __attribute__((amdgpu_waves_per_eu(local_m
       const size_t nx = (rowbase + (size_t)(jj + 1) * BLK) * D;
       kv.load(K + nx, V + nx, tid);
     }
+    if (jj == j) request_partials();
     f32x4 p[TL::NT];
     float mx = -INFINITY;
 #pragma unroll
@@ -216,9 +225,8 @@ __global__ __launch_bounds__(BLK * 4) __attribute__((amdgpu_waves_per_eu(local_m
     for (int jj = j0; jj < j; ++jj) block_step(std::false_type{}, jj);
     block_step(std::true_type{}, j);
   }
-  // merge the remote partials in slot order: entry r counts when 0 <= sel <= j - L and it does not
-  // repeat an earlier entry of the row.  A partial with normalised output o_r and log2 normaliser
-  // lse_r carries the weight 2^lse_r.
+  // merge the remote partials in slot order (the used entries above, then for R > RS the rest of the
+  // row).  A partial with normalised output o_r and log2 normaliser lse_r carries the weight 2^lse_r.
   auto merge = [&](float lr, const Raw4<T> (&po)[TL::ND]) __attribute__((always_inline)) {
     const float mnew = fmaxf(m, lr);
     const float a = fast_exp2(m - mnew);
@@ -229,12 +237,8 @@ __global__ __launch_bounds__(BLK * 4) __attribute__((amdgpu_waves_per_eu(local_m
     m = mnew;
   };
 #pragma unroll
-  for (int r = 0; r < RS; ++r) {
-    bool ok = sr[r] >= 0 && sr[r] <= j - s.L;
-#pragma unroll
-    for (int p = 0; p < r; ++p) ok = ok && sr[p] != sr[r];
-    if (ok) merge(plse[r], praw[r]);
-  }
+  for (int r = 0; r < RS; ++r)
+    if (use[r]) merge(plse[r], praw[r]);
   if constexpr (TAIL) {
     // slots RS .. R-1 (R > RS): the whole row is read at once, then the used slots' partials two at a
     // time, both requested before either is merged
