@@ -117,8 +117,9 @@ __global__ __launch_bounds__(kRemoteWaves * 64) void k_attn_remote(const T* __re
 // the first local block of K/V (held in registers until the LDS takes it; each later block is read
 // while the previous one is scored) and the query rows are read at the start; with the last (diagonal)
 // block, the partials of the row's first RS = min(R, 2) entries are requested, only for the entries
-// the token uses, so that no unused partial row is fetched.  RS is a template
-// argument so that these reads form one straight-line block the compiler need not wait on early.
+// the token uses, so that no unused partial row is fetched (and their registers are live only
+// through that block).  RS is a template argument so that these reads form one straight-line block
+// the compiler need not wait on early.
 
 // bf16 tiles are held to four waves per SIMD with D <= 64 (four 256-thread work-groups per CU) and to
 // two with D = 128 (left free, that shape took one wave per SIMD).
