@@ -250,6 +250,42 @@ __device__ inline int block_exclusive_scan(int v, int* tmp, int* total) {
   return before + x - v;
 }
 
+// Two exclusive scans at once (a and b per thread, NT a multiple of 64), with the barriers of one.
+// tmp holds 2 NT/64 ints.  Returns a's exclusive prefix, *b_before b's; *total_a, *total_b the sums.
+template <int NT>
+__device__ inline int block_exclusive_scan2(int a, int b, int* tmp, int* total_a, int* total_b, int* b_before) {
+  constexpr int NW = NT / 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = a, y = b;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int xa = __shfl_up(x, o), yb = __shfl_up(y, o);
+    if (lane >= o) {
+      x += xa;
+      y += yb;
+    }
+  }
+  if (lane == 63) {
+    tmp[wave] = x;
+    tmp[NW + wave] = y;
+  }
+  lds_barrier();
+  int ba = 0, sa = 0, bb = 0, sb = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const int ta = tmp[w], tb = tmp[NW + w];
+    ba += (w < wave) ? ta : 0;
+    bb += (w < wave) ? tb : 0;
+    sa += ta;
+    sb += tb;
+  }
+  lds_barrier();
+  *total_a = sa;
+  *total_b = sb;
+  *b_before = bb + y - b;
+  return ba + x - a;
+}
+
 // Profiling events: entry i of an optional event array is recorded on the stream when present
 // (a null array or a null entry records nothing).
 inline hipError_t mark_event(hipEvent_t* ev, int i, hipStream_t st) {

@@ -55,7 +55,7 @@ __global__ __launch_bounds__(kScatterThreads) void k_pair_scatter(const int32_t*
                                                               int32_t* __restrict__ poff, int32_t* __restrict__ ioff,
                                                               int32_t* __restrict__ items, Shape s) {
   extern __shared__ int sm[];
-  __shared__ int scan_tmp[kScatterThreads / 64];
+  __shared__ int scan_tmp[2 * (kScatterThreads / 64)];
   const int ne = s.ne, g = blockIdx.x, bh = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nwf = scatter_waves(ne);
@@ -102,9 +102,8 @@ __global__ __launch_bounds__(kScatterThreads) void k_pair_scatter(const int32_t*
     sum += start[a];
     isum += (start[a] + kItemPairs - 1) / kItemPairs;
   }
-  int total, itot;
-  int run = block_exclusive_scan<kScatterThreads>(sum, scan_tmp, &total);
-  int irun = block_exclusive_scan<kScatterThreads>(isum, scan_tmp, &itot);
+  int total, itot, irun;
+  int run = block_exclusive_scan2<kScatterThreads>(sum, isum, scan_tmp, &total, &itot, &irun);
   int32_t* po = poff + (size_t)bh * (ne + 1);
   int32_t* io = ioff + (size_t)bh * (ne + 1);
   int32_t* it = items + item_record(s, bh, 0);
@@ -133,28 +132,47 @@ __global__ __launch_bounds__(kScatterThreads) void k_pair_scatter(const int32_t*
   int nbits = 0;
   while ((1 << nbits) < ne) ++nbits;
   const unsigned long long lt = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+  // a token's entries are used when eligible (0 <= i <= j - L) and not repeated by an earlier entry.
+  // When R divides 64 the R entries of a token sit in adjacent lanes of one wave (entry x of the piece
+  // is in lane x % 64), so each lane tests its own entry against the earlier ones by lane shuffles
+  // before the keys are staged; otherwise the thread that owns a token rewrites its staged row.
+  const bool lane_rows = 64 % s.R == 0;  // then R is a power of two, as the block size always is
+  const int rsh = __builtin_ctz(s.R), bsh = __builtin_ctz(s.blk);
   for (int t0 = tfirst; t0 < tlast; t0 += tps) {
     const int nt = min(tps, tlast - t0), np = nt * s.R;
     const int share = ((np + nwf - 1) / nwf + 63) & ~63;
     if (t0 != tfirst) load_piece(t0);  // the piece's entries, all requested at once
+    if (lane_rows) {
+#pragma unroll
+      for (int u = 0; u < kSubPairs / kScatterThreads; ++u) {
+        const int x = u * kScatterThreads + tid, r = x & (s.R - 1);
+        const int e = v[u];
+        bool ok = e >= 0 && e <= ((t0 + (x >> rsh)) >> bsh) - s.L;
+        for (int q = 1; q < s.R; ++q) {
+          const int prev = __shfl(e, lane - q < 0 ? 0 : lane - q);
+          ok = ok && !(q <= r && prev == e);
+        }
+        v[u] = ok ? e : -1;
+      }
+    }
     __syncthreads();  // the previous piece is filed: its keys and the counts are free
 #pragma unroll
     for (int u = 0; u < kSubPairs / kScatterThreads; ++u) keys[u * kScatterThreads + tid] = v[u];
     for (int x = tid; x < nwf * ne; x += kScatterThreads) wc[x] = 0;
     __syncthreads();
-    // a token's entries are used when eligible (0 <= i <= j - L) and not repeated by an earlier entry;
-    // the thread that owns a token rewrites its row in place
-    for (int u = tid; u < nt; u += kScatterThreads) {
-      int* row = keys + u * s.R;
-      const int cutoff = (t0 + u) / s.blk - s.L;
-      for (int r = s.R - 1; r >= 0; --r) {
-        const int e = row[r];
-        bool ok = e >= 0 && e <= cutoff;
-        for (int q = 0; q < r; ++q) ok = ok && row[q] != e;
-        row[r] = ok ? e : -1;
+    if (!lane_rows) {
+      for (int u = tid; u < nt; u += kScatterThreads) {
+        int* row = keys + u * s.R;
+        const int cutoff = (t0 + u) / s.blk - s.L;
+        for (int r = s.R - 1; r >= 0; --r) {
+          const int e = row[r];
+          bool ok = e >= 0 && e <= cutoff;
+          for (int q = 0; q < r; ++q) ok = ok && row[q] != e;
+          row[r] = ok ? e : -1;
+        }
       }
+      __syncthreads();
     }
-    __syncthreads();
     const int pw0 = min(np, wave * share), pw1 = min(np, pw0 + share);
     if (wave < nwf)
       for (int p = pw0 + lane; p < pw1; p += 64) {
