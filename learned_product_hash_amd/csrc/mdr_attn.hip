@@ -137,6 +137,9 @@ __global__ __launch_bounds__(BLK * 4) __attribute__((amdgpu_waves_per_eu(local_m
   T* Vx = Ks + TL::K_ELEMS;
   int j, bh;
   query_block_of(s, blockIdx.x, gridDim.x, &bh, &j);  // query blocks of one head in order per XCD
+  // walked from the last query block down: the remote kernel just before ends with the highest
+  // blocks' items, so their K/V, the top tokens' query rows and partials are then still in the L2
+  j = s.nb - 1 - j;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int qi = wave * 16 + (lane & 15);
   const int t = j * BLK + qi;
