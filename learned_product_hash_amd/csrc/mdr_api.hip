@@ -261,11 +261,11 @@ bool routing_aligned(const mdr_routing* r) {
 mdr_status run_core(const Shape& s, const void* q, const void* k, const void* v, const float* cb, const float* bias,
                     const int32_t* force, void* out, const Buffers& b, hipStream_t st, hipEvent_t* ev = nullptr,
                     bool have_address = false) {
-  const bool remote = s.R > 0 && s.ne > 0;
+  const bool binned = pairs_binned(s);  // else the remote kernel scans the selection itself
   MDR_TRY(mark_event(ev, 0, st));
   const bool redirect = s.policy == MDR_OVERFLOW_REDIRECT;
   if (!have_address)
-    MDR_TRY(launch_address(s, k, cb, bias, b.ksum, b.addr, remote ? b.phist : nullptr, st, 0, -1,
+    MDR_TRY(launch_address(s, k, cb, bias, b.ksum, b.addr, binned ? b.phist : nullptr, st, 0, -1,
                            redirect ? b.alt : nullptr, b.amargin));
   MDR_TRY(mark_event(ev, 1, st));
   // the posting lists are built inside the probe kernel where a specialised probe exists (the post
@@ -278,9 +278,9 @@ mdr_status run_core(const Shape& s, const void* q, const void* k, const void* v,
   const ProbeExtra ex{redirect ? b.roff : nullptr, b.ridx, b.rtime, b.ndrop, b.probes, b.sel_score, b.pmargin,
                       b.smargin};
   MDR_TRY(launch_probe_rerank(s, q, cb, bias, b.ksum, b.off, b.idx, force, b.sel, b.ncand,
-                              remote ? b.phist : nullptr, st, fused ? &fp : nullptr, ex));
+                              binned ? b.phist : nullptr, st, fused ? &fp : nullptr, ex));
   MDR_TRY(mark_event(ev, 3, st));
-  MDR_TRY(launch_pair_scatter(s, b.sel, b.phist, b.poff, b.ioff, b.items, st));
+  if (binned) MDR_TRY(launch_pair_scatter(s, b.sel, b.phist, b.poff, b.ioff, b.items, st));
   MDR_TRY(launch_attend(s, q, k, v, b.sel, out, b, st, ev ? ev + 4 : nullptr));
   MDR_TRY(mark_event(ev, MDR_CORE_KERNELS, st));
   return MDR_OK;
@@ -440,9 +440,8 @@ mdr_status mdr_mixer_forward(const mdr_config* cfg, const void* x, const void* w
   const int tfirst = fused ? 0 : 3, tlast = project_out_tiled(s) ? 4 : 3;
   MDR_TRY(launch_transpose_weights(s, wq, wk, wv, wo, b.mwt, tfirst, tlast - tfirst, hs));
   if (fused) {
-    const bool remote = s.R > 0 && s.ne > 0;
     MDR_TRY(launch_qkv_fused(s, x, b.mq, b.mk, b.mv, codebook, code_bias, b.ksum, b.addr,
-                             s.policy == MDR_OVERFLOW_REDIRECT ? b.alt : nullptr, remote ? b.phist : nullptr,
+                             s.policy == MDR_OVERFLOW_REDIRECT ? b.alt : nullptr, pairs_binned(s) ? b.phist : nullptr,
                              b.mwt, hs, b.amargin));
   } else {
     MDR_TRY(launch_project_heads(s, x, wq, b.mq, true, hs));
@@ -512,7 +511,7 @@ mdr_status mdr_stage_attend_lse(const mdr_config* cfg, const void* q, const void
   if (st != MDR_OK) return st;
   b.lse = lse;
   hipStream_t hs = (hipStream_t)stream;
-  if (s.R > 0 && s.ne > 0) {
+  if (pairs_binned(s)) {
     MDR_TRY(launch_pair_count(s, sel, b.phist, hs));
     MDR_TRY(launch_pair_scatter(s, sel, b.phist, b.poff, b.ioff, b.items, hs));
   }
@@ -668,6 +667,26 @@ mdr_status mdr_selfcheck_indices(const mdr_config* cfg, char* msg, size_t msg_le
         istart += ni;
       }
     }
+  }
+  // the scanning remote kernel (short sequences): a bijection onto (b,h, eligible block i); the
+  // selection rows it reads (tokens (i + L) blk .. S - 1) and the pair ids it can form stay inside
+  if (remote && remote_scans(s)) {
+    const int n = (int)(BH * s.ne);
+    char* seen = (char*)calloc((size_t)n, 1);
+    if (!seen) return MDR_ERR_UNSUPPORTED;
+    const long long n_plse = (long long)(region_bytes(regs, nr, b.part_lse) / 4);
+    for (int id = 0; id < n && ck.ok; ++id) {
+      int bh, i;
+      remote_block_of(s, id, n, &bh, &i);
+      ck.in("scanned block", (long long)bh * s.ne + i, n);
+      if (!ck.ok) break;
+      if (seen[(size_t)bh * s.ne + i]++) ck.fail("scanned block mapped twice", i, s.ne);
+      ck.in("scan length", (long long)(s.S - (i + s.L) * s.blk), kScanMaxTokens + 1);
+      ck.in("scanned K/V row", (long long)(block_row(s, bh, i) + s.blk - 1), rows);
+      ck.in("scanned selection entry", ((long long)bh * s.S + s.S - 1) * s.R + s.R - 1, rows * s.R);
+      ck.in("scanned partial", (long long)partial_index(s, bh, s.S * s.R - 1), n_plse);
+    }
+    free(seen);
   }
   // query-block kernels (local attention, backward dQ): a bijection onto (b,h, j), windows inside
   {

@@ -44,6 +44,49 @@ __global__ __launch_bounds__(256) void k_fill(int32_t* p, long long n, int32_t v
   for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long long)gridDim.x * 256) p[i] = value;
 }
 
+// One wave's 16 (token, slot) pairs against the block staged in Ks / Vx: lane l's query is pair
+// l % 16 (qf, read from that pair's token row), pid its pair id t R + r (< 0: no pair, nothing is
+// stored).  Each pair's partial -- the output row normalised by its own sum and the log2 normaliser --
+// goes to [token][slot].  A pair's products depend on its own query column alone, so the partial does
+// not depend on which other pairs share the wave.
+template <typename T, int D, int BLK>
+__device__ __forceinline__ void remote_partials(const QFrag<T, D>& qf, const T* Ks, const T* Vx, int pid, int bh,
+                                                const Shape& s, T* __restrict__ part_o,
+                                                float* __restrict__ part_lse, int lane) {
+  using TL = Tile<T, D, BLK>;
+  // softmax in base 2 with the scale folded in: p = 2^(c s - c max s), c = scale * log2(e) > 0
+  const float c = s.scale * kLog2e;
+  f32x4 p[TL::NT];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int nn = 0; nn < TL::NT; ++nn) {
+    p[nn] = score_tile<T, D, BLK>(qf, Ks, nn, lane);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) mx = fmaxf(mx, p[nn][kk]);
+  }
+  mx = c * wave_max16(mx);
+  float sum = 0.f;
+#pragma unroll
+  for (int nn = 0; nn < TL::NT; ++nn)
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      p[nn][kk] = fast_exp2(fmaf(p[nn][kk], c, -mx));
+      sum += p[nn][kk];
+    }
+  sum = wave_sum16(sum);
+  f32x4 o[TL::ND];
+#pragma unroll
+  for (int dt = 0; dt < TL::ND; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  pv_block<T, D, BLK>(o, p, Vx, lane);
+  if (pid >= 0) {
+    const size_t pr = partial_index(s, bh, pid);  // the pair (token, slot)
+    const float inv = 1.f / sum;
+#pragma unroll
+    for (int dt = 0; dt < TL::ND; ++dt) store4<T>(part_o + pr * D + 16 * dt + 4 * (lane >> 4), o[dt], inv);
+    if ((lane >> 4) == 0) part_lse[pr] = mx + log2f(sum);
+  }
+}
+
 // One work-group per remote work item: kItemPairs pairs (or fewer) of one block's pair list, 16 per
 // wave.  The item record (block and pair ids in one read), then the block's K/V and the pairs' query
 // rows: two dependent reads ahead of the products.
@@ -80,37 +123,101 @@ __global__ __launch_bounds__(kRemoteWaves * 64) void k_attn_remote(const T* __re
   kv.store(Ks, Vx, tid);
   __syncthreads();
   if (wave * 16 >= n) return;  // no pairs for this wave (no barriers below)
-  // softmax in base 2 with the scale folded in: p = 2^(c s - c max s), c = scale * log2(e) > 0
-  const float c = s.scale * kLog2e;
-  f32x4 p[TL::NT];
-  float mx = -INFINITY;
+  remote_partials<T, D, BLK>(qf, Ks, Vx, pid, bh, s, part_o, part_lse, lane);
+}
+
+// Short sequences (remote_scans): one work-group per (b,h, eligible block i) finds the pairs that
+// selected block i itself, from the selection rows of the tokens that can see it (query blocks i + L
+// and later), so that no binning pass runs before it.  Thread tid reads the rows of tokens
+// t0 + c NTHR + tid; a token contributes its first entry equal to i (a repeat of an earlier entry of
+// the row is not a pair).  The pair ids are compacted into LDS in ascending token order (per-wave
+// ballot counts, one scan), then go 16 per wave, kItemPairs at a time, through remote_partials: the
+// same partials, bit for bit, as the binned kernel's.
+template <typename T, int D, int BLK, int R>
+__global__ __launch_bounds__(kRemoteWaves * 64) void k_attn_remote_scan(const T* __restrict__ Q,
+                                                                        const T* __restrict__ K,
+                                                                        const T* __restrict__ V,
+                                                                        const int32_t* __restrict__ sel,
+                                                                        T* __restrict__ part_o,
+                                                                        float* __restrict__ part_lse, Shape s) {
+  using TL = Tile<T, D, BLK>;
+  constexpr int NTHR = kRemoteWaves * 64;
+  constexpr int ROWS = kScanMaxTokens / NTHR;  // selection rows per thread
+  constexpr int NC = ROWS * kRemoteWaves;      // wave counts, (row, wave)-major = ascending tokens
+  static_assert(NC == 2 * 64, "the count scan takes two counts per lane of one wave");
+  extern __shared__ __align__(16) char lds_raw[];
+  T* Ks = (T*)lds_raw;
+  T* Vx = Ks + TL::K_ELEMS;
+  int32_t* cnt = (int32_t*)(Vx + TL::V_ELEMS);  // NC counts, then their exclusive scan; [NC] = total
+  int32_t* list = cnt + NC + 4;                 // the block's pair ids
+  int bh, i;
+  remote_block_of(s, blockIdx.x, gridDim.x, &bh, &i);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const size_t rowbase = (size_t)bh * s.S;
+  KVRegs<T, D, BLK, NTHR> kv;
+  kv.load(K + block_row(s, bh, i) * D, V + block_row(s, bh, i) * D, tid);
+  const int t0 = (i + s.L) * BLK;
+  int e[ROWS][R];
 #pragma unroll
-  for (int nn = 0; nn < TL::NT; ++nn) {
-    p[nn] = score_tile<T, D, BLK>(qf, Ks, nn, lane);
+  for (int c = 0; c < ROWS; ++c) {
+    const int t = t0 + c * NTHR + tid;
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) mx = fmaxf(mx, p[nn][kk]);
+    for (int r = 0; r < R; ++r) e[c][r] = t < s.S ? sel[(rowbase + t) * R + r] : -1;
   }
-  mx = c * wave_max16(mx);
-  float sum = 0.f;
+  // 2 bits per row: 1 + the slot of the token's pair with block i, 0 for none
+  unsigned hits = 0;
+  unsigned long long bal[ROWS];
 #pragma unroll
-  for (int nn = 0; nn < TL::NT; ++nn)
+  for (int c = 0; c < ROWS; ++c) {
+    int h = 0;
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      p[nn][kk] = fast_exp2(fmaf(p[nn][kk], c, -mx));
-      sum += p[nn][kk];
+    for (int r = R - 1; r >= 0; --r)
+      if (e[c][r] == i) h = r + 1;
+    hits |= (unsigned)h << (2 * c);
+    bal[c] = __ballot(h != 0);
+    if (lane == 0) cnt[c * kRemoteWaves + wave] = __popcll(bal[c]);
+  }
+  kv.store(Ks, Vx, tid);
+  __syncthreads();
+  if (wave == 0) {
+    const int a = cnt[2 * lane], b = cnt[2 * lane + 1];
+    int x = a + b;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int y = __shfl_up(x, d);
+      if (lane >= d) x += y;
     }
-  sum = wave_sum16(sum);
-  f32x4 o[TL::ND];
-#pragma unroll
-  for (int dt = 0; dt < TL::ND; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  pv_block<T, D, BLK>(o, p, Vx, lane);
-  if (pid >= 0) {
-    const size_t pr = partial_index(s, bh, pid);  // the pair (token, slot)
-    const float inv = 1.f / sum;
-#pragma unroll
-    for (int dt = 0; dt < TL::ND; ++dt) store4<T>(part_o + pr * D + 16 * dt + 4 * (lane >> 4), o[dt], inv);
-    if ((lane >> 4) == 0) part_lse[pr] = mx + log2f(sum);
+    cnt[2 * lane] = x - a - b;
+    cnt[2 * lane + 1] = x - b;
+    if (lane == 63) cnt[NC] = x;
   }
+  __syncthreads();
+  const unsigned long long below = (1ull << lane) - 1ull;
+#pragma unroll
+  for (int c = 0; c < ROWS; ++c) {
+    const int h = (hits >> (2 * c)) & 3;
+    if (h) list[cnt[c * kRemoteWaves + wave] + __popcll(bal[c] & below)] = (t0 + c * NTHR + tid) * R + h - 1;
+  }
+  __syncthreads();
+  const int n = cnt[NC];
+#pragma unroll 1
+  for (int base = wave * 16; base < n; base += kItemPairs) {  // no barriers in this loop
+    const int e = base + (lane & 15);
+    const int pid = e < n ? list[e] : -1;
+    QFrag<T, D> qf;
+    load_q<T, D>(qf, Q + (rowbase + (pid < 0 ? 0 : pid / R)) * D, lane);
+    // the tiles are read again in every round: an offset the compiler cannot see through keeps it from
+    // holding the whole block's operands in registers across rounds
+    int off = 0;
+    asm volatile("" : "+s"(off));
+    remote_partials<T, D, BLK>(qf, Ks + off, Vx + off, pid, bh, s, part_o, part_lse, lane);
+  }
+}
+
+// LDS of k_attn_remote_scan: the block's K/V, the wave counts and the pair list.
+template <typename T, int D, int BLK>
+constexpr size_t scan_lds_bytes() {
+  return Tile<T, D, BLK>::LDS_BYTES + (size_t)(kScanMaxTokens / (kRemoteWaves * 64) * kRemoteWaves + 4 + kScanMaxTokens) * 4;
 }
 
 // One work-group per query block: local blocks + merge of the remote partials.  The selection row,
@@ -301,7 +408,20 @@ hipError_t attend_impl(const Shape& s, const void* q, const void* k, const void*
   const bool remote = s.R > 0 && s.ne > 0;
   hipError_t e;
   if ((e = mark_event(ev, 0, st)) != hipSuccess) return e;
-  if (remote) {
+  if (remote && remote_scans(s)) {
+    const size_t rl = scan_lds_bytes<T, D, BLK>();
+    const void* kfn = s.R == 2 ? (const void*)k_attn_remote_scan<T, D, BLK, 2> : (const void*)k_attn_remote_scan<T, D, BLK, 1>;
+    if (rl > 65536 && (e = hipFuncSetAttribute(kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)rl)) != hipSuccess)
+      return e;
+    const unsigned grid = (unsigned)(s.B * s.H * s.ne);
+    if (s.R == 2)
+      hipLaunchKernelGGL((k_attn_remote_scan<T, D, BLK, 2>), dim3(grid), dim3(kRemoteWaves * 64), rl, st, (const T*)q,
+                         (const T*)k, (const T*)v, sel, (T*)b.part_o, b.part_lse, s);
+    else
+      hipLaunchKernelGGL((k_attn_remote_scan<T, D, BLK, 1>), dim3(grid), dim3(kRemoteWaves * 64), rl, st, (const T*)q,
+                         (const T*)k, (const T*)v, sel, (T*)b.part_o, b.part_lse, s);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  } else if (remote) {
     const size_t rl = remote_lds_bytes(s);
     if (rl > 65536 && (e = hipFuncSetAttribute((const void*)k_attn_remote<T, D, BLK>,
                                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)rl)) != hipSuccess)
@@ -315,6 +435,16 @@ hipError_t attend_impl(const Shape& s, const void* q, const void* k, const void*
          : s.R == 2 ? launch_local<T, D, BLK, 2>(s, q, k, v, sel, out, b, st)
          : s.R == 1 ? launch_local<T, D, BLK, 1>(s, q, k, v, sel, out, b, st)
                     : launch_local<T, D, BLK, 0>(s, q, k, v, sel, out, b, st);
+}
+
+template <typename T, int D>
+size_t scan_lds_d(int blk) {
+  return blk == 32 ? scan_lds_bytes<T, D, 32>() : blk == 64 ? scan_lds_bytes<T, D, 64>() : scan_lds_bytes<T, D, 128>();
+}
+
+template <typename T>
+size_t scan_lds_t(const Shape& s) {
+  return s.D == 32 ? scan_lds_d<T, 32>(s.blk) : s.D == 64 ? scan_lds_d<T, 64>(s.blk) : scan_lds_d<T, 128>(s.blk);
 }
 
 template <typename T, int D>
@@ -365,6 +495,11 @@ hipError_t launch_fill(int32_t* p, long long n, int32_t value, hipStream_t st) {
   if (blocks > 4096) blocks = 4096;
   hipLaunchKernelGGL(k_fill, dim3((unsigned)blocks), dim3(256), 0, st, p, n, value);
   return hipGetLastError();
+}
+
+bool remote_scans(const Shape& s) {
+  if (s.R < 1 || s.R > 2 || s.ne <= 0 || s.S > kScanMaxTokens) return false;
+  return (s.dtype == MDR_BF16 ? scan_lds_t<bf16>(s) : scan_lds_t<float>(s)) <= 160 * 1024;
 }
 
 size_t remote_lds_bytes(const Shape& s) {

@@ -146,6 +146,16 @@ __host__ __device__ inline void remote_work_of(const Shape& s, long long id, int
     *k = (int)(id % s.max_items);
   }
 }
+// Short sequences: the remote attention kernel finds each block's pairs itself, with no binning
+// pass before it (remote_scans), when a block's candidate tokens fit one scan: S <= kScanMaxTokens.
+constexpr int kScanMaxTokens = 8192;
+// The scanning remote kernel's work-group id -> (b,h, eligible block i), the blocks of one head in
+// order per XCD.  A bijection onto B H ne for n = B H ne.
+__host__ __device__ inline void remote_block_of(const Shape& s, int id, int n, int* bh, int* i) {
+  const int wg = xcd_chunked(id, n);
+  *i = wg % s.ne;
+  *bh = wg / s.ne;
+}
 __host__ __device__ inline long long remote_grid(const Shape& s) {
   const long long bh = (long long)s.B * s.H;
   return (s.pin ? (bh + kXcds - 1) / kXcds * kXcds : bh) * s.max_items;
@@ -349,6 +359,11 @@ hipError_t launch_pair_scatter(const Shape& s, const int32_t* sel, const int32_t
                                int32_t* ioff, int32_t* items, hipStream_t st);
 size_t pair_scatter_lds_bytes(const Shape& s);
 size_t remote_lds_bytes(const Shape& s);
+// True when the forward's remote attention scans the selection itself (k_attn_remote_scan: S <=
+// kScanMaxTokens, R <= 2, its LDS fits): no pair binning runs, and the probe kernels need not count.
+bool remote_scans(const Shape& s);
+// True when the forward's remote pairs go through the binning (pair counts, scatter, work items).
+inline bool pairs_binned(const Shape& s) { return s.R > 0 && s.ne > 0 && !remote_scans(s); }
 // The attention of a selection whose pairs are binned (items).  ev (optional, 2 entries):
 // recorded before attn_remote and attn_local.
 hipError_t launch_attend(const Shape& s, const void* q, const void* k, const void* v,
