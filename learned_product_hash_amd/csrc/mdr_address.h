@@ -147,7 +147,7 @@ __device__ __forceinline__ void address_from_summary(const CodeSlice<D>& cs, con
 // All 256 threads of the work-group call it (it contains barriers).  The codebook rows are
 // requested together with the key rows.  Writes ksum[bh, i, :] and addr[bh, i], and when `alt` is
 // given the block's alternate address (see address_from_summary).
-template <typename T, int D>
+template <typename T, int D, int BLK = 128>
 __device__ __forceinline__ void block_address(const T* __restrict__ K, const float* __restrict__ cb,
                                               const float* __restrict__ bias, float* __restrict__ ksum,
                                               int32_t* __restrict__ addr, int i, int bh, AddressLds<T, D>& sm,
@@ -165,10 +165,25 @@ __device__ __forceinline__ void block_address(const T* __restrict__ K, const flo
   float acc4[VEC];
 #pragma unroll
   for (int e = 0; e < VEC; ++e) acc4[e] = 0.f;
-  for (int r = rg; r < s.blk; r += RG) {
-    typename Vec16<T>::type v = *(const typename Vec16<T>::type*)(base + (size_t)r * D + ch * VEC);
+  // rows rg, rg + RG, ... of the block, all requested before the first is added (BLK: the largest
+  // block this instantiation takes; a slot past the block reads its last row and adds nothing), then
+  // added in that order.  No branches around the reads, so that the compiler need not wait on one
+  // before issuing the next.
+  constexpr int RMAX = (BLK + RG - 1) / RG;
+  typename Vec16<T>::type v[RMAX];
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) acc4[e] += to_f(v[e]);
+  for (int u = 0; u < RMAX; ++u) {
+    const int r = min(rg + u * RG, s.blk - 1);
+    v[u] = *(const typename Vec16<T>::type*)(base + (size_t)r * D + ch * VEC);
+  }
+#pragma unroll
+  for (int u = 0; u < RMAX; ++u) {
+    const bool in = rg + u * RG < s.blk;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      const float x = acc4[e] + to_f(v[u][e]);
+      acc4[e] = in ? x : acc4[e];
+    }
   }
 #pragma unroll
   for (int e = 0; e < VEC; ++e) sm.red[rg][ch * VEC + e] = acc4[e];

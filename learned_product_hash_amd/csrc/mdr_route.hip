@@ -29,7 +29,7 @@ namespace {
 // Block key summaries and product addresses: one work-group of 256 threads per (b,h, block); the
 // arithmetic is block_address() (mdr_address.h), shared with the decode path.  The work-group of
 // block i also clears column i of the pair counters when asked.
-template <typename T, int D>
+template <typename T, int D, int BLK>
 __global__ __launch_bounds__(256) void k_address(const T* __restrict__ K, const float* __restrict__ cb,
                                                  const float* __restrict__ bias, float* __restrict__ ksum,
                                                  int32_t* __restrict__ addr, int32_t* __restrict__ pair_zero,
@@ -39,7 +39,7 @@ __global__ __launch_bounds__(256) void k_address(const T* __restrict__ K, const 
   const int i = i0 + blockIdx.x;
   const int bh = blockIdx.y;
   if (pair_zero) clear_pair_counts(pair_zero, s, bh, i, threadIdx.x, 256);
-  block_address<T, D>(K, cb, bias, ksum, addr, i, bh, sm, s, alt, amargin);
+  block_address<T, D, BLK>(K, cb, bias, ksum, addr, i, bh, sm, s, alt, amargin);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -1327,25 +1327,34 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(probe_min_wa
   pc.end();
 }
 
+template <typename T, int D>
+hipError_t address_launch_d(const Shape& s, dim3 grid, const void* k, const float* cb, const float* bias, float* ksum,
+                            int32_t* addr, int32_t* cnt, int32_t* alt, float* am, int i0, hipStream_t st) {
+  switch (s.blk) {
+    case 32:
+      hipLaunchKernelGGL((k_address<T, D, 32>), grid, dim3(256), 0, st, (const T*)k, cb, bias, ksum, addr, cnt, alt, am, i0, s);
+      break;
+    case 64:
+      hipLaunchKernelGGL((k_address<T, D, 64>), grid, dim3(256), 0, st, (const T*)k, cb, bias, ksum, addr, cnt, alt, am, i0, s);
+      break;
+    default:
+      hipLaunchKernelGGL((k_address<T, D, 128>), grid, dim3(256), 0, st, (const T*)k, cb, bias, ksum, addr, cnt, alt, am, i0, s);
+      break;
+  }
+  return hipGetLastError();
+}
+
 template <typename T>
 hipError_t address_dispatch(const Shape& s, const void* k, const float* cb, const float* bias, float* ksum,
                             int32_t* addr, int32_t* cnt, int32_t* alt, float* am, int i0, int n, hipStream_t st) {
   if (n <= 0) return hipSuccess;
   dim3 grid(n, s.B * s.H);
   switch (s.D) {
-    case 32:
-      hipLaunchKernelGGL((k_address<T, 32>), grid, dim3(256), 0, st, (const T*)k, cb, bias, ksum, addr, cnt, alt, am, i0, s);
-      break;
-    case 64:
-      hipLaunchKernelGGL((k_address<T, 64>), grid, dim3(256), 0, st, (const T*)k, cb, bias, ksum, addr, cnt, alt, am, i0, s);
-      break;
-    case 128:
-      hipLaunchKernelGGL((k_address<T, 128>), grid, dim3(256), 0, st, (const T*)k, cb, bias, ksum, addr, cnt, alt, am, i0, s);
-      break;
-    default:
-      return hipErrorInvalidValue;
+    case 32: return address_launch_d<T, 32>(s, grid, k, cb, bias, ksum, addr, cnt, alt, am, i0, st);
+    case 64: return address_launch_d<T, 64>(s, grid, k, cb, bias, ksum, addr, cnt, alt, am, i0, st);
+    case 128: return address_launch_d<T, 128>(s, grid, k, cb, bias, ksum, addr, cnt, alt, am, i0, st);
+    default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 template <typename T, int D, int G, int C, int P, int R, bool FUSED, bool DIAG, int NT>
