@@ -280,7 +280,7 @@ mdr_status run_core(const Shape& s, const void* q, const void* k, const void* v,
   MDR_TRY(launch_probe_rerank(s, q, cb, bias, b.ksum, b.off, b.idx, force, b.sel, b.ncand,
                               binned ? b.phist : nullptr, st, fused ? &fp : nullptr, ex));
   MDR_TRY(mark_event(ev, 3, st));
-  if (binned) MDR_TRY(launch_pair_scatter(s, b.sel, b.phist, b.poff, b.ioff, b.items, st));
+  if (binned) MDR_TRY(launch_pair_scatter(s, b.sel, b.phist, b.poff, b.ioff, b.items, st, false));
   MDR_TRY(launch_attend(s, q, k, v, b.sel, out, b, st, ev ? ev + 4 : nullptr));
   MDR_TRY(mark_event(ev, MDR_CORE_KERNELS, st));
   return MDR_OK;
@@ -513,7 +513,7 @@ mdr_status mdr_stage_attend_lse(const mdr_config* cfg, const void* q, const void
   hipStream_t hs = (hipStream_t)stream;
   if (pairs_binned(s)) {
     MDR_TRY(launch_pair_count(s, sel, b.phist, hs));
-    MDR_TRY(launch_pair_scatter(s, sel, b.phist, b.poff, b.ioff, b.items, hs));
+    MDR_TRY(launch_pair_scatter(s, sel, b.phist, b.poff, b.ioff, b.items, hs, false));
   }
   MDR_TRY(launch_attend(s, q, k, v, sel, out, b, hs));
   return MDR_OK;
@@ -542,7 +542,7 @@ static mdr_status backward_core(const mdr_config* cfg, const void* q, const void
   MDR_TRY(mark_event(ev, 0, hs));
   if (s.R > 0 && s.ne > 0) {
     MDR_TRY(launch_pair_count(s, sel, b.phist, hs));
-    MDR_TRY(launch_pair_scatter(s, sel, b.phist, b.poff, b.ioff, b.items, hs));
+    MDR_TRY(launch_pair_scatter(s, sel, b.phist, b.poff, b.ioff, b.items, hs, true));
   }
   MDR_TRY(launch_attend_backward(s, q, k, v, sel, out, lse, d_out, dq, dk, dv, b, hs, ev ? ev + 1 : nullptr));
   MDR_TRY(mark_event(ev, MDR_BACKWARD_KERNELS, hs));

@@ -353,10 +353,12 @@ hipError_t launch_fill(int32_t* p, long long n, int32_t value, hipStream_t st);
 // Pair binning of a selection: launch_pair_count writes every token range's row of counts (the probe
 // kernels count their own selections instead, into counters the address kernel clears);
 // launch_pair_scatter turns the counts into the per-block lists, cut into the remote work items
-// (stable: ascending token within a block).
+// (stable: ascending token within a block, for the backward's fixed summation order; otherwise the
+// order within each token range's part of a list is arbitrary, which the forward's results do not
+// depend on).
 hipError_t launch_pair_count(const Shape& s, const int32_t* sel, int32_t* phist, hipStream_t st);
 hipError_t launch_pair_scatter(const Shape& s, const int32_t* sel, const int32_t* phist, int32_t* poff,
-                               int32_t* ioff, int32_t* items, hipStream_t st);
+                               int32_t* ioff, int32_t* items, hipStream_t st, bool stable);
 size_t pair_scatter_lds_bytes(const Shape& s);
 size_t remote_lds_bytes(const Shape& s);
 // True when the forward's remote attention scans the selection itself (k_attn_remote_scan: S <=

@@ -3,16 +3,19 @@
 // Routing is per query token, so the remote blocks of neighbouring tokens differ (aitechinspire.com
 // write-up, "Snapshot: key facts from the report": each query probes, reranks and keeps a fixed number
 // of remote blocks).  The attention reads each selected block's K/V once and applies it to every pair
-// that chose it, so the pairs are first grouped by block -- a stable counting sort in space linear in the
+// that chose it, so the pairs are first grouped by block -- a counting sort in space linear in the
 // sequence:
 //   counts   per (b,h), token range g (tbin tokens) and remote block i, the number of valid pairs: the
 //            probe kernels count their own selections; k_pair_count counts a selection passed in, one
 //            work-group per range writing its whole row (so the counters need no clearing first)
 //   scatter  k_pair_scatter, one work-group per (range, b,h): the totals over all ranges give each
 //            block's list offset (poff), the counts of the earlier ranges this range's first slot per
-//            block; its waves then file their pairs in ascending pair id (t R + r) with ballot ranks, so
-//            every list is in ascending token order whatever the timing.  The lists are stored as the
-//            remote work items: each block's list cut into records of kItemPairs pair ids.
+//            block; its pairs then go to their block's part of the list for this range.  For the
+//            backward the waves file them in ascending pair id (t R + r) with ballot ranks, so every
+//            list is in ascending token order whatever the timing; for the forward, whose partials
+//            depend on each pair's own query only, each takes the next slot by an LDS atomic.  The
+//            lists are stored as the remote work items: each block's list cut into records of
+//            kItemPairs pair ids.
 #include "mdr_internal.h"
 
 namespace mdr {
@@ -50,6 +53,12 @@ __global__ __launch_bounds__(kCountThreads) void k_pair_count(const int32_t* __r
   for (int i = tid; i < s.ne; i += kCountThreads) dst[i] = cnt[i];
 }
 
+// STABLE: the waves file their pairs with ballot ranks, so every list is in ascending pair id (the
+// backward's sums over a block's pairs then run in a fixed order).  Otherwise (the forward) each pair
+// takes the next slot of its block within the range's part of the list by an LDS atomic: the order
+// inside a range's part varies from call to call, but the forward computes every pair's partial from
+// its own query alone, so its results do not depend on it.
+template <bool STABLE>
 __global__ __launch_bounds__(kScatterThreads) void k_pair_scatter(const int32_t* __restrict__ sel,
                                                               const int32_t* __restrict__ phist,
                                                               int32_t* __restrict__ poff, int32_t* __restrict__ ioff,
@@ -138,6 +147,11 @@ __global__ __launch_bounds__(kScatterThreads) void k_pair_scatter(const int32_t*
   // before the keys are staged; otherwise the thread that owns a token rewrites its staged row.
   const bool lane_rows = 64 % s.R == 0;  // then R is a power of two, as the block size always is
   const int rsh = __builtin_ctz(s.R), bsh = __builtin_ctz(s.blk);
+  // unstable filing of pair pid into block i: the next free slot of the range's part of i's list
+  auto file = [&](int i, int pid) __attribute__((always_inline)) {
+    const int pos = atomicAdd(&base[i], 1) - start[i];
+    if (pos >= 0 && istart[i] + pos / kItemPairs < s.max_items) items[item_pair_slot(s, bh, istart[i], pos)] = pid;
+  };
   for (int t0 = tfirst; t0 < tlast; t0 += tps) {
     const int nt = min(tps, tlast - t0), np = nt * s.R;
     const int share = ((np + nwf - 1) / nwf + 63) & ~63;
@@ -156,9 +170,16 @@ __global__ __launch_bounds__(kScatterThreads) void k_pair_scatter(const int32_t*
       }
     }
     __syncthreads();  // the previous piece is filed: its keys and the counts are free
+    if (!STABLE && lane_rows) {  // the entries were tested in registers: file them from there
+#pragma unroll
+      for (int u = 0; u < kSubPairs / kScatterThreads; ++u)
+        if (v[u] >= 0) file(v[u], t0 * s.R + u * kScatterThreads + tid);
+      continue;
+    }
 #pragma unroll
     for (int u = 0; u < kSubPairs / kScatterThreads; ++u) keys[u * kScatterThreads + tid] = v[u];
-    for (int x = tid; x < nwf * ne; x += kScatterThreads) wc[x] = 0;
+    if (STABLE)
+      for (int x = tid; x < nwf * ne; x += kScatterThreads) wc[x] = 0;
     __syncthreads();
     if (!lane_rows) {
       for (int u = tid; u < nt; u += kScatterThreads) {
@@ -172,6 +193,11 @@ __global__ __launch_bounds__(kScatterThreads) void k_pair_scatter(const int32_t*
         }
       }
       __syncthreads();
+    }
+    if (!STABLE) {
+      for (int p = tid; p < np; p += kScatterThreads)
+        if (keys[p] >= 0) file(keys[p], t0 * s.R + p);
+      continue;
     }
     const int pw0 = min(np, wave * share), pw1 = min(np, pw0 + share);
     if (wave < nwf)
@@ -234,16 +260,20 @@ hipError_t launch_pair_count(const Shape& s, const int32_t* sel, int32_t* phist,
 }
 
 hipError_t launch_pair_scatter(const Shape& s, const int32_t* sel, const int32_t* phist, int32_t* poff,
-                               int32_t* ioff, int32_t* items, hipStream_t st) {
+                               int32_t* ioff, int32_t* items, hipStream_t st, bool stable) {
   if (s.R <= 0 || s.ne <= 0) return hipSuccess;
   const size_t lds = pair_scatter_lds_bytes(s);
+  const void* fn = stable ? (const void*)k_pair_scatter<true> : (const void*)k_pair_scatter<false>;
   if (lds > 65536) {
-    hipError_t e = hipFuncSetAttribute((const void*)k_pair_scatter, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)lds);
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(k_pair_scatter, dim3(s.ng, s.B * s.H), dim3(kScatterThreads), lds, st, sel, phist, poff, ioff,
-                     items, s);
+  if (stable)
+    hipLaunchKernelGGL(k_pair_scatter<true>, dim3(s.ng, s.B * s.H), dim3(kScatterThreads), lds, st, sel, phist, poff,
+                       ioff, items, s);
+  else
+    hipLaunchKernelGGL(k_pair_scatter<false>, dim3(s.ng, s.B * s.H), dim3(kScatterThreads), lds, st, sel, phist, poff,
+                       ioff, items, s);
   return hipGetLastError();
 }
 

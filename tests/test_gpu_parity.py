@@ -430,6 +430,40 @@ def test_stage_attend_hot_block(gpu_lib, name):
     assert err <= TOL[w.dtype]
 
 
+@pytest.mark.parametrize("over", [dict(seq=16384), dict(seq=12288, remote=3)])
+def test_stage_attend_binned_hot_block(gpu_lib, over):
+    """Past 8,192 tokens the forward bins its pairs, each taking the next slot of its block by an LDS
+    atomic, so the order inside a list varies between calls.  A hot block's list then spans many work
+    items; R = 3 takes the path that stages the entries in LDS.  Sampled tokens (every token of the
+    first and last query blocks, and a seeded spread) against the oracle, and two calls bit for bit
+    (each pair's partial depends on its own query alone)."""
+    mdr = gpu_lib
+    w = synth.workload("sweep", heads=2, **over)
+    inp = synth.make_core_inputs(w, 9)
+    sel = hot_block_selection(w, 9)
+    cfg = cfg_of(mdr, w)
+    dt = io_dtype(w)
+    q, k, v = (dev(inp[n], dt) for n in ("q", "k", "v"))
+    ws = mdr.workspace(cfg)
+    outs = []
+    for _ in range(2):
+        out = torch.empty_like(q)
+        mdr.mdr_stage_attend(cfg, q, k, v, dev(sel), out, ws)
+        torch.cuda.synchronize()
+        outs.append(host(out))
+    assert np.array_equal(outs[0], outs[1])
+    rng = np.random.default_rng(9)
+    toks = np.unique(np.concatenate([np.arange(w.block), np.arange(w.seq - w.block, w.seq),
+                                     rng.choice(w.seq, 384, replace=False)]))
+    err = 0.0
+    for b in range(w.batch):
+        for h in range(w.heads):
+            ref = attention_rows(w, inp, sel[b, h][toks], b, h, toks)
+            err = max(err, float(np.abs(outs[0][b, h, toks] - ref).max()))
+    print(f"{over}: block 0 pairs per head {int((sel[0, 0] == 0).sum())}, sampled max abs err {err:.3g}")
+    assert err <= TOL[w.dtype]
+
+
 @pytest.mark.parametrize("marked", [None, 2, 3])
 def test_profiled_form_gives_the_same_results(gpu_lib, marked):
     """mdr_routed_attention_profiled with every event, or with events around one kernel only (null
