@@ -44,11 +44,21 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}  # MI355X dense, published (fp32: no fp32 MFMA figure; vector)
+def _has(sym, name):
+    """sym (a substring, or a tuple of alternatives: rocprofv3 prints some names demangled and leaves
+    others, such as those with bf16 template arguments, mangled) occurs in the kernel name."""
+    return any(x in name for x in (sym if isinstance(sym, tuple) else (sym,)))
+
+
+def _label(sym):
+    return sym[0] if isinstance(sym, tuple) else sym
+
+
 KERNEL_SYMBOL = {  # substrings of the kernels' symbol names in rocprofv3 output
     "address": "k_address",
     "post": "k_post",
     "probe_rerank": "k_probe",
-    "attn_bin": "k_pair_scatter",
+    "attn_bin": ("k_pair_scatter<false>", "k_pair_scatterILb0E"),  # the forward's (unordered) filing
     "attn_remote": "k_attn_remote",
     "attn_local": "k_attn_local",
 }
@@ -65,8 +75,9 @@ MIXER_SYMBOL = {  # every listed substring must occur in the (mangled) kernel na
     "output projection": ("k_mm", "Lb1ELb0E"),
     "weight transposes": ("k_transpose",),
 }
-BACKWARD_SYMBOL = {  # the backward's binning also runs k_pair_scatter, listed with the forward's kernels
+BACKWARD_SYMBOL = {
     "pair_bin (count)": "k_pair_count",
+    "pair_bin (ordered scatter)": ("k_pair_scatter<true>", "k_pair_scatterILb1E"),
     "bwd_dot": "k_bwd_dot",
     "bwd_kv": "k_bwd_kv",
     "bwd_q": "k_bwd_q",
@@ -782,8 +793,8 @@ def ingest_pmc(fetch_csv, write_csv, w):
                                                    "write_kib": calib_w[0], "fetch_scale": sf, "write_scale": sw},
            "kernels": {}}
     for k, sym in KERNEL_SYMBOL.items():
-        fn = [n for n in fetch if sym in n]
-        wn = [n for n in write if sym in n]
+        fn = [n for n in fetch if _has(sym, n)]
+        wn = [n for n in write if _has(sym, n)]
         if not fn or not wn:
             continue
         fb = fetch[fn[0]] * sf * 1024
@@ -816,14 +827,14 @@ def summarize_rocprof(stats_csv, command, w, bench_log=None, stem="routed_attent
              "|---|---|---|---|---|---|---|"]
     for k, sym in KERNEL_SYMBOL.items():
         for r in rows:
-            if sym in r["Name"]:
+            if _has(sym, r["Name"]):
                 ev = f"{events[k]:.2f}" if k in events else "-"
-                lines.append(f"| {k} (`{sym}`) | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                lines.append(f"| {k} (`{_label(sym)}`) | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                              f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
                              f"{float(r['Percentage']):.1f}% | {ev} |")
     if timed:
         stage = list(STAGE_KERNELS)
-        avgs = [next((float(r["AverageNs"]) / 1e3 for r in rows if KERNEL_SYMBOL[k] in r["Name"]), None)
+        avgs = [next((float(r["AverageNs"]) / 1e3 for r in rows if _has(KERNEL_SYMBOL[k], r["Name"])), None)
                 for k in stage]
         tot = sum(avgs) if all(x is not None for x in avgs) else None
         lines += ["", f"The HIP-event column is bench.py's pass with an event before every kernel.  In its timed "
@@ -838,9 +849,9 @@ def summarize_rocprof(stats_csv, command, w, bench_log=None, stem="routed_attent
     bl = []
     for k, sym in BACKWARD_SYMBOL.items():
         for r in rows:
-            if sym in r["Name"]:
+            if _has(sym, r["Name"]):
                 ev = f"{bwd[k]:.2f}" if k in bwd else "-"
-                bl.append(f"| {k} (`{sym}`) | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                bl.append(f"| {k} (`{_label(sym)}`) | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                           f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
                           f"{float(r['Percentage']):.1f}% | {ev} |")
     if bl:
@@ -858,7 +869,7 @@ def summarize_rocprof(stats_csv, command, w, bench_log=None, stem="routed_attent
         lines += ["", "Mixer (mdr_mixer_forward at width 512; its core kernels are counted in the table above):", "",
                   "| kernel | calls | avg us | min us | max us | share of GPU time |", "|---|---|---|---|---|---|"] + ml
     known = list(KERNEL_SYMBOL.values()) + list(BACKWARD_SYMBOL.values()) + [v[0] for v in MIXER_SYMBOL.values()]
-    other = sum(float(r["Percentage"]) for r in rows if not any(sym in r["Name"] for sym in known))
+    other = sum(float(r["Percentage"]) for r in rows if not any(_has(sym, r["Name"]) for sym in known))
     lines += ["", f"Other kernels (input generation, torch copies, routing statistics): {other:.1f}% of GPU time.", ""]
     out = os.path.join(ROOT, "profiles", f"{stem}_{w.name}_{w.seq // 1024}k.md")
     os.makedirs(os.path.dirname(out), exist_ok=True)
