@@ -693,17 +693,23 @@ _CPU_JOB = {}  # the workload and its inputs, set before the worker processes ar
 
 
 def _cpu_task(task):
-    """One share of the CPU baseline: routing (with its head's index build) and gathered fp64 attention for
-    a contiguous token range of one head, on one thread."""
+    """One share of the CPU baseline: the packed C oracle (oracle/mdr_packed.c: routing with its head's
+    index build, then gathered fp64 attention) over a contiguous token range of one head, on one thread.
+    With kind "numpy" the NumPy oracle does the same share instead."""
     import numpy as np
     from threadpoolctl import threadpool_limits
 
-    import oracle
-
-    h, t0, t1 = task
+    kind, h, t0, t1 = task
     w, inp = _CPU_JOB["w"], _CPU_JOB["inputs"]
     q, k, v = (inp[n][0, h] for n in ("q", "k", "v"))
     bias = None if inp["bias"] is None else inp["bias"][h]
+    if kind == "packed":
+        from oracle import packed
+
+        packed.packed_forward(q, k, v, inp["codebook"][h], bias, w, t0, t1)
+        return t1 - t0
+    import oracle
+
     toks = np.arange(t0, t1)
     with threadpool_limits(1):
         r = oracle.route_head(q, k, inp["codebook"][h], bias, w, tokens=toks)
@@ -725,34 +731,76 @@ def host_cpu():
     return max(1, min(avail, 16)), avail, model
 
 
-def cpu_baseline(w, inputs, heads):
-    """The oracle as it stands (routing + gathered fp64 attention) on the host's cores: a pool of forked
-    worker processes (one BLAS thread each) over (head, token range) shares of the sample, so every core
-    has work; then the same oracle on one thread over one head, for the per-core rate.  Runs before the
-    process initialises the GPU, so forking is safe."""
+def cpu_baseline(w, inputs, heads, seed=0, sweep=True):
+    """The oracle on the host's cores: the packed C oracle (the timed value) and the NumPy oracle beside
+    it, each over (head, token range) shares of the sample on a pool of forked worker processes (one
+    thread each) so every core has work, then on one thread over one head for the per-core rate; with
+    sweep, the packed oracle's one-thread time on one head at 4K-32K tokens and its fitted exponent.
+    Runs before the process initialises the GPU, so forking is safe."""
     import multiprocessing as mp
 
+    import synth
+    from oracle import packed
+
+    packed._load()  # built (if needed) before the workers fork
     heads = min(heads, w.heads)
     cores, avail, model = host_cpu()
     parts = max(1, -(-cores // heads))
     bounds = [(w.seq * p) // parts for p in range(parts + 1)]
-    tasks = [(h, bounds[p], bounds[p + 1]) for h in range(heads) for p in range(parts)]
     _CPU_JOB.update(w=w, inputs=inputs)
-    t0 = time.perf_counter()
-    with mp.get_context("fork").Pool(cores) as pool:
-        done = sum(pool.map(_cpu_task, tasks, chunksize=1))
-    dt = time.perf_counter() - t0
-    t1 = time.perf_counter()
-    _cpu_task((0, 0, w.seq))
-    dt1 = time.perf_counter() - t1
-    return {"value": round(done / w.heads / dt, 2), "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "cpu_model": model, "host_cpus_visible": avail,
-            "one_thread_tokens_per_s": round(w.seq / w.heads / dt1, 2),
-            "sample": f"batch 0, heads 0-{heads - 1} of {w.heads}, all {w.seq} tokens each, split into {len(tasks)} "
-                      f"(head, token range) shares over {cores} forked worker processes (one BLAS thread each); "
-                      f"each share routes its tokens (with its head's index build) and runs gathered fp64 "
-                      f"attention; tokens/s counts a token as all {w.heads} heads; {dt:.1f} s wall. "
-                      f"One thread, head 0 alone: {dt1:.1f} s"}
+
+    def pooled(kind):
+        tasks = [(kind, h, bounds[p], bounds[p + 1]) for h in range(heads) for p in range(parts)]
+        t0 = time.perf_counter()
+        with mp.get_context("fork").Pool(cores) as pool:
+            done = sum(pool.map(_cpu_task, tasks, chunksize=1))
+        dt = time.perf_counter() - t0
+        t1 = time.perf_counter()
+        _cpu_task((kind, 0, 0, w.seq))
+        dt1 = time.perf_counter() - t1
+        return done / w.heads / dt, w.seq / w.heads / dt1, dt, dt1, len(tasks)
+
+    rate, rate1, dt, dt1, ntasks = pooled("packed")
+    nrate, nrate1, ndt, ndt1, _ = pooled("numpy")
+    res = {"value": round(rate, 2), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+           "cpu_model": model, "host_cpus_visible": avail,
+           "one_thread_tokens_per_s": round(rate1, 2),
+           "sample": f"the packed C oracle (oracle/mdr_packed.c, gcc -O2, one thread per process): batch 0, heads "
+                     f"0-{heads - 1} of {w.heads}, all {w.seq} tokens each, split into {ntasks} (head, token range) "
+                     f"shares over {cores} forked worker processes; each share routes its tokens (with its head's "
+                     f"index build) and runs gathered fp64 attention; tokens/s counts a token as all {w.heads} "
+                     f"heads; {dt:.2f} s wall. One thread, head 0 alone: {dt1:.2f} s",
+           "numpy_oracle": {"tokens_per_s": round(nrate, 2), "one_thread_tokens_per_s": round(nrate1, 2),
+                            "note": f"the NumPy oracle (oracle/mdr_oracle.py) on the same shares: {ndt:.1f} s wall; "
+                                    f"one thread, head 0: {ndt1:.1f} s"}}
+    if sweep and w.name == "sweep":
+        import numpy as np
+
+        seqs, secs, pairs = [4096, 8192, 16384, 32768], [], []
+        for S in seqs:
+            ws = synth.workload("sweep", seq=S)
+            inp = inputs if S == w.seq else synth.make_core_inputs(ws, seed)
+            bias = None if inp["bias"] is None else inp["bias"][0]
+            args = [inp[n][0, 0] for n in ("q", "k", "v")] + [inp["codebook"][0], bias, ws]
+            best = float("inf")
+            for _ in range(2):  # the faster of two runs
+                t1 = time.perf_counter()
+                sel, _ = packed.packed_forward(*args)
+                best = min(best, time.perf_counter() - t1)
+            secs.append(best)
+            t = np.arange(S)
+            local = t - np.maximum(0, (t // ws.block - ws.local + 1) * ws.block) + 1
+            pairs.append(int((sel >= 0).sum()) * ws.block + int(local.sum()))
+        slope = float(np.polyfit(np.log(seqs), np.log(secs), 1)[0])
+        pslope = float(np.polyfit(np.log(pairs), np.log(secs), 1)[0])
+        res["exponent"] = {"seqs": seqs, "s_one_head_one_thread": [round(x, 4) for x in secs],
+                           "attended_pairs_one_head": pairs, "slope_vs_seq": round(slope, 3),
+                           "slope_vs_attended_pairs": round(pslope, 3),
+                           "note": "the packed C oracle on head 0 of the sweep workload at each length, one thread, "
+                                   "the faster of two runs (routing with the index build, and gathered attention); "
+                                   "the pages report 0.993 "
+                                   "for their packed CPU routing over 4K-32K (CPU not stated)"}
+    return res
 
 
 # ----------------------------------------------------------------------------- PMC ingest
@@ -914,7 +962,7 @@ def main(argv=None):
     if not a.no_cpu and not a.mixer_only:
         # the CPU baseline forks worker processes, so it runs before anything touches the GPU
         inputs = synth.make_core_inputs(w, a.seed)
-        cpu = cpu_baseline(w, inputs, a.cpu_heads)
+        cpu = cpu_baseline(w, inputs, a.cpu_heads, a.seed, sweep=not a.no_sweep)
     import torch
 
     import learned_product_hash_amd as mdr

@@ -64,7 +64,8 @@ def test_cpu_baseline_uses_every_usable_core():
     r = bench.cpu_baseline(w, inp, 8)
     assert r["cores"] == cores and r["kind"] == "oracle" and r["cpu_model"] == model
     assert r["value"] > 0 and r["one_thread_tokens_per_s"] > 0
-    assert str(cores) in r["sample"]
+    assert str(cores) in r["sample"] and "packed C oracle" in r["sample"]
+    assert r["numpy_oracle"]["tokens_per_s"] > 0
 
 
 def test_strip_comments():
