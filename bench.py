@@ -749,8 +749,8 @@ def cpu_baseline(w, inputs, heads, seed=0, sweep=True):
     bounds = [(w.seq * p) // parts for p in range(parts + 1)]
     _CPU_JOB.update(w=w, inputs=inputs)
 
-    def pooled(kind):
-        tasks = [(kind, h, bounds[p], bounds[p + 1]) for h in range(heads) for p in range(parts)]
+    def pooled(kind, reps=1):
+        tasks = [(kind, h, bounds[p], bounds[p + 1]) for h in range(heads) for p in range(parts)] * reps
         t0 = time.perf_counter()
         with mp.get_context("fork").Pool(cores) as pool:
             done = sum(pool.map(_cpu_task, tasks, chunksize=1))
@@ -758,9 +758,9 @@ def cpu_baseline(w, inputs, heads, seed=0, sweep=True):
         t1 = time.perf_counter()
         _cpu_task((kind, 0, 0, w.seq))
         dt1 = time.perf_counter() - t1
-        return done / w.heads / dt, w.seq / w.heads / dt1, dt, dt1, len(tasks)
+        return done / w.heads / dt, w.seq / w.heads / dt1, dt, dt1, len(tasks) // reps
 
-    rate, rate1, dt, dt1, ntasks = pooled("packed")
+    rate, rate1, dt, dt1, ntasks = pooled("packed", reps=3)  # the sample three times: about 10 s of CPU work
     nrate, nrate1, ndt, ndt1, _ = pooled("numpy")
     res = {"value": round(rate, 2), "unit": "tokens/s", "cores": cores, "kind": "oracle",
            "cpu_model": model, "host_cpus_visible": avail,
@@ -768,8 +768,8 @@ def cpu_baseline(w, inputs, heads, seed=0, sweep=True):
            "sample": f"the packed C oracle (oracle/mdr_packed.c, gcc -O2, one thread per process): batch 0, heads "
                      f"0-{heads - 1} of {w.heads}, all {w.seq} tokens each, split into {ntasks} (head, token range) "
                      f"shares over {cores} forked worker processes; each share routes its tokens (with its head's "
-                     f"index build) and runs gathered fp64 attention; tokens/s counts a token as all {w.heads} "
-                     f"heads; {dt:.2f} s wall. One thread, head 0 alone: {dt1:.2f} s",
+                     f"index build) and runs gathered fp64 attention; the shares three times over; tokens/s "
+                     f"counts a token as all {w.heads} heads; {dt:.2f} s wall. One thread, head 0 alone: {dt1:.2f} s",
            "numpy_oracle": {"tokens_per_s": round(nrate, 2), "one_thread_tokens_per_s": round(nrate1, 2),
                             "note": f"the NumPy oracle (oracle/mdr_oracle.py) on the same shares: {ndt:.1f} s wall; "
                                     f"one thread, head 0: {ndt1:.1f} s"}}
