@@ -254,7 +254,8 @@ mdr_status mdr_routed_attention_noalloc(const mdr_config* cfg, const void* q, co
  * k-th kernel of the core path and events[MDR_CORE_KERNELS] after the last one.
  * attn_bin groups the selected (token, slot) pairs by remote block for
  * attn_remote.  A kernel a configuration does not need (attn_bin and
- * attn_remote when R = 0 or nb <= L) gets two adjacent events.  A NULL entry records nothing at that point (so a
+ * attn_remote when R = 0 or nb <= L; attn_bin up to 8192 tokens with R <= 2,
+ * where attn_remote finds each block's pairs itself) gets two adjacent events.  A NULL entry records nothing at that point (so a
  * caller can time one kernel alone); a NULL `events` array is rejected.
  * Everything else is as in mdr_routed_attention. */
 mdr_status mdr_routed_attention_profiled(const mdr_config* cfg, const void* q, const void* k, const void* v,
