@@ -26,20 +26,23 @@ namespace mdr {
 namespace {
 
 // ---------------------------------------------------------------------------------------------
-// Block key summaries and product addresses: one work-group of 256 threads per (b,h, block); the
-// arithmetic is block_address() (mdr_address.h), shared with the decode path.  The work-group of
-// block i also clears column i of the pair counters when asked.
-template <typename T, int D, int BLK>
+// Block key summaries and product addresses: one work-group of 256 threads per (b,h) and NB adjacent
+// blocks (blocks i0 + NB x .. of blockIdx.x = x, up to iend); the arithmetic is block_address()
+// (mdr_address.h), shared with the decode path, and gives every block the same bits whatever NB.  The
+// work-group also clears the pair counters' columns of its blocks when asked.
+template <typename T, int D, int BLK, int NB>
 __global__ __launch_bounds__(256) void k_address(const T* __restrict__ K, const float* __restrict__ cb,
                                                  const float* __restrict__ bias, float* __restrict__ ksum,
                                                  int32_t* __restrict__ addr, int32_t* __restrict__ pair_zero,
                                                  int32_t* __restrict__ alt, float* __restrict__ amargin, int i0,
-                                                 Shape s) {
-  __shared__ AddressLds<T, D> sm;
-  const int i = i0 + blockIdx.x;
+                                                 int iend, Shape s) {
+  __shared__ AddressLds<T, D, NB> sm;
+  const int i = i0 + blockIdx.x * NB;
+  const int nv = min(NB, iend - i);
   const int bh = blockIdx.y;
-  if (pair_zero) clear_pair_counts(pair_zero, s, bh, i, threadIdx.x, 256);
-  block_address<T, D, BLK>(K, cb, bias, ksum, addr, i, bh, sm, s, alt, amargin);
+  if (pair_zero)
+    for (int b = 0; b < nv; ++b) clear_pair_counts(pair_zero, s, bh, i + b, threadIdx.x, 256);
+  block_address<T, D, BLK, NB>(K, cb, bias, ksum, addr, i, bh, sm, s, alt, amargin, nv);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -1327,32 +1330,41 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(probe_min_wa
   pc.end();
 }
 
+// Two blocks per work-group when a thread's key rows of both fit in a few registers (at most four
+// 16-byte reads per block), else one.
+template <typename T, int D, int BLK>
+constexpr int address_blocks_per_group() {
+  return (BLK + AddressLds<T, D>::RG - 1) / AddressLds<T, D>::RG <= 4 ? 2 : 1;
+}
+
+template <typename T, int D, int BLK>
+hipError_t address_launch_b(const Shape& s, int n, const void* k, const float* cb, const float* bias, float* ksum,
+                            int32_t* addr, int32_t* cnt, int32_t* alt, float* am, int i0, hipStream_t st) {
+  constexpr int NB = address_blocks_per_group<T, D, BLK>();
+  const dim3 grid((n + NB - 1) / NB, s.B * s.H);
+  hipLaunchKernelGGL((k_address<T, D, BLK, NB>), grid, dim3(256), 0, st, (const T*)k, cb, bias, ksum, addr, cnt, alt,
+                     am, i0, i0 + n, s);
+  return hipGetLastError();
+}
+
 template <typename T, int D>
-hipError_t address_launch_d(const Shape& s, dim3 grid, const void* k, const float* cb, const float* bias, float* ksum,
+hipError_t address_launch_d(const Shape& s, int n, const void* k, const float* cb, const float* bias, float* ksum,
                             int32_t* addr, int32_t* cnt, int32_t* alt, float* am, int i0, hipStream_t st) {
   switch (s.blk) {
-    case 32:
-      hipLaunchKernelGGL((k_address<T, D, 32>), grid, dim3(256), 0, st, (const T*)k, cb, bias, ksum, addr, cnt, alt, am, i0, s);
-      break;
-    case 64:
-      hipLaunchKernelGGL((k_address<T, D, 64>), grid, dim3(256), 0, st, (const T*)k, cb, bias, ksum, addr, cnt, alt, am, i0, s);
-      break;
-    default:
-      hipLaunchKernelGGL((k_address<T, D, 128>), grid, dim3(256), 0, st, (const T*)k, cb, bias, ksum, addr, cnt, alt, am, i0, s);
-      break;
+    case 32: return address_launch_b<T, D, 32>(s, n, k, cb, bias, ksum, addr, cnt, alt, am, i0, st);
+    case 64: return address_launch_b<T, D, 64>(s, n, k, cb, bias, ksum, addr, cnt, alt, am, i0, st);
+    default: return address_launch_b<T, D, 128>(s, n, k, cb, bias, ksum, addr, cnt, alt, am, i0, st);
   }
-  return hipGetLastError();
 }
 
 template <typename T>
 hipError_t address_dispatch(const Shape& s, const void* k, const float* cb, const float* bias, float* ksum,
                             int32_t* addr, int32_t* cnt, int32_t* alt, float* am, int i0, int n, hipStream_t st) {
   if (n <= 0) return hipSuccess;
-  dim3 grid(n, s.B * s.H);
   switch (s.D) {
-    case 32: return address_launch_d<T, 32>(s, grid, k, cb, bias, ksum, addr, cnt, alt, am, i0, st);
-    case 64: return address_launch_d<T, 64>(s, grid, k, cb, bias, ksum, addr, cnt, alt, am, i0, st);
-    case 128: return address_launch_d<T, 128>(s, grid, k, cb, bias, ksum, addr, cnt, alt, am, i0, st);
+    case 32: return address_launch_d<T, 32>(s, n, k, cb, bias, ksum, addr, cnt, alt, am, i0, st);
+    case 64: return address_launch_d<T, 64>(s, n, k, cb, bias, ksum, addr, cnt, alt, am, i0, st);
+    case 128: return address_launch_d<T, 128>(s, n, k, cb, bias, ksum, addr, cnt, alt, am, i0, st);
     default: return hipErrorInvalidValue;
   }
 }
