@@ -373,6 +373,30 @@ def test_full_size_sampled(gpu_lib, name):
     assert err <= TOL[w.dtype]
 
 
+@pytest.mark.parametrize("name,over", [
+    ("long", dict(heads=2, seq=4096, remote=2)),                  # bf16, D 128, blocks of 128
+    ("skew", dict(batch=1, heads=4, seq=4096, remote=2)),         # bf16, D 128, blocks of 64
+    ("long", dict(heads=1, seq=2048, block=64, remote=1, dtype="f32")),  # fp32, D 128, blocks of 64, R = 1
+    ("recall", dict(batch=2, seq=8192, remote=2)),                # the longest sequence the scan takes
+])
+def test_short_sequence_remote_scan(gpu_lib, name, over):
+    """Up to 8,192 tokens with R <= 2 the remote kernel finds each block's pairs in the selection itself
+    (no binning kernel): head dims, block sizes and dtypes beyond the sweep's, against the oracle."""
+    mdr = gpu_lib
+    w = small(name, **over)
+    inp = synth.make_core_inputs(dataclass_replace_plant(w) if w.plant == "recall" else w, 10)
+    res = run_core(mdr, w, inp)
+    near = 0
+    err = 0.0
+    for b in range(w.batch):
+        for h in range(w.heads):
+            near += check_head_routing(w, inp, res, b, h)[1]
+            ref = attention_rows(w, inp, res["sel"][b, h], b, h, None, dense=w.seq <= 4096)
+            err = max(err, float(np.abs(res["out"][b, h] - ref).max()))
+    print(f"{name} {over}: selection near-ties {near}, max abs err {err:.3g}")
+    assert err <= TOL[w.dtype]
+
+
 @pytest.mark.parametrize("name,over", [("sweep", dict(probes=3)), ("long", dict(remote=3)),
                                        ("skew", dict(probes=5, remote=7)), ("recall", dict(codes=6, probes=11)),
                                        ("tiny", dict(subspaces=1, codes=8, probes=3))])
