@@ -11,12 +11,16 @@
 // each token's remote blocks separately would move every block many times, so the remote part
 // is regrouped by block:
 //   pairs          the selected (token, slot) pairs are binned by remote block (mdr_pairs.hip): each
-//                  block's list in ascending token order, cut into work items of kItemPairs pair ids
+//                  block's list by token range, cut into work items of kItemPairs pair ids (a pair's
+//                  partial depends on its own query alone, not on its place in the list)
 //   k_attn_remote  one work-group per work item: the block's K/V is staged in LDS, the item's pairs
 //                  go 16 per wave, their queries are gathered, S^T = K Q^T and O^T = V^T P^T run on
 //                  MFMA, and each pair's softmax partial (normalised output, log2 normaliser) is
 //                  stored at [token][slot].  The items of one (b,h) run on one XCD when the heads
 //                  divide evenly, so that head's query rows and partials share that XCD's L2
+//   k_attn_remote_scan  short sequences (at most kScanMaxTokens tokens, R <= 2): the same partials,
+//                  one work-group per (b,h, block), which finds the block's pairs in the selection
+//                  itself, so no binning pass runs
 //   k_attn_local   one work-group per query block: the L local blocks through LDS on MFMA with
 //                  the causal mask on the diagonal block and an online softmax, then the
 //                  remote partials of each token are merged in slot order and O is written.
