@@ -153,7 +153,7 @@ __global__ __launch_bounds__(kRemoteWaves * 64) void k_attn_remote_scan(const T*
   T* Ks = (T*)lds_raw;
   T* Vx = Ks + TL::K_ELEMS;
   int32_t* cnt = (int32_t*)(Vx + TL::V_ELEMS);  // NC counts, then their exclusive scan; [NC] = total
-  int32_t* list = cnt + NC + 4;                 // the block's pair ids
+  uint16_t* list = (uint16_t*)(cnt + NC + 4);   // the block's pair ids (below S R <= 2 kScanMaxTokens)
   int bh, i;
   remote_block_of(s, blockIdx.x, gridDim.x, &bh, &i);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -200,14 +200,15 @@ __global__ __launch_bounds__(kRemoteWaves * 64) void k_attn_remote_scan(const T*
 #pragma unroll
   for (int c = 0; c < ROWS; ++c) {
     const int h = (hits >> (2 * c)) & 3;
-    if (h) list[cnt[c * kRemoteWaves + wave] + __popcll(bal[c] & below)] = (t0 + c * NTHR + tid) * R + h - 1;
+    if (h)
+      list[cnt[c * kRemoteWaves + wave] + __popcll(bal[c] & below)] = (uint16_t)((t0 + c * NTHR + tid) * R + h - 1);
   }
   __syncthreads();
   const int n = cnt[NC];
 #pragma unroll 1
   for (int base = wave * 16; base < n; base += kItemPairs) {  // no barriers in this loop
     const int e = base + (lane & 15);
-    const int pid = e < n ? list[e] : -1;
+    const int pid = e < n ? (int)list[e] : -1;
     QFrag<T, D> qf;
     load_q<T, D>(qf, Q + (rowbase + (pid < 0 ? 0 : pid / R)) * D, lane);
     // the tiles are read again in every round: an offset the compiler cannot see through keeps it from
@@ -218,10 +219,13 @@ __global__ __launch_bounds__(kRemoteWaves * 64) void k_attn_remote_scan(const T*
   }
 }
 
-// LDS of k_attn_remote_scan: the block's K/V, the wave counts and the pair list.
+// LDS of k_attn_remote_scan: the block's K/V, the wave counts and the pair list (16-bit pair ids: every
+// pair id t R + r is below kScanMaxTokens R <= 65536).
+static_assert(kScanMaxTokens * 2 <= 65536, "16-bit pair ids");
 template <typename T, int D, int BLK>
 constexpr size_t scan_lds_bytes() {
-  return Tile<T, D, BLK>::LDS_BYTES + (size_t)(kScanMaxTokens / (kRemoteWaves * 64) * kRemoteWaves + 4 + kScanMaxTokens) * 4;
+  return Tile<T, D, BLK>::LDS_BYTES + (size_t)(kScanMaxTokens / (kRemoteWaves * 64) * kRemoteWaves + 4) * 4 +
+         (size_t)kScanMaxTokens * 2;
 }
 
 // One work-group per query block: local blocks + merge of the remote partials.  The selection row,
