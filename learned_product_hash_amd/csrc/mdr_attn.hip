@@ -220,12 +220,14 @@ __global__ __launch_bounds__(kRemoteWaves * 64) void k_attn_remote_scan(const T*
 }
 
 // LDS of k_attn_remote_scan: the block's K/V, the wave counts and the pair list (16-bit pair ids: every
-// pair id t R + r is below kScanMaxTokens R <= 65536).
+// pair id t R + r is below kScanMaxTokens R <= 65536), sized for the most pairs a block can have, one
+// per token that can see it: S - L blk.
 static_assert(kScanMaxTokens * 2 <= 65536, "16-bit pair ids");
 template <typename T, int D, int BLK>
-constexpr size_t scan_lds_bytes() {
+size_t scan_lds_bytes(const Shape& s) {
+  const size_t most = s.S > s.L * BLK ? (size_t)(s.S - s.L * BLK) : 0;
   return Tile<T, D, BLK>::LDS_BYTES + (size_t)(kScanMaxTokens / (kRemoteWaves * 64) * kRemoteWaves + 4) * 4 +
-         (size_t)kScanMaxTokens * 2;
+         (most * 2 + 15) / 16 * 16;
 }
 
 // One work-group per query block: local blocks + merge of the remote partials.  The selection row,
@@ -417,7 +419,7 @@ hipError_t attend_impl(const Shape& s, const void* q, const void* k, const void*
   hipError_t e;
   if ((e = mark_event(ev, 0, st)) != hipSuccess) return e;
   if (remote && remote_scans(s)) {
-    const size_t rl = scan_lds_bytes<T, D, BLK>();
+    const size_t rl = scan_lds_bytes<T, D, BLK>(s);
     const void* kfn = s.R == 2 ? (const void*)k_attn_remote_scan<T, D, BLK, 2> : (const void*)k_attn_remote_scan<T, D, BLK, 1>;
     if (rl > 65536 && (e = hipFuncSetAttribute(kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)rl)) != hipSuccess)
       return e;
@@ -446,13 +448,15 @@ hipError_t attend_impl(const Shape& s, const void* q, const void* k, const void*
 }
 
 template <typename T, int D>
-size_t scan_lds_d(int blk) {
-  return blk == 32 ? scan_lds_bytes<T, D, 32>() : blk == 64 ? scan_lds_bytes<T, D, 64>() : scan_lds_bytes<T, D, 128>();
+size_t scan_lds_d(const Shape& s) {
+  return s.blk == 32   ? scan_lds_bytes<T, D, 32>(s)
+         : s.blk == 64 ? scan_lds_bytes<T, D, 64>(s)
+                       : scan_lds_bytes<T, D, 128>(s);
 }
 
 template <typename T>
 size_t scan_lds_t(const Shape& s) {
-  return s.D == 32 ? scan_lds_d<T, 32>(s.blk) : s.D == 64 ? scan_lds_d<T, 64>(s.blk) : scan_lds_d<T, 128>(s.blk);
+  return s.D == 32 ? scan_lds_d<T, 32>(s) : s.D == 64 ? scan_lds_d<T, 64>(s) : scan_lds_d<T, 128>(s);
 }
 
 template <typename T, int D>
